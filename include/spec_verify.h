@@ -1,0 +1,200 @@
+/*
+ * spec_verify.h -- C ABI of the speculative-decoding verification step on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * One verification step for a batch of B requests, each carrying a draft tree
+ * (a chain is the tree whose node j has parent j-1) of T_b candidate tokens:
+ *
+ *   1. tree-masked grouped-query attention of every draft node against its
+ *      request's KV cache                          -> spec_verify_attn
+ *   2. lossless rejection sampling over the whole vocabulary, walking the tree
+ *      and emitting the accepted path plus one bonus token
+ *                                                   -> spec_verify_sample
+ *   3. both, back to back on one stream             -> spec_verify_step
+ *
+ * Sources (the method is defined there; section names are given per call):
+ *   [SD]   "Speculative Decoding: Accelerating Inference Speeds in Distributed
+ *          LLMs" (shyankdev.com blog).
+ *   [LOSSY] "Revisiting Lossy Verification in Speculative Decoding: Mechanisms,
+ *          Trade-offs, and Failure Modes" (arXiv 2607.26627).
+ *   [ECHO] "ECHO: Elastic Speculative Decoding with Sparse Gating for
+ *          High-Concurrency Scenarios" (arXiv 2604.09603).
+ *   [SPEED] "SPEED-Bench: A Unified and Diverse Benchmark for Speculative
+ *          Decoding" (arXiv 2604.09557).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every pointer in the argument structs is DEVICE memory owned by the
+ *    caller, except where a field says otherwise. The library allocates no
+ *    device memory; scratch lives in the caller's workspace (see
+ *    spec_verify_workspace_size). It keeps no state between calls and is
+ *    reentrant; two calls may run concurrently on different streams if they
+ *    use different workspaces and outputs.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream) and never synchronise with the host.
+ *  - Argument errors are found on the host before anything is enqueued: the
+ *    call then returns a non-SV_OK code, enqueues nothing and leaves a message
+ *    for spec_verify_last_error(). SV_ERR_HIP means a launch failed.
+ *  - Errors that depend on device data are OR-ed as SV_STATUS_* bits into the
+ *    optional device word `status` (the library never clears it: zero it
+ *    before the call for per-call status). Kernels stay in bounds whatever the
+ *    data: offending requests are skipped or clamped as each bit documents.
+ *  - Results are a pure function of the inputs (and of seed, step and
+ *    request ids): every reduction runs in a fixed order, so two identical
+ *    calls give bitwise identical outputs.
+ *  - Packing ("Flatten & Pack", [ECHO] Figure 3 and the super-tree of its
+ *    section 3.1): the nodes of all requests are concatenated; request b owns
+ *    packed nodes [cu_nodes[b], cu_nodes[b+1]), T_b = cu_nodes[b+1]-cu_nodes[b],
+ *    0 <= T_b <= 64, N = cu_nodes[B] = total_nodes. Local node j of request b
+ *    is packed node cu_nodes[b] + j.
+ *  - Trees are given as a parent array of LOCAL indices in topological order:
+ *    parent[cu_nodes[b]+j] is in [-1, j-1]; -1 means the node hangs off the
+ *    request's root (its last committed token).
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SV_OK = 0,
+  SV_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size or value      */
+  SV_ERR_TREE = 2,        /* reserved for host-visible tree errors            */
+  SV_ERR_UNSUPPORTED = 3, /* valid but unsupported shape (e.g. D not 64/128)  */
+  SV_ERR_WORKSPACE = 4,   /* workspace missing, misaligned or too small       */
+  SV_ERR_HIP = 5          /* a HIP launch failed                              */
+} sv_status;
+
+typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
+
+/* Data-error bits OR-ed into *status by the kernels. */
+#define SV_STATUS_TREE_INVALID   0x01 /* parent outside [-1, j-1]: node treated as a root child (attn) / request skipped (sample) */
+#define SV_STATUS_PACKING        0x02 /* cu_nodes not monotone, T_b > max_nodes, or cu_nodes[B] != total_nodes: request skipped */
+#define SV_STATUS_TOKEN_RANGE    0x04 /* draft token outside [0, V): request skipped */
+#define SV_STATUS_NONFINITE      0x08 /* NaN or +inf logit in a row, or a row whose logits are all -inf */
+#define SV_STATUS_ZERO_RESIDUAL  0x10 /* residual mass rounded to 0 after a rejection: distribution kept unchanged */
+#define SV_STATUS_CTX_RANGE      0x20 /* ctx_len[b] < 0 or ctx_len[b] + T_b > Lcap: request skipped */
+
+/* ------------------------------------------------------------------------ */
+/* Tree-masked GQA attention ([SD] "Tree Attention Mask Mechanics"; GQA as in
+ * [SD] "Interaction with Advanced Attention Architectures (GQA & MLA)").
+ *
+ * For request b, query head h (KV head g = h / (Hq/Hkv)) and local node j:
+ *   visible keys = context slots [0, ctx_len[b]) of the cache
+ *                  + draft slot ctx_len[b] + i for every i that is j itself or
+ *                    an ancestor of j (never a sibling branch);
+ *   s_t = scale * <q, k_t>,  w = softmax(s) over the visible keys,
+ *   out = sum_t w_t v_t.
+ * The draft node i's key/value sit in cache slot ctx_len[b] + i (node order).
+ * q and k are used as given (position encoding already applied).          */
+typedef struct {
+  int32_t B;           /* requests, >= 0                                      */
+  int32_t total_nodes; /* N = cu_nodes[B]                                     */
+  int32_t max_nodes;   /* upper bound on every T_b, 1..64; 0 means 64         */
+  int32_t Hq, Hkv, D;  /* Hq % Hkv == 0; D is 64 or 128                       */
+  sv_dtype dtype;      /* element type of q, k_cache, v_cache (SV_F32/SV_BF16) */
+  const void* q;       /* [N, Hq, D], 16-byte aligned                         */
+  const void* k_cache; /* [B, Hkv, Lcap, D], 16-byte aligned                  */
+  const void* v_cache; /* [B, Hkv, Lcap, D], 16-byte aligned                  */
+  int64_t Lcap;        /* slots per (request, KV head), >= 1                  */
+  const int32_t* ctx_len;  /* [B] committed context length L_b             */
+  const int32_t* cu_nodes; /* [B+1] packing offsets                        */
+  const int32_t* parent;   /* [N] local parent (-1 = root); may be NULL if anc_mask given */
+  const uint64_t* anc_mask;/* [N] optional: bit i set iff local node i is visible to the
+                              node (itself or an ancestor); used instead of parent if non-NULL */
+  float scale;         /* softmax scale; 0 means 1/sqrt(D)                    */
+  int32_t num_splits;  /* KV-length splits; 0 = chosen by the library         */
+  float* out;          /* [N, Hq, D] fp32, 16-byte aligned                    */
+  int32_t* status;     /* optional device word for SV_STATUS_* bits           */
+  void* prof_start;    /* optional hipEvent_t recorded right before the        */
+  void* prof_stop;     /*   attention kernel / right after it (measurement)   */
+} sv_attn_args;
+
+/* ------------------------------------------------------------------------ */
+/* Lossless rejection sampling over the tree ([SD] "Mathematical Rejection
+ * Sampling Algorithm" and "Proof of Lossless Distribution Equivalence";
+ * [LOSSY] section 2.1 h(x) = min(1, p/q) and appendix F.1 residual r(x)).
+ *
+ * Rows: request b owns rows cu_nodes[b] + b + r, r = 0..T_b. Row r = 0 is the
+ * root position (distribution of the first draft token); row r = 1 + j is the
+ * position after local node j. Node j is tested against the p and q rows of
+ * its parent's position. p = softmax(target_logits / temperature); q is used
+ * exactly as given (already tempered by the caller, not renormalised).
+ *
+ * Walk (temperature > 0): at the current position, children are tried in
+ * increasing node index; child c with token x is accepted iff
+ *   P(x) > 0 and u_c * Q(x) <= P(x),   u_c = U(b, c, purpose 0),
+ * where P is the current target distribution (p, then residuals). After a
+ * rejection P <- max(0, P - Q) / sum max(0, P - Q) (kept unchanged, with
+ * SV_STATUS_ZERO_RESIDUAL, if that sum is 0) and the next sibling is tried.
+ * On acceptance the walk descends into the accepted node's row. When no child
+ * is accepted (or there is none), the bonus token is
+ *   y = min{ x : sum_{t<=x} P(t) > U(b, 0, purpose 1) * sum_t P(t) }.
+ * Temperature 0 is greedy: accept the first child whose token equals the
+ * argmax of the raw logits of the row (lowest index on ties); the bonus token
+ * is the argmax of the final row.
+ *
+ * U(b, j, purpose) = (w0 + 0.5) * 2^-32 where w0 is word 0 of Philox4x32-10
+ * (Salmon et al., SC'11) with key = (seed & 0xffffffff, seed >> 32) and
+ * counter = (request_id[b], j, purpose, step).                            */
+typedef struct {
+  int32_t B, V;        /* requests (>= 0); vocabulary size (1 .. 1<<22)      */
+  int32_t total_nodes; /* N = cu_nodes[B]                                     */
+  int32_t max_nodes;   /* upper bound on every T_b, 1..64; 0 means 64         */
+  const int32_t* cu_nodes;     /* [B+1] packing offsets                    */
+  const int32_t* parent;       /* [N] local parent (-1 = root)             */
+  const int32_t* draft_tokens; /* [N] token of each node                   */
+  const float* target_logits;  /* [N+B, V] fp32 rows as described above    */
+  const float* draft_probs;    /* [N+B, V] fp32; may be NULL if temperature == 0 */
+  float temperature;   /* 0 = greedy; > 0 = sampled                           */
+  uint64_t seed;       /* Philox key                                          */
+  uint32_t step;       /* Philox counter word 3 (replay / advance)            */
+  const uint32_t* request_id; /* [B] Philox counter word 0; NULL means b    */
+  int32_t max_depth;   /* row capacity of the outputs, >= max_nodes (0 -> 64) */
+  int32_t* accept_len;      /* [B] accepted draft nodes (0..T_b); 0 for a skipped request */
+  int32_t* accepted_nodes;  /* [B, max_depth] local ids along the accepted path, -1 padded */
+  int32_t* out_tokens;      /* [B, max_depth+1] accepted tokens then the bonus token, -1 padded;
+                               all -1 for a request skipped because of a data error */
+  float* probs_out;         /* optional [N+B, V] fp32 p rows (temperature > 0 only) */
+  double* uniforms_out;     /* optional [N+B]: [n] = U(b, j, 0) for packed node n = cu_nodes[b]+j,
+                               [N+b] = U(b, 0, 1)                                   */
+  int32_t* residual_passes; /* optional [B]: vocabulary passes the walk made for residual masses */
+  int32_t* status;          /* optional device word for SV_STATUS_* bits           */
+  void* prof_start;         /* optional hipEvent_t recorded right before the row-statistics */
+  void* prof_stop;          /*   kernel / right after it (measurement)                     */
+} sv_sample_args;
+
+/* Bytes of workspace the calls need for these arguments (either pointer may be
+ * NULL). Depends only on host-visible fields. Returns 0 on invalid arguments
+ * (and sets the last error) or when no scratch is needed.                  */
+size_t spec_verify_workspace_size(const sv_attn_args* attn, const sv_sample_args* sample);
+
+/* Tree-masked GQA attention. ws: 256-byte aligned device buffer of at least
+ * spec_verify_workspace_size(attn, NULL) bytes (may be NULL if that is 0).  */
+sv_status spec_verify_attn(const sv_attn_args* attn, void* ws, size_t ws_bytes, void* stream);
+
+/* Rejection-sampling walk. ws as above with spec_verify_workspace_size(NULL, sample). */
+sv_status spec_verify_sample(const sv_sample_args* sample, void* ws, size_t ws_bytes, void* stream);
+
+/* Attention then sampling on one stream; the two argument sets must describe
+ * the same batch (B, total_nodes, cu_nodes). ws: spec_verify_workspace_size(attn, sample). */
+sv_status spec_verify_step(const sv_attn_args* attn, const sv_sample_args* sample,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/* Message of the last failed call on this thread ("" if none).             */
+const char* spec_verify_last_error(void);
+
+/* sizeof(sv_attn_args) for which == 0, sizeof(sv_sample_args) for which == 1,
+ * 0 otherwise: lets bindings check their struct layout against this one.   */
+size_t spec_verify_struct_size(int32_t which);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

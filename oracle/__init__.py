@@ -1,0 +1,234 @@
+"""fp64 CPU oracle of the speculative-decoding verification step.
+
+TEST INFRASTRUCTURE ONLY. The tests, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` use it to check and time the GPU library;
+the library itself never imports, links or runs anything from here, and the
+oracle shares no code with it (the two only consume the same input bytes).
+
+The arithmetic lives in ``oracle.c`` (plain C loops in fp64, built with the
+host compiler into ``liboracle.so``); this module marshals numpy arrays.
+
+Functions and the passages they follow:
+  philox4x32_10, uniform   Philox4x32-10 (Salmon et al., SC'11); the uniform
+                           r_i of [SD] "Mathematical Rejection Sampling Algorithm".
+  ancestors                [SD] "Tree Attention Mask Mechanics".
+  attention                [SD] "Tree Attention Mask Mechanics" and
+                           "Interaction with Advanced Attention Architectures".
+  target_probs, argmax     softmax(logits / T); greedy argmax.
+  residual                 [SD] R_i(x); [LOSSY] appendix F.1 r(x).
+  inverse_cdf              the draw from R_i / p.
+  verify                   the whole walk ([SD] acceptance rule; [LOSSY] 2.1 h(x)).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+ACCEPT_TOL = 1e-5  # |u - P/Q| below this marks an accept test as a near-tie
+CDF_TOL = 1e-6     # a CDF boundary this close to u marks the final draw as a near-tie
+
+
+def build(verbose: bool = False) -> str:
+    """Compile oracle.c into liboracle.so with the host C compiler."""
+    from .build_oracle import build_oracle
+
+    return build_oracle(verbose=verbose)
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    i32, i64, u32, u64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_double
+    lib.orc_philox4x32_10.argtypes = [P, P, P]
+    lib.orc_philox4x32_10.restype = None
+    lib.orc_uniform.argtypes = [u64, u32, u32, u32, u32]
+    lib.orc_uniform.restype = f64
+    lib.orc_ancestors.argtypes = [i32, P, P, P]
+    lib.orc_ancestors.restype = i32
+    lib.orc_attention.argtypes = [i32, i32, i32, i32, i32, P, P, P, i64, P, P, P, f64, i64, P, P, i32]
+    lib.orc_attention.restype = i32
+    lib.orc_target_probs.argtypes = [i32, P, f64, P]
+    lib.orc_target_probs.restype = i32
+    lib.orc_argmax.argtypes = [i32, P]
+    lib.orc_argmax.restype = i32
+    lib.orc_residual.argtypes = [i32, P, P, P]
+    lib.orc_residual.restype = f64
+    lib.orc_inverse_cdf.argtypes = [i32, P, f64, P]
+    lib.orc_inverse_cdf.restype = i32
+    lib.orc_verify.argtypes = [i32, i32, P, P, P, P, P, f64, u64, u32, P, i32, P, P, P, P, P, P, P, P, P, P,
+                               f64, f64, i32]
+    lib.orc_verify.restype = i32
+    lib.orc_target_rows.argtypes = [i32, P, f64, i64, P, P]
+    lib.orc_target_rows.restype = i32
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray | None):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle inputs must be C-contiguous"
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:
+        return max(1, os.cpu_count() or 1)
+
+
+def philox4x32_10(counter, key) -> np.ndarray:
+    ctr = np.ascontiguousarray(counter, dtype=np.uint32)
+    k = np.ascontiguousarray(key, dtype=np.uint32)
+    out = np.zeros(4, dtype=np.uint32)
+    _load().orc_philox4x32_10(_ptr(ctr), _ptr(k), _ptr(out))
+    return out
+
+
+def uniform(seed: int, request_id: int, j: int, purpose: int, step: int) -> float:
+    return float(_load().orc_uniform(seed, request_id, j, purpose, step))
+
+
+def ancestors(parent) -> tuple[np.ndarray, np.ndarray]:
+    """(anc bitmasks uint64 [T], depth int32 [T]); raises ValueError on a bad tree."""
+    par = np.ascontiguousarray(parent, dtype=np.int32)
+    T = par.shape[0]
+    anc = np.zeros(max(T, 1), dtype=np.uint64)
+    depth = np.zeros(max(T, 1), dtype=np.int32)
+    rc = _load().orc_ancestors(T, _ptr(par), _ptr(anc), _ptr(depth))
+    if rc != 0:
+        raise ValueError(f"invalid tree (code {rc})")
+    return anc[:T], depth[:T]
+
+
+def attention(q, k, v, ctx_len, cu_nodes, parent, *, Hq, Hkv, scale=None, dtype="f32", items=None,
+              nthreads=None) -> np.ndarray:
+    """fp64 tree-masked GQA attention.
+
+    q [N,Hq,D], k/v [B,Hkv,Lcap,D] as float32 arrays (dtype='f32') or as uint16
+    bf16 bit patterns (dtype='bf16'). items: optional int64 [n,2] of
+    (packed node, q head); returns [n, D] then, else [N, Hq, D].
+    """
+    q = np.ascontiguousarray(q)
+    k = np.ascontiguousarray(k)
+    v = np.ascontiguousarray(v)
+    code = {"f32": 0, "bf16": 1}[dtype]
+    if code == 0:
+        assert q.dtype == np.float32 and k.dtype == np.float32 and v.dtype == np.float32
+    else:
+        assert q.dtype == np.uint16 and k.dtype == np.uint16 and v.dtype == np.uint16
+    B = int(k.shape[0])
+    Lcap, D = int(k.shape[2]), int(k.shape[3])
+    N = int(q.shape[0])
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    ctx = np.ascontiguousarray(ctx_len, dtype=np.int32)
+    cu = np.ascontiguousarray(cu_nodes, dtype=np.int32)
+    par = np.ascontiguousarray(parent, dtype=np.int32)
+    if items is None:
+        n_items = N * Hq
+        out = np.zeros((N, Hq, D), dtype=np.float64)
+        it_ptr = None
+    else:
+        items = np.ascontiguousarray(items, dtype=np.int64).reshape(-1, 2)
+        n_items = items.shape[0]
+        out = np.zeros((n_items, D), dtype=np.float64)
+        it_ptr = _ptr(items)
+    rc = _load().orc_attention(B, Hq, Hkv, D, code, _ptr(q), _ptr(k), _ptr(v), Lcap, _ptr(ctx), _ptr(cu),
+                               _ptr(par), float(scale), n_items, it_ptr, _ptr(out),
+                               nthreads or _default_threads())
+    if rc != 0:
+        raise ValueError("oracle attention: bad packing or tree")
+    return out
+
+
+def target_probs(logits, temperature: float) -> np.ndarray:
+    row = np.ascontiguousarray(logits, dtype=np.float32)
+    p = np.zeros(row.shape[0], dtype=np.float64)
+    if _load().orc_target_probs(row.shape[0], _ptr(row), float(temperature), _ptr(p)):
+        raise ValueError("non-finite or all -inf logits")
+    return p
+
+
+def target_rows(logits2d, temperature: float, rows) -> np.ndarray:
+    lg = np.ascontiguousarray(logits2d, dtype=np.float32)
+    r = np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.zeros((r.shape[0], lg.shape[1]), dtype=np.float64)
+    if _load().orc_target_rows(lg.shape[1], _ptr(lg), float(temperature), r.shape[0], _ptr(r), _ptr(out)):
+        raise ValueError("non-finite or all -inf logits")
+    return out
+
+
+def argmax(logits) -> int:
+    row = np.ascontiguousarray(logits, dtype=np.float32)
+    return int(_load().orc_argmax(row.shape[0], _ptr(row)))
+
+
+def residual(P, Q) -> tuple[np.ndarray, float]:
+    P = np.ascontiguousarray(P, dtype=np.float64)
+    Q = np.ascontiguousarray(Q, dtype=np.float64)
+    out = np.zeros_like(P)
+    R = _load().orc_residual(P.shape[0], _ptr(P), _ptr(Q), _ptr(out))
+    return out, float(R)
+
+
+def inverse_cdf(P, u: float) -> tuple[int, float]:
+    P = np.ascontiguousarray(P, dtype=np.float64)
+    m = np.zeros(1, dtype=np.float64)
+    y = _load().orc_inverse_cdf(P.shape[0], _ptr(P), float(u), _ptr(m))
+    return int(y), float(m[0])
+
+
+def verify(cu_nodes, parent, tokens, logits, q, *, temperature, seed, step=0, request_id=None,
+           max_depth=None, accept_tol=ACCEPT_TOL, cdf_tol=CDF_TOL, nthreads=None) -> dict:
+    """The verification walk for a packed batch; returns a dict of numpy arrays.
+
+    logits, q: float32 [N+B, V] (q may be None when temperature == 0).
+    """
+    cu = np.ascontiguousarray(cu_nodes, dtype=np.int32)
+    B = cu.shape[0] - 1
+    N = int(cu[-1]) if B >= 0 else 0
+    par = np.ascontiguousarray(parent, dtype=np.int32)
+    tok = np.ascontiguousarray(tokens, dtype=np.int32)
+    lg = np.ascontiguousarray(logits, dtype=np.float32)
+    V = int(lg.shape[1])
+    qq = None if q is None else np.ascontiguousarray(q, dtype=np.float32)
+    if temperature > 0:
+        assert qq is not None and qq.shape == lg.shape
+    rid = None if request_id is None else np.ascontiguousarray(request_id, dtype=np.uint32)
+    if max_depth is None:
+        Ts = np.diff(cu)
+        max_depth = int(Ts.max()) if B > 0 else 0
+    out = {
+        "accept_len": np.zeros(B, np.int32),
+        "accepted_nodes": np.zeros((B, max(max_depth, 0)), np.int32),
+        "out_tokens": np.zeros((B, max_depth + 1), np.int32),
+        "uniforms": np.zeros(N + B, np.float64),
+        "flag_depth": np.zeros(B, np.int32),
+        "flag_kind": np.zeros(B, np.int32),
+        "n_rejections": np.zeros(B, np.int32),
+        "status": np.zeros(B, np.int32),
+        "min_accept_margin": np.zeros(B, np.float64),
+        "cdf_margin": np.zeros(B, np.float64),
+    }
+    rc = _load().orc_verify(B, V, _ptr(cu), _ptr(par), _ptr(tok), _ptr(lg), _ptr(qq), float(temperature),
+                            int(seed), int(step), _ptr(rid), int(max_depth), _ptr(out["accept_len"]),
+                            _ptr(out["accepted_nodes"]), _ptr(out["out_tokens"]), _ptr(out["uniforms"]),
+                            _ptr(out["flag_depth"]), _ptr(out["flag_kind"]), _ptr(out["n_rejections"]),
+                            _ptr(out["status"]), _ptr(out["min_accept_margin"]), _ptr(out["cdf_margin"]),
+                            float(accept_tol), float(cdf_tol), nthreads or _default_threads())
+    if rc != 0:
+        raise ValueError("oracle verify: bad arguments")
+    return out

@@ -1,0 +1,479 @@
+/*
+ * oracle.c -- plain fp64 CPU oracle of the speculative-decoding verification
+ * step. TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the bench's
+ * CPU-baseline leg call it to check and time the GPU library; the library
+ * never calls it and shares no code with it.
+ *
+ * Every function follows the definition on the source pages step by step, in
+ * fp64, with plain loops and no blocking, fusion or reordering:
+ *   [SD]    "Speculative Decoding: Accelerating Inference Speeds in
+ *           Distributed LLMs" (shyankdev.com blog)
+ *   [LOSSY] "Revisiting Lossy Verification in Speculative Decoding:
+ *           Mechanisms, Trade-offs, and Failure Modes"
+ *   [ECHO]  "ECHO: Elastic Speculative Decoding with Sparse Gating for
+ *           High-Concurrency Scenarios"
+ * plus Philox4x32-10 from Salmon, Moraes, Dror, Shaw, "Parallel Random
+ * Numbers: As Easy as 1, 2, 3" (SC'11).
+ *
+ * Readings of points the pages leave open are stated where they are used.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* Philox4x32-10 (Salmon et al., SC'11, section on the Philox family):
+ * ten rounds of the 4x32 Philox S-box; each round multiplies words 0 and 2
+ * by the two Philox multipliers, and the key is bumped by the two Weyl
+ * constants between rounds.                                                */
+#define ORC_PHILOX_M0 0xD2511F53u
+#define ORC_PHILOX_M1 0xCD9E8D57u
+#define ORC_PHILOX_W0 0x9E3779B9u
+#define ORC_PHILOX_W1 0xBB67AE85u
+
+void orc_philox4x32_10(const uint32_t ctr_in[4], const uint32_t key_in[2], uint32_t out[4]) {
+  uint32_t c0 = ctr_in[0], c1 = ctr_in[1], c2 = ctr_in[2], c3 = ctr_in[3];
+  uint32_t k0 = key_in[0], k1 = key_in[1];
+  for (int round = 0; round < 10; ++round) {
+    if (round > 0) {
+      k0 += ORC_PHILOX_W0;
+      k1 += ORC_PHILOX_W1;
+    }
+    uint64_t prod0 = (uint64_t)ORC_PHILOX_M0 * (uint64_t)c0;
+    uint64_t prod1 = (uint64_t)ORC_PHILOX_M1 * (uint64_t)c2;
+    uint32_t hi0 = (uint32_t)(prod0 >> 32), lo0 = (uint32_t)prod0;
+    uint32_t hi1 = (uint32_t)(prod1 >> 32), lo1 = (uint32_t)prod1;
+    uint32_t n0 = hi1 ^ c1 ^ k0;
+    uint32_t n1 = lo1;
+    uint32_t n2 = hi0 ^ c3 ^ k1;
+    uint32_t n3 = lo0;
+    c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+  }
+  out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* The uniform variate r_i of [SD] "Mathematical Rejection Sampling
+ * Algorithm": word 0 of Philox at counter (request id, node, purpose, step)
+ * mapped into the open interval (0, 1) as (w0 + 1/2) / 2^32 (exact in fp64). */
+double orc_uniform(uint64_t seed, uint32_t request_id, uint32_t j, uint32_t purpose, uint32_t step) {
+  uint32_t ctr[4] = {request_id, j, purpose, step};
+  uint32_t key[2] = {(uint32_t)(seed & 0xffffffffu), (uint32_t)(seed >> 32)};
+  uint32_t w[4];
+  orc_philox4x32_10(ctr, key, w);
+  return ((double)w[0] + 0.5) * (1.0 / 4294967296.0);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Tree ([SD] "Tree Attention Mask Mechanics"): node j sees itself and every
+ * ancestor, never a node of another branch. Ancestors are found by walking
+ * parent pointers. Returns 0, or 1 + the first node whose parent is not in
+ * [-1, j-1] (then anc/depth of later nodes are left unset).               */
+int orc_ancestors(int T, const int32_t* parent, uint64_t* anc, int32_t* depth) {
+  if (T < 0 || T > 64) return -1;
+  for (int j = 0; j < T; ++j) {
+    if (parent[j] < -1 || parent[j] >= j) return j + 1;
+    uint64_t mask = 0;
+    int d = 0;
+    for (int x = j; x >= 0; x = parent[x]) {
+      mask |= (uint64_t)1 << x;
+      ++d;
+    }
+    anc[j] = mask;
+    depth[j] = d; /* a child of the root has depth 1 */
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Work splitting for the slow loops: a plain parallel-for over an index
+ * range with one contiguous slice per thread.                              */
+typedef struct {
+  void (*fn)(void* ctx, int64_t i);
+  void* ctx;
+  int64_t begin, end;
+} orc_slice;
+
+static void* orc_slice_run(void* arg) {
+  orc_slice* s = (orc_slice*)arg;
+  for (int64_t i = s->begin; i < s->end; ++i) s->fn(s->ctx, i);
+  return NULL;
+}
+
+static void orc_parallel_for(int64_t n, int nthreads, void (*fn)(void*, int64_t), void* ctx) {
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > 256) nthreads = 256;
+  if ((int64_t)nthreads > n) nthreads = (int)(n > 0 ? n : 1);
+  if (nthreads == 1) {
+    for (int64_t i = 0; i < n; ++i) fn(ctx, i);
+    return;
+  }
+  pthread_t tids[256];
+  orc_slice slices[256];
+  int started[256];
+  for (int t = 0; t < nthreads; ++t) {
+    slices[t].fn = fn;
+    slices[t].ctx = ctx;
+    slices[t].begin = n * t / nthreads;
+    slices[t].end = n * (t + 1) / nthreads;
+    started[t] = pthread_create(&tids[t], NULL, orc_slice_run, &slices[t]) == 0;
+    if (!started[t]) orc_slice_run(&slices[t]);
+  }
+  for (int t = 0; t < nthreads; ++t)
+    if (started[t]) pthread_join(tids[t], NULL);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Element access: fp32 as is, bf16 by placing its 16 bits on top of an fp32
+ * (exact), both widened exactly to fp64.                                   */
+static double orc_load(const void* base, int dtype, int64_t idx) {
+  if (dtype == 0) return (double)((const float*)base)[idx];
+  uint32_t bits = (uint32_t)((const uint16_t*)base)[idx] << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+typedef struct {
+  int B, Hq, Hkv, D, dtype;
+  const void *q, *k, *v;
+  int64_t Lcap;
+  const int32_t *ctx_len, *cu_nodes, *parent;
+  double scale;
+  const int64_t* items; /* pairs (packed node, q head) */
+  double* out;
+  int* err;
+} orc_attn_ctx;
+
+/* [SD] "Tree Attention Mask Mechanics" + "Interaction with Advanced
+ * Attention Architectures (GQA & MLA)": one output vector of one query head
+ * of one draft node. The query head h reads KV head h / (Hq / Hkv). Keys:
+ * every committed context slot, then the draft slots of the node's own
+ * ancestors and of itself. Softmax in fp64 with the maximum subtracted.    */
+static void orc_attn_item(void* vctx, int64_t it) {
+  orc_attn_ctx* c = (orc_attn_ctx*)vctx;
+  int64_t n = c->items[2 * it], h = c->items[2 * it + 1];
+  double* o = c->out + it * c->D;
+  /* request owning packed node n: cu_nodes[b] <= n < cu_nodes[b+1] */
+  int b = -1;
+  for (int r = 0; r < c->B; ++r)
+    if (c->cu_nodes[r] <= n && n < c->cu_nodes[r + 1]) { b = r; break; }
+  if (b < 0) { *c->err = 1; return; }
+  int j = (int)(n - c->cu_nodes[b]);
+  int T = c->cu_nodes[b + 1] - c->cu_nodes[b];
+  const int32_t* par = c->parent + c->cu_nodes[b];
+  int64_t L = c->ctx_len[b];
+  if (T > 64 || L < 0 || L + T > c->Lcap) { *c->err = 1; return; }
+  /* visible draft nodes: j and its ancestors */
+  int visible[64];
+  int nvis = 0;
+  for (int x = j; x >= 0; x = par[x]) {
+    if (par[x] < -1 || par[x] >= x) { *c->err = 1; return; }
+    visible[nvis++] = x;
+  }
+  int G = c->Hq / c->Hkv;
+  int64_t g = h / G;
+  int64_t nkeys = L + nvis;
+  double* s = (double*)malloc(sizeof(double) * (size_t)nkeys);
+  int64_t* slot = (int64_t*)malloc(sizeof(int64_t) * (size_t)nkeys);
+  if (!s || !slot) { free(s); free(slot); *c->err = 1; return; }
+  for (int64_t t = 0; t < L; ++t) slot[t] = t;
+  for (int i = 0; i < nvis; ++i) slot[L + i] = L + visible[i];
+  int64_t qbase = (n * c->Hq + h) * c->D;
+  int64_t kvbase = ((int64_t)b * c->Hkv + g) * c->Lcap * c->D;
+  double m = -INFINITY;
+  for (int64_t t = 0; t < nkeys; ++t) {
+    double acc = 0.0;
+    for (int d = 0; d < c->D; ++d)
+      acc += orc_load(c->q, c->dtype, qbase + d) * orc_load(c->k, c->dtype, kvbase + slot[t] * c->D + d);
+    s[t] = c->scale * acc;
+    if (s[t] > m) m = s[t];
+  }
+  double denom = 0.0;
+  for (int64_t t = 0; t < nkeys; ++t) {
+    s[t] = exp(s[t] - m);
+    denom += s[t];
+  }
+  for (int d = 0; d < c->D; ++d) o[d] = 0.0;
+  for (int64_t t = 0; t < nkeys; ++t) {
+    double w = s[t] / denom;
+    for (int d = 0; d < c->D; ++d) o[d] += w * orc_load(c->v, c->dtype, kvbase + slot[t] * c->D + d);
+  }
+  free(s);
+  free(slot);
+}
+
+/* Attention for a list of (packed node, query head) pairs `items` [n_items,2]
+ * (or, if items is NULL, for every node and head in order); out [n_items, D].
+ * dtype 0 = fp32 inputs, 1 = bf16 inputs. Returns 0, or 1 on bad packing. */
+int orc_attention(int B, int Hq, int Hkv, int D, int dtype, const void* q, const void* k, const void* v,
+                  int64_t Lcap, const int32_t* ctx_len, const int32_t* cu_nodes, const int32_t* parent,
+                  double scale, int64_t n_items, const int64_t* items, double* out, int nthreads) {
+  if (Hkv <= 0 || Hq % Hkv != 0 || D <= 0) return 1;
+  int64_t* all = NULL;
+  if (!items) {
+    int64_t N = cu_nodes[B];
+    n_items = N * Hq;
+    all = (int64_t*)malloc(sizeof(int64_t) * 2 * (size_t)(n_items > 0 ? n_items : 1));
+    if (!all) return 1;
+    for (int64_t n = 0; n < N; ++n)
+      for (int h = 0; h < Hq; ++h) {
+        all[2 * (n * Hq + h)] = n;
+        all[2 * (n * Hq + h) + 1] = h;
+      }
+    items = all;
+  }
+  int err = 0;
+  orc_attn_ctx c = {B, Hq, Hkv, D, dtype, q, k, v, Lcap, ctx_len, cu_nodes, parent, scale, items, out, &err};
+  orc_parallel_for(n_items, nthreads, orc_attn_item, &c);
+  free(all);
+  return err;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Target distribution with temperature T > 0: p = softmax(logits / T), in
+ * fp64 with the maximum subtracted. Returns 0, or 1 if a logit is NaN/+inf or
+ * every logit is -inf.                                                     */
+int orc_target_probs(int V, const float* logits, double T, double* p) {
+  double m = -INFINITY;
+  for (int x = 0; x < V; ++x) {
+    double l = (double)logits[x];
+    if (isnan(l) || l == INFINITY) return 1;
+    double z = l / T;
+    if (z > m) m = z;
+  }
+  if (m == -INFINITY) return 1;
+  double S = 0.0;
+  for (int x = 0; x < V; ++x) {
+    p[x] = exp((double)logits[x] / T - m);
+    S += p[x];
+  }
+  for (int x = 0; x < V; ++x) p[x] /= S;
+  return 0;
+}
+
+/* Greedy target token: argmax of the raw logits, lowest index on ties.    */
+int orc_argmax(int V, const float* logits) {
+  int best = 0;
+  for (int x = 1; x < V; ++x)
+    if (logits[x] > logits[best]) best = x;
+  return best;
+}
+
+/* Residual after a rejection ([SD] R_i(x); [LOSSY] F.1 r(x)):
+ * out = max(0, P - Q) / sum max(0, P - Q). Returns the mass sum; if it is 0
+ * the distribution cannot be renormalised and out = P (kept unchanged).   */
+double orc_residual(int V, const double* P, const double* Q, double* out) {
+  double R = 0.0;
+  for (int x = 0; x < V; ++x) {
+    double d = P[x] - Q[x];
+    if (d > 0.0) R += d;
+  }
+  for (int x = 0; x < V; ++x) {
+    if (R > 0.0) {
+      double d = P[x] - Q[x];
+      out[x] = d > 0.0 ? d / R : 0.0;
+    } else {
+      out[x] = P[x];
+    }
+  }
+  return R;
+}
+
+/* Inverse-CDF draw from an (unnormalised) non-negative vector P:
+ * y = min{ x : sum_{t<=x} P(t) > u * sum_t P(t) } in vocabulary order; the
+ * strict '>' means a zero-mass token is never drawn. *margin (optional) is
+ * the distance from u to the normalised CDF values on both sides of y.
+ * Returns -1 if P has no mass.                                            */
+int orc_inverse_cdf(int V, const double* P, double u, double* margin) {
+  double total = 0.0;
+  for (int x = 0; x < V; ++x) total += P[x];
+  if (!(total > 0.0)) {
+    if (margin) *margin = 0.0;
+    return -1;
+  }
+  double target = u * total;
+  double run = 0.0;
+  for (int x = 0; x < V; ++x) {
+    double before = run;
+    run += P[x];
+    if (run > target) {
+      if (margin) {
+        double lo = u - before / total, hi = run / total - u;
+        *margin = lo < hi ? lo : hi;
+      }
+      return x;
+    }
+  }
+  /* only reachable through rounding when u*total lands on the last step */
+  for (int x = V - 1; x >= 0; --x)
+    if (P[x] > 0.0) {
+      if (margin) *margin = 0.0;
+      return x;
+    }
+  return -1;
+}
+
+/* ------------------------------------------------------------------------ */
+/* The verification walk of one request. */
+typedef struct {
+  int B, V;
+  const int32_t *cu_nodes, *parent, *tokens;
+  const float *logits, *q;
+  double T;
+  uint64_t seed;
+  uint32_t step;
+  const uint32_t* request_id;
+  int max_depth;
+  int32_t *accept_len, *accepted_nodes, *out_tokens;
+  double* uniforms_out;
+  int32_t *flag_depth, *flag_kind, *n_rejections, *status;
+  double *min_accept_margin, *cdf_margin;
+  double accept_tol, cdf_tol;
+} orc_walk_ctx;
+
+static void orc_walk_one(void* vctx, int64_t bi) {
+  orc_walk_ctx* c = (orc_walk_ctx*)vctx;
+  int b = (int)bi, V = c->V;
+  int64_t N = c->cu_nodes[c->B];
+  int32_t* acc_nodes = c->accepted_nodes + (int64_t)b * c->max_depth;
+  int32_t* toks_out = c->out_tokens + (int64_t)b * (c->max_depth + 1);
+  for (int i = 0; i < c->max_depth; ++i) acc_nodes[i] = -1;
+  for (int i = 0; i <= c->max_depth; ++i) toks_out[i] = -1;
+  c->accept_len[b] = 0;
+  c->flag_depth[b] = -1;
+  c->flag_kind[b] = -1;
+  c->n_rejections[b] = 0;
+  c->status[b] = 0;
+  c->min_accept_margin[b] = INFINITY;
+  c->cdf_margin[b] = INFINITY;
+
+  int64_t n0 = c->cu_nodes[b];
+  int T = c->cu_nodes[b + 1] - c->cu_nodes[b];
+  uint32_t rid = c->request_id ? c->request_id[b] : (uint32_t)b;
+  if (c->uniforms_out) {
+    for (int j = 0; j < T && j < 64; ++j) c->uniforms_out[n0 + j] = orc_uniform(c->seed, rid, (uint32_t)j, 0, c->step);
+    c->uniforms_out[N + b] = orc_uniform(c->seed, rid, 0, 1, c->step);
+  }
+  /* validate packing, tree and tokens */
+  if (T < 0 || T > 64 || T > c->max_depth) { c->status[b] |= 0x02; return; }
+  const int32_t* par = c->parent + n0;
+  const int32_t* tok = c->tokens + n0;
+  for (int j = 0; j < T; ++j) {
+    if (par[j] < -1 || par[j] >= j) { c->status[b] |= 0x01; return; }
+    if (tok[j] < 0 || tok[j] >= V) { c->status[b] |= 0x04; return; }
+  }
+  int64_t row0 = n0 + b; /* row of the root position; node j's row is row0 + 1 + j */
+
+  if (c->T == 0.0) {
+    /* Greedy verification: accept the first child equal to the target's
+     * argmax; the bonus token is the argmax at the final position.        */
+    int pos = -1, d = 0;
+    for (;;) {
+      const float* lrow = c->logits + (row0 + pos + 1) * (int64_t)V;
+      int a = orc_argmax(V, lrow);
+      int next = -1;
+      for (int ch = pos + 1; ch < T; ++ch)
+        if (par[ch] == pos && tok[ch] == a) { next = ch; break; }
+      if (next < 0) {
+        toks_out[d] = a;
+        break;
+      }
+      acc_nodes[d] = next;
+      toks_out[d] = tok[next];
+      ++d;
+      pos = next;
+    }
+    c->accept_len[b] = d;
+    return;
+  }
+
+  double* P = (double*)malloc(sizeof(double) * (size_t)V);
+  double* Q = (double*)malloc(sizeof(double) * (size_t)V);
+  double* tmp = (double*)malloc(sizeof(double) * (size_t)V);
+  if (!P || !Q || !tmp) { free(P); free(Q); free(tmp); c->status[b] |= 0x80; return; }
+
+  int pos = -1, d = 0;
+  for (;;) {
+    int64_t row = row0 + pos + 1;
+    /* target distribution at this position, and the draft distribution it
+     * is checked against ([SD]: node j is checked against p_i and q_i of the
+     * position it was drafted at, i.e. its parent's row)                  */
+    if (orc_target_probs(V, c->logits + row * (int64_t)V, c->T, P)) { c->status[b] |= 0x08; break; }
+    for (int x = 0; x < V; ++x) Q[x] = (double)c->q[row * (int64_t)V + x];
+    int accepted = -1;
+    for (int ch = pos + 1; ch < T; ++ch) {
+      if (par[ch] != pos) continue; /* children in increasing node index */
+      double u = orc_uniform(c->seed, rid, (uint32_t)ch, 0, c->step);
+      int x = tok[ch];
+      /* [SD] acceptance rule r <= min(1, p/q), written as u*q <= p with p > 0
+       * so that q(x) = 0 follows the formula (ratio +inf, accepted).      */
+      int ok = P[x] > 0.0 && u * Q[x] <= P[x];
+      double ratio = Q[x] > 0.0 ? P[x] / Q[x] : (P[x] > 0.0 ? INFINITY : 0.0);
+      double margin = fabs(u - ratio);
+      if (margin < c->min_accept_margin[b]) c->min_accept_margin[b] = margin;
+      if (margin < c->accept_tol && c->flag_depth[b] < 0) { c->flag_depth[b] = d; c->flag_kind[b] = 0; }
+      if (ok) { accepted = ch; break; }
+      /* rejected: the next sibling (a fresh draw from the same q) is tested
+       * against the renormalised residual of the current distribution      */
+      c->n_rejections[b] += 1;
+      double R = orc_residual(V, P, Q, tmp);
+      if (!(R > 0.0)) c->status[b] |= 0x10;
+      memcpy(P, tmp, sizeof(double) * (size_t)V);
+    }
+    if (accepted >= 0) {
+      acc_nodes[d] = accepted;
+      toks_out[d] = tok[accepted];
+      ++d;
+      pos = accepted;
+      continue;
+    }
+    /* no child accepted (or none to try): one token from the current
+     * distribution -- the residual after rejections, p at a leaf         */
+    double u = orc_uniform(c->seed, rid, 0, 1, c->step);
+    double margin = 0.0;
+    int y = orc_inverse_cdf(V, P, u, &margin);
+    c->cdf_margin[b] = margin;
+    if (margin < c->cdf_tol && c->flag_depth[b] < 0) { c->flag_depth[b] = d; c->flag_kind[b] = 1; }
+    toks_out[d] = y;
+    break;
+  }
+  c->accept_len[b] = d;
+  free(P);
+  free(Q);
+  free(tmp);
+}
+
+/* Verification of a packed batch (see the calling convention of the GPU
+ * library: rows cu_nodes[b] + b + r, r = 0 root, r = 1 + j after node j).
+ * T == 0 selects greedy verification. Per request it also reports
+ *   flag_depth: accepted nodes before the first decision closer than the
+ *               tolerance to its threshold (-1: none), flag_kind 0 = accept
+ *               test, 1 = final inverse-CDF draw;
+ *   n_rejections: rejections (= residual renormalisations);
+ *   status: SV_STATUS-like bits (0x01 tree, 0x02 packing, 0x04 token,
+ *           0x08 non-finite row, 0x10 zero residual, 0x80 out of memory);
+ *   min_accept_margin, cdf_margin: the smallest |u - P/Q| seen and the
+ *           margin of the final draw.                                     */
+int orc_verify(int B, int V, const int32_t* cu_nodes, const int32_t* parent, const int32_t* tokens,
+               const float* logits, const float* q, double T, uint64_t seed, uint32_t step,
+               const uint32_t* request_id, int max_depth, int32_t* accept_len, int32_t* accepted_nodes,
+               int32_t* out_tokens, double* uniforms_out, int32_t* flag_depth, int32_t* flag_kind,
+               int32_t* n_rejections, int32_t* status, double* min_accept_margin, double* cdf_margin,
+               double accept_tol, double cdf_tol, int nthreads) {
+  if (B < 0 || V < 1 || max_depth < 0 || T < 0.0) return 1;
+  orc_walk_ctx c = {B, V, cu_nodes, parent, tokens, logits, q, T, seed, step, request_id, max_depth,
+                    accept_len, accepted_nodes, out_tokens, uniforms_out, flag_depth, flag_kind,
+                    n_rejections, status, min_accept_margin, cdf_margin, accept_tol, cdf_tol};
+  orc_parallel_for(B, nthreads, orc_walk_one, &c);
+  return 0;
+}
+
+/* p rows for a list of row indices (probability parity checks). */
+int orc_target_rows(int V, const float* logits, double T, int64_t n_rows, const int64_t* rows, double* out) {
+  int bad = 0;
+  for (int64_t i = 0; i < n_rows; ++i)
+    bad |= orc_target_probs(V, logits + rows[i] * (int64_t)V, T, out + i * (int64_t)V);
+  return bad;
+}
