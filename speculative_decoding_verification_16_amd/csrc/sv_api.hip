@@ -1,0 +1,311 @@
+// sv_api.hip -- host side of the C ABI declared in include/spec_verify.h:
+// argument validation, launch planning, workspace layout and dispatch.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "spec_verify.h"
+#include "sv_device.h"
+#include "sv_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+sv_status fail(sv_status code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int eff_max_nodes(int32_t m) { return m == 0 ? sv::kMaxNodes : m; }
+
+// ---- attention -------------------------------------------------------------
+sv_status check_attn(const sv_attn_args* a) {
+  if (!a) return fail(SV_ERR_INVALID_ARG, "attn args is NULL");
+  if (a->B < 0) return fail(SV_ERR_INVALID_ARG, "B < 0");
+  if (a->total_nodes < 0) return fail(SV_ERR_INVALID_ARG, "total_nodes < 0");
+  if (a->max_nodes < 0 || a->max_nodes > sv::kMaxNodes)
+    return fail(SV_ERR_UNSUPPORTED, "max_nodes must be in [0, 64] (one 64-bit ancestor mask per node)");
+  if (a->Hq <= 0 || a->Hkv <= 0 || a->Hq % a->Hkv != 0)
+    return fail(SV_ERR_INVALID_ARG, "need Hq > 0, Hkv > 0 and Hq %% Hkv == 0");
+  if (a->D != 64 && a->D != 128) return fail(SV_ERR_UNSUPPORTED, "head dim D must be 64 or 128");
+  if (a->dtype != SV_F32 && a->dtype != SV_BF16) return fail(SV_ERR_INVALID_ARG, "dtype must be SV_F32 or SV_BF16");
+  if (a->Lcap < 1 || a->Lcap > (1ll << 24)) return fail(SV_ERR_INVALID_ARG, "Lcap must be in [1, 2^24]");
+  if (!(a->scale >= 0.f) || isinf(a->scale)) return fail(SV_ERR_INVALID_ARG, "scale must be finite and >= 0");
+  if (a->num_splits < 0) return fail(SV_ERR_INVALID_ARG, "num_splits < 0");
+  if ((int64_t)a->total_nodes * a->Hq * a->D >= (1ll << 31))
+    return fail(SV_ERR_UNSUPPORTED, "N * Hq * D must stay below 2^31");
+  const int64_t kv_head_bytes = a->Lcap * a->D * (a->dtype == SV_BF16 ? 2 : 4);
+  if (kv_head_bytes >= (1ll << 31)) return fail(SV_ERR_UNSUPPORTED, "Lcap * D * element size must stay below 2^31");
+  if (a->B == 0) return SV_OK;
+  if (!a->ctx_len || !a->cu_nodes) return fail(SV_ERR_INVALID_ARG, "ctx_len and cu_nodes are required");
+  if (a->total_nodes == 0) return SV_OK;
+  if (!a->q || !a->k_cache || !a->v_cache || !a->out)
+    return fail(SV_ERR_INVALID_ARG, "q, k_cache, v_cache and out are required");
+  if (!a->parent && !a->anc_mask) return fail(SV_ERR_INVALID_ARG, "one of parent / anc_mask is required");
+  if (!aligned(a->q, 16) || !aligned(a->k_cache, 16) || !aligned(a->v_cache, 16) || !aligned(a->out, 16))
+    return fail(SV_ERR_INVALID_ARG, "q, k_cache, v_cache and out must be 16-byte aligned");
+  if ((a->prof_start == nullptr) != (a->prof_stop == nullptr))
+    return fail(SV_ERR_INVALID_ARG, "prof_start and prof_stop must be given together");
+  return SV_OK;
+}
+
+sv::AttnPlan plan_attn(const sv_attn_args* a) {
+  sv::AttnPlan pl{};
+  const int G = a->Hq / a->Hkv;
+  const int rmax = G * eff_max_nodes(a->max_nodes);
+  pl.mfma = a->dtype == SV_BF16;
+  if (pl.mfma) {
+    pl.rows_per_wg = rmax <= 64 ? 64 : rmax <= 128 ? 128 : 256;
+    pl.rbw = pl.rows_per_wg == 256 ? 2 : 1;
+  } else {
+    pl.rows_per_wg = 8;
+    pl.rbw = 0;
+  }
+  pl.n_rowgroups = (rmax + pl.rows_per_wg - 1) / pl.rows_per_wg;
+  const int64_t max_splits_len = a->Lcap / 64 > 0 ? a->Lcap / 64 : 1;
+  if (a->num_splits > 0) {
+    pl.splits = (int)(a->num_splits < max_splits_len ? a->num_splits : max_splits_len);
+  } else {
+    // enough workgroups for 256 CUs, but each split keeps >= 256 keys and the
+    // partial outputs it adds stay below a quarter of the KV bytes
+    const int64_t items = (int64_t)a->B * a->Hkv * pl.n_rowgroups;
+    const int64_t want = (512 + items - 1) / (items > 0 ? items : 1);
+    const int64_t by_len = a->Lcap / 256 > 0 ? a->Lcap / 256 : 1;
+    const int64_t esz = a->dtype == SV_BF16 ? 2 : 4;
+    const int64_t kv_bytes = 2 * (int64_t)a->B * a->Hkv * a->Lcap * a->D * esz;
+    const int64_t part_bytes = 2 * (int64_t)a->total_nodes * a->Hq * (a->D + 2) * 4;
+    const int64_t by_traffic = part_bytes > 0 ? kv_bytes / (4 * part_bytes) : 256;
+    int64_t s = want;
+    if (s > by_len) s = by_len;
+    if (s > by_traffic) s = by_traffic;
+    if (s > 256) s = 256;
+    pl.splits = s < 1 ? 1 : (int)s;
+  }
+  return pl;
+}
+
+struct WsLayout {
+  size_t anc = 0, o_part = 0, ml_part = 0, stats = 0, total = 0;
+};
+
+size_t attn_part_bytes(const sv_attn_args* a, const sv::AttnPlan& pl, size_t* ml) {
+  if (pl.splits <= 1) {
+    *ml = 0;
+    return 0;
+  }
+  const size_t nh = (size_t)a->total_nodes * a->Hq;
+  *ml = (size_t)pl.splits * nh * sizeof(float2);
+  return (size_t)pl.splits * nh * a->D * sizeof(float);
+}
+
+int sample_nch(const sv_sample_args* s) { return (s->V + sv::kChunk - 1) / sv::kChunk; }
+
+WsLayout layout(const sv_attn_args* a, const sv_sample_args* s) {
+  WsLayout w;
+  size_t off = 0;
+  if (a && a->B > 0 && a->total_nodes > 0) {
+    const sv::AttnPlan pl = plan_attn(a);
+    if (!a->anc_mask) {
+      w.anc = off;
+      off += align_up((size_t)a->total_nodes * sizeof(uint64_t));
+    }
+    size_t ml = 0;
+    const size_t op = attn_part_bytes(a, pl, &ml);
+    if (op) {
+      w.o_part = off;
+      off += align_up(op);
+      w.ml_part = off;
+      off += align_up(ml);
+    }
+  }
+  if (s && s->B > 0) {
+    w.stats = off;
+    off += align_up(((size_t)s->total_nodes + s->B) * sample_nch(s) * sizeof(sv::ChunkStat));
+  }
+  w.total = off;
+  return w;
+}
+
+// ---- sampler ---------------------------------------------------------------
+sv_status check_sample(const sv_sample_args* s) {
+  if (!s) return fail(SV_ERR_INVALID_ARG, "sample args is NULL");
+  if (s->B < 0) return fail(SV_ERR_INVALID_ARG, "B < 0");
+  if (s->V < 1 || s->V > sv::kMaxVocab) return fail(SV_ERR_UNSUPPORTED, "V must be in [1, 2^22]");
+  if (s->total_nodes < 0) return fail(SV_ERR_INVALID_ARG, "total_nodes < 0");
+  if (s->max_nodes < 0 || s->max_nodes > sv::kMaxNodes)
+    return fail(SV_ERR_UNSUPPORTED, "max_nodes must be in [0, 64]");
+  if (!(s->temperature >= 0.f) || isinf(s->temperature))
+    return fail(SV_ERR_INVALID_ARG, "temperature must be finite and >= 0");
+  if (s->temperature > 0.f && !isfinite(1.4426950408889634 / (double)s->temperature) )
+    return fail(SV_ERR_INVALID_ARG, "temperature too small");
+  const int md_needed = eff_max_nodes(s->max_nodes);
+  if (s->max_depth < md_needed)
+    return fail(SV_ERR_INVALID_ARG, "max_depth (%d) must be >= max_nodes (%d)", s->max_depth, md_needed);
+  if (((int64_t)s->total_nodes + s->B) * (int64_t)s->V >= (1ll << 40))
+    return fail(SV_ERR_UNSUPPORTED, "(N + B) * V too large");
+  if (s->B == 0) return SV_OK;
+  if (!s->cu_nodes || !s->target_logits || !s->accept_len || !s->accepted_nodes || !s->out_tokens)
+    return fail(SV_ERR_INVALID_ARG, "cu_nodes, target_logits, accept_len, accepted_nodes, out_tokens are required");
+  if (s->total_nodes > 0 && (!s->parent || !s->draft_tokens))
+    return fail(SV_ERR_INVALID_ARG, "parent and draft_tokens are required when total_nodes > 0");
+  if (s->temperature > 0.f && !s->draft_probs)
+    return fail(SV_ERR_INVALID_ARG, "draft_probs is required when temperature > 0");
+  if (s->probs_out && s->temperature == 0.f)
+    return fail(SV_ERR_INVALID_ARG, "probs_out needs temperature > 0");
+  if (!aligned(s->target_logits, 4) || (s->draft_probs && !aligned(s->draft_probs, 4)))
+    return fail(SV_ERR_INVALID_ARG, "logit and probability rows must be 4-byte aligned");
+  if (!aligned(s->uniforms_out, 8)) return fail(SV_ERR_INVALID_ARG, "uniforms_out must be 8-byte aligned");
+  if ((s->prof_start == nullptr) != (s->prof_stop == nullptr))
+    return fail(SV_ERR_INVALID_ARG, "prof_start and prof_stop must be given together");
+  return SV_OK;
+}
+
+sv_status check_ws(const WsLayout& w, void* ws, size_t ws_bytes) {
+  if (w.total == 0) return SV_OK;
+  if (!ws) return fail(SV_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", w.total);
+  if (!aligned(ws, kAlign)) return fail(SV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < w.total) return fail(SV_ERR_WORKSPACE, "workspace too small: %zu < %zu", ws_bytes, w.total);
+  return SV_OK;
+}
+
+sv_status hip_fail(hipError_t e, const char* what) {
+  return fail(SV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+sv_status run_attn(const sv_attn_args* a, char* ws, const WsLayout& w, hipStream_t st) {
+  if (a->B == 0 || a->total_nodes == 0) return SV_OK;
+  const sv::AttnPlan pl = plan_attn(a);
+  const int mn = eff_max_nodes(a->max_nodes);
+  const uint64_t* anc = a->anc_mask;
+  if (!anc) {
+    uint64_t* w_anc = (uint64_t*)(ws + w.anc);
+    hipError_t e = sv::launch_tree_prep(a->B, a->total_nodes, mn, a->cu_nodes, a->parent, w_anc, a->status, st);
+    if (e != hipSuccess) return hip_fail(e, "tree prep launch");
+    anc = w_anc;
+  }
+  sv::AttnParams p{};
+  p.B = a->B;
+  p.N = a->total_nodes;
+  p.Hq = a->Hq;
+  p.Hkv = a->Hkv;
+  p.G = a->Hq / a->Hkv;
+  p.D = a->D;
+  p.max_nodes = mn;
+  p.Lcap = a->Lcap;
+  p.ctx_len = a->ctx_len;
+  p.cu_nodes = a->cu_nodes;
+  p.anc = anc;
+  p.q = a->q;
+  p.k = a->k_cache;
+  p.v = a->v_cache;
+  p.out = a->out;
+  p.o_part = pl.splits > 1 ? (float*)(ws + w.o_part) : nullptr;
+  p.ml_part = pl.splits > 1 ? (float2*)(ws + w.ml_part) : nullptr;
+  p.splits = pl.splits;
+  p.rows_per_wg = pl.rows_per_wg;
+  const float scale = a->scale > 0.f ? a->scale : (float)(1.0 / sqrt((double)a->D));
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  p.status = a->status;
+  hipError_t e = sv::launch_attention(p, pl, a->dtype == SV_BF16, st, (hipEvent_t)a->prof_start,
+                                      (hipEvent_t)a->prof_stop);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return SV_OK;
+}
+
+sv_status run_sample(const sv_sample_args* s, char* ws, const WsLayout& w, hipStream_t st) {
+  if (s->B == 0) return SV_OK;
+  sv::SampleParams p{};
+  p.B = s->B;
+  p.V = s->V;
+  p.N = s->total_nodes;
+  p.max_nodes = eff_max_nodes(s->max_nodes);
+  p.max_depth = s->max_depth;
+  p.nch = sample_nch(s);
+  p.cu_nodes = s->cu_nodes;
+  p.parent = s->parent;
+  p.tokens = s->draft_tokens;
+  p.logits = s->target_logits;
+  p.q = s->draft_probs;
+  p.greedy = s->temperature == 0.f;
+  p.c = p.greedy ? 0.f : (float)(1.4426950408889634 / (double)s->temperature);
+  p.seed = s->seed;
+  p.step = s->step;
+  p.request_id = s->request_id;
+  p.accept_len = s->accept_len;
+  p.accepted_nodes = s->accepted_nodes;
+  p.out_tokens = s->out_tokens;
+  p.probs_out = s->probs_out;
+  p.uniforms_out = s->uniforms_out;
+  p.residual_passes = s->residual_passes;
+  p.status = s->status;
+  p.stats = (sv::ChunkStat*)(ws + w.stats);
+  const bool vec4 = (s->V % 4 == 0) && aligned(s->target_logits, 16) && (!s->draft_probs || aligned(s->draft_probs, 16));
+  // a workgroup per request: wide enough to stream a whole row per residual pass
+  int threads = 64 * ((p.nch + 1) / 2);
+  if (threads < 64) threads = 64;
+  if (threads > 512) threads = 512;
+  hipError_t e = sv::launch_sampler(p, vec4, threads, st, (hipEvent_t)s->prof_start, (hipEvent_t)s->prof_stop);
+  if (e != hipSuccess) return hip_fail(e, "sampler launch");
+  return SV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t spec_verify_workspace_size(const sv_attn_args* attn, const sv_sample_args* sample) {
+  if (attn && check_attn(attn) != SV_OK) return 0;
+  if (sample && check_sample(sample) != SV_OK) return 0;
+  return layout(attn, sample).total;
+}
+
+sv_status spec_verify_attn(const sv_attn_args* attn, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  sv_status st = check_attn(attn);
+  if (st != SV_OK) return st;
+  const WsLayout w = layout(attn, nullptr);
+  if ((st = check_ws(w, ws, ws_bytes)) != SV_OK) return st;
+  return run_attn(attn, (char*)ws, w, (hipStream_t)stream);
+}
+
+sv_status spec_verify_sample(const sv_sample_args* sample, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  sv_status st = check_sample(sample);
+  if (st != SV_OK) return st;
+  const WsLayout w = layout(nullptr, sample);
+  if ((st = check_ws(w, ws, ws_bytes)) != SV_OK) return st;
+  return run_sample(sample, (char*)ws, w, (hipStream_t)stream);
+}
+
+sv_status spec_verify_step(const sv_attn_args* attn, const sv_sample_args* sample, void* ws, size_t ws_bytes,
+                           void* stream) {
+  g_err[0] = 0;
+  sv_status st = check_attn(attn);
+  if (st != SV_OK) return st;
+  if ((st = check_sample(sample)) != SV_OK) return st;
+  if (attn->B != sample->B || attn->total_nodes != sample->total_nodes || attn->cu_nodes != sample->cu_nodes)
+    return fail(SV_ERR_INVALID_ARG, "attn and sample args must describe the same batch (B, total_nodes, cu_nodes)");
+  const WsLayout w = layout(attn, sample);
+  if ((st = check_ws(w, ws, ws_bytes)) != SV_OK) return st;
+  if ((st = run_attn(attn, (char*)ws, w, (hipStream_t)stream)) != SV_OK) return st;
+  return run_sample(sample, (char*)ws, w, (hipStream_t)stream);
+}
+
+const char* spec_verify_last_error(void) { return g_err; }
+
+size_t spec_verify_struct_size(int32_t which) {
+  if (which == 0) return sizeof(sv_attn_args);
+  if (which == 1) return sizeof(sv_sample_args);
+  return 0;
+}
+
+}  // extern "C"

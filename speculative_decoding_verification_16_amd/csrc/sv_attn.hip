@@ -1,0 +1,515 @@
+// sv_attn.hip -- tree preprocessing and tree-masked GQA attention for gfx950.
+//
+// The mask follows "Speculative Decoding: Accelerating Inference Speeds in
+// Distributed LLMs", section "Tree Attention Mask Mechanics": a draft node
+// attends to the whole committed context, to its ancestors and to itself,
+// never to another branch. GQA: query head h reads KV head h / (Hq/Hkv)
+// (same page, "Interaction with Advanced Attention Architectures").
+//
+// Work decomposition: one workgroup per (request b, KV head g, row group,
+// KV split). The rows of a workgroup are the (node j, head-in-group hh)
+// pairs r = j*G + hh of one KV head, so every K/V byte fetched from HBM is
+// shared by all G*T_b query rows that read it. Long contexts are cut into
+// splits whose partial (max, sum, unnormalised output) are merged by a
+// second kernel (flash-decoding style split-K).
+#include "sv_device.h"
+#include "sv_internal.h"
+
+namespace sv {
+
+typedef short bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// Tree preprocessing: ancestor-or-self bitmask of every node. One wave per
+// request, lane j owns node j and climbs its parent chain (each step must go
+// to a strictly smaller index, so the climb ends within j steps).
+__global__ __launch_bounds__(64) void tree_prep_kernel(int B, int N, int max_nodes, const int32_t* cu_nodes,
+                                                       const int32_t* parent, uint64_t* anc, int32_t* status) {
+  __shared__ int32_t par[kMaxNodes];
+  const int b = blockIdx.x, j = threadIdx.x;
+  if (b == 0 && j == 0 && cu_nodes[B] != N) flag(status, kStPacking);
+  const int n0 = cu_nodes[b], n1 = cu_nodes[b + 1];
+  const int T = n1 - n0;
+  if (n0 < 0 || T < 0 || T > max_nodes || n1 > N) {
+    if (j == 0) flag(status, kStPacking);
+    return;
+  }
+  if (j < T) par[j] = parent[n0 + j];
+  __syncthreads();
+  if (j < T) {
+    uint64_t m = 1ull << j;
+    int prev = j, x = par[j];
+    bool bad = false;
+    while (x != -1) {
+      if (x < 0 || x >= prev) { bad = true; break; }
+      m |= 1ull << x;
+      prev = x;
+      x = par[x];
+    }
+    if (bad) {  // treated as a child of the root: sees the context and itself
+      m = 1ull << j;
+      flag(status, kStTree);
+    }
+    anc[n0 + j] = m;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 path: MFMA 16x16x32 (gfx950).
+//
+// S^T = K Q^T is computed per 16-key x 16-row block with K as the A operand
+// (keys x head-dim) and Q^T as the B operand, so the fp32 result leaves every
+// lane holding 4 consecutive keys of one query row (row = lane % 16). After
+// the online softmax those values are already laid out as the B operand of
+// O^T = V^T P^T; V^T comes from LDS. Each lane therefore keeps the running
+// max / sum of exactly one row and no transpose of P is needed.
+//
+// LDS tiles (64 keys):
+//   Ks [key][D]   16-byte unit u of row `key` stored at unit u ^ (key & 7);
+//   Vt [d][64]    key kappa stored at column pos(kappa) (pairs of 16-key
+//                 sub-tiles interleaved so a lane's 8 keys of one k-step
+//                 are contiguous), 16-byte unit u of row d stored at
+//                 u ^ sw(d). Both swizzles keep the MFMA-operand reads and
+//                 the tile writes free of most bank conflicts.
+__device__ __forceinline__ int vt_pos(int kappa) {
+  const int ks = kappa >> 5, rem = kappa & 31;
+  return (ks << 5) + (((rem & 15) >> 2) << 3) + ((rem >> 4) << 2) + (rem & 3);
+}
+__device__ __forceinline__ int vt_sw(int d) { return (d ^ (d >> 2)) & 7; }
+
+// NW waves per workgroup, RBW 16-row blocks per wave: 16 * RBW * NW rows.
+// WPE: waves per SIMD the register budget is sized for.
+template <int D, int RBW, int NW, int WPE>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE)))
+void attn_mfma_kernel(AttnParams p) {
+  constexpr int NT = 64 * NW;        // threads
+  constexpr int KT = 64;             // keys per tile
+  constexpr int KS = D / 32;         // k-steps of S^T (32 head dims each)
+  constexpr int DB = D / 16;         // 16-wide blocks of the output head dim
+  constexpr int UNITS = D / 8;       // 16-byte units per K row
+  constexpr int PER_THREAD = KT * D / 8 / NT; // K units / V items loaded per thread per tile
+  static_assert(PER_THREAD >= 1 && KT * D / 8 == PER_THREAD * NT, "tile / thread split");
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * D];
+  __shared__ __attribute__((aligned(16))) uint32_t Vt[D * KT / 2];
+
+  const int b = blockIdx.z, g = blockIdx.y;
+  const int rg = blockIdx.x / p.splits, split = blockIdx.x % p.splits;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g4 = lane >> 4;
+
+  const int n0 = p.cu_nodes[b], n1 = p.cu_nodes[b + 1];
+  const int T = n1 - n0;
+  if (n0 < 0 || T < 0 || T > p.max_nodes || n1 > p.N) return;  // flagged by tree prep / host
+  const int L = p.ctx_len[b];
+  if (L < 0 || (int64_t)L + T > p.Lcap) {
+    if (tid == 0 && blockIdx.x == 0 && g == 0) flag(p.status, kStCtx);
+    return;
+  }
+  const int R = p.G * T;
+  const int row0 = rg * p.rows_per_wg;
+  if (row0 >= R) return;
+  const int nkeys = L + T;
+  const int kchunk = ((nkeys + p.splits - 1) / p.splits + KT - 1) / KT * KT;
+  const int kb = split * kchunk;
+  const int ke = min(nkeys, kb + kchunk);
+  const int NH = p.N * p.Hq;
+
+  // rows of this lane: r = row0 + 16 * (wave + NW i) + l16
+  bf16x8_t qf[RBW][KS];
+  uint64_t amask[RBW];
+  int orow[RBW];  // packed (node, q head) index, -1 if the row does not exist
+  bool rb_any[RBW];
+#pragma unroll
+  for (int i = 0; i < RBW; ++i) {
+    const int rbase = row0 + 16 * (wave + NW * i);
+    rb_any[i] = rbase < R;
+    const int r = rbase + l16;
+    orow[i] = -1;
+    amask[i] = 0;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[i][ks] = bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+    if (r < R) {
+      const int j = r / p.G, hh = r - j * p.G;
+      orow[i] = (n0 + j) * p.Hq + g * p.G + hh;
+      amask[i] = p.anc[n0 + j];
+      const uint16_t* qp = (const uint16_t*)p.q + (int64_t)orow[i] * D;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[i][ks] = *(const bf16x8_t*)(qp + 32 * ks + 8 * g4);
+    }
+  }
+
+  if (kb >= ke) {  // empty split: contributes nothing to the merge
+#pragma unroll
+    for (int i = 0; i < RBW; ++i)
+      if (orow[i] >= 0 && g4 == 0) p.ml_part[(int64_t)split * NH + orow[i]] = make_float2(-INFINITY, 0.f);
+    return;
+  }
+
+  const int64_t head_off = ((int64_t)b * p.Hkv + g) * p.Lcap * D;
+  const uint16_t* kbase = (const uint16_t*)p.k + head_off;
+  const uint16_t* vbase = (const uint16_t*)p.v + head_off;
+
+  // K/V tiles come in through buffer loads: the resource covers exactly the
+  // keys [0, ke) of this (request, KV head), so a key past the split end reads
+  // as zero (never a stray cache slot), and the per-thread offsets are 32-bit
+  // constants with the tile start in the scalar offset.
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, ke * D * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, ke * D * 2, 0x00020000);
+  int koff[PER_THREAD], voff[PER_THREAD];
+#pragma unroll
+  for (int i = 0; i < PER_THREAD; ++i) {
+    const int c = tid + NT * i;
+    koff[i] = ((c / UNITS) * D + 8 * (c % UNITS)) * 2;
+    voff[i] = ((c / (D / 4)) * 2 * D + 4 * (c % (D / 4))) * 2;
+  }
+  i32x4_t kreg[PER_THREAD];
+  i32x2_t vreg[PER_THREAD][2];
+  auto load_tile = [&](int t0) {
+    const int so = t0 * D * 2;
+#pragma unroll
+    for (int i = 0; i < PER_THREAD; ++i) {
+      kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(krs, koff[i], so, 0);
+      vreg[i][0] = __builtin_amdgcn_raw_buffer_load_b64(vrs, voff[i], so, 0);
+      vreg[i][1] = __builtin_amdgcn_raw_buffer_load_b64(vrs, voff[i] + D * 2, so, 0);
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int i = 0; i < PER_THREAD; ++i) {
+      const int c = tid + NT * i;
+      const int kk = c / UNITS, dc = c % UNITS;
+      *(i32x4_t*)(Ks + kk * D + 8 * (dc ^ (kk & 7))) = kreg[i];
+      const int kp = c / (D / 4), dq = c % (D / 4);
+      const int pos = vt_pos(2 * kp);  // even key; its odd partner sits at pos + 1
+      const uint32_t ax = (uint32_t)vreg[i][0][0], ay = (uint32_t)vreg[i][0][1];
+      const uint32_t bx = (uint32_t)vreg[i][1][0], by = (uint32_t)vreg[i][1][1];
+      const uint32_t w[4] = {(ax & 0xffffu) | (bx << 16), (ax >> 16) | (bx & 0xffff0000u),
+                             (ay & 0xffffu) | (by << 16), (ay >> 16) | (by & 0xffff0000u)};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int d = 4 * dq + e;
+        Vt[d * 32 + (((pos >> 3) ^ vt_sw(d)) << 2) + ((pos >> 1) & 3)] = w[e];
+      }
+    }
+  };
+
+  f32x4_t o[RBW][DB];
+  float m[RBW], l[RBW];
+#pragma unroll
+  for (int i = 0; i < RBW; ++i) {
+    m[i] = -INFINITY;
+    l[i] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[i][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  load_tile(kb);
+  for (int t0 = kb; t0 < ke; t0 += KT) {
+    __syncthreads();
+    store_tile();
+    __syncthreads();
+    if (t0 + KT < ke) load_tile(t0 + KT);
+    const bool full = (t0 + KT <= ke) && (t0 + KT <= L);
+
+    // S^T for every owned row block; each K fragment is read from LDS once
+    f32x4_t s[RBW][4];
+#pragma unroll
+    for (int i = 0; i < RBW; ++i)
+#pragma unroll
+      for (int st = 0; st < 4; ++st) s[i][st] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+    for (int st = 0; st < 4; ++st) {
+      const int key = 16 * st + l16;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8_t a = *(const bf16x8_t*)(Ks + key * D + 8 * ((4 * ks + g4) ^ (key & 7)));
+#pragma unroll
+        for (int i = 0; i < RBW; ++i)
+          if (rb_any[i]) s[i][st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[i][ks], s[i][st], 0, 0, 0);
+      }
+    }
+
+    // online softmax (log2 domain), P^T packed as the PV B operand
+    bf16x8_t pk[RBW][2];
+#pragma unroll
+    for (int i = 0; i < RBW; ++i) {
+      if (!rb_any[i]) continue;
+      float x[16];
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[4 * st + e] = s[i][st][e] * p.scale_log2;
+      if (!full) {
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int kappa = t0 + 16 * st + 4 * g4 + e;
+            const bool vis = kappa < ke && (kappa < L || ((amask[i] >> (kappa - L)) & 1ull));
+            if (!vis) x[4 * st + e] = -INFINITY;
+          }
+      }
+      float mx = x[0];
+#pragma unroll
+      for (int t = 1; t < 16; ++t) mx = fmaxf(mx, x[t]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = fmaxf(m[i], mx);
+      const float msub = mnew == -INFINITY ? 0.f : mnew;
+      const float alpha = exp2f(m[i] - msub);  // m = -inf (nothing seen yet) -> 0
+      float pv[16];
+      float lsum = 0.f;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        pv[t] = exp2f(x[t] - msub);
+        lsum += pv[t];
+      }
+      l[i] = l[i] * alpha + lsum;
+      m[i] = mnew;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[i][db] *= alpha;
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        // element 4h + e  <->  sub-tile st = 2 k2 + h, value e
+        const float* lo = pv + 4 * (2 * k2);
+        const float* hi = pv + 4 * (2 * k2 + 1);
+        const uint32_t w0 = pack_bf16x2(lo[0], lo[1]), w1 = pack_bf16x2(lo[2], lo[3]);
+        const uint32_t w2 = pack_bf16x2(hi[0], hi[1]), w3 = pack_bf16x2(hi[2], hi[3]);
+        bf16x8_t v;
+        v[0] = (short)(w0 & 0xffff); v[1] = (short)(w0 >> 16);
+        v[2] = (short)(w1 & 0xffff); v[3] = (short)(w1 >> 16);
+        v[4] = (short)(w2 & 0xffff); v[5] = (short)(w2 >> 16);
+        v[6] = (short)(w3 & 0xffff); v[7] = (short)(w3 >> 16);
+        pk[i][k2] = v;
+      }
+    }
+
+    // O^T += V^T P^T; each V fragment is read from LDS once
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int d = 16 * db + l16;
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const bf16x8_t a = *(const bf16x8_t*)(Vt + d * 32 + (((4 * k2 + g4) ^ vt_sw(d)) << 2));
+#pragma unroll
+        for (int i = 0; i < RBW; ++i)
+          if (rb_any[i]) o[i][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pk[i][k2], o[i][db], 0, 0, 0);
+      }
+    }
+  }
+
+  // row sums across the four lane groups that share a row, then write
+#pragma unroll
+  for (int i = 0; i < RBW; ++i) {
+    if (!rb_any[i]) continue;
+    float lt = l[i] + __shfl_xor(l[i], 16);
+    lt += __shfl_xor(lt, 32);
+    if (orow[i] < 0) continue;
+    if (p.splits == 1) {
+      const float inv = 1.0f / lt;
+      float* op = p.out + (int64_t)orow[i] * D + 4 * g4;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const f32x4_t v = o[i][db] * inv;
+        *(float4*)(op + 16 * db) = make_float4(v[0], v[1], v[2], v[3]);
+      }
+    } else {
+      float* op = p.o_part + ((int64_t)split * NH + orow[i]) * D + 4 * g4;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const f32x4_t v = o[i][db];
+        *(float4*)(op + 16 * db) = make_float4(v[0], v[1], v[2], v[3]);
+      }
+      if (g4 == 0) p.ml_part[(int64_t)split * NH + orow[i]] = make_float2(m[i], lt);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 path (plain VALU): 8 query rows per workgroup, 32-key tiles in LDS.
+// Thread t handles row t/32 and, per tile, key t%32 for the scores and head
+// dims t%32 + 32k for the output.
+template <int D>
+__global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
+  constexpr int KT = 32, RW = 8, DPT = D / 32;
+  __shared__ float Qs[RW][D];
+  __shared__ float Ks[KT][D + 1];
+  __shared__ float Vs[KT][D];
+  __shared__ float Ps[RW][KT];
+
+  const int b = blockIdx.z, g = blockIdx.y;
+  const int rg = blockIdx.x / p.splits, split = blockIdx.x % p.splits;
+  const int tid = threadIdx.x, rl = tid >> 5, kl = tid & 31;
+  const int n0 = p.cu_nodes[b], n1 = p.cu_nodes[b + 1];
+  const int T = n1 - n0;
+  if (n0 < 0 || T < 0 || T > p.max_nodes || n1 > p.N) return;
+  const int L = p.ctx_len[b];
+  if (L < 0 || (int64_t)L + T > p.Lcap) {
+    if (tid == 0 && blockIdx.x == 0 && g == 0) flag(p.status, kStCtx);
+    return;
+  }
+  const int R = p.G * T;
+  const int row0 = rg * RW;
+  if (row0 >= R) return;
+  const int nkeys = L + T;
+  const int kchunk = ((nkeys + p.splits - 1) / p.splits + KT - 1) / KT * KT;
+  const int kb = split * kchunk;
+  const int ke = min(nkeys, kb + kchunk);
+  const int NH = p.N * p.Hq;
+  const float* q = (const float*)p.q;
+
+  for (int idx = tid; idx < RW * D; idx += 256) {
+    const int r = row0 + idx / D, d = idx % D;
+    float v = 0.f;
+    if (r < R) {
+      const int j = r / p.G, hh = r - j * p.G;
+      v = q[((int64_t)(n0 + j) * p.Hq + g * p.G + hh) * D + d];
+    }
+    Qs[idx / D][d] = v;
+  }
+  const int r = row0 + rl;
+  int orow = -1;
+  uint64_t amask = 0;
+  if (r < R) {
+    const int j = r / p.G, hh = r - j * p.G;
+    orow = (n0 + j) * p.Hq + g * p.G + hh;
+    amask = p.anc[n0 + j];
+  }
+  if (kb >= ke) {
+    if (orow >= 0 && kl == 0) p.ml_part[(int64_t)split * NH + orow] = make_float2(-INFINITY, 0.f);
+    return;
+  }
+  const int64_t head_off = ((int64_t)b * p.Hkv + g) * p.Lcap * D;
+  const float* kbase = (const float*)p.k + head_off;
+  const float* vbase = (const float*)p.v + head_off;
+
+  float m = -INFINITY, l = 0.f, o[DPT];
+#pragma unroll
+  for (int k2 = 0; k2 < DPT; ++k2) o[k2] = 0.f;
+
+  for (int t0 = kb; t0 < ke; t0 += KT) {
+    __syncthreads();
+    for (int idx = tid; idx < KT * D; idx += 256) {
+      const int kk = idx / D, d = idx % D, key = t0 + kk;
+      const bool in = key < ke;
+      Ks[kk][d] = in ? kbase[(int64_t)key * D + d] : 0.f;
+      Vs[kk][d] = in ? vbase[(int64_t)key * D + d] : 0.f;
+    }
+    __syncthreads();
+    float s = 0.f;
+#pragma unroll 8
+    for (int d = 0; d < D; ++d) s += Qs[rl][d] * Ks[kl][d];
+    float x = s * p.scale_log2;
+    const int key = t0 + kl;
+    const bool vis = key < ke && (key < L || ((amask >> (key - L)) & 1ull));
+    if (!vis) x = -INFINITY;
+    float mx = x;
+#pragma unroll
+    for (int o2 = 16; o2 > 0; o2 >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o2));
+    const float mnew = fmaxf(m, mx);
+    const float msub = mnew == -INFINITY ? 0.f : mnew;
+    const float alpha = exp2f(m - msub);
+    const float pv = exp2f(x - msub);
+    float ls = pv;
+#pragma unroll
+    for (int o2 = 16; o2 > 0; o2 >>= 1) ls += __shfl_xor(ls, o2);
+    l = l * alpha + ls;
+    m = mnew;
+    Ps[rl][kl] = pv;
+    __syncthreads();
+#pragma unroll
+    for (int k2 = 0; k2 < DPT; ++k2) {
+      const int d = kl + 32 * k2;
+      float acc = o[k2] * alpha;
+#pragma unroll 8
+      for (int kk = 0; kk < KT; ++kk) acc += Ps[rl][kk] * Vs[kk][d];
+      o[k2] = acc;
+    }
+  }
+  if (orow < 0) return;
+  if (p.splits == 1) {
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int k2 = 0; k2 < DPT; ++k2) p.out[(int64_t)orow * D + kl + 32 * k2] = o[k2] * inv;
+  } else {
+#pragma unroll
+    for (int k2 = 0; k2 < DPT; ++k2) p.o_part[((int64_t)split * NH + orow) * D + kl + 32 * k2] = o[k2];
+    if (kl == 0) p.ml_part[(int64_t)split * NH + orow] = make_float2(m, l);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Split-K merge: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+// One wave per (node, query head).
+__global__ __launch_bounds__(256) void attn_combine_kernel(int NH, int D, int splits, const float* o_part,
+                                                           const float2* ml_part, float* out) {
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (item >= NH) return;
+  float M = -INFINITY;
+  for (int s = 0; s < splits; ++s) {
+    const float2 ml = ml_part[(int64_t)s * NH + item];
+    if (ml.y > 0.f) M = fmaxf(M, ml.x);
+  }
+  float den = 0.f;
+  for (int s = 0; s < splits; ++s) {
+    const float2 ml = ml_part[(int64_t)s * NH + item];
+    if (ml.y > 0.f) den += exp2f(ml.x - M) * ml.y;
+  }
+  const float inv = 1.0f / den;
+  for (int d = lane; d < D; d += 64) {
+    float acc = 0.f;
+    for (int s = 0; s < splits; ++s) {
+      const float2 ml = ml_part[(int64_t)s * NH + item];
+      if (ml.y > 0.f) acc += exp2f(ml.x - M) * o_part[((int64_t)s * NH + item) * D + d];
+    }
+    out[(int64_t)item * D + d] = acc * inv;
+  }
+}
+
+// ---------------------------------------------------------------------------
+hipError_t launch_tree_prep(int B, int N, int max_nodes, const int32_t* cu_nodes, const int32_t* parent,
+                            uint64_t* anc, int32_t* status, hipStream_t stream) {
+  if (B <= 0) return hipSuccess;
+  tree_prep_kernel<<<dim3(B), dim3(64), 0, stream>>>(B, N, max_nodes, cu_nodes, parent, anc, status);
+  return hipGetLastError();
+}
+
+// rows per workgroup 64 / 128 / 256 -> (RBW, NW) = (1,4) / (1,8) / (2,8)
+template <int D>
+static void launch_mfma_d(const AttnParams& p, int rows_per_wg, dim3 grid, hipStream_t stream) {
+  if (rows_per_wg <= 64) attn_mfma_kernel<D, 1, 4, 3><<<grid, dim3(256), 0, stream>>>(p);
+  else if (rows_per_wg <= 128) attn_mfma_kernel<D, 1, 8, 3><<<grid, dim3(512), 0, stream>>>(p);
+  else attn_mfma_kernel<D, 2, 8, 2><<<grid, dim3(512), 0, stream>>>(p);
+}
+
+hipError_t launch_attention(const AttnParams& p, const AttnPlan& plan, bool bf16, hipStream_t stream,
+                            hipEvent_t ev_start, hipEvent_t ev_stop) {
+  if (p.B <= 0 || p.N <= 0) return hipSuccess;
+  const dim3 grid(plan.n_rowgroups * plan.splits, p.Hkv, p.B);
+  if (ev_start) (void)hipEventRecord(ev_start, stream);
+  if (bf16) {
+    if (p.D == 128) launch_mfma_d<128>(p, plan.rows_per_wg, grid, stream);
+    else launch_mfma_d<64>(p, plan.rows_per_wg, grid, stream);
+  } else {
+    if (p.D == 128) attn_valu_kernel<128><<<grid, dim3(256), 0, stream>>>(p);
+    else attn_valu_kernel<64><<<grid, dim3(256), 0, stream>>>(p);
+  }
+  if (ev_stop) (void)hipEventRecord(ev_stop, stream);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  if (plan.splits > 1) {
+    const int NH = p.N * p.Hq;
+    attn_combine_kernel<<<dim3((NH + 3) / 4), dim3(256), 0, stream>>>(NH, p.D, plan.splits, p.o_part, p.ml_part,
+                                                                        p.out);
+    err = hipGetLastError();
+  }
+  return err;
+}
+
+}  // namespace sv

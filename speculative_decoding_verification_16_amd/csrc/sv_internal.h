@@ -1,0 +1,73 @@
+// sv_internal.h -- parameter blocks and launchers shared between the host
+// dispatch (sv_api.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sv {
+
+struct ChunkStat;
+
+// ---- attention ---------------------------------------------------------------
+struct AttnParams {
+  int32_t B, N, Hq, Hkv, G, D;
+  int32_t max_nodes;       // bound on T_b used for validation
+  int64_t Lcap;
+  const int32_t* ctx_len;
+  const int32_t* cu_nodes;
+  const uint64_t* anc;     // [N] ancestor-or-self masks
+  const void* q;           // [N, Hq, D]
+  const void* k;           // [B, Hkv, Lcap, D]
+  const void* v;
+  float* out;              // [N, Hq, D] (used when splits == 1)
+  float* o_part;           // [splits, N*Hq, D] unnormalised partial outputs
+  float2* ml_part;         // [splits, N*Hq] (running max in log2 units, sum)
+  int32_t splits;
+  int32_t rows_per_wg;     // query rows (node, head-in-group) per workgroup
+  float scale_log2;        // softmax scale * log2(e)
+  int32_t* status;
+};
+
+struct AttnPlan {
+  bool mfma;        // bf16 MFMA path (else fp32 VALU path)
+  int rbw;          // MFMA path: 16-row blocks per wave
+  int rows_per_wg;
+  int n_rowgroups;  // workgroups per (request, KV head, split) along rows
+  int splits;
+};
+
+hipError_t launch_tree_prep(int B, int N, int max_nodes, const int32_t* cu_nodes, const int32_t* parent,
+                            uint64_t* anc, int32_t* status, hipStream_t stream);
+hipError_t launch_attention(const AttnParams& p, const AttnPlan& plan, bool bf16, hipStream_t stream,
+                            hipEvent_t ev_start, hipEvent_t ev_stop);
+
+// ---- sampler -----------------------------------------------------------------
+struct SampleParams {
+  int32_t B, V, N, max_nodes, max_depth;
+  int32_t nch;              // vocabulary chunks per row
+  const int32_t* cu_nodes;
+  const int32_t* parent;
+  const int32_t* tokens;
+  const float* logits;      // [N+B, V]
+  const float* q;           // [N+B, V] (unused when greedy)
+  float c;                  // log2(e) / temperature (0 when greedy)
+  bool greedy;
+  uint64_t seed;
+  uint32_t step;
+  const uint32_t* request_id;
+  int32_t* accept_len;
+  int32_t* accepted_nodes;
+  int32_t* out_tokens;
+  float* probs_out;
+  double* uniforms_out;
+  int32_t* residual_passes;
+  int32_t* status;
+  ChunkStat* stats;         // [N+B, nch] workspace
+};
+
+hipError_t launch_sampler(const SampleParams& p, bool vec4, int walk_threads, hipStream_t stream,
+                          hipEvent_t ev_start, hipEvent_t ev_stop);
+
+}  // namespace sv
