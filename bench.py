@@ -1,0 +1,297 @@
+"""Throughput of one speculative-decoding verification step on one MI355X.
+
+A step is one spec_verify_step call over one batch: tree preprocessing,
+tree-masked GQA attention of every draft node against its request's KV cache
+(one layer), the row-statistics pass over every target-logit row, and the
+rejection-sampling tree walk that emits the accepted path plus a bonus token.
+All inputs are synthetic, seeded, and resident in HBM before the timed region.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Prints one JSON line: verified draft tokens/s (sum of T_b over the batch per
+second), the roofline position of the dominant kernel (algorithmic bytes over
+its HIP-event-timed duration, against the 8 TB/s HBM3E peak), and the fp64 CPU
+oracle timed on a bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+DEFAULT_WORKLOAD = "c5_super_tree"
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = {
+    "attn_mfma_kernel": "speculative_decoding_verification_16_amd/csrc/sv_attn.hip",
+    "row_stats_kernel": "speculative_decoding_verification_16_amd/csrc/sv_sample.hip",
+}
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="wall-clock budget of the oracle's CPU-baseline sample (0 = skip)")
+    ap.add_argument("--no-events", action="store_true", help="time without the per-kernel HIP events")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES three times (calibrates the HBM "
+                         "byte counters of rocprofv3 against a kernel of known traffic) and exit")
+    return ap.parse_args()
+
+
+def copy_probe(nbytes: int):
+    import torch
+
+    n = nbytes // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / 3
+    print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4,
+                      "copy_GB_s": round(2 * n * 4 / dt / 1e9, 1)}), flush=True)
+
+
+def source_digest(rel: str) -> str:
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def counter_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of this
+    kernel and workload, or None when there is none or the kernel's source has
+    changed since the counters were taken."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_pmc.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_src = re.search(r"source_sha256_16:\s*([0-9a-f]{16})", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_src or not m_bytes:
+        return None
+    if m_src.group(1) != source_digest(KERNEL_SOURCES[kernel]):
+        return None
+    return float(m_bytes.group(1))
+
+
+def attention_bytes(w) -> float:
+    """Algorithmic bytes of one attention launch: every K and V slot a node can
+    see (context + draft slots) once, the queries once, the fp32 outputs once."""
+    e = 2 if w["dtype"] == "bf16" else 4
+    kv = 0
+    for b in range(w["B"]):
+        T = int(w["cu_nodes"][b + 1] - w["cu_nodes"][b])
+        if T > 0:
+            kv += w["Hkv"] * (int(w["ctx_len"][b]) + T) * w["D"] * 2 * e
+    return float(kv + w["N"] * w["Hq"] * w["D"] * (e + 4))
+
+
+def attention_flops(w) -> float:
+    """4 D flops per (query row, visible key): QK^T and PV."""
+    tot = 0
+    for b in range(w["B"]):
+        n0, n1 = int(w["cu_nodes"][b]), int(w["cu_nodes"][b + 1])
+        par = w["parent"][n0:n1]
+        depth = [0] * (n1 - n0)
+        for j in range(n1 - n0):
+            depth[j] = 1 + (depth[par[j]] if par[j] >= 0 else 0)
+        tot += sum(int(w["ctx_len"][b]) + d for d in depth)
+    return float(4 * w["D"] * w["Hq"] * tot)
+
+
+def row_stats_bytes(w) -> float:
+    """Algorithmic bytes of the row-statistics pass: each target-logit row once
+    (fp32) plus its 16-byte per-chunk statistics."""
+    rows = w["N"] + w["B"]
+    nch = (w["V"] + 4095) // 4096
+    return float(rows * w["V"] * 4 + rows * nch * 16)
+
+
+def cpu_baseline(w, budget_s: float):
+    """The fp64 oracle (attention of every (node, head) of a request, then the
+    verification walk) over whole requests in order until the budget is spent.
+    Returns verified draft tokens/s of that sample, the thread count and a
+    description."""
+    import numpy as np
+
+    import oracle
+
+    def bits(t):
+        import torch
+        if t.dtype == torch.bfloat16:
+            return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        return t.contiguous().cpu().numpy()
+
+    try:
+        threads = min(16, len(os.sched_getaffinity(0)))
+    except AttributeError:
+        threads = min(16, os.cpu_count() or 1)
+    cu, par, ctx = w["cu_nodes"], w["parent"], w["ctx_len"]
+    nodes_done, req_done, spent = 0, 0, 0.0
+    chunk = 4
+    while req_done < w["B"] and spent < budget_s:
+        b0, b1 = req_done, min(w["B"], req_done + chunk)
+        n0, n1 = int(cu[b0]), int(cu[b1])
+        r0, r1 = n0 + b0, n1 + b1
+        sub_cu = (cu[b0:b1 + 1] - cu[b0]).astype(np.int32)
+        q = bits(w["q"][n0:n1])
+        k = bits(w["k_cache"][b0:b1])
+        v = bits(w["v_cache"][b0:b1])
+        lg = w["logits"][r0:r1].cpu().numpy()
+        qq = w["draft_probs"][r0:r1].cpu().numpy()
+        toks = w["draft_tokens"][n0:n1].cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.attention(q, k, v, ctx[b0:b1], sub_cu, par[n0:n1], Hq=w["Hq"], Hkv=w["Hkv"], dtype=w["dtype"],
+                         nthreads=threads)
+        oracle.verify(sub_cu, par[n0:n1], toks, lg, qq, temperature=w["temperature"], seed=w["seed"],
+                      request_id=np.arange(b0, b1, dtype=np.uint32), nthreads=threads)
+        spent += time.perf_counter() - t0
+        nodes_done += n1 - n0
+        req_done = b1
+    desc = (f"first {req_done} of {w['B']} requests ({nodes_done} draft nodes): fp64 attention of every "
+            f"(node, query head) plus the verification walk, {spent:.1f} s")
+    return nodes_done / spent, threads, desc
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the verification step shards by request "
+              "with no inter-GPU traffic, and this build measures one GPU's share.", file=sys.stderr)
+        sys.exit(2)
+
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
+
+    import torch
+
+    import speculative_decoding_verification_16_amd as sv
+    from workloads import generate, get_config
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    sv.load_library()  # fails loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    cfg = get_config(args.workload)
+    w = generate(cfg, dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.Stream()  # default priority
+    with torch.cuda.stream(stream):
+        a = sv.AttnCall(w["q"], w["k_cache"], w["v_cache"], w["ctx_len_t"], w["cu_nodes_t"], parent=w["parent_t"],
+                        max_nodes=w["max_T"])
+        s = sv.SampleCall(a.keep["cu"], w["parent_t"], w["draft_tokens"], w["logits"], w["draft_probs"],
+                          temperature=cfg.temperature, seed=w["seed"], max_nodes=w["max_T"], residual_passes=True)
+        step = sv.StepCall(a, s)
+    torch.cuda.synchronize()
+
+    K, W = args.steps, args.warmup
+    use_events = not args.no_events
+    ev = None
+    if use_events:
+        mk = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+        ev = [(mk(), mk(), mk(), mk()) for _ in range(K)]
+
+    for _ in range(W):
+        a.set_prof_events(None, None)
+        s.set_prof_events(None, None)
+        step(stream)
+    stream.synchronize()
+    torch.cuda.synchronize()
+
+    t0 = time.perf_counter()
+    for i in range(K):
+        if use_events:
+            a.set_prof_events(ev[i][0], ev[i][1])
+            s.set_prof_events(ev[i][2], ev[i][3])
+        step(stream)
+    stream.synchronize()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    a.set_prof_events(None, None)
+    s.set_prof_events(None, None)
+
+    status = int(s.status.item()) | int(a.status.item())
+    if status:
+        print(f"device status bits set: {sv.status_names(status)}", file=sys.stderr)
+        sys.exit(1)
+
+    ms = elapsed / K * 1e3
+    value = w["N"] * K / elapsed
+    acc = s.accept_len.double()
+    passes = s.passes.double()
+
+    kernels = {}
+    attn_b, attn_f = attention_bytes(w), attention_flops(w)
+    rs_b = row_stats_bytes(w)
+    if use_events:
+        attn_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+        rs_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / K
+        attn_name = "attn_mfma_kernel" if w["dtype"] == "bf16" else "attn_valu_kernel"
+        kernels[attn_name] = {"us": attn_ms * 1e3, "alg_bytes": attn_b, "GB_s": attn_b / attn_ms / 1e6,
+                              "TFLOP_s": attn_f / attn_ms / 1e9}
+        kernels["row_stats_kernel"] = {"us": rs_ms * 1e3, "alg_bytes": rs_b, "GB_s": rs_b / rs_ms / 1e6}
+        rest_us = ms * 1e3 - attn_ms * 1e3 - rs_ms * 1e3
+        kernels["other(tree_prep+walk)"] = {"us": rest_us,
+                                            "residual_pass_bytes": float(passes.sum().item()) * 8 * w["V"]}
+        dom = max((k for k in kernels if "alg_bytes" in kernels[k]), key=lambda k: kernels[k]["us"])
+        dk = kernels[dom]
+        traffic = counter_traffic(dom, cfg.name)
+        roofline = {"kernel": dom, "bound": "hbm", "achieved": round(dk["GB_s"], 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(dk["GB_s"] / HBM_PEAK_GBS, 4),
+                    "traffic": traffic}
+    else:
+        roofline = None
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        v_cpu, threads, desc = cpu_baseline(w, args.cpu_seconds)
+        cpu = {"value": round(v_cpu, 2), "unit": "verified draft tokens/s", "cores": threads, "kind": "oracle",
+               "sample": desc}
+
+    line = {
+        "metric": "verified draft tokens/sec",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16+f32" if w["dtype"] == "bf16" else "f32",
+        "data": "synthetic (seeded; no dataset, no model weights)",
+        "config": {"workload": cfg.name, "B": w["B"], "draft_nodes": w["N"], "max_T": w["max_T"], "L": cfg.L,
+                   "Hq": cfg.Hq, "Hkv": cfg.Hkv, "D": cfg.D, "kv_dtype": cfg.dtype, "V": cfg.V,
+                   "temperature": cfg.temperature},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": {k: {kk: (round(vv, 2) if isinstance(vv, float) else vv) for kk, vv in d.items()}
+                    for k, d in kernels.items()},
+        "walk": {"mean_accept_len": round(float(acc.mean().item()), 4),
+                 "emitted_tokens_per_s": round(float((acc + 1).sum().item()) * K / elapsed, 1),
+                 "residual_passes_per_step": int(passes.sum().item())},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -61,7 +61,7 @@ def test_attention_explicit_mask_matches_parent():
             x, m = j, 0
             while x >= 0:
                 m |= 1 << x
-                x = par[x]
+                x = int(par[x])
             anc[n0 + j] = m
     anc_t = torch.from_numpy(anc.view(np.int64)).cuda()
     out_mask = sv.attn(w["q"], w["k_cache"], w["v_cache"], w["ctx_len_t"], w["cu_nodes_t"], anc_mask=anc_t,
