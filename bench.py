@@ -36,6 +36,41 @@ KERNEL_SOURCES = {
 }
 
 
+class HipEvents:
+    """Timing events created and read through the HIP runtime torch has loaded
+    (the library records them on its own stream, outside torch's bookkeeping)."""
+
+    def __init__(self, n: int):
+        import ctypes
+
+        import torch  # noqa: F401  (loads the runtime that libamdhip64.so.7 resolves to)
+
+        self._ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            rc = self.hip.hipEventCreate(ctypes.byref(h))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed ({rc})")
+            self.ev.append(h.value)
+
+    def ms(self, a: int, b: int) -> float:
+        out = self._ct.c_float()
+        rc = self.hip.hipEventElapsedTime(self._ct.byref(out), self.ev[a], self.ev[b])
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(out.value)
+
+    def close(self):
+        for h in self.ev:
+            self.hip.hipEventDestroy(h)
+        self.ev = []
+
+
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -206,8 +241,8 @@ def main():
     use_events = not args.no_events
     ev = None
     if use_events:
-        mk = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-        ev = [(mk(), mk(), mk(), mk()) for _ in range(K)]
+        hev = HipEvents(4 * K)
+        ev = [tuple(hev.ev[4 * i:4 * i + 4]) for i in range(K)]
 
     for _ in range(W):
         a.set_prof_events(None, None)
@@ -242,8 +277,9 @@ def main():
     attn_b, attn_f = attention_bytes(w), attention_flops(w)
     rs_b = row_stats_bytes(w)
     if use_events:
-        attn_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
-        rs_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / K
+        attn_ms = sum(hev.ms(4 * i, 4 * i + 1) for i in range(K)) / K
+        rs_ms = sum(hev.ms(4 * i + 2, 4 * i + 3) for i in range(K)) / K
+        hev.close()
         attn_name = "attn_mfma_kernel" if w["dtype"] == "bf16" else "attn_valu_kernel"
         kernels[attn_name] = {"us": attn_ms * 1e3, "alg_bytes": attn_b, "GB_s": attn_b / attn_ms / 1e6,
                               "TFLOP_s": attn_f / attn_ms / 1e9}

@@ -104,8 +104,11 @@ def _stream_handle(stream):
 
 
 def _event_handle(ev):
+    """A hipEvent_t: a raw handle (int) or a torch.cuda.Event."""
     if ev is None:
         return None
+    if isinstance(ev, int):
+        return ctypes.c_void_p(ev)
     return ctypes.c_void_p(int(ev.cuda_event))
 
 

@@ -27,6 +27,10 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 int eff_max_nodes(int32_t m) { return m == 0 ? sv::kMaxNodes : m; }
 
+#ifndef SV_ATTN_NBUF
+#define SV_ATTN_NBUF 2  // key tiles in flight per attention workgroup
+#endif
+
 // ---- attention -------------------------------------------------------------
 sv_status check_attn(const sv_attn_args* a) {
   if (!a) return fail(SV_ERR_INVALID_ARG, "attn args is NULL");
@@ -64,11 +68,11 @@ sv::AttnPlan plan_attn(const sv_attn_args* a) {
   const int rmax = G * eff_max_nodes(a->max_nodes);
   pl.mfma = a->dtype == SV_BF16;
   if (pl.mfma) {
-    pl.rows_per_wg = rmax <= 64 ? 64 : rmax <= 128 ? 128 : 256;
-    pl.rbw = pl.rows_per_wg == 256 ? 2 : 1;
+    pl.rows_per_wg = 64;
+    pl.nbuf = SV_ATTN_NBUF;
   } else {
     pl.rows_per_wg = 8;
-    pl.rbw = 0;
+    pl.nbuf = 0;
   }
   pl.n_rowgroups = (rmax + pl.rows_per_wg - 1) / pl.rows_per_wg;
   const int64_t max_splits_len = a->Lcap / 64 > 0 ? a->Lcap / 64 : 1;
@@ -212,6 +216,8 @@ sv_status run_attn(const sv_attn_args* a, char* ws, const WsLayout& w, hipStream
   p.ml_part = pl.splits > 1 ? (float2*)(ws + w.ml_part) : nullptr;
   p.splits = pl.splits;
   p.rows_per_wg = pl.rows_per_wg;
+  p.n_rowgroups = pl.n_rowgroups;
+  p.n_jobs = a->B * a->Hkv * pl.splits;
   const float scale = a->scale > 0.f ? a->scale : (float)(1.0 / sqrt((double)a->D));
   p.scale_log2 = (float)((double)scale * 1.4426950408889634);
   p.status = a->status;

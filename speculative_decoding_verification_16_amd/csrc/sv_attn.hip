@@ -80,12 +80,22 @@ __device__ __forceinline__ int vt_pos(int kappa) {
 }
 __device__ __forceinline__ int vt_sw(int d) { return (d ^ (d >> 2)) & 7; }
 
-// NW waves per workgroup, RBW 16-row blocks per wave: 16 * RBW * NW rows.
-// WPE: waves per SIMD the register budget is sized for.
-template <int D, int RBW, int NW, int WPE>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE)))
+// One workgroup = 4 waves = 64 query rows (one 16-row block per wave) of one
+// (request, KV head, KV split). Trees with more rows per KV head take several
+// row groups that stream the same keys; the linear block id is decoded so
+// that all row groups of one (request, KV head, split) land on the same XCD
+// (blocks go to XCDs round-robin by id) back to back, and their repeated key
+// reads are served by that XCD's L2.
+//
+// Memory pipeline: NBUF key tiles are in flight in registers (buffer loads
+// issued NBUF tiles ahead); each tile is written to LDS (K as is, V
+// transposed), consumed by the MFMAs, and its registers are refilled with the
+// tile NBUF positions later. Streaming decode attention is bound by HBM
+// latency x bytes in flight, so the ring depth is what sets the bandwidth.
+template <int D, int NBUF>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_mfma_kernel(AttnParams p) {
-  constexpr int NT = 64 * NW;        // threads
+  constexpr int NT = 256;            // threads
   constexpr int KT = 64;             // keys per tile
   constexpr int KS = D / 32;         // k-steps of S^T (32 head dims each)
   constexpr int DB = D / 16;         // 16-wide blocks of the output head dim
@@ -95,8 +105,16 @@ void attn_mfma_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * D];
   __shared__ __attribute__((aligned(16))) uint32_t Vt[D * KT / 2];
 
-  const int b = blockIdx.z, g = blockIdx.y;
-  const int rg = blockIdx.x / p.splits, split = blockIdx.x % p.splits;
+  // XCD-aware decode: id = ((job / 8) * n_rowgroups + rg) * 8 + job % 8
+  const int lin = blockIdx.x;
+  const int qd = lin >> 3;
+  const int rg = qd % p.n_rowgroups;
+  const int job = (qd / p.n_rowgroups) * 8 + (lin & 7);
+  if (job >= p.n_jobs) return;
+  const int split = job % p.splits;
+  const int bg = job / p.splits;
+  const int g = bg % p.Hkv, b = bg / p.Hkv;
+
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g4 = lane >> 4;
@@ -106,11 +124,11 @@ void attn_mfma_kernel(AttnParams p) {
   if (n0 < 0 || T < 0 || T > p.max_nodes || n1 > p.N) return;  // flagged by tree prep / host
   const int L = p.ctx_len[b];
   if (L < 0 || (int64_t)L + T > p.Lcap) {
-    if (tid == 0 && blockIdx.x == 0 && g == 0) flag(p.status, kStCtx);
+    if (tid == 0 && rg == 0 && split == 0 && g == 0) flag(p.status, kStCtx);
     return;
   }
   const int R = p.G * T;
-  const int row0 = rg * p.rows_per_wg;
+  const int row0 = rg * 64;
   if (row0 >= R) return;
   const int nkeys = L + T;
   const int kchunk = ((nkeys + p.splits - 1) / p.splits + KT - 1) / KT * KT;
@@ -118,34 +136,26 @@ void attn_mfma_kernel(AttnParams p) {
   const int ke = min(nkeys, kb + kchunk);
   const int NH = p.N * p.Hq;
 
-  // rows of this lane: r = row0 + 16 * (wave + NW i) + l16
-  bf16x8_t qf[RBW][KS];
-  uint64_t amask[RBW];
-  int orow[RBW];  // packed (node, q head) index, -1 if the row does not exist
-  bool rb_any[RBW];
+  // the 16 rows of this wave: r = row0 + 16 * wave + l16
+  const int rbase = row0 + 16 * wave;
+  const bool rb_any = rbase < R;
+  const int r = rbase + l16;
+  bf16x8_t qf[KS];
+  uint64_t amask = 0;
+  int orow = -1;  // packed (node, q head) index, -1 if the row does not exist
 #pragma unroll
-  for (int i = 0; i < RBW; ++i) {
-    const int rbase = row0 + 16 * (wave + NW * i);
-    rb_any[i] = rbase < R;
-    const int r = rbase + l16;
-    orow[i] = -1;
-    amask[i] = 0;
+  for (int ks = 0; ks < KS; ++ks) qf[ks] = bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+  if (r < R) {
+    const int j = r / p.G, hh = r - j * p.G;
+    orow = (n0 + j) * p.Hq + g * p.G + hh;
+    amask = p.anc[n0 + j];
+    const uint16_t* qp = (const uint16_t*)p.q + (int64_t)orow * D;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[i][ks] = bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
-    if (r < R) {
-      const int j = r / p.G, hh = r - j * p.G;
-      orow[i] = (n0 + j) * p.Hq + g * p.G + hh;
-      amask[i] = p.anc[n0 + j];
-      const uint16_t* qp = (const uint16_t*)p.q + (int64_t)orow[i] * D;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qf[i][ks] = *(const bf16x8_t*)(qp + 32 * ks + 8 * g4);
-    }
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = *(const bf16x8_t*)(qp + 32 * ks + 8 * g4);
   }
 
   if (kb >= ke) {  // empty split: contributes nothing to the merge
-#pragma unroll
-    for (int i = 0; i < RBW; ++i)
-      if (orow[i] >= 0 && g4 == 0) p.ml_part[(int64_t)split * NH + orow[i]] = make_float2(-INFINITY, 0.f);
+    if (orow >= 0 && g4 == 0) p.ml_part[(int64_t)split * NH + orow] = make_float2(-INFINITY, 0.f);
     return;
   }
 
@@ -168,91 +178,107 @@ void attn_mfma_kernel(AttnParams p) {
     koff[i] = ((c / UNITS) * D + 8 * (c % UNITS)) * 2;
     voff[i] = ((c / (D / 4)) * 2 * D + 4 * (c % (D / 4))) * 2;
   }
-  i32x4_t kreg[PER_THREAD];
-  i32x2_t vreg[PER_THREAD][2];
-  auto load_tile = [&](int t0) {
-    const int so = t0 * D * 2;
+  i32x4_t kreg[NBUF][PER_THREAD];
+  i32x2_t vreg[NBUF][PER_THREAD][2];
+
+  f32x4_t o[DB];
+  float m = -INFINITY, l = 0.f;
 #pragma unroll
-    for (int i = 0; i < PER_THREAD; ++i) {
-      kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(krs, koff[i], so, 0);
-      vreg[i][0] = __builtin_amdgcn_raw_buffer_load_b64(vrs, voff[i], so, 0);
-      vreg[i][1] = __builtin_amdgcn_raw_buffer_load_b64(vrs, voff[i] + D * 2, so, 0);
-    }
-  };
-  auto store_tile = [&]() {
+  for (int db = 0; db < DB; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // prologue: the first NBUF tiles
 #pragma unroll
-    for (int i = 0; i < PER_THREAD; ++i) {
-      const int c = tid + NT * i;
-      const int kk = c / UNITS, dc = c % UNITS;
-      *(i32x4_t*)(Ks + kk * D + 8 * (dc ^ (kk & 7))) = kreg[i];
-      const int kp = c / (D / 4), dq = c % (D / 4);
-      const int pos = vt_pos(2 * kp);  // even key; its odd partner sits at pos + 1
-      const uint32_t ax = (uint32_t)vreg[i][0][0], ay = (uint32_t)vreg[i][0][1];
-      const uint32_t bx = (uint32_t)vreg[i][1][0], by = (uint32_t)vreg[i][1][1];
-      const uint32_t w[4] = {(ax & 0xffffu) | (bx << 16), (ax >> 16) | (bx & 0xffff0000u),
-                             (ay & 0xffffu) | (by << 16), (ay >> 16) | (by & 0xffff0000u)};
+  for (int s = 0; s < NBUF; ++s) {
+    const int so = (kb + s * KT) * D * 2;
+    if (kb + s * KT < ke) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int d = 4 * dq + e;
-        Vt[d * 32 + (((pos >> 3) ^ vt_sw(d)) << 2) + ((pos >> 1) & 3)] = w[e];
+      for (int i = 0; i < PER_THREAD; ++i) {
+        kreg[s][i] = __builtin_amdgcn_raw_buffer_load_b128(krs, koff[i], so, 0);
+        vreg[s][i][0] = __builtin_amdgcn_raw_buffer_load_b64(vrs, voff[i], so, 0);
+        vreg[s][i][1] = __builtin_amdgcn_raw_buffer_load_b64(vrs, voff[i] + D * 2, so, 0);
       }
     }
-  };
-
-  f32x4_t o[RBW][DB];
-  float m[RBW], l[RBW];
-#pragma unroll
-  for (int i = 0; i < RBW; ++i) {
-    m[i] = -INFINITY;
-    l[i] = 0.f;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) o[i][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  load_tile(kb);
-  for (int t0 = kb; t0 < ke; t0 += KT) {
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (t0 + KT < ke) load_tile(t0 + KT);
-    const bool full = (t0 + KT <= ke) && (t0 + KT <= L);
-
-    // S^T for every owned row block; each K fragment is read from LDS once
-    f32x4_t s[RBW][4];
+  for (int tb = kb; tb < ke; tb += NBUF * KT) {
 #pragma unroll
-    for (int i = 0; i < RBW; ++i)
+    for (int s = 0; s < NBUF; ++s) {
+      const int t0 = tb + s * KT;
+      if (t0 >= ke) break;
+      __syncthreads();  // the previous tile's LDS reads are done
 #pragma unroll
-      for (int st = 0; st < 4; ++st) s[i][st] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-    for (int st = 0; st < 4; ++st) {
-      const int key = 16 * st + l16;
+      for (int i = 0; i < PER_THREAD; ++i) {
+        const int c = tid + NT * i;
+        const int kk = c / UNITS, dc = c % UNITS;
+        *(i32x4_t*)(Ks + kk * D + 8 * (dc ^ (kk & 7))) = kreg[s][i];
+        const int kp = c / (D / 4), dq = c % (D / 4);
+        const int pos = vt_pos(2 * kp);  // even key; its odd partner sits at pos + 1
+        const uint32_t ax = (uint32_t)vreg[s][i][0][0], ay = (uint32_t)vreg[s][i][0][1];
+        const uint32_t bx = (uint32_t)vreg[s][i][1][0], by = (uint32_t)vreg[s][i][1][1];
+        const uint32_t w[4] = {(ax & 0xffffu) | (bx << 16), (ax >> 16) | (bx & 0xffff0000u),
+                               (ay & 0xffffu) | (by << 16), (ay >> 16) | (by & 0xffff0000u)};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8_t a = *(const bf16x8_t*)(Ks + key * D + 8 * ((4 * ks + g4) ^ (key & 7)));
-#pragma unroll
-        for (int i = 0; i < RBW; ++i)
-          if (rb_any[i]) s[i][st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[i][ks], s[i][st], 0, 0, 0);
+        for (int e = 0; e < 4; ++e) {
+          const int d = 4 * dq + e;
+          Vt[d * 32 + (((pos >> 3) ^ vt_sw(d)) << 2) + ((pos >> 1) & 3)] = w[e];
+        }
       }
-    }
-
-    // online softmax (log2 domain), P^T packed as the PV B operand
-    bf16x8_t pk[RBW][2];
+      __syncthreads();
+      // refill this ring slot with the tile NBUF positions ahead
+      const int tn = t0 + NBUF * KT;
+      if (tn < ke) {
+        const int so = tn * D * 2;
 #pragma unroll
-    for (int i = 0; i < RBW; ++i) {
-      if (!rb_any[i]) continue;
+        for (int i = 0; i < PER_THREAD; ++i) {
+          kreg[s][i] = __builtin_amdgcn_raw_buffer_load_b128(krs, koff[i], so, 0);
+          vreg[s][i][0] = __builtin_amdgcn_raw_buffer_load_b64(vrs, voff[i], so, 0);
+          vreg[s][i][1] = __builtin_amdgcn_raw_buffer_load_b64(vrs, voff[i] + D * 2, so, 0);
+        }
+      }
+      if (!rb_any) continue;  // this wave has no rows: it only helps to stream the tiles
+      const bool full = (t0 + KT <= ke) && (t0 + KT <= L);
+      // visibility of the tile's 64 keys for this lane's row, built without
+      // branches: context keys, then the row's ancestor-or-self draft slots,
+      // cut at the split end (the short-circuit form of this test was
+      // miscompiled by the ROCm 7.2 compiler under this register budget)
+      uint64_t vis64 = ~0ull;
+      if (!full) {
+        const int dl = L - t0;  // tile bit of the first draft slot
+        const uint64_t ctx_bits = dl >= 64 ? ~0ull : (dl <= 0 ? 0ull : ((1ull << dl) - 1ull));
+        const uint64_t drf_bits = dl >= 64 ? 0ull : (dl >= 0 ? (amask << dl) : (-dl >= 64 ? 0ull : (amask >> -dl)));
+        const int dv = ke - t0;
+        const uint64_t valid = dv >= 64 ? ~0ull : ((1ull << dv) - 1ull);
+        vis64 = (ctx_bits | drf_bits) & valid;
+      }
+
+      // S^T for this row block
+      f32x4_t sc[4];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) sc[st] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const int key = 16 * st + l16;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8_t a = *(const bf16x8_t*)(Ks + key * D + 8 * ((4 * ks + g4) ^ (key & 7)));
+          sc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], sc[st], 0, 0, 0);
+        }
+      }
+
+      // online softmax (log2 domain), P^T packed as the PV B operand
       float x[16];
 #pragma unroll
       for (int st = 0; st < 4; ++st)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[4 * st + e] = s[i][st][e] * p.scale_log2;
-      if (!full) {
+        for (int e = 0; e < 4; ++e) x[4 * st + e] = sc[st][e] * p.scale_log2;
+      {
+        const uint64_t lane_bits = vis64 >> (4 * g4);
 #pragma unroll
         for (int st = 0; st < 4; ++st)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int kappa = t0 + 16 * st + 4 * g4 + e;
-            const bool vis = kappa < ke && (kappa < L || ((amask[i] >> (kappa - L)) & 1ull));
-            if (!vis) x[4 * st + e] = -INFINITY;
+            const bool vis = (lane_bits >> (16 * st + e)) & 1ull;
+            x[4 * st + e] = vis ? x[4 * st + e] : -INFINITY;
           }
       }
       float mx = x[0];
@@ -260,25 +286,25 @@ void attn_mfma_kernel(AttnParams p) {
       for (int t = 1; t < 16; ++t) mx = fmaxf(mx, x[t]);
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(m[i], mx);
+      const float mnew = fmaxf(m, mx);
       const float msub = mnew == -INFINITY ? 0.f : mnew;
-      const float alpha = exp2f(m[i] - msub);  // m = -inf (nothing seen yet) -> 0
-      float pv[16];
+      const float alpha = exp2f(m - msub);  // m = -inf (nothing seen yet) -> 0
       float lsum = 0.f;
 #pragma unroll
       for (int t = 0; t < 16; ++t) {
-        pv[t] = exp2f(x[t] - msub);
-        lsum += pv[t];
+        x[t] = exp2f(x[t] - msub);
+        lsum += x[t];
       }
-      l[i] = l[i] * alpha + lsum;
-      m[i] = mnew;
+      l = l * alpha + lsum;
+      m = mnew;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) o[i][db] *= alpha;
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      bf16x8_t pk[2];
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
         // element 4h + e  <->  sub-tile st = 2 k2 + h, value e
-        const float* lo = pv + 4 * (2 * k2);
-        const float* hi = pv + 4 * (2 * k2 + 1);
+        const float* lo = x + 4 * (2 * k2);
+        const float* hi = x + 4 * (2 * k2 + 1);
         const uint32_t w0 = pack_bf16x2(lo[0], lo[1]), w1 = pack_bf16x2(lo[2], lo[3]);
         const uint32_t w2 = pack_bf16x2(hi[0], hi[1]), w3 = pack_bf16x2(hi[2], hi[3]);
         bf16x8_t v;
@@ -286,48 +312,43 @@ void attn_mfma_kernel(AttnParams p) {
         v[2] = (short)(w1 & 0xffff); v[3] = (short)(w1 >> 16);
         v[4] = (short)(w2 & 0xffff); v[5] = (short)(w2 >> 16);
         v[6] = (short)(w3 & 0xffff); v[7] = (short)(w3 >> 16);
-        pk[i][k2] = v;
+        pk[k2] = v;
       }
-    }
 
-    // O^T += V^T P^T; each V fragment is read from LDS once
+      // O^T += V^T P^T
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const int d = 16 * db + l16;
+      for (int db = 0; db < DB; ++db) {
+        const int d = 16 * db + l16;
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        const bf16x8_t a = *(const bf16x8_t*)(Vt + d * 32 + (((4 * k2 + g4) ^ vt_sw(d)) << 2));
-#pragma unroll
-        for (int i = 0; i < RBW; ++i)
-          if (rb_any[i]) o[i][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pk[i][k2], o[i][db], 0, 0, 0);
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const bf16x8_t a = *(const bf16x8_t*)(Vt + d * 32 + (((4 * k2 + g4) ^ vt_sw(d)) << 2));
+          o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pk[k2], o[db], 0, 0, 0);
+        }
       }
     }
   }
 
+  if (!rb_any) return;
   // row sums across the four lane groups that share a row, then write
+  float lt = l + __shfl_xor(l, 16);
+  lt += __shfl_xor(lt, 32);
+  if (orow < 0) return;
+  if (p.splits == 1) {
+    const float inv = 1.0f / lt;
+    float* op = p.out + (int64_t)orow * D + 4 * g4;
 #pragma unroll
-  for (int i = 0; i < RBW; ++i) {
-    if (!rb_any[i]) continue;
-    float lt = l[i] + __shfl_xor(l[i], 16);
-    lt += __shfl_xor(lt, 32);
-    if (orow[i] < 0) continue;
-    if (p.splits == 1) {
-      const float inv = 1.0f / lt;
-      float* op = p.out + (int64_t)orow[i] * D + 4 * g4;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const f32x4_t v = o[i][db] * inv;
-        *(float4*)(op + 16 * db) = make_float4(v[0], v[1], v[2], v[3]);
-      }
-    } else {
-      float* op = p.o_part + ((int64_t)split * NH + orow[i]) * D + 4 * g4;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const f32x4_t v = o[i][db];
-        *(float4*)(op + 16 * db) = make_float4(v[0], v[1], v[2], v[3]);
-      }
-      if (g4 == 0) p.ml_part[(int64_t)split * NH + orow[i]] = make_float2(m[i], lt);
+    for (int db = 0; db < DB; ++db) {
+      const f32x4_t v = o[db] * inv;
+      *(float4*)(op + 16 * db) = make_float4(v[0], v[1], v[2], v[3]);
     }
+  } else {
+    float* op = p.o_part + ((int64_t)split * NH + orow) * D + 4 * g4;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const f32x4_t v = o[db];
+      *(float4*)(op + 16 * db) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+    if (g4 == 0) p.ml_part[(int64_t)split * NH + orow] = make_float2(m, lt);
   }
 }
 
@@ -407,8 +428,11 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
     for (int d = 0; d < D; ++d) s += Qs[rl][d] * Ks[kl][d];
     float x = s * p.scale_log2;
     const int key = t0 + kl;
-    const bool vis = key < ke && (key < L || ((amask >> (key - L)) & 1ull));
-    if (!vis) x = -INFINITY;
+    // branch-free visibility: context key, or an ancestor-or-self draft slot
+    const int rel = key - L;
+    const bool anc_bit = ((amask >> (rel & 63)) & 1ull) != 0;
+    const bool vis = (key < ke) & ((key < L) | ((rel >= 0) & anc_bit));
+    x = vis ? x : -INFINITY;
     float mx = x;
 #pragma unroll
     for (int o2 = 16; o2 > 0; o2 >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o2));
@@ -480,23 +504,24 @@ hipError_t launch_tree_prep(int B, int N, int max_nodes, const int32_t* cu_nodes
   return hipGetLastError();
 }
 
-// rows per workgroup 64 / 128 / 256 -> (RBW, NW) = (1,4) / (1,8) / (2,8)
 template <int D>
-static void launch_mfma_d(const AttnParams& p, int rows_per_wg, dim3 grid, hipStream_t stream) {
-  if (rows_per_wg <= 64) attn_mfma_kernel<D, 1, 4, 3><<<grid, dim3(256), 0, stream>>>(p);
-  else if (rows_per_wg <= 128) attn_mfma_kernel<D, 1, 8, 3><<<grid, dim3(512), 0, stream>>>(p);
-  else attn_mfma_kernel<D, 2, 8, 2><<<grid, dim3(512), 0, stream>>>(p);
+static void launch_mfma_d(const AttnParams& p, int nbuf, dim3 grid, hipStream_t stream) {
+  if (nbuf <= 2) attn_mfma_kernel<D, 2><<<grid, dim3(256), 0, stream>>>(p);
+  else attn_mfma_kernel<D, 3><<<grid, dim3(256), 0, stream>>>(p);
 }
 
 hipError_t launch_attention(const AttnParams& p, const AttnPlan& plan, bool bf16, hipStream_t stream,
                             hipEvent_t ev_start, hipEvent_t ev_stop) {
   if (p.B <= 0 || p.N <= 0) return hipSuccess;
-  const dim3 grid(plan.n_rowgroups * plan.splits, p.Hkv, p.B);
   if (ev_start) (void)hipEventRecord(ev_start, stream);
   if (bf16) {
-    if (p.D == 128) launch_mfma_d<128>(p, plan.rows_per_wg, grid, stream);
-    else launch_mfma_d<64>(p, plan.rows_per_wg, grid, stream);
+    // 1-D grid, decoded XCD-aware inside the kernel
+    const int64_t groups = ((int64_t)p.n_jobs + 7) / 8;
+    const dim3 grid((unsigned)(groups * 8 * p.n_rowgroups));
+    if (p.D == 128) launch_mfma_d<128>(p, plan.nbuf, grid, stream);
+    else launch_mfma_d<64>(p, plan.nbuf, grid, stream);
   } else {
+    const dim3 grid(plan.n_rowgroups * plan.splits, p.Hkv, p.B);
     if (p.D == 128) attn_valu_kernel<128><<<grid, dim3(256), 0, stream>>>(p);
     else attn_valu_kernel<64><<<grid, dim3(256), 0, stream>>>(p);
   }

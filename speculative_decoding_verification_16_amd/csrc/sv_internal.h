@@ -26,13 +26,15 @@ struct AttnParams {
   float2* ml_part;         // [splits, N*Hq] (running max in log2 units, sum)
   int32_t splits;
   int32_t rows_per_wg;     // query rows (node, head-in-group) per workgroup
+  int32_t n_rowgroups;     // workgroups along the rows of one (request, KV head, split)
+  int32_t n_jobs;          // B * Hkv * splits
   float scale_log2;        // softmax scale * log2(e)
   int32_t* status;
 };
 
 struct AttnPlan {
   bool mfma;        // bf16 MFMA path (else fp32 VALU path)
-  int rbw;          // MFMA path: 16-row blocks per wave
+  int nbuf;         // MFMA path: key tiles in flight per workgroup
   int rows_per_wg;
   int n_rowgroups;  // workgroups per (request, KV head, split) along rows
   int splits;
