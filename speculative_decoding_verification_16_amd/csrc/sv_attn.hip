@@ -21,6 +21,26 @@ typedef short bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// max over lanes l, l^16, l^32, l^48 (the four 16-lane rows of a wave) with
+// the gfx950 row-swap permutes instead of LDS-routed shuffles
+__device__ __forceinline__ float row_max4(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  v = fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+  const uint32_t w = __float_as_uint(v);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+  return fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+}
+__device__ __forceinline__ float row_sum4(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  v = __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+  const uint32_t w = __float_as_uint(v);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+  return __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+}
 
 // ---------------------------------------------------------------------------
 // Tree preprocessing: ancestor-or-self bitmask of every node. One wave per
@@ -265,13 +285,15 @@ void attn_mfma_kernel(AttnParams p) {
         }
       }
 
-      // online softmax (log2 domain), P^T packed as the PV B operand
+      // online softmax in the log2 domain: p = 2^(s * scale_log2 - m), the
+      // scale folded into one FMA, raw v_exp_f32 (arguments are <= 0, so only
+      // denormal results flush, which softmax weights below 2^-126 afford)
       float x[16];
 #pragma unroll
       for (int st = 0; st < 4; ++st)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[4 * st + e] = sc[st][e] * p.scale_log2;
-      {
+        for (int e = 0; e < 4; ++e) x[4 * st + e] = sc[st][e];
+      if (!full) {  // wave-uniform: only tiles that reach the draft slots or the split end
         const uint64_t lane_bits = vis64 >> (4 * g4);
 #pragma unroll
         for (int st = 0; st < 4; ++st)
@@ -284,35 +306,37 @@ void attn_mfma_kernel(AttnParams p) {
       float mx = x[0];
 #pragma unroll
       for (int t = 1; t < 16; ++t) mx = fmaxf(mx, x[t]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(m, mx);
+      // the row's 64 keys live in lanes l16, l16+16, l16+32, l16+48
+      mx = row_max4(mx);
+      const float mnew = fmaxf(m, mx * p.scale_log2);
       const float msub = mnew == -INFINITY ? 0.f : mnew;
-      const float alpha = exp2f(m - msub);  // m = -inf (nothing seen yet) -> 0
       float lsum = 0.f;
 #pragma unroll
       for (int t = 0; t < 16; ++t) {
-        x[t] = exp2f(x[t] - msub);
+        x[t] = __builtin_amdgcn_exp2f(fmaf(x[t], p.scale_log2, -msub));
         lsum += x[t];
       }
-      l = l * alpha + lsum;
-      m = mnew;
+      // rescale the running output only when some row's maximum moved
+      if (__any(mnew != m)) {
+        const float alpha = __builtin_amdgcn_exp2f(m - msub);  // m = -inf (nothing seen yet) -> 0
+        l *= alpha;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+        for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      }
+      l += lsum;
+      m = mnew;
       bf16x8_t pk[2];
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
-        // element 4h + e  <->  sub-tile st = 2 k2 + h, value e
+        // element 4h + e  <->  sub-tile st = 2 k2 + h, value e (RNE by v_cvt_pk_bf16_f32)
         const float* lo = x + 4 * (2 * k2);
         const float* hi = x + 4 * (2 * k2 + 1);
-        const uint32_t w0 = pack_bf16x2(lo[0], lo[1]), w1 = pack_bf16x2(lo[2], lo[3]);
-        const uint32_t w2 = pack_bf16x2(hi[0], hi[1]), w3 = pack_bf16x2(hi[2], hi[3]);
-        bf16x8_t v;
-        v[0] = (short)(w0 & 0xffff); v[1] = (short)(w0 >> 16);
-        v[2] = (short)(w1 & 0xffff); v[3] = (short)(w1 >> 16);
-        v[4] = (short)(w2 & 0xffff); v[5] = (short)(w2 >> 16);
-        v[6] = (short)(w3 & 0xffff); v[7] = (short)(w3 >> 16);
-        pk[k2] = v;
+        const bf16x2_t p01 = {(__bf16)lo[0], (__bf16)lo[1]}, p23 = {(__bf16)lo[2], (__bf16)lo[3]};
+        const bf16x2_t p45 = {(__bf16)hi[0], (__bf16)hi[1]}, p67 = {(__bf16)hi[2], (__bf16)hi[3]};
+        const uint32_t w0 = __builtin_bit_cast(uint32_t, p01), w1 = __builtin_bit_cast(uint32_t, p23);
+        const uint32_t w2 = __builtin_bit_cast(uint32_t, p45), w3 = __builtin_bit_cast(uint32_t, p67);
+        const i32x4_t wv = {(int)w0, (int)w1, (int)w2, (int)w3};
+        pk[k2] = __builtin_bit_cast(bf16x8_t, wv);
       }
 
       // O^T += V^T P^T
@@ -330,8 +354,7 @@ void attn_mfma_kernel(AttnParams p) {
 
   if (!rb_any) return;
   // row sums across the four lane groups that share a row, then write
-  float lt = l + __shfl_xor(l, 16);
-  lt += __shfl_xor(lt, 32);
+  const float lt = row_sum4(l);
   if (orow < 0) return;
   if (p.splits == 1) {
     const float inv = 1.0f / lt;
