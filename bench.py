@@ -324,7 +324,8 @@ def main():
                     for k, d in kernels.items()},
         "walk": {"mean_accept_len": round(float(acc.mean().item()), 4),
                  "emitted_tokens_per_s": round(float((acc + 1).sum().item()) * K / elapsed, 1),
-                 "residual_passes_per_step": int(passes.sum().item())},
+                 "residual_passes_per_step": int(passes.sum().item()),
+                 "max_residual_passes_per_request": int(passes.max().item())},
     }
     print(json.dumps(line), flush=True)
 

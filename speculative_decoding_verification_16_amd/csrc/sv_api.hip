@@ -98,7 +98,7 @@ sv::AttnPlan plan_attn(const sv_attn_args* a) {
 }
 
 struct WsLayout {
-  size_t anc = 0, o_part = 0, ml_part = 0, stats = 0, total = 0;
+  size_t anc = 0, o_part = 0, ml_part = 0, stats = 0, rowstats = 0, total = 0;
 };
 
 size_t attn_part_bytes(const sv_attn_args* a, const sv::AttnPlan& pl, size_t* ml) {
@@ -134,6 +134,8 @@ WsLayout layout(const sv_attn_args* a, const sv_sample_args* s) {
   if (s && s->B > 0) {
     w.stats = off;
     off += align_up(((size_t)s->total_nodes + s->B) * sample_nch(s) * sizeof(sv::ChunkStat));
+    w.rowstats = off;
+    off += align_up(((size_t)s->total_nodes + s->B) * sizeof(sv::RowStat));
   }
   w.total = off;
   return w;
@@ -254,12 +256,9 @@ sv_status run_sample(const sv_sample_args* s, char* ws, const WsLayout& w, hipSt
   p.residual_passes = s->residual_passes;
   p.status = s->status;
   p.stats = (sv::ChunkStat*)(ws + w.stats);
+  p.rowstats = (sv::RowStat*)(ws + w.rowstats);
   const bool vec4 = (s->V % 4 == 0) && aligned(s->target_logits, 16) && (!s->draft_probs || aligned(s->draft_probs, 16));
-  // a workgroup per request: wide enough to stream a whole row per residual pass
-  int threads = 64 * ((p.nch + 1) / 2);
-  if (threads < 64) threads = 64;
-  if (threads > 512) threads = 512;
-  hipError_t e = sv::launch_sampler(p, vec4, threads, st, (hipEvent_t)s->prof_start, (hipEvent_t)s->prof_stop);
+  hipError_t e = sv::launch_sampler(p, vec4, st, (hipEvent_t)s->prof_start, (hipEvent_t)s->prof_stop);
   if (e != hipSuccess) return hip_fail(e, "sampler launch");
   return SV_OK;
 }

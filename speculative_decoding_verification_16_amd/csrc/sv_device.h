@@ -22,6 +22,15 @@ struct ChunkStat {
 };
 static_assert(sizeof(ChunkStat) == 16, "ChunkStat layout");
 
+// Per-row normalisation of the target distribution, merged from the row's
+// chunk statistics: p(x) = exp2((logit - lmax) * log2(e) / T) / S.
+struct RowStat {
+  float lmax;   // largest raw logit of the row (-inf if none is finite)
+  int32_t arg;  // lowest index attaining lmax (greedy argmax)
+  double S;     // sum over the row of exp2((logit - lmax) * log2(e) / T)
+};
+static_assert(sizeof(RowStat) == 16, "RowStat layout");
+
 // Data-error bits (same values as SV_STATUS_* in the public header).
 constexpr int32_t kStTree = 0x01, kStPacking = 0x02, kStToken = 0x04, kStNonFinite = 0x08,
                   kStZeroResidual = 0x10, kStCtx = 0x20;
@@ -87,9 +96,11 @@ __device__ __forceinline__ double uniform01(uint64_t seed, uint32_t rid, uint32_
 
 // ---- target distribution ---------------------------------------------------
 // Unnormalised target weight of one logit relative to the row maximum:
-// exp((logit - lmax) / T) evaluated as exp2((logit - lmax) * log2(e)/T).
+// exp((logit - lmax) / T) evaluated as exp2((logit - lmax) * log2(e)/T) with
+// the hardware v_exp_f32 (the argument is <= 0; weights below 2^-126 flush to
+// zero, far below any probability the sampler can resolve).
 __device__ __forceinline__ float target_weight(float logit, float lmax, float c) {
-  return exp2f((logit - lmax) * c);
+  return __builtin_amdgcn_exp2f((logit - lmax) * c);
 }
 // p(x) as an fp32 value; every kernel that needs p uses exactly this.
 __device__ __forceinline__ float target_prob(float logit, float lmax, float c, float invS) {

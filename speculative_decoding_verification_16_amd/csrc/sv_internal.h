@@ -9,6 +9,7 @@
 namespace sv {
 
 struct ChunkStat;
+struct RowStat;
 
 // ---- attention ---------------------------------------------------------------
 struct AttnParams {
@@ -67,9 +68,10 @@ struct SampleParams {
   int32_t* residual_passes;
   int32_t* status;
   ChunkStat* stats;         // [N+B, nch] workspace
+  RowStat* rowstats;        // [N+B] workspace
 };
 
-hipError_t launch_sampler(const SampleParams& p, bool vec4, int walk_threads, hipStream_t stream,
-                          hipEvent_t ev_start, hipEvent_t ev_stop);
+hipError_t launch_sampler(const SampleParams& p, bool vec4, hipStream_t stream, hipEvent_t ev_start,
+                          hipEvent_t ev_stop);
 
 }  // namespace sv

@@ -13,7 +13,9 @@
 //     per 4096-token chunk the max logit, its first index and
 //     sum exp((logit - max)/T). That is all the walk needs to evaluate p at
 //     any token and to draw from p at a leaf.
-//  2. walk_kernel       -- one workgroup per request. It climbs down the tree
+//  2. row_finalize_kernel -- the per-row maximum, argmax and sum, merged from
+//     the chunk statistics.
+//  3. walk_kernel       -- one workgroup per request. It climbs down the tree
 //     doing the accept tests on gathered p(x), q(x). A residual mass is only
 //     computed when the walk actually rejects (a vocabulary pass over that
 //     one row, logits and q), so rows that are never rejected are read once,
@@ -95,96 +97,127 @@ __global__ __launch_bounds__(256) void row_stats_kernel(const float* __restrict_
   }
 }
 
-// Optional output of the p rows (tests and diagnostics): same grid as pass 1.
-template <bool VEC>
+// Pass 2: per-row normalisation merged from the chunk statistics (one wave
+// per row), so that the walk and the p-row output read 16 bytes per row.
+__global__ __launch_bounds__(256) void row_finalize_kernel(const ChunkStat* __restrict__ stats, int64_t rows,
+                                                           int nch, float c, RowStat* __restrict__ rs) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  float lmax, av;
+  double S;
+  int arg;
+  row_norm(stats + row * nch, nch, c, lmax, S, arg, av);
+  if (lane == 0) {
+    RowStat r;
+    r.lmax = lmax;
+    r.arg = arg;
+    r.S = S;
+    rs[row] = r;
+  }
+}
+
+// Optional output of the p rows (tests and diagnostics): one wave per
+// (row, chunk), every element evaluated exactly as the walk evaluates it.
 __global__ __launch_bounds__(256) void probs_kernel(const float* __restrict__ logits, int V, int64_t rows, int nch,
-                                                    float c, const ChunkStat* __restrict__ stats,
+                                                    float c, const RowStat* __restrict__ rs,
                                                     float* __restrict__ probs) {
   const int lane = threadIdx.x & 63;
   const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (item >= rows * nch) return;
   const int64_t row = item / nch;
   const int ch = (int)(item - row * nch);
-  float lmax, av;
-  double S;
-  int arg;
-  row_norm(stats + row * nch, nch, c, lmax, S, arg, av);
-  const float invS = (float)(1.0 / S);
+  const RowStat r = rs[row];
+  const float invS = (float)(1.0 / r.S);
   const float* src = logits + row * (int64_t)V;
   float* dst = probs + row * (int64_t)V;
   const int begin = ch * kChunk, end = min(V, begin + kChunk);
-  for (int idx = begin + lane; idx < end; idx += 64) dst[idx] = target_prob(src[idx], lmax, c, invS);
+  for (int idx = begin + lane; idx < end; idx += 64) dst[idx] = target_prob(src[idx], r.lmax, c, invS);
 }
 
 // ---------------------------------------------------------------------------
-// Walk helpers (whole workgroup).
+// Pass 3: the walk. One workgroup per request. Everything a decision needs
+// at the first level of a position (p and q at every drafted token, the row
+// normalisations) is gathered into LDS up front, in one round trip; every
+// thread then evaluates the same accept tests on the same LDS values and so
+// follows the same path without broadcasts. The whole workgroup joins the
+// vocabulary passes that rejections make (one per residual level) and the
+// final draw.
+
+constexpr int kWalkThreads = 512;
+constexpr int kWalkWaves = kWalkThreads / kWave;
+constexpr int kHalf = kChunk / 2;  // vocabulary unit of one wave in a residual pass
+constexpr int kDrawPerLane = kChunk / kWalkThreads;  // tokens of a chunk per lane in the draw
+static_assert(kDrawPerLane == 8, "the draw gives each lane two float4 of a chunk");
 
 struct WalkShared {
   int32_t par[kMaxNodes];
   int32_t tok[kMaxNodes];
   double u[kMaxNodes];
-  double csum[kMaxChunks];  // per-chunk masses of the distribution to draw from
-  double part[32];          // wave partials
-  float lmax;
-  double S;
-  int arg;
-  uint64_t kids;
-  int decision;
+  float lgx[kMaxNodes];       // target logit of node j's token at its parent's row
+  float qx[kMaxNodes];        // draft probability of node j's token at its parent's row
+  RowStat rs[kMaxNodes + 1];  // the request's rows: r = 0 root, r = 1 + j after node j
+  double csum[kMaxChunks];    // chunk masses of the distribution being drawn from
+  double hsum[2 * kMaxChunks];// half-chunk masses of a residual pass
+  double wtot[kWalkWaves];    // per-wave sums of the draw's scan
+  int32_t wcand[kWalkWaves];  // per-wave first crossing of the draw (-1: none)
+  int32_t wlast[kWalkWaves];  // per-wave last token with mass
   double total;
-  int ybest;
+  int32_t bad;
 };
 
-// mass of chunk ch under P(x) = max(0, p(x) - cc * q(x)) (unnormalised by M)
+// Mass of half-chunk h (2048 tokens) under max(0, p - cc q), one wave, its
+// logits and q requested in one go (32 + 32 values per lane).
 template <bool VEC>
-__device__ __forceinline__ double residual_chunk(const float* lrow, const float* qrow, int V, int ch, float lmax,
-                                                 float c, float invS, double cc, int lane) {
-  const int begin = ch * kChunk, end = min(V, begin + kChunk);
+__device__ __forceinline__ double residual_half(const float* lrow, const float* qrow, int V, int h, float lmax,
+                                                float c, float invS, double cc, int lane) {
+  const int begin = h * kHalf, end = min(V, begin + kHalf);
   double acc = 0.0;
   if (VEC) {
     const float4* l4 = (const float4*)(lrow + begin);
     const float4* q4 = (const float4*)(qrow + begin);
-    const int n4 = (end - begin) >> 2;
-#pragma unroll 1
-    for (int h = 0; h < 4; ++h) {
-      float4 lv[4], qv[4];
+    const int n4 = end > begin ? (end - begin) >> 2 : 0;  // V % 4 == 0 on this path
+    float4 lv[8], qv[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int idx = lane + 64 * (4 * h + i);
-        lv[i] = idx < n4 ? l4[idx] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-        qv[i] = idx < n4 ? q4[idx] : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
+    for (int i = 0; i < 8; ++i) {
+      const int idx = lane + 64 * i;
+      lv[i] = idx < n4 ? l4[idx] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+      qv[i] = idx < n4 ? q4[idx] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc += fmax(0.0, (double)target_prob(lv[i].x, lmax, c, invS) - cc * (double)qv[i].x);
-        acc += fmax(0.0, (double)target_prob(lv[i].y, lmax, c, invS) - cc * (double)qv[i].y);
-        acc += fmax(0.0, (double)target_prob(lv[i].z, lmax, c, invS) - cc * (double)qv[i].z);
-        acc += fmax(0.0, (double)target_prob(lv[i].w, lmax, c, invS) - cc * (double)qv[i].w);
-      }
+    for (int i = 0; i < 8; ++i) {
+      acc += fmax(0.0, (double)target_prob(lv[i].x, lmax, c, invS) - cc * (double)qv[i].x);
+      acc += fmax(0.0, (double)target_prob(lv[i].y, lmax, c, invS) - cc * (double)qv[i].y);
+      acc += fmax(0.0, (double)target_prob(lv[i].z, lmax, c, invS) - cc * (double)qv[i].z);
+      acc += fmax(0.0, (double)target_prob(lv[i].w, lmax, c, invS) - cc * (double)qv[i].w);
     }
   } else {
-    for (int idx = begin + lane; idx < end; idx += 64)
-      acc += fmax(0.0, (double)target_prob(lrow[idx], lmax, c, invS) - cc * (double)qrow[idx]);
+    float lv[32], qv[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const int idx = begin + lane + 64 * i;
+      lv[i] = idx < end ? lrow[idx] : -INFINITY;
+      qv[i] = idx < end ? qrow[idx] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) acc += fmax(0.0, (double)target_prob(lv[i], lmax, c, invS) - cc * (double)qv[i]);
   }
   return wave_sum(acc);
 }
 
-// one element of the distribution being drawn from (level 0: unnormalised p)
-__device__ __forceinline__ double draw_weight(const float* lrow, const float* qrow, int x, int level, float lmax,
-                                              float c, float invS, double cc) {
-  if (level == 0) return (double)target_weight(lrow[x], lmax, c);
-  return fmax(0.0, (double)target_prob(lrow[x], lmax, c, invS) - cc * (double)qrow[x]);
-}
-
-// Vocabulary pass: csum[ch] = mass of chunk ch under max(0, p - cc q);
-// returns the total (the same value in every thread).
+// Vocabulary pass of the whole workgroup: csum[ch] = mass of chunk ch under
+// max(0, p - cc q) (its two halves added in order); returns the total
+// (bitwise the same in every thread).
 template <bool VEC>
-__device__ double residual_pass(WalkShared& sh, const float* lrow, const float* qrow, int V, int nch, float lmax,
+__device__ __forceinline__ double residual_pass(WalkShared& sh, const float* lrow, const float* qrow, int V, int nch, float lmax,
                                 float c, float invS, double cc) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  for (int ch = wave; ch < nch; ch += nw) {
-    const double m = residual_chunk<VEC>(lrow, qrow, V, ch, lmax, c, invS, cc, lane);
-    if (lane == 0) sh.csum[ch] = m;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int h = wave; h < 2 * nch; h += kWalkWaves) {
+    const double m = residual_half<VEC>(lrow, qrow, V, h, lmax, c, invS, cc, lane);
+    if (lane == 0) sh.hsum[h] = m;
   }
+  __syncthreads();
+  for (int ch = threadIdx.x; ch < nch; ch += kWalkThreads) sh.csum[ch] = sh.hsum[2 * ch] + sh.hsum[2 * ch + 1];
   __syncthreads();
   if (wave == 0) {
     double a = 0.0;
@@ -194,101 +227,126 @@ __device__ double residual_pass(WalkShared& sh, const float* lrow, const float* 
   }
   __syncthreads();
   const double t = sh.total;
-  __syncthreads();  // everyone has the total before sh.total is reused
+  __syncthreads();  // every thread has the total before sh.total is reused
   return t;
 }
 
-// Inverse CDF over csum (masses per chunk, total = their sum): the smallest
-// token whose inclusive prefix exceeds u * total. The chunk is found by a
-// sequential prefix over chunk masses, the token by a wave scan inside it.
-__device__ int draw_token(WalkShared& sh, const float* lrow, const float* qrow, int V, int nch, int level,
+// Inverse CDF: the smallest token whose inclusive prefix mass exceeds
+// u * total. The chunk is found by a sequential prefix over the chunk masses
+// (every thread, same order, same result). Inside it, lane l of wave w owns
+// the 8 tokens at 512 w + 8 l: lane sums are scanned within each wave, the
+// wave totals are added in wave order, and the first lane whose inclusive
+// prefix crosses the remainder picks the token among its 8.
+template <bool VEC>
+__device__ __forceinline__ int draw_token(WalkShared& sh, const float* lrow, const float* qrow, int V, int nch, int level,
                           float lmax, float c, float invS, double cc, double u, double total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (threadIdx.x == 0) {
-    const double target = u * total;
-    double run = 0.0;
-    int chosen = -1;
-    double rem = 0.0;
-    for (int ch = 0; ch < nch; ++ch) {
-      const double m = sh.csum[ch];
-      if (m > 0.0) {
-        if (run + m > target) { chosen = ch; rem = target - run; break; }
-        run += m;
-      }
-    }
-    if (chosen < 0) {  // rounding: u*total beyond the sequential prefix; take the last chunk with mass
-      for (int ch = nch - 1; ch >= 0; --ch)
-        if (sh.csum[ch] > 0.0) { chosen = ch; rem = sh.csum[ch]; break; }
-    }
-    sh.decision = chosen;
-    sh.total = rem;
-  }
-  __syncthreads();
-  const int ch = sh.decision;
-  const double rem = sh.total;
-  if (wave == 0) {
-    int y = -1;
-    if (ch >= 0) {
-      // lane owns tokens [seg0, seg1) of the chunk
-      const int begin = ch * kChunk, end = min(V, begin + kChunk);
-      const int seg0 = begin + 64 * lane, seg1 = min(end, seg0 + 64);
-      double seg = 0.0;
-      int lastpos = -1;
-      for (int x = seg0; x < seg1; ++x) {
-        const double w = draw_weight(lrow, qrow, x, level, lmax, c, invS, cc);
-        seg += w;
-        if (w > 0.0) lastpos = x;
-      }
-      double incl = seg;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const double t = __shfl_up(incl, o);
-        if (lane >= o) incl += t;
-      }
-      const double excl = incl - seg;
-      const uint64_t hit = __ballot(incl > rem && seg > 0.0);
-      int found = -1;
-      if (hit) {
-        const int owner = __ffsll((unsigned long long)hit) - 1;
-        if (lane == owner) {
-          double run = excl;
-          for (int x = seg0; x < seg1; ++x) {
-            const double w = draw_weight(lrow, qrow, x, level, lmax, c, invS, cc);
-            run += w;
-            if (w > 0.0 && run > rem) { found = x; break; }
-            if (w > 0.0) lastpos = x;
-          }
-          if (found < 0) found = lastpos;
+  const double target = u * total;
+  double run = 0.0, rem = 0.0;
+  int chosen = -1, last = -1;
+  for (int ch = 0; ch < nch; ++ch) {
+    const double m = sh.csum[ch];
+    if (m > 0.0) {
+      last = ch;
+      if (chosen < 0) {
+        if (run + m > target) {
+          chosen = ch;
+          rem = target - run;
+        } else {
+          run += m;
         }
-        found = __shfl(found, owner);
-      } else {  // rounding: the chunk's last token with mass
-        int lp = lastpos;
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) lp = max(lp, __shfl_xor(lp, o));
-        found = lp;
       }
-      y = found;
     }
-    if (lane == 0) sh.ybest = y;
+  }
+  if (chosen < 0 && last >= 0) {  // rounding: u*total beyond the sequential prefix
+    chosen = last;
+    rem = sh.csum[last];
+  }
+  chosen = __builtin_amdgcn_readfirstlane(chosen);
+  if (chosen < 0) return -1;  // no mass anywhere (flagged by the caller's statistics)
+  const int begin = chosen * kChunk, end = min(V, begin + kChunk);
+  const int x0 = begin + kDrawPerLane * (kWave * wave + lane);
+  float lv[kDrawPerLane], qv[kDrawPerLane];
+  if (VEC) {  // V % 4 == 0 and begin % 4 == 0: a float4 is wholly in or out
+#pragma unroll
+    for (int h = 0; h < kDrawPerLane / 4; ++h) {
+      const int x = x0 + 4 * h;
+      const float4 l4 = x < end ? *(const float4*)(lrow + x) : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+      const float4 q4 = (level > 0 && x < end) ? *(const float4*)(qrow + x) : make_float4(0.f, 0.f, 0.f, 0.f);
+      lv[4 * h] = l4.x; lv[4 * h + 1] = l4.y; lv[4 * h + 2] = l4.z; lv[4 * h + 3] = l4.w;
+      qv[4 * h] = q4.x; qv[4 * h + 1] = q4.y; qv[4 * h + 2] = q4.z; qv[4 * h + 3] = q4.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kDrawPerLane; ++i) {
+      lv[i] = x0 + i < end ? lrow[x0 + i] : -INFINITY;
+      qv[i] = (level > 0 && x0 + i < end) ? qrow[x0 + i] : 0.f;
+    }
+  }
+  double w[kDrawPerLane];
+  double seg = 0.0;
+  int lastpos = -1;
+#pragma unroll
+  for (int i = 0; i < kDrawPerLane; ++i) {
+    // weights of the distribution being drawn from (level 0: unnormalised p)
+    w[i] = level == 0 ? (double)target_weight(lv[i], lmax, c)
+                      : fmax(0.0, (double)target_prob(lv[i], lmax, c, invS) - cc * (double)qv[i]);
+    seg += w[i];
+    lastpos = w[i] > 0.0 ? x0 + i : lastpos;
+  }
+  double incl = seg;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double t = __shfl_up(incl, o);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) sh.wtot[wave] = incl;
+  int lp = lastpos;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) lp = max(lp, __shfl_xor(lp, o));
+  if (lane == 0) sh.wlast[wave] = lp;
+  __syncthreads();
+  double base = 0.0;
+  for (int wv = 0; wv < wave; ++wv) base += sh.wtot[wv];
+  incl += base;
+  const double excl = incl - seg;
+  const uint64_t hit = __ballot(incl > rem && seg > 0.0);
+  if (lane == 0) sh.wcand[wave] = -1;
+  if (hit) {
+    const int owner = __ffsll((unsigned long long)hit) - 1;
+    double r = excl;
+    int found = -1;
+#pragma unroll
+    for (int i = 0; i < kDrawPerLane; ++i) {  // branch-free: the first crossing wins
+      r += w[i];
+      found = (found < 0 && w[i] > 0.0 && r > rem) ? x0 + i : found;
+    }
+    if (found < 0) found = lastpos;  // rounding inside the owning lane
+    found = __shfl(found, owner);
+    if (lane == 0) sh.wcand[wave] = found;
   }
   __syncthreads();
-  return sh.ybest;
+  int y = -1, ylast = -1;
+  for (int wv = 0; wv < kWalkWaves; ++wv) {
+    const int cnd = sh.wcand[wv];
+    y = (y < 0 && cnd >= 0) ? cnd : y;
+    ylast = max(ylast, sh.wlast[wv]);
+  }
+  if (y < 0) y = ylast;  // rounding: the chunk's last token with mass
+  __syncthreads();       // the per-wave slots are free again
+  return y;
 }
 
-// ---------------------------------------------------------------------------
-// Pass 2: the walk. One workgroup per request; thread 0 takes the decisions,
-// every thread joins the vocabulary passes. All control decisions are read
-// back from LDS after a barrier, so the whole workgroup follows one path.
 template <bool VEC>
-__global__ __launch_bounds__(512) void walk_kernel(SampleParams p) {
+__global__ __launch_bounds__(kWalkThreads) void walk_kernel(SampleParams p) {
   __shared__ WalkShared sh;
   const int b = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int md = p.max_depth;
   int32_t* acc_nodes = p.accepted_nodes + (int64_t)b * md;
   int32_t* toks_out = p.out_tokens + (int64_t)b * (md + 1);
-  for (int i = tid; i < md; i += blockDim.x) acc_nodes[i] = -1;
-  for (int i = tid; i <= md; i += blockDim.x) toks_out[i] = -1;
+  for (int i = tid; i < md; i += kWalkThreads) acc_nodes[i] = -1;
+  for (int i = tid; i <= md; i += kWalkThreads) toks_out[i] = -1;
 
   const int n0 = p.cu_nodes[b], n1 = p.cu_nodes[b + 1];
   const int T = n1 - n0;
@@ -312,19 +370,20 @@ __global__ __launch_bounds__(512) void walk_kernel(SampleParams p) {
   }
   if (tid == 0 && p.uniforms_out) p.uniforms_out[p.N + b] = uniform01(p.seed, rid, 0u, 1u, p.step);
   __syncthreads();
-  if (wave == 0) {
+  if (tid < kWave) {
     bool bad_tree = false, bad_tok = false;
     if (lane < T) {
       bad_tree = sh.par[lane] < -1 || sh.par[lane] >= lane;
       bad_tok = sh.tok[lane] < 0 || sh.tok[lane] >= p.V;
     }
     const bool any_tree = __any(bad_tree), any_tok = __any(bad_tok);
-    if (lane == 0) sh.decision = (any_tree ? kStTree : 0) | (any_tok ? kStToken : 0);
+    if (lane == 0) sh.bad = (any_tree ? kStTree : 0) | (any_tok ? kStToken : 0);
   }
   __syncthreads();
-  if (sh.decision) {
+  const int bad = __builtin_amdgcn_readfirstlane(sh.bad);
+  if (bad) {
     if (tid == 0) {
-      flag(p.status, sh.decision);
+      flag(p.status, bad);
       p.accept_len[b] = 0;
       if (p.residual_passes) p.residual_passes[b] = 0;
     }
@@ -333,69 +392,61 @@ __global__ __launch_bounds__(512) void walk_kernel(SampleParams p) {
 
   const int64_t V = p.V;
   const int64_t row0 = (int64_t)n0 + b;
+  // gathers: p-logit and q of every drafted token at its parent's row, and
+  // the normalisation of every row of the request
+  if (tid < T) {
+    const int64_t r = row0 + sh.par[tid] + 1;
+    sh.lgx[tid] = p.logits[r * V + sh.tok[tid]];
+    sh.qx[tid] = p.greedy ? 0.f : p.q[r * V + sh.tok[tid]];
+  }
+  if (tid <= T) sh.rs[tid] = p.rowstats[row0 + tid];
+  __syncthreads();
+
   int pos = -1, depth = 0, passes = 0, bonus = -1;
   for (;;) {
-    __syncthreads();  // all reads of the previous position's shared values are done
-    const int64_t row = row0 + pos + 1;
+    const int r = pos + 1;
+    const int64_t row = row0 + r;
     const float* lrow = p.logits + row * V;
     const float* qrow = p.greedy ? nullptr : p.q + row * V;
-    if (wave == 0) {
-      float lmax, av;
-      double S;
-      int arg;
-      row_norm(p.stats + row * p.nch, p.nch, p.c, lmax, S, arg, av);
-      const uint64_t kids = __ballot(lane < T && sh.par[lane] == pos);
-      if (lane == 0) {
-        sh.lmax = lmax;
-        sh.S = S;
-        sh.arg = arg;
-        sh.kids = kids;
-        if (lmax == -INFINITY) flag(p.status, kStNonFinite);
-      }
+    const RowStat st = sh.rs[r];
+    // children of pos in increasing index: the same ballot in every wave
+    const uint64_t kids = __ballot(lane < T && sh.par[lane] == pos);
+    if (st.lmax == -INFINITY) {  // no finite logit: p is undefined here, stop without a token
+      if (tid == 0) flag(p.status, kStNonFinite);
+      break;
     }
-    __syncthreads();
-    const float lmax = sh.lmax;
-    const double S = sh.S;
-    const uint64_t kids = sh.kids;
 
-    if (p.greedy) {
-      // accept the first child carrying the argmax token
-      const int a = sh.arg;
+    if (p.greedy) {  // accept the first child carrying the argmax token
       int next = -1;
       for (uint64_t k = kids; k; k &= k - 1) {
         const int ch = __ffsll((unsigned long long)k) - 1;
-        if (sh.tok[ch] == a) { next = ch; break; }
+        if (sh.tok[ch] == st.arg) { next = ch; break; }
       }
-      if (next < 0) { bonus = a; break; }
+      next = __builtin_amdgcn_readfirstlane(next);
+      if (next < 0) { bonus = st.arg; break; }
       if (tid == 0) { acc_nodes[depth] = next; toks_out[depth] = sh.tok[next]; }
       ++depth;
       pos = next;
       continue;
     }
 
-    const float invS = (float)(1.0 / S);
+    const float invS = (float)(1.0 / st.S);
     double cc = 0.0, M = 1.0;  // current distribution max(0, p - cc q) / M (cc = 0: p itself)
     int level = 0;
     bool csum_ok = false;      // csum holds the chunk masses of the current level
     int accepted = -1;
     for (uint64_t k = kids; k; k &= k - 1) {
       const int ch = __ffsll((unsigned long long)k) - 1;
-      if (tid == 0) {
-        const int x = sh.tok[ch];
-        const float pf = target_prob(lrow[x], lmax, p.c, invS);
-        const double qx = (double)qrow[x];
-        const double P = level == 0 ? (double)pf : fmax(0.0, (double)pf - cc * qx) / M;
-        sh.decision = (P > 0.0 && sh.u[ch] * qx <= P) ? 1 : 0;
-      }
-      __syncthreads();
-      const bool acc = sh.decision != 0;
-      __syncthreads();  // every thread has read the decision before it is reused
-      if (acc) { accepted = ch; break; }
-      // rejected: move to the next residual level
+      const float pf = target_prob(sh.lgx[ch], st.lmax, p.c, invS);
+      const double qv = (double)sh.qx[ch];
+      const double P = level == 0 ? (double)pf : fmax(0.0, (double)pf - cc * qv) / M;
+      const int ok = __builtin_amdgcn_readfirstlane((P > 0.0 && sh.u[ch] * qv <= P) ? 1 : 0);
+      if (ok) { accepted = ch; break; }
+      // rejected: the next sibling is tested against the next residual level
       const double cn = cc + M;
-      const double Mn = residual_pass<VEC>(sh, lrow, qrow, p.V, p.nch, lmax, p.c, invS, cn);
+      const double Mn = residual_pass<VEC>(sh, lrow, qrow, p.V, p.nch, st.lmax, p.c, invS, cn);
       ++passes;
-      if (Mn > 0.0) {
+      if (__builtin_amdgcn_readfirstlane(Mn > 0.0 ? 1 : 0)) {
         cc = cn;
         M = Mn;
         ++level;
@@ -414,30 +465,22 @@ __global__ __launch_bounds__(512) void walk_kernel(SampleParams p) {
     // final draw at this position from the current distribution
     double total;
     if (level == 0) {
-      const ChunkStat* st = p.stats + row * p.nch;
-      for (int ch = tid; ch < p.nch; ch += blockDim.x) {
-        const ChunkStat s = st[ch];
-        sh.csum[ch] = s.lmax == -INFINITY ? 0.0 : s.s * exp2((double)(s.lmax - lmax) * (double)p.c);
+      const ChunkStat* cs = p.stats + row * p.nch;
+      for (int ch = tid; ch < p.nch; ch += kWalkThreads) {
+        const ChunkStat s = cs[ch];
+        sh.csum[ch] = s.lmax == -INFINITY ? 0.0 : s.s * exp2((double)(s.lmax - st.lmax) * (double)p.c);
       }
       __syncthreads();
-      if (wave == 0) {
-        double a = 0.0;
-        for (int ch = lane; ch < p.nch; ch += 64) a += sh.csum[ch];
-        a = wave_sum(a);
-        if (lane == 0) sh.total = a;
-      }
-      __syncthreads();
-      total = sh.total;
-      __syncthreads();
+      total = st.S;
     } else {
       if (!csum_ok) {
-        residual_pass<VEC>(sh, lrow, qrow, p.V, p.nch, lmax, p.c, invS, cc);
+        residual_pass<VEC>(sh, lrow, qrow, p.V, p.nch, st.lmax, p.c, invS, cc);
         ++passes;
       }
       total = M;
     }
     const double uf = uniform01(p.seed, rid, 0u, 1u, p.step);
-    bonus = draw_token(sh, lrow, qrow, p.V, p.nch, level, lmax, p.c, invS, cc, uf, total);
+    bonus = draw_token<VEC>(sh, lrow, qrow, p.V, p.nch, level, st.lmax, p.c, invS, cc, uf, total);
     break;
   }
   if (tid == 0) {
@@ -448,8 +491,8 @@ __global__ __launch_bounds__(512) void walk_kernel(SampleParams p) {
 }
 
 // ---------------------------------------------------------------------------
-hipError_t launch_sampler(const SampleParams& p, bool vec4, int walk_threads, hipStream_t stream,
-                          hipEvent_t ev_start, hipEvent_t ev_stop) {
+hipError_t launch_sampler(const SampleParams& p, bool vec4, hipStream_t stream, hipEvent_t ev_start,
+                          hipEvent_t ev_stop) {
   if (p.B <= 0) return hipSuccess;
   const int64_t rows = (int64_t)p.N + p.B;
   const int64_t items = rows * p.nch;
@@ -465,14 +508,16 @@ hipError_t launch_sampler(const SampleParams& p, bool vec4, int walk_threads, hi
   if (ev_stop) (void)hipEventRecord(ev_stop, stream);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  row_finalize_kernel<<<dim3((unsigned)((rows + 3) / 4)), 256, 0, stream>>>(p.stats, rows, p.nch, p.c, p.rowstats);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
   if (p.probs_out && !p.greedy) {
-    if (vec4) probs_kernel<true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, p.probs_out);
-    else probs_kernel<false><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, p.probs_out);
+    probs_kernel<<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.rowstats, p.probs_out);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  if (vec4) walk_kernel<true><<<dim3(p.B), dim3(walk_threads), 0, stream>>>(p);
-  else walk_kernel<false><<<dim3(p.B), dim3(walk_threads), 0, stream>>>(p);
+  if (vec4) walk_kernel<true><<<dim3(p.B), dim3(kWalkThreads), 0, stream>>>(p);
+  else walk_kernel<false><<<dim3(p.B), dim3(kWalkThreads), 0, stream>>>(p);
   return hipGetLastError();
 }
 
