@@ -27,10 +27,6 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 int eff_max_nodes(int32_t m) { return m == 0 ? sv::kMaxNodes : m; }
 
-#ifndef SV_ATTN_NBUF
-#define SV_ATTN_NBUF 2  // key tiles in flight per attention workgroup
-#endif
-
 // ---- attention -------------------------------------------------------------
 sv_status check_attn(const sv_attn_args* a) {
   if (!a) return fail(SV_ERR_INVALID_ARG, "attn args is NULL");
@@ -68,11 +64,13 @@ sv::AttnPlan plan_attn(const sv_attn_args* a) {
   const int rmax = G * eff_max_nodes(a->max_nodes);
   pl.mfma = a->dtype == SV_BF16;
   if (pl.mfma) {
-    pl.rows_per_wg = 64;
-    pl.nbuf = SV_ATTN_NBUF;
+    // one 16-row block per wave by default; trees with more than 64 rows per
+    // KV head and too few (request, KV head) pairs to give every CU several
+    // workgroups take two row blocks per wave (fewer repeated key streams)
+    const int64_t jobs = (int64_t)a->B * a->Hkv;
+    pl.rows_per_wg = (rmax > 64 && jobs < 256) ? 128 : 64;
   } else {
     pl.rows_per_wg = 8;
-    pl.nbuf = 0;
   }
   pl.n_rowgroups = (rmax + pl.rows_per_wg - 1) / pl.rows_per_wg;
   const int64_t max_splits_len = a->Lcap / 64 > 0 ? a->Lcap / 64 : 1;

@@ -22,6 +22,9 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
 
 // max over lanes l, l^16, l^32, l^48 (the four 16-lane rows of a wave) with
 // the gfx950 row-swap permutes instead of LDS-routed shuffles
@@ -87,43 +90,41 @@ __global__ __launch_bounds__(64) void tree_prep_kernel(int B, int N, int max_nod
 // O^T = V^T P^T; V^T comes from LDS. Each lane therefore keeps the running
 // max / sum of exactly one row and no transpose of P is needed.
 //
-// LDS tiles (64 keys):
+// LDS tiles (64 keys), both row-major as they sit in the cache:
 //   Ks [key][D]   16-byte unit u of row `key` stored at unit u ^ (key & 7);
-//   Vt [d][64]    key kappa stored at column pos(kappa) (pairs of 16-key
-//                 sub-tiles interleaved so a lane's 8 keys of one k-step
-//                 are contiguous), 16-byte unit u of row d stored at
-//                 u ^ sw(d). Both swizzles keep the MFMA-operand reads and
-//                 the tile writes free of most bank conflicts.
-__device__ __forceinline__ int vt_pos(int kappa) {
-  const int ks = kappa >> 5, rem = kappa & 31;
-  return (ks << 5) + (((rem & 15) >> 2) << 3) + ((rem >> 4) << 2) + (rem & 3);
-}
-__device__ __forceinline__ int vt_sw(int d) { return (d ^ (d >> 2)) & 7; }
+//   Vs [key][D]   16-byte unit u of row `key` stored at unit u ^ 2 (key & 3).
+// Tile writes are whole 16-byte units; the K operand is read as 16-byte
+// units, the V^T operand with the gfx950 transposed reads. Both swizzles
+// keep the writes and the operand reads free of bank conflicts.
 
-// One workgroup = 4 waves = 64 query rows (one 16-row block per wave) of one
-// (request, KV head, KV split). Trees with more rows per KV head take several
-// row groups that stream the same keys; the linear block id is decoded so
-// that all row groups of one (request, KV head, split) land on the same XCD
-// (blocks go to XCDs round-robin by id) back to back, and their repeated key
-// reads are served by that XCD's L2.
+// One workgroup = NW waves; wave w owns the RBW 16-row blocks
+// r = row0 + 16 (w + NW i) + (lane % 16), i < RBW, of one (request, KV head,
+// KV split): 16 NW RBW query rows. Every K / V fragment a wave reads from LDS
+// feeds all of its row blocks. Trees with more rows than a workgroup holds
+// take several row groups that stream the same keys; the linear block id is
+// decoded so that all row groups of one (request, KV head, split) land on the
+// same XCD (blocks go to XCDs round-robin by id) back to back, and their
+// repeated key reads are served by that XCD's L2.
 //
 // Memory pipeline: NBUF key tiles are in flight in registers (buffer loads
-// issued NBUF tiles ahead); each tile is written to LDS (K as is, V
-// transposed), consumed by the MFMAs, and its registers are refilled with the
-// tile NBUF positions later. Streaming decode attention is bound by HBM
-// latency x bytes in flight, so the ring depth is what sets the bandwidth.
-template <int D, int NBUF>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+// issued NBUF tiles ahead); each tile is written to LDS, consumed by the
+// MFMAs, and its registers are refilled with the tile NBUF positions later.
+// Decode-shaped attention is bound by memory latency x bytes in flight per
+// CU, and measured on MI355X several independent workgroups per CU (WPE
+// waves per SIMD) hide it better than a deeper ring in fewer workgroups.
+template <int D, int NBUF, int NW, int RBW, int WPE = 2>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE)))
 void attn_mfma_kernel(AttnParams p) {
-  constexpr int NT = 256;            // threads
+  constexpr int NT = 64 * NW;        // threads
   constexpr int KT = 64;             // keys per tile
   constexpr int KS = D / 32;         // k-steps of S^T (32 head dims each)
   constexpr int DB = D / 16;         // 16-wide blocks of the output head dim
   constexpr int UNITS = D / 8;       // 16-byte units per K row
+  constexpr int ROWS = 16 * NW * RBW;
   constexpr int PER_THREAD = KT * D / 8 / NT; // K units / V items loaded per thread per tile
   static_assert(PER_THREAD >= 1 && KT * D / 8 == PER_THREAD * NT, "tile / thread split");
   __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * D];
-  __shared__ __attribute__((aligned(16))) uint32_t Vt[D * KT / 2];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[KT * D];
 
   // XCD-aware decode: id = ((job / 8) * n_rowgroups + rg) * 8 + job % 8
   const int lin = blockIdx.x;
@@ -148,7 +149,7 @@ void attn_mfma_kernel(AttnParams p) {
     return;
   }
   const int R = p.G * T;
-  const int row0 = rg * 64;
+  const int row0 = rg * ROWS;
   if (row0 >= R) return;
   const int nkeys = L + T;
   const int kchunk = ((nkeys + p.splits - 1) / p.splits + KT - 1) / KT * KT;
@@ -156,26 +157,36 @@ void attn_mfma_kernel(AttnParams p) {
   const int ke = min(nkeys, kb + kchunk);
   const int NH = p.N * p.Hq;
 
-  // the 16 rows of this wave: r = row0 + 16 * wave + l16
-  const int rbase = row0 + 16 * wave;
-  const bool rb_any = rbase < R;
-  const int r = rbase + l16;
-  bf16x8_t qf[KS];
-  uint64_t amask = 0;
-  int orow = -1;  // packed (node, q head) index, -1 if the row does not exist
+  // this wave's row blocks
+  bool rb_any[RBW];
+  bf16x8_t qf[RBW][KS];
+  uint64_t amask[RBW];
+  int orow[RBW];  // packed (node, q head) index, -1 if the row does not exist
+  bool wave_any = false;
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) qf[ks] = bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
-  if (r < R) {
-    const int j = r / p.G, hh = r - j * p.G;
-    orow = (n0 + j) * p.Hq + g * p.G + hh;
-    amask = p.anc[n0 + j];
-    const uint16_t* qp = (const uint16_t*)p.q + (int64_t)orow * D;
+  for (int i = 0; i < RBW; ++i) {
+    const int rbase = row0 + 16 * (wave + NW * i);
+    rb_any[i] = rbase < R;
+    wave_any |= rb_any[i];
+    const int r = rbase + l16;
+    amask[i] = 0;
+    orow[i] = -1;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = *(const bf16x8_t*)(qp + 32 * ks + 8 * g4);
+    for (int ks = 0; ks < KS; ++ks) qf[i][ks] = bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+    if (r < R) {
+      const int j = r / p.G, hh = r - j * p.G;
+      orow[i] = (n0 + j) * p.Hq + g * p.G + hh;
+      amask[i] = p.anc[n0 + j];
+      const uint16_t* qp = (const uint16_t*)p.q + (int64_t)orow[i] * D;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[i][ks] = *(const bf16x8_t*)(qp + 32 * ks + 8 * g4);
+    }
   }
 
   if (kb >= ke) {  // empty split: contributes nothing to the merge
-    if (orow >= 0 && g4 == 0) p.ml_part[(int64_t)split * NH + orow] = make_float2(-INFINITY, 0.f);
+#pragma unroll
+    for (int i = 0; i < RBW; ++i)
+      if (orow[i] >= 0 && g4 == 0) p.ml_part[(int64_t)split * NH + orow[i]] = make_float2(-INFINITY, 0.f);
     return;
   }
 
@@ -191,20 +202,27 @@ void attn_mfma_kernel(AttnParams p) {
       __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, ke * D * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, ke * D * 2, 0x00020000);
-  int koff[PER_THREAD], voff[PER_THREAD];
+  int koff[PER_THREAD];  // K and V share the per-thread offsets (16-byte unit c of the tile)
 #pragma unroll
   for (int i = 0; i < PER_THREAD; ++i) {
     const int c = tid + NT * i;
     koff[i] = ((c / UNITS) * D + 8 * (c % UNITS)) * 2;
-    voff[i] = ((c / (D / 4)) * 2 * D + 4 * (c % (D / 4))) * 2;
   }
   i32x4_t kreg[NBUF][PER_THREAD];
-  i32x2_t vreg[NBUF][PER_THREAD][2];
+  i32x4_t vreg[NBUF][PER_THREAD];
+  // V^T operand addressing for the transposed LDS reads (see the PV step)
+  const int vt_lane = (4 * g4 + (l16 >> 2)) * D + 4 * (l16 & 1) + 8 * ((l16 >> 1) & 1);
+  const int vt_sw = l16 >> 2;
 
-  f32x4_t o[DB];
-  float m = -INFINITY, l = 0.f;
+  f32x4_t o[RBW][DB];
+  float m[RBW], l[RBW];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < RBW; ++i) {
+    m[i] = -INFINITY;
+    l[i] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[i][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
 
   // prologue: the first NBUF tiles
 #pragma unroll
@@ -214,8 +232,7 @@ void attn_mfma_kernel(AttnParams p) {
 #pragma unroll
       for (int i = 0; i < PER_THREAD; ++i) {
         kreg[s][i] = __builtin_amdgcn_raw_buffer_load_b128(krs, koff[i], so, 0);
-        vreg[s][i][0] = __builtin_amdgcn_raw_buffer_load_b64(vrs, voff[i], so, 0);
-        vreg[s][i][1] = __builtin_amdgcn_raw_buffer_load_b64(vrs, voff[i] + D * 2, so, 0);
+        vreg[s][i] = __builtin_amdgcn_raw_buffer_load_b128(vrs, koff[i], so, 0);
       }
     }
   }
@@ -231,17 +248,7 @@ void attn_mfma_kernel(AttnParams p) {
         const int c = tid + NT * i;
         const int kk = c / UNITS, dc = c % UNITS;
         *(i32x4_t*)(Ks + kk * D + 8 * (dc ^ (kk & 7))) = kreg[s][i];
-        const int kp = c / (D / 4), dq = c % (D / 4);
-        const int pos = vt_pos(2 * kp);  // even key; its odd partner sits at pos + 1
-        const uint32_t ax = (uint32_t)vreg[s][i][0][0], ay = (uint32_t)vreg[s][i][0][1];
-        const uint32_t bx = (uint32_t)vreg[s][i][1][0], by = (uint32_t)vreg[s][i][1][1];
-        const uint32_t w[4] = {(ax & 0xffffu) | (bx << 16), (ax >> 16) | (bx & 0xffff0000u),
-                               (ay & 0xffffu) | (by << 16), (ay >> 16) | (by & 0xffff0000u)};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int d = 4 * dq + e;
-          Vt[d * 32 + (((pos >> 3) ^ vt_sw(d)) << 2) + ((pos >> 1) & 3)] = w[e];
-        }
+        *(i32x4_t*)(Vs + kk * D + 8 * (dc ^ (2 * (kk & 3)))) = vreg[s][i];
       }
       __syncthreads();
       // refill this ring slot with the tile NBUF positions ahead
@@ -251,127 +258,145 @@ void attn_mfma_kernel(AttnParams p) {
 #pragma unroll
         for (int i = 0; i < PER_THREAD; ++i) {
           kreg[s][i] = __builtin_amdgcn_raw_buffer_load_b128(krs, koff[i], so, 0);
-          vreg[s][i][0] = __builtin_amdgcn_raw_buffer_load_b64(vrs, voff[i], so, 0);
-          vreg[s][i][1] = __builtin_amdgcn_raw_buffer_load_b64(vrs, voff[i] + D * 2, so, 0);
+          vreg[s][i] = __builtin_amdgcn_raw_buffer_load_b128(vrs, koff[i], so, 0);
         }
       }
-      if (!rb_any) continue;  // this wave has no rows: it only helps to stream the tiles
+      if (!wave_any) continue;  // this wave has no rows: it only helps to stream the tiles
       const bool full = (t0 + KT <= ke) && (t0 + KT <= L);
-      // visibility of the tile's 64 keys for this lane's row, built without
-      // branches: context keys, then the row's ancestor-or-self draft slots,
-      // cut at the split end (the short-circuit form of this test was
-      // miscompiled by the ROCm 7.2 compiler under this register budget)
-      uint64_t vis64 = ~0ull;
-      if (!full) {
-        const int dl = L - t0;  // tile bit of the first draft slot
-        const uint64_t ctx_bits = dl >= 64 ? ~0ull : (dl <= 0 ? 0ull : ((1ull << dl) - 1ull));
-        const uint64_t drf_bits = dl >= 64 ? 0ull : (dl >= 0 ? (amask << dl) : (-dl >= 64 ? 0ull : (amask >> -dl)));
-        const int dv = ke - t0;
-        const uint64_t valid = dv >= 64 ? ~0ull : ((1ull << dv) - 1ull);
-        vis64 = (ctx_bits | drf_bits) & valid;
-      }
 
-      // S^T for this row block
-      f32x4_t sc[4];
+      // S^T for every row block of the wave; each K fragment is read once
+      f32x4_t sc[RBW][4];
 #pragma unroll
-      for (int st = 0; st < 4; ++st) sc[st] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < RBW; ++i)
+#pragma unroll
+        for (int st = 0; st < 4; ++st) sc[i][st] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         const int key = 16 * st + l16;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           const bf16x8_t a = *(const bf16x8_t*)(Ks + key * D + 8 * ((4 * ks + g4) ^ (key & 7)));
-          sc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], sc[st], 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < RBW; ++i)
+            if (rb_any[i]) sc[i][st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[i][ks], sc[i][st], 0, 0, 0);
         }
       }
 
       // online softmax in the log2 domain: p = 2^(s * scale_log2 - m), the
       // scale folded into one FMA, raw v_exp_f32 (arguments are <= 0, so only
       // denormal results flush, which softmax weights below 2^-126 afford)
-      float x[16];
+      bf16x8_t pk[RBW][2];
 #pragma unroll
-      for (int st = 0; st < 4; ++st)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[4 * st + e] = sc[st][e];
-      if (!full) {  // wave-uniform: only tiles that reach the draft slots or the split end
-        const uint64_t lane_bits = vis64 >> (4 * g4);
+      for (int i = 0; i < RBW; ++i) {
+        if (!rb_any[i]) continue;
+        float x[16];
 #pragma unroll
         for (int st = 0; st < 4; ++st)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const bool vis = (lane_bits >> (16 * st + e)) & 1ull;
-            x[4 * st + e] = vis ? x[4 * st + e] : -INFINITY;
-          }
-      }
-      float mx = x[0];
+          for (int e = 0; e < 4; ++e) x[4 * st + e] = sc[i][st][e];
+        if (!full) {  // wave-uniform: only tiles that reach the draft slots or the split end
+          // visibility of the tile's 64 keys for this lane's row, built
+          // without branches: context keys, then the row's ancestor-or-self
+          // draft slots, cut at the split end (the short-circuit form of this
+          // test was miscompiled by the ROCm 7.2 compiler under some register
+          // budgets)
+          const int dl = L - t0;  // tile bit of the first draft slot
+          const uint64_t ctx_bits = dl >= 64 ? ~0ull : (dl <= 0 ? 0ull : ((1ull << dl) - 1ull));
+          const uint64_t drf_bits =
+              dl >= 64 ? 0ull : (dl >= 0 ? (amask[i] << dl) : (-dl >= 64 ? 0ull : (amask[i] >> -dl)));
+          const int dv = ke - t0;
+          const uint64_t valid = dv >= 64 ? ~0ull : ((1ull << dv) - 1ull);
+          const uint64_t lane_bits = ((ctx_bits | drf_bits) & valid) >> (4 * g4);
 #pragma unroll
-      for (int t = 1; t < 16; ++t) mx = fmaxf(mx, x[t]);
-      // the row's 64 keys live in lanes l16, l16+16, l16+32, l16+48
-      mx = row_max4(mx);
-      const float mnew = fmaxf(m, mx * p.scale_log2);
-      const float msub = mnew == -INFINITY ? 0.f : mnew;
-      float lsum = 0.f;
+          for (int st = 0; st < 4; ++st)
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        x[t] = __builtin_amdgcn_exp2f(fmaf(x[t], p.scale_log2, -msub));
-        lsum += x[t];
-      }
-      // rescale the running output only when some row's maximum moved
-      if (__any(mnew != m)) {
-        const float alpha = __builtin_amdgcn_exp2f(m - msub);  // m = -inf (nothing seen yet) -> 0
-        l *= alpha;
+            for (int e = 0; e < 4; ++e) {
+              const bool vis = (lane_bits >> (16 * st + e)) & 1ull;
+              x[4 * st + e] = vis ? x[4 * st + e] : -INFINITY;
+            }
+        }
+        float mx = x[0];
 #pragma unroll
-        for (int db = 0; db < DB; ++db) o[db] *= alpha;
-      }
-      l += lsum;
-      m = mnew;
-      bf16x8_t pk[2];
+        for (int t = 1; t < 16; ++t) mx = fmaxf(mx, x[t]);
+        // the row's 64 keys live in lanes l16, l16+16, l16+32, l16+48
+        mx = row_max4(mx);
+        const float mnew = fmaxf(m[i], mx * p.scale_log2);
+        const float msub = mnew == -INFINITY ? 0.f : mnew;
+        float lsum = 0.f;
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        // element 4h + e  <->  sub-tile st = 2 k2 + h, value e (RNE by v_cvt_pk_bf16_f32)
-        const float* lo = x + 4 * (2 * k2);
-        const float* hi = x + 4 * (2 * k2 + 1);
-        const bf16x2_t p01 = {(__bf16)lo[0], (__bf16)lo[1]}, p23 = {(__bf16)lo[2], (__bf16)lo[3]};
-        const bf16x2_t p45 = {(__bf16)hi[0], (__bf16)hi[1]}, p67 = {(__bf16)hi[2], (__bf16)hi[3]};
-        const uint32_t w0 = __builtin_bit_cast(uint32_t, p01), w1 = __builtin_bit_cast(uint32_t, p23);
-        const uint32_t w2 = __builtin_bit_cast(uint32_t, p45), w3 = __builtin_bit_cast(uint32_t, p67);
-        const i32x4_t wv = {(int)w0, (int)w1, (int)w2, (int)w3};
-        pk[k2] = __builtin_bit_cast(bf16x8_t, wv);
-      }
-
-      // O^T += V^T P^T
+        for (int t = 0; t < 16; ++t) {
+          x[t] = __builtin_amdgcn_exp2f(fmaf(x[t], p.scale_log2, -msub));
+          lsum += x[t];
+        }
+        // rescale the running output only when some row's maximum moved
+        if (__any(mnew != m[i])) {
+          const float alpha = __builtin_amdgcn_exp2f(m[i] - msub);  // m = -inf (nothing seen yet) -> 0
+          l[i] *= alpha;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int d = 16 * db + l16;
+          for (int db = 0; db < DB; ++db) o[i][db] *= alpha;
+        }
+        l[i] += lsum;
+        m[i] = mnew;
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
-          const bf16x8_t a = *(const bf16x8_t*)(Vt + d * 32 + (((4 * k2 + g4) ^ vt_sw(d)) << 2));
-          o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pk[k2], o[db], 0, 0, 0);
+          // element 4h + e  <->  sub-tile st = 2 k2 + h, value e (RNE by v_cvt_pk_bf16_f32)
+          const float* lo = x + 4 * (2 * k2);
+          const float* hi = x + 4 * (2 * k2 + 1);
+          const bf16x2_t p01 = {(__bf16)lo[0], (__bf16)lo[1]}, p23 = {(__bf16)lo[2], (__bf16)lo[3]};
+          const bf16x2_t p45 = {(__bf16)hi[0], (__bf16)hi[1]}, p67 = {(__bf16)hi[2], (__bf16)hi[3]};
+          const i32x4_t wv = {(int)__builtin_bit_cast(uint32_t, p01), (int)__builtin_bit_cast(uint32_t, p23),
+                              (int)__builtin_bit_cast(uint32_t, p45), (int)__builtin_bit_cast(uint32_t, p67)};
+          pk[i][k2] = __builtin_bit_cast(bf16x8_t, wv);
+        }
+      }
+
+      // O^T += V^T P^T; each V fragment is read once for all row blocks.
+      // The V^T operand (lane l: head dim 16 db + l % 16, keys 32 k2 + 16 h +
+      // 4 (l / 16) + e for h = 0, 1 and e = 0..3, the key order of pk) comes
+      // straight from the row-major V tile through two ds_read_b64_tr_b16:
+      // in each 16-lane group, lane j points at the 4 head dims
+      // 16 db + 4 (j % 4) .. + 3 of key base + j / 4, and lane i receives
+      // element i % 4 of lanes i / 4, 4 + i / 4, 8 + i / 4, 12 + i / 4, i.e.
+      // keys base .. base + 3 of head dim 16 db + i.
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const int base = (32 * k2) * D + vt_lane + 16 * (db ^ vt_sw);
+          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(lds_u16_t*)(Vs + base));
+          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(lds_u16_t*)(Vs + base + 16 * D));
+          const bf16x8_t a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+          for (int i = 0; i < RBW; ++i)
+            if (rb_any[i]) o[i][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pk[i][k2], o[i][db], 0, 0, 0);
         }
       }
     }
   }
 
-  if (!rb_any) return;
   // row sums across the four lane groups that share a row, then write
-  const float lt = row_sum4(l);
-  if (orow < 0) return;
-  if (p.splits == 1) {
-    const float inv = 1.0f / lt;
-    float* op = p.out + (int64_t)orow * D + 4 * g4;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const f32x4_t v = o[db] * inv;
-      *(float4*)(op + 16 * db) = make_float4(v[0], v[1], v[2], v[3]);
-    }
-  } else {
-    float* op = p.o_part + ((int64_t)split * NH + orow) * D + 4 * g4;
+  for (int i = 0; i < RBW; ++i) {
+    if (!rb_any[i]) continue;
+    const float lt = row_sum4(l[i]);
+    if (orow[i] < 0) continue;
+    if (p.splits == 1) {
+      const float inv = 1.0f / lt;
+      float* op = p.out + (int64_t)orow[i] * D + 4 * g4;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const f32x4_t v = o[db];
-      *(float4*)(op + 16 * db) = make_float4(v[0], v[1], v[2], v[3]);
+      for (int db = 0; db < DB; ++db) {
+        const f32x4_t v = o[i][db] * inv;
+        *(float4*)(op + 16 * db) = make_float4(v[0], v[1], v[2], v[3]);
+      }
+    } else {
+      float* op = p.o_part + ((int64_t)split * NH + orow[i]) * D + 4 * g4;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const f32x4_t v = o[i][db];
+        *(float4*)(op + 16 * db) = make_float4(v[0], v[1], v[2], v[3]);
+      }
+      if (g4 == 0) p.ml_part[(int64_t)split * NH + orow[i]] = make_float2(m[i], lt);
     }
-    if (g4 == 0) p.ml_part[(int64_t)split * NH + orow] = make_float2(m, lt);
   }
 }
 
@@ -493,25 +518,43 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
 
 // ---------------------------------------------------------------------------
 // Split-K merge: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
-// One wave per (node, query head).
+// One wave per (node, query head): the split headers are reduced lane-
+// parallel (fixed butterfly order), then every lane sums its head dims over
+// the splits in split order with eight splits' loads in flight at a time.
 __global__ __launch_bounds__(256) void attn_combine_kernel(int NH, int D, int splits, const float* o_part,
                                                            const float2* ml_part, float* out) {
   const int item = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (item >= NH) return;
   float M = -INFINITY;
-  for (int s = 0; s < splits; ++s) {
+  for (int s = lane; s < splits; s += 64) {
     const float2 ml = ml_part[(int64_t)s * NH + item];
     if (ml.y > 0.f) M = fmaxf(M, ml.x);
   }
+  M = wave_max(M);
   float den = 0.f;
-  for (int s = 0; s < splits; ++s) {
+  for (int s = lane; s < splits; s += 64) {
     const float2 ml = ml_part[(int64_t)s * NH + item];
     if (ml.y > 0.f) den += exp2f(ml.x - M) * ml.y;
   }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) den += __shfl_xor(den, o);
   const float inv = 1.0f / den;
   for (int d = lane; d < D; d += 64) {
     float acc = 0.f;
-    for (int s = 0; s < splits; ++s) {
+    int s = 0;
+    for (; s + 8 <= splits; s += 8) {
+      float2 ml[8];
+      float ov[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        ml[u] = ml_part[(int64_t)(s + u) * NH + item];
+        ov[u] = o_part[((int64_t)(s + u) * NH + item) * D + d];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (ml[u].y > 0.f) acc += exp2f(ml[u].x - M) * ov[u];
+    }
+    for (; s < splits; ++s) {
       const float2 ml = ml_part[(int64_t)s * NH + item];
       if (ml.y > 0.f) acc += exp2f(ml.x - M) * o_part[((int64_t)s * NH + item) * D + d];
     }
@@ -527,10 +570,12 @@ hipError_t launch_tree_prep(int B, int N, int max_nodes, const int32_t* cu_nodes
   return hipGetLastError();
 }
 
+// 64 rows: one 16-row block per wave, three workgroups per CU, one key tile
+// in flight each; 128 rows: two row blocks per wave, two workgroups per CU.
 template <int D>
-static void launch_mfma_d(const AttnParams& p, int nbuf, dim3 grid, hipStream_t stream) {
-  if (nbuf <= 2) attn_mfma_kernel<D, 2><<<grid, dim3(256), 0, stream>>>(p);
-  else attn_mfma_kernel<D, 3><<<grid, dim3(256), 0, stream>>>(p);
+static void launch_mfma_d(const AttnParams& p, int rows_per_wg, dim3 grid, hipStream_t stream) {
+  if (rows_per_wg <= 64) attn_mfma_kernel<D, 1, 4, 1, 3><<<grid, dim3(256), 0, stream>>>(p);
+  else attn_mfma_kernel<D, 1, 4, 2, 2><<<grid, dim3(256), 0, stream>>>(p);
 }
 
 hipError_t launch_attention(const AttnParams& p, const AttnPlan& plan, bool bf16, hipStream_t stream,
@@ -541,8 +586,8 @@ hipError_t launch_attention(const AttnParams& p, const AttnPlan& plan, bool bf16
     // 1-D grid, decoded XCD-aware inside the kernel
     const int64_t groups = ((int64_t)p.n_jobs + 7) / 8;
     const dim3 grid((unsigned)(groups * 8 * p.n_rowgroups));
-    if (p.D == 128) launch_mfma_d<128>(p, plan.nbuf, grid, stream);
-    else launch_mfma_d<64>(p, plan.nbuf, grid, stream);
+    if (p.D == 128) launch_mfma_d<128>(p, plan.rows_per_wg, grid, stream);
+    else launch_mfma_d<64>(p, plan.rows_per_wg, grid, stream);
   } else {
     const dim3 grid(plan.n_rowgroups * plan.splits, p.Hkv, p.B);
     if (p.D == 128) attn_valu_kernel<128><<<grid, dim3(256), 0, stream>>>(p);

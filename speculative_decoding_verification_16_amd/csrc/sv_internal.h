@@ -35,7 +35,6 @@ struct AttnParams {
 
 struct AttnPlan {
   bool mfma;        // bf16 MFMA path (else fp32 VALU path)
-  int nbuf;         // MFMA path: key tiles in flight per workgroup
   int rows_per_wg;
   int n_rowgroups;  // workgroups per (request, KV head, split) along rows
   int splits;
