@@ -64,9 +64,9 @@ sv::AttnPlan plan_attn(const sv_attn_args* a) {
   const int rmax = G * eff_max_nodes(a->max_nodes);
   pl.mfma = a->dtype == SV_BF16;
   if (pl.mfma) {
-    // one 16-row block per wave by default; trees with more than 64 rows per
-    // KV head and too few (request, KV head) pairs to give every CU several
-    // workgroups take two row blocks per wave (fewer repeated key streams)
+    // 64-row workgroups by default; trees with more than 64 rows per KV head
+    // and too few (request, KV head) pairs to give every CU several
+    // workgroups take 128-row ones (fewer repeated key streams)
     const int64_t jobs = (int64_t)a->B * a->Hkv;
     pl.rows_per_wg = (rmax > 64 && jobs < 256) ? 128 : 64;
   } else {

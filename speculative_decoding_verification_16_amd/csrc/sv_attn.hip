@@ -570,12 +570,14 @@ hipError_t launch_tree_prep(int B, int N, int max_nodes, const int32_t* cu_nodes
   return hipGetLastError();
 }
 
-// 64 rows: one 16-row block per wave, three workgroups per CU, one key tile
-// in flight each; 128 rows: two row blocks per wave, two workgroups per CU.
+// 64 rows: 4 waves x one 16-row block, three workgroups per CU; 128 rows:
+// 8 waves x one 16-row block, two workgroups per CU. One key tile in flight
+// per workgroup in both (measured on MI355X: more independent workgroups per
+// CU beat deeper rings in fewer of them).
 template <int D>
 static void launch_mfma_d(const AttnParams& p, int rows_per_wg, dim3 grid, hipStream_t stream) {
   if (rows_per_wg <= 64) attn_mfma_kernel<D, 1, 4, 1, 3><<<grid, dim3(256), 0, stream>>>(p);
-  else attn_mfma_kernel<D, 1, 4, 2, 2><<<grid, dim3(256), 0, stream>>>(p);
+  else attn_mfma_kernel<D, 1, 8, 1, 4><<<grid, dim3(512), 0, stream>>>(p);
 }
 
 hipError_t launch_attention(const AttnParams& p, const AttnPlan& plan, bool bf16, hipStream_t stream,
