@@ -32,8 +32,18 @@ DEFAULT_WORKLOAD = "c5_super_tree"
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "attn_mfma_kernel": "speculative_decoding_verification_16_amd/csrc/sv_attn.hip",
+    "attn_mfma32_kernel": "speculative_decoding_verification_16_amd/csrc/sv_attn.hip",
     "row_stats_kernel": "speculative_decoding_verification_16_amd/csrc/sv_sample.hip",
 }
+
+
+def attention_kernel_name(w, cfg) -> str:
+    """Which attention kernel the library's plan launches: fp32 caches take the
+    VALU kernel; bf16 takes 16x16 MFMA tiles when a KV head carries at most 64
+    query rows (Hq/Hkv heads x max_T nodes), else 32x32 tiles."""
+    if w["dtype"] != "bf16":
+        return "attn_valu_kernel"
+    return "attn_mfma_kernel" if (cfg.Hq // cfg.Hkv) * w["max_T"] <= 64 else "attn_mfma32_kernel"
 
 
 class HipEvents:
@@ -280,7 +290,7 @@ def main():
         attn_ms = sum(hev.ms(4 * i, 4 * i + 1) for i in range(K)) / K
         rs_ms = sum(hev.ms(4 * i + 2, 4 * i + 3) for i in range(K)) / K
         hev.close()
-        attn_name = "attn_mfma_kernel" if w["dtype"] == "bf16" else "attn_valu_kernel"
+        attn_name = attention_kernel_name(w, cfg)
         kernels[attn_name] = {"us": attn_ms * 1e3, "alg_bytes": attn_b, "GB_s": attn_b / attn_ms / 1e6,
                               "TFLOP_s": attn_f / attn_ms / 1e9}
         kernels["row_stats_kernel"] = {"us": rs_ms * 1e3, "alg_bytes": rs_b, "GB_s": rs_b / rs_ms / 1e6}

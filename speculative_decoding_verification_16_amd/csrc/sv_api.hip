@@ -64,11 +64,9 @@ sv::AttnPlan plan_attn(const sv_attn_args* a) {
   const int rmax = G * eff_max_nodes(a->max_nodes);
   pl.mfma = a->dtype == SV_BF16;
   if (pl.mfma) {
-    // 64-row workgroups by default; trees with more than 64 rows per KV head
-    // and too few (request, KV head) pairs to give every CU several
-    // workgroups take 128-row ones (fewer repeated key streams)
-    const int64_t jobs = (int64_t)a->B * a->Hkv;
-    pl.rows_per_wg = (rmax > 64 && jobs < 256) ? 128 : 64;
+    // 64 rows (16x16 MFMA) when every KV head has at most 64 query rows,
+    // else 128-row workgroups on 32x32 MFMA tiles
+    pl.rows_per_wg = rmax <= 64 ? 64 : 128;
   } else {
     pl.rows_per_wg = 8;
   }

@@ -23,6 +23,7 @@ typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
 
@@ -401,6 +402,260 @@ void attn_mfma_kernel(AttnParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// bf16 path with 32x32 MFMA tiles (v_mfma_f32_32x32x16_bf16): every wave owns
+// 32 query rows, so each K / V fragment read from LDS feeds twice as many rows
+// as with 16x16 tiles at the same register cost per row.
+//
+// S^T = K Q^T per 32-key block: lane l holds keys 8 (v / 4) + 4 (l / 32) +
+// v % 4 (v = 0..15) of row l % 32. For the PV contraction the 64 keys of a
+// tile are taken in k-steps kk of 16: lane half h = l / 32 contributes keys
+// 16 kk + 4 h + 0..3 and 16 kk + 8 + 4 h + 0..3, exactly elements
+// 8 (kk % 2) .. + 7 of its score block kk / 2, so P^T needs no shuffle; the
+// V^T operand is read in the same key order with transposed LDS reads.
+// O^T per 32-dim block db: lane l holds dims 32 db + 8 (v / 4) + 4 h + v % 4
+// of row l % 32.
+template <int D, int NBUF, int NW, int WPE>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE)))
+void attn_mfma32_kernel(AttnParams p) {
+  constexpr int NT = 64 * NW;        // threads
+  constexpr int KT = 64;             // keys per tile
+  constexpr int KS = D / 16;         // k-steps of S^T (16 head dims each)
+  constexpr int DB = D / 32;         // 32-wide blocks of the output head dim
+  constexpr int UNITS = D / 8;       // 16-byte units per K / V row
+  constexpr int ROWS = 32 * NW;
+  constexpr int PER_THREAD = KT * D / 8 / NT;
+  static_assert(PER_THREAD >= 1 && KT * D / 8 == PER_THREAD * NT, "tile / thread split");
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[KT * D];
+
+  // XCD-aware decode: id = ((job / 8) * n_rowgroups + rg) * 8 + job % 8
+  const int lin = blockIdx.x;
+  const int qd = lin >> 3;
+  const int rg = qd % p.n_rowgroups;
+  const int job = (qd / p.n_rowgroups) * 8 + (lin & 7);
+  if (job >= p.n_jobs) return;
+  const int split = job % p.splits;
+  const int bg = job / p.splits;
+  const int g = bg % p.Hkv, b = bg / p.Hkv;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, h = lane >> 5;
+
+  const int n0 = p.cu_nodes[b], n1 = p.cu_nodes[b + 1];
+  const int T = n1 - n0;
+  if (n0 < 0 || T < 0 || T > p.max_nodes || n1 > p.N) return;  // flagged by tree prep / host
+  const int L = p.ctx_len[b];
+  if (L < 0 || (int64_t)L + T > p.Lcap) {
+    if (tid == 0 && rg == 0 && split == 0 && g == 0) flag(p.status, kStCtx);
+    return;
+  }
+  const int R = p.G * T;
+  const int row0 = rg * ROWS;
+  if (row0 >= R) return;
+  const int nkeys = L + T;
+  const int kchunk = ((nkeys + p.splits - 1) / p.splits + KT - 1) / KT * KT;
+  const int kb = split * kchunk;
+  const int ke = min(nkeys, kb + kchunk);
+  const int NH = p.N * p.Hq;
+
+  // the 32 rows of this wave: r = row0 + 32 wave + l32
+  const int rbase = row0 + 32 * wave;
+  const bool wave_any = rbase < R;
+  const int r = rbase + l32;
+  bf16x8_t qf[KS];
+  uint64_t amask = 0;
+  int orow = -1;  // packed (node, q head) index, -1 if the row does not exist
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) qf[ks] = bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+  if (r < R) {
+    const int j = r / p.G, hh = r - j * p.G;
+    orow = (n0 + j) * p.Hq + g * p.G + hh;
+    amask = p.anc[n0 + j];
+    const uint16_t* qp = (const uint16_t*)p.q + (int64_t)orow * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = *(const bf16x8_t*)(qp + 16 * ks + 8 * h);
+  }
+
+  if (kb >= ke) {  // empty split: contributes nothing to the merge
+    if (orow >= 0 && h == 0) p.ml_part[(int64_t)split * NH + orow] = make_float2(-INFINITY, 0.f);
+    return;
+  }
+
+  const int64_t head_off = ((int64_t)b * p.Hkv + g) * p.Lcap * D;
+  const uint16_t* kbase = (const uint16_t*)p.k + head_off;
+  const uint16_t* vbase = (const uint16_t*)p.v + head_off;
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, ke * D * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, ke * D * 2, 0x00020000);
+  int koff[PER_THREAD];
+#pragma unroll
+  for (int i = 0; i < PER_THREAD; ++i) {
+    const int c = tid + NT * i;
+    koff[i] = ((c / UNITS) * D + 8 * (c % UNITS)) * 2;
+  }
+  i32x4_t kreg[NBUF][PER_THREAD], vreg[NBUF][PER_THREAD];  // ring of key tiles in flight
+  // V^T operand addressing: lane l of 16-lane group G = l / 16 reads the head
+  // dims 16 (G % 2) + 4 (l % 4) .. + 3 of key base + (l % 16) / 4
+  const int lg = lane & 15, G = lane >> 4;
+  const int vt_s = lg >> 2, vt_dg = G & 1;
+  const int vt_lane = (4 * (G >> 1) + vt_s) * D + 4 * (lg & 1) + 8 * ((lg >> 1) & 1);
+
+  f32x16_t o[DB];
+  float m = -INFINITY, l = 0.f;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x16_t{};
+
+#pragma unroll
+  for (int s = 0; s < NBUF; ++s) {
+    if (kb + s * KT < ke) {
+      const int so = (kb + s * KT) * D * 2;
+#pragma unroll
+      for (int i = 0; i < PER_THREAD; ++i) {
+        kreg[s][i] = __builtin_amdgcn_raw_buffer_load_b128(krs, koff[i], so, 0);
+        vreg[s][i] = __builtin_amdgcn_raw_buffer_load_b128(vrs, koff[i], so, 0);
+      }
+    }
+  }
+
+  for (int tb = kb; tb < ke; tb += NBUF * KT) {
+#pragma unroll
+  for (int s = 0; s < NBUF; ++s) {
+    const int t0 = tb + s * KT;
+    if (t0 >= ke) break;
+    __syncthreads();  // the previous tile's LDS reads are done
+#pragma unroll
+    for (int i = 0; i < PER_THREAD; ++i) {
+      const int c = tid + NT * i;
+      const int kk = c / UNITS, dc = c % UNITS;
+      *(i32x4_t*)(Ks + kk * D + 8 * (dc ^ (kk & 7))) = kreg[s][i];
+      *(i32x4_t*)(Vs + kk * D + 8 * (dc ^ (2 * (kk & 3)))) = vreg[s][i];
+    }
+    __syncthreads();
+    if (t0 + NBUF * KT < ke) {  // refill this ring slot NBUF tiles ahead
+      const int so = (t0 + NBUF * KT) * D * 2;
+#pragma unroll
+      for (int i = 0; i < PER_THREAD; ++i) {
+        kreg[s][i] = __builtin_amdgcn_raw_buffer_load_b128(krs, koff[i], so, 0);
+        vreg[s][i] = __builtin_amdgcn_raw_buffer_load_b128(vrs, koff[i], so, 0);
+      }
+    }
+    if (!wave_any) continue;  // this wave has no rows: it only helps to stream the tiles
+    const bool full = (t0 + KT <= ke) && (t0 + KT <= L);
+
+    // S^T, two 32-key blocks
+    f32x16_t sc[2];
+#pragma unroll
+    for (int kq = 0; kq < 2; ++kq) {
+      sc[kq] = f32x16_t{};
+      const int key = 32 * kq + l32;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8_t a = *(const bf16x8_t*)(Ks + key * D + 8 * ((2 * ks + h) ^ (key & 7)));
+        sc[kq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sc[kq], 0, 0, 0);
+      }
+    }
+
+    // online softmax in the log2 domain (as in the 16x16 kernel)
+    if (!full) {  // wave-uniform: only tiles that reach the draft slots or the split end
+      const int dl = L - t0;
+      const uint64_t ctx_bits = dl >= 64 ? ~0ull : (dl <= 0 ? 0ull : ((1ull << dl) - 1ull));
+      const uint64_t drf_bits = dl >= 64 ? 0ull : (dl >= 0 ? (amask << dl) : (-dl >= 64 ? 0ull : (amask >> -dl)));
+      const int dv = ke - t0;
+      const uint64_t valid = dv >= 64 ? ~0ull : ((1ull << dv) - 1ull);
+      const uint64_t lane_bits = ((ctx_bits | drf_bits) & valid) >> (4 * h);
+#pragma unroll
+      for (int kq = 0; kq < 2; ++kq)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const bool vis = (lane_bits >> (32 * kq + 8 * (v >> 2) + (v & 3))) & 1ull;
+          sc[kq][v] = vis ? sc[kq][v] : -INFINITY;
+        }
+    }
+    float mx = sc[0][0];
+#pragma unroll
+    for (int kq = 0; kq < 2; ++kq)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[kq][v]);
+    {
+      // the row's other 32 keys are in lane l ^ 32
+      const uint32_t u = __float_as_uint(mx);
+      const auto r32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+      mx = fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+    }
+    const float mnew = fmaxf(m, mx * p.scale_log2);
+    const float msub = mnew == -INFINITY ? 0.f : mnew;
+    float lsum = 0.f;
+#pragma unroll
+    for (int kq = 0; kq < 2; ++kq)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        sc[kq][v] = __builtin_amdgcn_exp2f(fmaf(sc[kq][v], p.scale_log2, -msub));
+        lsum += sc[kq][v];
+      }
+    if (__any(mnew != m)) {
+      const float alpha = __builtin_amdgcn_exp2f(m - msub);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+    }
+    l += lsum;
+    m = mnew;
+
+    // O^T += V^T P^T in four 16-key steps
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int kq = kk >> 1, v0 = 8 * (kk & 1);
+      const bf16x2_t p01 = {(__bf16)sc[kq][v0 + 0], (__bf16)sc[kq][v0 + 1]};
+      const bf16x2_t p23 = {(__bf16)sc[kq][v0 + 2], (__bf16)sc[kq][v0 + 3]};
+      const bf16x2_t p45 = {(__bf16)sc[kq][v0 + 4], (__bf16)sc[kq][v0 + 5]};
+      const bf16x2_t p67 = {(__bf16)sc[kq][v0 + 6], (__bf16)sc[kq][v0 + 7]};
+      const i32x4_t wv = {(int)__builtin_bit_cast(uint32_t, p01), (int)__builtin_bit_cast(uint32_t, p23),
+                          (int)__builtin_bit_cast(uint32_t, p45), (int)__builtin_bit_cast(uint32_t, p67)};
+      const bf16x8_t pk = __builtin_bit_cast(bf16x8_t, wv);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int base = (16 * kk) * D + vt_lane + 16 * ((2 * db + vt_dg) ^ vt_s);
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(lds_u16_t*)(Vs + base));
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(lds_u16_t*)(Vs + base + 8 * D));
+        const bf16x8_t a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk, o[db], 0, 0, 0);
+      }
+    }
+  }
+  }
+
+  if (!wave_any) return;
+  float lt;
+  {
+    const uint32_t u = __float_as_uint(l);
+    const auto r32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    lt = __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+  }
+  if (orow < 0) return;
+  if (p.splits == 1) {
+    const float inv = 1.0f / lt;
+    float* op = p.out + (int64_t)orow * D + 4 * h;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g8 = 0; g8 < 4; ++g8)
+        *(float4*)(op + 32 * db + 8 * g8) = make_float4(o[db][4 * g8] * inv, o[db][4 * g8 + 1] * inv,
+                                                        o[db][4 * g8 + 2] * inv, o[db][4 * g8 + 3] * inv);
+  } else {
+    float* op = p.o_part + ((int64_t)split * NH + orow) * D + 4 * h;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g8 = 0; g8 < 4; ++g8)
+        *(float4*)(op + 32 * db + 8 * g8) = make_float4(o[db][4 * g8], o[db][4 * g8 + 1], o[db][4 * g8 + 2],
+                                                        o[db][4 * g8 + 3]);
+    if (h == 0) p.ml_part[(int64_t)split * NH + orow] = make_float2(m, lt);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 path (plain VALU): 8 query rows per workgroup, 32-key tiles in LDS.
 // Thread t handles row t/32 and, per tile, key t%32 for the scores and head
 // dims t%32 + 32k for the output.
@@ -570,14 +825,15 @@ hipError_t launch_tree_prep(int B, int N, int max_nodes, const int32_t* cu_nodes
   return hipGetLastError();
 }
 
-// 64 rows: 4 waves x one 16-row block, three workgroups per CU; 128 rows:
-// 8 waves x one 16-row block, two workgroups per CU. One key tile in flight
-// per workgroup in both (measured on MI355X: more independent workgroups per
-// CU beat deeper rings in fewer of them).
+// Up to 64 query rows per KV head (short chains, narrow trees): 4 waves x one
+// 16-row block (16x16 MFMA), three workgroups per CU. Wider trees: 4 waves x
+// one 32-row block (32x32 MFMA, half the LDS operand bytes per row), two
+// workgroups per CU. One key tile in flight per workgroup in both: measured
+// on MI355X, more independent workgroups per CU beat deeper rings.
 template <int D>
 static void launch_mfma_d(const AttnParams& p, int rows_per_wg, dim3 grid, hipStream_t stream) {
   if (rows_per_wg <= 64) attn_mfma_kernel<D, 1, 4, 1, 3><<<grid, dim3(256), 0, stream>>>(p);
-  else attn_mfma_kernel<D, 1, 8, 1, 4><<<grid, dim3(512), 0, stream>>>(p);
+  else attn_mfma32_kernel<D, 1, 4, 2><<<grid, dim3(256), 0, stream>>>(p);
 }
 
 hipError_t launch_attention(const AttnParams& p, const AttnPlan& plan, bool bf16, hipStream_t stream,
