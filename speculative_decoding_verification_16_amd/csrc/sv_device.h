@@ -107,6 +107,14 @@ __device__ __forceinline__ float target_prob(float logit, float lmax, float c, f
   return target_weight(logit, lmax, c) * invS;
 }
 
+// Residual weight of one token, S * max(0, p - cc q), in fp32: the caller
+// passes ccS = cc * S and divides sums of these weights by S in fp64. One fma
+// and one max per token; the rounding (a few fp32 ulps of p) stays far below
+// the 1e-6 CDF tolerance.
+__device__ __forceinline__ float residual_weight(float logit, float q, float lmax, float c, float ccS) {
+  return fmaxf(0.f, fmaf(-ccS, q, target_weight(logit, lmax, c)));
+}
+
 // Row normalisation from its chunk statistics, computed by one full wave
 // (every lane returns the same values): lmax = max over chunks,
 // S = sum_ch s_ch * exp2((lmax_ch - lmax) * c) in fp64, summed lane-strided

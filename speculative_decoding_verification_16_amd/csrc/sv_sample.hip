@@ -166,42 +166,70 @@ struct WalkShared {
   int32_t bad;
 };
 
-// Mass of half-chunk h (2048 tokens) under max(0, p - cc q), one wave, its
-// logits and q requested in one go (32 + 32 values per lane).
-template <bool VEC>
-__device__ __forceinline__ double residual_half(const float* lrow, const float* qrow, int V, int h, float lmax,
-                                                float c, float invS, double cc, int lane) {
-  const int begin = h * kHalf, end = min(V, begin + kHalf);
-  double acc = 0.0;
-  if (VEC) {
-    const float4* l4 = (const float4*)(lrow + begin);
-    const float4* q4 = (const float4*)(qrow + begin);
-    const int n4 = end > begin ? (end - begin) >> 2 : 0;  // V % 4 == 0 on this path
-    float4 lv[8], qv[8];
+// Mass of half-chunk h (2048 tokens) under max(0, p - cc q), one wave. The
+// vector path splits this into a load step (32 + 32 values per lane) and a
+// reduce step, so that a wave can have the next half-chunk in flight while it
+// reduces the current one. The loads are buffer loads whose resource covers
+// exactly the row: a float4 past the row's end reads as zero without touching
+// memory (the reduce masks it), so every step issues the same loads with no
+// branch, and the compiler waits for exactly the half-chunk being reduced.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+struct HalfRegs {
+  f32x4_t l[8], q[8];
+};
+
+__device__ __forceinline__ void half_load(HalfRegs& r, __amdgpu_buffer_rsrc_t lrs, __amdgpu_buffer_rsrc_t qrs, int h,
+                                          int lane) {
+  const int off = h * (kHalf * 4) + 16 * lane;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int idx = lane + 64 * i;
-      lv[i] = idx < n4 ? l4[idx] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-      qv[i] = idx < n4 ? q4[idx] : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      acc += fmax(0.0, (double)target_prob(lv[i].x, lmax, c, invS) - cc * (double)qv[i].x);
-      acc += fmax(0.0, (double)target_prob(lv[i].y, lmax, c, invS) - cc * (double)qv[i].y);
-      acc += fmax(0.0, (double)target_prob(lv[i].z, lmax, c, invS) - cc * (double)qv[i].z);
-      acc += fmax(0.0, (double)target_prob(lv[i].w, lmax, c, invS) - cc * (double)qv[i].w);
-    }
-  } else {
-    float lv[32], qv[32];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const int idx = begin + lane + 64 * i;
-      lv[i] = idx < end ? lrow[idx] : -INFINITY;
-      qv[i] = idx < end ? qrow[idx] : 0.f;
-    }
-#pragma unroll
-    for (int i = 0; i < 32; ++i) acc += fmax(0.0, (double)target_prob(lv[i], lmax, c, invS) - cc * (double)qv[i]);
+  for (int i = 0; i < 8; ++i) {
+    r.l[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(lrs, off + 1024 * i, 0, 0));
+    r.q[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(qrs, off + 1024 * i, 0, 0));
   }
+}
+
+// Unnormalised mass S * sum max(0, p - cc q) of the half-chunk in r: the four
+// tokens of a float4 are added in fp32, the rest in fp64. MASK drops float4s
+// past the row's end (only the row's last half-chunk needs it).
+template <bool MASK>
+__device__ __forceinline__ double half_reduce(const HalfRegs& r, int V, int h, int lane, float lmax, float c,
+                                              float ccS) {
+  const int n4 = V >> 2;
+  const int b4 = h * (kHalf / 4) + lane;
+  double acc = 0.0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float t = (residual_weight(r.l[i].x, r.q[i].x, lmax, c, ccS) +
+               residual_weight(r.l[i].y, r.q[i].y, lmax, c, ccS)) +
+              (residual_weight(r.l[i].z, r.q[i].z, lmax, c, ccS) +
+               residual_weight(r.l[i].w, r.q[i].w, lmax, c, ccS));
+    if (MASK) t = b4 + 64 * i < n4 ? t : 0.f;
+    acc += (double)t;
+  }
+  return wave_sum(acc);
+}
+
+template <bool VEC>
+__device__ __forceinline__ double half_mass(const HalfRegs& r, int V, int h, int lane, float lmax, float c, float ccS) {
+  // wave-uniform test: is the whole half-chunk inside the row?
+  return (h + 1) * kHalf <= V ? half_reduce<false>(r, V, h, lane, lmax, c, ccS)
+                              : half_reduce<true>(r, V, h, lane, lmax, c, ccS);
+}
+
+__device__ __forceinline__ double half_scalar(const float* lrow, const float* qrow, int V, int h, float lmax, float c,
+                                              float ccS, int lane) {
+  const int begin = h * kHalf, end = min(V, begin + kHalf);
+  float lv[32], qv[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const int idx = begin + lane + 64 * i;
+    lv[i] = idx < end ? lrow[idx] : -INFINITY;
+    qv[i] = idx < end ? qrow[idx] : 0.f;
+  }
+  double acc = 0.0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) acc += (double)residual_weight(lv[i], qv[i], lmax, c, ccS);
   return wave_sum(acc);
 }
 
@@ -210,11 +238,36 @@ __device__ __forceinline__ double residual_half(const float* lrow, const float* 
 // (bitwise the same in every thread).
 template <bool VEC>
 __device__ __forceinline__ double residual_pass(WalkShared& sh, const float* lrow, const float* qrow, int V, int nch, float lmax,
-                                float c, float invS, double cc) {
+                                float c, double S, double cc) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int h = wave; h < 2 * nch; h += kWalkWaves) {
-    const double m = residual_half<VEC>(lrow, qrow, V, h, lmax, c, invS, cc, lane);
-    if (lane == 0) sh.hsum[h] = m;
+  const int nh = 2 * nch;
+  const float ccS = (float)(cc * S);
+  const double invS = 1.0 / S;
+  if (VEC) {
+    // two half-chunks per wave in flight: the next one's loads are issued
+    // before the current one is reduced (past the row's end they read zeros).
+    if (wave < nh) {
+      const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc((void*)lrow, (short)0, V * 4, 0x00020000);
+      const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc((void*)qrow, (short)0, V * 4, 0x00020000);
+      HalfRegs ra, rb;
+      half_load(ra, lrs, qrs, wave, lane);
+      for (int h = wave; h < nh; h += 2 * kWalkWaves) {
+        const int h1 = h + kWalkWaves;
+        half_load(rb, lrs, qrs, h1, lane);
+        const double m0 = half_mass<VEC>(ra, V, h, lane, lmax, c, ccS);
+        if (lane == 0) sh.hsum[h] = m0 * invS;
+        half_load(ra, lrs, qrs, h1 + kWalkWaves, lane);
+        if (h1 < nh) {
+          const double m1 = half_mass<VEC>(rb, V, h1, lane, lmax, c, ccS);
+          if (lane == 0) sh.hsum[h1] = m1 * invS;
+        }
+      }
+    }
+  } else {
+    for (int h = wave; h < nh; h += kWalkWaves) {
+      const double m = half_scalar(lrow, qrow, V, h, lmax, c, ccS, lane);
+      if (lane == 0) sh.hsum[h] = m * invS;
+    }
   }
   __syncthreads();
   for (int ch = threadIdx.x; ch < nch; ch += kWalkThreads) sh.csum[ch] = sh.hsum[2 * ch] + sh.hsum[2 * ch + 1];
@@ -239,7 +292,9 @@ __device__ __forceinline__ double residual_pass(WalkShared& sh, const float* lro
 // prefix crosses the remainder picks the token among its 8.
 template <bool VEC>
 __device__ __forceinline__ int draw_token(WalkShared& sh, const float* lrow, const float* qrow, int V, int nch, int level,
-                          float lmax, float c, float invS, double cc, double u, double total) {
+                          float lmax, float c, double S, double cc, double u, double total) {
+  const float ccS = (float)(cc * S);
+  const double invS = 1.0 / S;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const double target = u * total;
   double run = 0.0, rem = 0.0;
@@ -288,9 +343,10 @@ __device__ __forceinline__ int draw_token(WalkShared& sh, const float* lrow, con
   int lastpos = -1;
 #pragma unroll
   for (int i = 0; i < kDrawPerLane; ++i) {
-    // weights of the distribution being drawn from (level 0: unnormalised p)
+    // weights of the distribution being drawn from (level 0: unnormalised p;
+    // above: max(0, p - cc q) as the residual passes compute it)
     w[i] = level == 0 ? (double)target_weight(lv[i], lmax, c)
-                      : fmax(0.0, (double)target_prob(lv[i], lmax, c, invS) - cc * (double)qv[i]);
+                      : (double)residual_weight(lv[i], qv[i], lmax, c, ccS) * invS;
     seg += w[i];
     lastpos = w[i] > 0.0 ? x0 + i : lastpos;
   }
@@ -444,7 +500,7 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(SampleParams p) {
       if (ok) { accepted = ch; break; }
       // rejected: the next sibling is tested against the next residual level
       const double cn = cc + M;
-      const double Mn = residual_pass<VEC>(sh, lrow, qrow, p.V, p.nch, st.lmax, p.c, invS, cn);
+      const double Mn = residual_pass<VEC>(sh, lrow, qrow, p.V, p.nch, st.lmax, p.c, st.S, cn);
       ++passes;
       if (__builtin_amdgcn_readfirstlane(Mn > 0.0 ? 1 : 0)) {
         cc = cn;
@@ -474,13 +530,13 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(SampleParams p) {
       total = st.S;
     } else {
       if (!csum_ok) {
-        residual_pass<VEC>(sh, lrow, qrow, p.V, p.nch, st.lmax, p.c, invS, cc);
+        residual_pass<VEC>(sh, lrow, qrow, p.V, p.nch, st.lmax, p.c, st.S, cc);
         ++passes;
       }
       total = M;
     }
     const double uf = uniform01(p.seed, rid, 0u, 1u, p.step);
-    bonus = draw_token<VEC>(sh, lrow, qrow, p.V, p.nch, level, st.lmax, p.c, invS, cc, uf, total);
+    bonus = draw_token<VEC>(sh, lrow, qrow, p.V, p.nch, level, st.lmax, p.c, st.S, cc, uf, total);
     break;
   }
   if (tid == 0) {
