@@ -71,6 +71,9 @@ sv::AttnPlan plan_attn(const sv_attn_args* a) {
     pl.rows_per_wg = 8;
   }
   pl.n_rowgroups = (rmax + pl.rows_per_wg - 1) / pl.rows_per_wg;
+  // with several row groups, requests with fewer rows would leave dead blocks
+  // spread through the grid; they are listed out on the device instead
+  pl.compact = pl.mfma && pl.n_rowgroups > 1;
   const int64_t max_splits_len = a->Lcap / 64 > 0 ? a->Lcap / 64 : 1;
   if (a->num_splits > 0) {
     pl.splits = (int)(a->num_splits < max_splits_len ? a->num_splits : max_splits_len);
@@ -94,7 +97,7 @@ sv::AttnPlan plan_attn(const sv_attn_args* a) {
 }
 
 struct WsLayout {
-  size_t anc = 0, o_part = 0, ml_part = 0, stats = 0, rowstats = 0, total = 0;
+  size_t anc = 0, o_part = 0, ml_part = 0, items = 0, item_tot = 0, stats = 0, rowstats = 0, total = 0;
 };
 
 size_t attn_part_bytes(const sv_attn_args* a, const sv::AttnPlan& pl, size_t* ml) {
@@ -117,6 +120,12 @@ WsLayout layout(const sv_attn_args* a, const sv_sample_args* s) {
     if (!a->anc_mask) {
       w.anc = off;
       off += align_up((size_t)a->total_nodes * sizeof(uint64_t));
+    }
+    if (pl.compact) {
+      w.items = off;
+      off += align_up((size_t)sv::attn_grid_blocks(a->B * a->Hkv * pl.splits, pl.n_rowgroups) * sizeof(int32_t));
+      w.item_tot = off;
+      off += align_up(8 * sizeof(int32_t));
     }
     size_t ml = 0;
     const size_t op = attn_part_bytes(a, pl, &ml);
@@ -187,13 +196,7 @@ sv_status run_attn(const sv_attn_args* a, char* ws, const WsLayout& w, hipStream
   if (a->B == 0 || a->total_nodes == 0) return SV_OK;
   const sv::AttnPlan pl = plan_attn(a);
   const int mn = eff_max_nodes(a->max_nodes);
-  const uint64_t* anc = a->anc_mask;
-  if (!anc) {
-    uint64_t* w_anc = (uint64_t*)(ws + w.anc);
-    hipError_t e = sv::launch_tree_prep(a->B, a->total_nodes, mn, a->cu_nodes, a->parent, w_anc, a->status, st);
-    if (e != hipSuccess) return hip_fail(e, "tree prep launch");
-    anc = w_anc;
-  }
+  uint64_t* w_anc = a->anc_mask ? nullptr : (uint64_t*)(ws + w.anc);  // built from parent when not given
   sv::AttnParams p{};
   p.B = a->B;
   p.N = a->total_nodes;
@@ -205,7 +208,7 @@ sv_status run_attn(const sv_attn_args* a, char* ws, const WsLayout& w, hipStream
   p.Lcap = a->Lcap;
   p.ctx_len = a->ctx_len;
   p.cu_nodes = a->cu_nodes;
-  p.anc = anc;
+  p.anc = a->anc_mask ? a->anc_mask : w_anc;
   p.q = a->q;
   p.k = a->k_cache;
   p.v = a->v_cache;
@@ -216,10 +219,14 @@ sv_status run_attn(const sv_attn_args* a, char* ws, const WsLayout& w, hipStream
   p.rows_per_wg = pl.rows_per_wg;
   p.n_rowgroups = pl.n_rowgroups;
   p.n_jobs = a->B * a->Hkv * pl.splits;
+  p.items = pl.compact ? (const int32_t*)(ws + w.items) : nullptr;
+  p.item_tot = pl.compact ? (const int32_t*)(ws + w.item_tot) : nullptr;
   const float scale = a->scale > 0.f ? a->scale : (float)(1.0 / sqrt((double)a->D));
   p.scale_log2 = (float)((double)scale * 1.4426950408889634);
   p.status = a->status;
-  hipError_t e = sv::launch_attention(p, pl, a->dtype == SV_BF16, st, (hipEvent_t)a->prof_start,
+  hipError_t e = sv::launch_attn_prep(p, pl, a->parent, w_anc, st);
+  if (e != hipSuccess) return hip_fail(e, "attention prep launch");
+  e = sv::launch_attention(p, pl, a->dtype == SV_BF16, st, (hipEvent_t)a->prof_start,
                                       (hipEvent_t)a->prof_stop);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return SV_OK;

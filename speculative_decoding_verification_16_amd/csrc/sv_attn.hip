@@ -48,37 +48,124 @@ __device__ __forceinline__ float row_sum4(float v) {
 
 // ---------------------------------------------------------------------------
 // Tree preprocessing: ancestor-or-self bitmask of every node. One wave per
-// request, lane j owns node j and climbs its parent chain (each step must go
-// to a strictly smaller index, so the climb ends within j steps).
-__global__ __launch_bounds__(64) void tree_prep_kernel(int B, int N, int max_nodes, const int32_t* cu_nodes,
-                                                       const int32_t* parent, uint64_t* anc, int32_t* status) {
-  __shared__ int32_t par[kMaxNodes];
-  const int b = blockIdx.x, j = threadIdx.x;
-  if (b == 0 && j == 0 && cu_nodes[B] != N) flag(status, kStPacking);
-  const int n0 = cu_nodes[b], n1 = cu_nodes[b + 1];
+// request; lane j owns node j and climbs its parent chain with wave shuffles
+// (each step must go to a strictly smaller index, so the climb ends within j
+// steps). A chain that breaks that rule marks the node as a child of the root.
+__device__ __forceinline__ void tree_masks(const AttnParams& p, const int32_t* parent, uint64_t* anc, int b, int j) {
+  if (b == 0 && j == 0 && p.cu_nodes[p.B] != p.N) flag(p.status, kStPacking);
+  const int n0 = p.cu_nodes[b], n1 = p.cu_nodes[b + 1];
   const int T = n1 - n0;
-  if (n0 < 0 || T < 0 || T > max_nodes || n1 > N) {
-    if (j == 0) flag(status, kStPacking);
+  if (n0 < 0 || T < 0 || T > p.max_nodes || n1 > p.N) {
+    if (j == 0) flag(p.status, kStPacking);
     return;
   }
-  if (j < T) par[j] = parent[n0 + j];
-  __syncthreads();
-  if (j < T) {
-    uint64_t m = 1ull << j;
-    int prev = j, x = par[j];
-    bool bad = false;
-    while (x != -1) {
-      if (x < 0 || x >= prev) { bad = true; break; }
-      m |= 1ull << x;
-      prev = x;
-      x = par[x];
+  const int pj = j < T ? parent[n0 + j] : -1;
+  uint64_t m = 1ull << j;
+  int x = pj, prev = j;
+  bool bad = false;
+  for (int step = 0; step < kMaxNodes; ++step) {
+    const bool act = j < T && !bad && x != -1;
+    if (!__any(act)) break;
+    if (act) {
+      if (x < 0 || x >= prev) {
+        bad = true;
+      } else {
+        m |= 1ull << x;
+        prev = x;
+      }
     }
+    const bool go = act && !bad;
+    const int nx = __shfl(pj, go ? x : 0);
+    x = go ? nx : x;
+  }
+  if (j < T) {
     if (bad) {  // treated as a child of the root: sees the context and itself
       m = 1ull << j;
-      flag(status, kStTree);
+      flag(p.status, kStTree);
     }
     anc[n0 + j] = m;
   }
+}
+
+// ---------------------------------------------------------------------------
+// Work list of the bf16 grid. Blocks go to the XCDs round-robin by id, so the
+// grid is decoded with the XCD class x = id % 8 fixed per job: all row groups
+// of one (request, KV head, split) run on the same XCD back to back, and
+// their repeated key reads are served by that XCD's L2. Without a list:
+// id = ((job / 8) * n_rowgroups + rg) * 8 + job % 8. When requests differ in
+// row count that grid holds blocks with no rows; they still take a turn in
+// the hardware's round-robin placement over CUs, which leaves CUs idle
+// (measured on MI355X: 448 of 512 workgroup slots busy for the batch-256
+// super tree). attn_plan_kernel therefore lists the live items of each class
+// first: block 8 k + x takes the k-th live item of class x.
+__device__ __forceinline__ bool decode_block(const AttnParams& p, int lin, int& job, int& rg) {
+  if (p.items) {
+    const int x = lin & 7, k = lin >> 3;
+    if (k >= p.item_tot[x]) return false;
+    const int it = p.items[lin];
+    job = it / p.n_rowgroups;
+    rg = it - job * p.n_rowgroups;
+  } else {
+    const int qd = lin >> 3;
+    rg = qd % p.n_rowgroups;
+    job = (qd / p.n_rowgroups) * 8 + (lin & 7);
+  }
+  return job < p.n_jobs;
+}
+
+// Work list, built by one workgroup of 1024 threads: thread t handles XCD
+// class x = t % 8 and,
+// per round of 128 jobs of that class, the job 8 (m0 + t / 8) + x. A job of
+// request b has ceil(G T_b / rows_per_wg) live row groups (none when the
+// request's packing is invalid: every kernel skips those requests). The
+// per-class exclusive prefix of those counts, in job order, places each
+// job's row groups next to each other in its class list.
+__device__ __forceinline__ void attn_plan(const AttnParams& p, int32_t* items, int32_t* item_tot) {
+  __shared__ int32_t sc[1024];
+  const int t = threadIdx.x, x = t & 7, k = t >> 3;
+  const int groups = (p.n_jobs + 7) >> 3;
+  const int per_req = p.Hkv * p.splits;
+  int carry = 0;
+  for (int m0 = 0; m0 < groups; m0 += 128) {
+    const int j = 8 * (m0 + k) + x;
+    int c = 0;
+    if (j < p.n_jobs) {
+      const int b = j / per_req;
+      const int n0 = p.cu_nodes[b], n1 = p.cu_nodes[b + 1];
+      const int T = n1 - n0;
+      if (n0 >= 0 && T > 0 && T <= p.max_nodes && n1 <= p.N)
+        c = min(p.n_rowgroups, (p.G * T + p.rows_per_wg - 1) / p.rows_per_wg);
+    }
+    // inclusive scan over the 128 jobs of each class (stride 8 in t)
+    int v = c;
+    sc[t] = v;
+    __syncthreads();
+    for (int s = 8; s < 1024; s <<= 1) {
+      const int add = t >= s ? sc[t - s] : 0;
+      __syncthreads();
+      v += add;
+      sc[t] = v;
+      __syncthreads();
+    }
+    const int first = carry + v - c;
+    for (int i = 0; i < c; ++i) items[8 * (first + i) + x] = j * p.n_rowgroups + i;
+    carry += sc[1016 + x];  // class total of this round (thread k = 127)
+    __syncthreads();        // sc is rewritten by the next round
+  }
+  if (k == 0) item_tot[x] = carry;
+}
+
+// One launch before the attention kernel: blocks [0, n_tree) build the
+// ancestor masks (16 requests per block, a wave each); one more block, when
+// the grid is compacted, builds the work list (it needs only the packing).
+__global__ __launch_bounds__(1024) void attn_prep_kernel(AttnParams p, const int32_t* parent, uint64_t* anc,
+                                                         int32_t* items, int32_t* item_tot, int n_tree) {
+  if ((int)blockIdx.x < n_tree) {  // block-uniform: the tree part has no barrier
+    const int b = blockIdx.x * 16 + (threadIdx.x >> 6);
+    if (b < p.B) tree_masks(p, parent, anc, b, threadIdx.x & 63);
+    return;
+  }
+  attn_plan(p, items, item_tot);
 }
 
 // ---------------------------------------------------------------------------
@@ -102,10 +189,7 @@ __global__ __launch_bounds__(64) void tree_prep_kernel(int B, int N, int max_nod
 // r = row0 + 16 (w + NW i) + (lane % 16), i < RBW, of one (request, KV head,
 // KV split): 16 NW RBW query rows. Every K / V fragment a wave reads from LDS
 // feeds all of its row blocks. Trees with more rows than a workgroup holds
-// take several row groups that stream the same keys; the linear block id is
-// decoded so that all row groups of one (request, KV head, split) land on the
-// same XCD (blocks go to XCDs round-robin by id) back to back, and their
-// repeated key reads are served by that XCD's L2.
+// take several row groups that stream the same keys (see decode_block).
 //
 // Memory pipeline: NBUF key tiles are in flight in registers (buffer loads
 // issued NBUF tiles ahead); each tile is written to LDS, consumed by the
@@ -127,12 +211,8 @@ void attn_mfma_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * D];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[KT * D];
 
-  // XCD-aware decode: id = ((job / 8) * n_rowgroups + rg) * 8 + job % 8
-  const int lin = blockIdx.x;
-  const int qd = lin >> 3;
-  const int rg = qd % p.n_rowgroups;
-  const int job = (qd / p.n_rowgroups) * 8 + (lin & 7);
-  if (job >= p.n_jobs) return;
+  int job, rg;
+  if (!decode_block(p, blockIdx.x, job, rg)) return;
   const int split = job % p.splits;
   const int bg = job / p.splits;
   const int g = bg % p.Hkv, b = bg / p.Hkv;
@@ -428,12 +508,8 @@ void attn_mfma32_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * D];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[KT * D];
 
-  // XCD-aware decode: id = ((job / 8) * n_rowgroups + rg) * 8 + job % 8
-  const int lin = blockIdx.x;
-  const int qd = lin >> 3;
-  const int rg = qd % p.n_rowgroups;
-  const int job = (qd / p.n_rowgroups) * 8 + (lin & 7);
-  if (job >= p.n_jobs) return;
+  int job, rg;
+  if (!decode_block(p, blockIdx.x, job, rg)) return;
   const int split = job % p.splits;
   const int bg = job / p.splits;
   const int g = bg % p.Hkv, b = bg / p.Hkv;
@@ -818,10 +894,14 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(int NH, int D, int sp
 }
 
 // ---------------------------------------------------------------------------
-hipError_t launch_tree_prep(int B, int N, int max_nodes, const int32_t* cu_nodes, const int32_t* parent,
-                            uint64_t* anc, int32_t* status, hipStream_t stream) {
-  if (B <= 0) return hipSuccess;
-  tree_prep_kernel<<<dim3(B), dim3(64), 0, stream>>>(B, N, max_nodes, cu_nodes, parent, anc, status);
+hipError_t launch_attn_prep(const AttnParams& p, const AttnPlan& plan, const int32_t* parent, uint64_t* anc,
+                            hipStream_t stream) {
+  if (p.B <= 0) return hipSuccess;
+  const int n_tree = anc ? (p.B + 15) / 16 : 0;
+  const int blocks = n_tree + (plan.compact ? 1 : 0);
+  if (blocks == 0) return hipSuccess;
+  attn_prep_kernel<<<dim3(blocks), dim3(1024), 0, stream>>>(p, parent, anc, const_cast<int32_t*>(p.items),
+                                                             const_cast<int32_t*>(p.item_tot), n_tree);
   return hipGetLastError();
 }
 
@@ -841,9 +921,8 @@ hipError_t launch_attention(const AttnParams& p, const AttnPlan& plan, bool bf16
   if (p.B <= 0 || p.N <= 0) return hipSuccess;
   if (ev_start) (void)hipEventRecord(ev_start, stream);
   if (bf16) {
-    // 1-D grid, decoded XCD-aware inside the kernel
-    const int64_t groups = ((int64_t)p.n_jobs + 7) / 8;
-    const dim3 grid((unsigned)(groups * 8 * p.n_rowgroups));
+    // 1-D grid, decoded XCD-aware inside the kernel (decode_block)
+    const dim3 grid((unsigned)attn_grid_blocks(p.n_jobs, p.n_rowgroups));
     if (p.D == 128) launch_mfma_d<128>(p, plan.rows_per_wg, grid, stream);
     else launch_mfma_d<64>(p, plan.rows_per_wg, grid, stream);
   } else {

@@ -29,6 +29,11 @@ struct AttnParams {
   int32_t rows_per_wg;     // query rows (node, head-in-group) per workgroup
   int32_t n_rowgroups;     // workgroups along the rows of one (request, KV head, split)
   int32_t n_jobs;          // B * Hkv * splits
+  // compacted work list (bf16 path with several row groups): entry 8 k + x is
+  // the k-th live (job, row group) item of XCD class x, encoded as
+  // job * n_rowgroups + row_group; item_tot[x] = live items of class x
+  const int32_t* items;
+  const int32_t* item_tot;
   float scale_log2;        // softmax scale * log2(e)
   int32_t* status;
 };
@@ -38,10 +43,16 @@ struct AttnPlan {
   int rows_per_wg;
   int n_rowgroups;  // workgroups per (request, KV head, split) along rows
   int splits;
+  bool compact;     // live (job, row group) items are listed on the device first
 };
 
-hipError_t launch_tree_prep(int B, int N, int max_nodes, const int32_t* cu_nodes, const int32_t* parent,
-                            uint64_t* anc, int32_t* status, hipStream_t stream);
+// blocks of the 1-D bf16 attention grid: 8-job groups x row groups
+inline int64_t attn_grid_blocks(int64_t n_jobs, int n_rowgroups) { return (n_jobs + 7) / 8 * 8 * n_rowgroups; }
+
+// ancestor masks (when anc is given: written there from parent) and the
+// compacted work list (when plan.compact), in one launch before the attention
+hipError_t launch_attn_prep(const AttnParams& p, const AttnPlan& plan, const int32_t* parent, uint64_t* anc,
+                            hipStream_t stream);
 hipError_t launch_attention(const AttnParams& p, const AttnPlan& plan, bool bf16, hipStream_t stream,
                             hipEvent_t ev_start, hipEvent_t ev_stop);
 

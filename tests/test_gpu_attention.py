@@ -72,11 +72,81 @@ def test_attention_explicit_mask_matches_parent():
     assert torch.equal(out_mask, out_par)
 
 
+def test_attention_malformed_parent_is_flagged_and_rooted():
+    """A parent link that does not point to a smaller index is flagged (bit
+    0x01), and every node whose chain crosses it attends as a child of the
+    root; the oracle sees the equivalent valid tree."""
+    cfg = scaled(C3, B=2, L=100)
+    w = generate(cfg, "cuda", sample=False, poison=True)
+    bad_par = w["parent"].copy()
+    n0 = int(w["cu_nodes"][1])
+    bad_par[n0 + 5] = 7        # forward link
+    bad_par[n0 + 20] = -3      # below -1
+    fixed = bad_par.copy()
+    for b in range(w["B"]):
+        a0, a1 = int(w["cu_nodes"][b]), int(w["cu_nodes"][b + 1])
+        for j in range(a1 - a0):
+            x, prev, ok = int(bad_par[a0 + j]), j, True
+            while x != -1:
+                if x < 0 or x >= prev:
+                    ok = False
+                    break
+                prev, x = x, int(bad_par[a0 + x])
+            if not ok:
+                fixed[a0 + j] = -1
+    assert (fixed != w["parent"]).sum() >= 2
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = sv.attn(w["q"], w["k_cache"], w["v_cache"], w["ctx_len_t"], w["cu_nodes_t"],
+                  parent=torch.from_numpy(bad_par).cuda(), max_nodes=w["max_T"], status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) & 0x01
+    w_ref = dict(w)
+    w_ref["parent"] = fixed
+    err = float(np.abs(out.cpu().numpy() - oracle_attention(w_ref)).max())
+    assert err <= ATTN_TOL["bf16"], err
+
+
 def test_attention_is_deterministic():
     w = generate(scaled(C5, B=8, K=90, L=500), "cuda", sample=False)
     a = _run(w, num_splits=4).clone()
     b = _run(w, num_splits=4)
     assert torch.equal(a, b)
+
+
+def test_attention_wide_trees_with_empty_requests():
+    """Wide trees (several row groups per KV head) mixed with requests that
+    have no nodes: the device-side work list must skip the empty requests and
+    still cover every row group of the others."""
+    cfg = scaled(C5, B=6, K=60, L=150)
+    w = generate(cfg, "cuda", sample=False, poison=True)
+    ref = oracle_attention(w)
+    B, insert_at = w["B"], [0, 3, 6]  # empty requests before original 0, 3 and after the last
+    cu_old = w["cu_nodes"]
+    order = []  # original request index, -1 for an empty one
+    for b in range(B + 1):
+        if b in insert_at:
+            order.append(-1)
+        if b < B:
+            order.append(b)
+    cu, ctx = [0], []
+    for b in order:
+        T = 0 if b < 0 else int(cu_old[b + 1] - cu_old[b])
+        cu.append(cu[-1] + T)
+        ctx.append(int(w["ctx_len"][b]) if b >= 0 else 7)
+    cu = np.asarray(cu, dtype=np.int32)
+    assert cu[-1] == cu_old[-1]
+    kc = torch.full((len(order),) + tuple(w["k_cache"].shape[1:]), float("nan"), device="cuda").to(w["k_cache"].dtype)
+    vc = torch.full_like(kc, float("nan"))
+    for nb, b in enumerate(order):
+        if b >= 0:
+            kc[nb] = w["k_cache"][b]
+            vc[nb] = w["v_cache"][b]
+    print(f"[attn] wide trees with empty requests: B={len(order)} N={w['N']}", flush=True)
+    out = sv.attn(w["q"], kc, vc, torch.from_numpy(np.asarray(ctx, dtype=np.int32)).cuda(),
+                  torch.from_numpy(cu).cuda(), parent=w["parent_t"], max_nodes=w["max_T"])
+    torch.cuda.synchronize()
+    err = float(np.abs(out.cpu().numpy() - ref).max())
+    assert err <= ATTN_TOL["bf16"], err
 
 
 def test_attention_empty_requests_and_bad_context():
