@@ -26,6 +26,7 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 // max over lanes l, l^16, l^32, l^48 (the four 16-lane rows of a wave) with
 // the gfx950 row-swap permutes instead of LDS-routed shuffles
@@ -309,20 +310,20 @@ void attn_mfma_kernel(AttnParams p) {
 #pragma unroll
   for (int s = 0; s < NBUF; ++s) {
     const int so = (kb + s * KT) * D * 2;
-    if (kb + s * KT < ke) {
 #pragma unroll
-      for (int i = 0; i < PER_THREAD; ++i) {
-        kreg[s][i] = __builtin_amdgcn_raw_buffer_load_b128(krs, koff[i], so, 0);
-        vreg[s][i] = __builtin_amdgcn_raw_buffer_load_b128(vrs, koff[i], so, 0);
-      }
+    for (int i = 0; i < PER_THREAD; ++i) {
+      kreg[s][i] = __builtin_amdgcn_raw_buffer_load_b128(krs, koff[i], so, 0);
+      vreg[s][i] = __builtin_amdgcn_raw_buffer_load_b128(vrs, koff[i], so, 0);
     }
+    // keep the slots' loads in slot order, as the ring refills them: the
+    // wait before writing slot s can then leave the later slots in flight
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   for (int tb = kb; tb < ke; tb += NBUF * KT) {
 #pragma unroll
     for (int s = 0; s < NBUF; ++s) {
       const int t0 = tb + s * KT;
-      if (t0 >= ke) break;
       __syncthreads();  // the previous tile's LDS reads are done
 #pragma unroll
       for (int i = 0; i < PER_THREAD; ++i) {
@@ -333,16 +334,17 @@ void attn_mfma_kernel(AttnParams p) {
       }
       __syncthreads();
       // refill this ring slot with the tile NBUF positions ahead
-      const int tn = t0 + NBUF * KT;
-      if (tn < ke) {
-        const int so = tn * D * 2;
+      {
+        const int so = (t0 + NBUF * KT) * D * 2;
 #pragma unroll
         for (int i = 0; i < PER_THREAD; ++i) {
           kreg[s][i] = __builtin_amdgcn_raw_buffer_load_b128(krs, koff[i], so, 0);
           vreg[s][i] = __builtin_amdgcn_raw_buffer_load_b128(vrs, koff[i], so, 0);
         }
       }
-      if (!wave_any) continue;  // this wave has no rows: it only helps to stream the tiles
+      // past the range (last ring round): the slot was only cycled; waves
+      // without rows only help to stream the tiles
+      if (t0 >= ke || !wave_any) continue;
       const bool full = (t0 + KT <= ke) && (t0 + KT <= L);
 
       // S^T for every row block of the wave; each K fragment is read once
@@ -494,7 +496,7 @@ void attn_mfma_kernel(AttnParams p) {
 // V^T operand is read in the same key order with transposed LDS reads.
 // O^T per 32-dim block db: lane l holds dims 32 db + 8 (v / 4) + 4 h + v % 4
 // of row l % 32.
-template <int D, int NBUF, int NW, int WPE>
+template <int D, int NW, int WPE>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE)))
 void attn_mfma32_kernel(AttnParams p) {
   constexpr int NT = 64 * NW;        // threads
@@ -503,10 +505,19 @@ void attn_mfma32_kernel(AttnParams p) {
   constexpr int DB = D / 32;         // 32-wide blocks of the output head dim
   constexpr int UNITS = D / 8;       // 16-byte units per K / V row
   constexpr int ROWS = 32 * NW;
-  constexpr int PER_THREAD = KT * D / 8 / NT;
-  static_assert(PER_THREAD >= 1 && KT * D / 8 == PER_THREAD * NT, "tile / thread split");
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[KT * D];
+  constexpr int PER_THREAD = KT * UNITS / NT;  // 16-byte units per thread per K or V tile
+  static_assert(PER_THREAD >= 1 && KT * UNITS == PER_THREAD * NT, "tile / thread split");
+  // two LDS buffers each for K and V, as four arrays so that the compiler can
+  // tell the buffer being filled from the one being read
+  __shared__ __attribute__((aligned(16))) uint16_t Ks0[KT * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks1[KT * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs0[KT * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs1[KT * D];
+  // LDS swizzles. K: 16-byte unit u of row `key` at u ^ (key & 15) for
+  // D = 128 (u ^ (key & 7) for D = 64), so the 16 keys that one 256-byte read
+  // pass serves hit 16 different units. V: as in the 16x16 kernel, 16-byte
+  // unit u at u ^ 2 (key & 3); the transposed reads stay within one pass.
+  constexpr int KSWM = D >= 128 ? 15 : 7;
 
   int job, rg;
   if (!decode_block(p, blockIdx.x, job, rg)) return;
@@ -561,17 +572,34 @@ void attn_mfma32_kernel(AttnParams p) {
   const int64_t head_off = ((int64_t)b * p.Hkv + g) * p.Lcap * D;
   const uint16_t* kbase = (const uint16_t*)p.k + head_off;
   const uint16_t* vbase = (const uint16_t*)p.v + head_off;
+  // the resources cover exactly keys [0, ke): a key past the split end reads
+  // as zero without touching memory, and so does a whole tile past the range
   const __amdgpu_buffer_rsrc_t krs =
       __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, ke * D * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, ke * D * 2, 0x00020000);
-  int koff[PER_THREAD];
+  // Tiles go from HBM straight into LDS (16-byte buffer loads with the LDS
+  // flag: lane i of a wave instruction fills the 16 bytes at the instruction's
+  // LDS base + 16 i). Thread c = tid + NT i fills unit c of a tile, row
+  // kk = c / UNITS, slot u = c % UNITS, with the global unit the reads expect
+  // in that slot: K unit u ^ (kk & KSWM), V unit u ^ 2 (kk & 3). The tile
+  // start goes into the per-lane offset, so the bounds check covers it.
+  int koff[PER_THREAD], voff[PER_THREAD];
 #pragma unroll
   for (int i = 0; i < PER_THREAD; ++i) {
     const int c = tid + NT * i;
-    koff[i] = ((c / UNITS) * D + 8 * (c % UNITS)) * 2;
+    const int kk = c / UNITS, u = c % UNITS;
+    koff[i] = (kk * D + 8 * (u ^ (kk & KSWM))) * 2;
+    voff[i] = (kk * D + 8 * (u ^ (2 * (kk & 3)))) * 2;
   }
-  i32x4_t kreg[NBUF][PER_THREAD], vreg[NBUF][PER_THREAD];  // ring of key tiles in flight
+  const int wunit = 64 * wave;  // first tile unit this wave's instructions fill
+  auto dma = [&](__amdgpu_buffer_rsrc_t rs, const int* off, uint16_t* dst, int t) {
+    const int tb = (kb + t * KT) * D * 2;
+#pragma unroll
+    for (int i = 0; i < PER_THREAD; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst + 8 * (wunit + NT * i)), 16,
+                                               (unsigned)(off[i] + tb), 0, 0, 0);
+  };
   // V^T operand addressing: lane l of 16-lane group G = l / 16 reads the head
   // dims 16 (G % 2) + 4 (l % 4) .. + 3 of key base + (l % 16) / 4
   const int lg = lane & 15, G = lane >> 4;
@@ -583,58 +611,28 @@ void attn_mfma32_kernel(AttnParams p) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x16_t{};
 
-#pragma unroll
-  for (int s = 0; s < NBUF; ++s) {
-    if (kb + s * KT < ke) {
-      const int so = (kb + s * KT) * D * 2;
-#pragma unroll
-      for (int i = 0; i < PER_THREAD; ++i) {
-        kreg[s][i] = __builtin_amdgcn_raw_buffer_load_b128(krs, koff[i], so, 0);
-        vreg[s][i] = __builtin_amdgcn_raw_buffer_load_b128(vrs, koff[i], so, 0);
-      }
-    }
-  }
-
-  for (int tb = kb; tb < ke; tb += NBUF * KT) {
-#pragma unroll
-  for (int s = 0; s < NBUF; ++s) {
-    const int t0 = tb + s * KT;
-    if (t0 >= ke) break;
-    __syncthreads();  // the previous tile's LDS reads are done
-#pragma unroll
-    for (int i = 0; i < PER_THREAD; ++i) {
-      const int c = tid + NT * i;
-      const int kk = c / UNITS, dc = c % UNITS;
-      *(i32x4_t*)(Ks + kk * D + 8 * (dc ^ (kk & 7))) = kreg[s][i];
-      *(i32x4_t*)(Vs + kk * D + 8 * (dc ^ (2 * (kk & 3)))) = vreg[s][i];
-    }
-    __syncthreads();
-    if (t0 + NBUF * KT < ke) {  // refill this ring slot NBUF tiles ahead
-      const int so = (t0 + NBUF * KT) * D * 2;
-#pragma unroll
-      for (int i = 0; i < PER_THREAD; ++i) {
-        kreg[s][i] = __builtin_amdgcn_raw_buffer_load_b128(krs, koff[i], so, 0);
-        vreg[s][i] = __builtin_amdgcn_raw_buffer_load_b128(vrs, koff[i], so, 0);
-      }
-    }
-    if (!wave_any) continue;  // this wave has no rows: it only helps to stream the tiles
-    const bool full = (t0 + KT <= ke) && (t0 + KT <= L);
-
-    // S^T, two 32-key blocks
-    f32x16_t sc[2];
+  // S^T of one tile, two 32-key blocks
+  auto s_tile = [&](const uint16_t* Kb, f32x16_t* sc) {
 #pragma unroll
     for (int kq = 0; kq < 2; ++kq) {
       sc[kq] = f32x16_t{};
       const int key = 32 * kq + l32;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8_t a = *(const bf16x8_t*)(Ks + key * D + 8 * ((2 * ks + h) ^ (key & 7)));
+        const bf16x8_t a = *(const bf16x8_t*)(Kb + key * D + 8 * ((2 * ks + h) ^ (key & KSWM)));
         sc[kq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sc[kq], 0, 0, 0);
       }
     }
+  };
 
-    // online softmax in the log2 domain (as in the 16x16 kernel)
-    if (!full) {  // wave-uniform: only tiles that reach the draft slots or the split end
+  // Tile t's online softmax (log2 domain, as in the 16x16 kernel) with
+  // S_{t+1} = K_{t+1} Q^T issued in four groups of four MFMAs between its
+  // steps, then O^T += V^T P^T in four 16-key steps. The S MFMAs do not
+  // depend on the softmax, so the MFMA pipe works on them while the VALU
+  // runs the max and the exponentials.
+  auto softmax_s_pv = [&](f32x16_t* sc, f32x16_t* sn, const uint16_t* Knxt, const uint16_t* Vb, int t) {
+    const int t0 = kb + t * KT;
+    if (!((t0 + KT <= ke) && (t0 + KT <= L))) {  // wave-uniform: tiles that reach the draft slots or the split end
       const int dl = L - t0;
       const uint64_t ctx_bits = dl >= 64 ? ~0ull : (dl <= 0 ? 0ull : ((1ull << dl) - 1ull));
       const uint64_t drf_bits = dl >= 64 ? 0ull : (dl >= 0 ? (amask << dl) : (-dl >= 64 ? 0ull : (amask >> -dl)));
@@ -649,6 +647,27 @@ void attn_mfma32_kernel(AttnParams p) {
           sc[kq][v] = vis ? sc[kq][v] : -INFINITY;
         }
     }
+    // K_{t+1} fragments (a tile past the range was filled with zeros)
+    bf16x8_t ka[2][KS];
+#pragma unroll
+    for (int kq = 0; kq < 2; ++kq) {
+      const int key = 32 * kq + l32;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        ka[kq][ks] = *(const bf16x8_t*)(Knxt + key * D + 8 * ((2 * ks + h) ^ (key & KSWM)));
+    }
+    sn[0] = f32x16_t{};
+    sn[1] = f32x16_t{};
+    auto s_group = [&](int q) {  // MFMAs 4q .. 4q + 3 of S_{t+1}
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int idx = 4 * q + j, kq = idx / KS, ks = idx % KS;
+        sn[kq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kq][ks], qf[ks], sn[kq], 0, 0, 0);
+      }
+    };
+    static_assert(2 * KS % 4 == 0, "S MFMAs come in groups of four");
+    constexpr int NG = 2 * KS / 4;  // groups: 4 for D = 128, 2 for D = 64
+    s_group(0);
     float mx = sc[0][0];
 #pragma unroll
     for (int kq = 0; kq < 2; ++kq)
@@ -662,14 +681,26 @@ void attn_mfma32_kernel(AttnParams p) {
     }
     const float mnew = fmaxf(m, mx * p.scale_log2);
     const float msub = mnew == -INFINITY ? 0.f : mnew;
+    if (NG > 1) s_group(1 % NG);
     float lsum = 0.f;
 #pragma unroll
-    for (int kq = 0; kq < 2; ++kq)
+    for (int v = 0; v < 16; ++v) {
+      sc[0][v] = __builtin_amdgcn_exp2f(fmaf(sc[0][v], p.scale_log2, -msub));
+      lsum += sc[0][v];
+    }
+    if (NG > 2) s_group(2 % NG);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        sc[kq][v] = __builtin_amdgcn_exp2f(fmaf(sc[kq][v], p.scale_log2, -msub));
-        lsum += sc[kq][v];
-      }
+    for (int v = 0; v < 16; ++v) {
+      sc[1][v] = __builtin_amdgcn_exp2f(fmaf(sc[1][v], p.scale_log2, -msub));
+      lsum += sc[1][v];
+    }
+    if (NG > 3) s_group(3 % NG);
+    // ask the scheduler to keep that interleaving: one MFMA, then VALU work
+#pragma unroll
+    for (int i = 0; i < 2 * KS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+    }
     if (__any(mnew != m)) {
       const float alpha = __builtin_amdgcn_exp2f(m - msub);
       l *= alpha;
@@ -678,8 +709,6 @@ void attn_mfma32_kernel(AttnParams p) {
     }
     l += lsum;
     m = mnew;
-
-    // O^T += V^T P^T in four 16-key steps
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int kq = kk >> 1, v0 = 8 * (kk & 1);
@@ -693,14 +722,46 @@ void attn_mfma32_kernel(AttnParams p) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const int base = (16 * kk) * D + vt_lane + 16 * ((2 * db + vt_dg) ^ vt_s);
-        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(lds_u16_t*)(Vs + base));
-        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(lds_u16_t*)(Vs + base + 8 * D));
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(lds_u16_t*)(Vb + base));
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(lds_u16_t*)(Vb + base + 8 * D));
         const bf16x8_t a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk, o[db], 0, 0, 0);
       }
     }
+  };
+
+  // Pipeline: K runs one tile ahead of V. At the top of iteration t the loads
+  // of K_{t+1} and V_t are in flight and S_t is in registers; after one wait
+  // and one barrier, K_{t+2} and V_{t+1} are issued into the buffers freed by
+  // K_t and V_{t-1}, then S_{t+1} is computed while tile t's softmax and PV
+  // run (the S MFMAs do not depend on the softmax, so the two can co-issue).
+  const int nt = (ke - kb + KT - 1) / KT;
+  f32x16_t sc[2], sn[2];
+  dma(krs, koff, Ks0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  dma(krs, koff, Ks1, 1);
+  dma(vrs, voff, Vs0, 0);
+  if (wave_any) s_tile(Ks0, sc);
+  // one iteration; cur / nxt are the buffers of tiles t and t + 1 (S of the
+  // tile after the last one is computed on the zeros the range check left in
+  // its buffer and never used)
+  // (scores of tile t in scur, tile t + 1 computed into snxt; the two sets
+  // swap roles from one iteration to the next)
+  auto step = [&](int t, uint16_t* Kcur, uint16_t* Knxt, uint16_t* Vcur, uint16_t* Vnxt, f32x16_t* scur,
+                  f32x16_t* snxt) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of K_{t+1} and V_t have landed
+    __syncthreads();                // everyone's have; K_t and V_{t-1} are no longer read
+    dma(krs, koff, Kcur, t + 2);
+    dma(vrs, voff, Vnxt, t + 1);
+    if (!wave_any) return;          // waves without rows only help to stream the tiles
+    softmax_s_pv(scur, snxt, Knxt, Vcur, t);
+  };
+  for (int t = 0; t < nt; t += 2) {
+    step(t, Ks0, Ks1, Vs0, Vs1, sc, sn);
+    if (t + 1 < nt) step(t + 1, Ks1, Ks0, Vs1, Vs0, sn, sc);
   }
-  }
+  __builtin_amdgcn_s_waitcnt(0);  // no load into LDS outlives the workgroup
 
   if (!wave_any) return;
   float lt;
@@ -906,14 +967,15 @@ hipError_t launch_attn_prep(const AttnParams& p, const AttnPlan& plan, const int
 }
 
 // Up to 64 query rows per KV head (short chains, narrow trees): 4 waves x one
-// 16-row block (16x16 MFMA), three workgroups per CU. Wider trees: 4 waves x
-// one 32-row block (32x32 MFMA, half the LDS operand bytes per row), two
-// workgroups per CU. One key tile in flight per workgroup in both: measured
-// on MI355X, more independent workgroups per CU beat deeper rings.
+// 16-row block (16x16 MFMA), three workgroups per CU, key tiles staged
+// through registers one tile ahead. Wider trees: 4 waves x one 32-row block
+// (32x32 MFMA, half the LDS operand bytes per row), two workgroups per CU,
+// key tiles loaded straight into double-buffered LDS with the next tile's S
+// computed alongside the current tile's softmax.
 template <int D>
 static void launch_mfma_d(const AttnParams& p, int rows_per_wg, dim3 grid, hipStream_t stream) {
   if (rows_per_wg <= 64) attn_mfma_kernel<D, 1, 4, 1, 3><<<grid, dim3(256), 0, stream>>>(p);
-  else attn_mfma32_kernel<D, 1, 4, 2><<<grid, dim3(256), 0, stream>>>(p);
+  else attn_mfma32_kernel<D, 4, 2><<<grid, dim3(256), 0, stream>>>(p);
 }
 
 hipError_t launch_attention(const AttnParams& p, const AttnPlan& plan, bool bf16, hipStream_t stream,
