@@ -909,49 +909,45 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Split-K merge: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
-// One wave per (node, query head): the split headers are reduced lane-
-// parallel (fixed butterfly order), then every lane sums its head dims over
-// the splits in split order with eight splits' loads in flight at a time.
+// Split-K merge: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s with
+// M = max_s m_s over the splits that saw a key. A row of D head dims is
+// spread over D / 4 lanes (one float4 each). Splits are taken eight at a
+// time: every header and partial row of a chunk is requested at once (no
+// load waits on another), then merged online in split order, rescaling the
+// running sums whenever the maximum grows.
 __global__ __launch_bounds__(256) void attn_combine_kernel(int NH, int D, int splits, const float* o_part,
                                                            const float2* ml_part, float* out) {
-  const int item = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int lpr = D >> 2;  // lanes per row
+  const int item = blockIdx.x * (256 / lpr) + threadIdx.x / lpr;
+  const int dl = threadIdx.x % lpr;
   if (item >= NH) return;
-  float M = -INFINITY;
-  for (int s = lane; s < splits; s += 64) {
-    const float2 ml = ml_part[(int64_t)s * NH + item];
-    if (ml.y > 0.f) M = fmaxf(M, ml.x);
-  }
-  M = wave_max(M);
-  float den = 0.f;
-  for (int s = lane; s < splits; s += 64) {
-    const float2 ml = ml_part[(int64_t)s * NH + item];
-    if (ml.y > 0.f) den += exp2f(ml.x - M) * ml.y;
-  }
+  const float4* o4 = (const float4*)o_part;
+  float M = -INFINITY, den = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = 0; s0 < splits; s0 += 8) {
+    float2 ml[8];
+    float4 ov[8];
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) den += __shfl_xor(den, o);
+    for (int u = 0; u < 8; ++u) {
+      const int s = min(s0 + u, splits - 1);  // a chunk past the last split re-reads it (ignored below)
+      ml[u] = ml_part[(int64_t)s * NH + item];
+      ov[u] = o4[((int64_t)s * NH + item) * lpr + dl];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (s0 + u >= splits || !(ml[u].y > 0.f)) continue;  // past the end, or the split saw no key of this row
+      const float mn = fmaxf(M, ml[u].x);
+      const float a = exp2f(M - mn), w = exp2f(ml[u].x - mn);  // M = -inf at first: a = 0
+      acc.x = acc.x * a + w * ov[u].x;
+      acc.y = acc.y * a + w * ov[u].y;
+      acc.z = acc.z * a + w * ov[u].z;
+      acc.w = acc.w * a + w * ov[u].w;
+      den = den * a + w * ml[u].y;
+      M = mn;
+    }
+  }
   const float inv = 1.0f / den;
-  for (int d = lane; d < D; d += 64) {
-    float acc = 0.f;
-    int s = 0;
-    for (; s + 8 <= splits; s += 8) {
-      float2 ml[8];
-      float ov[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        ml[u] = ml_part[(int64_t)(s + u) * NH + item];
-        ov[u] = o_part[((int64_t)(s + u) * NH + item) * D + d];
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (ml[u].y > 0.f) acc += exp2f(ml[u].x - M) * ov[u];
-    }
-    for (; s < splits; ++s) {
-      const float2 ml = ml_part[(int64_t)s * NH + item];
-      if (ml.y > 0.f) acc += exp2f(ml.x - M) * o_part[((int64_t)s * NH + item) * D + d];
-    }
-    out[(int64_t)item * D + d] = acc * inv;
-  }
+  ((float4*)out)[(int64_t)item * lpr + dl] = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
 }
 
 // ---------------------------------------------------------------------------
@@ -997,8 +993,9 @@ hipError_t launch_attention(const AttnParams& p, const AttnPlan& plan, bool bf16
   if (err != hipSuccess) return err;
   if (plan.splits > 1) {
     const int NH = p.N * p.Hq;
-    attn_combine_kernel<<<dim3((NH + 3) / 4), dim3(256), 0, stream>>>(NH, p.D, plan.splits, p.o_part, p.ml_part,
-                                                                        p.out);
+    const int rows_per_block = 256 / (p.D / 4);
+    attn_combine_kernel<<<dim3((NH + rows_per_block - 1) / rows_per_block), dim3(256), 0, stream>>>(
+        NH, p.D, plan.splits, p.o_part, p.ml_part, p.out);
     err = hipGetLastError();
   }
   return err;

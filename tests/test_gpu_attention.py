@@ -20,6 +20,7 @@ C2, C3, C5 = CONFIGS["c2_llama8b_chain"], CONFIGS["c3_eagle_tree"], CONFIGS["c5_
 SMALL = {
     "c1_full": CONFIGS["c1_tiny_chain"],
     "c2_small": scaled(C2, B=3, L=300),
+    "c2_long_ctx": scaled(C2, B=2, L=1200),  # room for 11 splits: two chunks of the merge
     "c3_small": scaled(C3, B=2, L=200),
     "c5_small": scaled(C5, B=6, K=60, L=150),
     "c4_small": scaled(C4_BUCKETS[10], B=2, L=700),
@@ -39,7 +40,7 @@ def _run(w, **kw):
     return out
 
 
-@pytest.mark.parametrize("splits", [0, 1, 3])
+@pytest.mark.parametrize("splits", [0, 1, 3, 11])
 @pytest.mark.parametrize("name", sorted(SMALL))
 def test_attention_small_all_outputs(name, splits):
     cfg = SMALL[name]
