@@ -295,7 +295,7 @@ def main():
                               "TFLOP_s": attn_f / attn_ms / 1e9}
         kernels["row_stats_kernel"] = {"us": rs_ms * 1e3, "alg_bytes": rs_b, "GB_s": rs_b / rs_ms / 1e6}
         rest_us = ms * 1e3 - attn_ms * 1e3 - rs_ms * 1e3
-        kernels["other(tree_prep+walk)"] = {"us": rest_us,
+        kernels["other(prep+finalize+walk)"] = {"us": rest_us,
                                             "residual_pass_bytes": float(passes.sum().item()) * 8 * w["V"]}
         dom = max((k for k in kernels if "alg_bytes" in kernels[k]), key=lambda k: kernels[k]["us"])
         dk = kernels[dom]

@@ -150,6 +150,25 @@ def test_attention_wide_trees_with_empty_requests():
     assert err <= ATTN_TOL["bf16"], err
 
 
+def test_attention_wide_trees_context_overflow_is_flagged():
+    """On the wide-tree path a request whose context overflows the cache is
+    flagged (bit 0x20) and skipped; the other requests are still exact."""
+    cfg = scaled(C5, B=5, K=50, L=120)
+    w = generate(cfg, "cuda", sample=False, poison=True)
+    ref = oracle_attention(w)
+    bad = w["ctx_len"].copy()
+    bad[2] = w["Lcap"] + 5
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = sv.attn(w["q"], w["k_cache"], w["v_cache"], torch.from_numpy(bad.astype(np.int32)).cuda(),
+                  w["cu_nodes_t"], parent=w["parent_t"], max_nodes=w["max_T"], status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) & 0x20
+    keep = np.ones(w["N"], dtype=bool)
+    keep[w["cu_nodes"][2]:w["cu_nodes"][3]] = False
+    err = float(np.abs(out.cpu().numpy()[keep] - ref[keep]).max())
+    assert err <= ATTN_TOL["bf16"], err
+
+
 def test_attention_empty_requests_and_bad_context():
     cfg = scaled(C2, B=3, L=64)
     w = generate(cfg, "cuda", sample=False)
