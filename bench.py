@@ -9,8 +9,10 @@ All inputs are synthetic, seeded, and resident in HBM before the timed region.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 Prints one JSON line: verified draft tokens/s (sum of T_b over the batch per
-second), the roofline position of the dominant kernel (algorithmic bytes over
-its HIP-event-timed duration, against the 8 TB/s HBM3E peak), and the fp64 CPU
+second) with the mean and the 10th / 50th / 90th percentile step time, the
+roofline position of the dominant kernel (algorithmic bytes over its
+HIP-event-timed duration, against the 8 TB/s HBM3E peak, with a measured
+device-to-device copy rate beside it), per-kernel times, and the fp64 CPU
 oracle timed on a bounded sample of the same workload on the host cores.
 """
 from __future__ import annotations
@@ -110,6 +112,28 @@ def copy_probe(nbytes: int):
     dt = (time.perf_counter() - t0) / 3
     print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4,
                       "copy_GB_s": round(2 * n * 4 / dt / 1e9, 1)}), flush=True)
+
+
+def copy_bandwidth(nbytes: int = 1 << 30, reps: int = 5) -> float:
+    """Measured device-to-device copy rate (bytes read + written per second,
+    GB/s) of a plain torch copy: the practical HBM ceiling reported beside
+    the vendor peak."""
+    import torch
+
+    n = nbytes // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * n * 4 / sec / 1e9
 
 
 def source_digest(rel: str) -> str:
@@ -261,15 +285,20 @@ def main():
     stream.synchronize()
     torch.cuda.synchronize()
 
+    st_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     t0 = time.perf_counter()
     for i in range(K):
         if use_events:
             a.set_prof_events(ev[i][0], ev[i][1])
             s.set_prof_events(ev[i][2], ev[i][3])
+        st_ev[i][0].record(stream)
         step(stream)
+        st_ev[i][1].record(stream)
     stream.synchronize()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    step_ms = sorted(e0.elapsed_time(e1) for e0, e1 in st_ev)
+    pct = lambda f: step_ms[min(K - 1, int(round(f * (K - 1))))]
     a.set_prof_events(None, None)
     s.set_prof_events(None, None)
 
@@ -302,7 +331,7 @@ def main():
         traffic = counter_traffic(dom, cfg.name)
         roofline = {"kernel": dom, "bound": "hbm", "achieved": round(dk["GB_s"], 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(dk["GB_s"] / HBM_PEAK_GBS, 4),
-                    "traffic": traffic}
+                    "traffic": traffic, "measured_copy_GB_s": round(copy_bandwidth(), 1)}
     else:
         roofline = None
 
@@ -320,6 +349,7 @@ def main():
         "steps": K,
         "warmup": W,
         "ms_per_step": round(ms, 4),
+        "step_ms_p10_p50_p90": [round(pct(0.1), 4), round(pct(0.5), 4), round(pct(0.9), 4)],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
