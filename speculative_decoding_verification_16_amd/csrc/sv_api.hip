@@ -64,9 +64,10 @@ sv::AttnPlan plan_attn(const sv_attn_args* a) {
   const int rmax = G * eff_max_nodes(a->max_nodes);
   pl.mfma = a->dtype == SV_BF16;
   if (pl.mfma) {
-    // 64 rows (16x16 MFMA) when every KV head has at most 64 query rows,
-    // else 128-row workgroups on 32x32 MFMA tiles
-    pl.rows_per_wg = rmax <= 64 ? 64 : 128;
+    // 64 rows (16x16 MFMA) when every KV head has at most 64 query rows; else
+    // 32x32 MFMA tiles, 256-row workgroups when every KV head fits in one,
+    // otherwise 128-row workgroups
+    pl.rows_per_wg = rmax <= 64 ? 64 : (rmax <= 128 || rmax > 256 ? 128 : 256);
   } else {
     pl.rows_per_wg = 8;
   }
@@ -81,7 +82,8 @@ sv::AttnPlan plan_attn(const sv_attn_args* a) {
     // enough workgroups for 256 CUs, but each split keeps >= 256 keys and the
     // partial outputs it adds stay below a quarter of the KV bytes
     const int64_t items = (int64_t)a->B * a->Hkv * pl.n_rowgroups;
-    const int64_t want = (512 + items - 1) / (items > 0 ? items : 1);
+    const int64_t slots = pl.rows_per_wg > 128 ? 256 : 512;  // 8-wave workgroups: one per CU
+    const int64_t want = (slots + items - 1) / (items > 0 ? items : 1);
     const int64_t by_len = a->Lcap / 256 > 0 ? a->Lcap / 256 : 1;
     const int64_t esz = a->dtype == SV_BF16 ? 2 : 4;
     const int64_t kv_bytes = 2 * (int64_t)a->B * a->Hkv * a->Lcap * a->D * esz;

@@ -27,6 +27,7 @@ SMALL = {
     "f32_tree": scaled(C3, B=2, L=100, dtype="f32"),
     "bf16_d64": scaled(C2, B=2, L=190, D=64, Hq=8, Hkv=2),
     "bf16_d64_wide_tree": scaled(C3, B=2, L=150, D=64, Hq=16, Hkv=2),
+    "bf16_d64_tree_256rows": scaled(C3, B=2, L=150, D=64, Hq=16, Hkv=4),  # 240 rows per KV head
     "f32_d128_gqa": scaled(C2, B=2, L=77, dtype="f32", Hq=8, Hkv=2),
     "wide_tree_rowgroups": scaled(C5, B=3, K=150, max_T=64, L=90, Hq=32, Hkv=4),
     "no_context": scaled(C3, B=2, L=0),
