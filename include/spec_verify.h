@@ -79,6 +79,8 @@ typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
 #define SV_STATUS_NONFINITE      0x08 /* NaN or +inf logit in a row, or a row whose logits are all -inf */
 #define SV_STATUS_ZERO_RESIDUAL  0x10 /* residual mass rounded to 0 after a rejection: distribution kept unchanged */
 #define SV_STATUS_CTX_RANGE      0x20 /* ctx_len[b] < 0 or ctx_len[b] + T_b > Lcap: request skipped */
+#define SV_STATUS_SYNC           0x40 /* a sampler workgroup gave up waiting for the other workgroups of its request
+                                         (not expected: they agree to cooperate only once all are running) */
 
 /* ------------------------------------------------------------------------ */
 /* Tree-masked GQA attention ([SD] "Tree Attention Mask Mechanics"; GQA as in

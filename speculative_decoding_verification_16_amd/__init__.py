@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(_PKG, "libspecverify.so")
 SV_OK, SV_ERR_INVALID_ARG, SV_ERR_TREE, SV_ERR_UNSUPPORTED, SV_ERR_WORKSPACE, SV_ERR_HIP = range(6)
 SV_F32, SV_BF16 = 0, 1
 STATUS_BITS = {0x01: "TREE_INVALID", 0x02: "PACKING", 0x04: "TOKEN_RANGE", 0x08: "NONFINITE",
-               0x10: "ZERO_RESIDUAL", 0x20: "CTX_RANGE"}
+               0x10: "ZERO_RESIDUAL", 0x20: "CTX_RANGE", 0x40: "SYNC"}
 
 _P = ctypes.c_void_p
 _i32, _i64, _u32, _u64, _f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_float

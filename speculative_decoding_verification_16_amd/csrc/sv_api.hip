@@ -99,7 +99,8 @@ sv::AttnPlan plan_attn(const sv_attn_args* a) {
 }
 
 struct WsLayout {
-  size_t anc = 0, o_part = 0, ml_part = 0, items = 0, item_tot = 0, stats = 0, rowstats = 0, total = 0;
+  size_t anc = 0, o_part = 0, ml_part = 0, items = 0, item_tot = 0, stats = 0, rowstats = 0, xs = 0, xcnt = 0,
+         total = 0;
 };
 
 size_t attn_part_bytes(const sv_attn_args* a, const sv::AttnPlan& pl, size_t* ml) {
@@ -143,6 +144,12 @@ WsLayout layout(const sv_attn_args* a, const sv_sample_args* s) {
     off += align_up(((size_t)s->total_nodes + s->B) * sample_nch(s) * sizeof(sv::ChunkStat));
     w.rowstats = off;
     off += align_up(((size_t)s->total_nodes + s->B) * sizeof(sv::RowStat));
+    if (sv::walk_slices(s->B, sample_nch(s), s->temperature == 0.f) > 1) {
+      w.xs = off;
+      off += align_up((size_t)s->B * 4 * sample_nch(s) * sizeof(double));
+      w.xcnt = off;
+      off += align_up((size_t)s->B * sv::kWalkSync * sizeof(int32_t));
+    }
   }
   w.total = off;
   return w;
@@ -262,6 +269,9 @@ sv_status run_sample(const sv_sample_args* s, char* ws, const WsLayout& w, hipSt
   p.status = s->status;
   p.stats = (sv::ChunkStat*)(ws + w.stats);
   p.rowstats = (sv::RowStat*)(ws + w.rowstats);
+  p.slices = w.xcnt ? sv::walk_slices(s->B, p.nch, p.greedy) : 1;
+  p.xs = w.xcnt ? (double*)(ws + w.xs) : nullptr;
+  p.xcnt = w.xcnt ? (int32_t*)(ws + w.xcnt) : nullptr;
   const bool vec4 = (s->V % 4 == 0) && aligned(s->target_logits, 16) && (!s->draft_probs || aligned(s->draft_probs, 16));
   hipError_t e = sv::launch_sampler(p, vec4, st, (hipEvent_t)s->prof_start, (hipEvent_t)s->prof_stop);
   if (e != hipSuccess) return hip_fail(e, "sampler launch");

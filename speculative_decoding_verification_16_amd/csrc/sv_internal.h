@@ -79,7 +79,22 @@ struct SampleParams {
   int32_t* status;
   ChunkStat* stats;         // [N+B, nch] workspace
   RowStat* rowstats;        // [N+B] workspace
+  int32_t slices;           // workgroups per request in the walk (1: no exchange)
+  double* xs;               // [B, 2, 2 nch] workspace when slices > 1
+  int32_t* xcnt;            // [B, kWalkSync] workspace when slices > 1 (zeroed by the sampler)
+  uint32_t join_ticks;      // start-up window of a request's slices (100 MHz ticks)
 };
+
+// per-request words of the walk's slice coordination: pass-barrier arrivals,
+// start-up arrivals, mode (0 undecided, 1 sliced, 2 + 4 s: slice s alone)
+constexpr int kWalkSync = 4;
+
+// compute units of the current device (cached per device; 256 if unknown)
+int device_cus();
+
+// workgroups per request for the walk: several (256 threads each) when the
+// batch leaves at least four workgroup slots per request, else 1
+int walk_slices(int B, int nch, bool greedy);
 
 hipError_t launch_sampler(const SampleParams& p, bool vec4, hipStream_t stream, hipEvent_t ev_start,
                           hipEvent_t ev_stop);

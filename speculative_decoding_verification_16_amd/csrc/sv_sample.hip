@@ -99,9 +99,13 @@ __global__ __launch_bounds__(256) void row_stats_kernel(const float* __restrict_
 
 // Pass 2: per-row normalisation merged from the chunk statistics (one wave
 // per row), so that the walk and the p-row output read 16 bytes per row.
+// It also clears the walk's per-request coordination words (xcnt, nsync entries).
 __global__ __launch_bounds__(256) void row_finalize_kernel(const ChunkStat* __restrict__ stats, int64_t rows,
-                                                           int nch, float c, RowStat* __restrict__ rs) {
+                                                           int nch, float c, RowStat* __restrict__ rs,
+                                                           int32_t* __restrict__ xcnt, int nsync) {
   const int lane = threadIdx.x & 63;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (xcnt && gid < nsync) xcnt[gid] = 0;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
   float lmax, av;
@@ -144,13 +148,28 @@ __global__ __launch_bounds__(256) void probs_kernel(const float* __restrict__ lo
 // vocabulary passes that rejections make (one per residual level) and the
 // final draw.
 
-constexpr int kWalkThreads = 512;
-constexpr int kWalkWaves = kWalkThreads / kWave;
-constexpr int kHalf = kChunk / 2;  // vocabulary unit of one wave in a residual pass
-constexpr int kDrawPerLane = kChunk / kWalkThreads;  // tokens of a chunk per lane in the draw
-static_assert(kDrawPerLane == 8, "the draw gives each lane two float4 of a chunk");
+constexpr int kHalf = kChunk / 2;      // vocabulary unit of one wave in a residual pass
+constexpr int kSpinLimit = 1 << 16;    // polls of a slice barrier before it gives up (flagged)
+constexpr uint32_t kJoinWindow = 2000; // default start-up window of a request's slices, 100 MHz ticks (20 us)
 
+// A request is served by S workgroups of NT threads: S = 1 with NT = 512, or
+// S > 1 "slices" with NT = 256. Every slice gathers the same inputs and takes
+// the same decisions; a residual pass is split over the waves of all slices,
+// which exchange their half-chunk masses through global memory and a
+// per-request arrival counter (agent-scope release / acquire), so every
+// slice then holds the same masses in the same order. Slice 0 alone writes
+// the request's outputs and draws.
+//
+// The slices of a request are ordinary workgroups, so nothing guarantees
+// that all of them are resident at once. Before the first exchange they
+// agree on a mode: each one counts itself in on arrival; once all S have
+// arrived (all are then running, and none leaves before the walk ends) the
+// request runs sliced, and if the window passes first, one slice claims the
+// request and walks it alone while the others leave. A slice never waits on
+// a workgroup that has not started.
+template <int NT>
 struct WalkShared {
+  static constexpr int NW = NT / kWave;
   int32_t par[kMaxNodes];
   int32_t tok[kMaxNodes];
   double u[kMaxNodes];
@@ -159,11 +178,20 @@ struct WalkShared {
   RowStat rs[kMaxNodes + 1];  // the request's rows: r = 0 root, r = 1 + j after node j
   double csum[kMaxChunks];    // chunk masses of the distribution being drawn from
   double hsum[2 * kMaxChunks];// half-chunk masses of a residual pass
-  double wtot[kWalkWaves];    // per-wave sums of the draw's scan
-  int32_t wcand[kWalkWaves];  // per-wave first crossing of the draw (-1: none)
-  int32_t wlast[kWalkWaves];  // per-wave last token with mass
+  double wtot[NW];            // per-wave sums of the draw's scan
+  int32_t wcand[NW];          // per-wave first crossing of the draw (-1: none)
+  int32_t wlast[NW];          // per-wave last token with mass
   double total;
   int32_t bad;
+  int32_t mode;               // slice mode agreed at start-up (sliced walks)
+};
+
+struct Slices {
+  int n;           // workgroups serving the request
+  int id;          // this one's index among them
+  double* xs;      // [2][2 nch] half-chunk masses, alternating buffer per pass
+  int32_t* cnt;    // arrivals at the request's pass barriers (zeroed before the walk)
+  int32_t* status;
 };
 
 // Mass of half-chunk h (2048 tokens) under max(0, p - cc q), one wave. The
@@ -233,44 +261,81 @@ __device__ __forceinline__ double half_scalar(const float* lrow, const float* qr
   return wave_sum(acc);
 }
 
-// Vocabulary pass of the whole workgroup: csum[ch] = mass of chunk ch under
-// max(0, p - cc q) (its two halves added in order); returns the total
-// (bitwise the same in every thread).
-template <bool VEC>
-__device__ __forceinline__ double residual_pass(WalkShared& sh, const float* lrow, const float* qrow, int V, int nch, float lmax,
-                                float c, double S, double cc) {
+// Vocabulary pass of the request's workgroups: csum[ch] = mass of chunk ch
+// under max(0, p - cc q) (its two halves added in order); returns the total
+// (bitwise the same in every thread of every slice). pass_no counts the
+// request's passes from 1 (the barrier target and the buffer parity).
+template <bool VEC, int NT>
+__device__ __forceinline__ double residual_pass(WalkShared<NT>& sh, const float* lrow, const float* qrow, int V, int nch,
+                                                float lmax, float c, double S, double cc, const Slices& sl,
+                                                int pass_no) {
+  constexpr int NW = NT / kWave;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nh = 2 * nch;
+  const int gw = sl.id * NW + wave, GW = sl.n * NW;  // this wave among all the request's waves
+  double* xb = sl.xs + (pass_no & 1) * nh;
   const float ccS = (float)(cc * S);
   const double invS = 1.0 / S;
   if (VEC) {
     // two half-chunks per wave in flight: the next one's loads are issued
     // before the current one is reduced (past the row's end they read zeros).
-    if (wave < nh) {
+    if (gw < nh) {
       const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc((void*)lrow, (short)0, V * 4, 0x00020000);
       const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc((void*)qrow, (short)0, V * 4, 0x00020000);
       HalfRegs ra, rb;
-      half_load(ra, lrs, qrs, wave, lane);
-      for (int h = wave; h < nh; h += 2 * kWalkWaves) {
-        const int h1 = h + kWalkWaves;
+      half_load(ra, lrs, qrs, gw, lane);
+      for (int h = gw; h < nh; h += 2 * GW) {
+        const int h1 = h + GW;
         half_load(rb, lrs, qrs, h1, lane);
-        const double m0 = half_mass<VEC>(ra, V, h, lane, lmax, c, ccS);
-        if (lane == 0) sh.hsum[h] = m0 * invS;
-        half_load(ra, lrs, qrs, h1 + kWalkWaves, lane);
+        const double m0 = half_mass<VEC>(ra, V, h, lane, lmax, c, ccS) * invS;
+        if (lane == 0) {
+          sh.hsum[h] = m0;
+          if (sl.n > 1) xb[h] = m0;
+        }
+        half_load(ra, lrs, qrs, h1 + GW, lane);
         if (h1 < nh) {
-          const double m1 = half_mass<VEC>(rb, V, h1, lane, lmax, c, ccS);
-          if (lane == 0) sh.hsum[h1] = m1 * invS;
+          const double m1 = half_mass<VEC>(rb, V, h1, lane, lmax, c, ccS) * invS;
+          if (lane == 0) {
+            sh.hsum[h1] = m1;
+            if (sl.n > 1) xb[h1] = m1;
+          }
         }
       }
     }
   } else {
-    for (int h = wave; h < nh; h += kWalkWaves) {
-      const double m = half_scalar(lrow, qrow, V, h, lmax, c, ccS, lane);
-      if (lane == 0) sh.hsum[h] = m * invS;
+    for (int h = gw; h < nh; h += GW) {
+      const double m = half_scalar(lrow, qrow, V, h, lmax, c, ccS, lane) * invS;
+      if (lane == 0) {
+        sh.hsum[h] = m;
+        if (sl.n > 1) xb[h] = m;
+      }
     }
   }
+  if (sl.n > 1) {
+    // every slice's masses are published, then read back by every slice.
+    // Each wave's stores reach the XCD's L2 before the barrier; one thread
+    // then releases them (L2 write-back) with its arrival, polls the counter
+    // with plain device-scope loads (an acquire per poll would invalidate
+    // the L2 each time), and acquires once when everyone has arrived.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      __hip_atomic_fetch_add(sl.cnt, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      const int target = sl.n * pass_no;
+      for (int spin = 0; __hip_atomic_load(sl.cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target; ++spin) {
+        if (spin >= kSpinLimit) {  // cannot happen while all slices are resident; never wait forever
+          flag(sl.status, kStSync);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    __syncthreads();
+    for (int h = threadIdx.x; h < nh; h += NT) sh.hsum[h] = xb[h];
+  }
   __syncthreads();
-  for (int ch = threadIdx.x; ch < nch; ch += kWalkThreads) sh.csum[ch] = sh.hsum[2 * ch] + sh.hsum[2 * ch + 1];
+  for (int ch = threadIdx.x; ch < nch; ch += NT) sh.csum[ch] = sh.hsum[2 * ch] + sh.hsum[2 * ch + 1];
   __syncthreads();
   if (wave == 0) {
     double a = 0.0;
@@ -287,12 +352,17 @@ __device__ __forceinline__ double residual_pass(WalkShared& sh, const float* lro
 // Inverse CDF: the smallest token whose inclusive prefix mass exceeds
 // u * total. The chunk is found by a sequential prefix over the chunk masses
 // (every thread, same order, same result). Inside it, lane l of wave w owns
-// the 8 tokens at 512 w + 8 l: lane sums are scanned within each wave, the
-// wave totals are added in wave order, and the first lane whose inclusive
-// prefix crosses the remainder picks the token among its 8.
-template <bool VEC>
-__device__ __forceinline__ int draw_token(WalkShared& sh, const float* lrow, const float* qrow, int V, int nch, int level,
-                          float lmax, float c, double S, double cc, double u, double total) {
+// the DPL = 4096 / NT tokens at 64 DPL w + DPL l: lane sums are scanned
+// within each wave, the wave totals are added in wave order, and the first
+// lane whose inclusive prefix crosses the remainder picks the token among its
+// DPL.
+template <bool VEC, int NT>
+__device__ __forceinline__ int draw_token(WalkShared<NT>& sh, const float* lrow, const float* qrow, int V, int nch,
+                                          int level, float lmax, float c, double S, double cc, double u,
+                                          double total) {
+  constexpr int NW = NT / kWave;
+  constexpr int kDrawPerLane = kChunk / NT;
+  static_assert(kDrawPerLane % 4 == 0, "the draw gives each lane whole float4 of a chunk");
   const float ccS = (float)(cc * S);
   const double invS = 1.0 / S;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -383,7 +453,7 @@ __device__ __forceinline__ int draw_token(WalkShared& sh, const float* lrow, con
   }
   __syncthreads();
   int y = -1, ylast = -1;
-  for (int wv = 0; wv < kWalkWaves; ++wv) {
+  for (int wv = 0; wv < NW; ++wv) {
     const int cnd = sh.wcand[wv];
     y = (y < 0 && cnd >= 0) ? cnd : y;
     ylast = max(ylast, sh.wlast[wv]);
@@ -393,27 +463,45 @@ __device__ __forceinline__ int draw_token(WalkShared& sh, const float* lrow, con
   return y;
 }
 
-template <bool VEC>
-__global__ __launch_bounds__(kWalkThreads) void walk_kernel(SampleParams p) {
-  __shared__ WalkShared sh;
-  const int b = blockIdx.x;
+// outputs of a request whose inputs are invalid: nothing accepted, no token
+__device__ __forceinline__ void skip_request(const SampleParams& p, int b, int32_t* acc_nodes, int32_t* toks_out,
+                                             int bits, bool clear) {
+  if (clear) {
+    for (int i = threadIdx.x; i < p.max_depth; i += blockDim.x) acc_nodes[i] = -1;
+    for (int i = threadIdx.x; i <= p.max_depth; i += blockDim.x) toks_out[i] = -1;
+  }
+  if (threadIdx.x == 0) {
+    flag(p.status, bits);
+    p.accept_len[b] = 0;
+    if (p.residual_passes) p.residual_passes[b] = 0;
+  }
+}
+
+template <bool VEC, int NT>
+__global__ __launch_bounds__(NT) void walk_kernel(SampleParams p) {
+  __shared__ WalkShared<NT> sh;
+  const int b = blockIdx.x / p.slices, slice = blockIdx.x - b * p.slices;
+  int32_t* sync = p.slices > 1 ? p.xcnt + (int64_t)b * kWalkSync : nullptr;  // [0] passes, [1] arrivals, [2] mode
+  if (sync && threadIdx.x == 0) __hip_atomic_fetch_add(sync + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t t_join = sync ? wall_clock64() : 0;
+  // slice 0 reports invalid requests and the uniforms (every slice computes
+  // the same; slice 0 runs whatever the mode turns out to be)
+  const bool first = slice == 0;
   const int tid = threadIdx.x, lane = tid & 63;
   const int md = p.max_depth;
   int32_t* acc_nodes = p.accepted_nodes + (int64_t)b * md;
   int32_t* toks_out = p.out_tokens + (int64_t)b * (md + 1);
-  for (int i = tid; i < md; i += kWalkThreads) acc_nodes[i] = -1;
-  for (int i = tid; i <= md; i += kWalkThreads) toks_out[i] = -1;
+  if (!sync) {  // a single workgroup: the outputs are its own from the start
+    for (int i = tid; i < md; i += NT) acc_nodes[i] = -1;
+    for (int i = tid; i <= md; i += NT) toks_out[i] = -1;
+  }
 
   const int n0 = p.cu_nodes[b], n1 = p.cu_nodes[b + 1];
   const int T = n1 - n0;
   const bool pack_ok = n0 >= 0 && T >= 0 && T <= p.max_nodes && n1 <= p.N;
-  if (b == 0 && tid == 0 && p.cu_nodes[p.B] != p.N) flag(p.status, kStPacking);
+  if (b == 0 && first && tid == 0 && p.cu_nodes[p.B] != p.N) flag(p.status, kStPacking);
   if (!pack_ok) {
-    if (tid == 0) {
-      flag(p.status, kStPacking);
-      p.accept_len[b] = 0;
-      if (p.residual_passes) p.residual_passes[b] = 0;
-    }
+    if (first) skip_request(p, b, acc_nodes, toks_out, kStPacking, sync != nullptr);
     return;
   }
   const uint32_t rid = p.request_id ? p.request_id[b] : (uint32_t)b;
@@ -422,9 +510,9 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(SampleParams p) {
     sh.tok[tid] = p.tokens[n0 + tid];
     const double u = uniform01(p.seed, rid, (uint32_t)tid, 0u, p.step);
     sh.u[tid] = u;
-    if (p.uniforms_out) p.uniforms_out[n0 + tid] = u;
+    if (first && p.uniforms_out) p.uniforms_out[n0 + tid] = u;
   }
-  if (tid == 0 && p.uniforms_out) p.uniforms_out[p.N + b] = uniform01(p.seed, rid, 0u, 1u, p.step);
+  if (first && tid == 0 && p.uniforms_out) p.uniforms_out[p.N + b] = uniform01(p.seed, rid, 0u, 1u, p.step);
   __syncthreads();
   if (tid < kWave) {
     bool bad_tree = false, bad_tok = false;
@@ -438,11 +526,7 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(SampleParams p) {
   __syncthreads();
   const int bad = __builtin_amdgcn_readfirstlane(sh.bad);
   if (bad) {
-    if (tid == 0) {
-      flag(p.status, bad);
-      p.accept_len[b] = 0;
-      if (p.residual_passes) p.residual_passes[b] = 0;
-    }
+    if (first) skip_request(p, b, acc_nodes, toks_out, bad, sync != nullptr);
     return;
   }
 
@@ -456,9 +540,48 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(SampleParams p) {
     sh.qx[tid] = p.greedy ? 0.f : p.q[r * V + sh.tok[tid]];
   }
   if (tid <= T) sh.rs[tid] = p.rowstats[row0 + tid];
+  // the mode: sliced, or this slice alone, or another slice alone (leave)
+  Slices sl{1, 0, nullptr, nullptr, p.status};
+  if (sync) {
+    if (tid == 0) {
+      int mode;
+      for (;;) {
+        mode = __hip_atomic_load(sync + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (mode != 0) break;
+        int want = 0;
+        if (p.join_ticks > 0 &&
+            __hip_atomic_load(sync + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= p.slices)
+          want = 1;
+        else if (wall_clock64() - t_join >= p.join_ticks) want = 2 + 4 * slice;
+        if (want) {
+          int expect = 0;
+          mode = __hip_atomic_compare_exchange_strong(sync + 2, &expect, want, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT)
+                     ? want
+                     : expect;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      sh.mode = mode;
+    }
+    __syncthreads();
+    const int mode = __builtin_amdgcn_readfirstlane(sh.mode);
+    if (mode == 1) {
+      sl = Slices{p.slices, slice, p.xs + (int64_t)b * 4 * p.nch, sync, p.status};
+    } else if (mode != 2 + 4 * slice) {
+      return;  // another slice walks this request alone
+    }
+    if (sl.id == 0) {
+      for (int i = tid; i < md; i += NT) acc_nodes[i] = -1;
+      for (int i = tid; i <= md; i += NT) toks_out[i] = -1;
+    }
+  }
+  const bool lead = sl.id == 0;  // the slice that writes the request's outputs and draws
   __syncthreads();
 
   int pos = -1, depth = 0, passes = 0, bonus = -1;
+  int npass = 0;  // slice barriers passed (every slice counts the same)
   for (;;) {
     const int r = pos + 1;
     const int64_t row = row0 + r;
@@ -468,7 +591,7 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(SampleParams p) {
     // children of pos in increasing index: the same ballot in every wave
     const uint64_t kids = __ballot(lane < T && sh.par[lane] == pos);
     if (st.lmax == -INFINITY) {  // no finite logit: p is undefined here, stop without a token
-      if (tid == 0) flag(p.status, kStNonFinite);
+      if (lead && tid == 0) flag(p.status, kStNonFinite);
       break;
     }
 
@@ -480,7 +603,7 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(SampleParams p) {
       }
       next = __builtin_amdgcn_readfirstlane(next);
       if (next < 0) { bonus = st.arg; break; }
-      if (tid == 0) { acc_nodes[depth] = next; toks_out[depth] = sh.tok[next]; }
+      if (lead && tid == 0) { acc_nodes[depth] = next; toks_out[depth] = sh.tok[next]; }
       ++depth;
       pos = next;
       continue;
@@ -500,7 +623,7 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(SampleParams p) {
       if (ok) { accepted = ch; break; }
       // rejected: the next sibling is tested against the next residual level
       const double cn = cc + M;
-      const double Mn = residual_pass<VEC>(sh, lrow, qrow, p.V, p.nch, st.lmax, p.c, st.S, cn);
+      const double Mn = residual_pass<VEC, NT>(sh, lrow, qrow, p.V, p.nch, st.lmax, p.c, st.S, cn, sl, ++npass);
       ++passes;
       if (__builtin_amdgcn_readfirstlane(Mn > 0.0 ? 1 : 0)) {
         cc = cn;
@@ -508,12 +631,12 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(SampleParams p) {
         ++level;
         csum_ok = true;
       } else {
-        if (tid == 0) flag(p.status, kStZeroResidual);
+        if (lead && tid == 0) flag(p.status, kStZeroResidual);
         csum_ok = false;
       }
     }
     if (accepted >= 0) {
-      if (tid == 0) { acc_nodes[depth] = accepted; toks_out[depth] = sh.tok[accepted]; }
+      if (lead && tid == 0) { acc_nodes[depth] = accepted; toks_out[depth] = sh.tok[accepted]; }
       ++depth;
       pos = accepted;
       continue;
@@ -522,7 +645,7 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(SampleParams p) {
     double total;
     if (level == 0) {
       const ChunkStat* cs = p.stats + row * p.nch;
-      for (int ch = tid; ch < p.nch; ch += kWalkThreads) {
+      for (int ch = tid; ch < p.nch; ch += NT) {
         const ChunkStat s = cs[ch];
         sh.csum[ch] = s.lmax == -INFINITY ? 0.0 : s.s * exp2((double)(s.lmax - st.lmax) * (double)p.c);
       }
@@ -530,16 +653,17 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(SampleParams p) {
       total = st.S;
     } else {
       if (!csum_ok) {
-        residual_pass<VEC>(sh, lrow, qrow, p.V, p.nch, st.lmax, p.c, st.S, cc);
+        residual_pass<VEC, NT>(sh, lrow, qrow, p.V, p.nch, st.lmax, p.c, st.S, cc, sl, ++npass);
         ++passes;
       }
       total = M;
     }
+    if (!lead) return;  // the draw needs no other slice: the rest are done
     const double uf = uniform01(p.seed, rid, 0u, 1u, p.step);
-    bonus = draw_token<VEC>(sh, lrow, qrow, p.V, p.nch, level, st.lmax, p.c, st.S, cc, uf, total);
+    bonus = draw_token<VEC, NT>(sh, lrow, qrow, p.V, p.nch, level, st.lmax, p.c, st.S, cc, uf, total);
     break;
   }
-  if (tid == 0) {
+  if (lead && tid == 0) {
     toks_out[depth] = bonus;
     p.accept_len[b] = depth;
     if (p.residual_passes) p.residual_passes[b] = passes;
@@ -564,7 +688,9 @@ hipError_t launch_sampler(const SampleParams& p, bool vec4, hipStream_t stream, 
   if (ev_stop) (void)hipEventRecord(ev_stop, stream);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  row_finalize_kernel<<<dim3((unsigned)((rows + 3) / 4)), 256, 0, stream>>>(p.stats, rows, p.nch, p.c, p.rowstats);
+  row_finalize_kernel<<<dim3((unsigned)((rows + 3) / 4)), 256, 0, stream>>>(p.stats, rows, p.nch, p.c, p.rowstats,
+                                                                            p.slices > 1 ? p.xcnt : nullptr,
+                                                                            p.B * kWalkSync);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (p.probs_out && !p.greedy) {
@@ -572,9 +698,59 @@ hipError_t launch_sampler(const SampleParams& p, bool vec4, hipStream_t stream, 
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  if (vec4) walk_kernel<true><<<dim3(p.B), dim3(kWalkThreads), 0, stream>>>(p);
-  else walk_kernel<false><<<dim3(p.B), dim3(kWalkThreads), 0, stream>>>(p);
+  if (p.slices > 1) {
+    // SV_WALK_JOIN_TICKS overrides the start-up window; 0 makes the first
+    // slice to look walk its request alone, so that tests reach that path
+    const char* env = getenv("SV_WALK_JOIN_TICKS");
+    const long ticks = env ? strtol(env, nullptr, 10) : -1L;
+    SampleParams ps = p;
+    ps.join_ticks = ticks >= 0 && ticks <= 100000000L ? (uint32_t)ticks : kJoinWindow;
+    const dim3 grid((unsigned)(p.B * p.slices));
+    if (vec4) walk_kernel<true, 256><<<grid, dim3(256), 0, stream>>>(ps);
+    else walk_kernel<false, 256><<<grid, dim3(256), 0, stream>>>(ps);
+  } else {
+    if (vec4) walk_kernel<true, 512><<<dim3(p.B), dim3(512), 0, stream>>>(p);
+    else walk_kernel<false, 512><<<dim3(p.B), dim3(512), 0, stream>>>(p);
+  }
   return hipGetLastError();
+}
+
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+int walk_slices(int B, int nch, bool greedy) {
+  if (greedy || B <= 0) return 1;
+  static int per_cu_cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
+  if (per_cu_cached[dev] == 0) {
+    int a = 0, b = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, walk_kernel<true, 256>, 256, 0) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, walk_kernel<false, 256>, 256, 0) != hipSuccess) {
+      (void)hipGetLastError();
+      a = b = 0;
+    }
+    per_cu_cached[dev] = max(1, min(a, b));  // 1 when unknown: then a batch of >= CUs requests gets 1 slice
+  }
+  const int64_t capacity = (int64_t)per_cu_cached[dev] * device_cus();
+  // every wave of the request gets at least one half-chunk; past 8 slices the
+  // wider exchange costs more than the shorter passes save (measured: 16
+  // slices were slower than 8 at batch 16 and 32, vocabulary 128256)
+  const int64_t by_work = (2 * (int64_t)nch + 3) / 4;
+  int64_t s = capacity / B;
+  if (s > by_work) s = by_work;
+  if (s > 8) s = 8;
+  // two slices would take the same CUs as one 512-thread workgroup per request
+  return s >= 4 ? (int)s : 1;
 }
 
 }  // namespace sv

@@ -166,3 +166,23 @@ def test_sampler_is_deterministic_and_step_matches_parts():
     assert torch.equal(rs["attn_out"], ra)
     for k in ("accept_len", "accepted_nodes", "out_tokens"):
         assert torch.equal(rs[k], r1[k]), k
+
+
+@pytest.mark.parametrize("ticks", ["0", "1"])
+@pytest.mark.parametrize("name", ["c2_small", "c3_small", "c4_small_cold", "c2_llama8b_chain"])
+def test_sliced_walk_fallback_matches(name, ticks, monkeypatch):
+    # Small batches walk each request with several workgroups that first agree
+    # to cooperate. A start-up window of 0 ticks makes the first workgroup to
+    # look walk its request alone; 1 tick mixes both outcomes across requests.
+    # Either way the outputs are bitwise those of the default window.
+    cfg = SMALL[name] if name in SMALL else get_config(name)
+    w = generate(cfg, "cuda", attn=False)
+    T = cfg.temperature
+    print(f"[sample-fallback] {name} ticks={ticks} B={w['B']} V={cfg.V}", flush=True)
+    ref = _gpu_sample(w, T)
+    monkeypatch.setenv("SV_WALK_JOIN_TICKS", ticks)
+    for _ in range(2):
+        r = _gpu_sample(w, T)
+        assert int(r["status"].item()) == 0, sv.status_names(int(r["status"].item()))
+        for k in ("accept_len", "accepted_nodes", "out_tokens", "uniforms", "residual_passes"):
+            assert torch.equal(r[k], ref[k]), k
