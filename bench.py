@@ -5,6 +5,8 @@ tree-masked GQA attention of every draft node against its request's KV cache
 (one layer), the row-statistics pass over every target-logit row, and the
 rejection-sampling tree walk that emits the accepted path plus a bonus token.
 All inputs are synthetic, seeded, and resident in HBM before the timed region.
+Workloads smaller than 512 MB are held in several copies that consecutive
+steps cycle through, so that no step finds its inputs in the last-level cache.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
@@ -20,6 +22,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import re
 import sys
@@ -30,6 +33,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+ROTATE_BYTES = 512 << 20  # inputs cycled per step: at least twice the 256 MB last-level cache
+MAX_INPUT_SETS = 8
 DEFAULT_WORKLOAD = "c5_super_tree"
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
@@ -86,8 +91,8 @@ class HipEvents:
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-clock budget of the oracle's CPU-baseline sample (0 = skip)")
@@ -260,15 +265,24 @@ def main():
     dev = torch.device("cuda:0")
     cfg = get_config(args.workload)
     w = generate(cfg, dev)
+    # Small workloads would stay in the 256 MB last-level cache from one step
+    # to the next: consecutive steps then cycle through copies of the inputs
+    # in separate buffers, at least 512 MB together (at most 8 copies).
+    set_bytes = attention_bytes(w) + 8 * w["V"] * (w["N"] + w["B"])
+    n_sets = max(1, min(MAX_INPUT_SETS, math.ceil(ROTATE_BYTES / set_bytes)))
+    sets = [w] + [generate(cfg, dev) for _ in range(n_sets - 1)]
     torch.cuda.synchronize()
 
     stream = torch.cuda.Stream()  # default priority
+    calls = []
     with torch.cuda.stream(stream):
-        a = sv.AttnCall(w["q"], w["k_cache"], w["v_cache"], w["ctx_len_t"], w["cu_nodes_t"], parent=w["parent_t"],
-                        max_nodes=w["max_T"])
-        s = sv.SampleCall(a.keep["cu"], w["parent_t"], w["draft_tokens"], w["logits"], w["draft_probs"],
-                          temperature=cfg.temperature, seed=w["seed"], max_nodes=w["max_T"], residual_passes=True)
-        step = sv.StepCall(a, s)
+        for x in sets:
+            a = sv.AttnCall(x["q"], x["k_cache"], x["v_cache"], x["ctx_len_t"], x["cu_nodes_t"], parent=x["parent_t"],
+                            max_nodes=x["max_T"])
+            s = sv.SampleCall(a.keep["cu"], x["parent_t"], x["draft_tokens"], x["logits"], x["draft_probs"],
+                              temperature=cfg.temperature, seed=x["seed"], max_nodes=x["max_T"],
+                              residual_passes=True)
+            calls.append((a, s, sv.StepCall(a, s)))
     torch.cuda.synchronize()
 
     K, W = args.steps, args.warmup
@@ -278,16 +292,15 @@ def main():
         hev = HipEvents(4 * K)
         ev = [tuple(hev.ev[4 * i:4 * i + 4]) for i in range(K)]
 
-    for _ in range(W):
-        a.set_prof_events(None, None)
-        s.set_prof_events(None, None)
-        step(stream)
+    for i in range(max(W, n_sets)):
+        calls[i % n_sets][2](stream)
     stream.synchronize()
     torch.cuda.synchronize()
 
     st_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     t0 = time.perf_counter()
     for i in range(K):
+        a, s, step = calls[i % n_sets]
         if use_events:
             a.set_prof_events(ev[i][0], ev[i][1])
             s.set_prof_events(ev[i][2], ev[i][3])
@@ -299,10 +312,12 @@ def main():
     elapsed = time.perf_counter() - t0
     step_ms = sorted(e0.elapsed_time(e1) for e0, e1 in st_ev)
     pct = lambda f: step_ms[min(K - 1, int(round(f * (K - 1))))]
-    a.set_prof_events(None, None)
-    s.set_prof_events(None, None)
-
-    status = int(s.status.item()) | int(a.status.item())
+    status = 0
+    for a, s, _ in calls:
+        a.set_prof_events(None, None)
+        s.set_prof_events(None, None)
+        status |= int(s.status.item()) | int(a.status.item())
+    a, s, _ = calls[0]
     if status:
         print(f"device status bits set: {sv.status_names(status)}", file=sys.stderr)
         sys.exit(1)
@@ -360,6 +375,7 @@ def main():
                    "temperature": cfg.temperature},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "input_sets": n_sets,
         "kernels": {k: {kk: (round(vv, 2) if isinstance(vv, float) else vv) for kk, vv in d.items()}
                     for k, d in kernels.items()},
         "walk": {"mean_accept_len": round(float(acc.mean().item()), 4),
