@@ -521,9 +521,15 @@ void attn_mfma32_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t Vs1[KT * D];
   // LDS swizzles. K: 16-byte unit u of row `key` at u ^ (key & 15) for
   // D = 128 (u ^ (key & 7) for D = 64), so the 16 keys that one 256-byte read
-  // pass serves hit 16 different units. V: as in the 16x16 kernel, 16-byte
-  // unit u at u ^ 2 (key & 3); the transposed reads stay within one pass.
+  // pass serves hit 16 different units. V: 16-byte unit u at u ^ VSW (key & 3).
+  // A transposed read spans four keys (key & 3) and, per 32-lane half, two
+  // logical 32-byte chunks; with VSW = 4 for D = 128 those eight (key,
+  // chunk) pairs sit in eight different chunks of the 256-byte bank row, so
+  // the read is free of bank conflicts (u ^ 2 (key & 3) left two of them per
+  // chunk: 2-way conflicts on every V read). D = 64 rows are 128 bytes and
+  // alternate bank halves, so u ^ 2 (key & 3) suffices there.
   constexpr int KSWM = D >= 128 ? 15 : 7;
+  constexpr int VSW = D >= 128 ? 4 : 2;
 
   int job, rg;
   if (!decode_block(p, blockIdx.x, job, rg)) return;
@@ -588,7 +594,7 @@ void attn_mfma32_kernel(AttnParams p) {
   // flag: lane i of a wave instruction fills the 16 bytes at the instruction's
   // LDS base + 16 i). Thread c = tid + NT i fills unit c of a tile, row
   // kk = c / UNITS, slot u = c % UNITS, with the global unit the reads expect
-  // in that slot: K unit u ^ (kk & KSWM), V unit u ^ 2 (kk & 3). The tile
+  // in that slot: K unit u ^ (kk & KSWM), V unit u ^ VSW (kk & 3). The tile
   // start goes into the per-lane offset, so the bounds check covers it.
   int koff[PER_THREAD], voff[PER_THREAD];
 #pragma unroll
@@ -596,7 +602,7 @@ void attn_mfma32_kernel(AttnParams p) {
     const int c = tid + NT * i;
     const int kk = c / UNITS, u = c % UNITS;
     koff[i] = (kk * D + 8 * (u ^ (kk & KSWM))) * 2;
-    voff[i] = (kk * D + 8 * (u ^ (2 * (kk & 3)))) * 2;
+    voff[i] = (kk * D + 8 * (u ^ (VSW * (kk & 3)))) * 2;
   }
   const int wunit = 64 * wave;  // first tile unit this wave's instructions fill
   // When this workgroup is the only reader of its slab range (the job has a
@@ -735,7 +741,7 @@ void attn_mfma32_kernel(AttnParams p) {
       const bf16x8_t pk = __builtin_bit_cast(bf16x8_t, wv);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const int base = (16 * kk) * D + vt_lane + 16 * ((2 * db + vt_dg) ^ vt_s);
+        const int base = (16 * kk) * D + vt_lane + 16 * ((2 * db + vt_dg) ^ ((VSW / 2) * vt_s));
         const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(lds_u16_t*)(Vb + base));
         const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(lds_u16_t*)(Vb + base + 8 * D));
         const bf16x8_t a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);

@@ -28,6 +28,8 @@ SMALL = {
     "bf16_d64": scaled(C2, B=2, L=190, D=64, Hq=8, Hkv=2),
     "bf16_d64_wide_tree": scaled(C3, B=2, L=150, D=64, Hq=16, Hkv=2),
     "bf16_d64_tree_256rows": scaled(C3, B=2, L=150, D=64, Hq=16, Hkv=4),  # 240 rows per KV head
+    "tree_180rows": scaled(C3, B=2, L=170, Hq=24, Hkv=8),  # 180 rows: a wave with half a block, one with none
+    "c5_trees_upto_256rows": scaled(C5, B=4, K=48, max_T=16, L=100),  # mixed 16..256 rows, empty row blocks
     "f32_d128_gqa": scaled(C2, B=2, L=77, dtype="f32", Hq=8, Hkv=2),
     "wide_tree_rowgroups": scaled(C5, B=3, K=150, max_T=64, L=90, Hq=32, Hkv=4),
     "no_context": scaled(C3, B=2, L=0),
