@@ -682,13 +682,12 @@ void attn_mfma32_kernel(AttnParams p) {
       for (int ks = 0; ks < KS; ++ks)
         ka[kq][ks] = *(const bf16x8_t*)(Knxt + key * D + 8 * ((2 * ks + h) ^ (key & KSWM)));
     }
-    sn[0] = f32x16_t{};
-    sn[1] = f32x16_t{};
-    auto s_group = [&](int q) {  // MFMAs 4q .. 4q + 3 of S_{t+1}
+    auto s_group = [&](int q) {  // MFMAs 4q .. 4q + 3 of S_{t+1} (each chain starts from zero)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int idx = 4 * q + j, kq = idx / KS, ks = idx % KS;
-        sn[kq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kq][ks], qf[ks], sn[kq], 0, 0, 0);
+        sn[kq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kq][ks], qf[ks], ks == 0 ? f32x16_t{} : sn[kq], 0, 0,
+                                                         0);
       }
     };
     static_assert(2 * KS % 4 == 0, "S MFMAs come in groups of four");
@@ -705,7 +704,13 @@ void attn_mfma32_kernel(AttnParams p) {
       const auto r32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
       mx = fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
     }
-    const float mnew = fmaxf(m, mx * p.scale_log2);
+    // The reference maximum moves only when some row's maximum exceeds it by
+    // more than 8 (log2 units): until then the exponentials stay below 2^8,
+    // exact to bf16's relative precision, and the rescale of O (64
+    // multiplies per lane) is skipped. The result is the same softmax.
+    // (Measured on MI355X: C3 attention 90 -> 84.5 us, C5 437 -> 419 us.)
+    float mnew = fmaxf(m, mx * p.scale_log2);
+    if (!__any(mnew > m + 8.f)) mnew = m;
     const float msub = mnew == -INFINITY ? 0.f : mnew;
     if (NG > 1) s_group(1 % NG);
     float lsum = 0.f;
