@@ -409,7 +409,10 @@ void attn_mfma_kernel(AttnParams p) {
         for (int t = 1; t < 16; ++t) mx = fmaxf(mx, x[t]);
         // the row's 64 keys live in lanes l16, l16+16, l16+32, l16+48
         mx = row_max4(mx);
-        const float mnew = fmaxf(m[i], mx * p.scale_log2);
+        // the reference maximum moves only by more than 8 (log2), as in the
+        // 32x32 kernel: exponentials stay below 2^8 and most rescales go
+        float mnew = fmaxf(m[i], mx * p.scale_log2);
+        if (!__any(mnew > m[i] + 8.f)) mnew = m[i];
         const float msub = mnew == -INFINITY ? 0.f : mnew;
         float lsum = 0.f;
 #pragma unroll
