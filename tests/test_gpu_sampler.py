@@ -186,3 +186,42 @@ def test_sliced_walk_fallback_matches(name, ticks, monkeypatch):
         assert int(r["status"].item()) == 0, sv.status_names(int(r["status"].item()))
         for k in ("accept_len", "accepted_nodes", "out_tokens", "uniforms", "residual_passes"):
             assert torch.equal(r[k], ref[k]), k
+
+
+BOARD_SKIP = ("the help-board walk (finished workgroups taking half-chunks of other requests' residual passes) "
+              "hung on its first GPU run (batch 3, 60-node trees) with no cause found by reading; it was taken out "
+              "of the library")
+
+
+@pytest.mark.parametrize("mode", ["single", pytest.param("board", marks=pytest.mark.skip(reason=BOARD_SKIP))])
+@pytest.mark.parametrize("name", ["c2_small", "c3_small", "c5_small_odd_vocab", "c4_small_cold", "max_tree_64"])
+def test_walk_modes_match(name, mode, monkeypatch):
+    # The walk runs with one workgroup per request or, for small batches,
+    # several workgroups per request. Forcing one workgroup per request must
+    # give bitwise the outputs of the automatic choice, and the oracle's.
+    cfg = SMALL[name]
+    w = generate(cfg, "cuda", attn=False)
+    T = cfg.temperature
+    print(f"[walk-mode] {name} {mode} B={w['B']} V={cfg.V}", flush=True)
+    ref = _gpu_sample(w, T)
+    monkeypatch.setenv("SV_WALK_MODE", mode)
+    for _ in range(2):
+        r = _gpu_sample(w, T)
+        assert int(r["status"].item()) == 0, sv.status_names(int(r["status"].item()))
+        for k in ("accept_len", "accepted_nodes", "out_tokens", "uniforms", "residual_passes"):
+            assert torch.equal(r[k], ref[k]), k
+    md = r["accepted_nodes"].shape[1]
+    compare_walk(r, _oracle(w, T, md), w["B"], greedy=False)
+
+
+@pytest.mark.skip(reason=BOARD_SKIP)
+def test_walk_board_full_batch_matches_single(monkeypatch):
+    # the batch-256 super tree uses the help board by default
+    w = generate(C5, "cuda", attn=False)
+    print(f"[walk-board] c5 B={w['B']}", flush=True)
+    ref = _gpu_sample(w, 1.0)
+    assert int(ref["status"].item()) == 0, sv.status_names(int(ref["status"].item()))
+    monkeypatch.setenv("SV_WALK_MODE", "single")
+    r = _gpu_sample(w, 1.0)
+    for k in ("accept_len", "accepted_nodes", "out_tokens", "uniforms", "residual_passes"):
+        assert torch.equal(r[k], ref[k]), k
