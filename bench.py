@@ -53,9 +53,15 @@ def attention_kernel_name(w, cfg) -> str:
     return "attn_mfma_kernel" if (cfg.Hq // cfg.Hkv) * w["max_T"] <= 64 else "attn_mfma32_kernel"
 
 
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence: timing kept, no system-scope fence
+
+
 class HipEvents:
     """Timing events created and read through the HIP runtime torch has loaded
-    (the library records them on its own stream, outside torch's bookkeeping)."""
+    (the library records them on its own stream, outside torch's bookkeeping).
+    They are created without the system-scope fence a default event performs
+    on each record: the timed steps then carry no cache flush per event (the
+    timestamps are device-side and need no host visibility of memory)."""
 
     def __init__(self, n: int):
         import ctypes
@@ -64,16 +70,22 @@ class HipEvents:
 
         self._ct = ctypes
         self.hip = ctypes.CDLL("libamdhip64.so.7")
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.ev = []
         for _ in range(n):
             h = ctypes.c_void_p()
-            rc = self.hip.hipEventCreate(ctypes.byref(h))
+            rc = self.hip.hipEventCreateWithFlags(ctypes.byref(h), HIP_EVENT_DISABLE_SYSTEM_FENCE)
             if rc != 0:
                 raise RuntimeError(f"hipEventCreate failed ({rc})")
             self.ev.append(h.value)
+
+    def record(self, i: int, stream) -> None:
+        rc = self.hip.hipEventRecord(self.ev[i], self._ct.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
 
     def ms(self, a: int, b: int) -> float:
         out = self._ct.c_float()
@@ -297,20 +309,21 @@ def main():
     stream.synchronize()
     torch.cuda.synchronize()
 
-    st_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    sev = HipEvents(2 * K)  # around each step, on the bench stream
     t0 = time.perf_counter()
     for i in range(K):
         a, s, step = calls[i % n_sets]
         if use_events:
             a.set_prof_events(ev[i][0], ev[i][1])
             s.set_prof_events(ev[i][2], ev[i][3])
-        st_ev[i][0].record(stream)
+        sev.record(2 * i, stream)
         step(stream)
-        st_ev[i][1].record(stream)
+        sev.record(2 * i + 1, stream)
     stream.synchronize()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    step_ms = sorted(e0.elapsed_time(e1) for e0, e1 in st_ev)
+    step_ms = sorted(sev.ms(2 * i, 2 * i + 1) for i in range(K))
+    sev.close()
     pct = lambda f: step_ms[min(K - 1, int(round(f * (K - 1))))]
     status = 0
     for a, s, _ in calls:
