@@ -18,10 +18,14 @@ Functions and the passages they follow:
   residual                 [SD] R_i(x); [LOSSY] appendix F.1 r(x).
   inverse_cdf              the draw from R_i / p.
   verify                   the whole walk ([SD] acceptance rule; [LOSSY] 2.1 h(x)).
+  min_p_theta,             [LOSSY] section 2.3: the min-p allowed set and the
+  truncate_min_p           truncated target p_Theta; verify(min_p=...) walks
+                           against p_Theta ("truncation sampling + SD", G.2/G.3).
 """
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 
 import numpy as np
@@ -66,11 +70,13 @@ def _load():
     lib.orc_residual.restype = f64
     lib.orc_inverse_cdf.argtypes = [i32, P, f64, P]
     lib.orc_inverse_cdf.restype = i32
-    lib.orc_verify.argtypes = [i32, i32, P, P, P, P, P, f64, u64, u32, P, i32, P, P, P, P, P, P, P, P, P, P,
-                               f64, f64, i32]
+    lib.orc_verify.argtypes = [i32, i32, P, P, P, P, P, f64, i32, ctypes.c_float, u64, u32, P, i32, P, P, P, P,
+                               P, P, P, P, P, P, f64, f64, i32]
     lib.orc_verify.restype = i32
     lib.orc_target_rows.argtypes = [i32, P, f64, i64, P, P]
     lib.orc_target_rows.restype = i32
+    lib.orc_truncate_min_p.argtypes = [i32, P, ctypes.c_float, P]
+    lib.orc_truncate_min_p.restype = None
     _lib = lib
     return lib
 
@@ -191,11 +197,30 @@ def inverse_cdf(P, u: float) -> tuple[int, float]:
     return int(y), float(m[0])
 
 
+def min_p_theta(temperature: float, min_p: float) -> float:
+    """Threshold on l_x - l_max of the min-p allowed set: fp32(T ln p_base),
+    from the fp32 values of T and p_base, as a caller passing fp32 arguments
+    gets it; -inf (no truncation) unless 0 < min_p < 1 and T > 0."""
+    T, pb = float(np.float32(temperature)), float(np.float32(min_p))
+    if not (T > 0.0 and 0.0 < pb < 1.0):
+        return float("-inf")
+    return float(np.float32(T * math.log(pb)))
+
+
+def truncate_min_p(logits_row, p_row, theta: float) -> np.ndarray:
+    """p_row (a normalised target row) truncated to the min-p allowed set."""
+    lg = np.ascontiguousarray(logits_row, dtype=np.float32)
+    p = np.array(p_row, dtype=np.float64, copy=True)
+    _load().orc_truncate_min_p(lg.shape[0], _ptr(lg), ctypes.c_float(theta), _ptr(p))
+    return p
+
+
 def verify(cu_nodes, parent, tokens, logits, q, *, temperature, seed, step=0, request_id=None,
-           max_depth=None, accept_tol=ACCEPT_TOL, cdf_tol=CDF_TOL, nthreads=None) -> dict:
+           max_depth=None, accept_tol=ACCEPT_TOL, cdf_tol=CDF_TOL, nthreads=None, min_p=0.0) -> dict:
     """The verification walk for a packed batch; returns a dict of numpy arrays.
 
     logits, q: float32 [N+B, V] (q may be None when temperature == 0).
+    min_p > 0 verifies against the min-p truncated target ([LOSSY] 2.3, G.2).
     """
     cu = np.ascontiguousarray(cu_nodes, dtype=np.int32)
     B = cu.shape[0] - 1
@@ -223,8 +248,10 @@ def verify(cu_nodes, parent, tokens, logits, q, *, temperature, seed, step=0, re
         "min_accept_margin": np.zeros(B, np.float64),
         "cdf_margin": np.zeros(B, np.float64),
     }
+    theta = min_p_theta(temperature, min_p)
+    trunc = 1 if theta > float("-inf") else 0
     rc = _load().orc_verify(B, V, _ptr(cu), _ptr(par), _ptr(tok), _ptr(lg), _ptr(qq), float(temperature),
-                            int(seed), int(step), _ptr(rid), int(max_depth), _ptr(out["accept_len"]),
+                            trunc, ctypes.c_float(theta), int(seed), int(step), _ptr(rid), int(max_depth), _ptr(out["accept_len"]),
                             _ptr(out["accepted_nodes"]), _ptr(out["out_tokens"]), _ptr(out["uniforms"]),
                             _ptr(out["flag_depth"]), _ptr(out["flag_kind"]), _ptr(out["n_rejections"]),
                             _ptr(out["status"]), _ptr(out["min_accept_margin"]), _ptr(out["cdf_margin"]),

@@ -253,6 +253,28 @@ int orc_target_probs(int V, const float* logits, double T, double* p) {
   return 0;
 }
 
+/* Min-p truncation of a target row ([LOSSY] section 2.3: the allowed set
+ * A = {x : p(x) >= p_base * max_v p(v)} and the truncated target
+ * p_Theta(x) = p(x) / Z on A, 0 elsewhere, which "truncation sampling + SD"
+ * verifies against, appendix G.2/G.3). Because p(x) / max p equals
+ * exp((l_x - l_max) / T), x is in A iff l_x - l_max >= T ln p_base. Reading:
+ * that comparison is made on the fp32 difference of the raw logits against
+ * theta = fp32(T ln p_base), so that every implementation decides
+ * membership identically. p (a normalised row) is masked and renormalised
+ * in place.                                                                */
+void orc_truncate_min_p(int V, const float* logits, float theta, double* p) {
+  float lmax = -INFINITY;
+  for (int x = 0; x < V; ++x)
+    if (logits[x] > lmax) lmax = logits[x];
+  double Z = 0.0;
+  for (int x = 0; x < V; ++x) {
+    float d = logits[x] - lmax;
+    if (!(d >= theta)) p[x] = 0.0;
+    Z += p[x];
+  }
+  for (int x = 0; x < V; ++x) p[x] /= Z;
+}
+
 /* Greedy target token: argmax of the raw logits, lowest index on ties.    */
 int orc_argmax(int V, const float* logits) {
   int best = 0;
@@ -322,6 +344,8 @@ typedef struct {
   const int32_t *cu_nodes, *parent, *tokens;
   const float *logits, *q;
   double T;
+  int trunc;     /* min-p truncation of every target row */
+  float theta;   /* its threshold on l_x - l_max         */
   uint64_t seed;
   uint32_t step;
   const uint32_t* request_id;
@@ -401,6 +425,7 @@ static void orc_walk_one(void* vctx, int64_t bi) {
      * is checked against ([SD]: node j is checked against p_i and q_i of the
      * position it was drafted at, i.e. its parent's row)                  */
     if (orc_target_probs(V, c->logits + row * (int64_t)V, c->T, P)) { c->status[b] |= 0x08; break; }
+    if (c->trunc) orc_truncate_min_p(V, c->logits + row * (int64_t)V, c->theta, P);
     for (int x = 0; x < V; ++x) Q[x] = (double)c->q[row * (int64_t)V + x];
     int accepted = -1;
     for (int ch = pos + 1; ch < T; ++ch) {
@@ -447,7 +472,9 @@ static void orc_walk_one(void* vctx, int64_t bi) {
 
 /* Verification of a packed batch (see the calling convention of the GPU
  * library: rows cu_nodes[b] + b + r, r = 0 root, r = 1 + j after node j).
- * T == 0 selects greedy verification. Per request it also reports
+ * T == 0 selects greedy verification; trunc != 0 verifies against the
+ * min-p truncated target (threshold theta, see orc_truncate_min_p). Per
+ * request it also reports
  *   flag_depth: accepted nodes before the first decision closer than the
  *               tolerance to its threshold (-1: none), flag_kind 0 = accept
  *               test, 1 = final inverse-CDF draw;
@@ -457,13 +484,14 @@ static void orc_walk_one(void* vctx, int64_t bi) {
  *   min_accept_margin, cdf_margin: the smallest |u - P/Q| seen and the
  *           margin of the final draw.                                     */
 int orc_verify(int B, int V, const int32_t* cu_nodes, const int32_t* parent, const int32_t* tokens,
-               const float* logits, const float* q, double T, uint64_t seed, uint32_t step,
+               const float* logits, const float* q, double T, int trunc, float theta, uint64_t seed,
+               uint32_t step,
                const uint32_t* request_id, int max_depth, int32_t* accept_len, int32_t* accepted_nodes,
                int32_t* out_tokens, double* uniforms_out, int32_t* flag_depth, int32_t* flag_kind,
                int32_t* n_rejections, int32_t* status, double* min_accept_margin, double* cdf_margin,
                double accept_tol, double cdf_tol, int nthreads) {
   if (B < 0 || V < 1 || max_depth < 0 || T < 0.0) return 1;
-  orc_walk_ctx c = {B, V, cu_nodes, parent, tokens, logits, q, T, seed, step, request_id, max_depth,
+  orc_walk_ctx c = {B, V, cu_nodes, parent, tokens, logits, q, T, trunc, theta, seed, step, request_id, max_depth,
                     accept_len, accepted_nodes, out_tokens, uniforms_out, flag_depth, flag_kind,
                     n_rejections, status, min_accept_margin, cdf_margin, accept_tol, cdf_tol};
   orc_parallel_for(B, nthreads, orc_walk_one, &c);
