@@ -109,6 +109,8 @@ def parse_args():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-clock budget of the oracle's CPU-baseline sample (0 = skip)")
     ap.add_argument("--no-events", action="store_true", help="time without the per-kernel HIP events")
+    ap.add_argument("--min-p", type=float, default=0.0,
+                    help="verify against the min-p truncated target (0 = plain lossless verification)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES three times (calibrates the HBM "
                          "byte counters of rocprofv3 against a kernel of known traffic) and exit")
@@ -208,7 +210,7 @@ def row_stats_bytes(w) -> float:
     return float(rows * w["V"] * 4 + rows * nch * 16)
 
 
-def cpu_baseline(w, budget_s: float):
+def cpu_baseline(w, budget_s: float, min_p: float = 0.0):
     """The fp64 oracle (attention of every (node, head) of a request, then the
     verification walk) over whole requests in order until the budget is spent.
     Returns verified draft tokens/s of that sample, the thread count and a
@@ -245,7 +247,7 @@ def cpu_baseline(w, budget_s: float):
         oracle.attention(q, k, v, ctx[b0:b1], sub_cu, par[n0:n1], Hq=w["Hq"], Hkv=w["Hkv"], dtype=w["dtype"],
                          nthreads=threads)
         oracle.verify(sub_cu, par[n0:n1], toks, lg, qq, temperature=w["temperature"], seed=w["seed"],
-                      request_id=np.arange(b0, b1, dtype=np.uint32), nthreads=threads)
+                      request_id=np.arange(b0, b1, dtype=np.uint32), nthreads=threads, min_p=min_p)
         spent += time.perf_counter() - t0
         nodes_done += n1 - n0
         req_done = b1
@@ -293,7 +295,7 @@ def main():
                             max_nodes=x["max_T"])
             s = sv.SampleCall(a.keep["cu"], x["parent_t"], x["draft_tokens"], x["logits"], x["draft_probs"],
                               temperature=cfg.temperature, seed=x["seed"], max_nodes=x["max_T"],
-                              residual_passes=True)
+                              residual_passes=True, min_p=args.min_p)
             calls.append((a, s, sv.StepCall(a, s)))
     torch.cuda.synchronize()
 
@@ -365,7 +367,7 @@ def main():
 
     cpu = None
     if args.cpu_seconds > 0:
-        v_cpu, threads, desc = cpu_baseline(w, args.cpu_seconds)
+        v_cpu, threads, desc = cpu_baseline(w, args.cpu_seconds, args.min_p)
         cpu = {"value": round(v_cpu, 2), "unit": "verified draft tokens/s", "cores": threads, "kind": "oracle",
                "sample": desc}
 
@@ -385,7 +387,7 @@ def main():
         "data": "synthetic (seeded; no dataset, no model weights)",
         "config": {"workload": cfg.name, "B": w["B"], "draft_nodes": w["N"], "max_T": w["max_T"], "L": cfg.L,
                    "Hq": cfg.Hq, "Hkv": cfg.Hkv, "D": cfg.D, "kv_dtype": cfg.dtype, "V": cfg.V,
-                   "temperature": cfg.temperature},
+                   "temperature": cfg.temperature, **({"min_p": args.min_p} if args.min_p > 0 else {})},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "input_sets": n_sets,

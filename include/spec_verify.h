@@ -154,6 +154,15 @@ typedef struct {
   const float* target_logits;  /* [N+B, V] fp32 rows as described above    */
   const float* draft_probs;    /* [N+B, V] fp32; may be NULL if temperature == 0 */
   float temperature;   /* 0 = greedy; > 0 = sampled                           */
+  float min_p;         /* 0 = off; in (0, 1) with temperature > 0: verify
+                          against the min-p truncated target ([LOSSY] 2.3,
+                          "truncation sampling + SD", G.2): p restricted to
+                          A = {x : l_x - l_max >= fp32(T ln min_p)} (that is,
+                          p(x) >= min_p * max p, decided on the fp32 logit
+                          difference) and renormalised; every rule below then
+                          applies with p_Theta in place of p. Each visited
+                          position costs one more vocabulary pass (the mass
+                          of A). Not with probs_out.                         */
   uint64_t seed;       /* Philox key                                          */
   uint32_t step;       /* Philox counter word 3 (replay / advance)            */
   const uint32_t* request_id; /* [B] Philox counter word 0; NULL means b    */

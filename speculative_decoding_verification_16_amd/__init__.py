@@ -41,7 +41,8 @@ class SvAttnArgs(ctypes.Structure):
 class SvSampleArgs(ctypes.Structure):
     _fields_ = [("B", _i32), ("V", _i32), ("total_nodes", _i32), ("max_nodes", _i32), ("cu_nodes", _P),
                 ("parent", _P), ("draft_tokens", _P), ("target_logits", _P), ("draft_probs", _P),
-                ("temperature", _f32), ("seed", _u64), ("step", _u32), ("request_id", _P), ("max_depth", _i32),
+                ("temperature", _f32), ("min_p", _f32), ("seed", _u64), ("step", _u32), ("request_id", _P),
+                ("max_depth", _i32),
                 ("accept_len", _P), ("accepted_nodes", _P), ("out_tokens", _P), ("probs_out", _P),
                 ("uniforms_out", _P), ("residual_passes", _P), ("status", _P), ("prof_start", _P),
                 ("prof_stop", _P)]
@@ -168,7 +169,7 @@ class SampleCall:
 
     def __init__(self, cu_nodes, parent, draft_tokens, target_logits, draft_probs, *, temperature, seed, step=0,
                  request_id=None, max_nodes=0, max_depth=None, probs_out=False, uniforms_out=False,
-                 residual_passes=False, status=None):
+                 residual_passes=False, status=None, min_p=0.0):
         load_library()
         dev = target_logits.device
         assert target_logits.is_cuda and target_logits.dtype == torch.float32 and target_logits.is_contiguous()
@@ -197,6 +198,7 @@ class SampleCall:
         s.cu_nodes, s.parent, s.draft_tokens = _ptr(cu), _ptr(self.keep["parent"]), _ptr(toks)
         s.target_logits, s.draft_probs = _ptr(target_logits), _ptr(draft_probs)
         s.temperature, s.seed, s.step = float(temperature), int(seed), int(step)
+        s.min_p = float(min_p)
         s.request_id = _ptr(self.keep["rid"])
         s.max_depth = md
         s.accept_len, s.accepted_nodes, s.out_tokens = _ptr(self.accept_len), _ptr(self.accepted_nodes), \

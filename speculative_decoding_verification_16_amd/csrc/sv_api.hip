@@ -167,6 +167,7 @@ sv_status check_sample(const sv_sample_args* s) {
     return fail(SV_ERR_INVALID_ARG, "temperature must be finite and >= 0");
   if (s->temperature > 0.f && !isfinite(1.4426950408889634 / (double)s->temperature) )
     return fail(SV_ERR_INVALID_ARG, "temperature too small");
+  if (!(s->min_p >= 0.f && s->min_p < 1.f)) return fail(SV_ERR_INVALID_ARG, "min_p must be in [0, 1)");
   const int md_needed = eff_max_nodes(s->max_nodes);
   if (s->max_depth < md_needed)
     return fail(SV_ERR_INVALID_ARG, "max_depth (%d) must be >= max_nodes (%d)", s->max_depth, md_needed);
@@ -181,6 +182,9 @@ sv_status check_sample(const sv_sample_args* s) {
     return fail(SV_ERR_INVALID_ARG, "draft_probs is required when temperature > 0");
   if (s->probs_out && s->temperature == 0.f)
     return fail(SV_ERR_INVALID_ARG, "probs_out needs temperature > 0");
+  if (s->probs_out && s->min_p > 0.f)
+    return fail(SV_ERR_UNSUPPORTED, "probs_out is not available with min_p > 0 (the truncated rows are normalised "
+                                    "only at the positions the walk visits)");
   if (!aligned(s->target_logits, 4) || (s->draft_probs && !aligned(s->draft_probs, 4)))
     return fail(SV_ERR_INVALID_ARG, "logit and probability rows must be 4-byte aligned");
   if (!aligned(s->uniforms_out, 8)) return fail(SV_ERR_INVALID_ARG, "uniforms_out must be 8-byte aligned");
@@ -257,6 +261,9 @@ sv_status run_sample(const sv_sample_args* s, char* ws, const WsLayout& w, hipSt
   p.q = s->draft_probs;
   p.greedy = s->temperature == 0.f;
   p.c = p.greedy ? 0.f : (float)(1.4426950408889634 / (double)s->temperature);
+  // min-p allowed set: logit - row max >= fp32(T ln min_p), from the fp32 T and min_p
+  p.trunc = !p.greedy && s->min_p > 0.f;
+  p.theta = p.trunc ? (float)((double)s->temperature * log((double)s->min_p)) : -INFINITY;
   p.seed = s->seed;
   p.step = s->step;
   p.request_id = s->request_id;

@@ -115,6 +115,15 @@ __device__ __forceinline__ float residual_weight(float logit, float q, float lma
   return fmaxf(0.f, fmaf(-ccS, q, target_weight(logit, lmax, c)));
 }
 
+// Min-p truncation ([LOSSY] section 2.3): token x is in the allowed set iff
+// logit - lmax >= theta with theta = fp32(T ln p_base) -- p(x) >= p_base
+// max p written on the fp32 logit difference, the comparison every side of
+// the library (and its checker) makes identically. TR = false: no truncation.
+template <bool TR>
+__device__ __forceinline__ float allowed(float w, float logit, float lmax, float theta) {
+  return (!TR || logit - lmax >= theta) ? w : 0.f;
+}
+
 // Row normalisation from its chunk statistics, computed by one full wave
 // (every lane returns the same values): lmax = max over chunks,
 // S = sum_ch s_ch * exp2((lmax_ch - lmax) * c) in fp64, summed lane-strided

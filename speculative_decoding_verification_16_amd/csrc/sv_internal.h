@@ -67,6 +67,8 @@ struct SampleParams {
   const float* q;           // [N+B, V] (unused when greedy)
   float c;                  // log2(e) / temperature (0 when greedy)
   bool greedy;
+  bool trunc;               // min-p truncation of the target rows
+  float theta;              // its threshold on logit - row max: fp32(T ln min_p)
   uint64_t seed;
   uint32_t step;
   const uint32_t* request_id;

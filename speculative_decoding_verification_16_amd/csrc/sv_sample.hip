@@ -225,33 +225,35 @@ __device__ __forceinline__ void half_load(HalfRegs& r, __amdgpu_buffer_rsrc_t lr
 // Unnormalised mass S * sum max(0, p - cc q) of the half-chunk in r: the four
 // tokens of a float4 are added in fp32, the rest in fp64. MASK drops float4s
 // past the row's end (only the row's last half-chunk needs it).
-template <bool MASK>
+template <bool MASK, bool TR>
 __device__ __forceinline__ double half_reduce(const HalfRegs& r, int V, int h, int lane, float lmax, float c,
-                                              float ccS) {
+                                              float ccS, float theta) {
   const int n4 = V >> 2;
   const int b4 = h * (kHalf / 4) + lane;
   double acc = 0.0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    float t = (residual_weight(r.l[i].x, r.q[i].x, lmax, c, ccS) +
-               residual_weight(r.l[i].y, r.q[i].y, lmax, c, ccS)) +
-              (residual_weight(r.l[i].z, r.q[i].z, lmax, c, ccS) +
-               residual_weight(r.l[i].w, r.q[i].w, lmax, c, ccS));
+    float t = (allowed<TR>(residual_weight(r.l[i].x, r.q[i].x, lmax, c, ccS), r.l[i].x, lmax, theta) +
+               allowed<TR>(residual_weight(r.l[i].y, r.q[i].y, lmax, c, ccS), r.l[i].y, lmax, theta)) +
+              (allowed<TR>(residual_weight(r.l[i].z, r.q[i].z, lmax, c, ccS), r.l[i].z, lmax, theta) +
+               allowed<TR>(residual_weight(r.l[i].w, r.q[i].w, lmax, c, ccS), r.l[i].w, lmax, theta));
     if (MASK) t = b4 + 64 * i < n4 ? t : 0.f;
     acc += (double)t;
   }
   return wave_sum(acc);
 }
 
-template <bool VEC>
-__device__ __forceinline__ double half_mass(const HalfRegs& r, int V, int h, int lane, float lmax, float c, float ccS) {
+template <bool VEC, bool TR>
+__device__ __forceinline__ double half_mass(const HalfRegs& r, int V, int h, int lane, float lmax, float c, float ccS,
+                                            float theta) {
   // wave-uniform test: is the whole half-chunk inside the row?
-  return (h + 1) * kHalf <= V ? half_reduce<false>(r, V, h, lane, lmax, c, ccS)
-                              : half_reduce<true>(r, V, h, lane, lmax, c, ccS);
+  return (h + 1) * kHalf <= V ? half_reduce<false, TR>(r, V, h, lane, lmax, c, ccS, theta)
+                              : half_reduce<true, TR>(r, V, h, lane, lmax, c, ccS, theta);
 }
 
+template <bool TR>
 __device__ __forceinline__ double half_scalar(const float* lrow, const float* qrow, int V, int h, float lmax, float c,
-                                              float ccS, int lane) {
+                                              float ccS, float theta, int lane) {
   const int begin = h * kHalf, end = min(V, begin + kHalf);
   float lv[32], qv[32];
 #pragma unroll
@@ -262,7 +264,8 @@ __device__ __forceinline__ double half_scalar(const float* lrow, const float* qr
   }
   double acc = 0.0;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) acc += (double)residual_weight(lv[i], qv[i], lmax, c, ccS);
+  for (int i = 0; i < 32; ++i)
+    acc += (double)allowed<TR>(residual_weight(lv[i], qv[i], lmax, c, ccS), lv[i], lmax, theta);
   return wave_sum(acc);
 }
 
@@ -270,10 +273,10 @@ __device__ __forceinline__ double half_scalar(const float* lrow, const float* qr
 // under max(0, p - cc q) (its two halves added in order); returns the total
 // (bitwise the same in every thread of every slice). pass_no counts the
 // request's passes from 1 (the barrier target and the buffer parity).
-template <bool VEC, int NT>
+template <bool VEC, int NT, bool TR>
 __device__ __forceinline__ double residual_pass(WalkShared<NT>& sh, const float* lrow, const float* qrow, int V, int nch,
-                                                float lmax, float c, double S, double cc, const Slices& sl,
-                                                int pass_no) {
+                                                float lmax, float c, float theta, double S, double cc,
+                                                const Slices& sl, int pass_no) {
   constexpr int NW = NT / kWave;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nh = 2 * nch;
@@ -286,20 +289,23 @@ __device__ __forceinline__ double residual_pass(WalkShared<NT>& sh, const float*
     // before the current one is reduced (past the row's end they read zeros).
     if (gw < nh) {
       const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc((void*)lrow, (short)0, V * 4, 0x00020000);
-      const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc((void*)qrow, (short)0, V * 4, 0x00020000);
+      // cc == 0 (the min-p visit pass: mass of p itself) needs no q: an empty
+      // resource makes every q load read zero without touching memory
+      const __amdgpu_buffer_rsrc_t qrs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)qrow, (short)0, cc == 0.0 ? 0 : V * 4, 0x00020000);
       HalfRegs ra, rb;
       half_load(ra, lrs, qrs, gw, lane);
       for (int h = gw; h < nh; h += 2 * GW) {
         const int h1 = h + GW;
         half_load(rb, lrs, qrs, h1, lane);
-        const double m0 = half_mass<VEC>(ra, V, h, lane, lmax, c, ccS) * invS;
+        const double m0 = half_mass<VEC, TR>(ra, V, h, lane, lmax, c, ccS, theta) * invS;
         if (lane == 0) {
           sh.hsum[h] = m0;
           if (sl.n > 1) xb[h] = m0;
         }
         half_load(ra, lrs, qrs, h1 + GW, lane);
         if (h1 < nh) {
-          const double m1 = half_mass<VEC>(rb, V, h1, lane, lmax, c, ccS) * invS;
+          const double m1 = half_mass<VEC, TR>(rb, V, h1, lane, lmax, c, ccS, theta) * invS;
           if (lane == 0) {
             sh.hsum[h1] = m1;
             if (sl.n > 1) xb[h1] = m1;
@@ -309,7 +315,7 @@ __device__ __forceinline__ double residual_pass(WalkShared<NT>& sh, const float*
     }
   } else {
     for (int h = gw; h < nh; h += GW) {
-      const double m = half_scalar(lrow, qrow, V, h, lmax, c, ccS, lane) * invS;
+      const double m = half_scalar<TR>(lrow, qrow, V, h, lmax, c, ccS, theta, lane) * invS;
       if (lane == 0) {
         sh.hsum[h] = m;
         if (sl.n > 1) xb[h] = m;
@@ -361,9 +367,9 @@ __device__ __forceinline__ double residual_pass(WalkShared<NT>& sh, const float*
 // within each wave, the wave totals are added in wave order, and the first
 // lane whose inclusive prefix crosses the remainder picks the token among its
 // DPL.
-template <bool VEC, int NT>
+template <bool VEC, int NT, bool TR>
 __device__ __forceinline__ int draw_token(WalkShared<NT>& sh, const float* lrow, const float* qrow, int V, int nch,
-                                          int level, float lmax, float c, double S, double cc, double u,
+                                          int level, float lmax, float c, float theta, double S, double cc, double u,
                                           double total) {
   constexpr int NW = NT / kWave;
   constexpr int kDrawPerLane = kChunk / NT;
@@ -420,8 +426,8 @@ __device__ __forceinline__ int draw_token(WalkShared<NT>& sh, const float* lrow,
   for (int i = 0; i < kDrawPerLane; ++i) {
     // weights of the distribution being drawn from (level 0: unnormalised p;
     // above: max(0, p - cc q) as the residual passes compute it)
-    w[i] = level == 0 ? (double)target_weight(lv[i], lmax, c)
-                      : (double)residual_weight(lv[i], qv[i], lmax, c, ccS) * invS;
+    w[i] = level == 0 ? (double)allowed<TR>(target_weight(lv[i], lmax, c), lv[i], lmax, theta)
+                      : (double)allowed<TR>(residual_weight(lv[i], qv[i], lmax, c, ccS), lv[i], lmax, theta) * invS;
     seg += w[i];
     lastpos = w[i] > 0.0 ? x0 + i : lastpos;
   }
@@ -482,7 +488,7 @@ __device__ __forceinline__ void skip_request(const SampleParams& p, int b, int32
   }
 }
 
-template <bool VEC, int NT>
+template <bool VEC, int NT, bool TR>
 __global__ __launch_bounds__(NT) void walk_kernel(SampleParams p) {
   __shared__ WalkShared<NT> sh;
   const int b = blockIdx.x / p.slices, slice = blockIdx.x - b * p.slices;
@@ -614,21 +620,30 @@ __global__ __launch_bounds__(NT) void walk_kernel(SampleParams p) {
       continue;
     }
 
-    const float invS = (float)(1.0 / st.S);
+    // The target here: p, or under min-p truncation p_Theta = p on the allowed
+    // set renormalised by its mass S_A (one vocabulary pass at this position,
+    // which also leaves the chunk masses of p_Theta in csum for a draw).
+    double Srow = st.S;
+    bool csum_ok = false;      // csum holds the chunk masses of the current level
+    if (TR) {
+      Srow = residual_pass<VEC, NT, TR>(sh, lrow, qrow, p.V, p.nch, st.lmax, p.c, p.theta, 1.0, 0.0, sl, ++npass);
+      csum_ok = true;
+    }
+    const float invS = (float)(1.0 / Srow);
     double cc = 0.0, M = 1.0;  // current distribution max(0, p - cc q) / M (cc = 0: p itself)
     int level = 0;
-    bool csum_ok = false;      // csum holds the chunk masses of the current level
     int accepted = -1;
     for (uint64_t k = kids; k; k &= k - 1) {
       const int ch = __ffsll((unsigned long long)k) - 1;
-      const float pf = target_prob(sh.lgx[ch], st.lmax, p.c, invS);
+      const float pf = allowed<TR>(target_prob(sh.lgx[ch], st.lmax, p.c, invS), sh.lgx[ch], st.lmax, p.theta);
       const double qv = (double)sh.qx[ch];
       const double P = level == 0 ? (double)pf : fmax(0.0, (double)pf - cc * qv) / M;
       const int ok = __builtin_amdgcn_readfirstlane((P > 0.0 && sh.u[ch] * qv <= P) ? 1 : 0);
       if (ok) { accepted = ch; break; }
       // rejected: the next sibling is tested against the next residual level
       const double cn = cc + M;
-      const double Mn = residual_pass<VEC, NT>(sh, lrow, qrow, p.V, p.nch, st.lmax, p.c, st.S, cn, sl, ++npass);
+      const double Mn =
+          residual_pass<VEC, NT, TR>(sh, lrow, qrow, p.V, p.nch, st.lmax, p.c, p.theta, Srow, cn, sl, ++npass);
       ++passes;
       if (__builtin_amdgcn_readfirstlane(Mn > 0.0 ? 1 : 0)) {
         cc = cn;
@@ -648,7 +663,9 @@ __global__ __launch_bounds__(NT) void walk_kernel(SampleParams p) {
     }
     // final draw at this position from the current distribution
     double total;
-    if (level == 0) {
+    if (level == 0 && TR) {  // the chunk masses of p_Theta from this position's pass
+      total = Srow;
+    } else if (level == 0) {
       const ChunkStat* cs = p.stats + row * p.nch;
       for (int ch = tid; ch < p.nch; ch += NT) {
         const ChunkStat s = cs[ch];
@@ -658,14 +675,14 @@ __global__ __launch_bounds__(NT) void walk_kernel(SampleParams p) {
       total = st.S;
     } else {
       if (!csum_ok) {
-        residual_pass<VEC, NT>(sh, lrow, qrow, p.V, p.nch, st.lmax, p.c, st.S, cc, sl, ++npass);
+        residual_pass<VEC, NT, TR>(sh, lrow, qrow, p.V, p.nch, st.lmax, p.c, p.theta, Srow, cc, sl, ++npass);
         ++passes;
       }
       total = M;
     }
     if (!lead) return;  // the draw needs no other slice: the rest are done
     const double uf = uniform01(p.seed, rid, 0u, 1u, p.step);
-    bonus = draw_token<VEC, NT>(sh, lrow, qrow, p.V, p.nch, level, st.lmax, p.c, st.S, cc, uf, total);
+    bonus = draw_token<VEC, NT, TR>(sh, lrow, qrow, p.V, p.nch, level, st.lmax, p.c, p.theta, Srow, cc, uf, total);
     break;
   }
   if (lead && tid == 0) {
@@ -711,11 +728,21 @@ hipError_t launch_sampler(const SampleParams& p, bool vec4, hipStream_t stream, 
     SampleParams ps = p;
     ps.join_ticks = ticks >= 0 && ticks <= 100000000L ? (uint32_t)ticks : kJoinWindow;
     const dim3 grid((unsigned)(p.B * p.slices));
-    if (vec4) walk_kernel<true, 256><<<grid, dim3(256), 0, stream>>>(ps);
-    else walk_kernel<false, 256><<<grid, dim3(256), 0, stream>>>(ps);
+    if (p.trunc) {
+      if (vec4) walk_kernel<true, 256, true><<<grid, dim3(256), 0, stream>>>(ps);
+      else walk_kernel<false, 256, true><<<grid, dim3(256), 0, stream>>>(ps);
+    } else {
+      if (vec4) walk_kernel<true, 256, false><<<grid, dim3(256), 0, stream>>>(ps);
+      else walk_kernel<false, 256, false><<<grid, dim3(256), 0, stream>>>(ps);
+    }
   } else {
-    if (vec4) walk_kernel<true, 512><<<dim3(p.B), dim3(512), 0, stream>>>(p);
-    else walk_kernel<false, 512><<<dim3(p.B), dim3(512), 0, stream>>>(p);
+    if (p.trunc) {
+      if (vec4) walk_kernel<true, 512, true><<<dim3(p.B), dim3(512), 0, stream>>>(p);
+      else walk_kernel<false, 512, true><<<dim3(p.B), dim3(512), 0, stream>>>(p);
+    } else {
+      if (vec4) walk_kernel<true, 512, false><<<dim3(p.B), dim3(512), 0, stream>>>(p);
+      else walk_kernel<false, 512, false><<<dim3(p.B), dim3(512), 0, stream>>>(p);
+    }
   }
   return hipGetLastError();
 }
@@ -742,12 +769,14 @@ int walk_slices(int B, int nch, bool greedy) {
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
   if (per_cu_cached[dev] == 0) {
     int a = 0, b = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, walk_kernel<true, 256>, 256, 0) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, walk_kernel<false, 256>, 256, 0) != hipSuccess) {
+    int t = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, walk_kernel<true, 256, false>, 256, 0) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, walk_kernel<false, 256, false>, 256, 0) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&t, walk_kernel<true, 256, true>, 256, 0) != hipSuccess) {
       (void)hipGetLastError();
-      a = b = 0;
+      a = b = t = 0;
     }
-    per_cu_cached[dev] = max(1, min(a, b));  // 1 when unknown: then a batch of >= CUs requests gets 1 slice
+    per_cu_cached[dev] = max(1, min(min(a, b), t));  // 1 when unknown: then a batch of >= CUs requests gets 1 slice
   }
   const int64_t capacity = (int64_t)per_cu_cached[dev] * device_cus();
   // every wave of the request gets at least one half-chunk; past 8 slices the

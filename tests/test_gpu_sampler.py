@@ -44,10 +44,10 @@ def _gpu_sample(w, temperature, **kw):
     return r
 
 
-def _oracle(w, temperature, max_depth, q=None):
+def _oracle(w, temperature, max_depth, q=None, min_p=0.0):
     return oracle.verify(w["cu_nodes"], w["parent"], w["draft_tokens"].cpu().numpy(), w["logits"].cpu().numpy(),
                          (q if q is not None else w["draft_probs"].cpu().numpy()) if temperature > 0 else None,
-                         temperature=temperature, seed=w["seed"], max_depth=max_depth)
+                         temperature=temperature, seed=w["seed"], max_depth=max_depth, min_p=min_p)
 
 
 @pytest.mark.parametrize("mode", ["sampled", "greedy"])
@@ -225,3 +225,110 @@ def test_walk_board_full_batch_matches_single(monkeypatch):
     r = _gpu_sample(w, 1.0)
     for k in ("accept_len", "accepted_nodes", "out_tokens", "uniforms", "residual_passes"):
         assert torch.equal(r[k], ref[k]), k
+
+
+# ---- min-p truncation sampling + speculative verification ([LOSSY] 2.3, G.2) ----
+MIN_P_SMALL = ["c1_full", "c2_small", "c3_small", "c5_small_odd_vocab", "c4_small_cold", "vocab_one", "max_tree_64"]
+
+
+def _assert_in_allowed_set(w, r, T, min_p):
+    """Every emitted token (accepted drafts and the bonus) lies in the min-p
+    set of the row it was drawn against: the fp32 rule l_x - l_max >= theta."""
+    theta = np.float32(oracle.min_p_theta(T, min_p))
+    lg = w["logits"].cpu().numpy()
+    acc = r["accept_len"].cpu().numpy()
+    nodes = r["accepted_nodes"].cpu().numpy()
+    toks = r["out_tokens"].cpu().numpy()
+    cu = w["cu_nodes"]
+    for b in range(w["B"]):
+        base = cu[b] + b  # request b's rows: base (root position), base + 1 + j (after node j)
+        pos = base
+        for d in range(acc[b] + 1):
+            row = lg[pos]
+            assert row[toks[b, d]] - row.max() >= theta, (b, d)
+            if d < acc[b]:
+                pos = base + 1 + nodes[b, d]
+
+
+@pytest.mark.parametrize("min_p", [0.05, 0.3])
+@pytest.mark.parametrize("name", MIN_P_SMALL)
+def test_sampler_min_p_small(name, min_p):
+    cfg = SMALL[name]
+    w = generate(cfg, "cuda", attn=False)
+    T = cfg.temperature
+    print(f"[min-p] {name} min_p={min_p} B={w['B']} N={w['N']} V={cfg.V}", flush=True)
+    r = _gpu_sample(w, T, min_p=min_p)
+    md = r["accepted_nodes"].shape[1]
+    ref = _oracle(w, T, md, min_p=min_p)
+    assert int(r["status"].item()) == 0, sv.status_names(int(r["status"].item()))
+    assert np.array_equal(r["uniforms"].cpu().numpy(), ref["uniforms"])
+    flagged = compare_walk(r, ref, w["B"], greedy=False)
+    print(f"  flagged near-ties: {flagged}/{w['B']}")
+    ok = ref["flag_depth"] < 0
+    assert np.array_equal(r["residual_passes"].cpu().numpy()[ok], ref["n_rejections"][ok])
+    _assert_in_allowed_set(w, r, T, min_p)
+
+
+@pytest.mark.parametrize("name", ["c2_llama8b_chain", "c3_eagle_tree", "c5_super_tree", "c4_L8192_B32_T0.5"])
+def test_sampler_min_p_full_size(name):
+    cfg = get_config(name)
+    w = generate(cfg, "cuda", attn=False)
+    T, min_p = cfg.temperature, 0.1
+    print(f"[min-p-full] {name} B={w['B']} N={w['N']} V={cfg.V}", flush=True)
+    r = _gpu_sample(w, T, min_p=min_p)
+    ref = _oracle(w, T, r["accepted_nodes"].shape[1], min_p=min_p)
+    assert int(r["status"].item()) == 0, sv.status_names(int(r["status"].item()))
+    flagged = compare_walk(r, ref, w["B"], greedy=False)
+    print(f"  flagged near-ties: {flagged}/{w['B']}; mean accept_len {r['accept_len'].float().mean().item():.3f}")
+    _assert_in_allowed_set(w, r, T, min_p)
+
+
+def test_min_p_tiny_matches_plain_and_greedy_ignores_it():
+    cfg = SMALL["c3_small"]
+    w = generate(cfg, "cuda", attn=False)
+    T = cfg.temperature
+    md = max(int(np.diff(w["cu_nodes"]).max()), 1)
+    ref = _oracle(w, T, md)  # the untruncated walk
+    r = _gpu_sample(w, T, min_p=1e-30)
+    compare_walk(r, ref, w["B"], greedy=False)
+    g0 = _gpu_sample(w, 0.0)
+    g1 = _gpu_sample(w, 0.0, min_p=0.5)
+    for k in ("accept_len", "accepted_nodes", "out_tokens"):
+        assert torch.equal(g0[k], g1[k]), k
+
+
+def test_min_p_rejects_probs_out_and_bad_values():
+    cfg = SMALL["c2_small"]
+    w = generate(cfg, "cuda", attn=False)
+    with pytest.raises(sv.SpecVerifyError):
+        _gpu_sample(w, 1.0, min_p=0.2, probs_out=True)
+    for bad in (-0.1, 1.0, float("nan")):
+        with pytest.raises(sv.SpecVerifyError):
+            _gpu_sample(w, 1.0, min_p=bad)
+
+
+@pytest.mark.parametrize("min_p", [0.1, 0.4])
+def test_gpu_min_p_chi_square(min_p):
+    """The emitted first token follows p_Theta (a chi-square over its support)
+    and never falls outside it; one accepted candidate has probability
+    sum_x min(p_Theta(x), q(x)) ([LOSSY] G.3)."""
+    rng = np.random.default_rng(211 if min_p < 0.2 else 212)
+    V, n, T = 8, 1_000_000, 1.0
+    parent = np.array([-1, 0], np.int32)
+    lg, q = rows_from_probs(rng, V, parent.size + 1, sharp=1.0, draft_noise=1.2)
+    cu, par, toks, logits, qq = replicated_batch(rng, parent, lg, q, n)
+    r = sv.sample(torch.from_numpy(cu).cuda(), torch.from_numpy(par).cuda(), torch.from_numpy(toks).cuda(),
+                  torch.from_numpy(logits).cuda(), torch.from_numpy(qq).cuda(), temperature=T, seed=4343,
+                  max_nodes=parent.size, min_p=min_p)
+    torch.cuda.synchronize()
+    p = softmax64(lg[0], T)
+    keep = p >= min_p * p.max()
+    pt = np.where(keep, p, 0.0) / p[keep].sum()
+    first = r["out_tokens"][:, 0].cpu().numpy()
+    counts = np.bincount(first, minlength=V)
+    assert counts[~keep].sum() == 0
+    assert stats.chisquare(counts[keep], pt[keep] * n).pvalue > 1e-3
+    acc = r["accept_len"].cpu().numpy()
+    a0 = float(np.minimum(pt, q[0]).sum())
+    freq = (acc >= 1).mean()
+    assert abs(freq - a0) < 5 * math.sqrt(a0 * (1 - a0) / n)
