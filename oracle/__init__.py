@@ -16,11 +16,15 @@ Functions and the passages they follow:
                            "Interaction with Advanced Attention Architectures".
   target_probs, argmax     softmax(logits / T); greedy argmax.
   residual                 [SD] R_i(x); [LOSSY] appendix F.1 r(x).
+  remove_candidate         [LOSSY] appendix G.3: the target after a deterministic
+                           candidate is tried and rejected.
   inverse_cdf              the draw from R_i / p.
   verify                   the whole walk ([SD] acceptance rule; [LOSSY] 2.1 h(x)).
   min_p_theta,             [LOSSY] section 2.3: the min-p allowed set and the
   truncate_min_p           truncated target p_Theta; verify(min_p=...) walks
                            against p_Theta ("truncation sampling + SD", G.2/G.3).
+  verify(siblings=...)     "deterministic": the G.3 rule for deterministic
+                           candidates (p~_i, candidates removed one by one).
 """
 from __future__ import annotations
 
@@ -70,13 +74,15 @@ def _load():
     lib.orc_residual.restype = f64
     lib.orc_inverse_cdf.argtypes = [i32, P, f64, P]
     lib.orc_inverse_cdf.restype = i32
-    lib.orc_verify.argtypes = [i32, i32, P, P, P, P, P, f64, i32, ctypes.c_float, u64, u32, P, i32, P, P, P, P,
+    lib.orc_verify.argtypes = [i32, i32, P, P, P, P, P, f64, i32, ctypes.c_float, i32, u64, u32, P, i32, P, P, P, P,
                                P, P, P, P, P, P, f64, f64, i32]
     lib.orc_verify.restype = i32
     lib.orc_target_rows.argtypes = [i32, P, f64, i64, P, P]
     lib.orc_target_rows.restype = i32
     lib.orc_truncate_min_p.argtypes = [i32, P, ctypes.c_float, P]
     lib.orc_truncate_min_p.restype = None
+    lib.orc_remove_candidate.argtypes = [i32, P, i32, P]
+    lib.orc_remove_candidate.restype = f64
     _lib = lib
     return lib
 
@@ -190,6 +196,14 @@ def residual(P, Q) -> tuple[np.ndarray, float]:
     return out, float(R)
 
 
+def remove_candidate(P, x: int) -> tuple[np.ndarray, float]:
+    """P with token x taken out and renormalised ([LOSSY] G.3), and the mass left."""
+    P = np.ascontiguousarray(P, dtype=np.float64)
+    out = np.zeros_like(P)
+    R = _load().orc_remove_candidate(P.shape[0], _ptr(P), int(x), _ptr(out))
+    return out, float(R)
+
+
 def inverse_cdf(P, u: float) -> tuple[int, float]:
     P = np.ascontiguousarray(P, dtype=np.float64)
     m = np.zeros(1, dtype=np.float64)
@@ -216,12 +230,21 @@ def truncate_min_p(logits_row, p_row, theta: float) -> np.ndarray:
 
 
 def verify(cu_nodes, parent, tokens, logits, q, *, temperature, seed, step=0, request_id=None,
-           max_depth=None, accept_tol=ACCEPT_TOL, cdf_tol=CDF_TOL, nthreads=None, min_p=0.0) -> dict:
+           max_depth=None, accept_tol=ACCEPT_TOL, cdf_tol=CDF_TOL, nthreads=None, min_p=0.0,
+           siblings="sampled") -> dict:
     """The verification walk for a packed batch; returns a dict of numpy arrays.
 
-    logits, q: float32 [N+B, V] (q may be None when temperature == 0).
+    logits, q: float32 [N+B, V] (q may be None when temperature == 0 or the
+    siblings are deterministic).
     min_p > 0 verifies against the min-p truncated target ([LOSSY] 2.3, G.2).
+    siblings="deterministic": the children of a node are deterministic
+    candidates ([LOSSY] G.3): candidate i is accepted with probability
+    p~_i(x^(i)), the target with the candidates tried before it removed and
+    renormalised; q is not used.
     """
+    if siblings not in ("sampled", "deterministic"):
+        raise ValueError("siblings must be 'sampled' or 'deterministic'")
+    det = 1 if siblings == "deterministic" else 0
     cu = np.ascontiguousarray(cu_nodes, dtype=np.int32)
     B = cu.shape[0] - 1
     N = int(cu[-1]) if B >= 0 else 0
@@ -230,7 +253,7 @@ def verify(cu_nodes, parent, tokens, logits, q, *, temperature, seed, step=0, re
     lg = np.ascontiguousarray(logits, dtype=np.float32)
     V = int(lg.shape[1])
     qq = None if q is None else np.ascontiguousarray(q, dtype=np.float32)
-    if temperature > 0:
+    if temperature > 0 and not det:
         assert qq is not None and qq.shape == lg.shape
     rid = None if request_id is None else np.ascontiguousarray(request_id, dtype=np.uint32)
     if max_depth is None:
@@ -251,7 +274,7 @@ def verify(cu_nodes, parent, tokens, logits, q, *, temperature, seed, step=0, re
     theta = min_p_theta(temperature, min_p)
     trunc = 1 if theta > float("-inf") else 0
     rc = _load().orc_verify(B, V, _ptr(cu), _ptr(par), _ptr(tok), _ptr(lg), _ptr(qq), float(temperature),
-                            trunc, ctypes.c_float(theta), int(seed), int(step), _ptr(rid), int(max_depth), _ptr(out["accept_len"]),
+                            trunc, ctypes.c_float(theta), det, int(seed), int(step), _ptr(rid), int(max_depth), _ptr(out["accept_len"]),
                             _ptr(out["accepted_nodes"]), _ptr(out["out_tokens"]), _ptr(out["uniforms"]),
                             _ptr(out["flag_depth"]), _ptr(out["flag_kind"]), _ptr(out["n_rejections"]),
                             _ptr(out["status"]), _ptr(out["min_accept_margin"]), _ptr(out["cdf_margin"]),

@@ -303,6 +303,19 @@ double orc_residual(int V, const double* P, const double* Q, double* out) {
   return R;
 }
 
+/* Removal of a tried deterministic candidate ([LOSSY] G.3: the target the
+ * i-th candidate is tested against is p_Theta with the candidates tried
+ * before it taken out and renormalised): out = P with P[x] set to 0, divided
+ * by the mass left. Returns that mass; if it is 0 nothing is left to
+ * renormalise and out = P (kept unchanged), as in orc_residual.           */
+double orc_remove_candidate(int V, const double* P, int x, double* out) {
+  double R = 0.0;
+  for (int t = 0; t < V; ++t)
+    if (t != x) R += P[t];
+  for (int t = 0; t < V; ++t) out[t] = R > 0.0 ? (t == x ? 0.0 : P[t] / R) : P[t];
+  return R;
+}
+
 /* Inverse-CDF draw from an (unnormalised) non-negative vector P:
  * y = min{ x : sum_{t<=x} P(t) > u * sum_t P(t) } in vocabulary order; the
  * strict '>' means a zero-mass token is never drawn. *margin (optional) is
@@ -346,6 +359,7 @@ typedef struct {
   double T;
   int trunc;     /* min-p truncation of every target row */
   float theta;   /* its threshold on l_x - l_max         */
+  int det;       /* siblings are deterministic candidates (q unused) */
   uint64_t seed;
   uint32_t step;
   const uint32_t* request_id;
@@ -426,12 +440,29 @@ static void orc_walk_one(void* vctx, int64_t bi) {
      * position it was drafted at, i.e. its parent's row)                  */
     if (orc_target_probs(V, c->logits + row * (int64_t)V, c->T, P)) { c->status[b] |= 0x08; break; }
     if (c->trunc) orc_truncate_min_p(V, c->logits + row * (int64_t)V, c->theta, P);
-    for (int x = 0; x < V; ++x) Q[x] = (double)c->q[row * (int64_t)V + x];
+    if (!c->det)
+      for (int x = 0; x < V; ++x) Q[x] = (double)c->q[row * (int64_t)V + x];
     int accepted = -1;
     for (int ch = pos + 1; ch < T; ++ch) {
       if (par[ch] != pos) continue; /* children in increasing node index */
       double u = orc_uniform(c->seed, rid, (uint32_t)ch, 0, c->step);
       int x = tok[ch];
+      if (c->det) {
+        /* [LOSSY] G.3, deterministic candidates: x^(i) is accepted with
+         * probability p~_i(x^(i)), i.e. iff u <= P(x) with P the target
+         * after the earlier candidates were taken out (a token tried
+         * before has P = 0 and is rejected).                              */
+        int ok = P[x] > 0.0 && u <= P[x];
+        double margin = fabs(u - P[x]);
+        if (margin < c->min_accept_margin[b]) c->min_accept_margin[b] = margin;
+        if (margin < c->accept_tol && c->flag_depth[b] < 0) { c->flag_depth[b] = d; c->flag_kind[b] = 0; }
+        if (ok) { accepted = ch; break; }
+        c->n_rejections[b] += 1;
+        double R = orc_remove_candidate(V, P, x, tmp);
+        if (!(R > 0.0)) c->status[b] |= 0x10;
+        memcpy(P, tmp, sizeof(double) * (size_t)V);
+        continue;
+      }
       /* [SD] acceptance rule r <= min(1, p/q), written as u*q <= p with p > 0
        * so that q(x) = 0 follows the formula (ratio +inf, accepted).      */
       int ok = P[x] > 0.0 && u * Q[x] <= P[x];
@@ -455,7 +486,8 @@ static void orc_walk_one(void* vctx, int64_t bi) {
       continue;
     }
     /* no child accepted (or none to try): one token from the current
-     * distribution -- the residual after rejections, p at a leaf         */
+     * distribution -- the residual after rejections (with deterministic
+     * candidates: the target without the tried ones), p at a leaf        */
     double u = orc_uniform(c->seed, rid, 0, 1, c->step);
     double margin = 0.0;
     int y = orc_inverse_cdf(V, P, u, &margin);
@@ -473,25 +505,28 @@ static void orc_walk_one(void* vctx, int64_t bi) {
 /* Verification of a packed batch (see the calling convention of the GPU
  * library: rows cu_nodes[b] + b + r, r = 0 root, r = 1 + j after node j).
  * T == 0 selects greedy verification; trunc != 0 verifies against the
- * min-p truncated target (threshold theta, see orc_truncate_min_p). Per
+ * min-p truncated target (threshold theta, see orc_truncate_min_p); det != 0
+ * treats the siblings as deterministic candidates ([LOSSY] G.3; q unused and
+ * may be NULL; a rejection takes the candidate out of the target). Per
  * request it also reports
  *   flag_depth: accepted nodes before the first decision closer than the
  *               tolerance to its threshold (-1: none), flag_kind 0 = accept
  *               test, 1 = final inverse-CDF draw;
- *   n_rejections: rejections (= residual renormalisations);
+ *   n_rejections: rejections (= residual renormalisations or removals);
  *   status: SV_STATUS-like bits (0x01 tree, 0x02 packing, 0x04 token,
  *           0x08 non-finite row, 0x10 zero residual, 0x80 out of memory);
  *   min_accept_margin, cdf_margin: the smallest |u - P/Q| seen and the
  *           margin of the final draw.                                     */
 int orc_verify(int B, int V, const int32_t* cu_nodes, const int32_t* parent, const int32_t* tokens,
-               const float* logits, const float* q, double T, int trunc, float theta, uint64_t seed,
-               uint32_t step,
+               const float* logits, const float* q, double T, int trunc, float theta, int det,
+               uint64_t seed, uint32_t step,
                const uint32_t* request_id, int max_depth, int32_t* accept_len, int32_t* accepted_nodes,
                int32_t* out_tokens, double* uniforms_out, int32_t* flag_depth, int32_t* flag_kind,
                int32_t* n_rejections, int32_t* status, double* min_accept_margin, double* cdf_margin,
                double accept_tol, double cdf_tol, int nthreads) {
   if (B < 0 || V < 1 || max_depth < 0 || T < 0.0) return 1;
-  orc_walk_ctx c = {B, V, cu_nodes, parent, tokens, logits, q, T, trunc, theta, seed, step, request_id, max_depth,
+  if (T > 0.0 && !det && !q) return 1;
+  orc_walk_ctx c = {B, V, cu_nodes, parent, tokens, logits, q, T, trunc, theta, det, seed, step, request_id, max_depth,
                     accept_len, accepted_nodes, out_tokens, uniforms_out, flag_depth, flag_kind,
                     n_rejections, status, min_accept_margin, cdf_margin, accept_tol, cdf_tol};
   orc_parallel_for(B, nthreads, orc_walk_one, &c);
