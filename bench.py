@@ -111,6 +111,9 @@ def parse_args():
     ap.add_argument("--no-events", action="store_true", help="time without the per-kernel HIP events")
     ap.add_argument("--min-p", type=float, default=0.0,
                     help="verify against the min-p truncated target (0 = plain lossless verification)")
+    ap.add_argument("--siblings", choices=["sampled", "deterministic"], default="sampled",
+                    help="sampled: draft tokens are draws from q; deterministic: the top-k of q as fixed "
+                         "candidates, verified by the deterministic-candidate rule (q is not read)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES three times (calibrates the HBM "
                          "byte counters of rocprofv3 against a kernel of known traffic) and exit")
@@ -210,7 +213,7 @@ def row_stats_bytes(w) -> float:
     return float(rows * w["V"] * 4 + rows * nch * 16)
 
 
-def cpu_baseline(w, budget_s: float, min_p: float = 0.0):
+def cpu_baseline(w, budget_s: float, min_p: float = 0.0, siblings: str = "sampled"):
     """The fp64 oracle (attention of every (node, head) of a request, then the
     verification walk) over whole requests in order until the budget is spent.
     Returns verified draft tokens/s of that sample, the thread count and a
@@ -247,7 +250,8 @@ def cpu_baseline(w, budget_s: float, min_p: float = 0.0):
         oracle.attention(q, k, v, ctx[b0:b1], sub_cu, par[n0:n1], Hq=w["Hq"], Hkv=w["Hkv"], dtype=w["dtype"],
                          nthreads=threads)
         oracle.verify(sub_cu, par[n0:n1], toks, lg, qq, temperature=w["temperature"], seed=w["seed"],
-                      request_id=np.arange(b0, b1, dtype=np.uint32), nthreads=threads, min_p=min_p)
+                      request_id=np.arange(b0, b1, dtype=np.uint32), nthreads=threads, min_p=min_p,
+                      siblings=siblings)
         spent += time.perf_counter() - t0
         nodes_done += n1 - n0
         req_done = b1
@@ -278,13 +282,15 @@ def main():
     sv.load_library()  # fails loudly if the HIP library is missing
     dev = torch.device("cuda:0")
     cfg = get_config(args.workload)
-    w = generate(cfg, dev)
+    det = args.siblings == "deterministic"
+    cand = "topk" if det else "sampled"
+    w = generate(cfg, dev, candidates=cand)
     # Small workloads would stay in the 256 MB last-level cache from one step
     # to the next: consecutive steps then cycle through copies of the inputs
     # in separate buffers, at least 512 MB together (at most 8 copies).
     set_bytes = attention_bytes(w) + 8 * w["V"] * (w["N"] + w["B"])
     n_sets = max(1, min(MAX_INPUT_SETS, math.ceil(ROTATE_BYTES / set_bytes)))
-    sets = [w] + [generate(cfg, dev) for _ in range(n_sets - 1)]
+    sets = [w] + [generate(cfg, dev, candidates=cand) for _ in range(n_sets - 1)]
     torch.cuda.synchronize()
 
     stream = torch.cuda.Stream()  # default priority
@@ -293,9 +299,10 @@ def main():
         for x in sets:
             a = sv.AttnCall(x["q"], x["k_cache"], x["v_cache"], x["ctx_len_t"], x["cu_nodes_t"], parent=x["parent_t"],
                             max_nodes=x["max_T"])
-            s = sv.SampleCall(a.keep["cu"], x["parent_t"], x["draft_tokens"], x["logits"], x["draft_probs"],
-                              temperature=cfg.temperature, seed=x["seed"], max_nodes=x["max_T"],
-                              residual_passes=True, min_p=args.min_p)
+            s = sv.SampleCall(a.keep["cu"], x["parent_t"], x["draft_tokens"], x["logits"],
+                              None if det else x["draft_probs"], temperature=cfg.temperature, seed=x["seed"],
+                              max_nodes=x["max_T"], residual_passes=True, min_p=args.min_p,
+                              siblings=args.siblings)
             calls.append((a, s, sv.StepCall(a, s)))
     torch.cuda.synchronize()
 
@@ -354,8 +361,11 @@ def main():
                               "TFLOP_s": attn_f / attn_ms / 1e9}
         kernels["row_stats_kernel"] = {"us": rs_ms * 1e3, "alg_bytes": rs_b, "GB_s": rs_b / rs_ms / 1e6}
         rest_us = ms * 1e3 - attn_ms * 1e3 - rs_ms * 1e3
+        # sampled siblings: one 8V pass (logits and q) per rejection; deterministic
+        # candidates need none (the min-p visit passes are not counted here)
+        per_pass = 0 if det else 8 * w["V"]
         kernels["other(prep+finalize+walk)"] = {"us": rest_us,
-                                            "residual_pass_bytes": float(passes.sum().item()) * 8 * w["V"]}
+                                            "residual_pass_bytes": float(passes.sum().item()) * per_pass}
         dom = max((k for k in kernels if "alg_bytes" in kernels[k]), key=lambda k: kernels[k]["us"])
         dk = kernels[dom]
         traffic = counter_traffic(dom, cfg.name)
@@ -367,7 +377,7 @@ def main():
 
     cpu = None
     if args.cpu_seconds > 0:
-        v_cpu, threads, desc = cpu_baseline(w, args.cpu_seconds, args.min_p)
+        v_cpu, threads, desc = cpu_baseline(w, args.cpu_seconds, args.min_p, args.siblings)
         cpu = {"value": round(v_cpu, 2), "unit": "verified draft tokens/s", "cores": threads, "kind": "oracle",
                "sample": desc}
 
@@ -387,7 +397,8 @@ def main():
         "data": "synthetic (seeded; no dataset, no model weights)",
         "config": {"workload": cfg.name, "B": w["B"], "draft_nodes": w["N"], "max_T": w["max_T"], "L": cfg.L,
                    "Hq": cfg.Hq, "Hkv": cfg.Hkv, "D": cfg.D, "kv_dtype": cfg.dtype, "V": cfg.V,
-                   "temperature": cfg.temperature, **({"min_p": args.min_p} if args.min_p > 0 else {})},
+                   "temperature": cfg.temperature, **({"min_p": args.min_p} if args.min_p > 0 else {}),
+                   **({"siblings": "deterministic (top-k of q)"} if det else {})},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "input_sets": n_sets,

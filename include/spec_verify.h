@@ -144,6 +144,22 @@ typedef struct {
  * U(b, j, purpose) = (w0 + 0.5) * 2^-32 where w0 is word 0 of Philox4x32-10
  * (Salmon et al., SC'11) with key = (seed & 0xffffffff, seed >> 32) and
  * counter = (request_id[b], j, purpose, step).                            */
+/* Sibling rule of the sampled walk ([LOSSY] appendix G.3).
+ *   SV_SIBLINGS_SAMPLED: the children of a node are independent draws from q
+ *     at its position; the rule above (q required).
+ *   SV_SIBLINGS_DETERMINISTIC: the children are fixed candidates (say the
+ *     drafter's top-k), tried in increasing node index. Candidate i with
+ *     token x is accepted iff P_i(x) > 0 and u_c <= P_i(x), where P_i is the
+ *     target with the tokens of the candidates rejected before it removed
+ *     and renormalised (P_1 = p; a token already removed has P = 0). With no
+ *     candidate accepted, the bonus token is drawn (inverse CDF as above)
+ *     from the target without the rejected candidates. The emitted tokens
+ *     follow p (p_Theta under min_p) exactly; q is not read (draft_probs may
+ *     be NULL) and the walk needs no vocabulary pass without min_p. A
+ *     remainder below 1e-12 of the row's mass counts as zero
+ *     (SV_STATUS_ZERO_RESIDUAL, candidate kept).                            */
+typedef enum { SV_SIBLINGS_SAMPLED = 0, SV_SIBLINGS_DETERMINISTIC = 1 } sv_siblings;
+
 typedef struct {
   int32_t B, V;        /* requests (>= 0); vocabulary size (1 .. 1<<22)      */
   int32_t total_nodes; /* N = cu_nodes[B]                                     */
@@ -152,7 +168,8 @@ typedef struct {
   const int32_t* parent;       /* [N] local parent (-1 = root)             */
   const int32_t* draft_tokens; /* [N] token of each node                   */
   const float* target_logits;  /* [N+B, V] fp32 rows as described above    */
-  const float* draft_probs;    /* [N+B, V] fp32; may be NULL if temperature == 0 */
+  const float* draft_probs;    /* [N+B, V] fp32; may be NULL if temperature == 0
+                                  or the siblings are deterministic         */
   float temperature;   /* 0 = greedy; > 0 = sampled                           */
   float min_p;         /* 0 = off; in (0, 1) with temperature > 0: verify
                           against the min-p truncated target ([LOSSY] 2.3,
@@ -163,6 +180,7 @@ typedef struct {
                           applies with p_Theta in place of p. Each visited
                           position costs one more vocabulary pass (the mass
                           of A). Not with probs_out.                         */
+  int32_t siblings;    /* sv_siblings: how the children of a node were drafted */
   uint64_t seed;       /* Philox key                                          */
   uint32_t step;       /* Philox counter word 3 (replay / advance)            */
   const uint32_t* request_id; /* [B] Philox counter word 0; NULL means b    */
@@ -174,7 +192,8 @@ typedef struct {
   float* probs_out;         /* optional [N+B, V] fp32 p rows (temperature > 0 only) */
   double* uniforms_out;     /* optional [N+B]: [n] = U(b, j, 0) for packed node n = cu_nodes[b]+j,
                                [N+b] = U(b, 0, 1)                                   */
-  int32_t* residual_passes; /* optional [B]: vocabulary passes the walk made for residual masses */
+  int32_t* residual_passes; /* optional [B]: rejections during the walk (with sampled siblings, each
+                               costs one vocabulary pass for the residual mass) */
   int32_t* status;          /* optional device word for SV_STATUS_* bits           */
   void* prof_start;         /* optional hipEvent_t recorded right before the row-statistics */
   void* prof_stop;          /*   kernel / right after it (measurement)                     */

@@ -115,6 +115,11 @@ size_t attn_part_bytes(const sv_attn_args* a, const sv::AttnPlan& pl, size_t* ml
 
 int sample_nch(const sv_sample_args* s) { return (s->V + sv::kChunk - 1) / sv::kChunk; }
 
+// does the walk make vocabulary passes (residual masses, the min-p visit pass)?
+bool walk_passes(const sv_sample_args* s) {
+  return s->temperature > 0.f && (s->siblings == SV_SIBLINGS_SAMPLED || s->min_p > 0.f);
+}
+
 WsLayout layout(const sv_attn_args* a, const sv_sample_args* s) {
   WsLayout w;
   size_t off = 0;
@@ -144,7 +149,7 @@ WsLayout layout(const sv_attn_args* a, const sv_sample_args* s) {
     off += align_up(((size_t)s->total_nodes + s->B) * sample_nch(s) * sizeof(sv::ChunkStat));
     w.rowstats = off;
     off += align_up(((size_t)s->total_nodes + s->B) * sizeof(sv::RowStat));
-    if (sv::walk_slices(s->B, sample_nch(s), s->temperature == 0.f) > 1) {
+    if (sv::walk_slices(s->B, sample_nch(s), walk_passes(s)) > 1) {
       w.xs = off;
       off += align_up((size_t)s->B * 4 * sample_nch(s) * sizeof(double));
       w.xcnt = off;
@@ -168,6 +173,8 @@ sv_status check_sample(const sv_sample_args* s) {
   if (s->temperature > 0.f && !isfinite(1.4426950408889634 / (double)s->temperature) )
     return fail(SV_ERR_INVALID_ARG, "temperature too small");
   if (!(s->min_p >= 0.f && s->min_p < 1.f)) return fail(SV_ERR_INVALID_ARG, "min_p must be in [0, 1)");
+  if (s->siblings != SV_SIBLINGS_SAMPLED && s->siblings != SV_SIBLINGS_DETERMINISTIC)
+    return fail(SV_ERR_INVALID_ARG, "siblings must be SV_SIBLINGS_SAMPLED or SV_SIBLINGS_DETERMINISTIC");
   const int md_needed = eff_max_nodes(s->max_nodes);
   if (s->max_depth < md_needed)
     return fail(SV_ERR_INVALID_ARG, "max_depth (%d) must be >= max_nodes (%d)", s->max_depth, md_needed);
@@ -178,8 +185,8 @@ sv_status check_sample(const sv_sample_args* s) {
     return fail(SV_ERR_INVALID_ARG, "cu_nodes, target_logits, accept_len, accepted_nodes, out_tokens are required");
   if (s->total_nodes > 0 && (!s->parent || !s->draft_tokens))
     return fail(SV_ERR_INVALID_ARG, "parent and draft_tokens are required when total_nodes > 0");
-  if (s->temperature > 0.f && !s->draft_probs)
-    return fail(SV_ERR_INVALID_ARG, "draft_probs is required when temperature > 0");
+  if (s->temperature > 0.f && s->siblings == SV_SIBLINGS_SAMPLED && !s->draft_probs)
+    return fail(SV_ERR_INVALID_ARG, "draft_probs is required when temperature > 0 with sampled siblings");
   if (s->probs_out && s->temperature == 0.f)
     return fail(SV_ERR_INVALID_ARG, "probs_out needs temperature > 0");
   if (s->probs_out && s->min_p > 0.f)
@@ -276,7 +283,8 @@ sv_status run_sample(const sv_sample_args* s, char* ws, const WsLayout& w, hipSt
   p.status = s->status;
   p.stats = (sv::ChunkStat*)(ws + w.stats);
   p.rowstats = (sv::RowStat*)(ws + w.rowstats);
-  p.slices = w.xcnt ? sv::walk_slices(s->B, p.nch, p.greedy) : 1;
+  p.det = s->siblings == SV_SIBLINGS_DETERMINISTIC;
+  p.slices = w.xcnt ? sv::walk_slices(s->B, p.nch, walk_passes(s)) : 1;
   p.xs = w.xcnt ? (double*)(ws + w.xs) : nullptr;
   p.xcnt = w.xcnt ? (int32_t*)(ws + w.xcnt) : nullptr;
   const bool vec4 = (s->V % 4 == 0) && aligned(s->target_logits, 16) && (!s->draft_probs || aligned(s->draft_probs, 16));

@@ -69,6 +69,7 @@ struct SampleParams {
   bool greedy;
   bool trunc;               // min-p truncation of the target rows
   float theta;              // its threshold on logit - row max: fp32(T ln min_p)
+  bool det;                 // siblings are deterministic candidates (q unused)
   uint64_t seed;
   uint32_t step;
   const uint32_t* request_id;
@@ -95,8 +96,9 @@ constexpr int kWalkSync = 4;
 int device_cus();
 
 // workgroups per request for the walk: several (256 threads each) when the
-// batch leaves at least four workgroup slots per request, else 1
-int walk_slices(int B, int nch, bool greedy);
+// walk makes vocabulary passes (passes) and the batch leaves at least four
+// workgroup slots per request, else 1
+int walk_slices(int B, int nch, bool passes);
 
 hipError_t launch_sampler(const SampleParams& p, bool vec4, hipStream_t stream, hipEvent_t ev_start,
                           hipEvent_t ev_stop);

@@ -182,6 +182,7 @@ struct WalkShared {
   double u[kMaxNodes];
   float lgx[kMaxNodes];       // target logit of node j's token at its parent's row
   float qx[kMaxNodes];        // draft probability of node j's token at its parent's row
+  double wx[kMaxNodes];       // deterministic siblings: unnormalised target mass of node j's token
   RowStat rs[kMaxNodes + 1];  // the request's rows: r = 0 root, r = 1 + j after node j
   double csum[kMaxChunks];    // chunk masses of the distribution being drawn from
   double hsum[2 * kMaxChunks];// half-chunk masses of a residual pass
@@ -223,8 +224,9 @@ __device__ __forceinline__ void half_load(HalfRegs& r, __amdgpu_buffer_rsrc_t lr
 }
 
 // Unnormalised mass S * sum max(0, p - cc q) of the half-chunk in r: the four
-// tokens of a float4 are added in fp32, the rest in fp64. MASK drops float4s
-// past the row's end (only the row's last half-chunk needs it).
+// tokens of a float4 are added in fp32 (in fp64 under truncation), the rest in
+// fp64. MASK drops float4s past the row's end (only the row's last half-chunk
+// needs it).
 template <bool MASK, bool TR>
 __device__ __forceinline__ double half_reduce(const HalfRegs& r, int V, int h, int lane, float lmax, float c,
                                               float ccS, float theta) {
@@ -233,12 +235,21 @@ __device__ __forceinline__ double half_reduce(const HalfRegs& r, int V, int h, i
   double acc = 0.0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    float t = (allowed<TR>(residual_weight(r.l[i].x, r.q[i].x, lmax, c, ccS), r.l[i].x, lmax, theta) +
-               allowed<TR>(residual_weight(r.l[i].y, r.q[i].y, lmax, c, ccS), r.l[i].y, lmax, theta)) +
-              (allowed<TR>(residual_weight(r.l[i].z, r.q[i].z, lmax, c, ccS), r.l[i].z, lmax, theta) +
-               allowed<TR>(residual_weight(r.l[i].w, r.q[i].w, lmax, c, ccS), r.l[i].w, lmax, theta));
-    if (MASK) t = b4 + 64 * i < n4 ? t : 0.f;
-    acc += (double)t;
+    const float w0 = allowed<TR>(residual_weight(r.l[i].x, r.q[i].x, lmax, c, ccS), r.l[i].x, lmax, theta);
+    const float w1 = allowed<TR>(residual_weight(r.l[i].y, r.q[i].y, lmax, c, ccS), r.l[i].y, lmax, theta);
+    const float w2 = allowed<TR>(residual_weight(r.l[i].z, r.q[i].z, lmax, c, ccS), r.l[i].z, lmax, theta);
+    const float w3 = allowed<TR>(residual_weight(r.l[i].w, r.q[i].w, lmax, c, ccS), r.l[i].w, lmax, theta);
+    if (TR) {
+      // every token in fp64: a deterministic candidate's weight can then be
+      // taken back out of these sums with no fp32 rounding left behind
+      double t = ((double)w0 + (double)w1) + ((double)w2 + (double)w3);
+      if (MASK) t = b4 + 64 * i < n4 ? t : 0.0;
+      acc += t;
+    } else {
+      float t = (w0 + w1) + (w2 + w3);
+      if (MASK) t = b4 + 64 * i < n4 ? t : 0.f;
+      acc += (double)t;
+    }
   }
   return wave_sum(acc);
 }
@@ -260,7 +271,7 @@ __device__ __forceinline__ double half_scalar(const float* lrow, const float* qr
   for (int i = 0; i < 32; ++i) {
     const int idx = begin + lane + 64 * i;
     lv[i] = idx < end ? lrow[idx] : -INFINITY;
-    qv[i] = idx < end ? qrow[idx] : 0.f;
+    qv[i] = (idx < end && ccS != 0.f) ? qrow[idx] : 0.f;  // cc = 0: p itself, q not needed
   }
   double acc = 0.0;
 #pragma unroll
@@ -367,10 +378,12 @@ __device__ __forceinline__ double residual_pass(WalkShared<NT>& sh, const float*
 // within each wave, the wave totals are added in wave order, and the first
 // lane whose inclusive prefix crosses the remainder picks the token among its
 // DPL.
+// removed: nodes whose tokens are out of the distribution (deterministic
+// siblings already tried); their weights count as zero.
 template <bool VEC, int NT, bool TR>
 __device__ __forceinline__ int draw_token(WalkShared<NT>& sh, const float* lrow, const float* qrow, int V, int nch,
                                           int level, float lmax, float c, float theta, double S, double cc, double u,
-                                          double total) {
+                                          double total, uint64_t removed) {
   constexpr int NW = NT / kWave;
   constexpr int kDrawPerLane = kChunk / NT;
   static_assert(kDrawPerLane % 4 == 0, "the draw gives each lane whole float4 of a chunk");
@@ -420,14 +433,26 @@ __device__ __forceinline__ int draw_token(WalkShared<NT>& sh, const float* lrow,
     }
   }
   double w[kDrawPerLane];
-  double seg = 0.0;
-  int lastpos = -1;
 #pragma unroll
   for (int i = 0; i < kDrawPerLane; ++i) {
     // weights of the distribution being drawn from (level 0: unnormalised p;
     // above: max(0, p - cc q) as the residual passes compute it)
     w[i] = level == 0 ? (double)allowed<TR>(target_weight(lv[i], lmax, c), lv[i], lmax, theta)
                       : (double)allowed<TR>(residual_weight(lv[i], qv[i], lmax, c, ccS), lv[i], lmax, theta) * invS;
+  }
+  if (removed) {  // the same in every thread
+    uint32_t m = 0;
+    for (uint64_t e = removed; e; e &= e - 1) {
+      const int d = sh.tok[__ffsll((unsigned long long)e) - 1] - x0;
+      if (d >= 0 && d < kDrawPerLane) m |= 1u << d;
+    }
+#pragma unroll
+    for (int i = 0; i < kDrawPerLane; ++i) w[i] = ((m >> i) & 1u) ? 0.0 : w[i];
+  }
+  double seg = 0.0;
+  int lastpos = -1;
+#pragma unroll
+  for (int i = 0; i < kDrawPerLane; ++i) {
     seg += w[i];
     lastpos = w[i] > 0.0 ? x0 + i : lastpos;
   }
@@ -547,8 +572,26 @@ __global__ __launch_bounds__(NT) void walk_kernel(SampleParams p) {
   // the normalisation of every row of the request
   if (tid < T) {
     const int64_t r = row0 + sh.par[tid] + 1;
-    sh.lgx[tid] = p.logits[r * V + sh.tok[tid]];
-    sh.qx[tid] = p.greedy ? 0.f : p.q[r * V + sh.tok[tid]];
+    const float lx = p.logits[r * V + sh.tok[tid]];
+    sh.lgx[tid] = lx;
+    sh.qx[tid] = (p.greedy || p.det) ? 0.f : p.q[r * V + sh.tok[tid]];
+    if (p.det && !p.greedy) {
+      // the token's unnormalised target mass, in the same terms as the sum it
+      // will be taken out of: under truncation the visit pass's fp32 weight
+      // relative to the row maximum; otherwise the row statistics' weight
+      // relative to its chunk's maximum, scaled as row_norm scales chunk sums
+      const RowStat rs = p.rowstats[r];
+      double wx;
+      if (TR) {
+        wx = (double)allowed<TR>(target_weight(lx, rs.lmax, p.c), lx, rs.lmax, p.theta);
+      } else {
+        const ChunkStat cs = p.stats[r * p.nch + sh.tok[tid] / kChunk];
+        wx = cs.lmax == -INFINITY ? 0.0
+                                  : (double)target_weight(lx, cs.lmax, p.c) *
+                                        exp2((double)(cs.lmax - rs.lmax) * (double)p.c);
+      }
+      sh.wx[tid] = wx;
+    }
   }
   if (tid <= T) sh.rs[tid] = p.rowstats[row0 + tid];
   // the mode: sliced, or this slice alone, or another slice alone (leave)
@@ -597,7 +640,7 @@ __global__ __launch_bounds__(NT) void walk_kernel(SampleParams p) {
     const int r = pos + 1;
     const int64_t row = row0 + r;
     const float* lrow = p.logits + row * V;
-    const float* qrow = p.greedy ? nullptr : p.q + row * V;
+    const float* qrow = (p.greedy || !p.q) ? nullptr : p.q + row * V;
     const RowStat st = sh.rs[r];
     // children of pos in increasing index: the same ballot in every wave
     const uint64_t kids = __ballot(lane < T && sh.par[lane] == pos);
@@ -629,6 +672,71 @@ __global__ __launch_bounds__(NT) void walk_kernel(SampleParams p) {
       Srow = residual_pass<VEC, NT, TR>(sh, lrow, qrow, p.V, p.nch, st.lmax, p.c, p.theta, 1.0, 0.0, sl, ++npass);
       csum_ok = true;
     }
+    if (p.det) {
+      // Deterministic candidates ([LOSSY] G.3): child i is accepted with
+      // probability p~_i(x) = W(x) / M_i, M_i being the target's mass left
+      // after the candidates rejected before it were taken out; a token
+      // already taken out has p~ = 0. No vocabulary pass: W comes from the
+      // gathers and M from the row's sum (under truncation, from this
+      // position's pass). A remainder below 1e-12 of the row's mass is
+      // rounding noise and counts as zero.
+      double M = Srow;
+      uint64_t removed = 0;  // children whose token is out of the target
+      int accepted = -1;
+      for (uint64_t k = kids; k; k &= k - 1) {
+        const int ch = __ffsll((unsigned long long)k) - 1;
+        const int x = sh.tok[ch];
+        bool dup = false;
+        for (uint64_t m = removed; m; m &= m - 1) dup |= sh.tok[__ffsll((unsigned long long)m) - 1] == x;
+        const double W = sh.wx[ch];
+        const double P = dup ? 0.0 : W / M;
+        const int ok = __builtin_amdgcn_readfirstlane((P > 0.0 && sh.u[ch] <= P) ? 1 : 0);
+        if (ok) { accepted = ch; break; }
+        ++passes;
+        if (!dup) {
+          const double Mn = M - W;
+          if (__builtin_amdgcn_readfirstlane(Mn > 1e-12 * Srow ? 1 : 0)) {
+            M = Mn;
+            removed |= 1ull << ch;
+          } else if (lead && tid == 0) {
+            flag(p.status, kStZeroResidual);
+          }
+        }
+      }
+      if (accepted >= 0) {
+        if (lead && tid == 0) { acc_nodes[depth] = accepted; toks_out[depth] = sh.tok[accepted]; }
+        ++depth;
+        pos = accepted;
+        continue;
+      }
+      if (!lead) return;  // the draw needs no other slice
+      // draw from the target without the removed candidates: chunk masses
+      // (from the row statistics, or this position's pass under truncation)
+      // minus the removed weights
+      if (!TR) {
+        const ChunkStat* cs = p.stats + row * p.nch;
+        for (int ch = tid; ch < p.nch; ch += NT) {
+          const ChunkStat s = cs[ch];
+          sh.csum[ch] = s.lmax == -INFINITY ? 0.0 : s.s * exp2((double)(s.lmax - st.lmax) * (double)p.c);
+        }
+        __syncthreads();
+      }
+      if (removed) {
+        if (tid == 0) {
+          for (uint64_t m = removed; m; m &= m - 1) {
+            const int j = __ffsll((unsigned long long)m) - 1;
+            const int ch = sh.tok[j] / kChunk;
+            const double before = sh.csum[ch], after = before - sh.wx[j];
+            sh.csum[ch] = after > 1e-12 * before ? after : 0.0;
+          }
+        }
+        __syncthreads();
+      }
+      const double uf = uniform01(p.seed, rid, 0u, 1u, p.step);
+      bonus = draw_token<VEC, NT, TR>(sh, lrow, qrow, p.V, p.nch, 0, st.lmax, p.c, p.theta, Srow, 0.0, uf, M, removed);
+      break;
+    }
+
     const float invS = (float)(1.0 / Srow);
     double cc = 0.0, M = 1.0;  // current distribution max(0, p - cc q) / M (cc = 0: p itself)
     int level = 0;
@@ -682,7 +790,7 @@ __global__ __launch_bounds__(NT) void walk_kernel(SampleParams p) {
     }
     if (!lead) return;  // the draw needs no other slice: the rest are done
     const double uf = uniform01(p.seed, rid, 0u, 1u, p.step);
-    bonus = draw_token<VEC, NT, TR>(sh, lrow, qrow, p.V, p.nch, level, st.lmax, p.c, p.theta, Srow, cc, uf, total);
+    bonus = draw_token<VEC, NT, TR>(sh, lrow, qrow, p.V, p.nch, level, st.lmax, p.c, p.theta, Srow, cc, uf, total, 0);
     break;
   }
   if (lead && tid == 0) {
@@ -759,8 +867,8 @@ int device_cus() {
   return cached[dev];
 }
 
-int walk_slices(int B, int nch, bool greedy) {
-  if (greedy || B <= 0) return 1;
+int walk_slices(int B, int nch, bool passes) {
+  if (!passes || B <= 0) return 1;
   // SV_WALK_MODE=single forces one workgroup per request (tests)
   const char* mode = getenv("SV_WALK_MODE");
   if (mode && !strcmp(mode, "single")) return 1;

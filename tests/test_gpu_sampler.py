@@ -332,3 +332,80 @@ def test_gpu_min_p_chi_square(min_p):
     a0 = float(np.minimum(pt, q[0]).sum())
     freq = (acc >= 1).mean()
     assert abs(freq - a0) < 5 * math.sqrt(a0 * (1 - a0) / n)
+
+
+# ---- deterministic-candidate siblings ([LOSSY] G.3) ----------------------------
+DET_SMALL = ["c1_full", "c2_small", "c3_small", "c5_small_odd_vocab", "c4_small_cold", "vocab_one", "max_tree_64"]
+
+
+def _det_pair(w, T, min_p):
+    """GPU (no q passed: it must not be read) and oracle under the deterministic rule."""
+    r = sv.sample(w["cu_nodes_t"], w["parent_t"], w["draft_tokens"], w["logits"], None, temperature=T,
+                  seed=w["seed"], max_nodes=w["max_T"], uniforms_out=True, residual_passes=True, min_p=min_p,
+                  siblings="deterministic")
+    torch.cuda.synchronize()
+    ref = oracle.verify(w["cu_nodes"], w["parent"], w["draft_tokens"].cpu().numpy(), w["logits"].cpu().numpy(), None,
+                        temperature=T, seed=w["seed"], max_depth=r["accepted_nodes"].shape[1], min_p=min_p,
+                        siblings="deterministic")
+    return r, ref
+
+
+@pytest.mark.parametrize("candidates", ["topk", "sampled"])  # sampled draws can repeat a sibling's token
+@pytest.mark.parametrize("min_p", [0.0, 0.2])
+@pytest.mark.parametrize("name", DET_SMALL)
+def test_sampler_deterministic_small(name, min_p, candidates):
+    cfg = SMALL[name]
+    w = generate(cfg, "cuda", attn=False, candidates=candidates)
+    print(f"[det] {name} min_p={min_p} {candidates} B={w['B']} N={w['N']} V={cfg.V}", flush=True)
+    r, ref = _det_pair(w, cfg.temperature, min_p)
+    assert int(r["status"].item()) == 0, sv.status_names(int(r["status"].item()))
+    assert np.array_equal(r["uniforms"].cpu().numpy(), ref["uniforms"])
+    flagged = compare_walk(r, ref, w["B"], greedy=False)
+    print(f"  flagged near-ties: {flagged}/{w['B']}")
+    ok = ref["flag_depth"] < 0
+    assert np.array_equal(r["residual_passes"].cpu().numpy()[ok], ref["n_rejections"][ok])
+    if min_p > 0:
+        _assert_in_allowed_set(w, r, cfg.temperature, min_p)
+
+
+@pytest.mark.parametrize("min_p", [0.0, 0.1])
+@pytest.mark.parametrize("name", ["c2_llama8b_chain", "c3_eagle_tree", "c5_super_tree"])
+def test_sampler_deterministic_full_size(name, min_p):
+    cfg = get_config(name)
+    w = generate(cfg, "cuda", attn=False, candidates="topk")
+    print(f"[det-full] {name} min_p={min_p} B={w['B']} N={w['N']} V={cfg.V}", flush=True)
+    r, ref = _det_pair(w, cfg.temperature, min_p)
+    assert int(r["status"].item()) == 0, sv.status_names(int(r["status"].item()))
+    flagged = compare_walk(r, ref, w["B"], greedy=False)
+    print(f"  flagged near-ties: {flagged}/{w['B']}; mean accept_len {r['accept_len'].float().mean().item():.3f}")
+
+
+@pytest.mark.parametrize("min_p", [0.0, 0.2])
+def test_gpu_deterministic_chi_square(min_p):
+    """Fixed candidates (the top two, then the top one again): the emitted
+    first token follows p (p_Theta), candidate i is accepted with probability
+    p(x^(i)), and the repeated token is never accepted ([LOSSY] G.3)."""
+    rng = np.random.default_rng(401 if min_p == 0 else 402)
+    V, n, T = 8, 1_000_000, 1.0
+    lg, _ = rows_from_probs(rng, V, 4, sharp=1.0)
+    p = softmax64(lg[0], T)
+    keep = p >= min_p * p.max() if min_p > 0 else np.ones(V, bool)
+    pt = np.where(keep, p, 0.0) / p[keep].sum()
+    order = np.argsort(-pt, kind="stable")
+    tokens = np.array([order[0], order[1], order[0]], np.int32)
+    parent = np.array([-1, -1, -1], np.int32)
+    cu = (np.arange(n + 1) * 3).astype(np.int32)
+    r = sv.sample(torch.from_numpy(cu).cuda(), torch.from_numpy(np.tile(parent, n)).cuda(),
+                  torch.from_numpy(np.tile(tokens, n)).cuda(), torch.from_numpy(np.tile(lg, (n, 1))).cuda(), None,
+                  temperature=T, seed=4545, max_nodes=3, min_p=min_p, siblings="deterministic")
+    torch.cuda.synchronize()
+    first = r["out_tokens"][:, 0].cpu().numpy()
+    counts = np.bincount(first, minlength=V)
+    assert counts[~keep].sum() == 0
+    assert stats.chisquare(counts[keep], pt[keep] * n).pvalue > 1e-3
+    acc = r["accept_len"].cpu().numpy()
+    node = np.where(acc > 0, r["accepted_nodes"][:, 0].cpu().numpy(), -1)
+    assert not (node == 2).any()
+    for i in range(2):
+        a = pt[tokens[i]]
+        assert abs((node == i).mean() - a) < 5 * math.sqrt(a * (1 - a) / n)

@@ -13,7 +13,9 @@ Recipe (also listed in the design notes):
       draft logits = target + N(0, draft_sigma^2); q = softmax(draft / temperature)
         computed in fp64 and stored as fp32 (the drafter's own distribution);
       draft token of node j ~ Categorical(q at its parent's row) (torch.multinomial),
-        siblings being independent draws.
+        siblings being independent draws; or, with candidates="topk", the r-th most
+        likely token of q at its parent's row, r being j's rank among its siblings
+        in node order (deterministic candidates, as an EAGLE-style drafter's top-k).
   * every request has ctx_len = L; the cache holds Lcap = L + max(T_b) slots per head.
 """
 from __future__ import annotations
@@ -108,8 +110,20 @@ def poison_unused_slots(k_cache: torch.Tensor, v_cache: torch.Tensor, ctx_len, c
         v_cache[b, :, used:, :] = float("nan")
 
 
+def sibling_ranks(cu: np.ndarray, parent: np.ndarray) -> np.ndarray:
+    """Rank of every packed node among the children of its parent (node order)."""
+    rank = np.zeros(parent.size, np.int64)
+    for b in range(cu.size - 1):
+        seen = {}
+        for j in range(int(cu[b + 1] - cu[b])):
+            pj = int(parent[cu[b] + j])
+            rank[cu[b] + j] = seen.get(pj, 0)
+            seen[pj] = rank[cu[b] + j] + 1
+    return rank
+
+
 def generate(cfg: WorkloadConfig, device="cpu", *, attn: bool = True, sample: bool = True,
-             poison: bool = False, row_chunk: int = 128) -> dict:
+             poison: bool = False, row_chunk: int = 128, candidates: str = "sampled") -> dict:
     """Seeded inputs of one verification step for `cfg` on `device`.
 
     Returns a dict with host-side structure (numpy: cu_nodes, parent, ctx_len,
@@ -157,9 +171,17 @@ def generate(cfg: WorkloadConfig, device="cpu", *, attn: bool = True, sample: bo
         prow = (cu[:-1][req] + req + parent + 1).astype(np.int64) if N > 0 else np.zeros(0, np.int64)
         prow_t = torch.from_numpy(prow).to(device)
         toks = torch.empty(N, device=device, dtype=torch.int64)
-        for s in range(0, N, row_chunk):
-            e = min(N, s + row_chunk)
-            toks[s:e] = torch.multinomial(probs[prow_t[s:e]], 1, generator=g).squeeze(1)
+        if candidates == "topk":
+            rank_t = torch.from_numpy(sibling_ranks(cu, parent)).to(device)
+            k = min(cfg.V, int(rank_t.max().item()) + 1) if N > 0 else 1
+            for s in range(0, N, row_chunk):
+                e = min(N, s + row_chunk)
+                top = torch.topk(probs[prow_t[s:e]], k, dim=1).indices
+                toks[s:e] = top.gather(1, rank_t[s:e].clamp(max=k - 1).unsqueeze(1)).squeeze(1)
+        else:
+            for s in range(0, N, row_chunk):
+                e = min(N, s + row_chunk)
+                toks[s:e] = torch.multinomial(probs[prow_t[s:e]], 1, generator=g).squeeze(1)
         out["logits"] = logits
         out["draft_probs"] = probs
         out["draft_tokens"] = toks.to(torch.int32)
