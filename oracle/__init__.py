@@ -25,6 +25,8 @@ Functions and the passages they follow:
                            against p_Theta ("truncation sampling + SD", G.2/G.3).
   verify(siblings=...)     "deterministic": the G.3 rule for deterministic
                            candidates (p~_i, candidates removed one by one).
+  verify(rule=...)         [LOSSY] 3.1 lossy accept tests: lenience (A.3) and
+                           interpolation / CoS (A.1).
 """
 from __future__ import annotations
 
@@ -40,6 +42,7 @@ _lib = None
 
 ACCEPT_TOL = 1e-5  # |u - P/Q| below this marks an accept test as a near-tie
 CDF_TOL = 1e-6     # a CDF boundary this close to u marks the final draw as a near-tie
+RULES = {"lossless": 0, "lenience": 1, "interpolation": 2}
 
 
 def build(verbose: bool = False) -> str:
@@ -74,7 +77,8 @@ def _load():
     lib.orc_residual.restype = f64
     lib.orc_inverse_cdf.argtypes = [i32, P, f64, P]
     lib.orc_inverse_cdf.restype = i32
-    lib.orc_verify.argtypes = [i32, i32, P, P, P, P, P, f64, i32, ctypes.c_float, i32, u64, u32, P, i32, P, P, P, P,
+    lib.orc_verify.argtypes = [i32, i32, P, P, P, P, P, f64, i32, ctypes.c_float, i32, i32, f64, u64, u32, P, i32,
+                               P, P, P, P,
                                P, P, P, P, P, P, f64, f64, i32]
     lib.orc_verify.restype = i32
     lib.orc_target_rows.argtypes = [i32, P, f64, i64, P, P]
@@ -231,7 +235,7 @@ def truncate_min_p(logits_row, p_row, theta: float) -> np.ndarray:
 
 def verify(cu_nodes, parent, tokens, logits, q, *, temperature, seed, step=0, request_id=None,
            max_depth=None, accept_tol=ACCEPT_TOL, cdf_tol=CDF_TOL, nthreads=None, min_p=0.0,
-           siblings="sampled") -> dict:
+           siblings="sampled", rule="lossless", rule_param=1.0) -> dict:
     """The verification walk for a packed batch; returns a dict of numpy arrays.
 
     logits, q: float32 [N+B, V] (q may be None when temperature == 0 or the
@@ -241,7 +245,12 @@ def verify(cu_nodes, parent, tokens, logits, q, *, temperature, seed, step=0, re
     candidates ([LOSSY] G.3): candidate i is accepted with probability
     p~_i(x^(i)), the target with the candidates tried before it removed and
     renormalised; q is not used.
+    rule="lenience" (rule_param = l) or "interpolation" (rule_param = lambda),
+    both in (0, 1]: the lossy accept tests of [LOSSY] 3.1 (h = min(1, p/(l q))
+    and h = min(1, (lambda p + (1 - lambda) q)/q)), residuals unchanged.
     """
+    if rule not in RULES:
+        raise ValueError(f"rule must be one of {sorted(RULES)}")
     if siblings not in ("sampled", "deterministic"):
         raise ValueError("siblings must be 'sampled' or 'deterministic'")
     det = 1 if siblings == "deterministic" else 0
@@ -274,7 +283,7 @@ def verify(cu_nodes, parent, tokens, logits, q, *, temperature, seed, step=0, re
     theta = min_p_theta(temperature, min_p)
     trunc = 1 if theta > float("-inf") else 0
     rc = _load().orc_verify(B, V, _ptr(cu), _ptr(par), _ptr(tok), _ptr(lg), _ptr(qq), float(temperature),
-                            trunc, ctypes.c_float(theta), det, int(seed), int(step), _ptr(rid), int(max_depth), _ptr(out["accept_len"]),
+                            trunc, ctypes.c_float(theta), det, RULES[rule], float(np.float32(rule_param)), int(seed), int(step), _ptr(rid), int(max_depth), _ptr(out["accept_len"]),
                             _ptr(out["accepted_nodes"]), _ptr(out["out_tokens"]), _ptr(out["uniforms"]),
                             _ptr(out["flag_depth"]), _ptr(out["flag_kind"]), _ptr(out["n_rejections"]),
                             _ptr(out["status"]), _ptr(out["min_accept_margin"]), _ptr(out["cdf_margin"]),

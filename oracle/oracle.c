@@ -360,6 +360,8 @@ typedef struct {
   int trunc;     /* min-p truncation of every target row */
   float theta;   /* its threshold on l_x - l_max         */
   int det;       /* siblings are deterministic candidates (q unused) */
+  int rule;      /* accept rule: 0 lossless, 1 lenience, 2 interpolation */
+  double rule_param; /* lenience l or interpolation lambda, in (0, 1]    */
   uint64_t seed;
   uint32_t step;
   const uint32_t* request_id;
@@ -464,9 +466,17 @@ static void orc_walk_one(void* vctx, int64_t bi) {
         continue;
       }
       /* [SD] acceptance rule r <= min(1, p/q), written as u*q <= p with p > 0
-       * so that q(x) = 0 follows the formula (ratio +inf, accepted).      */
-      int ok = P[x] > 0.0 && u * Q[x] <= P[x];
-      double ratio = Q[x] > 0.0 ? P[x] / Q[x] : (P[x] > 0.0 ? INFINITY : 0.0);
+       * so that q(x) = 0 follows the formula (ratio +inf, accepted). The
+       * lossy rules of [LOSSY] 3.1 change only this test: lenience
+       * h = min(1, p/(l q)) compares u*(l q) with p; interpolation (CoS)
+       * h = min(1, nu/q) with nu = lambda p + (1 - lambda) q compares u*q
+       * with nu. Both keep the residual max(0, P - q) of a rejection (A.3;
+       * A.1's r(x) is the same distribution).                              */
+      double num = P[x], den = Q[x];
+      if (c->rule == 1) den = c->rule_param * Q[x];
+      if (c->rule == 2) num = c->rule_param * P[x] + (1.0 - c->rule_param) * Q[x];
+      int ok = num > 0.0 && u * den <= num;
+      double ratio = den > 0.0 ? num / den : (num > 0.0 ? INFINITY : 0.0);
       double margin = fabs(u - ratio);
       if (margin < c->min_accept_margin[b]) c->min_accept_margin[b] = margin;
       if (margin < c->accept_tol && c->flag_depth[b] < 0) { c->flag_depth[b] = d; c->flag_kind[b] = 0; }
@@ -507,7 +517,9 @@ static void orc_walk_one(void* vctx, int64_t bi) {
  * T == 0 selects greedy verification; trunc != 0 verifies against the
  * min-p truncated target (threshold theta, see orc_truncate_min_p); det != 0
  * treats the siblings as deterministic candidates ([LOSSY] G.3; q unused and
- * may be NULL; a rejection takes the candidate out of the target). Per
+ * may be NULL; a rejection takes the candidate out of the target); rule 1/2
+ * selects the lossy lenience / interpolation accept test ([LOSSY] 3.1, A.1,
+ * A.3) with rule_param = l / lambda in (0, 1] (not with det). Per
  * request it also reports
  *   flag_depth: accepted nodes before the first decision closer than the
  *               tolerance to its threshold (-1: none), flag_kind 0 = accept
@@ -518,15 +530,17 @@ static void orc_walk_one(void* vctx, int64_t bi) {
  *   min_accept_margin, cdf_margin: the smallest |u - P/Q| seen and the
  *           margin of the final draw.                                     */
 int orc_verify(int B, int V, const int32_t* cu_nodes, const int32_t* parent, const int32_t* tokens,
-               const float* logits, const float* q, double T, int trunc, float theta, int det,
-               uint64_t seed, uint32_t step,
+               const float* logits, const float* q, double T, int trunc, float theta, int det, int rule,
+               double rule_param, uint64_t seed, uint32_t step,
                const uint32_t* request_id, int max_depth, int32_t* accept_len, int32_t* accepted_nodes,
                int32_t* out_tokens, double* uniforms_out, int32_t* flag_depth, int32_t* flag_kind,
                int32_t* n_rejections, int32_t* status, double* min_accept_margin, double* cdf_margin,
                double accept_tol, double cdf_tol, int nthreads) {
   if (B < 0 || V < 1 || max_depth < 0 || T < 0.0) return 1;
   if (T > 0.0 && !det && !q) return 1;
-  orc_walk_ctx c = {B, V, cu_nodes, parent, tokens, logits, q, T, trunc, theta, det, seed, step, request_id, max_depth,
+  if (rule < 0 || rule > 2 || (rule && !(rule_param > 0.0 && rule_param <= 1.0)) || (rule && det)) return 1;
+  orc_walk_ctx c = {B, V, cu_nodes, parent, tokens, logits, q, T, trunc, theta, det, rule, rule_param, seed, step,
+                    request_id, max_depth,
                     accept_len, accepted_nodes, out_tokens, uniforms_out, flag_depth, flag_kind,
                     n_rejections, status, min_accept_margin, cdf_margin, accept_tol, cdf_tol};
   orc_parallel_for(B, nthreads, orc_walk_one, &c);
