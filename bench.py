@@ -111,6 +111,9 @@ def parse_args():
     ap.add_argument("--no-events", action="store_true", help="time without the per-kernel HIP events")
     ap.add_argument("--min-p", type=float, default=0.0,
                     help="verify against the min-p truncated target (0 = plain lossless verification)")
+    ap.add_argument("--rule", choices=["lossless", "lenience", "interpolation"], default="lossless",
+                    help="accept test (lenience and interpolation are lossy, [LOSSY] 3.1)")
+    ap.add_argument("--rule-param", type=float, default=1.0, help="l or lambda of --rule, in (0, 1]")
     ap.add_argument("--siblings", choices=["sampled", "deterministic"], default="sampled",
                     help="sampled: draft tokens are draws from q; deterministic: the top-k of q as fixed "
                          "candidates, verified by the deterministic-candidate rule (q is not read)")
@@ -213,7 +216,8 @@ def row_stats_bytes(w) -> float:
     return float(rows * w["V"] * 4 + rows * nch * 16)
 
 
-def cpu_baseline(w, budget_s: float, min_p: float = 0.0, siblings: str = "sampled"):
+def cpu_baseline(w, budget_s: float, min_p: float = 0.0, siblings: str = "sampled", rule: str = "lossless",
+                 rule_param: float = 1.0):
     """The fp64 oracle (attention of every (node, head) of a request, then the
     verification walk) over whole requests in order until the budget is spent.
     Returns verified draft tokens/s of that sample, the thread count and a
@@ -251,7 +255,7 @@ def cpu_baseline(w, budget_s: float, min_p: float = 0.0, siblings: str = "sample
                          nthreads=threads)
         oracle.verify(sub_cu, par[n0:n1], toks, lg, qq, temperature=w["temperature"], seed=w["seed"],
                       request_id=np.arange(b0, b1, dtype=np.uint32), nthreads=threads, min_p=min_p,
-                      siblings=siblings)
+                      siblings=siblings, rule=rule, rule_param=rule_param)
         spent += time.perf_counter() - t0
         nodes_done += n1 - n0
         req_done = b1
@@ -302,7 +306,7 @@ def main():
             s = sv.SampleCall(a.keep["cu"], x["parent_t"], x["draft_tokens"], x["logits"],
                               None if det else x["draft_probs"], temperature=cfg.temperature, seed=x["seed"],
                               max_nodes=x["max_T"], residual_passes=True, min_p=args.min_p,
-                              siblings=args.siblings)
+                              siblings=args.siblings, rule=args.rule, rule_param=args.rule_param)
             calls.append((a, s, sv.StepCall(a, s)))
     torch.cuda.synchronize()
 
@@ -377,7 +381,7 @@ def main():
 
     cpu = None
     if args.cpu_seconds > 0:
-        v_cpu, threads, desc = cpu_baseline(w, args.cpu_seconds, args.min_p, args.siblings)
+        v_cpu, threads, desc = cpu_baseline(w, args.cpu_seconds, args.min_p, args.siblings, args.rule, args.rule_param)
         cpu = {"value": round(v_cpu, 2), "unit": "verified draft tokens/s", "cores": threads, "kind": "oracle",
                "sample": desc}
 
@@ -398,7 +402,8 @@ def main():
         "config": {"workload": cfg.name, "B": w["B"], "draft_nodes": w["N"], "max_T": w["max_T"], "L": cfg.L,
                    "Hq": cfg.Hq, "Hkv": cfg.Hkv, "D": cfg.D, "kv_dtype": cfg.dtype, "V": cfg.V,
                    "temperature": cfg.temperature, **({"min_p": args.min_p} if args.min_p > 0 else {}),
-                   **({"siblings": "deterministic (top-k of q)"} if det else {})},
+                   **({"siblings": "deterministic (top-k of q)"} if det else {}),
+                   **({"rule": args.rule, "rule_param": args.rule_param} if args.rule != "lossless" else {})},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "input_sets": n_sets,

@@ -160,6 +160,18 @@ typedef struct {
  *     (SV_STATUS_ZERO_RESIDUAL, candidate kept).                            */
 typedef enum { SV_SIBLINGS_SAMPLED = 0, SV_SIBLINGS_DETERMINISTIC = 1 } sv_siblings;
 
+/* Accept test of the sampled walk with sampled siblings ([LOSSY] section 3.1,
+ * collaborative verification; these change the emitted distribution).
+ *   SV_RULE_LOSSLESS: u * Q(x) <= P(x), the rule above.
+ *   SV_RULE_LENIENCE: u * (l Q(x)) <= P(x), h = min(1, P/(l Q)) with
+ *     l = rule_param in (0, 1] (appendix A.3).
+ *   SV_RULE_INTERPOLATION: u * Q(x) <= nu(x), nu = lambda P + (1 - lambda) Q,
+ *     h = min(1, nu/Q) with lambda = rule_param in (0, 1] (CoS; appendix A.1).
+ * Every other step is the lossless one: a rejection moves P to the residual
+ * max(0, P - Q) normalised (the residual both appendices give), and the bonus
+ * token is drawn from P. Products and sums are in fp64 from the fp32 rule_param. */
+typedef enum { SV_RULE_LOSSLESS = 0, SV_RULE_LENIENCE = 1, SV_RULE_INTERPOLATION = 2 } sv_rule;
+
 typedef struct {
   int32_t B, V;        /* requests (>= 0); vocabulary size (1 .. 1<<22)      */
   int32_t total_nodes; /* N = cu_nodes[B]                                     */
@@ -181,6 +193,8 @@ typedef struct {
                           position costs one more vocabulary pass (the mass
                           of A). Not with probs_out.                         */
   int32_t siblings;    /* sv_siblings: how the children of a node were drafted */
+  int32_t rule;        /* sv_rule (SV_RULE_LOSSLESS unless sampled siblings)   */
+  float rule_param;    /* l or lambda of the rule, in (0, 1]; unused when lossless */
   uint64_t seed;       /* Philox key                                          */
   uint32_t step;       /* Philox counter word 3 (replay / advance)            */
   const uint32_t* request_id; /* [B] Philox counter word 0; NULL means b    */

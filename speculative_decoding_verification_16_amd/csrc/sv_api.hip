@@ -175,6 +175,12 @@ sv_status check_sample(const sv_sample_args* s) {
   if (!(s->min_p >= 0.f && s->min_p < 1.f)) return fail(SV_ERR_INVALID_ARG, "min_p must be in [0, 1)");
   if (s->siblings != SV_SIBLINGS_SAMPLED && s->siblings != SV_SIBLINGS_DETERMINISTIC)
     return fail(SV_ERR_INVALID_ARG, "siblings must be SV_SIBLINGS_SAMPLED or SV_SIBLINGS_DETERMINISTIC");
+  if (s->rule != SV_RULE_LOSSLESS && s->rule != SV_RULE_LENIENCE && s->rule != SV_RULE_INTERPOLATION)
+    return fail(SV_ERR_INVALID_ARG, "rule must be SV_RULE_LOSSLESS, SV_RULE_LENIENCE or SV_RULE_INTERPOLATION");
+  if (s->rule != SV_RULE_LOSSLESS && !(s->rule_param > 0.f && s->rule_param <= 1.f))
+    return fail(SV_ERR_INVALID_ARG, "rule_param must be in (0, 1]");
+  if (s->rule != SV_RULE_LOSSLESS && s->siblings == SV_SIBLINGS_DETERMINISTIC)
+    return fail(SV_ERR_UNSUPPORTED, "the lenience and interpolation rules need sampled siblings (they test q)");
   const int md_needed = eff_max_nodes(s->max_nodes);
   if (s->max_depth < md_needed)
     return fail(SV_ERR_INVALID_ARG, "max_depth (%d) must be >= max_nodes (%d)", s->max_depth, md_needed);
@@ -284,6 +290,8 @@ sv_status run_sample(const sv_sample_args* s, char* ws, const WsLayout& w, hipSt
   p.stats = (sv::ChunkStat*)(ws + w.stats);
   p.rowstats = (sv::RowStat*)(ws + w.rowstats);
   p.det = s->siblings == SV_SIBLINGS_DETERMINISTIC;
+  p.rule = s->rule;
+  p.rule_param = s->rule_param;
   p.slices = w.xcnt ? sv::walk_slices(s->B, p.nch, walk_passes(s)) : 1;
   p.xs = w.xcnt ? (double*)(ws + w.xs) : nullptr;
   p.xcnt = w.xcnt ? (int32_t*)(ws + w.xcnt) : nullptr;

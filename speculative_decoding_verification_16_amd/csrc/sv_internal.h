@@ -70,6 +70,8 @@ struct SampleParams {
   bool trunc;               // min-p truncation of the target rows
   float theta;              // its threshold on logit - row max: fp32(T ln min_p)
   bool det;                 // siblings are deterministic candidates (q unused)
+  int32_t rule;             // accept test: 0 lossless, 1 lenience, 2 interpolation
+  float rule_param;         // l or lambda of the rule
   uint64_t seed;
   uint32_t step;
   const uint32_t* request_id;

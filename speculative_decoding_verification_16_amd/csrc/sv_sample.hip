@@ -746,7 +746,12 @@ __global__ __launch_bounds__(NT) void walk_kernel(SampleParams p) {
       const float pf = allowed<TR>(target_prob(sh.lgx[ch], st.lmax, p.c, invS), sh.lgx[ch], st.lmax, p.theta);
       const double qv = (double)sh.qx[ch];
       const double P = level == 0 ? (double)pf : fmax(0.0, (double)pf - cc * qv) / M;
-      const int ok = __builtin_amdgcn_readfirstlane((P > 0.0 && sh.u[ch] * qv <= P) ? 1 : 0);
+      // accept test u * den <= num: lossless (P, q), lenience (P, l q) or
+      // interpolation (lambda P + (1 - lambda) q, q)
+      const double rp = (double)p.rule_param;
+      const double num = p.rule == 2 ? rp * P + (1.0 - rp) * qv : P;
+      const double den = p.rule == 1 ? rp * qv : qv;
+      const int ok = __builtin_amdgcn_readfirstlane((num > 0.0 && sh.u[ch] * den <= num) ? 1 : 0);
       if (ok) { accepted = ch; break; }
       // rejected: the next sibling is tested against the next residual level
       const double cn = cc + M;

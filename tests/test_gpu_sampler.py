@@ -409,3 +409,75 @@ def test_gpu_deterministic_chi_square(min_p):
     for i in range(2):
         a = pt[tokens[i]]
         assert abs((node == i).mean() - a) < 5 * math.sqrt(a * (1 - a) / n)
+
+
+# ---- lossy accept rules ([LOSSY] 3.1: lenience, interpolation) ------------------
+LOSSY_SMALL = ["c1_full", "c2_small", "c3_small", "c5_small_odd_vocab", "c4_small_hot", "max_tree_64"]
+
+
+@pytest.mark.parametrize("rule,param", [("lenience", 0.5), ("interpolation", 0.6)])
+@pytest.mark.parametrize("name", LOSSY_SMALL)
+def test_sampler_lossy_rules_small(name, rule, param):
+    cfg = SMALL[name]
+    w = generate(cfg, "cuda", attn=False)
+    T = cfg.temperature
+    print(f"[lossy] {name} {rule}={param} B={w['B']} N={w['N']} V={cfg.V}", flush=True)
+    r = _gpu_sample(w, T, rule=rule, rule_param=param)
+    ref = oracle.verify(w["cu_nodes"], w["parent"], w["draft_tokens"].cpu().numpy(), w["logits"].cpu().numpy(),
+                        w["draft_probs"].cpu().numpy(), temperature=T, seed=w["seed"],
+                        max_depth=r["accepted_nodes"].shape[1], rule=rule, rule_param=param)
+    assert int(r["status"].item()) == 0, sv.status_names(int(r["status"].item()))
+    flagged = compare_walk(r, ref, w["B"], greedy=False)
+    print(f"  flagged near-ties: {flagged}/{w['B']}")
+    ok = ref["flag_depth"] < 0
+    assert np.array_equal(r["residual_passes"].cpu().numpy()[ok], ref["n_rejections"][ok])
+
+
+@pytest.mark.parametrize("name", ["c3_eagle_tree", "c5_super_tree"])
+def test_sampler_lenience_full_size(name):
+    cfg = get_config(name)
+    w = generate(cfg, "cuda", attn=False)
+    print(f"[lossy-full] {name} lenience=0.5 B={w['B']} N={w['N']} V={cfg.V}", flush=True)
+    r = _gpu_sample(w, cfg.temperature, rule="lenience", rule_param=0.5)
+    ref = oracle.verify(w["cu_nodes"], w["parent"], w["draft_tokens"].cpu().numpy(), w["logits"].cpu().numpy(),
+                        w["draft_probs"].cpu().numpy(), temperature=cfg.temperature, seed=w["seed"],
+                        max_depth=r["accepted_nodes"].shape[1], rule="lenience", rule_param=0.5)
+    assert int(r["status"].item()) == 0
+    flagged = compare_walk(r, ref, w["B"], greedy=False)
+    print(f"  flagged near-ties: {flagged}/{w['B']}; mean accept_len {r['accept_len'].float().mean().item():.3f}")
+
+
+def test_gpu_lenience_law():
+    """One drafted position at V = 8: the emitted law is the closed form of
+    [LOSSY] A.3 and the acceptance rate is sum min(q, p/l)."""
+    rng = np.random.default_rng(601)
+    V, n, ell = 8, 1_000_000, 0.5
+    lg, q = rows_from_probs(rng, V, 2, sharp=1.0, draft_noise=1.3)
+    cu, par, toks, logits, qq = replicated_batch(rng, np.array([-1], np.int32), lg, q, n)
+    r = sv.sample(torch.from_numpy(cu).cuda(), torch.from_numpy(par).cuda(), torch.from_numpy(toks).cuda(),
+                  torch.from_numpy(logits).cuda(), torch.from_numpy(qq).cuda(), temperature=1.0, seed=4646,
+                  max_nodes=1, rule="lenience", rule_param=ell)
+    torch.cuda.synchronize()
+    p, q0 = softmax64(lg[0]), q[0].astype(np.float64)
+    ceil = np.minimum(q0, p / ell)
+    law = ceil + (q0 - ceil).sum() / (q0 - np.minimum(q0, p)).sum() * (p - np.minimum(p, q0))
+    c = np.bincount(r["out_tokens"][:, 0].cpu().numpy(), minlength=V)
+    assert stats.chisquare(c, law / law.sum() * n).pvalue > 1e-3
+    a = float(ceil.sum())
+    freq = r["accept_len"].float().mean().item()
+    assert abs(freq - a) < 5 * math.sqrt(a * (1 - a) / n)
+
+
+def test_lossy_rule_arguments_and_greedy():
+    cfg = SMALL["c2_small"]
+    w = generate(cfg, "cuda", attn=False)
+    with pytest.raises(sv.SpecVerifyError):
+        _gpu_sample(w, 1.0, rule="lenience", rule_param=0.0)
+    with pytest.raises(sv.SpecVerifyError):
+        _gpu_sample(w, 1.0, rule="interpolation", rule_param=1.5)
+    with pytest.raises(sv.SpecVerifyError):
+        _gpu_sample(w, 1.0, rule="lenience", rule_param=0.5, siblings="deterministic")
+    g0 = _gpu_sample(w, 0.0)
+    g1 = _gpu_sample(w, 0.0, rule="interpolation", rule_param=0.5)
+    for k in ("accept_len", "accepted_nodes", "out_tokens"):
+        assert torch.equal(g0[k], g1[k]), k
