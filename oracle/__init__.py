@@ -42,7 +42,8 @@ _lib = None
 
 ACCEPT_TOL = 1e-5  # |u - P/Q| below this marks an accept test as a near-tie
 CDF_TOL = 1e-6     # a CDF boundary this close to u marks the final draw as a near-tie
-RULES = {"lossless": 0, "lenience": 1, "interpolation": 2}
+RULES = {"lossless": 0, "lenience": 1, "interpolation": 2, "truncation": 3}
+ETA_TOL = 1e-5  # near tie of a token to the eta threshold, log-probability units
 
 
 def build(verbose: bool = False) -> str:
@@ -77,7 +78,8 @@ def _load():
     lib.orc_residual.restype = f64
     lib.orc_inverse_cdf.argtypes = [i32, P, f64, P]
     lib.orc_inverse_cdf.restype = i32
-    lib.orc_verify.argtypes = [i32, i32, P, P, P, P, P, f64, i32, ctypes.c_float, i32, i32, f64, u64, u32, P, i32,
+    lib.orc_verify.argtypes = [i32, i32, P, P, P, P, P, f64, i32, ctypes.c_float, f64, f64, f64, i32, i32, f64, u64,
+                               u32, P, i32,
                                P, P, P, P,
                                P, P, P, P, P, P, f64, f64, i32]
     lib.orc_verify.restype = i32
@@ -85,6 +87,10 @@ def _load():
     lib.orc_target_rows.restype = i32
     lib.orc_truncate_min_p.argtypes = [i32, P, ctypes.c_float, P]
     lib.orc_truncate_min_p.restype = None
+    lib.orc_truncate_eta.argtypes = [i32, P, f64, f64, f64, P, P]
+    lib.orc_truncate_eta.restype = f64
+    lib.orc_row_entropy.argtypes = [i32, P, f64]
+    lib.orc_row_entropy.restype = f64
     lib.orc_remove_candidate.argtypes = [i32, P, i32, P]
     lib.orc_remove_candidate.restype = f64
     _lib = lib
@@ -233,9 +239,32 @@ def truncate_min_p(logits_row, p_row, theta: float) -> np.ndarray:
     return p
 
 
+def truncate_eta(logits_row, p_row, temperature: float, eps: float, delta: float) -> tuple[np.ndarray, float, float]:
+    """p_row truncated to the eta allowed set {p >= min(eps, delta e^-H)}; also
+    returns the fp64 threshold on l_x - l_max and the smallest distance of a
+    token to it (log-probability units)."""
+    lg = np.ascontiguousarray(logits_row, dtype=np.float32)
+    p = np.array(p_row, dtype=np.float64, copy=True)
+    m = np.zeros(1, np.float64)
+    th = _load().orc_truncate_eta(lg.shape[0], _ptr(lg), float(temperature), float(eps), float(delta), _ptr(p),
+                                  _ptr(m))
+    return p, float(th), float(m[0])
+
+
+def row_entropy(logits_row, temperature: float) -> float:
+    lg = np.ascontiguousarray(logits_row, dtype=np.float32)
+    return float(_load().orc_row_entropy(lg.shape[0], _ptr(lg), float(temperature)))
+
+
+def eta_params(eta) -> tuple[float, float]:
+    """(eps, delta) of the eta allowed set as fp32 arguments reach the library."""
+    eps, delta = eta
+    return float(np.float32(eps)), float(np.float32(delta))
+
+
 def verify(cu_nodes, parent, tokens, logits, q, *, temperature, seed, step=0, request_id=None,
            max_depth=None, accept_tol=ACCEPT_TOL, cdf_tol=CDF_TOL, nthreads=None, min_p=0.0,
-           siblings="sampled", rule="lossless", rule_param=1.0) -> dict:
+           siblings="sampled", rule="lossless", rule_param=1.0, eta=None, eta_tol=ETA_TOL) -> dict:
     """The verification walk for a packed batch; returns a dict of numpy arrays.
 
     logits, q: float32 [N+B, V] (q may be None when temperature == 0 or the
@@ -248,6 +277,12 @@ def verify(cu_nodes, parent, tokens, logits, q, *, temperature, seed, step=0, re
     rule="lenience" (rule_param = l) or "interpolation" (rule_param = lambda),
     both in (0, 1]: the lossy accept tests of [LOSSY] 3.1 (h = min(1, p/(l q))
     and h = min(1, (lambda p + (1 - lambda) q)/q)), residuals unchanged.
+    eta=(eps, delta): verify against the eta truncated target ([LOSSY] 2.3)
+    instead of min-p (flag_kind 2 marks a row with a token within eta_tol of
+    its threshold).
+    rule="truncation": truncation-based verification ([LOSSY] 3.2) over the
+    min-p or eta allowed set: accept iff the drafted token is allowed; after
+    every child of a position is rejected, draw from q restricted to the set.
     """
     if rule not in RULES:
         raise ValueError(f"rule must be one of {sorted(RULES)}")
@@ -282,8 +317,14 @@ def verify(cu_nodes, parent, tokens, logits, q, *, temperature, seed, step=0, re
     }
     theta = min_p_theta(temperature, min_p)
     trunc = 1 if theta > float("-inf") else 0
+    eps, delta = 0.0, 0.0
+    if eta is not None:
+        if trunc:
+            raise ValueError("min_p and eta are exclusive")
+        eps, delta = eta_params(eta)
+        trunc = 2 if temperature > 0 else 0
     rc = _load().orc_verify(B, V, _ptr(cu), _ptr(par), _ptr(tok), _ptr(lg), _ptr(qq), float(temperature),
-                            trunc, ctypes.c_float(theta), det, RULES[rule], float(np.float32(rule_param)), int(seed), int(step), _ptr(rid), int(max_depth), _ptr(out["accept_len"]),
+                            trunc, ctypes.c_float(theta), eps, delta, float(eta_tol), det, RULES[rule], float(np.float32(rule_param)), int(seed), int(step), _ptr(rid), int(max_depth), _ptr(out["accept_len"]),
                             _ptr(out["accepted_nodes"]), _ptr(out["out_tokens"]), _ptr(out["uniforms"]),
                             _ptr(out["flag_depth"]), _ptr(out["flag_kind"]), _ptr(out["n_rejections"]),
                             _ptr(out["status"]), _ptr(out["min_accept_margin"]), _ptr(out["cdf_margin"]),

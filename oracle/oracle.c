@@ -275,6 +275,59 @@ void orc_truncate_min_p(int V, const float* logits, float theta, double* p) {
   for (int x = 0; x < V; ++x) p[x] /= Z;
 }
 
+/* eta-sampling truncation ([LOSSY] section 2.3: the allowed set
+ * A = {x : p(x) >= min(eps, delta exp(-H(p)))}, H the Shannon entropy of the
+ * target row). With z_x = (l_x - l_max)/T, S = sum exp(z), p = exp(z)/S and
+ * H = ln S - sum p z, the test p(x) >= tau reads
+ * l_x - l_max >= T (ln S + ln tau). Reading: as for min-p, membership is
+ * decided on the fp32 logit difference against the fp32 rounding of that
+ * threshold; a row with some token within tol (in log-probability units) of
+ * the exact threshold is a near tie, reported through *margin so that a
+ * caller can flag it. p is masked and renormalised in place; returns the
+ * fp64 threshold.                                                          */
+double orc_truncate_eta(int V, const float* logits, double T, double eps, double delta, double* p, double* margin) {
+  float lmax = -INFINITY;
+  for (int x = 0; x < V; ++x)
+    if (logits[x] > lmax) lmax = logits[x];
+  double S = 0.0, E = 0.0;
+  for (int x = 0; x < V; ++x) {
+    double z = ((double)logits[x] - (double)lmax) / T;
+    double e = exp(z);
+    S += e;
+    E += e * z;
+  }
+  double H = log(S) - E / S;
+  double ln_tau = fmin(log(eps), log(delta) - H);
+  double th64 = T * (log(S) + ln_tau);
+  float th = (float)th64;
+  double Z = 0.0, mg = INFINITY;
+  for (int x = 0; x < V; ++x) {
+    float d = logits[x] - lmax;
+    double dist = fabs((double)d - th64) / T;
+    if (dist < mg) mg = dist;
+    if (!(d >= th)) p[x] = 0.0;
+    Z += p[x];
+  }
+  for (int x = 0; x < V; ++x) p[x] /= Z;
+  if (margin) *margin = mg;
+  return th64;
+}
+
+/* Entropy of the target row at temperature T, in nats (the H of the eta
+ * allowed set above), computed the same way.                              */
+double orc_row_entropy(int V, const float* logits, double T) {
+  float lmax = -INFINITY;
+  for (int x = 0; x < V; ++x)
+    if (logits[x] > lmax) lmax = logits[x];
+  double S = 0.0, E = 0.0;
+  for (int x = 0; x < V; ++x) {
+    double z = ((double)logits[x] - (double)lmax) / T;
+    S += exp(z);
+    E += exp(z) * z;
+  }
+  return log(S) - E / S;
+}
+
 /* Greedy target token: argmax of the raw logits, lowest index on ties.    */
 int orc_argmax(int V, const float* logits) {
   int best = 0;
@@ -357,10 +410,13 @@ typedef struct {
   const int32_t *cu_nodes, *parent, *tokens;
   const float *logits, *q;
   double T;
-  int trunc;     /* min-p truncation of every target row */
-  float theta;   /* its threshold on l_x - l_max         */
+  int trunc;     /* truncation of every target row: 0 none, 1 min-p, 2 eta */
+  float theta;   /* min-p: its threshold on l_x - l_max   */
+  double eta_eps, eta_delta; /* eta: its eps and delta   */
+  double eta_tol; /* eta: near-tie distance of a token to the threshold */
   int det;       /* siblings are deterministic candidates (q unused) */
-  int rule;      /* accept rule: 0 lossless, 1 lenience, 2 interpolation */
+  int rule;      /* accept rule: 0 lossless, 1 lenience, 2 interpolation,
+                    3 truncation-based (accept iff the token is allowed)   */
   double rule_param; /* lenience l or interpolation lambda, in (0, 1]    */
   uint64_t seed;
   uint32_t step;
@@ -441,7 +497,19 @@ static void orc_walk_one(void* vctx, int64_t bi) {
      * is checked against ([SD]: node j is checked against p_i and q_i of the
      * position it was drafted at, i.e. its parent's row)                  */
     if (orc_target_probs(V, c->logits + row * (int64_t)V, c->T, P)) { c->status[b] |= 0x08; break; }
-    if (c->trunc) orc_truncate_min_p(V, c->logits + row * (int64_t)V, c->theta, P);
+    const float* lrow = c->logits + row * (int64_t)V;
+    float th_row = c->theta; /* this position's threshold on l_x - l_max */
+    if (c->trunc == 1) orc_truncate_min_p(V, lrow, c->theta, P);
+    if (c->trunc == 2) {
+      double mg = INFINITY;
+      th_row = (float)orc_truncate_eta(V, lrow, c->T, c->eta_eps, c->eta_delta, P, &mg);
+      if (mg < c->eta_tol && c->flag_depth[b] < 0) { c->flag_depth[b] = d; c->flag_kind[b] = 2; }
+    }
+    float lmax_row = -INFINITY;
+    for (int x = 0; x < V; ++x)
+      if (lrow[x] > lmax_row) lmax_row = lrow[x];
+    int n_kids = 0;
+    for (int ch = pos + 1; ch < T; ++ch) n_kids += par[ch] == pos;
     if (!c->det)
       for (int x = 0; x < V; ++x) Q[x] = (double)c->q[row * (int64_t)V + x];
     int accepted = -1;
@@ -463,6 +531,16 @@ static void orc_walk_one(void* vctx, int64_t bi) {
         double R = orc_remove_candidate(V, P, x, tmp);
         if (!(R > 0.0)) c->status[b] |= 0x10;
         memcpy(P, tmp, sizeof(double) * (size_t)V);
+        continue;
+      }
+      if (c->rule == 3) {
+        /* [LOSSY] 3.2, truncation-based verification (SpecCascade with the
+         * min-p set, typical acceptance with the eta set): h(x) = 1 if x is
+         * in the allowed set, else 0 -- the fp32 membership test of the
+         * truncation above. No uniform is involved.                        */
+        float dx = lrow[x] - lmax_row;
+        if (dx >= th_row) { accepted = ch; break; }
+        c->n_rejections[b] += 1;
         continue;
       }
       /* [SD] acceptance rule r <= min(1, p/q), written as u*q <= p with p > 0
@@ -495,6 +573,26 @@ static void orc_walk_one(void* vctx, int64_t bi) {
       pos = accepted;
       continue;
     }
+    if (c->rule == 3 && n_kids > 0) {
+      /* every child rejected under truncation-based verification: the token
+       * comes from the draft restricted to the allowed set,
+       * r(x) = q(x) 1{x in A} / Z_A(q). Reading: [LOSSY] 3.2 gives the law
+       * the rule generates, q(x) / Z_A(q) on A and 0 elsewhere, but no
+       * residual; with P(generate x) = q(x) h(x) + (1 - Z_A(q)) r(x) this r is
+       * the only one that yields it, at any number of i.i.d. siblings. A
+       * zero Z_A(q) keeps the truncated target (flagged).                  */
+      double Z = 0.0;
+      for (int x = 0; x < V; ++x) {
+        float dx = lrow[x] - lmax_row;
+        tmp[x] = dx >= th_row ? (double)c->q[row * (int64_t)V + x] : 0.0;
+        Z += tmp[x];
+      }
+      if (Z > 0.0) {
+        for (int x = 0; x < V; ++x) P[x] = tmp[x] / Z;
+      } else {
+        c->status[b] |= 0x10;
+      }
+    }
     /* no child accepted (or none to try): one token from the current
      * distribution -- the residual after rejections (with deterministic
      * candidates: the target without the tried ones), p at a leaf        */
@@ -514,8 +612,12 @@ static void orc_walk_one(void* vctx, int64_t bi) {
 
 /* Verification of a packed batch (see the calling convention of the GPU
  * library: rows cu_nodes[b] + b + r, r = 0 root, r = 1 + j after node j).
- * T == 0 selects greedy verification; trunc != 0 verifies against the
- * min-p truncated target (threshold theta, see orc_truncate_min_p); det != 0
+ * T == 0 selects greedy verification; trunc = 1 verifies against the
+ * min-p truncated target (threshold theta, see orc_truncate_min_p), trunc = 2
+ * against the eta truncated target (eta_eps, eta_delta; a visited row with a
+ * token within eta_tol of its threshold is flagged, kind 2, see
+ * orc_truncate_eta); rule 3 is truncation-based verification ([LOSSY] 3.2)
+ * over the allowed set of trunc 1 or 2; det != 0
  * treats the siblings as deterministic candidates ([LOSSY] G.3; q unused and
  * may be NULL; a rejection takes the candidate out of the target); rule 1/2
  * selects the lossy lenience / interpolation accept test ([LOSSY] 3.1, A.1,
@@ -523,23 +625,28 @@ static void orc_walk_one(void* vctx, int64_t bi) {
  * request it also reports
  *   flag_depth: accepted nodes before the first decision closer than the
  *               tolerance to its threshold (-1: none), flag_kind 0 = accept
- *               test, 1 = final inverse-CDF draw;
+ *               test, 1 = final inverse-CDF draw, 2 = eta set boundary;
  *   n_rejections: rejections (= residual renormalisations or removals);
  *   status: SV_STATUS-like bits (0x01 tree, 0x02 packing, 0x04 token,
  *           0x08 non-finite row, 0x10 zero residual, 0x80 out of memory);
  *   min_accept_margin, cdf_margin: the smallest |u - P/Q| seen and the
  *           margin of the final draw.                                     */
 int orc_verify(int B, int V, const int32_t* cu_nodes, const int32_t* parent, const int32_t* tokens,
-               const float* logits, const float* q, double T, int trunc, float theta, int det, int rule,
-               double rule_param, uint64_t seed, uint32_t step,
+               const float* logits, const float* q, double T, int trunc, float theta, double eta_eps,
+               double eta_delta, double eta_tol, int det, int rule, double rule_param, uint64_t seed, uint32_t step,
                const uint32_t* request_id, int max_depth, int32_t* accept_len, int32_t* accepted_nodes,
                int32_t* out_tokens, double* uniforms_out, int32_t* flag_depth, int32_t* flag_kind,
                int32_t* n_rejections, int32_t* status, double* min_accept_margin, double* cdf_margin,
                double accept_tol, double cdf_tol, int nthreads) {
   if (B < 0 || V < 1 || max_depth < 0 || T < 0.0) return 1;
   if (T > 0.0 && !det && !q) return 1;
-  if (rule < 0 || rule > 2 || (rule && !(rule_param > 0.0 && rule_param <= 1.0)) || (rule && det)) return 1;
-  orc_walk_ctx c = {B, V, cu_nodes, parent, tokens, logits, q, T, trunc, theta, det, rule, rule_param, seed, step,
+  if (rule < 0 || rule > 3 || (rule && det)) return 1;
+  if ((rule == 1 || rule == 2) && !(rule_param > 0.0 && rule_param <= 1.0)) return 1;
+  if (rule == 3 && (!trunc || T == 0.0)) return 1; /* needs an allowed set */
+  if (trunc < 0 || trunc > 2) return 1;
+  if (trunc == 2 && !(eta_eps > 0.0 && eta_eps < 1.0 && eta_delta > 0.0 && eta_delta <= 1.0)) return 1;
+  orc_walk_ctx c = {B, V, cu_nodes, parent, tokens, logits, q, T, trunc, theta, eta_eps, eta_delta, eta_tol,
+                    det, rule, rule_param, seed, step,
                     request_id, max_depth,
                     accept_len, accepted_nodes, out_tokens, uniforms_out, flag_depth, flag_kind,
                     n_rejections, status, min_accept_margin, cdf_margin, accept_tol, cdf_tol};
