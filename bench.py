@@ -111,8 +111,11 @@ def parse_args():
     ap.add_argument("--no-events", action="store_true", help="time without the per-kernel HIP events")
     ap.add_argument("--min-p", type=float, default=0.0,
                     help="verify against the min-p truncated target (0 = plain lossless verification)")
-    ap.add_argument("--rule", choices=["lossless", "lenience", "interpolation"], default="lossless",
-                    help="accept test (lenience and interpolation are lossy, [LOSSY] 3.1)")
+    ap.add_argument("--eta", type=float, nargs=2, default=None, metavar=("EPS", "DELTA"),
+                    help="verify against the eta truncated target {p >= min(EPS, DELTA exp(-H))} instead")
+    ap.add_argument("--rule", choices=["lossless", "lenience", "interpolation", "truncation"], default="lossless",
+                    help="accept test (lenience and interpolation are lossy, [LOSSY] 3.1; truncation accepts "
+                         "any allowed token, [LOSSY] 3.2, and needs --min-p or --eta)")
     ap.add_argument("--rule-param", type=float, default=1.0, help="l or lambda of --rule, in (0, 1]")
     ap.add_argument("--siblings", choices=["sampled", "deterministic"], default="sampled",
                     help="sampled: draft tokens are draws from q; deterministic: the top-k of q as fixed "
@@ -217,7 +220,7 @@ def row_stats_bytes(w) -> float:
 
 
 def cpu_baseline(w, budget_s: float, min_p: float = 0.0, siblings: str = "sampled", rule: str = "lossless",
-                 rule_param: float = 1.0):
+                 rule_param: float = 1.0, eta=None):
     """The fp64 oracle (attention of every (node, head) of a request, then the
     verification walk) over whole requests in order until the budget is spent.
     Returns verified draft tokens/s of that sample, the thread count and a
@@ -255,7 +258,7 @@ def cpu_baseline(w, budget_s: float, min_p: float = 0.0, siblings: str = "sample
                          nthreads=threads)
         oracle.verify(sub_cu, par[n0:n1], toks, lg, qq, temperature=w["temperature"], seed=w["seed"],
                       request_id=np.arange(b0, b1, dtype=np.uint32), nthreads=threads, min_p=min_p,
-                      siblings=siblings, rule=rule, rule_param=rule_param)
+                      siblings=siblings, rule=rule, rule_param=rule_param, eta=eta)
         spent += time.perf_counter() - t0
         nodes_done += n1 - n0
         req_done = b1
@@ -306,7 +309,8 @@ def main():
             s = sv.SampleCall(a.keep["cu"], x["parent_t"], x["draft_tokens"], x["logits"],
                               None if det else x["draft_probs"], temperature=cfg.temperature, seed=x["seed"],
                               max_nodes=x["max_T"], residual_passes=True, min_p=args.min_p,
-                              siblings=args.siblings, rule=args.rule, rule_param=args.rule_param)
+                              siblings=args.siblings, rule=args.rule, rule_param=args.rule_param,
+                              eta=tuple(args.eta) if args.eta else None)
             calls.append((a, s, sv.StepCall(a, s)))
     torch.cuda.synchronize()
 
@@ -366,8 +370,9 @@ def main():
         kernels["row_stats_kernel"] = {"us": rs_ms * 1e3, "alg_bytes": rs_b, "GB_s": rs_b / rs_ms / 1e6}
         rest_us = ms * 1e3 - attn_ms * 1e3 - rs_ms * 1e3
         # sampled siblings: one 8V pass (logits and q) per rejection; deterministic
-        # candidates need none (the min-p visit passes are not counted here)
-        per_pass = 0 if det else 8 * w["V"]
+        # candidates and the truncation rule's membership tests need none (the
+        # truncation visit and redraw passes are not counted here)
+        per_pass = 0 if det or args.rule == "truncation" else 8 * w["V"]
         kernels["other(prep+finalize+walk)"] = {"us": rest_us,
                                             "residual_pass_bytes": float(passes.sum().item()) * per_pass}
         dom = max((k for k in kernels if "alg_bytes" in kernels[k]), key=lambda k: kernels[k]["us"])
@@ -381,7 +386,8 @@ def main():
 
     cpu = None
     if args.cpu_seconds > 0:
-        v_cpu, threads, desc = cpu_baseline(w, args.cpu_seconds, args.min_p, args.siblings, args.rule, args.rule_param)
+        v_cpu, threads, desc = cpu_baseline(w, args.cpu_seconds, args.min_p, args.siblings, args.rule, args.rule_param,
+                                            tuple(args.eta) if args.eta else None)
         cpu = {"value": round(v_cpu, 2), "unit": "verified draft tokens/s", "cores": threads, "kind": "oracle",
                "sample": desc}
 
@@ -403,7 +409,9 @@ def main():
                    "Hq": cfg.Hq, "Hkv": cfg.Hkv, "D": cfg.D, "kv_dtype": cfg.dtype, "V": cfg.V,
                    "temperature": cfg.temperature, **({"min_p": args.min_p} if args.min_p > 0 else {}),
                    **({"siblings": "deterministic (top-k of q)"} if det else {}),
-                   **({"rule": args.rule, "rule_param": args.rule_param} if args.rule != "lossless" else {})},
+                   **({"eta": list(args.eta)} if args.eta else {}),
+                   **({"rule": args.rule, "rule_param": args.rule_param} if args.rule in ("lenience", "interpolation")
+                      else {"rule": args.rule} if args.rule == "truncation" else {})},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "input_sets": n_sets,

@@ -170,7 +170,18 @@ typedef enum { SV_SIBLINGS_SAMPLED = 0, SV_SIBLINGS_DETERMINISTIC = 1 } sv_sibli
  * Every other step is the lossless one: a rejection moves P to the residual
  * max(0, P - Q) normalised (the residual both appendices give), and the bonus
  * token is drawn from P. Products and sums are in fp64 from the fp32 rule_param. */
-typedef enum { SV_RULE_LOSSLESS = 0, SV_RULE_LENIENCE = 1, SV_RULE_INTERPOLATION = 2 } sv_rule;
+/*   SV_RULE_TRUNCATION: truncation-based verification ([LOSSY] section 3.2;
+ *     SpecCascade with the min-p allowed set, typical acceptance with the eta
+ *     set): h(x) = 1 if x is in the allowed set of min_p or eta_eps/eta_delta
+ *     (one of them is required), else 0 -- the same fp32 membership test the
+ *     truncation makes; no uniform is used. After every child of a position
+ *     is rejected, the bonus token is drawn from q restricted to the set,
+ *     q(x) 1{x in A} / sum_A q (the residual that gives the section's law
+ *     q / Z_A(q); with no mass there the truncated target is used and
+ *     SV_STATUS_ZERO_RESIDUAL set); at a leaf from the truncated target.
+ *     rule_param is unused.                                                */
+typedef enum { SV_RULE_LOSSLESS = 0, SV_RULE_LENIENCE = 1, SV_RULE_INTERPOLATION = 2,
+               SV_RULE_TRUNCATION = 3 } sv_rule;
 
 typedef struct {
   int32_t B, V;        /* requests (>= 0); vocabulary size (1 .. 1<<22)      */
@@ -192,6 +203,15 @@ typedef struct {
                           applies with p_Theta in place of p. Each visited
                           position costs one more vocabulary pass (the mass
                           of A). Not with probs_out.                         */
+  float eta_eps;       /* 0 = off; in (0, 1) with temperature > 0 and min_p == 0:
+                          verify against the eta truncated target ([LOSSY] 2.3):
+                          A = {x : p(x) >= min(eta_eps, eta_delta exp(-H(p)))},
+                          H the entropy of p in nats, decided as
+                          l_x - l_max >= fp32(T (ln S + ln tau)) with S the
+                          row's sum of exp((l - l_max)/T), computed in fp64
+                          per row (an extra accumulator in the row statistics
+                          pass); otherwise as min_p. Not with probs_out.    */
+  float eta_delta;     /* delta of the eta set, in (0, 1] when eta_eps > 0     */
   int32_t siblings;    /* sv_siblings: how the children of a node were drafted */
   int32_t rule;        /* sv_rule (SV_RULE_LOSSLESS unless sampled siblings)   */
   float rule_param;    /* l or lambda of the rule, in (0, 1]; unused when lossless */

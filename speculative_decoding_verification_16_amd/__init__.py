@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(_PKG, "libspecverify.so")
 SV_OK, SV_ERR_INVALID_ARG, SV_ERR_TREE, SV_ERR_UNSUPPORTED, SV_ERR_WORKSPACE, SV_ERR_HIP = range(6)
 SV_F32, SV_BF16 = 0, 1
 SIBLINGS = {"sampled": 0, "deterministic": 1}  # sv_siblings
-RULES = {"lossless": 0, "lenience": 1, "interpolation": 2}  # sv_rule
+RULES = {"lossless": 0, "lenience": 1, "interpolation": 2, "truncation": 3}  # sv_rule
 STATUS_BITS = {0x01: "TREE_INVALID", 0x02: "PACKING", 0x04: "TOKEN_RANGE", 0x08: "NONFINITE",
                0x10: "ZERO_RESIDUAL", 0x20: "CTX_RANGE", 0x40: "SYNC"}
 
@@ -43,7 +43,8 @@ class SvAttnArgs(ctypes.Structure):
 class SvSampleArgs(ctypes.Structure):
     _fields_ = [("B", _i32), ("V", _i32), ("total_nodes", _i32), ("max_nodes", _i32), ("cu_nodes", _P),
                 ("parent", _P), ("draft_tokens", _P), ("target_logits", _P), ("draft_probs", _P),
-                ("temperature", _f32), ("min_p", _f32), ("siblings", _i32), ("rule", _i32), ("rule_param", _f32), ("seed", _u64), ("step", _u32), ("request_id", _P),
+                ("temperature", _f32), ("min_p", _f32), ("eta_eps", _f32), ("eta_delta", _f32), ("siblings", _i32),
+                ("rule", _i32), ("rule_param", _f32), ("seed", _u64), ("step", _u32), ("request_id", _P),
                 ("max_depth", _i32),
                 ("accept_len", _P), ("accepted_nodes", _P), ("out_tokens", _P), ("probs_out", _P),
                 ("uniforms_out", _P), ("residual_passes", _P), ("status", _P), ("prof_start", _P),
@@ -172,7 +173,7 @@ class SampleCall:
     def __init__(self, cu_nodes, parent, draft_tokens, target_logits, draft_probs, *, temperature, seed, step=0,
                  request_id=None, max_nodes=0, max_depth=None, probs_out=False, uniforms_out=False,
                  residual_passes=False, status=None, min_p=0.0, siblings="sampled", rule="lossless",
-                 rule_param=1.0):
+                 rule_param=1.0, eta=None):
         load_library()
         if siblings not in SIBLINGS:
             raise ValueError(f"siblings must be one of {sorted(SIBLINGS)}")
@@ -206,6 +207,8 @@ class SampleCall:
         s.target_logits, s.draft_probs = _ptr(target_logits), _ptr(draft_probs)
         s.temperature, s.seed, s.step = float(temperature), int(seed), int(step)
         s.min_p = float(min_p)
+        if eta is not None:  # (eps, delta) of the eta allowed set
+            s.eta_eps, s.eta_delta = float(eta[0]), float(eta[1])
         s.siblings = SIBLINGS[siblings]
         s.rule, s.rule_param = RULES[rule], float(rule_param)
         s.request_id = _ptr(self.keep["rid"])

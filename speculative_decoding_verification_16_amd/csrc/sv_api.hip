@@ -100,7 +100,7 @@ sv::AttnPlan plan_attn(const sv_attn_args* a) {
 
 struct WsLayout {
   size_t anc = 0, o_part = 0, ml_part = 0, items = 0, item_tot = 0, stats = 0, rowstats = 0, xs = 0, xcnt = 0,
-         total = 0;
+         ent = 0, rtheta = 0, total = 0;
 };
 
 size_t attn_part_bytes(const sv_attn_args* a, const sv::AttnPlan& pl, size_t* ml) {
@@ -117,7 +117,7 @@ int sample_nch(const sv_sample_args* s) { return (s->V + sv::kChunk - 1) / sv::k
 
 // does the walk make vocabulary passes (residual masses, the min-p visit pass)?
 bool walk_passes(const sv_sample_args* s) {
-  return s->temperature > 0.f && (s->siblings == SV_SIBLINGS_SAMPLED || s->min_p > 0.f);
+  return s->temperature > 0.f && (s->siblings == SV_SIBLINGS_SAMPLED || s->min_p > 0.f || s->eta_eps > 0.f);
 }
 
 WsLayout layout(const sv_attn_args* a, const sv_sample_args* s) {
@@ -149,6 +149,14 @@ WsLayout layout(const sv_attn_args* a, const sv_sample_args* s) {
     off += align_up(((size_t)s->total_nodes + s->B) * sample_nch(s) * sizeof(sv::ChunkStat));
     w.rowstats = off;
     off += align_up(((size_t)s->total_nodes + s->B) * sizeof(sv::RowStat));
+    if (s->temperature > 0.f && (s->min_p > 0.f || s->eta_eps > 0.f)) {
+      w.rtheta = off;  // per-row threshold of the allowed set
+      off += align_up(((size_t)s->total_nodes + s->B) * sizeof(float));
+    }
+    if (s->temperature > 0.f && s->eta_eps > 0.f) {
+      w.ent = off;  // per-chunk entropy accumulators of the eta set
+      off += align_up(((size_t)s->total_nodes + s->B) * sample_nch(s) * sizeof(double));
+    }
     if (sv::walk_slices(s->B, sample_nch(s), walk_passes(s)) > 1) {
       w.xs = off;
       off += align_up((size_t)s->B * 4 * sample_nch(s) * sizeof(double));
@@ -175,12 +183,22 @@ sv_status check_sample(const sv_sample_args* s) {
   if (!(s->min_p >= 0.f && s->min_p < 1.f)) return fail(SV_ERR_INVALID_ARG, "min_p must be in [0, 1)");
   if (s->siblings != SV_SIBLINGS_SAMPLED && s->siblings != SV_SIBLINGS_DETERMINISTIC)
     return fail(SV_ERR_INVALID_ARG, "siblings must be SV_SIBLINGS_SAMPLED or SV_SIBLINGS_DETERMINISTIC");
-  if (s->rule != SV_RULE_LOSSLESS && s->rule != SV_RULE_LENIENCE && s->rule != SV_RULE_INTERPOLATION)
-    return fail(SV_ERR_INVALID_ARG, "rule must be SV_RULE_LOSSLESS, SV_RULE_LENIENCE or SV_RULE_INTERPOLATION");
-  if (s->rule != SV_RULE_LOSSLESS && !(s->rule_param > 0.f && s->rule_param <= 1.f))
+  if (!(s->eta_eps == 0.f || (s->eta_eps > 0.f && s->eta_eps < 1.f)))
+    return fail(SV_ERR_INVALID_ARG, "eta_eps must be 0 or in (0, 1)");
+  if (s->eta_eps > 0.f && !(s->eta_delta > 0.f && s->eta_delta <= 1.f))
+    return fail(SV_ERR_INVALID_ARG, "eta_delta must be in (0, 1] when eta_eps > 0");
+  if (s->eta_eps > 0.f && s->min_p > 0.f) return fail(SV_ERR_INVALID_ARG, "min_p and eta_eps are exclusive");
+  if (s->rule != SV_RULE_LOSSLESS && s->rule != SV_RULE_LENIENCE && s->rule != SV_RULE_INTERPOLATION &&
+      s->rule != SV_RULE_TRUNCATION)
+    return fail(SV_ERR_INVALID_ARG,
+                "rule must be SV_RULE_LOSSLESS, SV_RULE_LENIENCE, SV_RULE_INTERPOLATION or SV_RULE_TRUNCATION");
+  if ((s->rule == SV_RULE_LENIENCE || s->rule == SV_RULE_INTERPOLATION) &&
+      !(s->rule_param > 0.f && s->rule_param <= 1.f))
     return fail(SV_ERR_INVALID_ARG, "rule_param must be in (0, 1]");
   if (s->rule != SV_RULE_LOSSLESS && s->siblings == SV_SIBLINGS_DETERMINISTIC)
-    return fail(SV_ERR_UNSUPPORTED, "the lenience and interpolation rules need sampled siblings (they test q)");
+    return fail(SV_ERR_UNSUPPORTED, "the lossy rules need sampled siblings (they test or draw from q)");
+  if (s->rule == SV_RULE_TRUNCATION && !(s->temperature > 0.f && (s->min_p > 0.f || s->eta_eps > 0.f)))
+    return fail(SV_ERR_INVALID_ARG, "SV_RULE_TRUNCATION needs temperature > 0 and an allowed set (min_p or eta_eps)");
   const int md_needed = eff_max_nodes(s->max_nodes);
   if (s->max_depth < md_needed)
     return fail(SV_ERR_INVALID_ARG, "max_depth (%d) must be >= max_nodes (%d)", s->max_depth, md_needed);
@@ -195,8 +213,8 @@ sv_status check_sample(const sv_sample_args* s) {
     return fail(SV_ERR_INVALID_ARG, "draft_probs is required when temperature > 0 with sampled siblings");
   if (s->probs_out && s->temperature == 0.f)
     return fail(SV_ERR_INVALID_ARG, "probs_out needs temperature > 0");
-  if (s->probs_out && s->min_p > 0.f)
-    return fail(SV_ERR_UNSUPPORTED, "probs_out is not available with min_p > 0 (the truncated rows are normalised "
+  if (s->probs_out && (s->min_p > 0.f || s->eta_eps > 0.f))
+    return fail(SV_ERR_UNSUPPORTED, "probs_out is not available with truncation (the truncated rows are normalised "
                                     "only at the positions the walk visits)");
   if (!aligned(s->target_logits, 4) || (s->draft_probs && !aligned(s->draft_probs, 4)))
     return fail(SV_ERR_INVALID_ARG, "logit and probability rows must be 4-byte aligned");
@@ -275,8 +293,16 @@ sv_status run_sample(const sv_sample_args* s, char* ws, const WsLayout& w, hipSt
   p.greedy = s->temperature == 0.f;
   p.c = p.greedy ? 0.f : (float)(1.4426950408889634 / (double)s->temperature);
   // min-p allowed set: logit - row max >= fp32(T ln min_p), from the fp32 T and min_p
-  p.trunc = !p.greedy && s->min_p > 0.f;
-  p.theta = p.trunc ? (float)((double)s->temperature * log((double)s->min_p)) : -INFINITY;
+  p.eta = !p.greedy && s->eta_eps > 0.f;
+  p.trunc = !p.greedy && (s->min_p > 0.f || p.eta);
+  p.theta = (p.trunc && !p.eta) ? (float)((double)s->temperature * log((double)s->min_p)) : -INFINITY;
+  // eta allowed set: the per-row threshold T (ln S + min(ln eps, ln delta - H))
+  // is formed by the row finalisation from these fp64 logs of the fp32 inputs
+  p.temp = (double)s->temperature;
+  p.ln_eps = p.eta ? log((double)s->eta_eps) : 0.0;
+  p.ln_delta = p.eta ? log((double)s->eta_delta) : 0.0;
+  p.ent = w.ent ? (double*)(ws + w.ent) : nullptr;
+  p.rtheta = w.rtheta ? (float*)(ws + w.rtheta) : nullptr;
   p.seed = s->seed;
   p.step = s->step;
   p.request_id = s->request_id;

@@ -67,10 +67,14 @@ struct SampleParams {
   const float* q;           // [N+B, V] (unused when greedy)
   float c;                  // log2(e) / temperature (0 when greedy)
   bool greedy;
-  bool trunc;               // min-p truncation of the target rows
-  float theta;              // its threshold on logit - row max: fp32(T ln min_p)
+  bool trunc;               // truncation of the target rows (min-p or eta)
+  bool eta;                 // the eta allowed set (else min-p)
+  float theta;              // min-p threshold on logit - row max: fp32(T ln min_p)
+  double temp, ln_eps, ln_delta; // eta: temperature, ln eps, ln delta
+  double* ent;              // [N+B, nch] eta: per-chunk sum of w * log2-exponent
+  float* rtheta;            // [N+B] per-row threshold of the allowed set (trunc)
   bool det;                 // siblings are deterministic candidates (q unused)
-  int32_t rule;             // accept test: 0 lossless, 1 lenience, 2 interpolation
+  int32_t rule;             // accept test: 0 lossless, 1 lenience, 2 interpolation, 3 truncation
   float rule_param;         // l or lambda of the rule
   uint64_t seed;
   uint32_t step;

@@ -41,10 +41,12 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // ---------------------------------------------------------------------------
 // Pass 1: per (row, chunk) statistics. One wave per chunk of 4096 logits; a
 // lane holds 64 of them in registers, so the row is read from HBM once.
-template <bool GREEDY, bool VEC>
+// ENT also sums w * y per chunk (y = (logit - max) * c, w = exp2(y)): with the
+// chunk sums it gives the row's entropy, which the eta allowed set needs.
+template <bool GREEDY, bool VEC, bool ENT = false>
 __global__ __launch_bounds__(256) void row_stats_kernel(const float* __restrict__ logits, int V, int64_t rows,
                                                         int nch, float c, ChunkStat* __restrict__ stats,
-                                                        int32_t* status) {
+                                                        int32_t* status, double* __restrict__ ent = nullptr) {
   const int lane = threadIdx.x & 63;
   const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (item >= rows * nch) return;
@@ -89,11 +91,16 @@ __global__ __launch_bounds__(256) void row_stats_kernel(const float* __restrict_
   }
   if (__any(bad) && lane == 0) flag(status, kStNonFinite);
   wave_argmax(mx, ai);
-  double s = 0.0;
+  double s = 0.0, e = 0.0;
   if (!GREEDY && mx != -INFINITY) {
 #pragma unroll
-    for (int i = 0; i < 64; ++i) s += (double)target_weight(x[i], mx, c);
+    for (int i = 0; i < 64; ++i) {
+      const float w = target_weight(x[i], mx, c);
+      s += (double)w;
+      if (ENT) e += w > 0.f ? (double)(w * ((x[i] - mx) * c)) : 0.0;
+    }
     s = wave_sum(s);
+    if (ENT) e = wave_sum(e);
   }
   if (lane == 0) {
     ChunkStat st;
@@ -101,30 +108,53 @@ __global__ __launch_bounds__(256) void row_stats_kernel(const float* __restrict_
     st.arg = mx == -INFINITY ? begin : ai;
     st.s = s;
     stats[item] = st;
+    if (ENT) ent[item] = e;
   }
 }
 
 // Pass 2: per-row normalisation merged from the chunk statistics (one wave
 // per row), so that the walk and the p-row output read 16 bytes per row.
 // It also clears the walk's per-request coordination words (xcnt, nsync entries).
-__global__ __launch_bounds__(256) void row_finalize_kernel(const ChunkStat* __restrict__ stats, int64_t rows,
-                                                           int nch, float c, RowStat* __restrict__ rs,
-                                                           int32_t* __restrict__ xcnt, int nsync) {
+// Under truncation it also writes the row's threshold on logit - row max:
+// min-p's constant, or for the eta set T (ln S + min(ln eps, ln delta - H))
+// with the entropy H = ln S - E / S, E = sum_x w_x z_x (z in nats relative to
+// the row maximum) merged from the chunk accumulators like S.
+__global__ __launch_bounds__(256) void row_finalize_kernel(SampleParams p, int64_t rows, int nsync) {
   const int lane = threadIdx.x & 63;
+  const int nch = p.nch;
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (xcnt && gid < nsync) xcnt[gid] = 0;
+  if (p.slices > 1 && gid < nsync) p.xcnt[gid] = 0;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
+  const ChunkStat* st = p.stats + row * nch;
   float lmax, av;
   double S;
   int arg;
-  row_norm(stats + row * nch, nch, c, lmax, S, arg, av);
+  row_norm(st, nch, p.c, lmax, S, arg, av);
+  float th = p.theta;
+  if (p.eta) {
+    double acc = 0.0;
+    if (lmax != -INFINITY) {
+      for (int ch = lane; ch < nch; ch += kWave) {
+        const ChunkStat cs = st[ch];
+        if (cs.lmax != -INFINITY) {
+          const double dl = (double)(cs.lmax - lmax) * (double)p.c;  // chunk max relative to the row's, log2 units
+          acc += exp2(dl) * (p.ent[row * nch + ch] + dl * cs.s);
+        }
+      }
+    }
+    const double E = wave_sum(acc) * 0.69314718055994530942;  // log2 units -> nats
+    const double lnS = log(S);
+    const double H = lnS - E / S;
+    th = (float)(p.temp * (lnS + fmin(p.ln_eps, p.ln_delta - H)));
+  }
   if (lane == 0) {
     RowStat r;
     r.lmax = lmax;
     r.arg = arg;
     r.S = S;
-    rs[row] = r;
+    p.rowstats[row] = r;
+    if (p.trunc) p.rtheta[row] = th;
   }
 }
 
@@ -184,6 +214,7 @@ struct WalkShared {
   float qx[kMaxNodes];        // draft probability of node j's token at its parent's row
   double wx[kMaxNodes];       // deterministic siblings: unnormalised target mass of node j's token
   RowStat rs[kMaxNodes + 1];  // the request's rows: r = 0 root, r = 1 + j after node j
+  float th[kMaxNodes + 1];    // their thresholds of the allowed set (truncation)
   double csum[kMaxChunks];    // chunk masses of the distribution being drawn from
   double hsum[2 * kMaxChunks];// half-chunk masses of a residual pass
   double wtot[NW];            // per-wave sums of the draw's scan
@@ -228,17 +259,17 @@ __device__ __forceinline__ void half_load(HalfRegs& r, __amdgpu_buffer_rsrc_t lr
 // fp64. MASK drops float4s past the row's end (only the row's last half-chunk
 // needs it).
 template <bool MASK, bool TR>
-__device__ __forceinline__ double half_reduce(const HalfRegs& r, int V, int h, int lane, float lmax, float c,
+__device__ __forceinline__ double half_reduce(const HalfRegs& r, int V, int h, int lane, float lw, float lmax, float c,
                                               float ccS, float theta) {
   const int n4 = V >> 2;
   const int b4 = h * (kHalf / 4) + lane;
   double acc = 0.0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float w0 = allowed<TR>(residual_weight(r.l[i].x, r.q[i].x, lmax, c, ccS), r.l[i].x, lmax, theta);
-    const float w1 = allowed<TR>(residual_weight(r.l[i].y, r.q[i].y, lmax, c, ccS), r.l[i].y, lmax, theta);
-    const float w2 = allowed<TR>(residual_weight(r.l[i].z, r.q[i].z, lmax, c, ccS), r.l[i].z, lmax, theta);
-    const float w3 = allowed<TR>(residual_weight(r.l[i].w, r.q[i].w, lmax, c, ccS), r.l[i].w, lmax, theta);
+    const float w0 = allowed<TR>(residual_weight(r.l[i].x, r.q[i].x, lw, c, ccS), r.l[i].x, lmax, theta);
+    const float w1 = allowed<TR>(residual_weight(r.l[i].y, r.q[i].y, lw, c, ccS), r.l[i].y, lmax, theta);
+    const float w2 = allowed<TR>(residual_weight(r.l[i].z, r.q[i].z, lw, c, ccS), r.l[i].z, lmax, theta);
+    const float w3 = allowed<TR>(residual_weight(r.l[i].w, r.q[i].w, lw, c, ccS), r.l[i].w, lmax, theta);
     if (TR) {
       // every token in fp64: a deterministic candidate's weight can then be
       // taken back out of these sums with no fp32 rounding left behind
@@ -255,16 +286,16 @@ __device__ __forceinline__ double half_reduce(const HalfRegs& r, int V, int h, i
 }
 
 template <bool VEC, bool TR>
-__device__ __forceinline__ double half_mass(const HalfRegs& r, int V, int h, int lane, float lmax, float c, float ccS,
-                                            float theta) {
+__device__ __forceinline__ double half_mass(const HalfRegs& r, int V, int h, int lane, float lw, float lmax, float c,
+                                            float ccS, float theta) {
   // wave-uniform test: is the whole half-chunk inside the row?
-  return (h + 1) * kHalf <= V ? half_reduce<false, TR>(r, V, h, lane, lmax, c, ccS, theta)
-                              : half_reduce<true, TR>(r, V, h, lane, lmax, c, ccS, theta);
+  return (h + 1) * kHalf <= V ? half_reduce<false, TR>(r, V, h, lane, lw, lmax, c, ccS, theta)
+                              : half_reduce<true, TR>(r, V, h, lane, lw, lmax, c, ccS, theta);
 }
 
 template <bool TR>
-__device__ __forceinline__ double half_scalar(const float* lrow, const float* qrow, int V, int h, float lmax, float c,
-                                              float ccS, float theta, int lane) {
+__device__ __forceinline__ double half_scalar(const float* lrow, const float* qrow, int V, int h, float lw, float lmax,
+                                              float c, float ccS, float theta, int lane) {
   const int begin = h * kHalf, end = min(V, begin + kHalf);
   float lv[32], qv[32];
 #pragma unroll
@@ -276,7 +307,7 @@ __device__ __forceinline__ double half_scalar(const float* lrow, const float* qr
   double acc = 0.0;
 #pragma unroll
   for (int i = 0; i < 32; ++i)
-    acc += (double)allowed<TR>(residual_weight(lv[i], qv[i], lmax, c, ccS), lv[i], lmax, theta);
+    acc += (double)allowed<TR>(residual_weight(lv[i], qv[i], lw, c, ccS), lv[i], lmax, theta);
   return wave_sum(acc);
 }
 
@@ -284,9 +315,12 @@ __device__ __forceinline__ double half_scalar(const float* lrow, const float* qr
 // under max(0, p - cc q) (its two halves added in order); returns the total
 // (bitwise the same in every thread of every slice). pass_no counts the
 // request's passes from 1 (the barrier target and the buffer parity).
+// lw is the reference maximum of the p weight (the row maximum lmax; +inf
+// switches p off, so that with S = 1 and cc = -1 the masses are those of q);
+// membership in the allowed set is always decided against lmax.
 template <bool VEC, int NT, bool TR>
 __device__ __forceinline__ double residual_pass(WalkShared<NT>& sh, const float* lrow, const float* qrow, int V, int nch,
-                                                float lmax, float c, float theta, double S, double cc,
+                                                float lw, float lmax, float c, float theta, double S, double cc,
                                                 const Slices& sl, int pass_no) {
   constexpr int NW = NT / kWave;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -309,14 +343,14 @@ __device__ __forceinline__ double residual_pass(WalkShared<NT>& sh, const float*
       for (int h = gw; h < nh; h += 2 * GW) {
         const int h1 = h + GW;
         half_load(rb, lrs, qrs, h1, lane);
-        const double m0 = half_mass<VEC, TR>(ra, V, h, lane, lmax, c, ccS, theta) * invS;
+        const double m0 = half_mass<VEC, TR>(ra, V, h, lane, lw, lmax, c, ccS, theta) * invS;
         if (lane == 0) {
           sh.hsum[h] = m0;
           if (sl.n > 1) xb[h] = m0;
         }
         half_load(ra, lrs, qrs, h1 + GW, lane);
         if (h1 < nh) {
-          const double m1 = half_mass<VEC, TR>(rb, V, h1, lane, lmax, c, ccS, theta) * invS;
+          const double m1 = half_mass<VEC, TR>(rb, V, h1, lane, lw, lmax, c, ccS, theta) * invS;
           if (lane == 0) {
             sh.hsum[h1] = m1;
             if (sl.n > 1) xb[h1] = m1;
@@ -326,7 +360,7 @@ __device__ __forceinline__ double residual_pass(WalkShared<NT>& sh, const float*
     }
   } else {
     for (int h = gw; h < nh; h += GW) {
-      const double m = half_scalar<TR>(lrow, qrow, V, h, lmax, c, ccS, theta, lane) * invS;
+      const double m = half_scalar<TR>(lrow, qrow, V, h, lw, lmax, c, ccS, theta, lane) * invS;
       if (lane == 0) {
         sh.hsum[h] = m;
         if (sl.n > 1) xb[h] = m;
@@ -382,8 +416,8 @@ __device__ __forceinline__ double residual_pass(WalkShared<NT>& sh, const float*
 // siblings already tried); their weights count as zero.
 template <bool VEC, int NT, bool TR>
 __device__ __forceinline__ int draw_token(WalkShared<NT>& sh, const float* lrow, const float* qrow, int V, int nch,
-                                          int level, float lmax, float c, float theta, double S, double cc, double u,
-                                          double total, uint64_t removed) {
+                                          int level, float lw, float lmax, float c, float theta, double S, double cc,
+                                          double u, double total, uint64_t removed) {
   constexpr int NW = NT / kWave;
   constexpr int kDrawPerLane = kChunk / NT;
   static_assert(kDrawPerLane % 4 == 0, "the draw gives each lane whole float4 of a chunk");
@@ -438,7 +472,7 @@ __device__ __forceinline__ int draw_token(WalkShared<NT>& sh, const float* lrow,
     // weights of the distribution being drawn from (level 0: unnormalised p;
     // above: max(0, p - cc q) as the residual passes compute it)
     w[i] = level == 0 ? (double)allowed<TR>(target_weight(lv[i], lmax, c), lv[i], lmax, theta)
-                      : (double)allowed<TR>(residual_weight(lv[i], qv[i], lmax, c, ccS), lv[i], lmax, theta) * invS;
+                      : (double)allowed<TR>(residual_weight(lv[i], qv[i], lw, c, ccS), lv[i], lmax, theta) * invS;
   }
   if (removed) {  // the same in every thread
     uint32_t m = 0;
@@ -583,7 +617,7 @@ __global__ __launch_bounds__(NT) void walk_kernel(SampleParams p) {
       const RowStat rs = p.rowstats[r];
       double wx;
       if (TR) {
-        wx = (double)allowed<TR>(target_weight(lx, rs.lmax, p.c), lx, rs.lmax, p.theta);
+        wx = (double)allowed<TR>(target_weight(lx, rs.lmax, p.c), lx, rs.lmax, p.rtheta[r]);
       } else {
         const ChunkStat cs = p.stats[r * p.nch + sh.tok[tid] / kChunk];
         wx = cs.lmax == -INFINITY ? 0.0
@@ -593,7 +627,10 @@ __global__ __launch_bounds__(NT) void walk_kernel(SampleParams p) {
       sh.wx[tid] = wx;
     }
   }
-  if (tid <= T) sh.rs[tid] = p.rowstats[row0 + tid];
+  if (tid <= T) {
+    sh.rs[tid] = p.rowstats[row0 + tid];
+    sh.th[tid] = TR ? p.rtheta[row0 + tid] : -INFINITY;
+  }
   // the mode: sliced, or this slice alone, or another slice alone (leave)
   Slices sl{1, 0, nullptr, nullptr, p.status};
   if (sync) {
@@ -642,6 +679,7 @@ __global__ __launch_bounds__(NT) void walk_kernel(SampleParams p) {
     const float* lrow = p.logits + row * V;
     const float* qrow = (p.greedy || !p.q) ? nullptr : p.q + row * V;
     const RowStat st = sh.rs[r];
+    const float th = sh.th[r];  // this row's threshold of the allowed set (TR)
     // children of pos in increasing index: the same ballot in every wave
     const uint64_t kids = __ballot(lane < T && sh.par[lane] == pos);
     if (st.lmax == -INFINITY) {  // no finite logit: p is undefined here, stop without a token
@@ -663,13 +701,56 @@ __global__ __launch_bounds__(NT) void walk_kernel(SampleParams p) {
       continue;
     }
 
+    if (TR && p.rule == 3) {
+      // Truncation-based verification ([LOSSY] 3.2): the first child whose
+      // token is in the allowed set is accepted (the fp32 membership test of
+      // the truncation; no uniform). With every child rejected the token is
+      // drawn from q restricted to the set: a pass with the p weight switched
+      // off (reference maximum +inf) and cc S = -1 leaves q 1{x in A} masses.
+      // At a leaf it is drawn from the truncated target.
+      int accepted = -1;
+      for (uint64_t k = kids; k; k &= k - 1) {
+        const int ch = __ffsll((unsigned long long)k) - 1;
+        if (sh.lgx[ch] - st.lmax >= th) { accepted = ch; break; }
+        ++passes;  // rejections
+      }
+      accepted = __builtin_amdgcn_readfirstlane(accepted);
+      if (accepted >= 0) {
+        if (lead && tid == 0) { acc_nodes[depth] = accepted; toks_out[depth] = sh.tok[accepted]; }
+        ++depth;
+        pos = accepted;
+        continue;
+      }
+      int level = 0;
+      float lw = st.lmax;
+      double cc = 0.0, total = 0.0;
+      if (kids) {
+        total = residual_pass<VEC, NT, TR>(sh, lrow, qrow, p.V, p.nch, INFINITY, st.lmax, p.c, th, 1.0, -1.0, sl,
+                                           ++npass);
+        if (__builtin_amdgcn_readfirstlane(total > 0.0 ? 1 : 0)) {
+          level = 1;
+          lw = INFINITY;
+          cc = -1.0;
+        } else if (lead && tid == 0) {
+          flag(p.status, kStZeroResidual);
+        }
+      }
+      if (level == 0)
+        total = residual_pass<VEC, NT, TR>(sh, lrow, qrow, p.V, p.nch, st.lmax, st.lmax, p.c, th, 1.0, 0.0, sl,
+                                           ++npass);
+      if (!lead) return;  // the draw needs no other slice
+      const double uf = uniform01(p.seed, rid, 0u, 1u, p.step);
+      bonus = draw_token<VEC, NT, TR>(sh, lrow, qrow, p.V, p.nch, level, lw, st.lmax, p.c, th, 1.0, cc, uf, total, 0);
+      break;
+    }
+
     // The target here: p, or under min-p truncation p_Theta = p on the allowed
     // set renormalised by its mass S_A (one vocabulary pass at this position,
     // which also leaves the chunk masses of p_Theta in csum for a draw).
     double Srow = st.S;
     bool csum_ok = false;      // csum holds the chunk masses of the current level
     if (TR) {
-      Srow = residual_pass<VEC, NT, TR>(sh, lrow, qrow, p.V, p.nch, st.lmax, p.c, p.theta, 1.0, 0.0, sl, ++npass);
+      Srow = residual_pass<VEC, NT, TR>(sh, lrow, qrow, p.V, p.nch, st.lmax, st.lmax, p.c, th, 1.0, 0.0, sl, ++npass);
       csum_ok = true;
     }
     if (p.det) {
@@ -733,7 +814,8 @@ __global__ __launch_bounds__(NT) void walk_kernel(SampleParams p) {
         __syncthreads();
       }
       const double uf = uniform01(p.seed, rid, 0u, 1u, p.step);
-      bonus = draw_token<VEC, NT, TR>(sh, lrow, qrow, p.V, p.nch, 0, st.lmax, p.c, p.theta, Srow, 0.0, uf, M, removed);
+      bonus = draw_token<VEC, NT, TR>(sh, lrow, qrow, p.V, p.nch, 0, st.lmax, st.lmax, p.c, th, Srow, 0.0, uf, M,
+                                      removed);
       break;
     }
 
@@ -743,7 +825,7 @@ __global__ __launch_bounds__(NT) void walk_kernel(SampleParams p) {
     int accepted = -1;
     for (uint64_t k = kids; k; k &= k - 1) {
       const int ch = __ffsll((unsigned long long)k) - 1;
-      const float pf = allowed<TR>(target_prob(sh.lgx[ch], st.lmax, p.c, invS), sh.lgx[ch], st.lmax, p.theta);
+      const float pf = allowed<TR>(target_prob(sh.lgx[ch], st.lmax, p.c, invS), sh.lgx[ch], st.lmax, th);
       const double qv = (double)sh.qx[ch];
       const double P = level == 0 ? (double)pf : fmax(0.0, (double)pf - cc * qv) / M;
       // accept test u * den <= num: lossless (P, q), lenience (P, l q) or
@@ -756,7 +838,7 @@ __global__ __launch_bounds__(NT) void walk_kernel(SampleParams p) {
       // rejected: the next sibling is tested against the next residual level
       const double cn = cc + M;
       const double Mn =
-          residual_pass<VEC, NT, TR>(sh, lrow, qrow, p.V, p.nch, st.lmax, p.c, p.theta, Srow, cn, sl, ++npass);
+          residual_pass<VEC, NT, TR>(sh, lrow, qrow, p.V, p.nch, st.lmax, st.lmax, p.c, th, Srow, cn, sl, ++npass);
       ++passes;
       if (__builtin_amdgcn_readfirstlane(Mn > 0.0 ? 1 : 0)) {
         cc = cn;
@@ -788,14 +870,15 @@ __global__ __launch_bounds__(NT) void walk_kernel(SampleParams p) {
       total = st.S;
     } else {
       if (!csum_ok) {
-        residual_pass<VEC, NT, TR>(sh, lrow, qrow, p.V, p.nch, st.lmax, p.c, p.theta, Srow, cc, sl, ++npass);
+        residual_pass<VEC, NT, TR>(sh, lrow, qrow, p.V, p.nch, st.lmax, st.lmax, p.c, th, Srow, cc, sl, ++npass);
         ++passes;
       }
       total = M;
     }
     if (!lead) return;  // the draw needs no other slice: the rest are done
     const double uf = uniform01(p.seed, rid, 0u, 1u, p.step);
-    bonus = draw_token<VEC, NT, TR>(sh, lrow, qrow, p.V, p.nch, level, st.lmax, p.c, p.theta, Srow, cc, uf, total, 0);
+    bonus = draw_token<VEC, NT, TR>(sh, lrow, qrow, p.V, p.nch, level, st.lmax, st.lmax, p.c, th, Srow, cc, uf, total,
+                                    0);
     break;
   }
   if (lead && tid == 0) {
@@ -816,6 +899,13 @@ hipError_t launch_sampler(const SampleParams& p, bool vec4, hipStream_t stream, 
   if (p.greedy) {
     if (vec4) row_stats_kernel<true, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, p.status);
     else row_stats_kernel<true, false><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, p.status);
+  } else if (p.eta) {
+    if (vec4)
+      row_stats_kernel<false, true, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, p.status,
+                                                                    p.ent);
+    else
+      row_stats_kernel<false, false, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats,
+                                                                     p.status, p.ent);
   } else {
     if (vec4) row_stats_kernel<false, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, p.status);
     else row_stats_kernel<false, false><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, p.status);
@@ -823,9 +913,7 @@ hipError_t launch_sampler(const SampleParams& p, bool vec4, hipStream_t stream, 
   if (ev_stop) (void)hipEventRecord(ev_stop, stream);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  row_finalize_kernel<<<dim3((unsigned)((rows + 3) / 4)), 256, 0, stream>>>(p.stats, rows, p.nch, p.c, p.rowstats,
-                                                                            p.slices > 1 ? p.xcnt : nullptr,
-                                                                            p.B * kWalkSync);
+  row_finalize_kernel<<<dim3((unsigned)((rows + 3) / 4)), 256, 0, stream>>>(p, rows, p.B * kWalkSync);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (p.probs_out && !p.greedy) {

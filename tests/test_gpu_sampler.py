@@ -481,3 +481,143 @@ def test_lossy_rule_arguments_and_greedy():
     g1 = _gpu_sample(w, 0.0, rule="interpolation", rule_param=0.5)
     for k in ("accept_len", "accepted_nodes", "out_tokens"):
         assert torch.equal(g0[k], g1[k]), k
+
+
+# ---- eta truncation and truncation-based verification ([LOSSY] 2.3, 3.2) --------
+TRUNC_SMALL = ["c1_full", "c2_small", "c3_small", "c5_small_odd_vocab", "c4_small_cold", "max_tree_64"]
+SETS = {"min_p": {"min_p": 0.1}, "eta": {"eta": (0.05, 0.3)}}
+
+
+def _oracle_kw(w, T, md, **kw):
+    return oracle.verify(w["cu_nodes"], w["parent"], w["draft_tokens"].cpu().numpy(), w["logits"].cpu().numpy(),
+                         w["draft_probs"].cpu().numpy(), temperature=T, seed=w["seed"], max_depth=md, **kw)
+
+
+def _emitted_rows(w, r):
+    """(row, token) of every emitted token: accepted drafts and the bonus."""
+    acc = r["accept_len"].cpu().numpy()
+    nodes = r["accepted_nodes"].cpu().numpy()
+    toks = r["out_tokens"].cpu().numpy()
+    out = []
+    for b in range(w["B"]):
+        base = w["cu_nodes"][b] + b
+        pos = base
+        for d in range(acc[b] + 1):
+            out.append((pos, toks[b, d]))
+            if d < acc[b]:
+                pos = base + 1 + nodes[b, d]
+    return out
+
+
+@pytest.mark.parametrize("kind", sorted(SETS))
+@pytest.mark.parametrize("name", TRUNC_SMALL)
+def test_sampler_truncation_rule_small(name, kind):
+    cfg = SMALL[name]
+    w = generate(cfg, "cuda", attn=False)
+    T = cfg.temperature
+    print(f"[trunc-rule] {name} {kind} B={w['B']} N={w['N']} V={cfg.V}", flush=True)
+    r = _gpu_sample(w, T, rule="truncation", **SETS[kind])
+    ref = _oracle_kw(w, T, r["accepted_nodes"].shape[1], rule="truncation", **SETS[kind])
+    assert int(r["status"].item()) == 0, sv.status_names(int(r["status"].item()))
+    assert np.array_equal(r["uniforms"].cpu().numpy(), ref["uniforms"])
+    flagged = compare_walk(r, ref, w["B"], greedy=False)
+    print(f"  flagged near-ties: {flagged}/{w['B']}")
+    ok = ref["flag_depth"] < 0
+    assert np.array_equal(r["residual_passes"].cpu().numpy()[ok], ref["n_rejections"][ok])
+    if kind == "min_p":
+        _assert_in_allowed_set(w, r, T, 0.1)
+
+
+@pytest.mark.parametrize("siblings", ["sampled", "deterministic"])
+@pytest.mark.parametrize("name", TRUNC_SMALL)
+def test_sampler_eta_small(name, siblings):
+    cfg = SMALL[name]
+    w = generate(cfg, "cuda", attn=False)
+    T = cfg.temperature
+    print(f"[eta] {name} {siblings} B={w['B']} N={w['N']} V={cfg.V}", flush=True)
+    r = _gpu_sample(w, T, eta=(0.05, 0.3), siblings=siblings)
+    ref = _oracle_kw(w, T, r["accepted_nodes"].shape[1], eta=(0.05, 0.3), siblings=siblings)
+    assert int(r["status"].item()) == 0, sv.status_names(int(r["status"].item()))
+    flagged = compare_walk(r, ref, w["B"], greedy=False)
+    print(f"  flagged near-ties: {flagged}/{w['B']}")
+    ok = ref["flag_depth"] < 0
+    assert np.array_equal(r["residual_passes"].cpu().numpy()[ok], ref["n_rejections"][ok])
+
+
+@pytest.mark.parametrize("kind", sorted(SETS))
+@pytest.mark.parametrize("name", ["c3_eagle_tree", "c5_super_tree"])
+def test_sampler_truncation_rule_full_size(name, kind):
+    cfg = get_config(name)
+    w = generate(cfg, "cuda", attn=False)
+    print(f"[trunc-rule-full] {name} {kind} B={w['B']} N={w['N']} V={cfg.V}", flush=True)
+    r = _gpu_sample(w, cfg.temperature, rule="truncation", **SETS[kind])
+    ref = _oracle_kw(w, cfg.temperature, r["accepted_nodes"].shape[1], rule="truncation", **SETS[kind])
+    assert int(r["status"].item()) == 0
+    flagged = compare_walk(r, ref, w["B"], greedy=False)
+    print(f"  flagged near-ties: {flagged}/{w['B']}; mean accept_len {r['accept_len'].float().mean().item():.3f}")
+
+
+@pytest.mark.parametrize("name", ["c3_eagle_tree", "c5_super_tree"])
+def test_sampler_eta_full_size(name):
+    cfg = get_config(name)
+    w = generate(cfg, "cuda", attn=False)
+    print(f"[eta-full] {name} B={w['B']} N={w['N']} V={cfg.V}", flush=True)
+    r = _gpu_sample(w, cfg.temperature, eta=(0.05, 0.3))
+    ref = _oracle_kw(w, cfg.temperature, r["accepted_nodes"].shape[1], eta=(0.05, 0.3))
+    assert int(r["status"].item()) == 0
+    flagged = compare_walk(r, ref, w["B"], greedy=False)
+    print(f"  flagged near-ties: {flagged}/{w['B']}; mean accept_len {r['accept_len'].float().mean().item():.3f}")
+
+
+@pytest.mark.parametrize("kind", sorted(SETS))
+def test_gpu_truncation_rule_law(kind):
+    """Three i.i.d. siblings at V = 8: the emitted token follows q / Z_A(q) on
+    the allowed set ([LOSSY] 3.2) and one is accepted with probability
+    1 - (1 - Z_A(q))^3."""
+    V, n = 8, 1_000_000
+    sets = {"min_p": {"min_p": 0.2}, "eta": {"eta": (0.1, 0.4)}}[kind]
+    for s in range(701, 800):  # first seed with a proper allowed set
+        rng = np.random.default_rng(s)
+        lg, q = rows_from_probs(rng, V, 4, sharp=1.6, draft_noise=1.2)
+        p = softmax64(lg[0])
+        if kind == "min_p":
+            keep = p >= np.float32(0.2) * p.max()
+        else:
+            H = float(stats.entropy(p))
+            keep = p >= min(float(np.float32(0.1)), float(np.float32(0.4)) * math.exp(-H))
+        if 2 < keep.sum() < V:
+            break
+    parent = np.array([-1, -1, -1], np.int32)
+    cu, par, toks, logits, qq = replicated_batch(rng, parent, lg, q, n)
+    r = sv.sample(torch.from_numpy(cu).cuda(), torch.from_numpy(par).cuda(), torch.from_numpy(toks).cuda(),
+                  torch.from_numpy(logits).cuda(), torch.from_numpy(qq).cuda(), temperature=1.0, seed=4747,
+                  max_nodes=3, rule="truncation", **sets)
+    torch.cuda.synchronize()
+    q0 = q[0].astype(np.float64)
+    ZA = q0[keep].sum()
+    c = np.bincount(r["out_tokens"][:, 0].cpu().numpy(), minlength=V)
+    assert c[~keep].sum() == 0
+    assert stats.chisquare(c[keep], q0[keep] / ZA * n).pvalue > 1e-3
+    a = 1 - (1 - ZA) ** 3
+    freq = (r["accept_len"].cpu().numpy() >= 1).mean()
+    assert abs(freq - a) < 5 * math.sqrt(a * (1 - a) / n)
+
+
+def test_truncation_arguments():
+    cfg = SMALL["c2_small"]
+    w = generate(cfg, "cuda", attn=False)
+    with pytest.raises(sv.SpecVerifyError):  # no allowed set
+        _gpu_sample(w, 1.0, rule="truncation")
+    with pytest.raises(sv.SpecVerifyError):
+        _gpu_sample(w, 1.0, rule="truncation", min_p=0.2, siblings="deterministic")
+    with pytest.raises(sv.SpecVerifyError):
+        _gpu_sample(w, 1.0, eta=(0.1, 0.3), min_p=0.2)
+    with pytest.raises(sv.SpecVerifyError):
+        _gpu_sample(w, 1.0, eta=(0.1, 0.3), probs_out=True)
+    for bad in ((1.0, 0.3), (-0.1, 0.3), (0.1, 0.0), (0.1, 1.5)):
+        with pytest.raises(sv.SpecVerifyError):
+            _gpu_sample(w, 1.0, eta=bad)
+    g0 = _gpu_sample(w, 0.0)
+    g1 = _gpu_sample(w, 0.0, eta=(0.1, 0.3))
+    for k in ("accept_len", "accepted_nodes", "out_tokens"):
+        assert torch.equal(g0[k], g1[k]), k
