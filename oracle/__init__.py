@@ -70,6 +70,9 @@ def _load():
     lib.orc_ancestors.restype = i32
     lib.orc_attention.argtypes = [i32, i32, i32, i32, i32, P, P, P, i64, P, P, P, f64, i64, P, P, i32]
     lib.orc_attention.restype = i32
+    lib.orc_attention_paged.argtypes = [i32, i32, i32, i32, i32, P, P, P, i64, P, P, P, f64, i64, P, P, i32, P, i32,
+                                        i32, i64]
+    lib.orc_attention_paged.restype = i32
     lib.orc_target_probs.argtypes = [i32, P, f64, P]
     lib.orc_target_probs.restype = i32
     lib.orc_argmax.argtypes = [i32, P]
@@ -136,12 +139,15 @@ def ancestors(parent) -> tuple[np.ndarray, np.ndarray]:
 
 
 def attention(q, k, v, ctx_len, cu_nodes, parent, *, Hq, Hkv, scale=None, dtype="f32", items=None,
-              nthreads=None) -> np.ndarray:
+              nthreads=None, block_table=None) -> np.ndarray:
     """fp64 tree-masked GQA attention.
 
     q [N,Hq,D], k/v [B,Hkv,Lcap,D] as float32 arrays (dtype='f32') or as uint16
     bf16 bit patterns (dtype='bf16'). items: optional int64 [n,2] of
     (packed node, q head); returns [n, D] then, else [N, Hq, D].
+    block_table: int32 [B, max_blocks] for paged caches; k/v are then pools
+    [num_blocks, Hkv, block_size, D] and slot t of request b sits in block
+    block_table[b, t // block_size] at row t % block_size.
     """
     q = np.ascontiguousarray(q)
     k = np.ascontiguousarray(k)
@@ -151,8 +157,15 @@ def attention(q, k, v, ctx_len, cu_nodes, parent, *, Hq, Hkv, scale=None, dtype=
         assert q.dtype == np.float32 and k.dtype == np.float32 and v.dtype == np.float32
     else:
         assert q.dtype == np.uint16 and k.dtype == np.uint16 and v.dtype == np.uint16
-    B = int(k.shape[0])
-    Lcap, D = int(k.shape[2]), int(k.shape[3])
+    D = int(k.shape[3])
+    if block_table is None:
+        B, Lcap = int(k.shape[0]), int(k.shape[2])
+        bt, bs, mb, nb = None, 0, 0, 0
+    else:
+        bt = np.ascontiguousarray(block_table, dtype=np.int32)
+        B, mb = int(bt.shape[0]), int(bt.shape[1])
+        bs, nb = int(k.shape[2]), int(k.shape[0])
+        Lcap = mb * bs
     N = int(q.shape[0])
     if scale is None:
         scale = 1.0 / np.sqrt(D)
@@ -168,9 +181,9 @@ def attention(q, k, v, ctx_len, cu_nodes, parent, *, Hq, Hkv, scale=None, dtype=
         n_items = items.shape[0]
         out = np.zeros((n_items, D), dtype=np.float64)
         it_ptr = _ptr(items)
-    rc = _load().orc_attention(B, Hq, Hkv, D, code, _ptr(q), _ptr(k), _ptr(v), Lcap, _ptr(ctx), _ptr(cu),
-                               _ptr(par), float(scale), n_items, it_ptr, _ptr(out),
-                               nthreads or _default_threads())
+    rc = _load().orc_attention_paged(B, Hq, Hkv, D, code, _ptr(q), _ptr(k), _ptr(v), Lcap, _ptr(ctx), _ptr(cu),
+                                     _ptr(par), float(scale), n_items, it_ptr, _ptr(out),
+                                     nthreads or _default_threads(), _ptr(bt), bs, mb, nb)
     if rc != 0:
         raise ValueError("oracle attention: bad packing or tree")
     return out

@@ -144,7 +144,22 @@ typedef struct {
   const int64_t* items; /* pairs (packed node, q head) */
   double* out;
   int* err;
+  /* paged caches (block_table != NULL): pools [num_blocks, Hkv, block_size, D] */
+  const int32_t* block_table; /* [B, max_blocks] */
+  int block_size, max_blocks;
+  int64_t num_blocks;
 } orc_attn_ctx;
+
+/* Element index of dim 0 of cache slot t of request b, KV head g: the
+ * contiguous layout [B, Hkv, Lcap, D], or through the block table, where slot
+ * t of request b sits in block block_table[b, t / block_size] at row
+ * t % block_size. -1 if the block id is out of range.                      */
+static int64_t orc_slot_index(const orc_attn_ctx* c, int b, int64_t g, int64_t t) {
+  if (!c->block_table) return (((int64_t)b * c->Hkv + g) * c->Lcap + t) * c->D;
+  int64_t blk = c->block_table[(int64_t)b * c->max_blocks + t / c->block_size];
+  if (blk < 0 || blk >= c->num_blocks) return -1;
+  return ((blk * c->Hkv + g) * c->block_size + t % c->block_size) * c->D;
+}
 
 /* [SD] "Tree Attention Mask Mechanics" + "Interaction with Advanced
  * Attention Architectures (GQA & MLA)": one output vector of one query head
@@ -181,12 +196,15 @@ static void orc_attn_item(void* vctx, int64_t it) {
   for (int64_t t = 0; t < L; ++t) slot[t] = t;
   for (int i = 0; i < nvis; ++i) slot[L + i] = L + visible[i];
   int64_t qbase = (n * c->Hq + h) * c->D;
-  int64_t kvbase = ((int64_t)b * c->Hkv + g) * c->Lcap * c->D;
+  for (int64_t t = 0; t < nkeys; ++t) {
+    slot[t] = orc_slot_index(c, b, g, slot[t]); /* slot -> element index */
+    if (slot[t] < 0) { free(s); free(slot); *c->err = 1; return; }
+  }
   double m = -INFINITY;
   for (int64_t t = 0; t < nkeys; ++t) {
     double acc = 0.0;
     for (int d = 0; d < c->D; ++d)
-      acc += orc_load(c->q, c->dtype, qbase + d) * orc_load(c->k, c->dtype, kvbase + slot[t] * c->D + d);
+      acc += orc_load(c->q, c->dtype, qbase + d) * orc_load(c->k, c->dtype, slot[t] + d);
     s[t] = c->scale * acc;
     if (s[t] > m) m = s[t];
   }
@@ -198,7 +216,7 @@ static void orc_attn_item(void* vctx, int64_t it) {
   for (int d = 0; d < c->D; ++d) o[d] = 0.0;
   for (int64_t t = 0; t < nkeys; ++t) {
     double w = s[t] / denom;
-    for (int d = 0; d < c->D; ++d) o[d] += w * orc_load(c->v, c->dtype, kvbase + slot[t] * c->D + d);
+    for (int d = 0; d < c->D; ++d) o[d] += w * orc_load(c->v, c->dtype, slot[t] + d);
   }
   free(s);
   free(slot);
@@ -206,11 +224,15 @@ static void orc_attn_item(void* vctx, int64_t it) {
 
 /* Attention for a list of (packed node, query head) pairs `items` [n_items,2]
  * (or, if items is NULL, for every node and head in order); out [n_items, D].
- * dtype 0 = fp32 inputs, 1 = bf16 inputs. Returns 0, or 1 on bad packing. */
-int orc_attention(int B, int Hq, int Hkv, int D, int dtype, const void* q, const void* k, const void* v,
-                  int64_t Lcap, const int32_t* ctx_len, const int32_t* cu_nodes, const int32_t* parent,
-                  double scale, int64_t n_items, const int64_t* items, double* out, int nthreads) {
+ * dtype 0 = fp32 inputs, 1 = bf16 inputs. block_table != NULL reads paged
+ * caches (see orc_slot_index; Lcap = max_blocks * block_size). Returns 0, or
+ * 1 on bad packing or a block id out of range.                            */
+int orc_attention_paged(int B, int Hq, int Hkv, int D, int dtype, const void* q, const void* k, const void* v,
+                        int64_t Lcap, const int32_t* ctx_len, const int32_t* cu_nodes, const int32_t* parent,
+                        double scale, int64_t n_items, const int64_t* items, double* out, int nthreads,
+                        const int32_t* block_table, int block_size, int max_blocks, int64_t num_blocks) {
   if (Hkv <= 0 || Hq % Hkv != 0 || D <= 0) return 1;
+  if (block_table && (block_size <= 0 || max_blocks <= 0 || Lcap != (int64_t)block_size * max_blocks)) return 1;
   int64_t* all = NULL;
   if (!items) {
     int64_t N = cu_nodes[B];
@@ -225,10 +247,18 @@ int orc_attention(int B, int Hq, int Hkv, int D, int dtype, const void* q, const
     items = all;
   }
   int err = 0;
-  orc_attn_ctx c = {B, Hq, Hkv, D, dtype, q, k, v, Lcap, ctx_len, cu_nodes, parent, scale, items, out, &err};
+  orc_attn_ctx c = {B, Hq, Hkv, D, dtype, q, k, v, Lcap, ctx_len, cu_nodes, parent, scale, items, out, &err,
+                    block_table, block_size, max_blocks, num_blocks};
   orc_parallel_for(n_items, nthreads, orc_attn_item, &c);
   free(all);
   return err;
+}
+
+int orc_attention(int B, int Hq, int Hkv, int D, int dtype, const void* q, const void* k, const void* v,
+                  int64_t Lcap, const int32_t* ctx_len, const int32_t* cu_nodes, const int32_t* parent,
+                  double scale, int64_t n_items, const int64_t* items, double* out, int nthreads) {
+  return orc_attention_paged(B, Hq, Hkv, D, dtype, q, k, v, Lcap, ctx_len, cu_nodes, parent, scale, n_items, items,
+                             out, nthreads, NULL, 0, 0, 0);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -6,7 +6,8 @@ arithmetic and is the one piece of code shared by the GPU library's tests and
 bench on one side and the oracle on the other.
 """
 from .configs import CONFIGS, C4_BUCKETS, WorkloadConfig, get_config, scaled
-from .gen import (chain_tree, eagle_tree, generate, super_tree_sizes, super_tree_parents, poison_unused_slots)
+from .gen import (chain_tree, eagle_tree, generate, super_tree_sizes, super_tree_parents, poison_unused_slots,
+                  to_paged)
 
 __all__ = ["CONFIGS", "C4_BUCKETS", "WorkloadConfig", "get_config", "scaled", "chain_tree", "eagle_tree",
            "generate", "super_tree_sizes", "super_tree_parents", "poison_unused_slots"]

@@ -186,3 +186,46 @@ def generate(cfg: WorkloadConfig, device="cpu", *, attn: bool = True, sample: bo
         out["draft_probs"] = probs
         out["draft_tokens"] = toks.to(torch.int32)
     return out
+
+
+def to_paged(k_cache, v_cache, block_size: int, rng: np.random.Generator, spare_blocks: int = 3,
+             share_prefix_blocks: int = 0):
+    """Lay contiguous caches [B, Hkv, Lcap, D] out as paged pools.
+
+    Each request's Lcap slots are cut into Lcap / block_size blocks that land
+    in a shuffled pool of B * max_blocks + spare_blocks blocks; the spare
+    blocks are filled with NaN, so that a read through a wrong block id shows.
+    share_prefix_blocks > 0 makes every request's first blocks the same pool
+    blocks as request 0's (a shared prompt prefix): request b's data in those
+    slots is then request 0's. Works on numpy arrays and torch tensors.
+    Returns (k_pool, v_pool, block_table int32 [B, max_blocks]).
+    """
+    B, Hkv, Lcap, D = k_cache.shape
+    assert Lcap % block_size == 0
+    mb = Lcap // block_size
+    nblk = B * mb + spare_blocks
+    perm = rng.permutation(nblk)[: B * mb].reshape(B, mb).astype(np.int32)
+    if share_prefix_blocks:
+        perm[1:, :share_prefix_blocks] = perm[0, :share_prefix_blocks]
+    is_torch = isinstance(k_cache, torch.Tensor)
+
+    def pool_of(x):
+        if is_torch:
+            pool = torch.full((nblk, Hkv, block_size, D), float("nan"), dtype=x.dtype, device=x.device)
+            blocks = x.reshape(B, Hkv, mb, block_size, D).permute(0, 2, 1, 3, 4)
+            for b in range(B):
+                pool[torch.as_tensor(perm[b], device=x.device).long()] = blocks[b]
+            if share_prefix_blocks:
+                pool[torch.as_tensor(perm[0, :share_prefix_blocks], device=x.device).long()] = \
+                    blocks[0, :share_prefix_blocks]
+            return pool
+        fill = np.uint16(0x7FC0) if x.dtype == np.uint16 else np.nan
+        pool = np.full((nblk, Hkv, block_size, D), fill, dtype=x.dtype)
+        blocks = x.reshape(B, Hkv, mb, block_size, D).transpose(0, 2, 1, 3, 4)
+        for b in range(B):
+            pool[perm[b]] = blocks[b]
+        if share_prefix_blocks:
+            pool[perm[0, :share_prefix_blocks]] = blocks[0, :share_prefix_blocks]
+        return pool
+
+    return pool_of(k_cache), pool_of(v_cache), perm
