@@ -120,6 +120,9 @@ def parse_args():
     ap.add_argument("--siblings", choices=["sampled", "deterministic"], default="sampled",
                     help="sampled: draft tokens are draws from q; deterministic: the top-k of q as fixed "
                          "candidates, verified by the deterministic-candidate rule (q is not read)")
+    ap.add_argument("--paged", type=int, default=0, metavar="BLOCK",
+                    help="lay the KV caches out as a shuffled pool of BLOCK-slot blocks read through a block "
+                         "table (BLOCK a multiple of 64; 0 = contiguous caches)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES three times (calibrates the HBM "
                          "byte counters of rocprofv3 against a kernel of known traffic) and exit")
@@ -298,14 +301,33 @@ def main():
     set_bytes = attention_bytes(w) + 8 * w["V"] * (w["N"] + w["B"])
     n_sets = max(1, min(MAX_INPUT_SETS, math.ceil(ROTATE_BYTES / set_bytes)))
     sets = [w] + [generate(cfg, dev, candidates=cand) for _ in range(n_sets - 1)]
+    if args.paged:
+        import numpy as np
+
+        from workloads import to_paged
+        bs = args.paged
+        for i, x in enumerate(sets):
+            k, v = x["k_cache"], x["v_cache"]
+            B_, H_, Lc, D_ = k.shape
+            Lp = (Lc + bs - 1) // bs * bs
+            if Lp != Lc:
+                pad = torch.zeros((B_, H_, Lp - Lc, D_), dtype=k.dtype, device=dev)
+                k, v = torch.cat([k, pad], dim=2), torch.cat([v, pad], dim=2)
+            kp, vp, bt = to_paged(k, v, bs, np.random.default_rng(77 + i), spare_blocks=0)
+            x["k_pool"], x["v_pool"], x["block_table"] = kp, vp, torch.from_numpy(bt).to(dev)
+            del k, v
     torch.cuda.synchronize()
 
     stream = torch.cuda.Stream()  # default priority
     calls = []
     with torch.cuda.stream(stream):
         for x in sets:
-            a = sv.AttnCall(x["q"], x["k_cache"], x["v_cache"], x["ctx_len_t"], x["cu_nodes_t"], parent=x["parent_t"],
-                            max_nodes=x["max_T"])
+            if args.paged:
+                a = sv.AttnCall(x["q"], x["k_pool"], x["v_pool"], x["ctx_len_t"], x["cu_nodes_t"],
+                                parent=x["parent_t"], max_nodes=x["max_T"], block_table=x["block_table"])
+            else:
+                a = sv.AttnCall(x["q"], x["k_cache"], x["v_cache"], x["ctx_len_t"], x["cu_nodes_t"],
+                                parent=x["parent_t"], max_nodes=x["max_T"])
             s = sv.SampleCall(a.keep["cu"], x["parent_t"], x["draft_tokens"], x["logits"],
                               None if det else x["draft_probs"], temperature=cfg.temperature, seed=x["seed"],
                               max_nodes=x["max_T"], residual_passes=True, min_p=args.min_p,
@@ -410,6 +432,7 @@ def main():
                    "temperature": cfg.temperature, **({"min_p": args.min_p} if args.min_p > 0 else {}),
                    **({"siblings": "deterministic (top-k of q)"} if det else {}),
                    **({"eta": list(args.eta)} if args.eta else {}),
+                   **({"kv_layout": f"paged, {args.paged}-slot blocks"} if args.paged else {}),
                    **({"rule": args.rule, "rule_param": args.rule_param} if args.rule in ("lenience", "interpolation")
                       else {"rule": args.rule} if args.rule == "truncation" else {})},
         "roofline": roofline,

@@ -81,6 +81,8 @@ typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
 #define SV_STATUS_CTX_RANGE      0x20 /* ctx_len[b] < 0 or ctx_len[b] + T_b > Lcap: request skipped */
 #define SV_STATUS_SYNC           0x40 /* a sampler workgroup gave up waiting for the other workgroups of its request
                                          (not expected: they agree to cooperate only once all are running) */
+#define SV_STATUS_BLOCK_RANGE    0x80 /* paged caches: a block id outside [0, num_blocks): its keys read as zeros,
+                                         the request's outputs are undefined, nothing is read out of bounds */
 
 /* ------------------------------------------------------------------------ */
 /* Tree-masked GQA attention ([SD] "Tree Attention Mask Mechanics"; GQA as in
@@ -115,6 +117,20 @@ typedef struct {
   int32_t* status;     /* optional device word for SV_STATUS_* bits           */
   void* prof_start;    /* optional hipEvent_t recorded right before the        */
   void* prof_stop;     /*   attention kernel / right after it (measurement)   */
+  /* Paged caches (optional; the layout of PagedAttention-style engines, which
+   * [SD] "Tree Attention Mask Mechanics" names as the kernels a tree mask is
+   * handed to). block_table == NULL: k_cache / v_cache are [B, Hkv, Lcap, D].
+   * Otherwise they are pools [num_blocks, Hkv, block_size, D], and slot t of
+   * request b (committed context and draft slots alike) sits in block
+   * block_table[b * max_blocks + t / block_size] at row t % block_size;
+   * Lcap must equal max_blocks * block_size. Blocks may be shared between
+   * requests (a common prefix). block_size is a multiple of 64 (one 64-key
+   * tile never spans two blocks). An id outside [0, num_blocks) sets
+   * SV_STATUS_BLOCK_RANGE.                                                 */
+  const int32_t* block_table; /* [B, max_blocks] device memory, or NULL     */
+  int32_t block_size;
+  int32_t max_blocks;
+  int64_t num_blocks;
 } sv_attn_args;
 
 /* ------------------------------------------------------------------------ */

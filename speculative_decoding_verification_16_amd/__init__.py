@@ -27,7 +27,7 @@ SV_F32, SV_BF16 = 0, 1
 SIBLINGS = {"sampled": 0, "deterministic": 1}  # sv_siblings
 RULES = {"lossless": 0, "lenience": 1, "interpolation": 2, "truncation": 3}  # sv_rule
 STATUS_BITS = {0x01: "TREE_INVALID", 0x02: "PACKING", 0x04: "TOKEN_RANGE", 0x08: "NONFINITE",
-               0x10: "ZERO_RESIDUAL", 0x20: "CTX_RANGE", 0x40: "SYNC"}
+               0x10: "ZERO_RESIDUAL", 0x20: "CTX_RANGE", 0x40: "SYNC", 0x80: "BLOCK_RANGE"}
 
 _P = ctypes.c_void_p
 _i32, _i64, _u32, _u64, _f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_float
@@ -37,7 +37,8 @@ class SvAttnArgs(ctypes.Structure):
     _fields_ = [("B", _i32), ("total_nodes", _i32), ("max_nodes", _i32), ("Hq", _i32), ("Hkv", _i32), ("D", _i32),
                 ("dtype", _i32), ("q", _P), ("k_cache", _P), ("v_cache", _P), ("Lcap", _i64), ("ctx_len", _P),
                 ("cu_nodes", _P), ("parent", _P), ("anc_mask", _P), ("scale", _f32), ("num_splits", _i32),
-                ("out", _P), ("status", _P), ("prof_start", _P), ("prof_stop", _P)]
+                ("out", _P), ("status", _P), ("prof_start", _P), ("prof_stop", _P), ("block_table", _P),
+                ("block_size", _i32), ("max_blocks", _i32), ("num_blocks", _i64)]
 
 
 class SvSampleArgs(ctypes.Structure):
@@ -125,7 +126,9 @@ class AttnCall:
     """Prepared spec_verify_attn call (outputs and workspace allocated once)."""
 
     def __init__(self, q, k_cache, v_cache, ctx_len, cu_nodes, *, parent=None, anc_mask=None, max_nodes=0,
-                 scale=0.0, num_splits=0, out=None, status=None):
+                 scale=0.0, num_splits=0, out=None, status=None, block_table=None):
+        """block_table: int32 [B, max_blocks] for paged caches; k_cache and
+        v_cache are then pools [num_blocks, Hkv, block_size, D]."""
         load_library()
         dev = q.device
         assert q.is_cuda and q.dim() == 3 and k_cache.dim() == 4 and v_cache.shape == k_cache.shape
@@ -135,8 +138,15 @@ class AttnCall:
         N, Hq, D = q.shape
         B, Hkv, Lcap, D2 = k_cache.shape
         assert D == D2
+        if block_table is not None:
+            block_table = _dev_i32(block_table, dev)
+            assert block_table.dim() == 2
+            num_blocks, block_size = B, Lcap
+            B, max_blocks = block_table.shape
+            Lcap = max_blocks * block_size
         self.keep = {"q": q, "k": k_cache, "v": v_cache, "ctx": _dev_i32(ctx_len, dev), "cu": _dev_i32(cu_nodes, dev),
-                     "parent": None if parent is None else _dev_i32(parent, dev), "anc": anc_mask}
+                     "parent": None if parent is None else _dev_i32(parent, dev), "anc": anc_mask,
+                     "block_table": block_table}
         if anc_mask is not None:
             assert anc_mask.dtype == torch.int64 and anc_mask.is_contiguous()
         self.out = out if out is not None else torch.empty((N, Hq, D), dtype=torch.float32, device=dev)
@@ -151,6 +161,9 @@ class AttnCall:
         a.anc_mask = _ptr(anc_mask)
         a.scale, a.num_splits = float(scale), int(num_splits)
         a.out, a.status = _ptr(self.out), _ptr(self.status)
+        if block_table is not None:
+            a.block_table, a.block_size, a.max_blocks, a.num_blocks = _ptr(block_table), block_size, max_blocks, \
+                num_blocks
         self.args = a
         lib = load_library()
         self.ws_bytes = lib.spec_verify_workspace_size(ctypes.byref(a), None)

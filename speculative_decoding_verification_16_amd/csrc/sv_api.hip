@@ -39,12 +39,23 @@ sv_status check_attn(const sv_attn_args* a) {
   if (a->D != 64 && a->D != 128) return fail(SV_ERR_UNSUPPORTED, "head dim D must be 64 or 128");
   if (a->dtype != SV_F32 && a->dtype != SV_BF16) return fail(SV_ERR_INVALID_ARG, "dtype must be SV_F32 or SV_BF16");
   if (a->Lcap < 1 || a->Lcap > (1ll << 24)) return fail(SV_ERR_INVALID_ARG, "Lcap must be in [1, 2^24]");
+  if (a->block_table) {
+    if (a->block_size <= 0 || a->block_size % 64 != 0)
+      return fail(SV_ERR_UNSUPPORTED, "block_size must be a positive multiple of 64");
+    if (a->max_blocks <= 0 || (int64_t)a->max_blocks * a->block_size != a->Lcap)
+      return fail(SV_ERR_INVALID_ARG, "paged caches need max_blocks > 0 and Lcap == max_blocks * block_size");
+    if (a->num_blocks <= 0) return fail(SV_ERR_INVALID_ARG, "num_blocks must be > 0");
+    if (!aligned(a->block_table, 4)) return fail(SV_ERR_INVALID_ARG, "block_table must be 4-byte aligned");
+  }
   if (!(a->scale >= 0.f) || isinf(a->scale)) return fail(SV_ERR_INVALID_ARG, "scale must be finite and >= 0");
   if (a->num_splits < 0) return fail(SV_ERR_INVALID_ARG, "num_splits < 0");
   if ((int64_t)a->total_nodes * a->Hq * a->D >= (1ll << 31))
     return fail(SV_ERR_UNSUPPORTED, "N * Hq * D must stay below 2^31");
+  // contiguous caches are addressed per (request, KV head) with 32-bit offsets;
+  // paged ones per 64-key tile
   const int64_t kv_head_bytes = a->Lcap * a->D * (a->dtype == SV_BF16 ? 2 : 4);
-  if (kv_head_bytes >= (1ll << 31)) return fail(SV_ERR_UNSUPPORTED, "Lcap * D * element size must stay below 2^31");
+  if (!a->block_table && kv_head_bytes >= (1ll << 31))
+    return fail(SV_ERR_UNSUPPORTED, "Lcap * D * element size must stay below 2^31");
   if (a->B == 0) return SV_OK;
   if (!a->ctx_len || !a->cu_nodes) return fail(SV_ERR_INVALID_ARG, "ctx_len and cu_nodes are required");
   if (a->total_nodes == 0) return SV_OK;
@@ -268,6 +279,10 @@ sv_status run_attn(const sv_attn_args* a, char* ws, const WsLayout& w, hipStream
   const float scale = a->scale > 0.f ? a->scale : (float)(1.0 / sqrt((double)a->D));
   p.scale_log2 = (float)((double)scale * 1.4426950408889634);
   p.status = a->status;
+  p.block_table = a->block_table;
+  p.block_size = a->block_table ? a->block_size : 0;
+  p.max_blocks = a->block_table ? a->max_blocks : 0;
+  p.num_blocks = a->block_table ? a->num_blocks : 0;
   hipError_t e = sv::launch_attn_prep(p, pl, a->parent, w_anc, st);
   if (e != hipSuccess) return hip_fail(e, "attention prep launch");
   e = sv::launch_attention(p, pl, a->dtype == SV_BF16, st, (hipEvent_t)a->prof_start,

@@ -118,6 +118,33 @@ __device__ __forceinline__ bool decode_block(const AttnParams& p, int lin, int& 
   return job < p.n_jobs;
 }
 
+// Paged caches: element offset of logical slot t (a multiple of 64, so that
+// its 64-key tile lies in one block) of request b, KV head g, in the pool;
+// ok = false (flagged) for a block id out of range. t is uniform over the
+// workgroup, so the table read is a scalar load.
+__device__ __forceinline__ int64_t paged_slot(const AttnParams& p, int b, int g, int t, int D, bool& ok) {
+  const int blk = p.block_table[(int64_t)b * p.max_blocks + t / p.block_size];
+  ok = blk >= 0 && (int64_t)blk < p.num_blocks;
+  if (!ok) {
+    if (threadIdx.x == 0) flag(p.status, kStBlock);
+    return 0;
+  }
+  return (((int64_t)blk * p.Hkv + g) * p.block_size + t % p.block_size) * D;
+}
+
+// Buffer resource over the keys [t, min(t + 64, ke)) of a paged pool (pool:
+// bf16 or fp32 elements of ESZ bytes): it reads zeros past ke, for a tile past
+// the range and for a block id out of range, without touching memory.
+template <int ESZ>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t paged_tile(const AttnParams& p, const void* pool, int b, int g,
+                                                             int t, int ke, int D) {
+  const int valid = min(64, ke - t);
+  bool ok = false;
+  const int64_t eo = valid > 0 ? paged_slot(p, b, g, t, D, ok) : 0;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)pool + eo * ESZ), (short)0,
+                                           ok ? valid * D * ESZ : 0, 0x00020000);
+}
+
 // Work list, built by one workgroup of 1024 threads: thread t handles XCD
 // class x = t % 8 and,
 // per round of 128 jobs of that class, the job 8 (m0 + t / 8) + x. A job of
@@ -202,7 +229,7 @@ __global__ __launch_bounds__(1024) void attn_prep_kernel(AttnParams p, const int
 // Decode-shaped attention is bound by memory latency x bytes in flight per
 // CU, and measured on MI355X several independent workgroups per CU (WPE
 // waves per SIMD) hide it better than a deeper ring in fewer workgroups.
-template <int D, int NBUF, int NW, int RBW, int WPE = 2>
+template <int D, int NBUF, int NW, int RBW, int WPE = 2, bool PAGED = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE)))
 void attn_mfma_kernel(AttnParams p) {
   constexpr int NT = 64 * NW;        // threads
@@ -276,7 +303,7 @@ void attn_mfma_kernel(AttnParams p) {
     return;
   }
 
-  const int64_t head_off = ((int64_t)b * p.Hkv + g) * p.Lcap * D;
+  const int64_t head_off = PAGED ? 0 : ((int64_t)b * p.Hkv + g) * p.Lcap * D;  // paged: per tile instead
   const uint16_t* kbase = (const uint16_t*)p.k + head_off;
   const uint16_t* vbase = (const uint16_t*)p.v + head_off;
 
@@ -312,14 +339,17 @@ void attn_mfma_kernel(AttnParams p) {
 
   // prologue: the first NBUF tiles. Every load is non-temporal: this kernel
   // serves at most 64 rows per KV head, so each key range has one reader
-  // (measured on MI355X: 11 % faster on 32k-token contexts).
+  // (measured on MI355X: 11 % faster on 32k-token contexts). Paged caches:
+  // one resource per tile, over that tile's block rows.
 #pragma unroll
   for (int s = 0; s < NBUF; ++s) {
-    const int so = (kb + s * KT) * D * 2;
+    const int so = PAGED ? 0 : (kb + s * KT) * D * 2;
+    const __amdgpu_buffer_rsrc_t kr = PAGED ? paged_tile<2>(p, p.k, b, g, kb + s * KT, ke, D) : krs;
+    const __amdgpu_buffer_rsrc_t vr = PAGED ? paged_tile<2>(p, p.v, b, g, kb + s * KT, ke, D) : vrs;
 #pragma unroll
     for (int i = 0; i < PER_THREAD; ++i) {
-      kreg[s][i] = __builtin_amdgcn_raw_buffer_load_b128(krs, koff[i], so, kAuxNT);
-      vreg[s][i] = __builtin_amdgcn_raw_buffer_load_b128(vrs, koff[i], so, kAuxNT);
+      kreg[s][i] = __builtin_amdgcn_raw_buffer_load_b128(kr, koff[i], so, kAuxNT);
+      vreg[s][i] = __builtin_amdgcn_raw_buffer_load_b128(vr, koff[i], so, kAuxNT);
     }
     // keep the slots' loads in slot order, as the ring refills them: the
     // wait before writing slot s can then leave the later slots in flight
@@ -341,11 +371,13 @@ void attn_mfma_kernel(AttnParams p) {
       __syncthreads();
       // refill this ring slot with the tile NBUF positions ahead
       {
-        const int so = (t0 + NBUF * KT) * D * 2;
+        const int so = PAGED ? 0 : (t0 + NBUF * KT) * D * 2;
+        const __amdgpu_buffer_rsrc_t kr = PAGED ? paged_tile<2>(p, p.k, b, g, t0 + NBUF * KT, ke, D) : krs;
+        const __amdgpu_buffer_rsrc_t vr = PAGED ? paged_tile<2>(p, p.v, b, g, t0 + NBUF * KT, ke, D) : vrs;
 #pragma unroll
         for (int i = 0; i < PER_THREAD; ++i) {
-          kreg[s][i] = __builtin_amdgcn_raw_buffer_load_b128(krs, koff[i], so, kAuxNT);
-          vreg[s][i] = __builtin_amdgcn_raw_buffer_load_b128(vrs, koff[i], so, kAuxNT);
+          kreg[s][i] = __builtin_amdgcn_raw_buffer_load_b128(kr, koff[i], so, kAuxNT);
+          vreg[s][i] = __builtin_amdgcn_raw_buffer_load_b128(vr, koff[i], so, kAuxNT);
         }
       }
       // past the range (last ring round): the slot was only cycled; waves
@@ -505,7 +537,7 @@ void attn_mfma_kernel(AttnParams p) {
 // V^T operand is read in the same key order with transposed LDS reads.
 // O^T per 32-dim block db: lane l holds dims 32 db + 8 (v / 4) + 4 h + v % 4
 // of row l % 32.
-template <int D, int NW, int WPE>
+template <int D, int NW, int WPE, bool PAGED = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE)))
 void attn_mfma32_kernel(AttnParams p) {
   constexpr int NT = 64 * NW;        // threads
@@ -584,7 +616,7 @@ void attn_mfma32_kernel(AttnParams p) {
     return;
   }
 
-  const int64_t head_off = ((int64_t)b * p.Hkv + g) * p.Lcap * D;
+  const int64_t head_off = PAGED ? 0 : ((int64_t)b * p.Hkv + g) * p.Lcap * D;  // paged: per tile instead
   const uint16_t* kbase = (const uint16_t*)p.k + head_off;
   const uint16_t* vbase = (const uint16_t*)p.v + head_off;
   // the resources cover exactly keys [0, ke): a key past the split end reads
@@ -614,8 +646,13 @@ void attn_mfma32_kernel(AttnParams p) {
   // on MI355X: non-temporal everywhere slowed the batch-256 super tree by
   // 6 %, whose larger trees have two to four row groups.)
   const bool stream_once = R <= ROWS;
-  auto dma = [&](__amdgpu_buffer_rsrc_t rs, const int* off, uint16_t* dst, int t) {
-    const int tb = (kb + t * KT) * D * 2;
+  // (paged caches: a resource over the tile's block rows, built per tile)
+  auto dma = [&](__amdgpu_buffer_rsrc_t rs, const void* pool, const int* off, uint16_t* dst, int t) {
+    int tb = (kb + t * KT) * D * 2;
+    if (PAGED) {
+      rs = paged_tile<2>(p, pool, b, g, kb + t * KT, ke, D);
+      tb = 0;
+    }
     if (stream_once) {
 #pragma unroll
       for (int i = 0; i < PER_THREAD; ++i)
@@ -765,11 +802,11 @@ void attn_mfma32_kernel(AttnParams p) {
   // run (the S MFMAs do not depend on the softmax, so the two can co-issue).
   const int nt = (ke - kb + KT - 1) / KT;
   f32x16_t sc[2], sn[2];
-  dma(krs, koff, Ks0, 0);
+  dma(krs, p.k, koff, Ks0, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  dma(krs, koff, Ks1, 1);
-  dma(vrs, voff, Vs0, 0);
+  dma(krs, p.k, koff, Ks1, 1);
+  dma(vrs, p.v, voff, Vs0, 0);
   if (wave_any) s_tile(Ks0, sc);
   // one iteration; cur / nxt are the buffers of tiles t and t + 1 (S of the
   // tile after the last one is computed on the zeros the range check left in
@@ -780,8 +817,8 @@ void attn_mfma32_kernel(AttnParams p) {
                   f32x16_t* snxt) {
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of K_{t+1} and V_t have landed
     __syncthreads();                // everyone's have; K_t and V_{t-1} are no longer read
-    dma(krs, koff, Kcur, t + 2);
-    dma(vrs, voff, Vnxt, t + 1);
+    dma(krs, p.k, koff, Kcur, t + 2);
+    dma(vrs, p.v, voff, Vnxt, t + 1);
     if (!wave_any) return;          // waves without rows only help to stream the tiles
     softmax_s_pv(scur, snxt, Knxt, Vcur, t);
   };
@@ -824,7 +861,7 @@ void attn_mfma32_kernel(AttnParams p) {
 // fp32 path (plain VALU): 8 query rows per workgroup, 32-key tiles in LDS.
 // Thread t handles row t/32 and, per tile, key t%32 for the scores and head
 // dims t%32 + 32k for the output.
-template <int D>
+template <int D, bool PAGED = false>
 __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
   constexpr int KT = 32, RW = 8, DPT = D / 32;
   __shared__ float Qs[RW][D];
@@ -874,7 +911,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
     if (orow >= 0 && kl == 0) p.ml_part[(int64_t)split * NH + orow] = make_float2(-INFINITY, 0.f);
     return;
   }
-  const int64_t head_off = ((int64_t)b * p.Hkv + g) * p.Lcap * D;
+  const int64_t head_off = PAGED ? 0 : ((int64_t)b * p.Hkv + g) * p.Lcap * D;  // paged: per tile instead
   const float* kbase = (const float*)p.k + head_off;
   const float* vbase = (const float*)p.v + head_off;
 
@@ -884,11 +921,16 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
 
   for (int t0 = kb; t0 < ke; t0 += KT) {
     __syncthreads();
+    // paged caches: the 32-key tile lies in one block (block_size % 64 == 0,
+    // t0 % 32 == 0); a block id out of range reads as zeros (flagged)
+    int64_t tile_off = (int64_t)t0 * D;
+    bool tile_ok = true;
+    if (PAGED) tile_off = paged_slot(p, b, g, t0, D, tile_ok);
     for (int idx = tid; idx < KT * D; idx += 256) {
       const int kk = idx / D, d = idx % D, key = t0 + kk;
-      const bool in = key < ke;
-      Ks[kk][d] = in ? kbase[(int64_t)key * D + d] : 0.f;
-      Vs[kk][d] = in ? vbase[(int64_t)key * D + d] : 0.f;
+      const bool in = key < ke && tile_ok;
+      Ks[kk][d] = in ? kbase[tile_off + (int64_t)kk * D + d] : 0.f;
+      Vs[kk][d] = in ? vbase[tile_off + (int64_t)kk * D + d] : 0.f;
     }
     __syncthreads();
     float s = 0.f;
@@ -1000,11 +1042,11 @@ hipError_t launch_attn_prep(const AttnParams& p, const AttnPlan& plan, const int
 // 4 waves (128 rows, two workgroups per CU) with row groups (measured on
 // MI355X: the 8-wave form is 6 % faster on 240-row trees, the 4-wave form
 // faster on trees of up to 272 rows whose sizes vary).
-template <int D>
+template <int D, bool PAGED>
 static void launch_mfma_d(const AttnParams& p, int rows_per_wg, dim3 grid, hipStream_t stream) {
-  if (rows_per_wg <= 64) attn_mfma_kernel<D, 1, 4, 1, 3><<<grid, dim3(256), 0, stream>>>(p);
-  else if (rows_per_wg <= 128) attn_mfma32_kernel<D, 4, 2><<<grid, dim3(256), 0, stream>>>(p);
-  else attn_mfma32_kernel<D, 8, 1><<<grid, dim3(512), 0, stream>>>(p);
+  if (rows_per_wg <= 64) attn_mfma_kernel<D, 1, 4, 1, 3, PAGED><<<grid, dim3(256), 0, stream>>>(p);
+  else if (rows_per_wg <= 128) attn_mfma32_kernel<D, 4, 2, PAGED><<<grid, dim3(256), 0, stream>>>(p);
+  else attn_mfma32_kernel<D, 8, 1, PAGED><<<grid, dim3(512), 0, stream>>>(p);
 }
 
 hipError_t launch_attention(const AttnParams& p, const AttnPlan& plan, bool bf16, hipStream_t stream,
@@ -1014,12 +1056,23 @@ hipError_t launch_attention(const AttnParams& p, const AttnPlan& plan, bool bf16
   if (bf16) {
     // 1-D grid, decoded XCD-aware inside the kernel (decode_block)
     const dim3 grid((unsigned)attn_grid_blocks(p.n_jobs, p.n_rowgroups));
-    if (p.D == 128) launch_mfma_d<128>(p, plan.rows_per_wg, grid, stream);
-    else launch_mfma_d<64>(p, plan.rows_per_wg, grid, stream);
+    const bool paged = p.block_table != nullptr;
+    if (p.D == 128) {
+      if (paged) launch_mfma_d<128, true>(p, plan.rows_per_wg, grid, stream);
+      else launch_mfma_d<128, false>(p, plan.rows_per_wg, grid, stream);
+    } else {
+      if (paged) launch_mfma_d<64, true>(p, plan.rows_per_wg, grid, stream);
+      else launch_mfma_d<64, false>(p, plan.rows_per_wg, grid, stream);
+    }
   } else {
     const dim3 grid(plan.n_rowgroups * plan.splits, p.Hkv, p.B);
-    if (p.D == 128) attn_valu_kernel<128><<<grid, dim3(256), 0, stream>>>(p);
-    else attn_valu_kernel<64><<<grid, dim3(256), 0, stream>>>(p);
+    if (p.block_table) {
+      if (p.D == 128) attn_valu_kernel<128, true><<<grid, dim3(256), 0, stream>>>(p);
+      else attn_valu_kernel<64, true><<<grid, dim3(256), 0, stream>>>(p);
+    } else {
+      if (p.D == 128) attn_valu_kernel<128><<<grid, dim3(256), 0, stream>>>(p);
+      else attn_valu_kernel<64><<<grid, dim3(256), 0, stream>>>(p);
+    }
   }
   if (ev_stop) (void)hipEventRecord(ev_stop, stream);
   hipError_t err = hipGetLastError();

@@ -33,7 +33,7 @@ static_assert(sizeof(RowStat) == 16, "RowStat layout");
 
 // Data-error bits (same values as SV_STATUS_* in the public header).
 constexpr int32_t kStTree = 0x01, kStPacking = 0x02, kStToken = 0x04, kStNonFinite = 0x08,
-                  kStZeroResidual = 0x10, kStCtx = 0x20, kStSync = 0x40;
+                  kStZeroResidual = 0x10, kStCtx = 0x20, kStSync = 0x40, kStBlock = 0x80;
 
 __device__ __forceinline__ void flag(int32_t* status, int32_t bits) {
   if (status) atomicOr(status, bits);

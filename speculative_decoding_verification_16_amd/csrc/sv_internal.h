@@ -36,6 +36,11 @@ struct AttnParams {
   const int32_t* item_tot;
   float scale_log2;        // softmax scale * log2(e)
   int32_t* status;
+  // paged caches: k / v are pools [num_blocks, Hkv, block_size, D] and slot t
+  // of request b is row t % block_size of block block_table[b, t / block_size]
+  const int32_t* block_table;  // [B, max_blocks], or null (contiguous caches)
+  int32_t block_size, max_blocks;
+  int64_t num_blocks;
 };
 
 struct AttnPlan {

@@ -17,9 +17,10 @@ def host_bits(t: torch.Tensor) -> np.ndarray:
     return t.contiguous().cpu().numpy()
 
 
-def oracle_attention(w, items=None):
+def oracle_attention(w, items=None, block_table=None):
     return oracle.attention(host_bits(w["q"]), host_bits(w["k_cache"]), host_bits(w["v_cache"]), w["ctx_len"],
-                            w["cu_nodes"], w["parent"], Hq=w["Hq"], Hkv=w["Hkv"], dtype=w["dtype"], items=items)
+                            w["cu_nodes"], w["parent"], Hq=w["Hq"], Hkv=w["Hkv"], dtype=w["dtype"], items=items,
+                            block_table=block_table)
 
 
 def sample_items(w, n, seed=0):

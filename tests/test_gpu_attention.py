@@ -213,3 +213,94 @@ def test_attention_full_size_sampled_outputs(name):
     got = out[torch.from_numpy(items[:, 0]).cuda(), torch.from_numpy(items[:, 1]).cuda()].cpu().numpy()
     err = float(np.abs(got - ref).max())
     assert err <= ATTN_TOL[cfg.dtype], err
+
+
+# ---- paged KV caches (block table into a pool of blocks) ------------------------
+PAGED = ["c1_full", "c2_small", "c2_long_ctx", "c3_small", "c5_small", "f32_tree", "bf16_d64_tree_256rows",
+         "tree_180rows", "c5_trees_upto_256rows", "wide_tree_rowgroups", "no_context"]
+
+
+def _paged(w, bs, seed, share=0):
+    """The workload's caches padded to a multiple of bs slots (NaN) and laid out
+    as shuffled pools with NaN spare blocks."""
+    from workloads import to_paged
+
+    k, v = w["k_cache"], w["v_cache"]
+    B, Hkv, Lcap, D = k.shape
+    Lp = (Lcap + bs - 1) // bs * bs
+    if Lp != Lcap:
+        pad = torch.full((B, Hkv, Lp - Lcap, D), float("nan"), dtype=k.dtype, device=k.device)
+        k, v = torch.cat([k, pad], dim=2).contiguous(), torch.cat([v, pad], dim=2).contiguous()
+    kp, vp, bt = to_paged(k, v, bs, np.random.default_rng(seed), share_prefix_blocks=share)
+    return kp.contiguous(), vp.contiguous(), torch.from_numpy(bt).cuda(), k, v
+
+
+@pytest.mark.parametrize("splits", [0, 3])
+@pytest.mark.parametrize("bs", [64, 256])
+@pytest.mark.parametrize("name", PAGED)
+def test_paged_attention_matches(name, bs, splits):
+    cfg = SMALL[name]
+    w = generate(cfg, "cuda", sample=False, poison=True)
+    print(f"[attn-paged] {name} bs={bs} splits={splits} B={w['B']} N={w['N']} L={cfg.L}", flush=True)
+    kp, vp, bt, kc, vc = _paged(w, bs, 901 + bs)
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out_p = sv.attn(w["q"], kp, vp, w["ctx_len_t"], w["cu_nodes_t"], parent=w["parent_t"], max_nodes=w["max_T"],
+                    num_splits=splits, block_table=bt, status=st)
+    out_c = sv.attn(w["q"], kc, vc, w["ctx_len_t"], w["cu_nodes_t"], parent=w["parent_t"], max_nodes=w["max_T"],
+                    num_splits=splits)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0, sv.status_names(int(st.item()))
+    # same loads in the same order: the paged kernels give the contiguous result bit for bit
+    assert torch.equal(out_p, out_c)
+    ref = oracle_attention({**w, "k_cache": kp, "v_cache": vp}, block_table=bt.cpu().numpy())
+    err = float(np.abs(out_p.cpu().numpy() - ref).max())
+    assert err <= ATTN_TOL[cfg.dtype], err
+
+
+@pytest.mark.parametrize("name", ["c3_eagle_tree", "c5_super_tree", "c4_L32768_B1_T1"])
+def test_paged_attention_full_size(name):
+    cfg = get_config(name)
+    w = generate(cfg, "cuda", sample=False)
+    print(f"[attn-paged-full] {name} B={w['B']} N={w['N']} L={cfg.L}", flush=True)
+    kp, vp, bt, kc, vc = _paged(w, 128, 911)
+    del w["k_cache"], w["v_cache"]
+    out_p = sv.attn(w["q"], kp, vp, w["ctx_len_t"], w["cu_nodes_t"], parent=w["parent_t"], max_nodes=w["max_T"],
+                    block_table=bt)
+    out_c = sv.attn(w["q"], kc, vc, w["ctx_len_t"], w["cu_nodes_t"], parent=w["parent_t"], max_nodes=w["max_T"])
+    torch.cuda.synchronize()
+    assert torch.equal(out_p, out_c)
+    items = sample_items(w, 24, seed=5)
+    ref = oracle_attention({**w, "k_cache": kp, "v_cache": vp}, items=items, block_table=bt.cpu().numpy())
+    got = out_p.cpu().numpy()[items[:, 0], items[:, 1]]
+    assert float(np.abs(got - ref).max()) <= ATTN_TOL[cfg.dtype]
+
+
+def test_paged_attention_shared_prefix_and_bad_block():
+    cfg = SMALL["c3_small"]
+    w = generate(cfg, "cuda", sample=False)
+    kp, vp, bt, _, _ = _paged(w, 64, 921, share=2)
+    out = sv.attn(w["q"], kp, vp, w["ctx_len_t"], w["cu_nodes_t"], parent=w["parent_t"], max_nodes=w["max_T"],
+                  block_table=bt)
+    torch.cuda.synchronize()
+    ref = oracle_attention({**w, "k_cache": kp, "v_cache": vp}, block_table=bt.cpu().numpy())
+    assert float(np.abs(out.cpu().numpy() - ref).max()) <= ATTN_TOL[cfg.dtype]
+    # a block id past the pool: flagged, nothing read out of bounds, other requests exact
+    bad = bt.clone()
+    bad[1, 0] = kp.shape[0] + 1000
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out_b = sv.attn(w["q"], kp, vp, w["ctx_len_t"], w["cu_nodes_t"], parent=w["parent_t"], max_nodes=w["max_T"],
+                    block_table=bad, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) & 0x80
+    n1 = int(w["cu_nodes"][1])
+    assert torch.equal(out_b[:n1], out[:n1])
+    # a table with too few blocks for the context: flagged and skipped, like a short Lcap
+    st2 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    sv.attn(w["q"], kp, vp, w["ctx_len_t"], w["cu_nodes_t"], parent=w["parent_t"], max_nodes=w["max_T"],
+            status=st2, block_table=bt[:, :1].contiguous())
+    torch.cuda.synchronize()
+    assert int(st2.item()) & 0x20
+    odd = torch.zeros((kp.shape[0], kp.shape[1], 32, kp.shape[3]), dtype=kp.dtype, device="cuda")
+    with pytest.raises(sv.SpecVerifyError):  # block size not a multiple of 64
+        sv.attn(w["q"], odd, odd, w["ctx_len_t"], w["cu_nodes_t"], parent=w["parent_t"], max_nodes=w["max_T"],
+                block_table=bt)
