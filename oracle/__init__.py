@@ -94,6 +94,8 @@ def _load():
     lib.orc_truncate_eta.restype = f64
     lib.orc_row_entropy.argtypes = [i32, P, f64]
     lib.orc_row_entropy.restype = f64
+    lib.orc_pack.argtypes = [i32, P, P, P, P, i64, P, P, P, P, P, P]
+    lib.orc_pack.restype = i32
     lib.orc_remove_candidate.argtypes = [i32, P, i32, P]
     lib.orc_remove_candidate.restype = f64
     _lib = lib
@@ -344,4 +346,31 @@ def verify(cu_nodes, parent, tokens, logits, q, *, temperature, seed, step=0, re
                             float(accept_tol), float(cdf_tol), nthreads or _default_threads())
     if rc != 0:
         raise ValueError("oracle verify: bad arguments")
+    return out
+
+
+def pack(cu_cand, cand_parent, cand_token, cand_score, budget: int) -> dict:
+    """Budgeted super-tree packing ([ECHO] 3.1, Figure 3 step 3): keep the
+    `budget` best candidates by (min score on the path, descending; request;
+    local index) and pack them request by request; see orc_pack."""
+    cu = np.ascontiguousarray(cu_cand, dtype=np.int32)
+    B = cu.shape[0] - 1
+    par = np.ascontiguousarray(cand_parent, dtype=np.int32)
+    tok = np.ascontiguousarray(cand_token, dtype=np.int32)
+    sc = np.ascontiguousarray(cand_score, dtype=np.float32)
+    M = int(cu[-1]) if B > 0 else 0
+    cap = max(min(int(budget), M), 1)
+    out = {"cu_nodes": np.zeros(B + 1, np.int32), "parent": np.zeros(cap, np.int32),
+           "draft_tokens": np.zeros(cap, np.int32), "src": np.zeros(cap, np.int32)}
+    n = np.zeros(1, np.int32)
+    st = np.zeros(1, np.int32)
+    rc = _load().orc_pack(B, _ptr(cu), _ptr(par), _ptr(tok), _ptr(sc), int(budget), _ptr(out["cu_nodes"]),
+                          _ptr(out["parent"]), _ptr(out["draft_tokens"]), _ptr(out["src"]), _ptr(n), _ptr(st))
+    if rc != 0:
+        raise ValueError("oracle pack: bad arguments")
+    N = int(n[0])
+    for k in ("parent", "draft_tokens", "src"):
+        out[k] = out[k][:N]
+    out["total_nodes"] = N
+    out["status"] = int(st[0])
     return out

@@ -691,3 +691,102 @@ int orc_target_rows(int V, const float* logits, double T, int64_t n_rows, const 
     bad |= orc_target_probs(V, logits + rows[i] * (int64_t)V, T, out + i * (int64_t)V);
   return bad;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Budgeted super-tree packing ([ECHO] section 3.1: the batch's candidate
+ * trees form one super-tree verified in one pass under the global cap
+ * sum_i K_i <= K_max; Figure 3, step 3, flattens and packs the ragged
+ * result into one dense layout). Reading: each candidate carries a score S
+ * (ECHO's path score, the cumulative log q of its path: higher is better);
+ * its effective score is the smallest score on its path,
+ * S'(j) = min(S(j), S'(parent(j))), and the packer keeps the K_max best
+ * candidates in the order (S' descending, request ascending, local index
+ * ascending). S' never rises along a path and a parent precedes its child
+ * at equal S', so a kept node's ancestors are kept; for path scores (which
+ * never rise) this is the K_max best candidates. A NaN score counts as
+ * -inf and -0 as +0. Kept nodes are packed request by request in their
+ * original order, parents renumbered. A request with a parent outside
+ * [-1, j-1] or more than 64 candidates keeps nothing (status bit 0x01 /
+ * 0x02).                                                                  */
+typedef struct {
+  float s;   /* effective score */
+  int64_t m; /* candidate index  */
+} orc_pack_key;
+
+static int orc_pack_cmp(const void* a, const void* b) {
+  const orc_pack_key* x = (const orc_pack_key*)a;
+  const orc_pack_key* y = (const orc_pack_key*)b;
+  if (x->s > y->s) return -1;
+  if (x->s < y->s) return 1;
+  return x->m < y->m ? -1 : (x->m > y->m ? 1 : 0);
+}
+
+static float orc_canon_score(float s) {
+  if (s != s) return -INFINITY;
+  if (s == 0.0f) return 0.0f;
+  return s;
+}
+
+int orc_pack(int B, const int32_t* cu_cand, const int32_t* cand_parent, const int32_t* cand_token,
+             const float* cand_score, int64_t budget, int32_t* cu_nodes, int32_t* parent, int32_t* tokens,
+             int32_t* src, int32_t* total_nodes, int32_t* status) {
+  if (B < 0 || budget < 0) return 1;
+  int64_t M = B > 0 ? cu_cand[B] : 0;
+  orc_pack_key* keys = (orc_pack_key*)malloc(sizeof(orc_pack_key) * (size_t)(M > 0 ? M : 1));
+  float* eff = (float*)malloc(sizeof(float) * (size_t)(M > 0 ? M : 1));
+  char* keep = (char*)calloc((size_t)(M > 0 ? M : 1), 1);
+  if (!keys || !eff || !keep) { free(keys); free(eff); free(keep); return 1; }
+  *status = 0;
+  int64_t n_valid = 0;
+  for (int b = 0; b < B; ++b) {
+    int64_t c0 = cu_cand[b], c1 = cu_cand[b + 1];
+    int T = (int)(c1 - c0);
+    int ok = T >= 0 && T <= 64 && c0 >= 0 && c1 <= M;
+    if (!ok) { *status |= 0x02; continue; }
+    for (int j = 0; j < T; ++j)
+      if (cand_parent[c0 + j] < -1 || cand_parent[c0 + j] >= j) ok = 0;
+    if (!ok) { *status |= 0x01; continue; }
+    for (int j = 0; j < T; ++j) {
+      /* smallest score on the path from j up to its top ancestor */
+      float e = orc_canon_score(cand_score[c0 + j]);
+      for (int x = cand_parent[c0 + j]; x >= 0; x = cand_parent[c0 + x]) {
+        float sx = orc_canon_score(cand_score[c0 + x]);
+        if (sx < e) e = sx;
+      }
+      eff[c0 + j] = e;
+      keys[n_valid].s = e;
+      keys[n_valid].m = c0 + j;
+      ++n_valid;
+    }
+  }
+  qsort(keys, (size_t)n_valid, sizeof(orc_pack_key), orc_pack_cmp);
+  int64_t K = budget < n_valid ? budget : n_valid;
+  for (int64_t i = 0; i < K; ++i) keep[keys[i].m] = 1;
+  int64_t n = 0;
+  cu_nodes[0] = 0;
+  for (int b = 0; b < B; ++b) {
+    int64_t c0 = cu_cand[b], c1 = cu_cand[b + 1];
+    int T = (int)(c1 - c0);
+    int newidx[64];
+    int cnt = 0;
+    if (T >= 0 && T <= 64 && c0 >= 0 && c1 <= M) {
+      for (int j = 0; j < T; ++j) {
+        newidx[j] = -1;
+        if (!keep[c0 + j]) continue;
+        int p = cand_parent[c0 + j];
+        newidx[j] = cnt;
+        parent[n] = p < 0 ? -1 : newidx[p];
+        tokens[n] = cand_token[c0 + j];
+        src[n] = (int32_t)(c0 + j);
+        ++n;
+        ++cnt;
+      }
+    }
+    cu_nodes[b + 1] = (int32_t)n;
+  }
+  *total_nodes = (int32_t)n;
+  free(keys);
+  free(eff);
+  free(keep);
+  return 0;
+}
