@@ -124,9 +124,9 @@ typedef struct {
    * request b (committed context and draft slots alike) sits in block
    * block_table[b * max_blocks + t / block_size] at row t % block_size;
    * Lcap must equal max_blocks * block_size. Blocks may be shared between
-   * requests (a common prefix). block_size is a multiple of 64 (one 64-key
-   * tile never spans two blocks). An id outside [0, num_blocks) sets
-   * SV_STATUS_BLOCK_RANGE.                                                 */
+   * requests (a common prefix). block_size is a power of two, at least 64
+   * (one 64-key tile never spans two blocks). An id outside [0, num_blocks)
+   * sets SV_STATUS_BLOCK_RANGE.                                            */
   const int32_t* block_table; /* [B, max_blocks] device memory, or NULL     */
   int32_t block_size;
   int32_t max_blocks;
@@ -249,6 +249,54 @@ typedef struct {
   void* prof_stop;          /*   kernel / right after it (measurement)                     */
 } sv_sample_args;
 
+/* ------------------------------------------------------------------------ */
+/* Budgeted super-tree packing ([ECHO] section 3.1, "Super-Tree View": the
+ * batch's candidate trees are verified as one flattened union under the
+ * global cap sum_i K_i <= K_max; Figure 3, step 3: the ragged batch is
+ * flattened and packed into one dense layout). The step before
+ * spec_verify_step: its outputs are that call's cu_nodes, parent and
+ * draft_tokens, and src tells the caller which candidate's q row, hidden
+ * state and K/V each packed node carries.
+ *
+ * Candidate j of request b (local index, parents before children) has score
+ * S (for instance ECHO's path score, the cumulative log q of its path:
+ * higher is better; a NaN counts as -inf, -0 as +0). Its effective score is
+ * the smallest score on its path, e(j) = min(S(j), e(parent(j))). The
+ * min(budget, valid candidates) best candidates by (e descending, candidate
+ * index ascending) are kept. That set holds every kept node's ancestors,
+ * and for path scores, which never rise along a path, it is the K_max best
+ * candidates. Kept nodes are packed request by request in their original
+ * order with renumbered parents.
+ *
+ * Data errors: a request with more than 64 candidates (SV_STATUS_PACKING)
+ * or a parent outside [-1, j-1] (SV_STATUS_TREE_INVALID) keeps nothing;
+ * offsets that are not non-decreasing from cu_cand[0] = 0 to total_cand
+ * keep nothing at all (SV_STATUS_PACKING).                                 */
+typedef struct {
+  int32_t B;                  /* requests, 0 .. 8192                          */
+  int32_t total_cand;         /* M = cu_cand[B], 0 .. 2^24                    */
+  const int32_t* cu_cand;     /* [B+1] candidate offsets                      */
+  const int32_t* cand_parent; /* [M] local parent, -1 for a child of the root */
+  const int32_t* cand_token;  /* [M] token of each candidate                  */
+  const float* cand_score;    /* [M] score, higher is better                  */
+  int32_t budget;             /* K_max >= 0                                   */
+  int32_t* cu_nodes;          /* [B+1] out: packed offsets                    */
+  int32_t* parent;            /* [min(budget, M)] out: packed local parents   */
+  int32_t* draft_tokens;      /* [min(budget, M)] out: packed tokens          */
+  int32_t* src;               /* [min(budget, M)] out: candidate index of each packed node */
+  int32_t* total_nodes;       /* [1] out: N = cu_nodes[B]                     */
+  int32_t* status;            /* optional device word for SV_STATUS_* bits    */
+} sv_pack_args;
+
+/* Workspace bytes of spec_verify_pack (8 per candidate; 0 on invalid
+ * arguments, with the last error set, or when M == 0).                    */
+size_t spec_verify_pack_workspace_size(const sv_pack_args* pack);
+
+/* Budgeted packing; ws: 256-byte aligned device buffer of at least
+ * spec_verify_pack_workspace_size(pack) bytes. All pointers are device
+ * memory owned by the caller; asynchronous on stream.                      */
+sv_status spec_verify_pack(const sv_pack_args* pack, void* ws, size_t ws_bytes, void* stream);
+
 /* Bytes of workspace the calls need for these arguments (either pointer may be
  * NULL). Depends only on host-visible fields. Returns 0 on invalid arguments
  * (and sets the last error) or when no scratch is needed.                  */
@@ -270,7 +318,8 @@ sv_status spec_verify_step(const sv_attn_args* attn, const sv_sample_args* sampl
 const char* spec_verify_last_error(void);
 
 /* sizeof(sv_attn_args) for which == 0, sizeof(sv_sample_args) for which == 1,
- * 0 otherwise: lets bindings check their struct layout against this one.   */
+ * sizeof(sv_pack_args) for which == 2, 0 otherwise: lets bindings check
+ * their struct layout against this one.                                    */
 size_t spec_verify_struct_size(int32_t which);
 
 #ifdef __cplusplus

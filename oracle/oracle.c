@@ -707,7 +707,8 @@ int orc_target_rows(int V, const float* logits, double T, int64_t n_rows, const 
  * -inf and -0 as +0. Kept nodes are packed request by request in their
  * original order, parents renumbered. A request with a parent outside
  * [-1, j-1] or more than 64 candidates keeps nothing (status bit 0x01 /
- * 0x02).                                                                  */
+ * 0x02); offsets that are not non-decreasing from cu_cand[0] = 0 reject
+ * the whole batch (0x02, nothing kept).                                   */
 typedef struct {
   float s;   /* effective score */
   int64_t m; /* candidate index  */
@@ -737,6 +738,16 @@ int orc_pack(int B, const int32_t* cu_cand, const int32_t* cand_parent, const in
   char* keep = (char*)calloc((size_t)(M > 0 ? M : 1), 1);
   if (!keys || !eff || !keep) { free(keys); free(eff); free(keep); return 1; }
   *status = 0;
+  int mono = B == 0 || cu_cand[0] == 0;
+  for (int b = 0; b < B; ++b)
+    if (cu_cand[b + 1] < cu_cand[b]) mono = 0;
+  if (!mono) {
+    for (int b = 0; b <= B; ++b) cu_nodes[b] = 0;
+    *total_nodes = 0;
+    *status = 0x02;
+    free(keys); free(eff); free(keep);
+    return 0;
+  }
   int64_t n_valid = 0;
   for (int b = 0; b < B; ++b) {
     int64_t c0 = cu_cand[b], c1 = cu_cand[b + 1];

@@ -65,7 +65,9 @@ def load_library(path: str = LIB_PATH):
     lib = ctypes.CDLL(path)
     lib.spec_verify_workspace_size.argtypes = [_P, _P]
     lib.spec_verify_workspace_size.restype = ctypes.c_size_t
-    for name in ("spec_verify_attn", "spec_verify_sample"):
+    lib.spec_verify_pack_workspace_size.argtypes = [_P]
+    lib.spec_verify_pack_workspace_size.restype = ctypes.c_size_t
+    for name in ("spec_verify_attn", "spec_verify_sample", "spec_verify_pack"):
         getattr(lib, name).argtypes = [_P, _P, ctypes.c_size_t, _P]
         getattr(lib, name).restype = ctypes.c_int
     lib.spec_verify_step.argtypes = [_P, _P, _P, ctypes.c_size_t, _P]
@@ -75,7 +77,8 @@ def load_library(path: str = LIB_PATH):
     lib.spec_verify_struct_size.argtypes = [_i32]
     lib.spec_verify_struct_size.restype = ctypes.c_size_t
     if lib.spec_verify_struct_size(0) != ctypes.sizeof(SvAttnArgs) or \
-            lib.spec_verify_struct_size(1) != ctypes.sizeof(SvSampleArgs):
+            lib.spec_verify_struct_size(1) != ctypes.sizeof(SvSampleArgs) or \
+            lib.spec_verify_struct_size(2) != ctypes.sizeof(SvPackArgs):
         raise RuntimeError("argument struct layout of the binding does not match the library")
     _lib = lib
     return lib
@@ -296,3 +299,56 @@ def step(q, k_cache, v_cache, ctx_len, cu_nodes, parent, draft_tokens, target_lo
     s = SampleCall(a.keep["cu"], parent, draft_tokens, target_logits, draft_probs, temperature=temperature,
                    seed=seed, max_nodes=max_nodes, **(sample_kw or {}))
     return StepCall(a, s)()
+
+
+# ---------------------------------------------------------------------------
+class SvPackArgs(ctypes.Structure):
+    _fields_ = [("B", _i32), ("total_cand", _i32), ("cu_cand", _P), ("cand_parent", _P), ("cand_token", _P),
+                ("cand_score", _P), ("budget", _i32), ("cu_nodes", _P), ("parent", _P), ("draft_tokens", _P),
+                ("src", _P), ("total_nodes", _P), ("status", _P)]
+
+
+class PackCall:
+    """Prepared spec_verify_pack call: budgeted super-tree packing of the
+    batch's candidate trees (outputs sized for min(budget, candidates))."""
+
+    def __init__(self, cu_cand, cand_parent, cand_token, cand_score, *, budget, status=None):
+        lib = load_library()
+        dev = cand_score.device if torch.is_tensor(cand_score) else torch.device("cuda")
+        cu = _dev_i32(cu_cand, dev)
+        par = _dev_i32(cand_parent, dev)
+        tok = _dev_i32(cand_token, dev)
+        sc = torch.as_tensor(cand_score, dtype=torch.float32, device=dev).contiguous()
+        B, M = cu.numel() - 1, par.numel()
+        cap = max(min(int(budget), M), 1)
+        self.keep = {"cu": cu, "par": par, "tok": tok, "score": sc}
+        self.cu_nodes = torch.empty(B + 1, dtype=torch.int32, device=dev)
+        self.parent = torch.empty(cap, dtype=torch.int32, device=dev)
+        self.draft_tokens = torch.empty(cap, dtype=torch.int32, device=dev)
+        self.src = torch.empty(cap, dtype=torch.int32, device=dev)
+        self.total = torch.empty(1, dtype=torch.int32, device=dev)
+        self.status = status if status is not None else torch.zeros(1, dtype=torch.int32, device=dev)
+        a = SvPackArgs()
+        a.B, a.total_cand, a.budget = B, M, int(budget)
+        a.cu_cand, a.cand_parent, a.cand_token, a.cand_score = _ptr(cu), _ptr(par), _ptr(tok), _ptr(sc)
+        a.cu_nodes, a.parent, a.draft_tokens, a.src = _ptr(self.cu_nodes), _ptr(self.parent), \
+            _ptr(self.draft_tokens), _ptr(self.src)
+        a.total_nodes, a.status = _ptr(self.total), _ptr(self.status)
+        self.args = a
+        self.ws_bytes = lib.spec_verify_pack_workspace_size(ctypes.byref(a))
+        if self.ws_bytes == 0 and lib.spec_verify_last_error():
+            _check(SV_ERR_INVALID_ARG)
+        self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+    def __call__(self, stream=None):
+        _check(load_library().spec_verify_pack(ctypes.byref(self.args), _ptr(self.ws), self.ws_bytes,
+                                               _stream_handle(stream)))
+        return {"cu_nodes": self.cu_nodes, "parent": self.parent, "draft_tokens": self.draft_tokens,
+                "src": self.src, "total_nodes": self.total, "status": self.status}
+
+
+def pack(cu_cand, cand_parent, cand_token, cand_score, *, budget, **kw):
+    """Budgeted super-tree packing; returns a dict of device tensors (parent,
+    draft_tokens and src hold min(budget, candidates) entries, the first
+    total_nodes of them valid)."""
+    return PackCall(cu_cand, cand_parent, cand_token, cand_score, budget=budget, **kw)()

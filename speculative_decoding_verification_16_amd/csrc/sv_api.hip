@@ -40,11 +40,13 @@ sv_status check_attn(const sv_attn_args* a) {
   if (a->dtype != SV_F32 && a->dtype != SV_BF16) return fail(SV_ERR_INVALID_ARG, "dtype must be SV_F32 or SV_BF16");
   if (a->Lcap < 1 || a->Lcap > (1ll << 24)) return fail(SV_ERR_INVALID_ARG, "Lcap must be in [1, 2^24]");
   if (a->block_table) {
-    if (a->block_size <= 0 || a->block_size % 64 != 0)
-      return fail(SV_ERR_UNSUPPORTED, "block_size must be a positive multiple of 64");
+    if (a->block_size < 64 || (a->block_size & (a->block_size - 1)) != 0)
+      return fail(SV_ERR_UNSUPPORTED, "block_size must be a power of two, at least 64");
     if (a->max_blocks <= 0 || (int64_t)a->max_blocks * a->block_size != a->Lcap)
       return fail(SV_ERR_INVALID_ARG, "paged caches need max_blocks > 0 and Lcap == max_blocks * block_size");
     if (a->num_blocks <= 0) return fail(SV_ERR_INVALID_ARG, "num_blocks must be > 0");
+    if (a->max_blocks > 192 * 256)
+      return fail(SV_ERR_UNSUPPORTED, "max_blocks above 49152 (a split holds at most 256 block ids)");
     if (!aligned(a->block_table, 4)) return fail(SV_ERR_INVALID_ARG, "block_table must be 4-byte aligned");
   }
   if (!(a->scale >= 0.f) || isinf(a->scale)) return fail(SV_ERR_INVALID_ARG, "scale must be finite and >= 0");
@@ -105,6 +107,13 @@ sv::AttnPlan plan_attn(const sv_attn_args* a) {
     if (s > by_traffic) s = by_traffic;
     if (s > 256) s = 256;
     pl.splits = s < 1 ? 1 : (int)s;
+  }
+  if (a->block_table) {
+    // paged caches: a split's key range spans at most 256 blocks (the block
+    // ids a workgroup holds in registers); 192 per split leaves room for the
+    // 64-key rounding of the range and an unaligned start
+    const int64_t need = (a->max_blocks + 191) / 192;
+    if (pl.splits < need) pl.splits = (int)need;
   }
   return pl;
 }
@@ -243,6 +252,20 @@ sv_status check_ws(const WsLayout& w, void* ws, size_t ws_bytes) {
   return SV_OK;
 }
 
+sv_status check_pack(const sv_pack_args* k) {
+  if (!k) return fail(SV_ERR_INVALID_ARG, "pack args is NULL");
+  if (k->B < 0 || k->B > sv::kPackMaxB) return fail(SV_ERR_UNSUPPORTED, "B must be in [0, %d]", sv::kPackMaxB);
+  if (k->total_cand < 0 || k->total_cand > (1 << 24)) return fail(SV_ERR_INVALID_ARG, "total_cand must be in [0, 2^24]");
+  if (k->budget < 0) return fail(SV_ERR_INVALID_ARG, "budget < 0");
+  if (!k->cu_cand || !k->cu_nodes || !k->total_nodes)
+    return fail(SV_ERR_INVALID_ARG, "cu_cand, cu_nodes and total_nodes are required");
+  if (k->total_cand > 0 && (!k->cand_parent || !k->cand_token || !k->cand_score))
+    return fail(SV_ERR_INVALID_ARG, "cand_parent, cand_token and cand_score are required when total_cand > 0");
+  if (k->total_cand > 0 && k->budget > 0 && (!k->parent || !k->draft_tokens || !k->src))
+    return fail(SV_ERR_INVALID_ARG, "parent, draft_tokens and src are required when something can be kept");
+  return SV_OK;
+}
+
 sv_status hip_fail(hipError_t e, const char* what) {
   return fail(SV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
@@ -283,6 +306,8 @@ sv_status run_attn(const sv_attn_args* a, char* ws, const WsLayout& w, hipStream
   p.block_size = a->block_table ? a->block_size : 0;
   p.max_blocks = a->block_table ? a->max_blocks : 0;
   p.num_blocks = a->block_table ? a->num_blocks : 0;
+  p.bs_shift = 0;
+  while (a->block_table && (1 << p.bs_shift) < a->block_size) ++p.bs_shift;
   hipError_t e = sv::launch_attn_prep(p, pl, a->parent, w_anc, st);
   if (e != hipSuccess) return hip_fail(e, "attention prep launch");
   e = sv::launch_attention(p, pl, a->dtype == SV_BF16, st, (hipEvent_t)a->prof_start,
@@ -389,7 +414,42 @@ const char* spec_verify_last_error(void) { return g_err; }
 size_t spec_verify_struct_size(int32_t which) {
   if (which == 0) return sizeof(sv_attn_args);
   if (which == 1) return sizeof(sv_sample_args);
+  if (which == 2) return sizeof(sv_pack_args);
   return 0;
+}
+
+size_t spec_verify_pack_workspace_size(const sv_pack_args* pk) {
+  g_err[0] = 0;
+  if (check_pack(pk) != SV_OK) return 0;
+  return align_up((size_t)pk->total_cand * sizeof(uint64_t));
+}
+
+sv_status spec_verify_pack(const sv_pack_args* pk, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  sv_status st = check_pack(pk);
+  if (st != SV_OK) return st;
+  WsLayout w;
+  w.total = align_up((size_t)pk->total_cand * sizeof(uint64_t));
+  if ((st = check_ws(w, ws, ws_bytes)) != SV_OK) return st;
+  if (pk->B == 0) return SV_OK;
+  sv::PackParams p{};
+  p.B = pk->B;
+  p.M = pk->total_cand;
+  p.cu_cand = pk->cu_cand;
+  p.par = pk->cand_parent;
+  p.tok = pk->cand_token;
+  p.score = pk->cand_score;
+  p.budget = pk->budget;
+  p.cu_nodes = pk->cu_nodes;
+  p.parent = pk->parent;
+  p.tokens = pk->draft_tokens;
+  p.src = pk->src;
+  p.total = pk->total_nodes;
+  p.status = pk->status;
+  p.keys = (uint64_t*)ws;
+  const hipError_t e = sv::launch_pack(p, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "packing launch");
+  return SV_OK;
 }
 
 }  // extern "C"

@@ -118,18 +118,45 @@ __device__ __forceinline__ bool decode_block(const AttnParams& p, int lin, int& 
   return job < p.n_jobs;
 }
 
-// Paged caches: element offset of logical slot t (a multiple of 64, so that
-// its 64-key tile lies in one block) of request b, KV head g, in the pool;
-// ok = false (flagged) for a block id out of range. t is uniform over the
-// workgroup, so the table read is a scalar load.
-__device__ __forceinline__ int64_t paged_slot(const AttnParams& p, int b, int g, int t, int D, bool& ok) {
-  const int blk = p.block_table[(int64_t)b * p.max_blocks + t / p.block_size];
+// Paged caches. Before its first tile a workgroup loads the block ids of its
+// key range, up to 256 blocks (the planner splits longer ranges),
+// into four VGPRs per lane (lane i of register k: block first + 64 k + i); a
+// tile's id is then a v_readlane. No memory access and no wait sits on the
+// path that issues a tile's loads: a table read there made every refill
+// drain the loads in flight (measured on MI355X: 14-28 % slower attention
+// with a scalar load per tile, 13-23 % with a window reloaded in the loop).
+struct PagedIds {
+  int first = 0;            // block index of lane 0 of ids[0] (uniform)
+  int ids[4] = {-1, -1, -1, -1};
+};
+
+__device__ __forceinline__ void paged_load(const AttnParams& p, int b, int kb, PagedIds& pg) {
+  pg.first = kb >> p.bs_shift;
+  const int lane = (int)(threadIdx.x & 63);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int idx = pg.first + 64 * k + lane;
+    pg.ids[k] = idx < p.max_blocks ? p.block_table[(int64_t)b * p.max_blocks + idx] : -1;
+  }
+}
+
+// element offset of logical slot t (uniform; its 64-key tile lies in one
+// block) of request b, KV head g, in the pool; ok = false (flagged) for a
+// block id out of range
+__device__ __forceinline__ int64_t paged_slot(const AttnParams& p, int b, int g, int t, int D, bool& ok,
+                                              const PagedIds& pg) {
+  const int bi = (t >> p.bs_shift) - pg.first;
+  const int l = bi & 63;
+  const int r0 = __builtin_amdgcn_readlane(pg.ids[0], l), r1 = __builtin_amdgcn_readlane(pg.ids[1], l);
+  const int r2 = __builtin_amdgcn_readlane(pg.ids[2], l), r3 = __builtin_amdgcn_readlane(pg.ids[3], l);
+  const int k = bi >> 6;
+  const int blk = (bi < 0 || k > 3) ? -1 : (k == 0 ? r0 : (k == 1 ? r1 : (k == 2 ? r2 : r3)));
   ok = blk >= 0 && (int64_t)blk < p.num_blocks;
   if (!ok) {
     if (threadIdx.x == 0) flag(p.status, kStBlock);
     return 0;
   }
-  return (((int64_t)blk * p.Hkv + g) * p.block_size + t % p.block_size) * D;
+  return ((((int64_t)blk * p.Hkv + g) << p.bs_shift) + (t & (p.block_size - 1))) * D;
 }
 
 // Buffer resource over the keys [t, min(t + 64, ke)) of a paged pool (pool:
@@ -137,10 +164,10 @@ __device__ __forceinline__ int64_t paged_slot(const AttnParams& p, int b, int g,
 // the range and for a block id out of range, without touching memory.
 template <int ESZ>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t paged_tile(const AttnParams& p, const void* pool, int b, int g,
-                                                             int t, int ke, int D) {
+                                                             int t, int ke, int D, const PagedIds& pg) {
   const int valid = min(64, ke - t);
   bool ok = false;
-  const int64_t eo = valid > 0 ? paged_slot(p, b, g, t, D, ok) : 0;
+  const int64_t eo = valid > 0 ? paged_slot(p, b, g, t, D, ok, pg) : 0;
   return __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)pool + eo * ESZ), (short)0,
                                            ok ? valid * D * ESZ : 0, 0x00020000);
 }
@@ -341,11 +368,13 @@ void attn_mfma_kernel(AttnParams p) {
   // serves at most 64 rows per KV head, so each key range has one reader
   // (measured on MI355X: 11 % faster on 32k-token contexts). Paged caches:
   // one resource per tile, over that tile's block rows.
+  PagedIds pg;
+  if (PAGED) paged_load(p, b, kb, pg);
 #pragma unroll
   for (int s = 0; s < NBUF; ++s) {
     const int so = PAGED ? 0 : (kb + s * KT) * D * 2;
-    const __amdgpu_buffer_rsrc_t kr = PAGED ? paged_tile<2>(p, p.k, b, g, kb + s * KT, ke, D) : krs;
-    const __amdgpu_buffer_rsrc_t vr = PAGED ? paged_tile<2>(p, p.v, b, g, kb + s * KT, ke, D) : vrs;
+    const __amdgpu_buffer_rsrc_t kr = PAGED ? paged_tile<2>(p, p.k, b, g, kb + s * KT, ke, D, pg) : krs;
+    const __amdgpu_buffer_rsrc_t vr = PAGED ? paged_tile<2>(p, p.v, b, g, kb + s * KT, ke, D, pg) : vrs;
 #pragma unroll
     for (int i = 0; i < PER_THREAD; ++i) {
       kreg[s][i] = __builtin_amdgcn_raw_buffer_load_b128(kr, koff[i], so, kAuxNT);
@@ -372,8 +401,8 @@ void attn_mfma_kernel(AttnParams p) {
       // refill this ring slot with the tile NBUF positions ahead
       {
         const int so = PAGED ? 0 : (t0 + NBUF * KT) * D * 2;
-        const __amdgpu_buffer_rsrc_t kr = PAGED ? paged_tile<2>(p, p.k, b, g, t0 + NBUF * KT, ke, D) : krs;
-        const __amdgpu_buffer_rsrc_t vr = PAGED ? paged_tile<2>(p, p.v, b, g, t0 + NBUF * KT, ke, D) : vrs;
+        const __amdgpu_buffer_rsrc_t kr = PAGED ? paged_tile<2>(p, p.k, b, g, t0 + NBUF * KT, ke, D, pg) : krs;
+        const __amdgpu_buffer_rsrc_t vr = PAGED ? paged_tile<2>(p, p.v, b, g, t0 + NBUF * KT, ke, D, pg) : vrs;
 #pragma unroll
         for (int i = 0; i < PER_THREAD; ++i) {
           kreg[s][i] = __builtin_amdgcn_raw_buffer_load_b128(kr, koff[i], so, kAuxNT);
@@ -647,10 +676,12 @@ void attn_mfma32_kernel(AttnParams p) {
   // 6 %, whose larger trees have two to four row groups.)
   const bool stream_once = R <= ROWS;
   // (paged caches: a resource over the tile's block rows, built per tile)
+  PagedIds pg;
+  if (PAGED) paged_load(p, b, kb, pg);
   auto dma = [&](__amdgpu_buffer_rsrc_t rs, const void* pool, const int* off, uint16_t* dst, int t) {
     int tb = (kb + t * KT) * D * 2;
     if (PAGED) {
-      rs = paged_tile<2>(p, pool, b, g, kb + t * KT, ke, D);
+      rs = paged_tile<2>(p, pool, b, g, kb + t * KT, ke, D, pg);
       tb = 0;
     }
     if (stream_once) {
@@ -919,13 +950,15 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
 #pragma unroll
   for (int k2 = 0; k2 < DPT; ++k2) o[k2] = 0.f;
 
+  PagedIds pg;
+  if (PAGED) paged_load(p, b, kb, pg);
   for (int t0 = kb; t0 < ke; t0 += KT) {
     __syncthreads();
     // paged caches: the 32-key tile lies in one block (block_size % 64 == 0,
     // t0 % 32 == 0); a block id out of range reads as zeros (flagged)
     int64_t tile_off = (int64_t)t0 * D;
     bool tile_ok = true;
-    if (PAGED) tile_off = paged_slot(p, b, g, t0, D, tile_ok);
+    if (PAGED) tile_off = paged_slot(p, b, g, t0, D, tile_ok, pg);
     for (int idx = tid; idx < KT * D; idx += 256) {
       const int kk = idx / D, d = idx % D, key = t0 + kk;
       const bool in = key < ke && tile_ok;

@@ -40,6 +40,7 @@ struct AttnParams {
   // of request b is row t % block_size of block block_table[b, t / block_size]
   const int32_t* block_table;  // [B, max_blocks], or null (contiguous caches)
   int32_t block_size, max_blocks;
+  int32_t bs_shift;            // log2(block_size)
   int64_t num_blocks;
 };
 
@@ -113,5 +114,25 @@ int walk_slices(int B, int nch, bool passes);
 
 hipError_t launch_sampler(const SampleParams& p, bool vec4, hipStream_t stream, hipEvent_t ev_start,
                           hipEvent_t ev_stop);
+
+// ---- budgeted super-tree packing ------------------------------------------------
+constexpr int kPackMaxB = 8192;  // requests per packing call (one workgroup's LDS scan)
+struct PackParams {
+  int32_t B;
+  int64_t M;                // candidates, cu_cand[B]
+  const int32_t* cu_cand;   // [B+1]
+  const int32_t* par;       // [M] local parents
+  const int32_t* tok;       // [M]
+  const float* score;       // [M]
+  int32_t budget;           // K_max
+  int32_t* cu_nodes;        // [B+1]
+  int32_t* parent;          // [min(budget, M)]
+  int32_t* tokens;
+  int32_t* src;
+  int32_t* total;           // [1]
+  int32_t* status;
+  uint64_t* keys;           // [M] workspace
+};
+hipError_t launch_pack(const PackParams& p, hipStream_t stream);
 
 }  // namespace sv

@@ -155,3 +155,6 @@ def test_nan_and_invalid_requests():
     bad[5] = 3  # parent not before the node: request 1 keeps nothing
     out = oracle.pack(cu, bad, tok, sc, 8)
     assert out["status"] & 0x01 and out["cu_nodes"][2] == out["cu_nodes"][1] == 4
+    # offsets that go backwards reject the whole batch
+    out = oracle.pack(np.array([0, 5, 3, 8], np.int32), np.zeros(8, np.int32) - 1, tok, sc, 8)
+    assert out["status"] & 0x02 and out["total_nodes"] == 0
