@@ -70,9 +70,11 @@ def _load():
     lib.orc_ancestors.restype = i32
     lib.orc_attention.argtypes = [i32, i32, i32, i32, i32, P, P, P, i64, P, P, P, f64, i64, P, P, i32]
     lib.orc_attention.restype = i32
-    lib.orc_attention_paged.argtypes = [i32, i32, i32, i32, i32, P, P, P, i64, P, P, P, f64, i64, P, P, i32, P, i32,
-                                        i32, i64]
-    lib.orc_attention_paged.restype = i32
+    lib.orc_attention_ex.argtypes = [i32, i32, i32, i32, i32, P, P, P, i64, P, P, P, f64, i64, P, P, i32, P, i32,
+                                     i32, i64, i32, f64, f64]
+    lib.orc_attention_ex.restype = i32
+    lib.orc_fp8_e4m3.argtypes = [ctypes.c_uint8]
+    lib.orc_fp8_e4m3.restype = f64
     lib.orc_target_probs.argtypes = [i32, P, f64, P]
     lib.orc_target_probs.restype = i32
     lib.orc_argmax.argtypes = [i32, P]
@@ -140,8 +142,13 @@ def ancestors(parent) -> tuple[np.ndarray, np.ndarray]:
     return anc[:T], depth[:T]
 
 
+def fp8_e4m3(byte: int) -> float:
+    """Value of one OCP FP8 E4M3 (finite form) byte."""
+    return float(_load().orc_fp8_e4m3(int(byte)))
+
+
 def attention(q, k, v, ctx_len, cu_nodes, parent, *, Hq, Hkv, scale=None, dtype="f32", items=None,
-              nthreads=None, block_table=None) -> np.ndarray:
+              nthreads=None, block_table=None, kv_fp8_scales=None) -> np.ndarray:
     """fp64 tree-masked GQA attention.
 
     q [N,Hq,D], k/v [B,Hkv,Lcap,D] as float32 arrays (dtype='f32') or as uint16
@@ -150,15 +157,22 @@ def attention(q, k, v, ctx_len, cu_nodes, parent, *, Hq, Hkv, scale=None, dtype=
     block_table: int32 [B, max_blocks] for paged caches; k/v are then pools
     [num_blocks, Hkv, block_size, D] and slot t of request b sits in block
     block_table[b, t // block_size] at row t % block_size.
+    kv_fp8_scales=(k_scale, v_scale): k/v are uint8 OCP FP8 E4M3 bytes whose
+    element values are the decoded bytes times the scale (q keeps dtype).
     """
     q = np.ascontiguousarray(q)
     k = np.ascontiguousarray(k)
     v = np.ascontiguousarray(v)
     code = {"f32": 0, "bf16": 1}[dtype]
-    if code == 0:
-        assert q.dtype == np.float32 and k.dtype == np.float32 and v.dtype == np.float32
+    kv_code, ks, vs = code, 1.0, 1.0
+    if kv_fp8_scales is not None:
+        assert k.dtype == np.uint8 and v.dtype == np.uint8
+        kv_code, (ks, vs) = 2, (float(np.float32(kv_fp8_scales[0])), float(np.float32(kv_fp8_scales[1])))
+    elif code == 0:
+        assert k.dtype == np.float32 and v.dtype == np.float32
     else:
-        assert q.dtype == np.uint16 and k.dtype == np.uint16 and v.dtype == np.uint16
+        assert k.dtype == np.uint16 and v.dtype == np.uint16
+    assert q.dtype == (np.float32 if code == 0 else np.uint16)
     D = int(k.shape[3])
     if block_table is None:
         B, Lcap = int(k.shape[0]), int(k.shape[2])
@@ -183,9 +197,9 @@ def attention(q, k, v, ctx_len, cu_nodes, parent, *, Hq, Hkv, scale=None, dtype=
         n_items = items.shape[0]
         out = np.zeros((n_items, D), dtype=np.float64)
         it_ptr = _ptr(items)
-    rc = _load().orc_attention_paged(B, Hq, Hkv, D, code, _ptr(q), _ptr(k), _ptr(v), Lcap, _ptr(ctx), _ptr(cu),
-                                     _ptr(par), float(scale), n_items, it_ptr, _ptr(out),
-                                     nthreads or _default_threads(), _ptr(bt), bs, mb, nb)
+    rc = _load().orc_attention_ex(B, Hq, Hkv, D, code, _ptr(q), _ptr(k), _ptr(v), Lcap, _ptr(ctx), _ptr(cu),
+                                  _ptr(par), float(scale), n_items, it_ptr, _ptr(out),
+                                  nthreads or _default_threads(), _ptr(bt), bs, mb, nb, kv_code, ks, vs)
     if rc != 0:
         raise ValueError("oracle attention: bad packing or tree")
     return out

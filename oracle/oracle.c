@@ -125,10 +125,23 @@ static void orc_parallel_for(int64_t n, int nthreads, void (*fn)(void*, int64_t)
 }
 
 /* ------------------------------------------------------------------------ */
+/* FP8 E4M3 in the OCP 8-bit floating point format (finite form, "E4M3FN"):
+ * sign, 4 exponent bits with bias 7, 3 mantissa bits; exponent 0 holds the
+ * subnormals m/8 * 2^-6; S.1111.111 is NaN and there is no infinity.      */
+double orc_fp8_e4m3(uint8_t x) {
+  int s = x >> 7, e = (x >> 3) & 15, m = x & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0) v = ldexp((double)m / 8.0, -6);
+  else v = ldexp(1.0 + (double)m / 8.0, e - 7);
+  return s ? -v : v;
+}
+
 /* Element access: fp32 as is, bf16 by placing its 16 bits on top of an fp32
- * (exact), both widened exactly to fp64.                                   */
+ * (exact), fp8 E4M3 decoded as above; all widened exactly to fp64.        */
 static double orc_load(const void* base, int dtype, int64_t idx) {
   if (dtype == 0) return (double)((const float*)base)[idx];
+  if (dtype == 2) return orc_fp8_e4m3(((const uint8_t*)base)[idx]);
   uint32_t bits = (uint32_t)((const uint16_t*)base)[idx] << 16;
   float f;
   memcpy(&f, &bits, sizeof f);
@@ -137,6 +150,8 @@ static double orc_load(const void* base, int dtype, int64_t idx) {
 
 typedef struct {
   int B, Hq, Hkv, D, dtype;
+  int kv_dtype;            /* element type of the caches (2: fp8 E4M3)  */
+  double k_scale, v_scale; /* cache element value = stored value * scale */
   const void *q, *k, *v;
   int64_t Lcap;
   const int32_t *ctx_len, *cu_nodes, *parent;
@@ -204,7 +219,7 @@ static void orc_attn_item(void* vctx, int64_t it) {
   for (int64_t t = 0; t < nkeys; ++t) {
     double acc = 0.0;
     for (int d = 0; d < c->D; ++d)
-      acc += orc_load(c->q, c->dtype, qbase + d) * orc_load(c->k, c->dtype, slot[t] + d);
+      acc += orc_load(c->q, c->dtype, qbase + d) * (c->k_scale * orc_load(c->k, c->kv_dtype, slot[t] + d));
     s[t] = c->scale * acc;
     if (s[t] > m) m = s[t];
   }
@@ -216,7 +231,7 @@ static void orc_attn_item(void* vctx, int64_t it) {
   for (int d = 0; d < c->D; ++d) o[d] = 0.0;
   for (int64_t t = 0; t < nkeys; ++t) {
     double w = s[t] / denom;
-    for (int d = 0; d < c->D; ++d) o[d] += w * orc_load(c->v, c->dtype, slot[t] + d);
+    for (int d = 0; d < c->D; ++d) o[d] += w * (c->v_scale * orc_load(c->v, c->kv_dtype, slot[t] + d));
   }
   free(s);
   free(slot);
@@ -224,13 +239,16 @@ static void orc_attn_item(void* vctx, int64_t it) {
 
 /* Attention for a list of (packed node, query head) pairs `items` [n_items,2]
  * (or, if items is NULL, for every node and head in order); out [n_items, D].
- * dtype 0 = fp32 inputs, 1 = bf16 inputs. block_table != NULL reads paged
- * caches (see orc_slot_index; Lcap = max_blocks * block_size). Returns 0, or
- * 1 on bad packing or a block id out of range.                            */
-int orc_attention_paged(int B, int Hq, int Hkv, int D, int dtype, const void* q, const void* k, const void* v,
-                        int64_t Lcap, const int32_t* ctx_len, const int32_t* cu_nodes, const int32_t* parent,
-                        double scale, int64_t n_items, const int64_t* items, double* out, int nthreads,
-                        const int32_t* block_table, int block_size, int max_blocks, int64_t num_blocks) {
+ * dtype 0 = fp32 inputs, 1 = bf16 inputs; kv_dtype the caches' type (the
+ * same, or 2 = fp8 E4M3 whose elements are scaled by k_scale / v_scale).
+ * block_table != NULL reads paged caches (see orc_slot_index; Lcap =
+ * max_blocks * block_size). Returns 0, or 1 on bad packing or a block id
+ * out of range.                                                           */
+int orc_attention_ex(int B, int Hq, int Hkv, int D, int dtype, const void* q, const void* k, const void* v,
+                     int64_t Lcap, const int32_t* ctx_len, const int32_t* cu_nodes, const int32_t* parent,
+                     double scale, int64_t n_items, const int64_t* items, double* out, int nthreads,
+                     const int32_t* block_table, int block_size, int max_blocks, int64_t num_blocks, int kv_dtype,
+                     double k_scale, double v_scale) {
   if (Hkv <= 0 || Hq % Hkv != 0 || D <= 0) return 1;
   if (block_table && (block_size <= 0 || max_blocks <= 0 || Lcap != (int64_t)block_size * max_blocks)) return 1;
   int64_t* all = NULL;
@@ -247,8 +265,8 @@ int orc_attention_paged(int B, int Hq, int Hkv, int D, int dtype, const void* q,
     items = all;
   }
   int err = 0;
-  orc_attn_ctx c = {B, Hq, Hkv, D, dtype, q, k, v, Lcap, ctx_len, cu_nodes, parent, scale, items, out, &err,
-                    block_table, block_size, max_blocks, num_blocks};
+  orc_attn_ctx c = {B, Hq, Hkv, D, dtype, kv_dtype, k_scale, v_scale, q, k, v, Lcap, ctx_len, cu_nodes,
+                    parent, scale, items, out, &err, block_table, block_size, max_blocks, num_blocks};
   orc_parallel_for(n_items, nthreads, orc_attn_item, &c);
   free(all);
   return err;
@@ -257,8 +275,8 @@ int orc_attention_paged(int B, int Hq, int Hkv, int D, int dtype, const void* q,
 int orc_attention(int B, int Hq, int Hkv, int D, int dtype, const void* q, const void* k, const void* v,
                   int64_t Lcap, const int32_t* ctx_len, const int32_t* cu_nodes, const int32_t* parent,
                   double scale, int64_t n_items, const int64_t* items, double* out, int nthreads) {
-  return orc_attention_paged(B, Hq, Hkv, D, dtype, q, k, v, Lcap, ctx_len, cu_nodes, parent, scale, n_items, items,
-                             out, nthreads, NULL, 0, 0, 0);
+  return orc_attention_ex(B, Hq, Hkv, D, dtype, q, k, v, Lcap, ctx_len, cu_nodes, parent, scale, n_items, items,
+                          out, nthreads, NULL, 0, 0, 0, dtype, 1.0, 1.0);
 }
 
 /* ------------------------------------------------------------------------ */

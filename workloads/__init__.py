@@ -7,7 +7,7 @@ bench on one side and the oracle on the other.
 """
 from .configs import CONFIGS, C4_BUCKETS, WorkloadConfig, get_config, scaled
 from .gen import (chain_tree, eagle_tree, generate, super_tree_sizes, super_tree_parents, poison_unused_slots,
-                  to_paged)
+                  to_fp8_e4m3, to_paged)
 
 __all__ = ["CONFIGS", "C4_BUCKETS", "WorkloadConfig", "get_config", "scaled", "chain_tree", "eagle_tree",
            "generate", "super_tree_sizes", "super_tree_parents", "poison_unused_slots"]

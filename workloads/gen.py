@@ -229,3 +229,10 @@ def to_paged(k_cache, v_cache, block_size: int, rng: np.random.Generator, spare_
         return pool
 
     return pool_of(k_cache), pool_of(v_cache), perm
+
+
+def to_fp8_e4m3(x, scale: float):
+    """x / scale rounded to OCP FP8 E4M3 (finite form) by torch, returned as
+    uint8 bytes (a caller's fp8 cache holds these; value = byte * scale)."""
+    t = torch.as_tensor(x).float() / scale
+    return t.clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
