@@ -44,12 +44,15 @@ KERNEL_SOURCES = {
 }
 
 
-def attention_kernel_name(w, cfg) -> str:
+def attention_kernel_name(w, cfg, kv_fp8: bool = False) -> str:
     """Which attention kernel the library's plan launches: fp32 caches take the
     VALU kernel; bf16 takes 16x16 MFMA tiles when a KV head carries at most 64
-    query rows (Hq/Hkv heads x max_T nodes), else 32x32 tiles."""
+    query rows (Hq/Hkv heads x max_T nodes), else 32x32 tiles; fp8 caches
+    always take the 16x16 kernel."""
     if w["dtype"] != "bf16":
         return "attn_valu_kernel"
+    if kv_fp8:
+        return "attn_mfma_kernel"
     return "attn_mfma_kernel" if (cfg.Hq // cfg.Hkv) * w["max_T"] <= 64 else "attn_mfma32_kernel"
 
 
@@ -123,6 +126,8 @@ def parse_args():
     ap.add_argument("--paged", type=int, default=0, metavar="BLOCK",
                     help="lay the KV caches out as a shuffled pool of BLOCK-slot blocks read through a block "
                          "table (BLOCK a multiple of 64; 0 = contiguous caches)")
+    ap.add_argument("--kv-fp8", action="store_true",
+                    help="quantise the KV caches to OCP FP8 E4M3 bytes with per-tensor scales (bf16 workloads)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES three times (calibrates the HBM "
                          "byte counters of rocprofv3 against a kernel of known traffic) and exit")
@@ -189,15 +194,17 @@ def counter_traffic(kernel: str, workload: str):
     return float(m_bytes.group(1))
 
 
-def attention_bytes(w) -> float:
+def attention_bytes(w, kv_elem: int = 0) -> float:
     """Algorithmic bytes of one attention launch: every K and V slot a node can
-    see (context + draft slots) once, the queries once, the fp32 outputs once."""
+    see (context + draft slots) once, the queries once, the fp32 outputs once.
+    kv_elem: bytes per cache element (0: the query element size; 1: fp8)."""
     e = 2 if w["dtype"] == "bf16" else 4
+    ekv = kv_elem or e
     kv = 0
     for b in range(w["B"]):
         T = int(w["cu_nodes"][b + 1] - w["cu_nodes"][b])
         if T > 0:
-            kv += w["Hkv"] * (int(w["ctx_len"][b]) + T) * w["D"] * 2 * e
+            kv += w["Hkv"] * (int(w["ctx_len"][b]) + T) * w["D"] * 2 * ekv
     return float(kv + w["N"] * w["Hq"] * w["D"] * (e + 4))
 
 
@@ -301,6 +308,13 @@ def main():
     set_bytes = attention_bytes(w) + 8 * w["V"] * (w["N"] + w["B"])
     n_sets = max(1, min(MAX_INPUT_SETS, math.ceil(ROTATE_BYTES / set_bytes)))
     sets = [w] + [generate(cfg, dev, candidates=cand) for _ in range(n_sets - 1)]
+    if args.kv_fp8:
+        from workloads import to_fp8_e4m3
+        for x in sets:
+            ks = float(x["k_cache"].float().abs().amax()) / 448.0
+            vs = float(x["v_cache"].float().abs().amax()) / 448.0
+            x["k_cache"], x["v_cache"] = to_fp8_e4m3(x["k_cache"], ks), to_fp8_e4m3(x["v_cache"], vs)
+            x["kv_scales"] = (ks, vs)
     if args.paged:
         import numpy as np
 
@@ -324,10 +338,11 @@ def main():
         for x in sets:
             if args.paged:
                 a = sv.AttnCall(x["q"], x["k_pool"], x["v_pool"], x["ctx_len_t"], x["cu_nodes_t"],
-                                parent=x["parent_t"], max_nodes=x["max_T"], block_table=x["block_table"])
+                                parent=x["parent_t"], max_nodes=x["max_T"], block_table=x["block_table"],
+                                kv_fp8_scales=x.get("kv_scales"))
             else:
                 a = sv.AttnCall(x["q"], x["k_cache"], x["v_cache"], x["ctx_len_t"], x["cu_nodes_t"],
-                                parent=x["parent_t"], max_nodes=x["max_T"])
+                                parent=x["parent_t"], max_nodes=x["max_T"], kv_fp8_scales=x.get("kv_scales"))
             s = sv.SampleCall(a.keep["cu"], x["parent_t"], x["draft_tokens"], x["logits"],
                               None if det else x["draft_probs"], temperature=cfg.temperature, seed=x["seed"],
                               max_nodes=x["max_T"], residual_passes=True, min_p=args.min_p,
@@ -380,13 +395,13 @@ def main():
     passes = s.passes.double()
 
     kernels = {}
-    attn_b, attn_f = attention_bytes(w), attention_flops(w)
+    attn_b, attn_f = attention_bytes(w, 1 if args.kv_fp8 else 0), attention_flops(w)
     rs_b = row_stats_bytes(w)
     if use_events:
         attn_ms = sum(hev.ms(4 * i, 4 * i + 1) for i in range(K)) / K
         rs_ms = sum(hev.ms(4 * i + 2, 4 * i + 3) for i in range(K)) / K
         hev.close()
-        attn_name = attention_kernel_name(w, cfg)
+        attn_name = attention_kernel_name(w, cfg, args.kv_fp8)
         kernels[attn_name] = {"us": attn_ms * 1e3, "alg_bytes": attn_b, "GB_s": attn_b / attn_ms / 1e6,
                               "TFLOP_s": attn_f / attn_ms / 1e9}
         kernels["row_stats_kernel"] = {"us": rs_ms * 1e3, "alg_bytes": rs_b, "GB_s": rs_b / rs_ms / 1e6}
@@ -399,7 +414,8 @@ def main():
                                             "residual_pass_bytes": float(passes.sum().item()) * per_pass}
         dom = max((k for k in kernels if "alg_bytes" in kernels[k]), key=lambda k: kernels[k]["us"])
         dk = kernels[dom]
-        traffic = counter_traffic(dom, cfg.name)
+        # the committed counters were taken with contiguous bf16 caches
+        traffic = counter_traffic(dom, cfg.name) if not (args.paged or args.kv_fp8) else None
         roofline = {"kernel": dom, "bound": "hbm", "achieved": round(dk["GB_s"], 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(dk["GB_s"] / HBM_PEAK_GBS, 4),
                     "traffic": traffic, "measured_copy_GB_s": round(copy_bandwidth(), 1)}
@@ -425,7 +441,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16+f32" if w["dtype"] == "bf16" else "f32",
+        "dtype": ("bf16+fp8+f32" if args.kv_fp8 else "bf16+f32") if w["dtype"] == "bf16" else "f32",
         "data": "synthetic (seeded; no dataset, no model weights)",
         "config": {"workload": cfg.name, "B": w["B"], "draft_nodes": w["N"], "max_T": w["max_T"], "L": cfg.L,
                    "Hq": cfg.Hq, "Hkv": cfg.Hkv, "D": cfg.D, "kv_dtype": cfg.dtype, "V": cfg.V,
@@ -433,6 +449,7 @@ def main():
                    **({"siblings": "deterministic (top-k of q)"} if det else {}),
                    **({"eta": list(args.eta)} if args.eta else {}),
                    **({"kv_layout": f"paged, {args.paged}-slot blocks"} if args.paged else {}),
+                   **({"kv_dtype": "fp8 e4m3 (scaled)"} if args.kv_fp8 else {}),
                    **({"rule": args.rule, "rule_param": args.rule_param} if args.rule in ("lenience", "interpolation")
                       else {"rule": args.rule} if args.rule == "truncation" else {})},
         "roofline": roofline,

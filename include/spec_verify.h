@@ -131,6 +131,15 @@ typedef struct {
   int32_t block_size;
   int32_t max_blocks;
   int64_t num_blocks;
+  /* FP8 caches (optional; with dtype SV_BF16 for q). kv_fp8 = 1: k_cache and
+   * v_cache hold OCP FP8 E4M3 (finite form) bytes, contiguous or paged as
+   * above, and the value of a key (value) element is its byte's value times
+   * k_scale (v_scale), both finite and > 0. E4M3 values are exact in bf16;
+   * k_scale is folded into the softmax scale and v_scale into the output.
+   * Every tree runs on 64-row workgroups (row groups for wider trees).     */
+  int32_t kv_fp8;
+  float k_scale;
+  float v_scale;
 } sv_attn_args;
 
 /* ------------------------------------------------------------------------ */

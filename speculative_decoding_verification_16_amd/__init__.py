@@ -38,7 +38,8 @@ class SvAttnArgs(ctypes.Structure):
                 ("dtype", _i32), ("q", _P), ("k_cache", _P), ("v_cache", _P), ("Lcap", _i64), ("ctx_len", _P),
                 ("cu_nodes", _P), ("parent", _P), ("anc_mask", _P), ("scale", _f32), ("num_splits", _i32),
                 ("out", _P), ("status", _P), ("prof_start", _P), ("prof_stop", _P), ("block_table", _P),
-                ("block_size", _i32), ("max_blocks", _i32), ("num_blocks", _i64)]
+                ("block_size", _i32), ("max_blocks", _i32), ("num_blocks", _i64), ("kv_fp8", _i32),
+                ("k_scale", _f32), ("v_scale", _f32)]
 
 
 class SvSampleArgs(ctypes.Structure):
@@ -129,13 +130,18 @@ class AttnCall:
     """Prepared spec_verify_attn call (outputs and workspace allocated once)."""
 
     def __init__(self, q, k_cache, v_cache, ctx_len, cu_nodes, *, parent=None, anc_mask=None, max_nodes=0,
-                 scale=0.0, num_splits=0, out=None, status=None, block_table=None):
+                 scale=0.0, num_splits=0, out=None, status=None, block_table=None, kv_fp8_scales=None):
         """block_table: int32 [B, max_blocks] for paged caches; k_cache and
-        v_cache are then pools [num_blocks, Hkv, block_size, D]."""
+        v_cache are then pools [num_blocks, Hkv, block_size, D].
+        kv_fp8_scales=(k_scale, v_scale): k_cache / v_cache are uint8 tensors
+        of OCP FP8 E4M3 bytes (q bf16)."""
         load_library()
         dev = q.device
         assert q.is_cuda and q.dim() == 3 and k_cache.dim() == 4 and v_cache.shape == k_cache.shape
-        assert q.dtype == k_cache.dtype == v_cache.dtype and q.dtype in (torch.float32, torch.bfloat16)
+        if kv_fp8_scales is None:
+            assert q.dtype == k_cache.dtype == v_cache.dtype and q.dtype in (torch.float32, torch.bfloat16)
+        else:
+            assert q.dtype == torch.bfloat16 and k_cache.dtype == v_cache.dtype == torch.uint8
         for t in (q, k_cache, v_cache):
             assert t.is_contiguous()
         N, Hq, D = q.shape
@@ -167,6 +173,8 @@ class AttnCall:
         if block_table is not None:
             a.block_table, a.block_size, a.max_blocks, a.num_blocks = _ptr(block_table), block_size, max_blocks, \
                 num_blocks
+        if kv_fp8_scales is not None:
+            a.kv_fp8, a.k_scale, a.v_scale = 1, float(kv_fp8_scales[0]), float(kv_fp8_scales[1])
         self.args = a
         lib = load_library()
         self.ws_bytes = lib.spec_verify_workspace_size(ctypes.byref(a), None)

@@ -38,6 +38,10 @@ sv_status check_attn(const sv_attn_args* a) {
     return fail(SV_ERR_INVALID_ARG, "need Hq > 0, Hkv > 0 and Hq %% Hkv == 0");
   if (a->D != 64 && a->D != 128) return fail(SV_ERR_UNSUPPORTED, "head dim D must be 64 or 128");
   if (a->dtype != SV_F32 && a->dtype != SV_BF16) return fail(SV_ERR_INVALID_ARG, "dtype must be SV_F32 or SV_BF16");
+  if (a->kv_fp8 != 0 && a->kv_fp8 != 1) return fail(SV_ERR_INVALID_ARG, "kv_fp8 must be 0 or 1");
+  if (a->kv_fp8 && a->dtype != SV_BF16) return fail(SV_ERR_UNSUPPORTED, "fp8 caches need bf16 queries (dtype SV_BF16)");
+  if (a->kv_fp8 && !(a->k_scale > 0.f && a->v_scale > 0.f && !isinf(a->k_scale) && !isinf(a->v_scale)))
+    return fail(SV_ERR_INVALID_ARG, "k_scale and v_scale must be finite and > 0");
   if (a->Lcap < 1 || a->Lcap > (1ll << 24)) return fail(SV_ERR_INVALID_ARG, "Lcap must be in [1, 2^24]");
   if (a->block_table) {
     if (a->block_size < 64 || (a->block_size & (a->block_size - 1)) != 0)
@@ -55,7 +59,7 @@ sv_status check_attn(const sv_attn_args* a) {
     return fail(SV_ERR_UNSUPPORTED, "N * Hq * D must stay below 2^31");
   // contiguous caches are addressed per (request, KV head) with 32-bit offsets;
   // paged ones per 64-key tile
-  const int64_t kv_head_bytes = a->Lcap * a->D * (a->dtype == SV_BF16 ? 2 : 4);
+  const int64_t kv_head_bytes = a->Lcap * a->D * (a->kv_fp8 ? 1 : (a->dtype == SV_BF16 ? 2 : 4));
   if (!a->block_table && kv_head_bytes >= (1ll << 31))
     return fail(SV_ERR_UNSUPPORTED, "Lcap * D * element size must stay below 2^31");
   if (a->B == 0) return SV_OK;
@@ -81,6 +85,7 @@ sv::AttnPlan plan_attn(const sv_attn_args* a) {
     // 32x32 MFMA tiles, 256-row workgroups when every KV head fits in one,
     // otherwise 128-row workgroups
     pl.rows_per_wg = rmax <= 64 ? 64 : (rmax <= 128 || rmax > 256 ? 128 : 256);
+    if (a->kv_fp8) pl.rows_per_wg = 64;  // the fp8 caches run on the 64-row (16x16 MFMA) kernel
   } else {
     pl.rows_per_wg = 8;
   }
@@ -98,7 +103,7 @@ sv::AttnPlan plan_attn(const sv_attn_args* a) {
     const int64_t slots = pl.rows_per_wg > 128 ? 256 : 512;  // 8-wave workgroups: one per CU
     const int64_t want = (slots + items - 1) / (items > 0 ? items : 1);
     const int64_t by_len = a->Lcap / 256 > 0 ? a->Lcap / 256 : 1;
-    const int64_t esz = a->dtype == SV_BF16 ? 2 : 4;
+    const int64_t esz = a->kv_fp8 ? 1 : (a->dtype == SV_BF16 ? 2 : 4);
     const int64_t kv_bytes = 2 * (int64_t)a->B * a->Hkv * a->Lcap * a->D * esz;
     const int64_t part_bytes = 2 * (int64_t)a->total_nodes * a->Hq * (a->D + 2) * 4;
     const int64_t by_traffic = part_bytes > 0 ? kv_bytes / (4 * part_bytes) : 256;
@@ -300,7 +305,9 @@ sv_status run_attn(const sv_attn_args* a, char* ws, const WsLayout& w, hipStream
   p.items = pl.compact ? (const int32_t*)(ws + w.items) : nullptr;
   p.item_tot = pl.compact ? (const int32_t*)(ws + w.item_tot) : nullptr;
   const float scale = a->scale > 0.f ? a->scale : (float)(1.0 / sqrt((double)a->D));
-  p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  p.kv_fp8 = a->kv_fp8 != 0;
+  p.v_scale = a->kv_fp8 ? a->v_scale : 1.f;
+  p.scale_log2 = (float)((double)scale * (a->kv_fp8 ? (double)a->k_scale : 1.0) * 1.4426950408889634);
   p.status = a->status;
   p.block_table = a->block_table;
   p.block_size = a->block_table ? a->block_size : 0;

@@ -256,9 +256,47 @@ __global__ __launch_bounds__(1024) void attn_prep_kernel(AttnParams p, const int
 // Decode-shaped attention is bound by memory latency x bytes in flight per
 // CU, and measured on MI355X several independent workgroups per CU (WPE
 // waves per SIMD) hide it better than a deeper ring in fewer workgroups.
-template <int D, int NBUF, int NW, int RBW, int WPE = 2, bool PAGED = false>
+// FP8 caches (OCP E4M3, finite form): eight bytes per 16-byte LDS unit are
+// loaded and widened to bf16 (every E4M3 value is exact in bf16) before the
+// LDS write; k_scale is folded into the softmax scale by the host and
+// v_scale multiplies the output. The rest of the kernel is unchanged.
+__device__ __forceinline__ i32x4_t widen_fp8x8(i32x2_t x) {
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)x.x, 1.0f, false);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)x.x, 1.0f, true);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)x.y, 1.0f, false);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)x.y, 1.0f, true);
+  return i32x4_t{(int)__builtin_bit_cast(uint32_t, a), (int)__builtin_bit_cast(uint32_t, b),
+                 (int)__builtin_bit_cast(uint32_t, c), (int)__builtin_bit_cast(uint32_t, d)};
+}
+
+// Loads are non-temporal when the workgroup is the only reader of its key
+// range (one row group per job); with several row groups (wide trees on fp8
+// caches) they go through L2, where the job's other row groups, placed on the
+// same XCD, find them.
+template <bool FP8>
+struct KvUnit {
+  using T = i32x4_t;  // one 16-byte unit of bf16
+  static __device__ __forceinline__ T load(__amdgpu_buffer_rsrc_t r, int off, int so, bool once) {
+    return once ? __builtin_amdgcn_raw_buffer_load_b128(r, off, so, kAuxNT)
+                : __builtin_amdgcn_raw_buffer_load_b128(r, off, so, 0);
+  }
+  static __device__ __forceinline__ i32x4_t bf16(T x) { return x; }
+};
+template <>
+struct KvUnit<true> {
+  using T = i32x2_t;  // the same unit as eight fp8 bytes
+  static __device__ __forceinline__ T load(__amdgpu_buffer_rsrc_t r, int off, int so, bool once) {
+    return __builtin_bit_cast(i32x2_t, once ? __builtin_amdgcn_raw_buffer_load_b64(r, off, so, kAuxNT)
+                                            : __builtin_amdgcn_raw_buffer_load_b64(r, off, so, 0));
+  }
+  static __device__ __forceinline__ i32x4_t bf16(T x) { return widen_fp8x8(x); }
+};
+
+template <int D, int NBUF, int NW, int RBW, int WPE = 2, bool PAGED = false, bool FP8 = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE)))
 void attn_mfma_kernel(AttnParams p) {
+  constexpr int ESZ = FP8 ? 1 : 2;   // bytes per cache element
+  using KU = KvUnit<FP8>;
   constexpr int NT = 64 * NW;        // threads
   constexpr int KT = 64;             // keys per tile
   constexpr int KS = D / 32;         // k-steps of S^T (32 head dims each)
@@ -331,25 +369,25 @@ void attn_mfma_kernel(AttnParams p) {
   }
 
   const int64_t head_off = PAGED ? 0 : ((int64_t)b * p.Hkv + g) * p.Lcap * D;  // paged: per tile instead
-  const uint16_t* kbase = (const uint16_t*)p.k + head_off;
-  const uint16_t* vbase = (const uint16_t*)p.v + head_off;
+  const char* kbase = (const char*)p.k + head_off * ESZ;
+  const char* vbase = (const char*)p.v + head_off * ESZ;
 
   // K/V tiles come in through buffer loads: the resource covers exactly the
   // keys [0, ke) of this (request, KV head), so a key past the split end reads
   // as zero (never a stray cache slot), and the per-thread offsets are 32-bit
   // constants with the tile start in the scalar offset.
   const __amdgpu_buffer_rsrc_t krs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, ke * D * 2, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, ke * D * ESZ, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, ke * D * 2, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, ke * D * ESZ, 0x00020000);
   int koff[PER_THREAD];  // K and V share the per-thread offsets (16-byte unit c of the tile)
 #pragma unroll
   for (int i = 0; i < PER_THREAD; ++i) {
     const int c = tid + NT * i;
-    koff[i] = ((c / UNITS) * D + 8 * (c % UNITS)) * 2;
+    koff[i] = ((c / UNITS) * D + 8 * (c % UNITS)) * ESZ;
   }
-  i32x4_t kreg[NBUF][PER_THREAD];
-  i32x4_t vreg[NBUF][PER_THREAD];
+  typename KU::T kreg[NBUF][PER_THREAD];
+  typename KU::T vreg[NBUF][PER_THREAD];
   // V^T operand addressing for the transposed LDS reads (see the PV step)
   const int vt_lane = (4 * g4 + (l16 >> 2)) * D + 4 * (l16 & 1) + 8 * ((l16 >> 1) & 1);
   const int vt_sw = l16 >> 2;
@@ -370,15 +408,16 @@ void attn_mfma_kernel(AttnParams p) {
   // one resource per tile, over that tile's block rows.
   PagedIds pg;
   if (PAGED) paged_load(p, b, kb, pg);
+  const bool once = R <= ROWS;  // the only reader of this key range
 #pragma unroll
   for (int s = 0; s < NBUF; ++s) {
-    const int so = PAGED ? 0 : (kb + s * KT) * D * 2;
-    const __amdgpu_buffer_rsrc_t kr = PAGED ? paged_tile<2>(p, p.k, b, g, kb + s * KT, ke, D, pg) : krs;
-    const __amdgpu_buffer_rsrc_t vr = PAGED ? paged_tile<2>(p, p.v, b, g, kb + s * KT, ke, D, pg) : vrs;
+    const int so = PAGED ? 0 : (kb + s * KT) * D * ESZ;
+    const __amdgpu_buffer_rsrc_t kr = PAGED ? paged_tile<ESZ>(p, p.k, b, g, kb + s * KT, ke, D, pg) : krs;
+    const __amdgpu_buffer_rsrc_t vr = PAGED ? paged_tile<ESZ>(p, p.v, b, g, kb + s * KT, ke, D, pg) : vrs;
 #pragma unroll
     for (int i = 0; i < PER_THREAD; ++i) {
-      kreg[s][i] = __builtin_amdgcn_raw_buffer_load_b128(kr, koff[i], so, kAuxNT);
-      vreg[s][i] = __builtin_amdgcn_raw_buffer_load_b128(vr, koff[i], so, kAuxNT);
+      kreg[s][i] = KU::load(kr, koff[i], so, once);
+      vreg[s][i] = KU::load(vr, koff[i], so, once);
     }
     // keep the slots' loads in slot order, as the ring refills them: the
     // wait before writing slot s can then leave the later slots in flight
@@ -394,19 +433,19 @@ void attn_mfma_kernel(AttnParams p) {
       for (int i = 0; i < PER_THREAD; ++i) {
         const int c = tid + NT * i;
         const int kk = c / UNITS, dc = c % UNITS;
-        *(i32x4_t*)(Ks + kk * D + 8 * (dc ^ (kk & 7))) = kreg[s][i];
-        *(i32x4_t*)(Vs + kk * D + 8 * (dc ^ (2 * (kk & 3)))) = vreg[s][i];
+        *(i32x4_t*)(Ks + kk * D + 8 * (dc ^ (kk & 7))) = KU::bf16(kreg[s][i]);
+        *(i32x4_t*)(Vs + kk * D + 8 * (dc ^ (2 * (kk & 3)))) = KU::bf16(vreg[s][i]);
       }
       __syncthreads();
       // refill this ring slot with the tile NBUF positions ahead
       {
-        const int so = PAGED ? 0 : (t0 + NBUF * KT) * D * 2;
-        const __amdgpu_buffer_rsrc_t kr = PAGED ? paged_tile<2>(p, p.k, b, g, t0 + NBUF * KT, ke, D, pg) : krs;
-        const __amdgpu_buffer_rsrc_t vr = PAGED ? paged_tile<2>(p, p.v, b, g, t0 + NBUF * KT, ke, D, pg) : vrs;
+        const int so = PAGED ? 0 : (t0 + NBUF * KT) * D * ESZ;
+        const __amdgpu_buffer_rsrc_t kr = PAGED ? paged_tile<ESZ>(p, p.k, b, g, t0 + NBUF * KT, ke, D, pg) : krs;
+        const __amdgpu_buffer_rsrc_t vr = PAGED ? paged_tile<ESZ>(p, p.v, b, g, t0 + NBUF * KT, ke, D, pg) : vrs;
 #pragma unroll
         for (int i = 0; i < PER_THREAD; ++i) {
-          kreg[s][i] = __builtin_amdgcn_raw_buffer_load_b128(kr, koff[i], so, kAuxNT);
-          vreg[s][i] = __builtin_amdgcn_raw_buffer_load_b128(vr, koff[i], so, kAuxNT);
+          kreg[s][i] = KU::load(kr, koff[i], so, once);
+          vreg[s][i] = KU::load(vr, koff[i], so, once);
         }
       }
       // past the range (last ring round): the slot was only cycled; waves
@@ -534,7 +573,7 @@ void attn_mfma_kernel(AttnParams p) {
     const float lt = row_sum4(l[i]);
     if (orow[i] < 0) continue;
     if (p.splits == 1) {
-      const float inv = 1.0f / lt;
+      const float inv = (FP8 ? p.v_scale : 1.0f) / lt;
       float* op = p.out + (int64_t)orow[i] * D + 4 * g4;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
@@ -545,7 +584,7 @@ void attn_mfma_kernel(AttnParams p) {
       float* op = p.o_part + ((int64_t)split * NH + orow[i]) * D + 4 * g4;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const f32x4_t v = o[i][db];
+        const f32x4_t v = FP8 ? o[i][db] * p.v_scale : o[i][db];
         *(float4*)(op + 16 * db) = make_float4(v[0], v[1], v[2], v[3]);
       }
       if (g4 == 0) p.ml_part[(int64_t)split * NH + orow[i]] = make_float2(m[i], lt);
@@ -1077,7 +1116,8 @@ hipError_t launch_attn_prep(const AttnParams& p, const AttnPlan& plan, const int
 // faster on trees of up to 272 rows whose sizes vary).
 template <int D, bool PAGED>
 static void launch_mfma_d(const AttnParams& p, int rows_per_wg, dim3 grid, hipStream_t stream) {
-  if (rows_per_wg <= 64) attn_mfma_kernel<D, 1, 4, 1, 3, PAGED><<<grid, dim3(256), 0, stream>>>(p);
+  if (p.kv_fp8) attn_mfma_kernel<D, 1, 4, 1, 3, PAGED, true><<<grid, dim3(256), 0, stream>>>(p);  // 64-row groups
+  else if (rows_per_wg <= 64) attn_mfma_kernel<D, 1, 4, 1, 3, PAGED><<<grid, dim3(256), 0, stream>>>(p);
   else if (rows_per_wg <= 128) attn_mfma32_kernel<D, 4, 2, PAGED><<<grid, dim3(256), 0, stream>>>(p);
   else attn_mfma32_kernel<D, 8, 1, PAGED><<<grid, dim3(512), 0, stream>>>(p);
 }

@@ -42,6 +42,10 @@ struct AttnParams {
   int32_t block_size, max_blocks;
   int32_t bs_shift;            // log2(block_size)
   int64_t num_blocks;
+  // fp8 caches (OCP E4M3 bytes): k_scale is folded into scale_log2, v_scale
+  // multiplies the output
+  bool kv_fp8;
+  float v_scale;
 };
 
 struct AttnPlan {

@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import speculative_decoding_verification_16_amd as sv
 from gpu_helpers import ATTN_TOL, host_bits, oracle_attention, sample_items
 from workloads import C4_BUCKETS, CONFIGS, generate, get_config, scaled
@@ -229,7 +230,8 @@ def _paged(w, bs, seed, share=0):
     B, Hkv, Lcap, D = k.shape
     Lp = (Lcap + bs - 1) // bs * bs
     if Lp != Lcap:
-        pad = torch.full((B, Hkv, Lp - Lcap, D), float("nan"), dtype=k.dtype, device=k.device)
+        fill = 0x7F if k.dtype == torch.uint8 else float("nan")  # NaN (0x7F in fp8 E4M3)
+        pad = torch.full((B, Hkv, Lp - Lcap, D), fill, dtype=k.dtype, device=k.device)
         k, v = torch.cat([k, pad], dim=2).contiguous(), torch.cat([v, pad], dim=2).contiguous()
     kp, vp, bt = to_paged(k, v, bs, np.random.default_rng(seed), share_prefix_blocks=share)
     return kp.contiguous(), vp.contiguous(), torch.from_numpy(bt).cuda(), k, v
@@ -304,3 +306,81 @@ def test_paged_attention_shared_prefix_and_bad_block():
     with pytest.raises(sv.SpecVerifyError):  # block size not a multiple of 64
         sv.attn(w["q"], odd, odd, w["ctx_len_t"], w["cu_nodes_t"], parent=w["parent_t"], max_nodes=w["max_T"],
                 block_table=bt)
+
+
+# ---- fp8 (OCP E4M3) KV caches ------------------------------------------------------
+FP8 = ["c2_small", "c2_long_ctx", "c3_small", "c5_small", "c4_small", "bf16_d64", "bf16_d64_tree_256rows",
+       "tree_180rows", "c5_trees_upto_256rows", "wide_tree_rowgroups", "no_context"]
+K_SCALE, V_SCALE = 1.0 / 64, 1.0 / 128
+
+
+def _fp8_caches(w, seed):
+    """The workload's caches scaled by random magnitudes 2^U(-8, 1) (K) and
+    2^U(-8, 0) (V), so that the bytes span subnormals to the clamp at 448,
+    then quantised to E4M3 bytes (NaN poison stays NaN)."""
+    from workloads import to_fp8_e4m3
+
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    k, v = w["k_cache"].float(), w["v_cache"].float()
+    mk = torch.exp2(torch.rand(k.shape, generator=g, device="cuda") * 9 - 8)
+    mv = torch.exp2(torch.rand(v.shape, generator=g, device="cuda") * 8 - 8)
+    return to_fp8_e4m3(k * mk, K_SCALE).contiguous(), to_fp8_e4m3(v * mv, V_SCALE).contiguous()
+
+
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("splits", [0, 3])
+@pytest.mark.parametrize("name", FP8)
+def test_fp8_attention_matches(name, splits, paged):
+    cfg = SMALL[name]
+    w = generate(cfg, "cuda", sample=False, poison=True)
+    print(f"[attn-fp8] {name} splits={splits} paged={paged} B={w['B']} N={w['N']} L={cfg.L}", flush=True)
+    k8, v8 = _fp8_caches(w, 1301)
+    kw, bt = {}, None
+    if paged:
+        kp, vp, btt, _, _ = _paged({**w, "k_cache": k8, "v_cache": v8}, 128, 1311)
+        k8, v8, bt = kp, vp, btt
+        kw = {"block_table": bt}
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = sv.attn(w["q"], k8, v8, w["ctx_len_t"], w["cu_nodes_t"], parent=w["parent_t"], max_nodes=w["max_T"],
+                  num_splits=splits, status=st, kv_fp8_scales=(K_SCALE, V_SCALE), **kw)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0, sv.status_names(int(st.item()))
+    ref = oracle.attention(host_bits(w["q"]), k8.cpu().numpy(), v8.cpu().numpy(), w["ctx_len"], w["cu_nodes"],
+                           w["parent"], Hq=w["Hq"], Hkv=w["Hkv"], dtype="bf16",
+                           block_table=None if bt is None else bt.cpu().numpy(), kv_fp8_scales=(K_SCALE, V_SCALE))
+    err = float(np.abs(out.cpu().numpy() - ref).max())
+    assert err <= ATTN_TOL["bf16"], err
+
+
+@pytest.mark.parametrize("name", ["c4_L32768_B8_T1", "c5_super_tree"])
+def test_fp8_attention_full_size(name):
+    cfg = get_config(name)
+    w = generate(cfg, "cuda", sample=False)
+    print(f"[attn-fp8-full] {name} B={w['B']} N={w['N']} L={cfg.L}", flush=True)
+    k8, v8 = _fp8_caches(w, 1321)
+    del w["k_cache"], w["v_cache"]
+    out = sv.attn(w["q"], k8, v8, w["ctx_len_t"], w["cu_nodes_t"], parent=w["parent_t"], max_nodes=w["max_T"],
+                  kv_fp8_scales=(K_SCALE, V_SCALE))
+    torch.cuda.synchronize()
+    items = sample_items(w, 24, seed=7)
+    ref = oracle.attention(host_bits(w["q"]), k8.cpu().numpy(), v8.cpu().numpy(), w["ctx_len"], w["cu_nodes"],
+                           w["parent"], Hq=w["Hq"], Hkv=w["Hkv"], dtype="bf16", items=items,
+                           kv_fp8_scales=(K_SCALE, V_SCALE))
+    got = out.cpu().numpy()[items[:, 0], items[:, 1]]
+    assert float(np.abs(got - ref).max()) <= ATTN_TOL["bf16"]
+
+
+def test_fp8_attention_arguments():
+    cfg = SMALL["f32_tree"]
+    w = generate(cfg, "cuda", sample=False)
+    u8 = torch.zeros(w["k_cache"].shape, dtype=torch.uint8, device="cuda")
+    with pytest.raises((sv.SpecVerifyError, AssertionError)):  # fp8 caches need bf16 queries
+        sv.attn(w["q"], u8, u8, w["ctx_len_t"], w["cu_nodes_t"], parent=w["parent_t"], max_nodes=w["max_T"],
+                kv_fp8_scales=(1.0, 1.0))
+    w2 = generate(SMALL["c2_small"], "cuda", sample=False)
+    u8 = torch.zeros(w2["k_cache"].shape, dtype=torch.uint8, device="cuda")
+    for bad in ((0.0, 1.0), (1.0, float("inf")), (-1.0, 1.0)):
+        with pytest.raises(sv.SpecVerifyError):
+            sv.attn(w2["q"], u8, u8, w2["ctx_len_t"], w2["cu_nodes_t"], parent=w2["parent_t"],
+                    max_nodes=w2["max_T"], kv_fp8_scales=bad)

@@ -211,7 +211,8 @@ def to_paged(k_cache, v_cache, block_size: int, rng: np.random.Generator, spare_
 
     def pool_of(x):
         if is_torch:
-            pool = torch.full((nblk, Hkv, block_size, D), float("nan"), dtype=x.dtype, device=x.device)
+            fill = 0x7F if x.dtype == torch.uint8 else float("nan")  # 0x7F: the fp8 E4M3 NaN
+            pool = torch.full((nblk, Hkv, block_size, D), fill, dtype=x.dtype, device=x.device)
             blocks = x.reshape(B, Hkv, mb, block_size, D).permute(0, 2, 1, 3, 4)
             for b in range(B):
                 pool[torch.as_tensor(perm[b], device=x.device).long()] = blocks[b]
@@ -219,7 +220,7 @@ def to_paged(k_cache, v_cache, block_size: int, rng: np.random.Generator, spare_
                 pool[torch.as_tensor(perm[0, :share_prefix_blocks], device=x.device).long()] = \
                     blocks[0, :share_prefix_blocks]
             return pool
-        fill = np.uint16(0x7FC0) if x.dtype == np.uint16 else np.nan
+        fill = np.uint16(0x7FC0) if x.dtype == np.uint16 else (np.uint8(0x7F) if x.dtype == np.uint8 else np.nan)
         pool = np.full((nblk, Hkv, block_size, D), fill, dtype=x.dtype)
         blocks = x.reshape(B, Hkv, mb, block_size, D).transpose(0, 2, 1, 3, 4)
         for b in range(B):
