@@ -259,8 +259,8 @@ def test_greedy_matches_brute_force():
 
 
 def test_invalid_inputs_flag_request():
-    lg = np.zeros((4, 6), np.float32)
-    q = np.full((4, 6), 1 / 6, np.float32)
+    lg = np.zeros((5, 6), np.float32)  # N + B = 3 + 2 rows
+    q = np.full((5, 6), 1 / 6, np.float32)
     out = _run(np.array([0, 2, 3], np.int32), np.array([-1, 1, -1], np.int32), np.array([0, 1, 2], np.int32),
                lg, q, max_depth=2)
     assert out["status"][0] & 0x01 and out["out_tokens"][0].tolist() == [-1, -1, -1]
