@@ -12,11 +12,6 @@
 // shared by all G*T_b query rows that read it. Long contexts are cut into
 // splits whose partial (max, sum, unnormalised output) are merged by a
 // second kernel (flash-decoding style split-K).
-//
-// Cache layouts: contiguous [B, Hkv, Lcap, D]; paged pools read through a
-// block table (the same page names PagedAttention tree variants as the
-// kernels the mask is handed to), in PAGED forms of every kernel; and fp8
-// E4M3 bytes with per-tensor scales, in an FP8 form of the 64-row kernel.
 #include "sv_device.h"
 #include "sv_internal.h"
 
