@@ -126,6 +126,9 @@ def parse_args():
     ap.add_argument("--paged", type=int, default=0, metavar="BLOCK",
                     help="lay the KV caches out as a shuffled pool of BLOCK-slot blocks read through a block "
                          "table (BLOCK a multiple of 64; 0 = contiguous caches)")
+    ap.add_argument("--hash-inputs", action="store_true",
+                    help="record the SHA-256 (first 16 hex digits) of every input buffer of the first input set "
+                         "in the JSON line (copies them to the host: seconds for the large workloads)")
     ap.add_argument("--kv-fp8", action="store_true",
                     help="quantise the KV caches to OCP FP8 E4M3 bytes with per-tensor scales (bf16 workloads)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -331,6 +334,15 @@ def main():
             x["k_pool"], x["v_pool"], x["block_table"] = kp, vp, torch.from_numpy(bt).to(dev)
             del k, v
     torch.cuda.synchronize()
+    input_sha = None
+    if args.hash_inputs:
+        input_sha = {}
+        for key in ("q", "k_cache", "v_cache", "ctx_len_t", "cu_nodes_t", "parent_t", "draft_tokens", "logits",
+                    "draft_probs", "k_pool", "v_pool", "block_table"):
+            t = w.get(key)
+            if isinstance(t, torch.Tensor):
+                h = hashlib.sha256(t.contiguous().view(torch.uint8).cpu().numpy().tobytes()).hexdigest()[:16]
+                input_sha[key] = h
 
     stream = torch.cuda.Stream()  # default priority
     calls = []
@@ -455,6 +467,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "input_sets": n_sets,
+        **({"input_sha256_16": input_sha} if input_sha else {}),
         "kernels": {k: {kk: (round(vv, 2) if isinstance(vv, float) else vv) for kk, vv in d.items()}
                     for k, d in kernels.items()},
         "walk": {"mean_accept_len": round(float(acc.mean().item()), 4),
