@@ -126,6 +126,9 @@ def parse_args():
     ap.add_argument("--paged", type=int, default=0, metavar="BLOCK",
                     help="lay the KV caches out as a shuffled pool of BLOCK-slot blocks read through a block "
                          "table (BLOCK a multiple of 64; 0 = contiguous caches)")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture each input set's step in a HIP graph once and time graph replays (launch-bound "
+                         "small workloads); per-kernel events and the roofline object are then not recorded")
     ap.add_argument("--hash-inputs", action="store_true",
                     help="record the SHA-256 (first 16 hex digits) of every input buffer of the first input set "
                          "in the JSON line (copies them to the host: seconds for the large workloads)")
@@ -364,7 +367,7 @@ def main():
     torch.cuda.synchronize()
 
     K, W = args.steps, args.warmup
-    use_events = not args.no_events
+    use_events = not (args.no_events or args.graph)
     ev = None
     if use_events:
         hev = HipEvents(4 * K)
@@ -374,6 +377,21 @@ def main():
         calls[i % n_sets][2](stream)
     stream.synchronize()
     torch.cuda.synchronize()
+    graphs = None
+    if args.graph:
+        # the library launches kernels only (no allocation, copy, memset or
+        # synchronization), so a step captures as is
+        graphs = []
+        for _, _, step in calls:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                step(stream)
+            graphs.append(g)
+        with torch.cuda.stream(stream):
+            for i in range(max(W, n_sets)):
+                graphs[i % n_sets].replay()
+        stream.synchronize()
+        torch.cuda.synchronize()
 
     sev = HipEvents(2 * K)  # around each step, on the bench stream
     t0 = time.perf_counter()
@@ -383,7 +401,11 @@ def main():
             a.set_prof_events(ev[i][0], ev[i][1])
             s.set_prof_events(ev[i][2], ev[i][3])
         sev.record(2 * i, stream)
-        step(stream)
+        if graphs is not None:
+            with torch.cuda.stream(stream):
+                graphs[i % n_sets].replay()
+        else:
+            step(stream)
         sev.record(2 * i + 1, stream)
     stream.synchronize()
     torch.cuda.synchronize()
@@ -468,6 +490,7 @@ def main():
         "cpu_baseline": cpu,
         "input_sets": n_sets,
         **({"input_sha256_16": input_sha} if input_sha else {}),
+        **({"hip_graph": True} if args.graph else {}),
         "kernels": {k: {kk: (round(vv, 2) if isinstance(vv, float) else vv) for kk, vv in d.items()}
                     for k, d in kernels.items()},
         "walk": {"mean_accept_len": round(float(acc.mean().item()), 4),
