@@ -557,7 +557,7 @@ def test_sampler_truncation_rule_full_size(name, kind):
     print(f"  flagged near-ties: {flagged}/{w['B']}; mean accept_len {r['accept_len'].float().mean().item():.3f}")
 
 
-@pytest.mark.parametrize("name", ["c3_eagle_tree", "c5_super_tree"])
+@pytest.mark.parametrize("name", ["c3_eagle_tree", "c5_super_tree", "c4_L8192_B32_T0.5", "c4_L8192_B32_T2"])
 def test_sampler_eta_full_size(name):
     cfg = get_config(name)
     w = generate(cfg, "cuda", attn=False)
