@@ -21,8 +21,11 @@ Functions and the passages they follow:
   inverse_cdf              the draw from R_i / p.
   verify                   the whole walk ([SD] acceptance rule; [LOSSY] 2.1 h(x)).
   min_p_theta,             [LOSSY] section 2.3: the min-p allowed set and the
-  truncate_min_p           truncated target p_Theta; verify(min_p=...) walks
+  truncate_min_p, allowed  truncated target p_Theta, membership decided from
+                           the definition in fp64; verify(min_p=...) walks
                            against p_Theta ("truncation sampling + SD", G.2/G.3).
+  eta_threshold,           [LOSSY] section 2.3: the eta allowed set
+  truncate_eta             {p >= min(eps, delta exp(-H))}.
   verify(siblings=...)     "deterministic": the G.3 rule for deterministic
                            candidates (p~_i, candidates removed one by one).
   verify(rule=...)         [LOSSY] 3.1 lossy accept tests: lenience (A.3) and
@@ -43,7 +46,7 @@ _lib = None
 ACCEPT_TOL = 1e-5  # |u - P/Q| below this marks an accept test as a near-tie
 CDF_TOL = 1e-6     # a CDF boundary this close to u marks the final draw as a near-tie
 RULES = {"lossless": 0, "lenience": 1, "interpolation": 2, "truncation": 3}
-ETA_TOL = 1e-5  # near tie of a token to the eta threshold, log-probability units
+SET_TOL = 0.0  # allowed-set band: 0 = each set's own error bound (see verify)
 
 
 def build(verbose: bool = False) -> str:
@@ -83,15 +86,23 @@ def _load():
     lib.orc_residual.restype = f64
     lib.orc_inverse_cdf.argtypes = [i32, P, f64, P]
     lib.orc_inverse_cdf.restype = i32
-    lib.orc_verify.argtypes = [i32, i32, P, P, P, P, P, f64, i32, ctypes.c_float, f64, f64, f64, i32, i32, f64, u64,
+    lib.orc_verify.argtypes = [i32, i32, P, P, P, P, P, f64, i32, f64, f64, f64, f64, i32, i32, f64, u64,
                                u32, P, i32,
                                P, P, P, P,
                                P, P, P, P, P, P, f64, f64, i32]
     lib.orc_verify.restype = i32
     lib.orc_target_rows.argtypes = [i32, P, f64, i64, P, P]
     lib.orc_target_rows.restype = i32
-    lib.orc_truncate_min_p.argtypes = [i32, P, ctypes.c_float, P]
+    lib.orc_truncate_min_p.argtypes = [i32, P, f64, P]
     lib.orc_truncate_min_p.restype = None
+    lib.orc_min_p_threshold.argtypes = [f64, f64]
+    lib.orc_min_p_threshold.restype = f64
+    lib.orc_eta_threshold.argtypes = [i32, P, f64, f64, f64, P, P]
+    lib.orc_eta_threshold.restype = f64
+    lib.orc_allowed.argtypes = [ctypes.c_float, ctypes.c_float, f64]
+    lib.orc_allowed.restype = i32
+    lib.orc_row_finite.argtypes = [i32, P]
+    lib.orc_row_finite.restype = i32
     lib.orc_truncate_eta.argtypes = [i32, P, f64, f64, f64, P, P]
     lib.orc_truncate_eta.restype = f64
     lib.orc_row_entropy.argtypes = [i32, P, f64]
@@ -251,21 +262,41 @@ def inverse_cdf(P, u: float) -> tuple[int, float]:
 
 
 def min_p_theta(temperature: float, min_p: float) -> float:
-    """Threshold on l_x - l_max of the min-p allowed set: fp32(T ln p_base),
-    from the fp32 values of T and p_base, as a caller passing fp32 arguments
-    gets it; -inf (no truncation) unless 0 < min_p < 1 and T > 0."""
+    """Threshold on l_x - l_max of the min-p allowed set: T ln p_base in fp64,
+    from the fp32 values of T and p_base as a caller passing fp32 arguments
+    gets them; -inf (no truncation) unless 0 < min_p < 1 and T > 0."""
     T, pb = float(np.float32(temperature)), float(np.float32(min_p))
     if not (T > 0.0 and 0.0 < pb < 1.0):
         return float("-inf")
-    return float(np.float32(T * math.log(pb)))
+    return float(_load().orc_min_p_threshold(T, pb))
+
+
+def allowed(logit: float, lmax: float, theta: float) -> bool:
+    """Membership test of the allowed sets: fp64(l_x) - fp64(l_max) >= theta."""
+    return bool(_load().orc_allowed(float(np.float32(logit)), float(np.float32(lmax)), float(theta)))
 
 
 def truncate_min_p(logits_row, p_row, theta: float) -> np.ndarray:
     """p_row (a normalised target row) truncated to the min-p allowed set."""
     lg = np.ascontiguousarray(logits_row, dtype=np.float32)
     p = np.array(p_row, dtype=np.float64, copy=True)
-    _load().orc_truncate_min_p(lg.shape[0], _ptr(lg), ctypes.c_float(theta), _ptr(p))
+    _load().orc_truncate_min_p(lg.shape[0], _ptr(lg), float(theta), _ptr(p))
     return p
+
+
+def eta_threshold(logits_row, temperature: float, eps: float, delta: float) -> tuple[float, float, float]:
+    """(threshold on l_x - l_max, G = E_p[-z], Var_p(z)) of the eta allowed set."""
+    lg = np.ascontiguousarray(logits_row, dtype=np.float32)
+    g = np.zeros(1, np.float64)
+    v = np.zeros(1, np.float64)
+    th = _load().orc_eta_threshold(lg.shape[0], _ptr(lg), float(temperature), float(eps), float(delta), _ptr(g),
+                                   _ptr(v))
+    return float(th), float(g[0]), float(v[0])
+
+
+def row_finite(logits_row) -> bool:
+    lg = np.ascontiguousarray(logits_row, dtype=np.float32)
+    return bool(_load().orc_row_finite(lg.shape[0], _ptr(lg)))
 
 
 def truncate_eta(logits_row, p_row, temperature: float, eps: float, delta: float) -> tuple[np.ndarray, float, float]:
@@ -293,7 +324,7 @@ def eta_params(eta) -> tuple[float, float]:
 
 def verify(cu_nodes, parent, tokens, logits, q, *, temperature, seed, step=0, request_id=None,
            max_depth=None, accept_tol=ACCEPT_TOL, cdf_tol=CDF_TOL, nthreads=None, min_p=0.0,
-           siblings="sampled", rule="lossless", rule_param=1.0, eta=None, eta_tol=ETA_TOL) -> dict:
+           siblings="sampled", rule="lossless", rule_param=1.0, eta=None, set_tol=SET_TOL) -> dict:
     """The verification walk for a packed batch; returns a dict of numpy arrays.
 
     logits, q: float32 [N+B, V] (q may be None when temperature == 0 or the
@@ -307,8 +338,13 @@ def verify(cu_nodes, parent, tokens, logits, q, *, temperature, seed, step=0, re
     both in (0, 1]: the lossy accept tests of [LOSSY] 3.1 (h = min(1, p/(l q))
     and h = min(1, (lambda p + (1 - lambda) q)/q)), residuals unchanged.
     eta=(eps, delta): verify against the eta truncated target ([LOSSY] 2.3)
-    instead of min-p (flag_kind 2 marks a row with a token within eta_tol of
-    its threshold).
+    instead of min-p.
+    Allowed-set membership is the definition in fp64 (l_x - l_max against the
+    fp64 threshold). flag_kind 2 marks a position whose outcome some threshold
+    within the set's band would change; set_tol > 0 fixes the band's
+    half-width (log-probability units), 0 takes each set's own error bound:
+    fp64 rounding of T ln p_base for min-p, the first-order bound of a
+    threshold evaluated with fp32 weights for eta.
     rule="truncation": truncation-based verification ([LOSSY] 3.2) over the
     min-p or eta allowed set: accept iff the drafted token is allowed; after
     every child of a position is rejected, draw from q restricted to the set.
@@ -346,6 +382,7 @@ def verify(cu_nodes, parent, tokens, logits, q, *, temperature, seed, step=0, re
     }
     theta = min_p_theta(temperature, min_p)
     trunc = 1 if theta > float("-inf") else 0
+    p_base = float(np.float32(min_p)) if trunc else 0.0
     eps, delta = 0.0, 0.0
     if eta is not None:
         if trunc:
@@ -353,7 +390,9 @@ def verify(cu_nodes, parent, tokens, logits, q, *, temperature, seed, step=0, re
         eps, delta = eta_params(eta)
         trunc = 2 if temperature > 0 else 0
     rc = _load().orc_verify(B, V, _ptr(cu), _ptr(par), _ptr(tok), _ptr(lg), _ptr(qq), float(temperature),
-                            trunc, ctypes.c_float(theta), eps, delta, float(eta_tol), det, RULES[rule], float(np.float32(rule_param)), int(seed), int(step), _ptr(rid), int(max_depth), _ptr(out["accept_len"]),
+                            trunc, p_base, eps, delta, float(set_tol), det, RULES[rule],
+                            float(np.float32(rule_param)), int(seed), int(step), _ptr(rid), int(max_depth),
+                            _ptr(out["accept_len"]),
                             _ptr(out["accepted_nodes"]), _ptr(out["out_tokens"]), _ptr(out["uniforms"]),
                             _ptr(out["flag_depth"]), _ptr(out["flag_kind"]), _ptr(out["n_rejections"]),
                             _ptr(out["status"]), _ptr(out["min_accept_margin"]), _ptr(out["cdf_margin"]),

@@ -301,86 +301,120 @@ int orc_target_probs(int V, const float* logits, double T, double* p) {
   return 0;
 }
 
-/* Min-p truncation of a target row ([LOSSY] section 2.3: the allowed set
- * A = {x : p(x) >= p_base * max_v p(v)} and the truncated target
- * p_Theta(x) = p(x) / Z on A, 0 elsewhere, which "truncation sampling + SD"
- * verifies against, appendix G.2/G.3). Because p(x) / max p equals
- * exp((l_x - l_max) / T), x is in A iff l_x - l_max >= T ln p_base. Reading:
- * that comparison is made on the fp32 difference of the raw logits against
- * theta = fp32(T ln p_base), so that every implementation decides
- * membership identically. p (a normalised row) is masked and renormalised
- * in place.                                                                */
-void orc_truncate_min_p(int V, const float* logits, float theta, double* p) {
-  float lmax = -INFINITY;
+/* Allowed sets of truncation sampling ([LOSSY] section 2.3). Both are
+ * thresholds on the target probability relative to its maximum: with
+ * z_x = (l_x - l_max) / T, p(x) / max p = exp(z_x), so p(x) >= tau is
+ * l_x - l_max >= T (ln S + ln tau) (S = sum exp(z)) and p(x) >= p_base max p
+ * is l_x - l_max >= T ln p_base. Membership is decided from that definition in
+ * fp64: the difference of the two fp32 logits is formed in fp64 (exact for
+ * any two logits within a factor 2^29 of each other) and compared with the
+ * fp64 threshold.                                                          */
+int orc_allowed(float lx, float lmax, double th) { return (double)lx - (double)lmax >= th; }
+
+/* Largest logit of a row (fp32; -inf if none is above -inf; NaN ignored). */
+static float orc_row_max(int V, const float* logits) {
+  float m = -INFINITY;
   for (int x = 0; x < V; ++x)
-    if (logits[x] > lmax) lmax = logits[x];
+    if (logits[x] > m) m = logits[x];
+  return m;
+}
+
+/* Masks the normalised row p to {x : l_x - l_max >= th} and renormalises in
+ * place; returns the mass kept.                                            */
+double orc_truncate(int V, const float* logits, double th, double* p) {
+  const float lmax = orc_row_max(V, logits);
   double Z = 0.0;
   for (int x = 0; x < V; ++x) {
-    float d = logits[x] - lmax;
-    if (!(d >= theta)) p[x] = 0.0;
+    if (!orc_allowed(logits[x], lmax, th)) p[x] = 0.0;
     Z += p[x];
   }
   for (int x = 0; x < V; ++x) p[x] /= Z;
+  return Z;
 }
 
-/* eta-sampling truncation ([LOSSY] section 2.3: the allowed set
- * A = {x : p(x) >= min(eps, delta exp(-H(p)))}, H the Shannon entropy of the
- * target row). With z_x = (l_x - l_max)/T, S = sum exp(z), p = exp(z)/S and
- * H = ln S - sum p z, the test p(x) >= tau reads
- * l_x - l_max >= T (ln S + ln tau). Reading: as for min-p, membership is
- * decided on the fp32 logit difference against the fp32 rounding of that
- * threshold; a row with some token within tol (in log-probability units) of
- * the exact threshold is a near tie, reported through *margin so that a
- * caller can flag it. p is masked and renormalised in place; returns the
- * fp64 threshold.                                                          */
+/* Min-p ([LOSSY] section 2.3: A = {x : p(x) >= p_base * max_v p(v)}, and the
+ * truncated target p_Theta(x) = p(x) / Z on A, 0 elsewhere, which "truncation
+ * sampling + SD" verifies against, appendix G.2/G.3): the threshold
+ * T ln p_base on l_x - l_max. p (a normalised row) is masked and
+ * renormalised in place.                                                    */
+double orc_min_p_threshold(double T, double p_base) { return T * log(p_base); }
+
+void orc_truncate_min_p(int V, const float* logits, double theta, double* p) { orc_truncate(V, logits, theta, p); }
+
+/* eta-sampling ([LOSSY] section 2.3: A = {x : p(x) >= min(eps, delta exp(-H(p)))},
+ * H the Shannon entropy of the target row in nats). With S = sum exp(z),
+ * G = E_p[-z] (>= 0) and H = ln S + G, the threshold on l_x - l_max is
+ * T (ln S + min(ln eps, ln delta - H)). Also returns G and the variance of z
+ * under p (both in nats), from which a caller bounds how far a threshold
+ * computed with fp32 weights can sit from this one.                       */
+double orc_eta_threshold(int V, const float* logits, double T, double eps, double delta, double* gap, double* var) {
+  const float lmax = orc_row_max(V, logits);
+  double S = 0.0, E1 = 0.0, E2 = 0.0;
+  for (int x = 0; x < V; ++x) {
+    double z = ((double)logits[x] - (double)lmax) / T;
+    double e = exp(z);
+    S += e;
+    if (e > 0.0) {
+      E1 += e * z;
+      E2 += e * z * z;
+    }
+  }
+  double G = -E1 / S;
+  double H = log(S) + G;
+  if (gap) *gap = G;
+  if (var) *var = fmax(0.0, E2 / S - G * G);
+  return T * (log(S) + fmin(log(eps), log(delta) - H));
+}
+
+/* The eta truncation of a normalised row p in place; returns the threshold.
+ * *margin (optional): the smallest distance of a token to it, in
+ * log-probability units (|l_x - l_max - th| / T).                         */
 double orc_truncate_eta(int V, const float* logits, double T, double eps, double delta, double* p, double* margin) {
-  float lmax = -INFINITY;
-  for (int x = 0; x < V; ++x)
-    if (logits[x] > lmax) lmax = logits[x];
+  double th = orc_eta_threshold(V, logits, T, eps, delta, NULL, NULL);
+  const float lmax = orc_row_max(V, logits);
+  double mg = INFINITY;
+  for (int x = 0; x < V; ++x) {
+    double dist = fabs(((double)logits[x] - (double)lmax) - th) / T;
+    if (dist < mg) mg = dist;
+  }
+  orc_truncate(V, logits, th, p);
+  if (margin) *margin = mg;
+  return th;
+}
+
+/* Entropy of the target row at temperature T, in nats (the H of the eta
+ * allowed set above): H = -sum p ln p = ln S - sum p z.                    */
+double orc_row_entropy(int V, const float* logits, double T) {
+  const float lmax = orc_row_max(V, logits);
   double S = 0.0, E = 0.0;
   for (int x = 0; x < V; ++x) {
     double z = ((double)logits[x] - (double)lmax) / T;
     double e = exp(z);
     S += e;
-    E += e * z;
-  }
-  double H = log(S) - E / S;
-  double ln_tau = fmin(log(eps), log(delta) - H);
-  double th64 = T * (log(S) + ln_tau);
-  float th = (float)th64;
-  double Z = 0.0, mg = INFINITY;
-  for (int x = 0; x < V; ++x) {
-    float d = logits[x] - lmax;
-    double dist = fabs((double)d - th64) / T;
-    if (dist < mg) mg = dist;
-    if (!(d >= th)) p[x] = 0.0;
-    Z += p[x];
-  }
-  for (int x = 0; x < V; ++x) p[x] /= Z;
-  if (margin) *margin = mg;
-  return th64;
-}
-
-/* Entropy of the target row at temperature T, in nats (the H of the eta
- * allowed set above), computed the same way.                              */
-double orc_row_entropy(int V, const float* logits, double T) {
-  float lmax = -INFINITY;
-  for (int x = 0; x < V; ++x)
-    if (logits[x] > lmax) lmax = logits[x];
-  double S = 0.0, E = 0.0;
-  for (int x = 0; x < V; ++x) {
-    double z = ((double)logits[x] - (double)lmax) / T;
-    S += exp(z);
-    E += exp(z) * z;
+    if (e > 0.0) E += e * z;
   }
   return log(S) - E / S;
 }
 
-/* Greedy target token: argmax of the raw logits, lowest index on ties.    */
+/* Does the row define a target distribution? Not if a logit is NaN or +inf,
+ * or if every logit is -inf (then softmax has no value).                   */
+int orc_row_finite(int V, const float* logits) {
+  int any = 0;
+  for (int x = 0; x < V; ++x) {
+    if (isnan(logits[x]) || logits[x] == INFINITY) return 0;
+    if (logits[x] > -INFINITY) any = 1;
+  }
+  return any;
+}
+
+/* Greedy target token: argmax of the raw logits, lowest index on ties; NaN
+ * entries are passed over (-1 if the row has no non-NaN entry).           */
 int orc_argmax(int V, const float* logits) {
-  int best = 0;
-  for (int x = 1; x < V; ++x)
-    if (logits[x] > logits[best]) best = x;
+  int best = -1;
+  for (int x = 0; x < V; ++x) {
+    if (isnan(logits[x])) continue;
+    if (best < 0 || logits[x] > logits[best]) best = x;
+  }
   return best;
 }
 
@@ -459,9 +493,10 @@ typedef struct {
   const float *logits, *q;
   double T;
   int trunc;     /* truncation of every target row: 0 none, 1 min-p, 2 eta */
-  float theta;   /* min-p: its threshold on l_x - l_max   */
-  double eta_eps, eta_delta; /* eta: its eps and delta   */
-  double eta_tol; /* eta: near-tie distance of a token to the threshold */
+  double p_base; /* min-p: its p_base                                        */
+  double eta_eps, eta_delta; /* eta: its eps and delta                      */
+  double set_tol; /* > 0: half-width of the allowed-set band in log-probability
+                     units; 0: the band each set's own error bound gives   */
   int det;       /* siblings are deterministic candidates (q unused) */
   int rule;      /* accept rule: 0 lossless, 1 lenience, 2 interpolation,
                     3 truncation-based (accept iff the token is allowed)   */
@@ -476,6 +511,181 @@ typedef struct {
   double *min_accept_margin, *cdf_margin;
   double accept_tol, cdf_tol;
 } orc_walk_ctx;
+
+/* What the decisions at one position observed. */
+typedef struct {
+  double min_accept_margin; /* smallest |u - h| over its accept tests      */
+  double cdf_margin;        /* margin of its draw (INFINITY: no draw)      */
+  int near_kind;            /* first near tie: 0 accept test, 1 draw,
+                               3 deterministic remainder near 0; -1 none  */
+  int rejections;
+  int status;
+} orc_rec;
+
+/* A deterministic candidate's remainder at or below this fraction of the
+ * row's mass is a near tie: a computation that subtracts fp32 weights from
+ * their sum cannot tell it from zero.                                      */
+#define ORC_REMAINDER_TOL 1e-11
+
+/* The decisions at one position of request b: the children of pos (local
+ * index, -1 = root) are tried in increasing index against the row's target
+ * -- p, or with truncation p_Theta over {x : l_x - l_max >= th} -- and when
+ * none is accepted one token is drawn from the current distribution.
+ * Returns the accepted child, or -1 with *bonus = the drawn token (-1 when
+ * the row defines no distribution). Scratch: P, Q, tmp of V doubles.      */
+static int orc_position(const orc_walk_ctx* c, int b, int pos, double th, orc_rec* rec, int* bonus, double* P,
+                        double* Q, double* tmp) {
+  const int V = c->V;
+  const int64_t n0 = c->cu_nodes[b];
+  const int T = c->cu_nodes[b + 1] - c->cu_nodes[b];
+  const int32_t* par = c->parent + n0;
+  const int32_t* tok = c->tokens + n0;
+  const uint32_t rid = c->request_id ? c->request_id[b] : (uint32_t)b;
+  const int64_t row = n0 + b + pos + 1; /* root row n0 + b, node j's row n0 + b + 1 + j */
+  const float* lrow = c->logits + row * (int64_t)V;
+  rec->min_accept_margin = INFINITY;
+  rec->cdf_margin = INFINITY;
+  rec->near_kind = -1;
+  rec->rejections = 0;
+  rec->status = 0;
+  *bonus = -1;
+  /* target distribution at this position, and the draft distribution it is
+   * checked against ([SD]: node j is checked against p_i and q_i of the
+   * position it was drafted at, i.e. its parent's row)                     */
+  if (orc_target_probs(V, lrow, c->T, P)) {
+    rec->status |= 0x08;
+    return -1;
+  }
+  const float lmax = orc_row_max(V, lrow);
+  if (c->trunc) orc_truncate(V, lrow, th, P);
+  if (!c->det)
+    for (int x = 0; x < V; ++x) Q[x] = (double)c->q[row * (int64_t)V + x];
+  int n_kids = 0;
+  double remain = 1.0; /* deterministic candidates: fraction of the row's mass left */
+  for (int ch = pos + 1; ch < T; ++ch) {
+    if (par[ch] != pos) continue; /* children in increasing node index */
+    ++n_kids;
+    double u = orc_uniform(c->seed, rid, (uint32_t)ch, 0, c->step);
+    int x = tok[ch];
+    if (c->det) {
+      /* [LOSSY] G.3, deterministic candidates: x^(i) is accepted with
+       * probability p~_i(x^(i)), i.e. iff u <= P(x) with P the target after
+       * the earlier candidates were taken out (a token tried before has
+       * P = 0 and is rejected).                                             */
+      double margin = fabs(u - P[x]);
+      if (margin < rec->min_accept_margin) rec->min_accept_margin = margin;
+      if (margin < c->accept_tol && rec->near_kind < 0) rec->near_kind = 0;
+      if (P[x] > 0.0 && u <= P[x]) return ch;
+      rec->rejections += 1;
+      double R = orc_remove_candidate(V, P, x, tmp);
+      if (!(R > 0.0)) rec->status |= 0x10;
+      else remain *= R;
+      if (remain <= ORC_REMAINDER_TOL && rec->near_kind < 0) rec->near_kind = 3;
+      memcpy(P, tmp, sizeof(double) * (size_t)V);
+      continue;
+    }
+    if (c->rule == 3) {
+      /* [LOSSY] 3.2, truncation-based verification (SpecCascade with the
+       * min-p set, typical acceptance with the eta set): h(x) = 1 if x is in
+       * the allowed set, else 0. No uniform is involved.                    */
+      if (orc_allowed(lrow[x], lmax, th)) return ch;
+      rec->rejections += 1;
+      continue;
+    }
+    /* [SD] acceptance rule r <= min(1, p/q), written as u*q <= p with p > 0
+     * so that q(x) = 0 follows the formula (ratio +inf, accepted). The lossy
+     * rules of [LOSSY] 3.1 change only this test: lenience h = min(1, p/(l q))
+     * compares u*(l q) with p; interpolation (CoS) h = min(1, nu/q) with
+     * nu = lambda p + (1 - lambda) q compares u*q with nu. Both keep the
+     * residual max(0, P - q) of a rejection (A.3; A.1's r(x) is the same
+     * distribution).                                                        */
+    double num = P[x], den = Q[x];
+    if (c->rule == 1) den = c->rule_param * Q[x];
+    if (c->rule == 2) num = c->rule_param * P[x] + (1.0 - c->rule_param) * Q[x];
+    double ratio = den > 0.0 ? num / den : (num > 0.0 ? INFINITY : 0.0);
+    double margin = fabs(u - ratio);
+    if (margin < rec->min_accept_margin) rec->min_accept_margin = margin;
+    if (margin < c->accept_tol && rec->near_kind < 0) rec->near_kind = 0;
+    if (num > 0.0 && u * den <= num) return ch;
+    /* rejected: the next sibling (a fresh draw from the same q) is tested
+     * against the renormalised residual of the current distribution       */
+    rec->rejections += 1;
+    double R = orc_residual(V, P, Q, tmp);
+    if (!(R > 0.0)) rec->status |= 0x10;
+    memcpy(P, tmp, sizeof(double) * (size_t)V);
+  }
+  if (c->rule == 3 && n_kids > 0) {
+    /* every child rejected under truncation-based verification: the token
+     * comes from the draft restricted to the allowed set,
+     * r(x) = q(x) 1{x in A} / Z_A(q). Reading: [LOSSY] 3.2 gives the law the
+     * rule generates, q(x) / Z_A(q) on A and 0 elsewhere, but no residual;
+     * with P(generate x) = q(x) h(x) + (1 - Z_A(q)) r(x) this r is the only
+     * one that yields it, at any number of i.i.d. siblings. A zero Z_A(q)
+     * keeps the truncated target (flagged).                                 */
+    double Z = 0.0;
+    for (int x = 0; x < V; ++x) {
+      tmp[x] = orc_allowed(lrow[x], lmax, th) ? Q[x] : 0.0;
+      Z += tmp[x];
+    }
+    if (Z > 0.0) {
+      for (int x = 0; x < V; ++x) P[x] = tmp[x] / Z;
+    } else {
+      rec->status |= 0x10;
+    }
+  }
+  /* no child accepted (or none to try): one token from the current
+   * distribution -- the residual after rejections (with deterministic
+   * candidates: the target without the tried ones), p at a leaf          */
+  double u = orc_uniform(c->seed, rid, 0, 1, c->step);
+  double margin = 0.0;
+  *bonus = orc_inverse_cdf(V, P, u, &margin);
+  rec->cdf_margin = margin;
+  if (margin < c->cdf_tol && rec->near_kind < 0) rec->near_kind = 1;
+  return -1;
+}
+
+static int orc_cmp_desc(const void* a, const void* b) {
+  double x = *(const double*)a, y = *(const double*)b;
+  return x > y ? -1 : (x < y ? 1 : 0);
+}
+
+/* Does a threshold inside the band change the decisions at this position?
+ * The sets {x : l_x - l_max >= t} for t in [th - band, th + band] differ
+ * only in the tokens whose l_x - l_max lies in that interval; ordered by
+ * that difference they enter one at a time, so the distinct sets are the
+ * set without any of them and the sets with the top k of them. Each is
+ * evaluated; 1 if one gives another outcome (accepted child, or bonus
+ * token) than (acc, bonus).                                                */
+static int orc_band_changes(const orc_walk_ctx* c, int b, int pos, double th, double band, int acc, int bonus,
+                            double* P, double* Q, double* tmp) {
+  const int V = c->V;
+  const int64_t row = c->cu_nodes[b] + b + pos + 1;
+  const float* lrow = c->logits + row * (int64_t)V;
+  const float lmax = orc_row_max(V, lrow);
+  int m = 0;
+  for (int x = 0; x < V; ++x)
+    if (fabs(((double)lrow[x] - (double)lmax) - th) <= band) ++m;
+  if (m == 0) return 0;
+  double* dv = (double*)malloc(sizeof(double) * (size_t)m);
+  if (!dv) return 1;
+  m = 0;
+  for (int x = 0; x < V; ++x) {
+    double d = (double)lrow[x] - (double)lmax;
+    if (fabs(d - th) <= band) dv[m++] = d;
+  }
+  qsort(dv, (size_t)m, sizeof(double), orc_cmp_desc);
+  int changed = 0;
+  for (int k = -1; k < m && !changed; ++k) {
+    if (k >= 1 && dv[k] == dv[k - 1]) continue; /* the same set as before */
+    double t = k < 0 ? nextafter(dv[0], INFINITY) : dv[k];
+    orc_rec r;
+    int y = -1;
+    int a = orc_position(c, b, pos, t, &r, &y, P, Q, tmp);
+    changed = a != acc || (a < 0 && y != bonus);
+  }
+  free(dv);
+  return changed;
+}
 
 static void orc_walk_one(void* vctx, int64_t bi) {
   orc_walk_ctx* c = (orc_walk_ctx*)vctx;
@@ -512,10 +722,16 @@ static void orc_walk_one(void* vctx, int64_t bi) {
 
   if (c->T == 0.0) {
     /* Greedy verification: accept the first child equal to the target's
-     * argmax; the bonus token is the argmax at the final position.        */
+     * argmax; the bonus token is the argmax at the final position. A row
+     * with no distribution (NaN, +inf, all -inf) stops the walk without a
+     * token, as in sampled verification.                                   */
     int pos = -1, d = 0;
     for (;;) {
       const float* lrow = c->logits + (row0 + pos + 1) * (int64_t)V;
+      if (!orc_row_finite(V, lrow)) {
+        c->status[b] |= 0x08;
+        break;
+      }
       int a = orc_argmax(V, lrow);
       int next = -1;
       for (int ch = pos + 1; ch < T; ++ch)
@@ -540,116 +756,49 @@ static void orc_walk_one(void* vctx, int64_t bi) {
 
   int pos = -1, d = 0;
   for (;;) {
-    int64_t row = row0 + pos + 1;
-    /* target distribution at this position, and the draft distribution it
-     * is checked against ([SD]: node j is checked against p_i and q_i of the
-     * position it was drafted at, i.e. its parent's row)                  */
-    if (orc_target_probs(V, c->logits + row * (int64_t)V, c->T, P)) { c->status[b] |= 0x08; break; }
-    const float* lrow = c->logits + row * (int64_t)V;
-    float th_row = c->theta; /* this position's threshold on l_x - l_max */
-    if (c->trunc == 1) orc_truncate_min_p(V, lrow, c->theta, P);
-    if (c->trunc == 2) {
-      double mg = INFINITY;
-      th_row = (float)orc_truncate_eta(V, lrow, c->T, c->eta_eps, c->eta_delta, P, &mg);
-      if (mg < c->eta_tol && c->flag_depth[b] < 0) { c->flag_depth[b] = d; c->flag_kind[b] = 2; }
+    const float* lrow = c->logits + (row0 + pos + 1) * (int64_t)V;
+    /* this position's allowed-set threshold, and the band around it within
+     * which another correct evaluation may place its own threshold        */
+    double th = -INFINITY, band = 0.0;
+    if (c->trunc == 1) {
+      th = orc_min_p_threshold(c->T, c->p_base);
+      /* T ln p_base in fp64 on either side: a few fp64 ulps apart at most */
+      band = c->set_tol > 0.0 ? c->set_tol * c->T : 1e-12 * fmax(1.0, fabs(th));
+    } else if (c->trunc == 2 && orc_row_finite(V, lrow)) {
+      double G = 0.0, Var = 0.0;
+      th = orc_eta_threshold(V, lrow, c->T, c->eta_eps, c->eta_delta, &G, &Var);
+      /* An evaluation that weighs each token with an fp32 exponential of an
+       * fp32 argument (relative error of the argument <= 3 * 2^-24, of the
+       * exponential <= 2^-22) and sums in fp64 gets ln S within
+       * 2^-24 (3 G + 4) and G within 2^-24 (12 G + 3 Var + 6 G^2) (first
+       * order); the threshold is T (ln S + ln eps) or T (ln delta - G).     */
+      band = c->set_tol > 0.0 ? c->set_tol * c->T
+                              : c->T * ldexp(8.0 + 12.0 * G + 3.0 * Var + 6.0 * G * G, -24);
     }
-    float lmax_row = -INFINITY;
-    for (int x = 0; x < V; ++x)
-      if (lrow[x] > lmax_row) lmax_row = lrow[x];
-    int n_kids = 0;
-    for (int ch = pos + 1; ch < T; ++ch) n_kids += par[ch] == pos;
-    if (!c->det)
-      for (int x = 0; x < V; ++x) Q[x] = (double)c->q[row * (int64_t)V + x];
-    int accepted = -1;
-    for (int ch = pos + 1; ch < T; ++ch) {
-      if (par[ch] != pos) continue; /* children in increasing node index */
-      double u = orc_uniform(c->seed, rid, (uint32_t)ch, 0, c->step);
-      int x = tok[ch];
-      if (c->det) {
-        /* [LOSSY] G.3, deterministic candidates: x^(i) is accepted with
-         * probability p~_i(x^(i)), i.e. iff u <= P(x) with P the target
-         * after the earlier candidates were taken out (a token tried
-         * before has P = 0 and is rejected).                              */
-        int ok = P[x] > 0.0 && u <= P[x];
-        double margin = fabs(u - P[x]);
-        if (margin < c->min_accept_margin[b]) c->min_accept_margin[b] = margin;
-        if (margin < c->accept_tol && c->flag_depth[b] < 0) { c->flag_depth[b] = d; c->flag_kind[b] = 0; }
-        if (ok) { accepted = ch; break; }
-        c->n_rejections[b] += 1;
-        double R = orc_remove_candidate(V, P, x, tmp);
-        if (!(R > 0.0)) c->status[b] |= 0x10;
-        memcpy(P, tmp, sizeof(double) * (size_t)V);
-        continue;
+    orc_rec rec;
+    int bonus = -1;
+    int acc = orc_position(c, b, pos, th, &rec, &bonus, P, Q, tmp);
+    c->n_rejections[b] += rec.rejections;
+    c->status[b] |= rec.status;
+    if (rec.min_accept_margin < c->min_accept_margin[b]) c->min_accept_margin[b] = rec.min_accept_margin;
+    if (rec.cdf_margin < INFINITY) c->cdf_margin[b] = rec.cdf_margin;
+    if (c->flag_depth[b] < 0) {
+      if (c->trunc && !(rec.status & 0x08) && orc_band_changes(c, b, pos, th, band, acc, bonus, P, Q, tmp)) {
+        c->flag_depth[b] = d;
+        c->flag_kind[b] = 2;
+      } else if (rec.near_kind >= 0) {
+        c->flag_depth[b] = d;
+        c->flag_kind[b] = rec.near_kind;
       }
-      if (c->rule == 3) {
-        /* [LOSSY] 3.2, truncation-based verification (SpecCascade with the
-         * min-p set, typical acceptance with the eta set): h(x) = 1 if x is
-         * in the allowed set, else 0 -- the fp32 membership test of the
-         * truncation above. No uniform is involved.                        */
-        float dx = lrow[x] - lmax_row;
-        if (dx >= th_row) { accepted = ch; break; }
-        c->n_rejections[b] += 1;
-        continue;
-      }
-      /* [SD] acceptance rule r <= min(1, p/q), written as u*q <= p with p > 0
-       * so that q(x) = 0 follows the formula (ratio +inf, accepted). The
-       * lossy rules of [LOSSY] 3.1 change only this test: lenience
-       * h = min(1, p/(l q)) compares u*(l q) with p; interpolation (CoS)
-       * h = min(1, nu/q) with nu = lambda p + (1 - lambda) q compares u*q
-       * with nu. Both keep the residual max(0, P - q) of a rejection (A.3;
-       * A.1's r(x) is the same distribution).                              */
-      double num = P[x], den = Q[x];
-      if (c->rule == 1) den = c->rule_param * Q[x];
-      if (c->rule == 2) num = c->rule_param * P[x] + (1.0 - c->rule_param) * Q[x];
-      int ok = num > 0.0 && u * den <= num;
-      double ratio = den > 0.0 ? num / den : (num > 0.0 ? INFINITY : 0.0);
-      double margin = fabs(u - ratio);
-      if (margin < c->min_accept_margin[b]) c->min_accept_margin[b] = margin;
-      if (margin < c->accept_tol && c->flag_depth[b] < 0) { c->flag_depth[b] = d; c->flag_kind[b] = 0; }
-      if (ok) { accepted = ch; break; }
-      /* rejected: the next sibling (a fresh draw from the same q) is tested
-       * against the renormalised residual of the current distribution      */
-      c->n_rejections[b] += 1;
-      double R = orc_residual(V, P, Q, tmp);
-      if (!(R > 0.0)) c->status[b] |= 0x10;
-      memcpy(P, tmp, sizeof(double) * (size_t)V);
     }
-    if (accepted >= 0) {
-      acc_nodes[d] = accepted;
-      toks_out[d] = tok[accepted];
+    if (acc >= 0) {
+      acc_nodes[d] = acc;
+      toks_out[d] = tok[acc];
       ++d;
-      pos = accepted;
+      pos = acc;
       continue;
     }
-    if (c->rule == 3 && n_kids > 0) {
-      /* every child rejected under truncation-based verification: the token
-       * comes from the draft restricted to the allowed set,
-       * r(x) = q(x) 1{x in A} / Z_A(q). Reading: [LOSSY] 3.2 gives the law
-       * the rule generates, q(x) / Z_A(q) on A and 0 elsewhere, but no
-       * residual; with P(generate x) = q(x) h(x) + (1 - Z_A(q)) r(x) this r is
-       * the only one that yields it, at any number of i.i.d. siblings. A
-       * zero Z_A(q) keeps the truncated target (flagged).                  */
-      double Z = 0.0;
-      for (int x = 0; x < V; ++x) {
-        float dx = lrow[x] - lmax_row;
-        tmp[x] = dx >= th_row ? (double)c->q[row * (int64_t)V + x] : 0.0;
-        Z += tmp[x];
-      }
-      if (Z > 0.0) {
-        for (int x = 0; x < V; ++x) P[x] = tmp[x] / Z;
-      } else {
-        c->status[b] |= 0x10;
-      }
-    }
-    /* no child accepted (or none to try): one token from the current
-     * distribution -- the residual after rejections (with deterministic
-     * candidates: the target without the tried ones), p at a leaf        */
-    double u = orc_uniform(c->seed, rid, 0, 1, c->step);
-    double margin = 0.0;
-    int y = orc_inverse_cdf(V, P, u, &margin);
-    c->cdf_margin[b] = margin;
-    if (margin < c->cdf_tol && c->flag_depth[b] < 0) { c->flag_depth[b] = d; c->flag_kind[b] = 1; }
-    toks_out[d] = y;
+    toks_out[d] = bonus;
     break;
   }
   c->accept_len[b] = d;
@@ -660,28 +809,32 @@ static void orc_walk_one(void* vctx, int64_t bi) {
 
 /* Verification of a packed batch (see the calling convention of the GPU
  * library: rows cu_nodes[b] + b + r, r = 0 root, r = 1 + j after node j).
- * T == 0 selects greedy verification; trunc = 1 verifies against the
- * min-p truncated target (threshold theta, see orc_truncate_min_p), trunc = 2
- * against the eta truncated target (eta_eps, eta_delta; a visited row with a
- * token within eta_tol of its threshold is flagged, kind 2, see
- * orc_truncate_eta); rule 3 is truncation-based verification ([LOSSY] 3.2)
- * over the allowed set of trunc 1 or 2; det != 0
- * treats the siblings as deterministic candidates ([LOSSY] G.3; q unused and
- * may be NULL; a rejection takes the candidate out of the target); rule 1/2
- * selects the lossy lenience / interpolation accept test ([LOSSY] 3.1, A.1,
- * A.3) with rule_param = l / lambda in (0, 1] (not with det). Per
+ * T == 0 selects greedy verification; trunc = 1 verifies against the min-p
+ * truncated target (p_base), trunc = 2 against the eta truncated target
+ * (eta_eps, eta_delta); rule 3 is truncation-based verification
+ * ([LOSSY] 3.2) over the allowed set of trunc 1 or 2; det != 0 treats the
+ * siblings as deterministic candidates ([LOSSY] G.3; q unused and may be
+ * NULL; a rejection takes the candidate out of the target); rule 1/2
+ * selects the lossy lenience / interpolation accept test ([LOSSY] 3.1,
+ * A.1, A.3) with rule_param = l / lambda in (0, 1] (not with det). Per
  * request it also reports
- *   flag_depth: accepted nodes before the first decision closer than the
- *               tolerance to its threshold (-1: none), flag_kind 0 = accept
- *               test, 1 = final inverse-CDF draw, 2 = eta set boundary;
+ *   flag_depth: accepted nodes before the first decision that is not fixed
+ *               by the inputs to within the stated tolerances (-1: none);
+ *   flag_kind:  0 = accept test with |u - h| < accept_tol, 1 = final draw
+ *               with a CDF boundary within cdf_tol of u, 2 = allowed-set
+ *               boundary: a threshold within the set's band (set_tol, or
+ *               the set's own error bound when set_tol == 0) changes the
+ *               position's outcome, 3 = deterministic remainder at most
+ *               1e-11 of the row's mass;
  *   n_rejections: rejections (= residual renormalisations or removals);
  *   status: SV_STATUS-like bits (0x01 tree, 0x02 packing, 0x04 token,
- *           0x08 non-finite row, 0x10 zero residual, 0x80 out of memory);
- *   min_accept_margin, cdf_margin: the smallest |u - P/Q| seen and the
+ *           0x08 non-finite row reached, 0x10 zero residual, 0x80 out of
+ *           memory);
+ *   min_accept_margin, cdf_margin: the smallest |u - h| seen and the
  *           margin of the final draw.                                     */
 int orc_verify(int B, int V, const int32_t* cu_nodes, const int32_t* parent, const int32_t* tokens,
-               const float* logits, const float* q, double T, int trunc, float theta, double eta_eps,
-               double eta_delta, double eta_tol, int det, int rule, double rule_param, uint64_t seed, uint32_t step,
+               const float* logits, const float* q, double T, int trunc, double p_base, double eta_eps,
+               double eta_delta, double set_tol, int det, int rule, double rule_param, uint64_t seed, uint32_t step,
                const uint32_t* request_id, int max_depth, int32_t* accept_len, int32_t* accepted_nodes,
                int32_t* out_tokens, double* uniforms_out, int32_t* flag_depth, int32_t* flag_kind,
                int32_t* n_rejections, int32_t* status, double* min_accept_margin, double* cdf_margin,
@@ -691,9 +844,11 @@ int orc_verify(int B, int V, const int32_t* cu_nodes, const int32_t* parent, con
   if (rule < 0 || rule > 3 || (rule && det)) return 1;
   if ((rule == 1 || rule == 2) && !(rule_param > 0.0 && rule_param <= 1.0)) return 1;
   if (rule == 3 && (!trunc || T == 0.0)) return 1; /* needs an allowed set */
-  if (trunc < 0 || trunc > 2) return 1;
+  if (trunc < 0 || trunc > 2 || set_tol < 0.0) return 1;
+  if (trunc == 1 && !(p_base > 0.0 && p_base < 1.0)) return 1;
   if (trunc == 2 && !(eta_eps > 0.0 && eta_eps < 1.0 && eta_delta > 0.0 && eta_delta <= 1.0)) return 1;
-  orc_walk_ctx c = {B, V, cu_nodes, parent, tokens, logits, q, T, trunc, theta, eta_eps, eta_delta, eta_tol,
+  if (T == 0.0) trunc = 0; /* greedy: the argmax is always allowed */
+  orc_walk_ctx c = {B, V, cu_nodes, parent, tokens, logits, q, T, trunc, p_base, eta_eps, eta_delta, set_tol,
                     det, rule, rule_param, seed, step,
                     request_id, max_depth,
                     accept_len, accepted_nodes, out_tokens, uniforms_out, flag_depth, flag_kind,
