@@ -131,7 +131,8 @@ def parse_args():
                          "small workloads); per-kernel events and the roofline object are then not recorded")
     ap.add_argument("--hash-inputs", action="store_true",
                     help="record the SHA-256 (first 16 hex digits) of every input buffer of the first input set "
-                         "in the JSON line (copies them to the host: seconds for the large workloads)")
+                         "in the JSON line (always done for workloads under 512 MB; copies them to the host: "
+                         "seconds for the large workloads)")
     ap.add_argument("--kv-fp8", action="store_true",
                     help="quantise the KV caches to OCP FP8 E4M3 bytes with per-tensor scales (bf16 workloads)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -239,8 +240,8 @@ def cpu_baseline(w, budget_s: float, min_p: float = 0.0, siblings: str = "sample
                  rule_param: float = 1.0, eta=None):
     """The fp64 oracle (attention of every (node, head) of a request, then the
     verification walk) over whole requests in order until the budget is spent.
-    Returns verified draft tokens/s of that sample, the thread count and a
-    description."""
+    Returns verified draft tokens/s of that sample, the thread count, a
+    description, and the oracle's walk outputs per request of the sample."""
     import numpy as np
 
     import oracle
@@ -258,6 +259,7 @@ def cpu_baseline(w, budget_s: float, min_p: float = 0.0, siblings: str = "sample
     cu, par, ctx = w["cu_nodes"], w["parent"], w["ctx_len"]
     nodes_done, req_done, spent = 0, 0, 0.0
     chunk = 4
+    ref = {}
     while req_done < w["B"] and spent < budget_s:
         b0, b1 = req_done, min(w["B"], req_done + chunk)
         n0, n1 = int(cu[b0]), int(cu[b1])
@@ -272,15 +274,96 @@ def cpu_baseline(w, budget_s: float, min_p: float = 0.0, siblings: str = "sample
         t0 = time.perf_counter()
         oracle.attention(q, k, v, ctx[b0:b1], sub_cu, par[n0:n1], Hq=w["Hq"], Hkv=w["Hkv"], dtype=w["dtype"],
                          nthreads=threads)
-        oracle.verify(sub_cu, par[n0:n1], toks, lg, qq, temperature=w["temperature"], seed=w["seed"],
-                      request_id=np.arange(b0, b1, dtype=np.uint32), nthreads=threads, min_p=min_p,
-                      siblings=siblings, rule=rule, rule_param=rule_param, eta=eta)
+        o = oracle.verify(sub_cu, par[n0:n1], toks, lg, qq, temperature=w["temperature"], seed=w["seed"],
+                          request_id=np.arange(b0, b1, dtype=np.uint32), nthreads=threads, min_p=min_p,
+                          siblings=siblings, rule=rule, rule_param=rule_param, eta=eta, max_depth=64)
         spent += time.perf_counter() - t0
+        for i, b in enumerate(range(b0, b1)):
+            ref[b] = {k: o[k][i] for k in ("accept_len", "accepted_nodes", "out_tokens", "flag_depth", "flag_kind",
+                                           "draw_mass")}
         nodes_done += n1 - n0
         req_done = b1
     desc = (f"first {req_done} of {w['B']} requests ({nodes_done} draft nodes): fp64 attention of every "
             f"(node, query head) plus the verification walk, {spent:.1f} s")
-    return nodes_done / spent, threads, desc
+    return nodes_done / spent, threads, desc, ref
+
+
+def compare_sample(s, ref: dict) -> dict:
+    """The GPU's walk outputs on the requests of the CPU-baseline sample against
+    the oracle's: bit for bit, except after a decision the oracle flags as a
+    near tie (only the path decided before it must agree). Returns the counts:
+    checked, flagged by kind, flagged requests identical in full anyway,
+    mismatched (must be 0), and the final-draw near ties expected from the
+    1e-6 CDF tolerance (a draw of a token of mass m is one with probability
+    min(1, 2e-6 / m))."""
+    acc = s.accept_len.cpu().numpy()
+    nodes = s.accepted_nodes.cpu().numpy()
+    toks = s.out_tokens.cpu().numpy()
+    md = nodes.shape[1]
+    kinds = {0: "accept_test", 1: "final_draw", 2: "allowed_set_boundary", 3: "remainder"}
+    out = {"checked": len(ref), "flagged": 0, "flagged_by_kind": {}, "flagged_identical": 0, "mismatched": 0,
+           "final_draw_expected": 0.0}
+    for b, o in ref.items():
+        fd = int(o["flag_depth"])
+        full = acc[b] == o["accept_len"] and (nodes[b] == o["accepted_nodes"][:md]).all() and \
+            (toks[b] == o["out_tokens"][:md + 1]).all()
+        m = float(o["draw_mass"])
+        out["final_draw_expected"] += min(1.0, 2e-6 / m) if m > 0 else 0.0
+        if fd >= 0:
+            out["flagged"] += 1
+            k = kinds.get(int(o["flag_kind"]), str(int(o["flag_kind"])))
+            out["flagged_by_kind"][k] = out["flagged_by_kind"].get(k, 0) + 1
+            out["flagged_identical"] += int(full)
+            same = (nodes[b, :fd] == o["accepted_nodes"][:fd]).all() and (toks[b, :fd] == o["out_tokens"][:fd]).all()
+        else:
+            same = full
+        out["mismatched"] += 0 if same else 1
+    out["final_draw_expected"] = round(out["final_draw_expected"], 2)
+    return out
+
+
+def walk_metrics(w, s, K: int, elapsed: float, passes) -> dict:
+    """Acceptance statistics of the first input set's batch: the mean accepted
+    length, AL = mean emitted tokens per step ([SPEED] section 3.4: accepted
+    drafts plus the token the target always adds), the conditional acceptance
+    rate per depth AR_d (accepted at depth d among requests that reached
+    depth d with at least one candidate there), ECHO's mean accepted tokens
+    (MAT, the mean accepted length) and draft utilisation u = accepted length
+    over the tree's depth ([ECHO] section 5.1, averaged over requests with a
+    tree)."""
+    import numpy as np
+
+    acc = s.accept_len.cpu().numpy()
+    nodes = s.accepted_nodes.cpu().numpy()
+    cu, par = w["cu_nodes"], w["parent"]
+    reached, accepted, util = {}, {}, []
+    for b in range(w["B"]):
+        p = par[cu[b]:cu[b + 1]]
+        if p.size == 0:
+            continue
+        depth = np.zeros(p.size, np.int64)
+        for j in range(p.size):
+            depth[j] = 1 + (depth[p[j]] if p[j] >= 0 else 0)
+        util.append(acc[b] / depth.max())
+        pos = -1
+        for d in range(p.size):
+            if not (p == pos).any():
+                break
+            reached[d] = reached.get(d, 0) + 1
+            if acc[b] > d:
+                accepted[d] = accepted.get(d, 0) + 1
+                pos = int(nodes[b, d])
+            else:
+                break
+    ar = [round(accepted.get(d, 0) / reached[d], 4) for d in sorted(reached)]
+    return {"mean_accept_len": round(float(acc.mean()), 4),
+            "AL": round(float(acc.mean()) + 1.0, 4),
+            "AR_per_depth": ar,
+            "MAT": round(float(acc.mean()), 4),
+            "draft_utilisation_u": round(float(np.mean(util)), 4) if util else None,
+            "emitted_tokens_per_s": round(float((acc + 1).sum()) * K / elapsed, 1),
+            "residual_passes_per_step": int(passes.sum().item()),
+            "max_residual_passes_per_request": int(passes.max().item())}
 
 
 def main():
@@ -338,7 +421,7 @@ def main():
             del k, v
     torch.cuda.synchronize()
     input_sha = None
-    if args.hash_inputs:
+    if args.hash_inputs or set_bytes < ROTATE_BYTES:
         input_sha = {}
         for key in ("q", "k_cache", "v_cache", "ctx_len_t", "cu_nodes_t", "parent_t", "draft_tokens", "logits",
                     "draft_probs", "k_pool", "v_pool", "block_table"):
@@ -368,10 +451,7 @@ def main():
 
     K, W = args.steps, args.warmup
     use_events = not (args.no_events or args.graph)
-    ev = None
-    if use_events:
-        hev = HipEvents(4 * K)
-        ev = [tuple(hev.ev[4 * i:4 * i + 4]) for i in range(K)]
+    hev = HipEvents(5 * K) if use_events else None  # per step: attn start/stop, sampler start, stats stop, sampler stop
 
     for i in range(max(W, n_sets)):
         calls[i % n_sets][2](stream)
@@ -397,13 +477,12 @@ def main():
     t0 = time.perf_counter()
     for i in range(K):
         a, s, step = calls[i % n_sets]
-        if use_events:
-            a.set_prof_events(ev[i][0], ev[i][1])
-            s.set_prof_events(ev[i][2], ev[i][3])
         sev.record(2 * i, stream)
         if graphs is not None:
             with torch.cuda.stream(stream):
                 graphs[i % n_sets].replay()
+        elif use_events:
+            step.timed(stream, *hev.ev[5 * i:5 * i + 5])
         else:
             step(stream)
         sev.record(2 * i + 1, stream)
@@ -415,8 +494,6 @@ def main():
     pct = lambda f: step_ms[min(K - 1, int(round(f * (K - 1))))]
     status = 0
     for a, s, _ in calls:
-        a.set_prof_events(None, None)
-        s.set_prof_events(None, None)
         status |= int(s.status.item()) | int(a.status.item())
     a, s, _ = calls[0]
     if status:
@@ -426,42 +503,54 @@ def main():
     ms = elapsed / K * 1e3
     value = w["N"] * K / elapsed
     acc = s.accept_len.double()
+    # residual passes per step, averaged over the input sets (each set runs
+    # K / n_sets of the timed steps)
+    passes_per_set = [float(c[1].passes.double().sum().item()) for c in calls]
+    passes_mean = sum(passes_per_set) / len(passes_per_set)
     passes = s.passes.double()
 
     kernels = {}
     attn_b, attn_f = attention_bytes(w, 1 if args.kv_fp8 else 0), attention_flops(w)
     rs_b = row_stats_bytes(w)
+    # sampled siblings: one 8V pass (logits and q) per rejection; deterministic
+    # candidates and the truncation rule's membership tests need none (the
+    # truncation visit and redraw passes are not counted here)
+    per_pass = 0 if det or args.rule == "truncation" else 8 * w["V"]
+    roofline = None
     if use_events:
-        attn_ms = sum(hev.ms(4 * i, 4 * i + 1) for i in range(K)) / K
-        rs_ms = sum(hev.ms(4 * i + 2, 4 * i + 3) for i in range(K)) / K
+        attn_ms = sum(hev.ms(5 * i, 5 * i + 1) for i in range(K)) / K
+        rs_ms = sum(hev.ms(5 * i + 2, 5 * i + 3) for i in range(K)) / K
+        smp_ms = sum(hev.ms(5 * i + 2, 5 * i + 4) for i in range(K)) / K
         hev.close()
         attn_name = attention_kernel_name(w, cfg, args.kv_fp8)
         kernels[attn_name] = {"us": attn_ms * 1e3, "alg_bytes": attn_b, "GB_s": attn_b / attn_ms / 1e6,
                               "TFLOP_s": attn_f / attn_ms / 1e9}
         kernels["row_stats_kernel"] = {"us": rs_ms * 1e3, "alg_bytes": rs_b, "GB_s": rs_b / rs_ms / 1e6}
-        rest_us = ms * 1e3 - attn_ms * 1e3 - rs_ms * 1e3
-        # sampled siblings: one 8V pass (logits and q) per rejection; deterministic
-        # candidates and the truncation rule's membership tests need none (the
-        # truncation visit and redraw passes are not counted here)
-        per_pass = 0 if det or args.rule == "truncation" else 8 * w["V"]
-        kernels["other(prep+finalize+walk)"] = {"us": rest_us,
-                                            "residual_pass_bytes": float(passes.sum().item()) * per_pass}
-        dom = max((k for k in kernels if "alg_bytes" in kernels[k]), key=lambda k: kernels[k]["us"])
+        # the whole sampler (row statistics + finalisation + walk) on the lazy
+        # denominator: every logit row once, plus the residual passes the walk
+        # made (logits and q of the rejected row)
+        smp_b = rs_b + passes_mean * per_pass
+        kernels["sampler(stats+finalize+walk)"] = {
+            "us": smp_ms * 1e3, "alg_bytes": smp_b, "GB_s": smp_b / smp_ms / 1e6,
+            "frac": smp_b / smp_ms / 1e6 / HBM_PEAK_GBS, "residual_pass_bytes": passes_mean * per_pass}
+        rest_us = ms * 1e3 - attn_ms * 1e3 - smp_ms * 1e3
+        kernels["other(prep+combine)"] = {"us": rest_us}
+        dom = attn_name if attn_ms >= rs_ms else "row_stats_kernel"
         dk = kernels[dom]
         # the committed counters were taken with contiguous bf16 caches
         traffic = counter_traffic(dom, cfg.name) if not (args.paged or args.kv_fp8) else None
         roofline = {"kernel": dom, "bound": "hbm", "achieved": round(dk["GB_s"], 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(dk["GB_s"] / HBM_PEAK_GBS, 4),
                     "traffic": traffic, "measured_copy_GB_s": round(copy_bandwidth(), 1)}
-    else:
-        roofline = None
 
     cpu = None
+    parity = None
     if args.cpu_seconds > 0:
-        v_cpu, threads, desc = cpu_baseline(w, args.cpu_seconds, args.min_p, args.siblings, args.rule, args.rule_param,
-                                            tuple(args.eta) if args.eta else None)
+        v_cpu, threads, desc, ref = cpu_baseline(w, args.cpu_seconds, args.min_p, args.siblings, args.rule,
+                                                 args.rule_param, tuple(args.eta) if args.eta else None)
         cpu = {"value": round(v_cpu, 2), "unit": "verified draft tokens/s", "cores": threads, "kind": "oracle",
                "sample": desc}
+        parity = compare_sample(s, ref)
 
     line = {
         "metric": "verified draft tokens/sec",
@@ -479,7 +568,8 @@ def main():
         "data": "synthetic (seeded; no dataset, no model weights)",
         "config": {"workload": cfg.name, "B": w["B"], "draft_nodes": w["N"], "max_T": w["max_T"], "L": cfg.L,
                    "Hq": cfg.Hq, "Hkv": cfg.Hkv, "D": cfg.D, "kv_dtype": cfg.dtype, "V": cfg.V,
-                   "temperature": cfg.temperature, **({"min_p": args.min_p} if args.min_p > 0 else {}),
+                   "temperature": cfg.temperature, "input_seed": cfg.seed, "library_seed": cfg.lib_seed,
+                   **({"min_p": args.min_p} if args.min_p > 0 else {}),
                    **({"siblings": "deterministic (top-k of q)"} if det else {}),
                    **({"eta": list(args.eta)} if args.eta else {}),
                    **({"kv_layout": f"paged, {args.paged}-slot blocks"} if args.paged else {}),
@@ -488,15 +578,13 @@ def main():
                       else {"rule": args.rule} if args.rule == "truncation" else {})},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "near_ties": parity,
         "input_sets": n_sets,
         **({"input_sha256_16": input_sha} if input_sha else {}),
         **({"hip_graph": True} if args.graph else {}),
-        "kernels": {k: {kk: (round(vv, 2) if isinstance(vv, float) else vv) for kk, vv in d.items()}
-                    for k, d in kernels.items()},
-        "walk": {"mean_accept_len": round(float(acc.mean().item()), 4),
-                 "emitted_tokens_per_s": round(float((acc + 1).sum().item()) * K / elapsed, 1),
-                 "residual_passes_per_step": int(passes.sum().item()),
-                 "max_residual_passes_per_request": int(passes.max().item())},
+        "kernels": {k: {kk: (round(vv, 4 if kk == "frac" else 2) if isinstance(vv, float) else vv)
+                        for kk, vv in d.items()} for k, d in kernels.items()},
+        "walk": walk_metrics(w, s, K, elapsed, passes),
     }
     print(json.dumps(line), flush=True)
 

@@ -76,7 +76,9 @@ typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
 #define SV_STATUS_TREE_INVALID   0x01 /* parent outside [-1, j-1]: node treated as a root child (attn) / request skipped (sample) */
 #define SV_STATUS_PACKING        0x02 /* cu_nodes not monotone, T_b > max_nodes, or cu_nodes[B] != total_nodes: request skipped */
 #define SV_STATUS_TOKEN_RANGE    0x04 /* draft token outside [0, V): request skipped */
-#define SV_STATUS_NONFINITE      0x08 /* NaN or +inf logit in a row, or a row whose logits are all -inf */
+#define SV_STATUS_NONFINITE      0x08 /* a row with a NaN or +inf logit, or whose logits are all -inf: it has no
+                                         target distribution; a walk that reaches it stops there, without a
+                                         token at that position (out_tokens[b][accept_len[b]] = -1) */
 #define SV_STATUS_ZERO_RESIDUAL  0x10 /* residual mass rounded to 0 after a rejection: distribution kept unchanged */
 #define SV_STATUS_CTX_RANGE      0x20 /* ctx_len[b] < 0 or ctx_len[b] + T_b > Lcap: request skipped */
 #define SV_STATUS_SYNC           0x40 /* a sampler workgroup gave up waiting for the other workgroups of its request
@@ -115,8 +117,6 @@ typedef struct {
   int32_t num_splits;  /* KV-length splits; 0 = chosen by the library         */
   float* out;          /* [N, Hq, D] fp32, 16-byte aligned                    */
   int32_t* status;     /* optional device word for SV_STATUS_* bits           */
-  void* prof_start;    /* optional hipEvent_t recorded right before the        */
-  void* prof_stop;     /*   attention kernel / right after it (measurement)   */
   /* Paged caches (optional; the layout of PagedAttention-style engines, which
    * [SD] "Tree Attention Mask Mechanics" names as the kernels a tree mask is
    * handed to). block_table == NULL: k_cache / v_cache are [B, Hkv, Lcap, D].
@@ -222,20 +222,25 @@ typedef struct {
   float min_p;         /* 0 = off; in (0, 1) with temperature > 0: verify
                           against the min-p truncated target ([LOSSY] 2.3,
                           "truncation sampling + SD", G.2): p restricted to
-                          A = {x : l_x - l_max >= fp32(T ln min_p)} (that is,
-                          p(x) >= min_p * max p, decided on the fp32 logit
-                          difference) and renormalised; every rule below then
-                          applies with p_Theta in place of p. Each visited
-                          position costs one more vocabulary pass (the mass
-                          of A). Not with probs_out.                         */
+                          A = {x : p(x) >= min_p * max p}, decided exactly as
+                          l_x - l_max >= T ln min_p (the logit difference and
+                          the threshold in fp64, from the fp32 T and min_p),
+                          and renormalised; every rule below then applies
+                          with p_Theta in place of p. Each visited position
+                          costs one more vocabulary pass (the mass of A).
+                          Not with probs_out.                                */
   float eta_eps;       /* 0 = off; in (0, 1) with temperature > 0 and min_p == 0:
                           verify against the eta truncated target ([LOSSY] 2.3):
                           A = {x : p(x) >= min(eta_eps, eta_delta exp(-H(p)))},
                           H the entropy of p in nats, decided as
-                          l_x - l_max >= fp32(T (ln S + ln tau)) with S the
-                          row's sum of exp((l - l_max)/T), computed in fp64
-                          per row (an extra accumulator in the row statistics
-                          pass); otherwise as min_p. Not with probs_out.    */
+                          l_x - l_max >= T (ln S + ln tau) with S the row's
+                          sum of exp((l - l_max)/T); the threshold is formed
+                          in fp64 per row from the row statistics pass (an
+                          extra accumulator there), whose fp32 weights put it
+                          within about 2^-24 (8 + 12 G + 3 Var + 6 G^2) T of
+                          the exact one (G = E_p[(l_max - l)/T], Var the
+                          variance of l/T under p); otherwise as min_p. Not
+                          with probs_out.                                   */
   float eta_delta;     /* delta of the eta set, in (0, 1] when eta_eps > 0     */
   int32_t siblings;    /* sv_siblings: how the children of a node were drafted */
   int32_t rule;        /* sv_rule (SV_RULE_LOSSLESS unless sampled siblings)   */
@@ -254,9 +259,23 @@ typedef struct {
   int32_t* residual_passes; /* optional [B]: rejections during the walk (with sampled siblings, each
                                costs one vocabulary pass for the residual mass) */
   int32_t* status;          /* optional device word for SV_STATUS_* bits           */
-  void* prof_start;         /* optional hipEvent_t recorded right before the row-statistics */
-  void* prof_stop;          /*   kernel / right after it (measurement)                     */
+  /* Layout of the walk (results are bitwise the same in every layout):
+   *   SV_WALK_AUTO: one 512-thread workgroup per request, or, when the walk
+   *     makes vocabulary passes and the batch leaves at least four workgroup
+   *     slots per request on the device, up to 8 256-thread workgroups
+   *     ("slices") per request that split every pass;
+   *   SV_WALK_SINGLE: always one workgroup per request;
+   *   SV_WALK_SLICED: slices whenever the walk makes vocabulary passes.
+   * The slices of a request first agree to cooperate: once all have started
+   * they walk it together; if join_ticks of the 100 MHz device clock pass
+   * first, one of them walks it alone. join_ticks: 0 = 2000 (20 us);
+   * > 0 = that many (at most 10^8); -1 = none (the first slice to look
+   * walks alone).                                                          */
+  int32_t walk_mode;
+  int32_t join_ticks;
 } sv_sample_args;
+
+enum { SV_WALK_AUTO = 0, SV_WALK_SINGLE = 1, SV_WALK_SLICED = 2 };
 
 /* ------------------------------------------------------------------------ */
 /* Budgeted super-tree packing ([ECHO] section 3.1, "Super-Tree View": the
@@ -322,6 +341,21 @@ sv_status spec_verify_sample(const sv_sample_args* sample, void* ws, size_t ws_b
  * the same batch (B, total_nodes, cu_nodes). ws: spec_verify_workspace_size(attn, sample). */
 sv_status spec_verify_step(const sv_attn_args* attn, const sv_sample_args* sample,
                            void* ws, size_t ws_bytes, void* stream);
+
+/* Timing events of spec_verify_step_timed (measurement): hipEvent_t handles
+ * created by the caller, each recorded on the call's stream when non-NULL. */
+typedef struct {
+  void* attn_start;   /* before the attention kernel (after tree preparation) */
+  void* attn_stop;    /* after the attention kernel (before a split merge)    */
+  void* sample_start; /* before the sampler's row-statistics kernel           */
+  void* stats_stop;   /* after the row-statistics kernel                      */
+  void* sample_stop;  /* after the walk (the sampler's last kernel)           */
+} sv_timing;
+
+/* spec_verify_step that also records the events of *timing (may be NULL);
+ * otherwise identical.                                                     */
+sv_status spec_verify_step_timed(const sv_attn_args* attn, const sv_sample_args* sample, void* ws, size_t ws_bytes,
+                                 void* stream, const sv_timing* timing);
 
 /* Message of the last failed call on this thread ("" if none).             */
 const char* spec_verify_last_error(void);

@@ -89,7 +89,7 @@ def _load():
     lib.orc_verify.argtypes = [i32, i32, P, P, P, P, P, f64, i32, f64, f64, f64, f64, i32, i32, f64, u64,
                                u32, P, i32,
                                P, P, P, P,
-                               P, P, P, P, P, P, f64, f64, i32]
+                               P, P, P, P, P, P, P, f64, f64, i32]
     lib.orc_verify.restype = i32
     lib.orc_target_rows.argtypes = [i32, P, f64, i64, P, P]
     lib.orc_target_rows.restype = i32
@@ -343,8 +343,9 @@ def verify(cu_nodes, parent, tokens, logits, q, *, temperature, seed, step=0, re
     fp64 threshold). flag_kind 2 marks a position whose outcome some threshold
     within the set's band would change; set_tol > 0 fixes the band's
     half-width (log-probability units), 0 takes each set's own error bound:
-    fp64 rounding of T ln p_base for min-p, the first-order bound of a
-    threshold evaluated with fp32 weights for eta.
+    fp64 rounding of T ln p_base for min-p, the first-order bound of two
+    fp64 evaluations of the eta threshold (sums of V fp64 weights in any
+    order) for eta.
     rule="truncation": truncation-based verification ([LOSSY] 3.2) over the
     min-p or eta allowed set: accept iff the drafted token is allowed; after
     every child of a position is rejected, draw from q restricted to the set.
@@ -379,6 +380,7 @@ def verify(cu_nodes, parent, tokens, logits, q, *, temperature, seed, step=0, re
         "status": np.zeros(B, np.int32),
         "min_accept_margin": np.zeros(B, np.float64),
         "cdf_margin": np.zeros(B, np.float64),
+        "draw_mass": np.zeros(B, np.float64),
     }
     theta = min_p_theta(temperature, min_p)
     trunc = 1 if theta > float("-inf") else 0
@@ -396,7 +398,8 @@ def verify(cu_nodes, parent, tokens, logits, q, *, temperature, seed, step=0, re
                             _ptr(out["accepted_nodes"]), _ptr(out["out_tokens"]), _ptr(out["uniforms"]),
                             _ptr(out["flag_depth"]), _ptr(out["flag_kind"]), _ptr(out["n_rejections"]),
                             _ptr(out["status"]), _ptr(out["min_accept_margin"]), _ptr(out["cdf_margin"]),
-                            float(accept_tol), float(cdf_tol), nthreads or _default_threads())
+                            _ptr(out["draw_mass"]), float(accept_tol), float(cdf_tol),
+                            nthreads or _default_threads())
     if rc != 0:
         raise ValueError("oracle verify: bad arguments")
     return out

@@ -508,7 +508,7 @@ typedef struct {
   int32_t *accept_len, *accepted_nodes, *out_tokens;
   double* uniforms_out;
   int32_t *flag_depth, *flag_kind, *n_rejections, *status;
-  double *min_accept_margin, *cdf_margin;
+  double *min_accept_margin, *cdf_margin, *draw_mass;
   double accept_tol, cdf_tol;
 } orc_walk_ctx;
 
@@ -516,6 +516,7 @@ typedef struct {
 typedef struct {
   double min_accept_margin; /* smallest |u - h| over its accept tests      */
   double cdf_margin;        /* margin of its draw (INFINITY: no draw)      */
+  double draw_mass;         /* probability of the drawn token (0: no draw) */
   int near_kind;            /* first near tie: 0 accept test, 1 draw,
                                3 deterministic remainder near 0; -1 none  */
   int rejections;
@@ -545,6 +546,7 @@ static int orc_position(const orc_walk_ctx* c, int b, int pos, double th, orc_re
   const float* lrow = c->logits + row * (int64_t)V;
   rec->min_accept_margin = INFINITY;
   rec->cdf_margin = INFINITY;
+  rec->draw_mass = 0.0;
   rec->near_kind = -1;
   rec->rejections = 0;
   rec->status = 0;
@@ -640,6 +642,11 @@ static int orc_position(const orc_walk_ctx* c, int b, int pos, double th, orc_re
   double margin = 0.0;
   *bonus = orc_inverse_cdf(V, P, u, &margin);
   rec->cdf_margin = margin;
+  if (*bonus >= 0) {
+    double total = 0.0;
+    for (int x = 0; x < V; ++x) total += P[x];
+    rec->draw_mass = P[*bonus] / total;
+  }
   if (margin < c->cdf_tol && rec->near_kind < 0) rec->near_kind = 1;
   return -1;
 }
@@ -702,6 +709,7 @@ static void orc_walk_one(void* vctx, int64_t bi) {
   c->status[b] = 0;
   c->min_accept_margin[b] = INFINITY;
   c->cdf_margin[b] = INFINITY;
+  c->draw_mass[b] = 0.0;
 
   int64_t n0 = c->cu_nodes[b];
   int T = c->cu_nodes[b + 1] - c->cu_nodes[b];
@@ -767,13 +775,13 @@ static void orc_walk_one(void* vctx, int64_t bi) {
     } else if (c->trunc == 2 && orc_row_finite(V, lrow)) {
       double G = 0.0, Var = 0.0;
       th = orc_eta_threshold(V, lrow, c->T, c->eta_eps, c->eta_delta, &G, &Var);
-      /* An evaluation that weighs each token with an fp32 exponential of an
-       * fp32 argument (relative error of the argument <= 3 * 2^-24, of the
-       * exponential <= 2^-22) and sums in fp64 gets ln S within
-       * 2^-24 (3 G + 4) and G within 2^-24 (12 G + 3 Var + 6 G^2) (first
-       * order); the threshold is T (ln S + ln eps) or T (ln delta - G).     */
+      /* Two evaluations of the threshold T (ln S + ln eps) or T (ln delta - G)
+       * that weigh each token in fp64 (argument and exponential within a few
+       * fp64 roundings) and sum V terms in fp64 in any order differ by at
+       * most 2^-53 (V + 64) (8 + 8 G + 4 Var + 4 G^2) T (first order, every
+       * rounding aligned): the band of the set's own error bound.           */
       band = c->set_tol > 0.0 ? c->set_tol * c->T
-                              : c->T * ldexp(8.0 + 12.0 * G + 3.0 * Var + 6.0 * G * G, -24);
+                              : c->T * ldexp((double)(V + 64) * (8.0 + 8.0 * G + 4.0 * Var + 4.0 * G * G), -53);
     }
     orc_rec rec;
     int bonus = -1;
@@ -782,6 +790,7 @@ static void orc_walk_one(void* vctx, int64_t bi) {
     c->status[b] |= rec.status;
     if (rec.min_accept_margin < c->min_accept_margin[b]) c->min_accept_margin[b] = rec.min_accept_margin;
     if (rec.cdf_margin < INFINITY) c->cdf_margin[b] = rec.cdf_margin;
+    c->draw_mass[b] = rec.draw_mass;
     if (c->flag_depth[b] < 0) {
       if (c->trunc && !(rec.status & 0x08) && orc_band_changes(c, b, pos, th, band, acc, bonus, P, Q, tmp)) {
         c->flag_depth[b] = d;
@@ -823,22 +832,26 @@ static void orc_walk_one(void* vctx, int64_t bi) {
  *   flag_kind:  0 = accept test with |u - h| < accept_tol, 1 = final draw
  *               with a CDF boundary within cdf_tol of u, 2 = allowed-set
  *               boundary: a threshold within the set's band (set_tol, or
- *               the set's own error bound when set_tol == 0) changes the
- *               position's outcome, 3 = deterministic remainder at most
- *               1e-11 of the row's mass;
+ *               the set's own error bound when set_tol == 0: fp64 rounding
+ *               of its evaluation) changes the position's outcome,
+ *               3 = deterministic remainder at most 1e-11 of the row's mass;
  *   n_rejections: rejections (= residual renormalisations or removals);
  *   status: SV_STATUS-like bits (0x01 tree, 0x02 packing, 0x04 token,
  *           0x08 non-finite row reached, 0x10 zero residual, 0x80 out of
  *           memory);
  *   min_accept_margin, cdf_margin: the smallest |u - h| seen and the
- *           margin of the final draw.                                     */
+ *           margin of the final draw;
+ *   draw_mass: probability of the drawn token under the distribution it
+ *           was drawn from (0: no draw). Given the token, u is uniform over
+ *           its CDF interval, so the draw is a near tie (margin < cdf_tol)
+ *           with probability min(1, 2 cdf_tol / draw_mass).              */
 int orc_verify(int B, int V, const int32_t* cu_nodes, const int32_t* parent, const int32_t* tokens,
                const float* logits, const float* q, double T, int trunc, double p_base, double eta_eps,
                double eta_delta, double set_tol, int det, int rule, double rule_param, uint64_t seed, uint32_t step,
                const uint32_t* request_id, int max_depth, int32_t* accept_len, int32_t* accepted_nodes,
                int32_t* out_tokens, double* uniforms_out, int32_t* flag_depth, int32_t* flag_kind,
                int32_t* n_rejections, int32_t* status, double* min_accept_margin, double* cdf_margin,
-               double accept_tol, double cdf_tol, int nthreads) {
+               double* draw_mass, double accept_tol, double cdf_tol, int nthreads) {
   if (B < 0 || V < 1 || max_depth < 0 || T < 0.0) return 1;
   if (T > 0.0 && !det && !q) return 1;
   if (rule < 0 || rule > 3 || (rule && det)) return 1;
@@ -852,7 +865,7 @@ int orc_verify(int B, int V, const int32_t* cu_nodes, const int32_t* parent, con
                     det, rule, rule_param, seed, step,
                     request_id, max_depth,
                     accept_len, accepted_nodes, out_tokens, uniforms_out, flag_depth, flag_kind,
-                    n_rejections, status, min_accept_margin, cdf_margin, accept_tol, cdf_tol};
+                    n_rejections, status, min_accept_margin, cdf_margin, draw_mass, accept_tol, cdf_tol};
   orc_parallel_for(B, nthreads, orc_walk_one, &c);
   return 0;
 }

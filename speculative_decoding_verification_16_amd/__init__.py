@@ -25,6 +25,7 @@ LIB_PATH = os.path.join(_PKG, "libspecverify.so")
 SV_OK, SV_ERR_INVALID_ARG, SV_ERR_TREE, SV_ERR_UNSUPPORTED, SV_ERR_WORKSPACE, SV_ERR_HIP = range(6)
 SV_F32, SV_BF16 = 0, 1
 SIBLINGS = {"sampled": 0, "deterministic": 1}  # sv_siblings
+WALK_MODES = {"auto": 0, "single": 1, "sliced": 2}  # sv_sample_args.walk_mode
 RULES = {"lossless": 0, "lenience": 1, "interpolation": 2, "truncation": 3}  # sv_rule
 STATUS_BITS = {0x01: "TREE_INVALID", 0x02: "PACKING", 0x04: "TOKEN_RANGE", 0x08: "NONFINITE",
                0x10: "ZERO_RESIDUAL", 0x20: "CTX_RANGE", 0x40: "SYNC", 0x80: "BLOCK_RANGE"}
@@ -37,7 +38,7 @@ class SvAttnArgs(ctypes.Structure):
     _fields_ = [("B", _i32), ("total_nodes", _i32), ("max_nodes", _i32), ("Hq", _i32), ("Hkv", _i32), ("D", _i32),
                 ("dtype", _i32), ("q", _P), ("k_cache", _P), ("v_cache", _P), ("Lcap", _i64), ("ctx_len", _P),
                 ("cu_nodes", _P), ("parent", _P), ("anc_mask", _P), ("scale", _f32), ("num_splits", _i32),
-                ("out", _P), ("status", _P), ("prof_start", _P), ("prof_stop", _P), ("block_table", _P),
+                ("out", _P), ("status", _P), ("block_table", _P),
                 ("block_size", _i32), ("max_blocks", _i32), ("num_blocks", _i64), ("kv_fp8", _i32),
                 ("k_scale", _f32), ("v_scale", _f32)]
 
@@ -49,8 +50,13 @@ class SvSampleArgs(ctypes.Structure):
                 ("rule", _i32), ("rule_param", _f32), ("seed", _u64), ("step", _u32), ("request_id", _P),
                 ("max_depth", _i32),
                 ("accept_len", _P), ("accepted_nodes", _P), ("out_tokens", _P), ("probs_out", _P),
-                ("uniforms_out", _P), ("residual_passes", _P), ("status", _P), ("prof_start", _P),
-                ("prof_stop", _P)]
+                ("uniforms_out", _P), ("residual_passes", _P), ("status", _P), ("walk_mode", _i32),
+                ("join_ticks", _i32)]
+
+
+class SvTiming(ctypes.Structure):
+    _fields_ = [("attn_start", _P), ("attn_stop", _P), ("sample_start", _P), ("stats_stop", _P),
+                ("sample_stop", _P)]
 
 
 _lib = None
@@ -73,6 +79,8 @@ def load_library(path: str = LIB_PATH):
         getattr(lib, name).restype = ctypes.c_int
     lib.spec_verify_step.argtypes = [_P, _P, _P, ctypes.c_size_t, _P]
     lib.spec_verify_step.restype = ctypes.c_int
+    lib.spec_verify_step_timed.argtypes = [_P, _P, _P, ctypes.c_size_t, _P, _P]
+    lib.spec_verify_step_timed.restype = ctypes.c_int
     lib.spec_verify_last_error.argtypes = []
     lib.spec_verify_last_error.restype = ctypes.c_char_p
     lib.spec_verify_struct_size.argtypes = [_i32]
@@ -182,9 +190,6 @@ class AttnCall:
             _check(SV_ERR_INVALID_ARG)
         self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=dev)
 
-    def set_prof_events(self, start, stop):
-        self.args.prof_start, self.args.prof_stop = _event_handle(start), _event_handle(stop)
-
     def __call__(self, stream=None):
         _check(load_library().spec_verify_attn(ctypes.byref(self.args), _ptr(self.ws), self.ws_bytes,
                                                _stream_handle(stream)))
@@ -197,12 +202,14 @@ class SampleCall:
     def __init__(self, cu_nodes, parent, draft_tokens, target_logits, draft_probs, *, temperature, seed, step=0,
                  request_id=None, max_nodes=0, max_depth=None, probs_out=False, uniforms_out=False,
                  residual_passes=False, status=None, min_p=0.0, siblings="sampled", rule="lossless",
-                 rule_param=1.0, eta=None):
+                 rule_param=1.0, eta=None, walk_mode="auto", join_ticks=0):
         load_library()
         if siblings not in SIBLINGS:
             raise ValueError(f"siblings must be one of {sorted(SIBLINGS)}")
         if rule not in RULES:
             raise ValueError(f"rule must be one of {sorted(RULES)}")
+        if walk_mode not in WALK_MODES:
+            raise ValueError(f"walk_mode must be one of {sorted(WALK_MODES)}")
         dev = target_logits.device
         assert target_logits.is_cuda and target_logits.dtype == torch.float32 and target_logits.is_contiguous()
         cu = _dev_i32(cu_nodes, dev)
@@ -241,15 +248,13 @@ class SampleCall:
             _ptr(self.out_tokens)
         s.probs_out, s.uniforms_out, s.residual_passes = _ptr(self.probs), _ptr(self.uniforms), _ptr(self.passes)
         s.status = _ptr(self.status)
+        s.walk_mode, s.join_ticks = WALK_MODES[walk_mode], int(join_ticks)
         self.args = s
         lib = load_library()
         self.ws_bytes = lib.spec_verify_workspace_size(None, ctypes.byref(s))
         if self.ws_bytes == 0 and lib.spec_verify_last_error():
             _check(SV_ERR_INVALID_ARG)
         self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=dev)
-
-    def set_prof_events(self, start, stop):
-        self.args.prof_start, self.args.prof_stop = _event_handle(start), _event_handle(stop)
 
     def results(self) -> dict:
         r = {"accept_len": self.accept_len, "accepted_nodes": self.accepted_nodes, "out_tokens": self.out_tokens,
@@ -286,6 +291,19 @@ class StepCall:
     def __call__(self, stream=None):
         _check(load_library().spec_verify_step(ctypes.byref(self.attn.args), ctypes.byref(self.sample.args),
                                                _ptr(self.ws), self.ws_bytes, _stream_handle(stream)))
+        return self._results()
+
+    def timed(self, stream, attn_start=None, attn_stop=None, sample_start=None, stats_stop=None, sample_stop=None):
+        """spec_verify_step_timed: the same step, recording the given hipEvent_t
+        handles (raw ints or torch.cuda.Event) on the stream."""
+        t = SvTiming(_event_handle(attn_start), _event_handle(attn_stop), _event_handle(sample_start),
+                     _event_handle(stats_stop), _event_handle(sample_stop))
+        _check(load_library().spec_verify_step_timed(ctypes.byref(self.attn.args), ctypes.byref(self.sample.args),
+                                                     _ptr(self.ws), self.ws_bytes, _stream_handle(stream),
+                                                     ctypes.byref(t)))
+        return self._results()
+
+    def _results(self):
         r = self.sample.results()
         r["attn_out"] = self.attn.out
         return r

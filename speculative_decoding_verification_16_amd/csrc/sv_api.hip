@@ -70,8 +70,6 @@ sv_status check_attn(const sv_attn_args* a) {
   if (!a->parent && !a->anc_mask) return fail(SV_ERR_INVALID_ARG, "one of parent / anc_mask is required");
   if (!aligned(a->q, 16) || !aligned(a->k_cache, 16) || !aligned(a->v_cache, 16) || !aligned(a->out, 16))
     return fail(SV_ERR_INVALID_ARG, "q, k_cache, v_cache and out must be 16-byte aligned");
-  if ((a->prof_start == nullptr) != (a->prof_stop == nullptr))
-    return fail(SV_ERR_INVALID_ARG, "prof_start and prof_stop must be given together");
   return SV_OK;
 }
 
@@ -176,13 +174,15 @@ WsLayout layout(const sv_attn_args* a, const sv_sample_args* s) {
     off += align_up(((size_t)s->total_nodes + s->B) * sizeof(sv::RowStat));
     if (s->temperature > 0.f && (s->min_p > 0.f || s->eta_eps > 0.f)) {
       w.rtheta = off;  // per-row threshold of the allowed set
-      off += align_up(((size_t)s->total_nodes + s->B) * sizeof(float));
+      off += align_up(((size_t)s->total_nodes + s->B) * sizeof(sv::RowThr));
     }
     if (s->temperature > 0.f && s->eta_eps > 0.f) {
       w.ent = off;  // per-chunk entropy accumulators of the eta set
-      off += align_up(((size_t)s->total_nodes + s->B) * sample_nch(s) * sizeof(double));
+      off += align_up(((size_t)s->total_nodes + s->B) * sample_nch(s) * sizeof(double2));
     }
-    if (sv::walk_slices(s->B, sample_nch(s), walk_passes(s)) > 1) {
+    if (walk_passes(s) && s->walk_mode != SV_WALK_SINGLE) {
+      // the sliced walk's exchange buffers (reserved whenever the walk may be
+      // sliced, so that the size does not depend on the device)
       w.xs = off;
       off += align_up((size_t)s->B * 4 * sample_nch(s) * sizeof(double));
       w.xcnt = off;
@@ -224,6 +224,10 @@ sv_status check_sample(const sv_sample_args* s) {
     return fail(SV_ERR_UNSUPPORTED, "the lossy rules need sampled siblings (they test or draw from q)");
   if (s->rule == SV_RULE_TRUNCATION && !(s->temperature > 0.f && (s->min_p > 0.f || s->eta_eps > 0.f)))
     return fail(SV_ERR_INVALID_ARG, "SV_RULE_TRUNCATION needs temperature > 0 and an allowed set (min_p or eta_eps)");
+  if (s->walk_mode != SV_WALK_AUTO && s->walk_mode != SV_WALK_SINGLE && s->walk_mode != SV_WALK_SLICED)
+    return fail(SV_ERR_INVALID_ARG, "walk_mode must be SV_WALK_AUTO, SV_WALK_SINGLE or SV_WALK_SLICED");
+  if (s->join_ticks < -1 || s->join_ticks > 100000000)
+    return fail(SV_ERR_INVALID_ARG, "join_ticks must be in [-1, 10^8]");
   const int md_needed = eff_max_nodes(s->max_nodes);
   if (s->max_depth < md_needed)
     return fail(SV_ERR_INVALID_ARG, "max_depth (%d) must be >= max_nodes (%d)", s->max_depth, md_needed);
@@ -244,8 +248,6 @@ sv_status check_sample(const sv_sample_args* s) {
   if (!aligned(s->target_logits, 4) || (s->draft_probs && !aligned(s->draft_probs, 4)))
     return fail(SV_ERR_INVALID_ARG, "logit and probability rows must be 4-byte aligned");
   if (!aligned(s->uniforms_out, 8)) return fail(SV_ERR_INVALID_ARG, "uniforms_out must be 8-byte aligned");
-  if ((s->prof_start == nullptr) != (s->prof_stop == nullptr))
-    return fail(SV_ERR_INVALID_ARG, "prof_start and prof_stop must be given together");
   return SV_OK;
 }
 
@@ -275,7 +277,8 @@ sv_status hip_fail(hipError_t e, const char* what) {
   return fail(SV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-sv_status run_attn(const sv_attn_args* a, char* ws, const WsLayout& w, hipStream_t st) {
+sv_status run_attn(const sv_attn_args* a, char* ws, const WsLayout& w, hipStream_t st, hipEvent_t ev_start,
+                   hipEvent_t ev_stop) {
   if (a->B == 0 || a->total_nodes == 0) return SV_OK;
   const sv::AttnPlan pl = plan_attn(a);
   const int mn = eff_max_nodes(a->max_nodes);
@@ -317,13 +320,13 @@ sv_status run_attn(const sv_attn_args* a, char* ws, const WsLayout& w, hipStream
   while (a->block_table && (1 << p.bs_shift) < a->block_size) ++p.bs_shift;
   hipError_t e = sv::launch_attn_prep(p, pl, a->parent, w_anc, st);
   if (e != hipSuccess) return hip_fail(e, "attention prep launch");
-  e = sv::launch_attention(p, pl, a->dtype == SV_BF16, st, (hipEvent_t)a->prof_start,
-                                      (hipEvent_t)a->prof_stop);
+  e = sv::launch_attention(p, pl, a->dtype == SV_BF16, st, ev_start, ev_stop);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return SV_OK;
 }
 
-sv_status run_sample(const sv_sample_args* s, char* ws, const WsLayout& w, hipStream_t st) {
+sv_status run_sample(const sv_sample_args* s, char* ws, const WsLayout& w, hipStream_t st,
+                     const sv::SampleEvents& ev) {
   if (s->B == 0) return SV_OK;
   sv::SampleParams p{};
   p.B = s->B;
@@ -338,18 +341,19 @@ sv_status run_sample(const sv_sample_args* s, char* ws, const WsLayout& w, hipSt
   p.logits = s->target_logits;
   p.q = s->draft_probs;
   p.greedy = s->temperature == 0.f;
-  p.c = p.greedy ? 0.f : (float)(1.4426950408889634 / (double)s->temperature);
-  // min-p allowed set: logit - row max >= fp32(T ln min_p), from the fp32 T and min_p
+  p.c64 = p.greedy ? 0.0 : 1.4426950408889634 / (double)s->temperature;
+  p.c = (float)p.c64;
+  // min-p allowed set: logit - row max >= T ln min_p in fp64, from the fp32 T and min_p
   p.eta = !p.greedy && s->eta_eps > 0.f;
   p.trunc = !p.greedy && (s->min_p > 0.f || p.eta);
-  p.theta = (p.trunc && !p.eta) ? (float)((double)s->temperature * log((double)s->min_p)) : -INFINITY;
+  p.mp_thr = sv::make_row_thr((p.trunc && !p.eta) ? (double)s->temperature * log((double)s->min_p) : 0.0);
   // eta allowed set: the per-row threshold T (ln S + min(ln eps, ln delta - H))
   // is formed by the row finalisation from these fp64 logs of the fp32 inputs
   p.temp = (double)s->temperature;
   p.ln_eps = p.eta ? log((double)s->eta_eps) : 0.0;
   p.ln_delta = p.eta ? log((double)s->eta_delta) : 0.0;
-  p.ent = w.ent ? (double*)(ws + w.ent) : nullptr;
-  p.rtheta = w.rtheta ? (float*)(ws + w.rtheta) : nullptr;
+  p.ent = w.ent ? (double2*)(ws + w.ent) : nullptr;
+  p.rthr = w.rtheta ? (sv::RowThr*)(ws + w.rtheta) : nullptr;
   p.seed = s->seed;
   p.step = s->step;
   p.request_id = s->request_id;
@@ -365,11 +369,12 @@ sv_status run_sample(const sv_sample_args* s, char* ws, const WsLayout& w, hipSt
   p.det = s->siblings == SV_SIBLINGS_DETERMINISTIC;
   p.rule = s->rule;
   p.rule_param = s->rule_param;
-  p.slices = w.xcnt ? sv::walk_slices(s->B, p.nch, walk_passes(s)) : 1;
+  p.slices = w.xcnt ? sv::walk_slices(s->B, p.nch, walk_passes(s), s->walk_mode) : 1;
   p.xs = w.xcnt ? (double*)(ws + w.xs) : nullptr;
   p.xcnt = w.xcnt ? (int32_t*)(ws + w.xcnt) : nullptr;
+  p.join_ticks = s->join_ticks == 0 ? sv::kJoinWindow : (s->join_ticks < 0 ? 0u : (uint32_t)s->join_ticks);
   const bool vec4 = (s->V % 4 == 0) && aligned(s->target_logits, 16) && (!s->draft_probs || aligned(s->draft_probs, 16));
-  hipError_t e = sv::launch_sampler(p, vec4, st, (hipEvent_t)s->prof_start, (hipEvent_t)s->prof_stop);
+  hipError_t e = sv::launch_sampler(p, vec4, st, ev);
   if (e != hipSuccess) return hip_fail(e, "sampler launch");
   return SV_OK;
 }
@@ -390,7 +395,7 @@ sv_status spec_verify_attn(const sv_attn_args* attn, void* ws, size_t ws_bytes, 
   if (st != SV_OK) return st;
   const WsLayout w = layout(attn, nullptr);
   if ((st = check_ws(w, ws, ws_bytes)) != SV_OK) return st;
-  return run_attn(attn, (char*)ws, w, (hipStream_t)stream);
+  return run_attn(attn, (char*)ws, w, (hipStream_t)stream, nullptr, nullptr);
 }
 
 sv_status spec_verify_sample(const sv_sample_args* sample, void* ws, size_t ws_bytes, void* stream) {
@@ -399,11 +404,11 @@ sv_status spec_verify_sample(const sv_sample_args* sample, void* ws, size_t ws_b
   if (st != SV_OK) return st;
   const WsLayout w = layout(nullptr, sample);
   if ((st = check_ws(w, ws, ws_bytes)) != SV_OK) return st;
-  return run_sample(sample, (char*)ws, w, (hipStream_t)stream);
+  return run_sample(sample, (char*)ws, w, (hipStream_t)stream, sv::SampleEvents{});
 }
 
-sv_status spec_verify_step(const sv_attn_args* attn, const sv_sample_args* sample, void* ws, size_t ws_bytes,
-                           void* stream) {
+sv_status spec_verify_step_timed(const sv_attn_args* attn, const sv_sample_args* sample, void* ws, size_t ws_bytes,
+                                 void* stream, const sv_timing* timing) {
   g_err[0] = 0;
   sv_status st = check_attn(attn);
   if (st != SV_OK) return st;
@@ -412,9 +417,19 @@ sv_status spec_verify_step(const sv_attn_args* attn, const sv_sample_args* sampl
     return fail(SV_ERR_INVALID_ARG, "attn and sample args must describe the same batch (B, total_nodes, cu_nodes)");
   const WsLayout w = layout(attn, sample);
   if ((st = check_ws(w, ws, ws_bytes)) != SV_OK) return st;
-  if ((st = run_attn(attn, (char*)ws, w, (hipStream_t)stream)) != SV_OK) return st;
-  return run_sample(sample, (char*)ws, w, (hipStream_t)stream);
+  const sv_timing t = timing ? *timing : sv_timing{};
+  if ((st = run_attn(attn, (char*)ws, w, (hipStream_t)stream, (hipEvent_t)t.attn_start, (hipEvent_t)t.attn_stop)) !=
+      SV_OK)
+    return st;
+  return run_sample(sample, (char*)ws, w, (hipStream_t)stream,
+                    sv::SampleEvents{(hipEvent_t)t.sample_start, (hipEvent_t)t.stats_stop, (hipEvent_t)t.sample_stop});
 }
+
+sv_status spec_verify_step(const sv_attn_args* attn, const sv_sample_args* sample, void* ws, size_t ws_bytes,
+                           void* stream) {
+  return spec_verify_step_timed(attn, sample, ws, ws_bytes, stream, nullptr);
+}
+
 
 const char* spec_verify_last_error(void) { return g_err; }
 

@@ -17,7 +17,7 @@ constexpr int kMaxChunks = kMaxVocab / kChunk;
 // Per (row, vocabulary chunk) statistics written by the row-statistics pass.
 struct ChunkStat {
   float lmax;   // largest raw logit of the chunk (-inf if none finite)
-  int32_t arg;  // lowest index attaining lmax (greedy argmax)
+  int32_t arg;  // lowest index attaining lmax (greedy argmax); -1: the chunk holds a NaN or +inf
   double s;     // sum over the chunk of exp2((logit - lmax) * log2(e) / T)
 };
 static_assert(sizeof(ChunkStat) == 16, "ChunkStat layout");
@@ -25,7 +25,7 @@ static_assert(sizeof(ChunkStat) == 16, "ChunkStat layout");
 // Per-row normalisation of the target distribution, merged from the row's
 // chunk statistics: p(x) = exp2((logit - lmax) * log2(e) / T) / S.
 struct RowStat {
-  float lmax;   // largest raw logit of the row (-inf if none is finite)
+  float lmax;   // largest raw logit of the row (-inf if none is finite, or if one is NaN or +inf)
   int32_t arg;  // lowest index attaining lmax (greedy argmax)
   double S;     // sum over the row of exp2((logit - lmax) * log2(e) / T)
 };
@@ -107,6 +107,30 @@ __device__ __forceinline__ float target_prob(float logit, float lmax, float c, f
   return target_weight(logit, lmax, c) * invS;
 }
 
+// 2^y for y <= 0 in fp64, within a few fp64 ulps: with k = floor(256 y),
+// y = k / 256 + r / 256, r in [0, 1]; 2^y = 2^(k >> 8) * 2^((k & 255) / 256)
+// * 2^(r / 256), the middle factor from a table of 256 doubles (tab[j],
+// built with the fp64 exp2 of the math library), the last from its Taylor
+// polynomial in t = r ln 2 / 256 (t <= 0.0028: the first term left out is
+// below 1e-18), the first by exponent scaling. About 14 fp64 and integer
+// operations against several times that for a general fp64 exp2. 0 below
+// 2^-1074.
+constexpr int kExp2Tab = 256;
+__device__ __forceinline__ double exp2_neg_f64(double y, const double* tab) {
+  if (!(y > -1075.0)) return 0.0;
+  const double ys = y * 256.0;  // exact
+  const double kf = floor(ys);
+  const int k = (int)kf;
+  const double t = (ys - kf) * (0.69314718055994530942 / 256.0);
+  double q = 1.0 / 120.0;
+  q = fma(q, t, 1.0 / 24.0);
+  q = fma(q, t, 1.0 / 6.0);
+  q = fma(q, t, 0.5);
+  q = fma(q, t, 1.0);
+  q = fma(q, t, 1.0);
+  return ldexp(tab[k & (kExp2Tab - 1)] * q, k >> 8);  // k >> 8 = floor(k / 256), k & 255 = k mod 256
+}
+
 // Residual weight of one token, S * max(0, p - cc q), in fp32: the caller
 // passes ccS = cc * S and divides sums of these weights by S in fp64. One fma
 // and one max per token; the rounding (a few fp32 ulps of p) stays far below
@@ -115,32 +139,78 @@ __device__ __forceinline__ float residual_weight(float logit, float q, float lma
   return fmaxf(0.f, fmaf(-ccS, q, target_weight(logit, lmax, c)));
 }
 
-// Min-p truncation ([LOSSY] section 2.3): token x is in the allowed set iff
-// logit - lmax >= theta with theta = fp32(T ln p_base) -- p(x) >= p_base
-// max p written on the fp32 logit difference, the comparison every side of
-// the library (and its checker) makes identically. TR = false: no truncation.
+// Allowed set of truncation sampling ([LOSSY] section 2.3): token x is in it
+// iff l_x - l_max >= th, with th the row's threshold in fp64 (T ln p_base for
+// min-p; T (ln S + min(ln eps, ln delta - H)) for eta) -- p(x) >= p_base max p
+// (or p(x) >= tau) written on the logit difference. The difference is formed
+// in fp64 (exact for logits within a factor 2^29 of each other), but only for
+// the rare tokens whose fp32 difference falls in the guard band [lo, hi): an
+// fp32 difference d at or above hi implies the exact one is >= th, and one
+// below lo implies it is < th (lo and hi are th -/+ 2^-20 |th| rounded
+// outward to fp32, wider than the 2^-24 relative rounding of d). So the
+// set is the definition's, decided exactly.
+struct RowThr {
+  double th;  // threshold on l_x - l_max
+  float lo;   // fp32 guard band: d >= hi is in, d < lo is out
+  float hi;
+};
+static_assert(sizeof(RowThr) == 16, "RowThr layout");
+
+__host__ __device__ inline RowThr make_row_thr(double th) {
+  RowThr t;
+  t.th = th;
+  const double g = ldexp(fabs(th), -20);
+  float hi = (float)(th + g), lo = (float)(th - g);
+  if ((double)hi < th + g) hi = nextafterf(hi, INFINITY);
+  if ((double)lo > th - g) lo = nextafterf(lo, -INFINITY);
+  t.lo = lo;
+  t.hi = hi;
+  return t;
+}
+
+// w if x is allowed (or TR is false: no truncation), else 0
 template <bool TR>
-__device__ __forceinline__ float allowed(float w, float logit, float lmax, float theta) {
-  return (!TR || logit - lmax >= theta) ? w : 0.f;
+__device__ __forceinline__ float allowed(float w, float logit, float lmax, const RowThr& t) {
+  if (!TR) return w;
+  const float d = logit - lmax;
+  bool in = d >= t.hi;
+  if (!in && d >= t.lo) in = (double)logit - (double)lmax >= t.th;
+  return in ? w : 0.f;
+}
+template <bool TR>
+__device__ __forceinline__ bool is_allowed(float logit, float lmax, const RowThr& t) {
+  return allowed<TR>(1.f, logit, lmax, t) != 0.f;
 }
 
 // Row normalisation from its chunk statistics, computed by one full wave
 // (every lane returns the same values): lmax = max over chunks,
 // S = sum_ch s_ch * exp2((lmax_ch - lmax) * c) in fp64, summed lane-strided
-// then by butterfly, so every caller gets bitwise the same S.
+// then by butterfly, so every caller gets bitwise the same S. A row with a
+// NaN or +inf logit (a chunk whose arg is kBadChunk) has no distribution:
+// it gets lmax = -inf, like a row whose logits are all -inf.
+constexpr int32_t kBadChunk = -1;
 __device__ __forceinline__ void row_norm(const ChunkStat* st, int nch, float c, float& lmax, double& S,
                                          int& arg, float& argval) {
   const int lane = threadIdx.x & (kWave - 1);
   float m = -INFINITY;
   float av = -INFINITY;
   int ai = 0x7fffffff;
+  bool bad = false;
   for (int ch = lane; ch < nch; ch += kWave) {
     const ChunkStat s = st[ch];
+    bad |= s.arg == kBadChunk;
     m = fmaxf(m, s.lmax);
     if (s.lmax > av || (s.lmax == av && s.arg < ai)) { av = s.lmax; ai = s.arg; }
   }
   m = wave_max(m);
   wave_argmax(av, ai);
+  if (__any(bad)) {
+    lmax = -INFINITY;
+    S = 0.0;
+    arg = kBadChunk;
+    argval = -INFINITY;
+    return;
+  }
   double acc = 0.0;
   if (m != -INFINITY) {
     for (int ch = lane; ch < nch; ch += kWave) {

@@ -6,10 +6,9 @@
 #include <stddef.h>
 #include <stdint.h>
 
-namespace sv {
+#include "sv_device.h"
 
-struct ChunkStat;
-struct RowStat;
+namespace sv {
 
 // ---- attention ---------------------------------------------------------------
 struct AttnParams {
@@ -76,13 +75,14 @@ struct SampleParams {
   const float* logits;      // [N+B, V]
   const float* q;           // [N+B, V] (unused when greedy)
   float c;                  // log2(e) / temperature (0 when greedy)
+  double c64;               // the same in fp64 (the eta set's fp64 sums)
   bool greedy;
   bool trunc;               // truncation of the target rows (min-p or eta)
   bool eta;                 // the eta allowed set (else min-p)
-  float theta;              // min-p threshold on logit - row max: fp32(T ln min_p)
+  RowThr mp_thr;            // min-p threshold on logit - row max: T ln min_p in fp64
   double temp, ln_eps, ln_delta; // eta: temperature, ln eps, ln delta
-  double* ent;              // [N+B, nch] eta: per-chunk sum of w * log2-exponent
-  float* rtheta;            // [N+B] per-row threshold of the allowed set (trunc)
+  double2* ent;             // [N+B, nch] eta: per-chunk fp64 sums of w and of w * log2-exponent
+  RowThr* rthr;             // [N+B] per-row threshold of the allowed set (trunc)
   bool det;                 // siblings are deterministic candidates (q unused)
   int32_t rule;             // accept test: 0 lossless, 1 lenience, 2 interpolation, 3 truncation
   float rule_param;         // l or lambda of the rule
@@ -101,7 +101,8 @@ struct SampleParams {
   int32_t slices;           // workgroups per request in the walk (1: no exchange)
   double* xs;               // [B, 2, 2 nch] workspace when slices > 1
   int32_t* xcnt;            // [B, kWalkSync] workspace when slices > 1 (zeroed by the sampler)
-  uint32_t join_ticks;      // start-up window of a request's slices (100 MHz ticks)
+  uint32_t join_ticks;      // start-up window of a request's slices (100 MHz ticks; 0: none, the
+                            // first slice to look walks its request alone)
 };
 
 // per-request words of the walk's slice coordination: pass-barrier arrivals,
@@ -111,13 +112,23 @@ constexpr int kWalkSync = 4;
 // compute units of the current device (cached per device; 256 if unknown)
 int device_cus();
 
-// workgroups per request for the walk: several (256 threads each) when the
-// walk makes vocabulary passes (passes) and the batch leaves at least four
-// workgroup slots per request, else 1
-int walk_slices(int B, int nch, bool passes);
+// walk layouts (sv_sample_args.walk_mode)
+constexpr int kWalkAuto = 0, kWalkSingle = 1, kWalkSliced = 2;
+constexpr uint32_t kJoinWindow = 2000;  // default start-up window of a request's slices, 100 MHz ticks (20 us)
 
-hipError_t launch_sampler(const SampleParams& p, bool vec4, hipStream_t stream, hipEvent_t ev_start,
-                          hipEvent_t ev_stop);
+// workgroups per request for the walk: 1 without vocabulary passes (passes)
+// or in the single layout; min(8, work) "slices" of 256 threads in the sliced
+// layout; automatically, slices when the batch leaves at least four
+// workgroup slots per request on the current device, else 1
+int walk_slices(int B, int nch, bool passes, int mode);
+
+// optional timing events of the sampler (recorded on its stream when set)
+struct SampleEvents {
+  hipEvent_t start;       // before the row-statistics kernel
+  hipEvent_t stats_stop;  // after it
+  hipEvent_t stop;        // after the walk
+};
+hipError_t launch_sampler(const SampleParams& p, bool vec4, hipStream_t stream, const SampleEvents& ev);
 
 // ---- budgeted super-tree packing ------------------------------------------------
 constexpr int kPackMaxB = 8192;  // requests per packing call (one workgroup's LDS scan)

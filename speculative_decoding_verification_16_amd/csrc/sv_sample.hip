@@ -28,9 +28,6 @@
 // max(0, p - (c_k + M(c_k)) q) / M(c_k), whose mass is M(c_{k+1}) / M(c_k).)
 // So each level costs exactly one pass that evaluates M at the new c, and
 // the same pass yields the per-chunk masses the inverse CDF needs.
-#include <stdlib.h>
-#include <string.h>
-
 #include "sv_device.h"
 #include "sv_internal.h"
 
@@ -41,14 +38,25 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // ---------------------------------------------------------------------------
 // Pass 1: per (row, chunk) statistics. One wave per chunk of 4096 logits; a
 // lane holds 64 of them in registers, so the row is read from HBM once.
-// ENT also sums w * y per chunk (y = (logit - max) * c, w = exp2(y)): with the
-// chunk sums it gives the row's entropy, which the eta allowed set needs.
+// ENT (the eta allowed set) also sums, per chunk and in fp64 with fp64
+// weights, w64 = 2^y and w64 * y, y = (logit - max) * log2(e)/T formed in
+// fp64: the row's entropy and the threshold come from these, within a few
+// fp64 roundings of their exact values, so that the set is decided as its
+// definition says (the fp32 weights of the sums for p would put the
+// threshold up to ~1e-5 T off on flat rows).
 template <bool GREEDY, bool VEC, bool ENT = false>
 __global__ __launch_bounds__(256) void row_stats_kernel(const float* __restrict__ logits, int V, int64_t rows,
                                                         int nch, float c, ChunkStat* __restrict__ stats,
-                                                        int32_t* status, double* __restrict__ ent = nullptr) {
+                                                        int32_t* status, double2* __restrict__ ent = nullptr,
+                                                        double c64 = 0.0) {
   const int lane = threadIdx.x & 63;
   const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  __shared__ double tab[ENT ? kExp2Tab : 1];  // 2^(j/256) for exp2_neg_f64
+  if (ENT) {
+    static_assert(kExp2Tab == 256, "one table entry per thread of the 256-thread workgroup");
+    tab[threadIdx.x] = exp2((double)threadIdx.x / 256.0);
+    __syncthreads();  // before any thread leaves
+  }
   if (item >= rows * nch) return;
   const int64_t row = item / nch;
   const int ch = (int)(item - row * nch);
@@ -89,36 +97,46 @@ __global__ __launch_bounds__(256) void row_stats_kernel(const float* __restrict_
       ai = VEC ? begin + 4 * (lane + 64 * (i >> 2)) + (i & 3) : begin + lane + 64 * i;
     }
   }
-  if (__any(bad) && lane == 0) flag(status, kStNonFinite);
+  const bool any_bad = __any(bad);
+  if (any_bad && lane == 0) flag(status, kStNonFinite);
   wave_argmax(mx, ai);
-  double s = 0.0, e = 0.0;
+  double s = 0.0, s64 = 0.0, e64 = 0.0;
   if (!GREEDY && mx != -INFINITY) {
 #pragma unroll
     for (int i = 0; i < 64; ++i) {
       const float w = target_weight(x[i], mx, c);
       s += (double)w;
-      if (ENT) e += w > 0.f ? (double)(w * ((x[i] - mx) * c)) : 0.0;
+      if (ENT && x[i] != -INFINITY) {
+        const double y = ((double)x[i] - (double)mx) * c64;
+        const double w64 = exp2_neg_f64(y, tab);
+        s64 += w64;
+        e64 += w64 * y;
+      }
     }
     s = wave_sum(s);
-    if (ENT) e = wave_sum(e);
+    if (ENT) {
+      s64 = wave_sum(s64);
+      e64 = wave_sum(e64);
+    }
   }
   if (lane == 0) {
     ChunkStat st;
     st.lmax = mx;
-    st.arg = mx == -INFINITY ? begin : ai;
+    st.arg = any_bad ? kBadChunk : (mx == -INFINITY ? begin : ai);
     st.s = s;
     stats[item] = st;
-    if (ENT) ent[item] = e;
+    if (ENT) ent[item] = make_double2(s64, e64);
   }
 }
 
 // Pass 2: per-row normalisation merged from the chunk statistics (one wave
 // per row), so that the walk and the p-row output read 16 bytes per row.
 // It also clears the walk's per-request coordination words (xcnt, nsync entries).
-// Under truncation it also writes the row's threshold on logit - row max:
-// min-p's constant, or for the eta set T (ln S + min(ln eps, ln delta - H))
-// with the entropy H = ln S - E / S, E = sum_x w_x z_x (z in nats relative to
-// the row maximum) merged from the chunk accumulators like S.
+// Under truncation it also writes the row's threshold on logit - row max (in
+// fp64, with its fp32 guard band): min-p's constant, or for the eta set
+// T (ln S + min(ln eps, ln delta - H)) with the entropy H = ln S - E / S,
+// E = sum_x w_x z_x (z in nats relative to the row maximum) merged from the
+// chunk accumulators like S.
 __global__ __launch_bounds__(256) void row_finalize_kernel(SampleParams p, int64_t rows, int nsync) {
   const int lane = threadIdx.x & 63;
   const int nch = p.nch;
@@ -131,22 +149,26 @@ __global__ __launch_bounds__(256) void row_finalize_kernel(SampleParams p, int64
   double S;
   int arg;
   row_norm(st, nch, p.c, lmax, S, arg, av);
-  float th = p.theta;
-  if (p.eta) {
-    double acc = 0.0;
-    if (lmax != -INFINITY) {
-      for (int ch = lane; ch < nch; ch += kWave) {
-        const ChunkStat cs = st[ch];
-        if (cs.lmax != -INFINITY) {
-          const double dl = (double)(cs.lmax - lmax) * (double)p.c;  // chunk max relative to the row's, log2 units
-          acc += exp2(dl) * (p.ent[row * nch + ch] + dl * cs.s);
-        }
+  RowThr thr = p.mp_thr;
+  if (p.eta && lmax != -INFINITY) {
+    // the row's S and E = sum_x w_x y_x (y in log2 units relative to the row
+    // maximum) from the chunks' fp64 sums, all in fp64
+    double accS = 0.0, accE = 0.0;
+    for (int ch = lane; ch < nch; ch += kWave) {
+      const ChunkStat cs = st[ch];
+      if (cs.lmax != -INFINITY) {
+        const double dl = ((double)cs.lmax - (double)lmax) * p.c64;  // chunk max relative to the row's
+        const double2 se = p.ent[row * nch + ch];
+        const double sc = exp2(dl);
+        accS += sc * se.x;
+        accE += sc * (se.y + dl * se.x);
       }
     }
-    const double E = wave_sum(acc) * 0.69314718055994530942;  // log2 units -> nats
-    const double lnS = log(S);
-    const double H = lnS - E / S;
-    th = (float)(p.temp * (lnS + fmin(p.ln_eps, p.ln_delta - H)));
+    const double S64 = wave_sum(accS);
+    const double E = wave_sum(accE) * 0.69314718055994530942;  // log2 units -> nats
+    const double lnS = log(S64);
+    const double H = lnS - E / S64;
+    thr = make_row_thr(p.temp * (lnS + fmin(p.ln_eps, p.ln_delta - H)));
   }
   if (lane == 0) {
     RowStat r;
@@ -154,7 +176,7 @@ __global__ __launch_bounds__(256) void row_finalize_kernel(SampleParams p, int64
     r.arg = arg;
     r.S = S;
     p.rowstats[row] = r;
-    if (p.trunc) p.rtheta[row] = th;
+    if (p.trunc) p.rthr[row] = thr;
   }
 }
 
@@ -187,7 +209,6 @@ __global__ __launch_bounds__(256) void probs_kernel(const float* __restrict__ lo
 
 constexpr int kHalf = kChunk / 2;      // vocabulary unit of one wave in a residual pass
 constexpr int kSpinLimit = 1 << 16;    // polls of a slice barrier before it gives up (flagged)
-constexpr uint32_t kJoinWindow = 2000; // default start-up window of a request's slices, 100 MHz ticks (20 us)
 
 // A request is served by S workgroups of NT threads: S = 1 with NT = 512, or
 // S > 1 "slices" with NT = 256. Every slice gathers the same inputs and takes
@@ -214,7 +235,7 @@ struct WalkShared {
   float qx[kMaxNodes];        // draft probability of node j's token at its parent's row
   double wx[kMaxNodes];       // deterministic siblings: unnormalised target mass of node j's token
   RowStat rs[kMaxNodes + 1];  // the request's rows: r = 0 root, r = 1 + j after node j
-  float th[kMaxNodes + 1];    // their thresholds of the allowed set (truncation)
+  RowThr th[kMaxNodes + 1];   // their thresholds of the allowed set (truncation)
   double csum[kMaxChunks];    // chunk masses of the distribution being drawn from
   double hsum[2 * kMaxChunks];// half-chunk masses of a residual pass
   double wtot[NW];            // per-wave sums of the draw's scan
@@ -260,7 +281,7 @@ __device__ __forceinline__ void half_load(HalfRegs& r, __amdgpu_buffer_rsrc_t lr
 // needs it).
 template <bool MASK, bool TR>
 __device__ __forceinline__ double half_reduce(const HalfRegs& r, int V, int h, int lane, float lw, float lmax, float c,
-                                              float ccS, float theta) {
+                                              float ccS, const RowThr& theta) {
   const int n4 = V >> 2;
   const int b4 = h * (kHalf / 4) + lane;
   double acc = 0.0;
@@ -287,7 +308,7 @@ __device__ __forceinline__ double half_reduce(const HalfRegs& r, int V, int h, i
 
 template <bool VEC, bool TR>
 __device__ __forceinline__ double half_mass(const HalfRegs& r, int V, int h, int lane, float lw, float lmax, float c,
-                                            float ccS, float theta) {
+                                            float ccS, const RowThr& theta) {
   // wave-uniform test: is the whole half-chunk inside the row?
   return (h + 1) * kHalf <= V ? half_reduce<false, TR>(r, V, h, lane, lw, lmax, c, ccS, theta)
                               : half_reduce<true, TR>(r, V, h, lane, lw, lmax, c, ccS, theta);
@@ -295,7 +316,7 @@ __device__ __forceinline__ double half_mass(const HalfRegs& r, int V, int h, int
 
 template <bool TR>
 __device__ __forceinline__ double half_scalar(const float* lrow, const float* qrow, int V, int h, float lw, float lmax,
-                                              float c, float ccS, float theta, int lane) {
+                                              float c, float ccS, const RowThr& theta, int lane) {
   const int begin = h * kHalf, end = min(V, begin + kHalf);
   float lv[32], qv[32];
 #pragma unroll
@@ -320,7 +341,8 @@ __device__ __forceinline__ double half_scalar(const float* lrow, const float* qr
 // membership in the allowed set is always decided against lmax.
 template <bool VEC, int NT, bool TR>
 __device__ __forceinline__ double residual_pass(WalkShared<NT>& sh, const float* lrow, const float* qrow, int V, int nch,
-                                                float lw, float lmax, float c, float theta, double S, double cc,
+                                                float lw, float lmax, float c, const RowThr& theta, double S,
+                                                double cc,
                                                 const Slices& sl, int pass_no) {
   constexpr int NW = NT / kWave;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -416,7 +438,8 @@ __device__ __forceinline__ double residual_pass(WalkShared<NT>& sh, const float*
 // siblings already tried); their weights count as zero.
 template <bool VEC, int NT, bool TR>
 __device__ __forceinline__ int draw_token(WalkShared<NT>& sh, const float* lrow, const float* qrow, int V, int nch,
-                                          int level, float lw, float lmax, float c, float theta, double S, double cc,
+                                          int level, float lw, float lmax, float c, const RowThr& theta, double S,
+                                          double cc,
                                           double u, double total, uint64_t removed) {
   constexpr int NW = NT / kWave;
   constexpr int kDrawPerLane = kChunk / NT;
@@ -617,7 +640,7 @@ __global__ __launch_bounds__(NT) void walk_kernel(SampleParams p) {
       const RowStat rs = p.rowstats[r];
       double wx;
       if (TR) {
-        wx = (double)allowed<TR>(target_weight(lx, rs.lmax, p.c), lx, rs.lmax, p.rtheta[r]);
+        wx = (double)allowed<TR>(target_weight(lx, rs.lmax, p.c), lx, rs.lmax, p.rthr[r]);
       } else {
         const ChunkStat cs = p.stats[r * p.nch + sh.tok[tid] / kChunk];
         wx = cs.lmax == -INFINITY ? 0.0
@@ -629,7 +652,7 @@ __global__ __launch_bounds__(NT) void walk_kernel(SampleParams p) {
   }
   if (tid <= T) {
     sh.rs[tid] = p.rowstats[row0 + tid];
-    sh.th[tid] = TR ? p.rtheta[row0 + tid] : -INFINITY;
+    if (TR) sh.th[tid] = p.rthr[row0 + tid];
   }
   // the mode: sliced, or this slice alone, or another slice alone (leave)
   Slices sl{1, 0, nullptr, nullptr, p.status};
@@ -679,7 +702,7 @@ __global__ __launch_bounds__(NT) void walk_kernel(SampleParams p) {
     const float* lrow = p.logits + row * V;
     const float* qrow = (p.greedy || !p.q) ? nullptr : p.q + row * V;
     const RowStat st = sh.rs[r];
-    const float th = sh.th[r];  // this row's threshold of the allowed set (TR)
+    const RowThr th = TR ? sh.th[r] : RowThr{};  // this row's threshold of the allowed set
     // children of pos in increasing index: the same ballot in every wave
     const uint64_t kids = __ballot(lane < T && sh.par[lane] == pos);
     if (st.lmax == -INFINITY) {  // no finite logit: p is undefined here, stop without a token
@@ -711,7 +734,7 @@ __global__ __launch_bounds__(NT) void walk_kernel(SampleParams p) {
       int accepted = -1;
       for (uint64_t k = kids; k; k &= k - 1) {
         const int ch = __ffsll((unsigned long long)k) - 1;
-        if (sh.lgx[ch] - st.lmax >= th) { accepted = ch; break; }
+        if (is_allowed<TR>(sh.lgx[ch], st.lmax, th)) { accepted = ch; break; }
         ++passes;  // rejections
       }
       accepted = __builtin_amdgcn_readfirstlane(accepted);
@@ -889,28 +912,27 @@ __global__ __launch_bounds__(NT) void walk_kernel(SampleParams p) {
 }
 
 // ---------------------------------------------------------------------------
-hipError_t launch_sampler(const SampleParams& p, bool vec4, hipStream_t stream, hipEvent_t ev_start,
-                          hipEvent_t ev_stop) {
+hipError_t launch_sampler(const SampleParams& p, bool vec4, hipStream_t stream, const SampleEvents& ev) {
   if (p.B <= 0) return hipSuccess;
   const int64_t rows = (int64_t)p.N + p.B;
   const int64_t items = rows * p.nch;
   const dim3 sgrid((unsigned)((items + 3) / 4));
-  if (ev_start) (void)hipEventRecord(ev_start, stream);
+  if (ev.start) (void)hipEventRecord(ev.start, stream);
   if (p.greedy) {
     if (vec4) row_stats_kernel<true, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, p.status);
     else row_stats_kernel<true, false><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, p.status);
   } else if (p.eta) {
     if (vec4)
       row_stats_kernel<false, true, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, p.status,
-                                                                    p.ent);
+                                                                    p.ent, p.c64);
     else
       row_stats_kernel<false, false, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats,
-                                                                     p.status, p.ent);
+                                                                     p.status, p.ent, p.c64);
   } else {
     if (vec4) row_stats_kernel<false, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, p.status);
     else row_stats_kernel<false, false><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, p.status);
   }
-  if (ev_stop) (void)hipEventRecord(ev_stop, stream);
+  if (ev.stats_stop) (void)hipEventRecord(ev.stats_stop, stream);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   row_finalize_kernel<<<dim3((unsigned)((rows + 3) / 4)), 256, 0, stream>>>(p, rows, p.B * kWalkSync);
@@ -922,19 +944,13 @@ hipError_t launch_sampler(const SampleParams& p, bool vec4, hipStream_t stream, 
     if (err != hipSuccess) return err;
   }
   if (p.slices > 1) {
-    // SV_WALK_JOIN_TICKS overrides the start-up window; 0 makes the first
-    // slice to look walk its request alone, so that tests reach that path
-    const char* env = getenv("SV_WALK_JOIN_TICKS");
-    const long ticks = env ? strtol(env, nullptr, 10) : -1L;
-    SampleParams ps = p;
-    ps.join_ticks = ticks >= 0 && ticks <= 100000000L ? (uint32_t)ticks : kJoinWindow;
     const dim3 grid((unsigned)(p.B * p.slices));
     if (p.trunc) {
-      if (vec4) walk_kernel<true, 256, true><<<grid, dim3(256), 0, stream>>>(ps);
-      else walk_kernel<false, 256, true><<<grid, dim3(256), 0, stream>>>(ps);
+      if (vec4) walk_kernel<true, 256, true><<<grid, dim3(256), 0, stream>>>(p);
+      else walk_kernel<false, 256, true><<<grid, dim3(256), 0, stream>>>(p);
     } else {
-      if (vec4) walk_kernel<true, 256, false><<<grid, dim3(256), 0, stream>>>(ps);
-      else walk_kernel<false, 256, false><<<grid, dim3(256), 0, stream>>>(ps);
+      if (vec4) walk_kernel<true, 256, false><<<grid, dim3(256), 0, stream>>>(p);
+      else walk_kernel<false, 256, false><<<grid, dim3(256), 0, stream>>>(p);
     }
   } else {
     if (p.trunc) {
@@ -945,6 +961,7 @@ hipError_t launch_sampler(const SampleParams& p, bool vec4, hipStream_t stream, 
       else walk_kernel<false, 512, false><<<dim3(p.B), dim3(512), 0, stream>>>(p);
     }
   }
+  if (ev.stop) (void)hipEventRecord(ev.stop, stream);
   return hipGetLastError();
 }
 
@@ -960,11 +977,13 @@ int device_cus() {
   return cached[dev];
 }
 
-int walk_slices(int B, int nch, bool passes) {
-  if (!passes || B <= 0) return 1;
-  // SV_WALK_MODE=single forces one workgroup per request (tests)
-  const char* mode = getenv("SV_WALK_MODE");
-  if (mode && !strcmp(mode, "single")) return 1;
+int walk_slices(int B, int nch, bool passes, int mode) {
+  if (!passes || B <= 0 || mode == kWalkSingle) return 1;
+  // every wave of the request gets at least one half-chunk; past 8 slices the
+  // wider exchange costs more than the shorter passes save (measured: 16
+  // slices were slower than 8 at batch 16 and 32, vocabulary 128256)
+  const int64_t by_work = (2 * (int64_t)nch + 3) / 4;
+  if (mode == kWalkSliced) return by_work >= 2 ? (int)(by_work < 8 ? by_work : 8) : 1;
   static int per_cu_cached[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
@@ -980,10 +999,6 @@ int walk_slices(int B, int nch, bool passes) {
     per_cu_cached[dev] = max(1, min(min(a, b), t));  // 1 when unknown: then a batch of >= CUs requests gets 1 slice
   }
   const int64_t capacity = (int64_t)per_cu_cached[dev] * device_cus();
-  // every wave of the request gets at least one half-chunk; past 8 slices the
-  // wider exchange costs more than the shorter passes save (measured: 16
-  // slices were slower than 8 at batch 16 and 32, vocabulary 128256)
-  const int64_t by_work = (2 * (int64_t)nch + 3) / 4;
   int64_t s = capacity / B;
   if (s > by_work) s = by_work;
   if (s > 8) s = 8;

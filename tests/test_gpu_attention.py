@@ -198,8 +198,10 @@ def test_attention_empty_requests_and_bad_context():
     assert int(status.item()) & 0x20
 
 
-FULL = ["c2_llama8b_chain", "c3_eagle_tree", "c5_super_tree", "c4_L32768_B1_T1", "c4_L8192_B32_T1",
-        "c4_L1024_B8_T0.5"]
+# C2, C3, C5 and every (L, B) shape of the throughput buckets (attention does
+# not depend on the temperature)
+FULL = ["c2_llama8b_chain", "c3_eagle_tree", "c5_super_tree"] + [
+    f"c4_L{L}_B{B}_T1" for L in (1024, 2048, 8192, 16384, 32768) for B in (1, 8, 32)]
 
 
 @pytest.mark.parametrize("name", FULL)

@@ -15,8 +15,8 @@ difference against T ln p_base, or against the eta threshold). Pins:
   one changes at its flagged depth for some threshold there (thresholds
   moved through p_base, or through delta when every row's eta threshold is
   T (ln delta - G));
-- the derived eta band (first-order error bound of a threshold computed from
-  fp32 weights) is of the size the analysis gives on the workload rows;
+- the derived eta band (first-order bound of two fp64 evaluations of the
+  threshold) is of the size the analysis gives on the workload rows;
 - rows without a distribution (NaN, +inf, all -inf) stop greedy and sampled
   walks alike, without a bonus token.
 """
@@ -176,24 +176,21 @@ def test_eta_band_flag_is_exact():
 
 @pytest.mark.parametrize("T", [0.5, 1.0, 2.0])
 def test_eta_derived_band_size(T):
-    """The first-order bound 2^-24 (8 + 12 G + 3 Var + 6 G^2) of the eta
-    threshold on N(0, 3^2) rows over a 128256-token vocabulary (the
-    throughput buckets' rows) lies between 1e-7 and 1e-4 log-probability
-    units. At T <= 1 the threshold lies in the sparse upper tail and no row's
-    band holds a token; at T = 2 it lies among the bulk of the logits, where
-    boundary tokens are common (they carry little mass, and a row is flagged
-    only when one of them changes a decision)."""
+    """The band of two fp64 evaluations of the eta threshold,
+    2^-53 (V + 64) (8 + 8 G + 4 Var + 4 G^2), on N(0, 3^2) rows over a
+    128256-token vocabulary (the throughput buckets' rows) lies between 1e-12
+    and 1e-7 log-probability units, and no row's band holds a token (at T = 2
+    the threshold lies among the bulk of the logits, the densest place)."""
     rng = np.random.default_rng(913 + int(4 * T))
     V, rows, hits = 128256, 6, 0
     for _ in range(rows):
         lg = (rng.standard_normal(V) * 3).astype(np.float32)
         th, G, var = oracle.eta_threshold(lg, T, float(np.float32(0.05)), float(np.float32(0.3)))
-        band = math.ldexp(8 + 12 * G + 3 * var + 6 * G * G, -24)
-        assert 1e-7 < band < 1e-4, (G, var, band)
+        band = math.ldexp((V + 64) * (8 + 8 * G + 4 * var + 4 * G * G), -53)
+        assert 1e-12 < band < 1e-7, (G, var, band)
         d = lg.astype(np.float64) - float(lg.max())
         hits += int((np.abs(d - th) <= band * T).any())
-    if T <= 1.0:
-        assert hits == 0
+    assert hits == 0
 
 
 def _nonfinite_batch():
