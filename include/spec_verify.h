@@ -357,6 +357,20 @@ typedef struct {
 sv_status spec_verify_step_timed(const sv_attn_args* attn, const sv_sample_args* sample, void* ws, size_t ws_bytes,
                                  void* stream, const sv_timing* timing);
 
+/* spec_verify_step without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Its scratch is a 64 MiB (2^26-byte)
+ * array owned by the library, one per GPU, held from the library's loading
+ * on that GPU until the process ends; its address is looked up once per
+ * device (the first call on it, with that device current). Every call on a
+ * GPU shares that GPU's array and leaves its contents behind: calls that
+ * overlap on one GPU (other streams or other host threads) race and must
+ * not be issued. Arguments whose workspace (spec_verify_workspace_size)
+ * exceeds 64 MiB are rejected with SV_ERR_UNSUPPORTED before anything is
+ * enqueued. Allocates nothing; the results are bitwise those of
+ * spec_verify_step.                                                        */
+sv_status spec_verify_step_noalloc(const sv_attn_args* attn, const sv_sample_args* sample, void* stream);
+
 /* Message of the last failed call on this thread ("" if none).             */
 const char* spec_verify_last_error(void);
 

@@ -81,6 +81,8 @@ def load_library(path: str = LIB_PATH):
     lib.spec_verify_step.restype = ctypes.c_int
     lib.spec_verify_step_timed.argtypes = [_P, _P, _P, ctypes.c_size_t, _P, _P]
     lib.spec_verify_step_timed.restype = ctypes.c_int
+    lib.spec_verify_step_noalloc.argtypes = [_P, _P, _P]
+    lib.spec_verify_step_noalloc.restype = ctypes.c_int
     lib.spec_verify_last_error.argtypes = []
     lib.spec_verify_last_error.restype = ctypes.c_char_p
     lib.spec_verify_struct_size.argtypes = [_i32]
@@ -301,6 +303,13 @@ class StepCall:
         _check(load_library().spec_verify_step_timed(ctypes.byref(self.attn.args), ctypes.byref(self.sample.args),
                                                      _ptr(self.ws), self.ws_bytes, _stream_handle(stream),
                                                      ctypes.byref(t)))
+        return self._results()
+
+    def noalloc(self, stream=None):
+        """spec_verify_step_noalloc: the same step on the library's own scratch
+        (this call's workspace is not used)."""
+        _check(load_library().spec_verify_step_noalloc(ctypes.byref(self.attn.args), ctypes.byref(self.sample.args),
+                                                       _stream_handle(stream)))
         return self._results()
 
     def _results(self):

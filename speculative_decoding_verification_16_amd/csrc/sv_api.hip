@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "spec_verify.h"
 #include "sv_device.h"
 #include "sv_internal.h"
@@ -379,6 +381,35 @@ sv_status run_sample(const sv_sample_args* s, char* ws, const WsLayout& w, hipSt
   return SV_OK;
 }
 
+// ---- library-owned scratch (spec_verify_step_noalloc) ----------------------
+// A file-scope device array stands in for the caller's workspace. Each GPU
+// holds its own copy (allocated when the code object is loaded on it, kept
+// until the process ends); host code must use the address that
+// hipGetSymbolAddress returns for the current device, never the array's
+// name, which on the host is only a stand-in symbol.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};
+
+sv_status scratch_for_current_device(char** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(SV_ERR_UNSUPPORTED, "device index %d above 63", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr || !aligned(ptr, kAlign)) return fail(SV_ERR_HIP, "scratch array has no usable device address");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = (char*)g_scratch_ptr[dev];
+  return SV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -430,6 +461,23 @@ sv_status spec_verify_step(const sv_attn_args* attn, const sv_sample_args* sampl
   return spec_verify_step_timed(attn, sample, ws, ws_bytes, stream, nullptr);
 }
 
+sv_status spec_verify_step_noalloc(const sv_attn_args* attn, const sv_sample_args* sample, void* stream) {
+  g_err[0] = 0;
+  sv_status st = check_attn(attn);
+  if (st != SV_OK) return st;
+  if ((st = check_sample(sample)) != SV_OK) return st;
+  const WsLayout w = layout(attn, sample);
+  if (w.total > kScratchBytes)
+    return fail(SV_ERR_UNSUPPORTED, "spec_verify_step_noalloc: these arguments need %zu bytes of scratch, above the "
+                                    "library's %zu (64 MiB; use spec_verify_step with a caller workspace)",
+                w.total, kScratchBytes);
+  char* ws = nullptr;
+  if ((st = scratch_for_current_device(&ws)) != SV_OK) return st;
+  // the kernels write every scratch word they later read (the walk's slice
+  // counters are cleared by the row finalisation of the same call), so the
+  // previous call's contents need no clearing
+  return spec_verify_step_timed(attn, sample, ws, kScratchBytes, stream, nullptr);
+}
 
 const char* spec_verify_last_error(void) { return g_err; }
 
