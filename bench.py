@@ -123,6 +123,8 @@ def parse_args():
     ap.add_argument("--siblings", choices=["sampled", "deterministic"], default="sampled",
                     help="sampled: draft tokens are draws from q; deterministic: the top-k of q as fixed "
                          "candidates, verified by the deterministic-candidate rule (q is not read)")
+    ap.add_argument("--walk-mode", choices=["auto", "single", "sliced"], default="auto",
+                    help="tree-walk layout (auto picks from the batch size and vocabulary)")
     ap.add_argument("--paged", type=int, default=0, metavar="BLOCK",
                     help="lay the KV caches out as a shuffled pool of BLOCK-slot blocks read through a block "
                          "table (BLOCK a multiple of 64; 0 = contiguous caches)")
@@ -445,7 +447,7 @@ def main():
                               None if det else x["draft_probs"], temperature=cfg.temperature, seed=x["seed"],
                               max_nodes=x["max_T"], residual_passes=True, min_p=args.min_p,
                               siblings=args.siblings, rule=args.rule, rule_param=args.rule_param,
-                              eta=tuple(args.eta) if args.eta else None)
+                              eta=tuple(args.eta) if args.eta else None, walk_mode=args.walk_mode)
             calls.append((a, s, sv.StepCall(a, s)))
     torch.cuda.synchronize()
 
@@ -572,6 +574,7 @@ def main():
                    **({"min_p": args.min_p} if args.min_p > 0 else {}),
                    **({"siblings": "deterministic (top-k of q)"} if det else {}),
                    **({"eta": list(args.eta)} if args.eta else {}),
+                   **({"walk_mode": args.walk_mode} if args.walk_mode != "auto" else {}),
                    **({"kv_layout": f"paged, {args.paged}-slot blocks"} if args.paged else {}),
                    **({"kv_dtype": "fp8 e4m3 (scaled)"} if args.kv_fp8 else {}),
                    **({"rule": args.rule, "rule_param": args.rule_param} if args.rule in ("lenience", "interpolation")

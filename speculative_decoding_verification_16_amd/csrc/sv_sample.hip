@@ -332,6 +332,12 @@ __device__ __forceinline__ double half_scalar(const float* lrow, const float* qr
   return wave_sum(acc);
 }
 
+// A half-chunk mass for the other slices of the request: a device-coherent
+// store (it reaches memory, not only this XCD's L2).
+__device__ __forceinline__ void publish(double* dst, double v) {
+  __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Vocabulary pass of the request's workgroups: csum[ch] = mass of chunk ch
 // under max(0, p - cc q) (its two halves added in order); returns the total
 // (bitwise the same in every thread of every slice). pass_no counts the
@@ -368,14 +374,14 @@ __device__ __forceinline__ double residual_pass(WalkShared<NT>& sh, const float*
         const double m0 = half_mass<VEC, TR>(ra, V, h, lane, lw, lmax, c, ccS, theta) * invS;
         if (lane == 0) {
           sh.hsum[h] = m0;
-          if (sl.n > 1) xb[h] = m0;
+          if (sl.n > 1) publish(xb + h, m0);
         }
         half_load(ra, lrs, qrs, h1 + GW, lane);
         if (h1 < nh) {
           const double m1 = half_mass<VEC, TR>(rb, V, h1, lane, lw, lmax, c, ccS, theta) * invS;
           if (lane == 0) {
             sh.hsum[h1] = m1;
-            if (sl.n > 1) xb[h1] = m1;
+            if (sl.n > 1) publish(xb + h1, m1);
           }
         }
       }
@@ -385,20 +391,22 @@ __device__ __forceinline__ double residual_pass(WalkShared<NT>& sh, const float*
       const double m = half_scalar<TR>(lrow, qrow, V, h, lw, lmax, c, ccS, theta, lane) * invS;
       if (lane == 0) {
         sh.hsum[h] = m;
-        if (sl.n > 1) xb[h] = m;
+        if (sl.n > 1) publish(xb + h, m);
       }
     }
   }
   if (sl.n > 1) {
     // every slice's masses are published, then read back by every slice.
-    // Each wave's stores reach the XCD's L2 before the barrier; one thread
-    // then releases them (L2 write-back) with its arrival, polls the counter
-    // with plain device-scope loads (an acquire per poll would invalidate
-    // the L2 each time), and acquires once when everyone has arrived.
+    // The masses go to memory with device-coherent stores (past the XCD's
+    // non-coherent L2, no write-back of the whole L2 as a release fence
+    // would do) and come back with device-coherent loads (no invalidation of
+    // the L2 either); the wait before the arrival makes sure this wave's
+    // stores have completed, so a slice that sees every arrival reads every
+    // slice's masses.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0) {
-      __hip_atomic_fetch_add(sl.cnt, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_add(sl.cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const int target = sl.n * pass_no;
       for (int spin = 0; __hip_atomic_load(sl.cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target; ++spin) {
         if (spin >= kSpinLimit) {  // cannot happen while all slices are resident; never wait forever
@@ -407,10 +415,10 @@ __device__ __forceinline__ double residual_pass(WalkShared<NT>& sh, const float*
         }
         __builtin_amdgcn_s_sleep(1);
       }
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
     __syncthreads();
-    for (int h = threadIdx.x; h < nh; h += NT) sh.hsum[h] = xb[h];
+    for (int h = threadIdx.x; h < nh; h += NT)
+      sh.hsum[h] = __hip_atomic_load(xb + h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
   for (int ch = threadIdx.x; ch < nch; ch += NT) sh.csum[ch] = sh.hsum[2 * ch] + sh.hsum[2 * ch + 1];

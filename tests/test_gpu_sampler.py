@@ -235,6 +235,23 @@ def test_walk_modes_match(name, mode):
     compare_walk(r, _oracle(w, T, md), w["B"], greedy=False)
 
 
+@pytest.mark.parametrize("name,mode", [("c5_super_tree", "sliced"), ("c2_llama8b_chain", "single"),
+                                       ("c3_eagle_tree", "single"), ("c4_L8192_B32_T2", "single")])
+def test_walk_layouts_full_size_bitwise(name, mode):
+    """The automatic layout (one workgroup per request for the batch-256 super
+    tree, slices for the small batches) and the other layout give bitwise the
+    same walk at full size."""
+    cfg = get_config(name)
+    w = generate(cfg, "cuda", attn=False)
+    print(f"[walk-layout-full] {name} {mode} B={w['B']}", flush=True)
+    ref = _gpu_sample(w, cfg.temperature)
+    assert int(ref["status"].item()) == 0, sv.status_names(int(ref["status"].item()))
+    r = _gpu_sample(w, cfg.temperature, walk_mode=mode)
+    assert int(r["status"].item()) == 0, sv.status_names(int(r["status"].item()))
+    for k in ("accept_len", "accepted_nodes", "out_tokens", "uniforms", "residual_passes"):
+        assert torch.equal(r[k], ref[k]), k
+
+
 @pytest.mark.skip(reason=BOARD_SKIP)
 def test_walk_board_full_batch_matches_single():
     # the batch-256 super tree used the help board by default
