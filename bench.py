@@ -46,13 +46,11 @@ KERNEL_SOURCES = {
 
 def attention_kernel_name(w, cfg, kv_fp8: bool = False) -> str:
     """Which attention kernel the library's plan launches: fp32 caches take the
-    VALU kernel; bf16 takes 16x16 MFMA tiles when a KV head carries at most 64
-    query rows (Hq/Hkv heads x max_T nodes), else 32x32 tiles; fp8 caches
-    always take the 16x16 kernel."""
+    VALU kernel; bf16 queries (over bf16 or fp8 caches) take 16x16 MFMA tiles
+    when a KV head carries at most 64 query rows (Hq/Hkv heads x max_T nodes),
+    else 32x32 tiles."""
     if w["dtype"] != "bf16":
         return "attn_valu_kernel"
-    if kv_fp8:
-        return "attn_mfma_kernel"
     return "attn_mfma_kernel" if (cfg.Hq // cfg.Hkv) * w["max_T"] <= 64 else "attn_mfma32_kernel"
 
 

@@ -136,7 +136,8 @@ typedef struct {
    * above, and the value of a key (value) element is its byte's value times
    * k_scale (v_scale), both finite and > 0. E4M3 values are exact in bf16;
    * k_scale is folded into the softmax scale and v_scale into the output.
-   * Every tree runs on 64-row workgroups (row groups for wider trees).     */
+   * The kernels are those of bf16 caches (16x16 or 32x32 MFMA tiles by the
+   * rows per KV head); the bytes are widened to bf16 on their way to LDS.  */
   int32_t kv_fp8;
   float k_scale;
   float v_scale;

@@ -85,7 +85,6 @@ sv::AttnPlan plan_attn(const sv_attn_args* a) {
     // 32x32 MFMA tiles, 256-row workgroups when every KV head fits in one,
     // otherwise 128-row workgroups
     pl.rows_per_wg = rmax <= 64 ? 64 : (rmax <= 128 || rmax > 256 ? 128 : 256);
-    if (a->kv_fp8) pl.rows_per_wg = 64;  // the fp8 caches run on the 64-row (16x16 MFMA) kernel
   } else {
     pl.rows_per_wg = 8;
   }
@@ -98,7 +97,9 @@ sv::AttnPlan plan_attn(const sv_attn_args* a) {
     pl.splits = (int)(a->num_splits < max_splits_len ? a->num_splits : max_splits_len);
   } else {
     // enough workgroups for 256 CUs, but each split keeps >= 256 keys and the
-    // partial outputs it adds stay below a quarter of the KV bytes
+    // partial outputs it adds stay below half of the KV bytes (a quarter left
+    // fp8 caches, whose KV bytes are half, one split on 128 workgroups for the
+    // 60-node trees at batch 16)
     const int64_t items = (int64_t)a->B * a->Hkv * pl.n_rowgroups;
     const int64_t slots = pl.rows_per_wg > 128 ? 256 : 512;  // 8-wave workgroups: one per CU
     const int64_t want = (slots + items - 1) / (items > 0 ? items : 1);
@@ -106,7 +107,7 @@ sv::AttnPlan plan_attn(const sv_attn_args* a) {
     const int64_t esz = a->kv_fp8 ? 1 : (a->dtype == SV_BF16 ? 2 : 4);
     const int64_t kv_bytes = 2 * (int64_t)a->B * a->Hkv * a->Lcap * a->D * esz;
     const int64_t part_bytes = 2 * (int64_t)a->total_nodes * a->Hq * (a->D + 2) * 4;
-    const int64_t by_traffic = part_bytes > 0 ? kv_bytes / (4 * part_bytes) : 256;
+    const int64_t by_traffic = part_bytes > 0 ? kv_bytes / (2 * part_bytes) : 256;
     int64_t s = want;
     if (s > by_len) s = by_len;
     if (s > by_traffic) s = by_traffic;

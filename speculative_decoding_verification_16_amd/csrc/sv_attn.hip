@@ -605,7 +605,7 @@ void attn_mfma_kernel(AttnParams p) {
 // V^T operand is read in the same key order with transposed LDS reads.
 // O^T per 32-dim block db: lane l holds dims 32 db + 8 (v / 4) + 4 h + v % 4
 // of row l % 32.
-template <int D, int NW, int WPE, bool PAGED = false>
+template <int D, int NW, int WPE, bool PAGED = false, bool FP8 = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE)))
 void attn_mfma32_kernel(AttnParams p) {
   constexpr int NT = 64 * NW;        // threads
@@ -616,6 +616,7 @@ void attn_mfma32_kernel(AttnParams p) {
   constexpr int ROWS = 32 * NW;
   constexpr int PER_THREAD = KT * UNITS / NT;  // 16-byte units per thread per K or V tile
   static_assert(PER_THREAD >= 1 && KT * UNITS == PER_THREAD * NT, "tile / thread split");
+  constexpr int ESZ = FP8 ? 1 : 2;   // bytes per cache element
   // two LDS buffers each for K and V, as four arrays so that the compiler can
   // tell the buffer being filled from the one being read
   __shared__ __attribute__((aligned(16))) uint16_t Ks0[KT * D];
@@ -685,14 +686,14 @@ void attn_mfma32_kernel(AttnParams p) {
   }
 
   const int64_t head_off = PAGED ? 0 : ((int64_t)b * p.Hkv + g) * p.Lcap * D;  // paged: per tile instead
-  const uint16_t* kbase = (const uint16_t*)p.k + head_off;
-  const uint16_t* vbase = (const uint16_t*)p.v + head_off;
+  const char* kbase = (const char*)p.k + head_off * ESZ;
+  const char* vbase = (const char*)p.v + head_off * ESZ;
   // the resources cover exactly keys [0, ke): a key past the split end reads
   // as zero without touching memory, and so does a whole tile past the range
   const __amdgpu_buffer_rsrc_t krs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, ke * D * 2, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, ke * D * ESZ, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, ke * D * 2, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, ke * D * ESZ, 0x00020000);
   // Tiles go from HBM straight into LDS (16-byte buffer loads with the LDS
   // flag: lane i of a wave instruction fills the 16 bytes at the instruction's
   // LDS base + 16 i). Thread c = tid + NT i fills unit c of a tile, row
@@ -720,7 +721,7 @@ void attn_mfma32_kernel(AttnParams p) {
   auto dma = [&](__amdgpu_buffer_rsrc_t rs, const void* pool, const int* off, uint16_t* dst, int t) {
     int tb = (kb + t * KT) * D * 2;
     if (PAGED) {
-      rs = paged_tile<2>(p, pool, b, g, kb + t * KT, ke, D, pg);
+      rs = paged_tile<ESZ>(p, pool, b, g, kb + t * KT, ke, D, pg);
       tb = 0;
     }
     if (stream_once) {
@@ -733,6 +734,44 @@ void attn_mfma32_kernel(AttnParams p) {
       for (int i = 0; i < PER_THREAD; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst + 8 * (wunit + NT * i)), 16,
                                                  (unsigned)(off[i] + tb), 0, 0, 0);
+    }
+  };
+  // FP8 caches: no LDS DMA (it cannot widen). Thread c loads the eight fp8
+  // bytes of unit c of a tile (row kk = c / UNITS, head dims 8 u .. 8 u + 7,
+  // u = c % UNITS) into registers, widens them to bf16 (every E4M3 value is
+  // exact in bf16) and writes them to the LDS slot the DMA would have filled
+  // with that unit: u ^ (kk & KSWM) for K, u ^ VSW (kk & 3) for V (the XOR
+  // swizzle is its own inverse). The reads and MFMAs are those of bf16.
+  i32x2_t k8[FP8 ? PER_THREAD : 1], v8[FP8 ? PER_THREAD : 1];
+  auto fetch8 = [&](__amdgpu_buffer_rsrc_t rs, const void* pool, i32x2_t* dst, int t) {
+    int tb = (kb + t * KT) * D;
+    if (PAGED) {
+      rs = paged_tile<1>(p, pool, b, g, kb + t * KT, ke, D, pg);
+      tb = 0;
+    }
+    if (stream_once) {
+#pragma unroll
+      for (int i = 0; i < PER_THREAD; ++i) {
+        const int c = tid + NT * i;
+        dst[i] = __builtin_bit_cast(
+            i32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rs, (c / UNITS) * D + 8 * (c % UNITS), tb, kAuxNT));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < PER_THREAD; ++i) {
+        const int c = tid + NT * i;
+        dst[i] = __builtin_bit_cast(i32x2_t,
+                                    __builtin_amdgcn_raw_buffer_load_b64(rs, (c / UNITS) * D + 8 * (c % UNITS), tb, 0));
+      }
+    }
+  };
+  auto store8 = [&](const i32x2_t* src, uint16_t* lds, bool is_v) {
+#pragma unroll
+    for (int i = 0; i < PER_THREAD; ++i) {
+      const int c = tid + NT * i;
+      const int kk = c / UNITS, u = c % UNITS;
+      const int slot = is_v ? (u ^ (VSW * (kk & 3))) : (u ^ (kk & KSWM));
+      *(i32x4_t*)(lds + kk * D + 8 * slot) = widen_fp8x8(src[i]);
     }
   };
   // V^T operand addressing: lane l of 16-lane group G = l / 16 reads the head
@@ -872,12 +911,23 @@ void attn_mfma32_kernel(AttnParams p) {
   // run (the S MFMAs do not depend on the softmax, so the two can co-issue).
   const int nt = (ke - kb + KT - 1) / KT;
   f32x16_t sc[2], sn[2];
-  dma(krs, p.k, koff, Ks0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  dma(krs, p.k, koff, Ks1, 1);
-  dma(vrs, p.v, voff, Vs0, 0);
-  if (wave_any) s_tile(Ks0, sc);
+  if constexpr (FP8) {
+    fetch8(krs, p.k, k8, 0);
+    store8(k8, Ks0, false);
+    __syncthreads();
+    fetch8(krs, p.k, k8, 1);
+    fetch8(vrs, p.v, v8, 0);
+    if (wave_any) s_tile(Ks0, sc);
+    store8(k8, Ks1, false);
+    store8(v8, Vs0, true);
+  } else {
+    dma(krs, p.k, koff, Ks0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    dma(krs, p.k, koff, Ks1, 1);
+    dma(vrs, p.v, voff, Vs0, 0);
+    if (wave_any) s_tile(Ks0, sc);
+  }
   // one iteration; cur / nxt are the buffers of tiles t and t + 1 (S of the
   // tile after the last one is computed on the zeros the range check left in
   // its buffer and never used)
@@ -885,6 +935,19 @@ void attn_mfma32_kernel(AttnParams p) {
   // swap roles from one iteration to the next)
   auto step = [&](int t, uint16_t* Kcur, uint16_t* Knxt, uint16_t* Vcur, uint16_t* Vnxt, f32x16_t* scur,
                   f32x16_t* snxt) {
+    if constexpr (FP8) {
+      // K_{t+1} and V_t were written to LDS at the end of the last step; K_t
+      // and V_{t-1} are no longer read once everyone is past the barrier, so
+      // K_{t+2} and V_{t+1} go there after this step's work (their loads fly
+      // meanwhile)
+      __syncthreads();
+      fetch8(krs, p.k, k8, t + 2);
+      fetch8(vrs, p.v, v8, t + 1);
+      if (wave_any) softmax_s_pv(scur, snxt, Knxt, Vcur, t);
+      store8(k8, Kcur, false);
+      store8(v8, Vnxt, true);
+      return;
+    }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of K_{t+1} and V_t have landed
     __syncthreads();                // everyone's have; K_t and V_{t-1} are no longer read
     dma(krs, p.k, koff, Kcur, t + 2);
@@ -907,7 +970,7 @@ void attn_mfma32_kernel(AttnParams p) {
   }
   if (orow < 0) return;
   if (p.splits == 1) {
-    const float inv = 1.0f / lt;
+    const float inv = (FP8 ? p.v_scale : 1.0f) / lt;
     float* op = p.out + (int64_t)orow * D + 4 * h;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -917,12 +980,13 @@ void attn_mfma32_kernel(AttnParams p) {
                                                         o[db][4 * g8 + 2] * inv, o[db][4 * g8 + 3] * inv);
   } else {
     float* op = p.o_part + ((int64_t)split * NH + orow) * D + 4 * h;
+    const float vs = FP8 ? p.v_scale : 1.0f;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int g8 = 0; g8 < 4; ++g8)
-        *(float4*)(op + 32 * db + 8 * g8) = make_float4(o[db][4 * g8], o[db][4 * g8 + 1], o[db][4 * g8 + 2],
-                                                        o[db][4 * g8 + 3]);
+        *(float4*)(op + 32 * db + 8 * g8) = make_float4(o[db][4 * g8] * vs, o[db][4 * g8 + 1] * vs,
+                                                        o[db][4 * g8 + 2] * vs, o[db][4 * g8 + 3] * vs);
     if (h == 0) p.ml_part[(int64_t)split * NH + orow] = make_float2(m, lt);
   }
 }
@@ -1113,11 +1177,18 @@ hipError_t launch_attn_prep(const AttnParams& p, const AttnPlan& plan, const int
 // KV head's rows fit in 256, so that each slab is read by one workgroup, else
 // 4 waves (128 rows, two workgroups per CU) with row groups (measured on
 // MI355X: the 8-wave form is 6 % faster on 240-row trees, the 4-wave form
-// faster on trees of up to 272 rows whose sizes vary).
+// faster on trees of up to 272 rows whose sizes vary). FP8 caches take the
+// same kernels, the 32x32 one with its tiles staged through registers
+// (measured on MI355X: 90 us against 137 us on the 64-row kernel for the
+// 60-node trees at batch 16, 436 us against 481 us for the batch-256 super
+// tree).
 template <int D, bool PAGED>
 static void launch_mfma_d(const AttnParams& p, int rows_per_wg, dim3 grid, hipStream_t stream) {
-  if (p.kv_fp8) attn_mfma_kernel<D, 1, 4, 1, 3, PAGED, true><<<grid, dim3(256), 0, stream>>>(p);  // 64-row groups
-  else if (rows_per_wg <= 64) attn_mfma_kernel<D, 1, 4, 1, 3, PAGED><<<grid, dim3(256), 0, stream>>>(p);
+  if (p.kv_fp8) {
+    if (rows_per_wg <= 64) attn_mfma_kernel<D, 1, 4, 1, 3, PAGED, true><<<grid, dim3(256), 0, stream>>>(p);
+    else if (rows_per_wg <= 128) attn_mfma32_kernel<D, 4, 2, PAGED, true><<<grid, dim3(256), 0, stream>>>(p);
+    else attn_mfma32_kernel<D, 8, 1, PAGED, true><<<grid, dim3(512), 0, stream>>>(p);
+  } else if (rows_per_wg <= 64) attn_mfma_kernel<D, 1, 4, 1, 3, PAGED><<<grid, dim3(256), 0, stream>>>(p);
   else if (rows_per_wg <= 128) attn_mfma32_kernel<D, 4, 2, PAGED><<<grid, dim3(256), 0, stream>>>(p);
   else attn_mfma32_kernel<D, 8, 1, PAGED><<<grid, dim3(512), 0, stream>>>(p);
 }

@@ -355,7 +355,7 @@ def test_fp8_attention_matches(name, splits, paged):
     assert err <= ATTN_TOL["bf16"], err
 
 
-@pytest.mark.parametrize("name", ["c4_L32768_B8_T1", "c5_super_tree"])
+@pytest.mark.parametrize("name", ["c4_L32768_B8_T1", "c3_eagle_tree", "c5_super_tree"])
 def test_fp8_attention_full_size(name):
     cfg = get_config(name)
     w = generate(cfg, "cuda", sample=False)
