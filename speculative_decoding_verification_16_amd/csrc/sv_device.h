@@ -182,43 +182,85 @@ __device__ __forceinline__ bool is_allowed(float logit, float lmax, const RowThr
   return allowed<TR>(1.f, logit, lmax, t) != 0.f;
 }
 
-// Row normalisation from its chunk statistics, computed by one full wave
-// (every lane returns the same values): lmax = max over chunks,
-// S = sum_ch s_ch * exp2((lmax_ch - lmax) * c) in fp64, summed lane-strided
-// then by butterfly, so every caller gets bitwise the same S. A row with a
-// NaN or +inf logit (a chunk whose arg is kBadChunk) has no distribution:
-// it gets lmax = -inf, like a row whose logits are all -inf.
+// Row normalisation from its chunk statistics, computed by a group of 4
+// lanes (lanes 4 k .. 4 k + 3 of a wave, all active; every lane of the group
+// returns the same values): lmax = max over chunks,
+// S = sum_ch s_ch * exp2((lmax_ch - lmax) * c) in fp64, summed group-strided
+// then by a butterfly inside the group, so every caller gets bitwise the same
+// S. A row with a NaN or +inf logit (a chunk whose arg is kBadChunk) has no
+// distribution: it gets lmax = -inf, like a row whose logits are all -inf.
+// A wave normalises 16 rows at once, so a workgroup of 256 threads covers
+// the 65 rows of the largest request in two rounds and usually in one, each
+// lane's chunk loads independent of each other.
 constexpr int32_t kBadChunk = -1;
+constexpr int kRowGroup = 4;
+__device__ __forceinline__ bool group_any(bool v) {
+  const uint64_t bal = __ballot(v);
+  return ((bal >> ((threadIdx.x & (kWave - 1)) & ~(kRowGroup - 1))) & ((1ull << kRowGroup) - 1)) != 0;
+}
+__device__ __forceinline__ double group_sum(double v) {
+#pragma unroll
+  for (int o = kRowGroup / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+// (Up to kRowRegs chunks per lane -- 64 chunks, a vocabulary of 262144 --
+// the statistics are read once into registers; beyond, twice.)
+constexpr int kRowRegs = 16;
+__device__ __forceinline__ void row_norm_acc(const ChunkStat& s, float& m, float& av, int& ai, bool& bad) {
+  bad |= s.arg == kBadChunk;
+  m = fmaxf(m, s.lmax);
+  if (s.lmax > av || (s.lmax == av && s.arg < ai)) { av = s.lmax; ai = s.arg; }
+}
 __device__ __forceinline__ void row_norm(const ChunkStat* st, int nch, float c, float& lmax, double& S,
                                          int& arg, float& argval) {
-  const int lane = threadIdx.x & (kWave - 1);
+  const int gl = threadIdx.x & (kRowGroup - 1);
   float m = -INFINITY;
   float av = -INFINITY;
   int ai = 0x7fffffff;
   bool bad = false;
-  for (int ch = lane; ch < nch; ch += kWave) {
-    const ChunkStat s = st[ch];
-    bad |= s.arg == kBadChunk;
-    m = fmaxf(m, s.lmax);
-    if (s.lmax > av || (s.lmax == av && s.arg < ai)) { av = s.lmax; ai = s.arg; }
+  const bool in_regs = nch <= kRowRegs * kRowGroup;
+  ChunkStat cs[kRowRegs];
+  if (in_regs) {
+#pragma unroll
+    for (int k = 0; k < kRowRegs; ++k) {
+      const int ch = gl + kRowGroup * k;
+      if (ch < nch) cs[k] = st[ch];
+      else cs[k] = ChunkStat{-INFINITY, 0x7fffffff, 0.0};
+    }
+#pragma unroll
+    for (int k = 0; k < kRowRegs; ++k) row_norm_acc(cs[k], m, av, ai, bad);
+  } else {
+    for (int ch = gl; ch < nch; ch += kRowGroup) row_norm_acc(st[ch], m, av, ai, bad);
   }
-  m = wave_max(m);
-  wave_argmax(av, ai);
-  if (__any(bad)) {
+#pragma unroll
+  for (int o = kRowGroup / 2; o > 0; o >>= 1) {
+    m = fmaxf(m, __shfl_xor(m, o));
+    const float ov = __shfl_xor(av, o);
+    const int oi = __shfl_xor(ai, o);
+    if (ov > av || (ov == av && oi < ai)) { av = ov; ai = oi; }
+  }
+  if (group_any(bad)) {
     lmax = -INFINITY;
     S = 0.0;
     arg = kBadChunk;
     argval = -INFINITY;
     return;
   }
+  // the chunks in the same order on both paths: lane gl sums gl, gl + 4, ...
   double acc = 0.0;
   if (m != -INFINITY) {
-    for (int ch = lane; ch < nch; ch += kWave) {
-      const ChunkStat s = st[ch];
-      if (s.lmax != -INFINITY) acc += s.s * exp2((double)(s.lmax - m) * (double)c);
+    if (in_regs) {
+#pragma unroll
+      for (int k = 0; k < kRowRegs; ++k)
+        if (cs[k].lmax != -INFINITY) acc += cs[k].s * exp2((double)(cs[k].lmax - m) * (double)c);
+    } else {
+      for (int ch = gl; ch < nch; ch += kRowGroup) {
+        const ChunkStat s = st[ch];
+        if (s.lmax != -INFINITY) acc += s.s * exp2((double)(s.lmax - m) * (double)c);
+      }
     }
   }
-  S = wave_sum(acc);
+  S = group_sum(acc);
   lmax = m;
   arg = ai;
   argval = av;

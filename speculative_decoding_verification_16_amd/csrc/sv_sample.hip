@@ -13,9 +13,10 @@
 //     per 4096-token chunk the max logit, its first index and
 //     sum exp((logit - max)/T). That is all the walk needs to evaluate p at
 //     any token and to draw from p at a leaf.
-//  2. row_finalize_kernel -- the per-row maximum, argmax and sum, merged from
-//     the chunk statistics.
-//  3. walk_kernel       -- one workgroup per request. It climbs down the tree
+//  2. walk_kernel       -- one workgroup per request. It merges the chunk
+//     statistics of its own rows into the per-row maximum, argmax and sum
+//     (row_finalize_kernel does the same for all rows when the p rows are
+//     requested as an output), then climbs down the tree
 //     doing the accept tests on gathered p(x), q(x). A residual mass is only
 //     computed when the walk actually rejects (a vocabulary pass over that
 //     one row, logits and q), so rows that are never rejected are read once,
@@ -47,10 +48,13 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 template <bool GREEDY, bool VEC, bool ENT = false>
 __global__ __launch_bounds__(256) void row_stats_kernel(const float* __restrict__ logits, int V, int64_t rows,
                                                         int nch, float c, ChunkStat* __restrict__ stats,
-                                                        int32_t* status, double2* __restrict__ ent = nullptr,
-                                                        double c64 = 0.0) {
+                                                        int32_t* status, int32_t* xcnt, int nsync,
+                                                        double2* __restrict__ ent = nullptr, double c64 = 0.0) {
   const int lane = threadIdx.x & 63;
   const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  // the sliced walk's per-request coordination words start at zero (the
+  // grid has at least 64 threads per row, so more than nsync = 4 B)
+  if (xcnt && (int64_t)blockIdx.x * 256 + threadIdx.x < nsync) xcnt[blockIdx.x * 256 + threadIdx.x] = 0;
   __shared__ double tab[ENT ? kExp2Tab : 1];  // 2^(j/256) for exp2_neg_f64
   if (ENT) {
     static_assert(kExp2Tab == 256, "one table entry per thread of the 256-thread workgroup");
@@ -129,32 +133,28 @@ __global__ __launch_bounds__(256) void row_stats_kernel(const float* __restrict_
   }
 }
 
-// Pass 2: per-row normalisation merged from the chunk statistics (one wave
-// per row), so that the walk and the p-row output read 16 bytes per row.
-// It also clears the walk's per-request coordination words (xcnt, nsync entries).
-// Under truncation it also writes the row's threshold on logit - row max (in
-// fp64, with its fp32 guard band): min-p's constant, or for the eta set
-// T (ln S + min(ln eps, ln delta - H)) with the entropy H = ln S - E / S,
-// E = sum_x w_x z_x (z in nats relative to the row maximum) merged from the
-// chunk accumulators like S.
-__global__ __launch_bounds__(256) void row_finalize_kernel(SampleParams p, int64_t rows, int nsync) {
-  const int lane = threadIdx.x & 63;
+// Per-row normalisation merged from the chunk statistics, by one 4-lane
+// group (row_norm); under truncation also the row's threshold on
+// logit - row max (in fp64, with its fp32 guard band): min-p's constant, or
+// for the eta set T (ln S + min(ln eps, ln delta - H)) with the entropy
+// H = ln S - E / S, E = sum_x w_x z_x (z in nats relative to the row maximum)
+// merged from the chunk accumulators like S. The walk runs it for its own
+// rows; row_finalize_kernel runs it for every row when the p rows are an
+// output, so both see bitwise the same values.
+__device__ __forceinline__ void finalize_row(const SampleParams& p, int64_t row, RowStat& r, RowThr& thr) {
+  const int gl = threadIdx.x & (kRowGroup - 1);
   const int nch = p.nch;
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (p.slices > 1 && gid < nsync) p.xcnt[gid] = 0;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
   const ChunkStat* st = p.stats + row * nch;
   float lmax, av;
   double S;
   int arg;
   row_norm(st, nch, p.c, lmax, S, arg, av);
-  RowThr thr = p.mp_thr;
+  thr = p.mp_thr;
   if (p.eta && lmax != -INFINITY) {
     // the row's S and E = sum_x w_x y_x (y in log2 units relative to the row
     // maximum) from the chunks' fp64 sums, all in fp64
     double accS = 0.0, accE = 0.0;
-    for (int ch = lane; ch < nch; ch += kWave) {
+    for (int ch = gl; ch < nch; ch += kRowGroup) {
       const ChunkStat cs = st[ch];
       if (cs.lmax != -INFINITY) {
         const double dl = ((double)cs.lmax - (double)lmax) * p.c64;  // chunk max relative to the row's
@@ -164,17 +164,25 @@ __global__ __launch_bounds__(256) void row_finalize_kernel(SampleParams p, int64
         accE += sc * (se.y + dl * se.x);
       }
     }
-    const double S64 = wave_sum(accS);
-    const double E = wave_sum(accE) * 0.69314718055994530942;  // log2 units -> nats
+    const double S64 = group_sum(accS);
+    const double E = group_sum(accE) * 0.69314718055994530942;  // log2 units -> nats
     const double lnS = log(S64);
     const double H = lnS - E / S64;
     thr = make_row_thr(p.temp * (lnS + fmin(p.ln_eps, p.ln_delta - H)));
   }
-  if (lane == 0) {
-    RowStat r;
-    r.lmax = lmax;
-    r.arg = arg;
-    r.S = S;
+  r.lmax = lmax;
+  r.arg = arg;
+  r.S = S;
+}
+
+// Every row's normalisation, for the p-row output (64 rows per workgroup).
+__global__ __launch_bounds__(256) void row_finalize_kernel(SampleParams p, int64_t rows) {
+  const int64_t row = (int64_t)blockIdx.x * (256 / kRowGroup) + (threadIdx.x / kRowGroup);
+  if (row >= rows) return;  // the whole 4-lane group leaves together
+  RowStat r;
+  RowThr thr;
+  finalize_row(p, row, r, thr);
+  if ((threadIdx.x & (kRowGroup - 1)) == 0) {
     p.rowstats[row] = r;
     if (p.trunc) p.rthr[row] = thr;
   }
@@ -332,6 +340,16 @@ __device__ __forceinline__ double half_scalar(const float* lrow, const float* qr
   return wave_sum(acc);
 }
 
+// A row pointer the whole workgroup shares, in scalar registers: buffer
+// resources built from it stay uniform (a resource the compiler must treat
+// as per-lane costs a loop of scalar reads around every load).
+__device__ __forceinline__ const float* uniform_ptr(const float* ptr) {
+  const uint64_t v = (uint64_t)ptr;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const float*)(((uint64_t)hi << 32) | lo);
+}
+
 // A half-chunk mass for the other slices of the request: a device-coherent
 // store (it reaches memory, not only this XCD's L2).
 __device__ __forceinline__ void publish(double* dst, double v) {
@@ -361,11 +379,13 @@ __device__ __forceinline__ double residual_pass(WalkShared<NT>& sh, const float*
     // two half-chunks per wave in flight: the next one's loads are issued
     // before the current one is reduced (past the row's end they read zeros).
     if (gw < nh) {
-      const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc((void*)lrow, (short)0, V * 4, 0x00020000);
+      const __amdgpu_buffer_rsrc_t lrs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(lrow), (short)0, V * 4, 0x00020000);
       // cc == 0 (the min-p visit pass: mass of p itself) needs no q: an empty
       // resource makes every q load read zero without touching memory
       const __amdgpu_buffer_rsrc_t qrs =
-          __builtin_amdgcn_make_buffer_rsrc((void*)qrow, (short)0, cc == 0.0 ? 0 : V * 4, 0x00020000);
+          __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(qrow), (short)0,
+                                            __builtin_amdgcn_readfirstlane(cc == 0.0 ? 0 : V * 4), 0x00020000);
       HalfRegs ra, rb;
       half_load(ra, lrs, qrs, gw, lane);
       for (int h = gw; h < nh; h += 2 * GW) {
@@ -614,6 +634,21 @@ __global__ __launch_bounds__(NT) void walk_kernel(SampleParams p) {
     if (first && p.uniforms_out) p.uniforms_out[n0 + tid] = u;
   }
   if (first && tid == 0 && p.uniforms_out) p.uniforms_out[p.N + b] = uniform01(p.seed, rid, 0u, 1u, p.step);
+  // the normalisation of every row of the request (row r = 0 root, 1 + j after
+  // node j), one 4-lane group per row; its loads need only the packing, so
+  // they overlap those of the tree
+  // (uniform by construction; said explicitly, so that the compiler keeps the
+  // rows' buffer resources in scalar registers)
+  const int64_t row0 = (int64_t)__builtin_amdgcn_readfirstlane(n0 + b);
+  for (int r = tid / kRowGroup; r <= T; r += NT / kRowGroup) {
+    RowStat rs;
+    RowThr th;
+    finalize_row(p, row0 + r, rs, th);
+    if ((tid & (kRowGroup - 1)) == 0) {
+      sh.rs[r] = rs;
+      if (TR) sh.th[r] = th;
+    }
+  }
   __syncthreads();
   if (tid < kWave) {
     bool bad_tree = false, bad_tok = false;
@@ -632,35 +667,32 @@ __global__ __launch_bounds__(NT) void walk_kernel(SampleParams p) {
   }
 
   const int64_t V = p.V;
-  const int64_t row0 = (int64_t)n0 + b;
-  // gathers: p-logit and q of every drafted token at its parent's row, and
-  // the normalisation of every row of the request
+  // gathers: p-logit and q of every drafted token at its parent's row
   if (tid < T) {
     const int64_t r = row0 + sh.par[tid] + 1;
-    const float lx = p.logits[r * V + sh.tok[tid]];
-    sh.lgx[tid] = lx;
+    sh.lgx[tid] = p.logits[r * V + sh.tok[tid]];
     sh.qx[tid] = (p.greedy || p.det) ? 0.f : p.q[r * V + sh.tok[tid]];
-    if (p.det && !p.greedy) {
-      // the token's unnormalised target mass, in the same terms as the sum it
-      // will be taken out of: under truncation the visit pass's fp32 weight
-      // relative to the row maximum; otherwise the row statistics' weight
-      // relative to its chunk's maximum, scaled as row_norm scales chunk sums
-      const RowStat rs = p.rowstats[r];
-      double wx;
-      if (TR) {
-        wx = (double)allowed<TR>(target_weight(lx, rs.lmax, p.c), lx, rs.lmax, p.rthr[r]);
-      } else {
-        const ChunkStat cs = p.stats[r * p.nch + sh.tok[tid] / kChunk];
-        wx = cs.lmax == -INFINITY ? 0.0
-                                  : (double)target_weight(lx, cs.lmax, p.c) *
-                                        exp2((double)(cs.lmax - rs.lmax) * (double)p.c);
-      }
-      sh.wx[tid] = wx;
-    }
   }
-  if (tid <= T) {
-    sh.rs[tid] = p.rowstats[row0 + tid];
-    if (TR) sh.th[tid] = p.rthr[row0 + tid];
+  __syncthreads();
+  if (p.det && !p.greedy && tid < T) {
+    // the token's unnormalised target mass, in the same terms as the sum it
+    // will be taken out of: under truncation the visit pass's fp32 weight
+    // relative to the row maximum; otherwise the row statistics' weight
+    // relative to its chunk's maximum, scaled as row_norm scales chunk sums
+    const int pr = sh.par[tid] + 1;
+    const int64_t r = row0 + pr;
+    const float lx = sh.lgx[tid];
+    const RowStat rs = sh.rs[pr];
+    double wx;
+    if (TR) {
+      wx = (double)allowed<TR>(target_weight(lx, rs.lmax, p.c), lx, rs.lmax, sh.th[pr]);
+    } else {
+      const ChunkStat cs = p.stats[r * p.nch + sh.tok[tid] / kChunk];
+      wx = cs.lmax == -INFINITY ? 0.0
+                                : (double)target_weight(lx, cs.lmax, p.c) *
+                                      exp2((double)(cs.lmax - rs.lmax) * (double)p.c);
+    }
+    sh.wx[tid] = wx;
   }
   // the mode: sliced, or this slice alone, or another slice alone (leave)
   Slices sl{1, 0, nullptr, nullptr, p.status};
@@ -925,28 +957,30 @@ hipError_t launch_sampler(const SampleParams& p, bool vec4, hipStream_t stream, 
   const int64_t rows = (int64_t)p.N + p.B;
   const int64_t items = rows * p.nch;
   const dim3 sgrid((unsigned)((items + 3) / 4));
+  int32_t* xc = p.slices > 1 ? p.xcnt : nullptr;
+  const int ns = p.B * kWalkSync;
   if (ev.start) (void)hipEventRecord(ev.start, stream);
   if (p.greedy) {
-    if (vec4) row_stats_kernel<true, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, p.status);
-    else row_stats_kernel<true, false><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, p.status);
+    if (vec4) row_stats_kernel<true, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, p.status, xc, ns);
+    else row_stats_kernel<true, false><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, p.status, xc, ns);
   } else if (p.eta) {
     if (vec4)
       row_stats_kernel<false, true, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, p.status,
-                                                                    p.ent, p.c64);
+                                                                    xc, ns, p.ent, p.c64);
     else
       row_stats_kernel<false, false, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats,
-                                                                     p.status, p.ent, p.c64);
+                                                                     p.status, xc, ns, p.ent, p.c64);
   } else {
-    if (vec4) row_stats_kernel<false, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, p.status);
-    else row_stats_kernel<false, false><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, p.status);
+    if (vec4) row_stats_kernel<false, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, p.status, xc, ns);
+    else row_stats_kernel<false, false><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, p.status, xc, ns);
   }
   if (ev.stats_stop) (void)hipEventRecord(ev.stats_stop, stream);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  row_finalize_kernel<<<dim3((unsigned)((rows + 3) / 4)), 256, 0, stream>>>(p, rows, p.B * kWalkSync);
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
   if (p.probs_out && !p.greedy) {
+    row_finalize_kernel<<<dim3((unsigned)((rows + 63) / 64)), 256, 0, stream>>>(p, rows);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
     probs_kernel<<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.rowstats, p.probs_out);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
