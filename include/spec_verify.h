@@ -103,7 +103,7 @@ typedef struct {
   int32_t total_nodes; /* N = cu_nodes[B]                                     */
   int32_t max_nodes;   /* upper bound on every T_b, 1..64; 0 means 64         */
   int32_t Hq, Hkv, D;  /* Hq % Hkv == 0; D is 64 or 128                       */
-  sv_dtype dtype;      /* element type of q, k_cache, v_cache (SV_F32/SV_BF16) */
+  int32_t dtype;       /* sv_dtype: element type of q, k_cache, v_cache      */
   const void* q;       /* [N, Hq, D], 16-byte aligned                         */
   const void* k_cache; /* [B, Hkv, Lcap, D], 16-byte aligned                  */
   const void* v_cache; /* [B, Hkv, Lcap, D], 16-byte aligned                  */

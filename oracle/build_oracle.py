@@ -25,5 +25,30 @@ def build_oracle(verbose: bool = False) -> str:
     return out
 
 
+def clang() -> str | None:
+    """The ROCm LLVM clang (its AddressSanitizer runtime is the one the
+    sanitised library build links too), or None."""
+    for cand in ("/opt/rocm/llvm/bin/clang", shutil.which("clang")):
+        if cand and os.path.exists(cand):
+            return cand
+    return None
+
+
+def build_oracle_sanitized(out: str, verbose: bool = False) -> str:
+    """oracle.c with AddressSanitizer and UndefinedBehaviorSanitizer (CPU
+    checks of the oracle itself; same arithmetic flags as the normal build)."""
+    cc = clang()
+    if cc is None:
+        raise RuntimeError("clang not found for the sanitised oracle build")
+    src = os.path.join(_HERE, "oracle.c")
+    cmd = [cc, "-std=c11", "-O1", "-g", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer",
+           "-shared-libsan", "-o", out, src, "-lm", "-lpthread"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    return out
+
+
 if __name__ == "__main__":
     print(build_oracle(verbose=True))
