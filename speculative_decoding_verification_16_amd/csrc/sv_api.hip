@@ -280,12 +280,18 @@ sv_status hip_fail(hipError_t e, const char* what) {
   return fail(SV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// defer_merge: when set, the split-K merge is described there for the
+// caller's next launch instead of being launched (the step runs it inside
+// the row-statistics launch)
 sv_status run_attn(const sv_attn_args* a, char* ws, const WsLayout& w, hipStream_t st, hipEvent_t ev_start,
-                   hipEvent_t ev_stop) {
+                   hipEvent_t ev_stop, sv::MergeArgs* defer_merge = nullptr) {
   if (a->B == 0 || a->total_nodes == 0) return SV_OK;
   const sv::AttnPlan pl = plan_attn(a);
   const int mn = eff_max_nodes(a->max_nodes);
-  uint64_t* w_anc = a->anc_mask ? nullptr : (uint64_t*)(ws + w.anc);  // built from parent when not given
+  // masks built from parent when not given: by the prep kernel when the plan
+  // needs it anyway (a work list), else by each attention workgroup in LDS
+  const bool prep_masks = !a->anc_mask && pl.compact;
+  uint64_t* w_anc = prep_masks ? (uint64_t*)(ws + w.anc) : nullptr;
   sv::AttnParams p{};
   p.B = a->B;
   p.N = a->total_nodes;
@@ -298,6 +304,7 @@ sv_status run_attn(const sv_attn_args* a, char* ws, const WsLayout& w, hipStream
   p.ctx_len = a->ctx_len;
   p.cu_nodes = a->cu_nodes;
   p.anc = a->anc_mask ? a->anc_mask : w_anc;
+  p.parent = a->parent;
   p.q = a->q;
   p.k = a->k_cache;
   p.v = a->v_cache;
@@ -323,15 +330,16 @@ sv_status run_attn(const sv_attn_args* a, char* ws, const WsLayout& w, hipStream
   while (a->block_table && (1 << p.bs_shift) < a->block_size) ++p.bs_shift;
   hipError_t e = sv::launch_attn_prep(p, pl, a->parent, w_anc, st);
   if (e != hipSuccess) return hip_fail(e, "attention prep launch");
-  e = sv::launch_attention(p, pl, a->dtype == SV_BF16, st, ev_start, ev_stop);
+  e = sv::launch_attention(p, pl, a->dtype == SV_BF16, st, ev_start, ev_stop, defer_merge);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return SV_OK;
 }
 
 sv_status run_sample(const sv_sample_args* s, char* ws, const WsLayout& w, hipStream_t st,
-                     const sv::SampleEvents& ev) {
+                     const sv::SampleEvents& ev, const sv::MergeArgs& merge = sv::MergeArgs{}) {
   if (s->B == 0) return SV_OK;
   sv::SampleParams p{};
+  p.merge = merge;
   p.B = s->B;
   p.V = s->V;
   p.N = s->total_nodes;
@@ -450,11 +458,15 @@ sv_status spec_verify_step_timed(const sv_attn_args* attn, const sv_sample_args*
   const WsLayout w = layout(attn, sample);
   if ((st = check_ws(w, ws, ws_bytes)) != SV_OK) return st;
   const sv_timing t = timing ? *timing : sv_timing{};
-  if ((st = run_attn(attn, (char*)ws, w, (hipStream_t)stream, (hipEvent_t)t.attn_start, (hipEvent_t)t.attn_stop)) !=
-      SV_OK)
+  // the attention's split-K merge runs as extra blocks of the sampler's
+  // row-statistics launch (the sampler does not read the attention output)
+  sv::MergeArgs merge{};
+  if ((st = run_attn(attn, (char*)ws, w, (hipStream_t)stream, (hipEvent_t)t.attn_start, (hipEvent_t)t.attn_stop,
+                     &merge)) != SV_OK)
     return st;
   return run_sample(sample, (char*)ws, w, (hipStream_t)stream,
-                    sv::SampleEvents{(hipEvent_t)t.sample_start, (hipEvent_t)t.stats_stop, (hipEvent_t)t.sample_stop});
+                    sv::SampleEvents{(hipEvent_t)t.sample_start, (hipEvent_t)t.stats_stop, (hipEvent_t)t.sample_stop},
+                    merge);
 }
 
 sv_status spec_verify_step(const sv_attn_args* attn, const sv_sample_args* sample, void* ws, size_t ws_bytes,
@@ -475,8 +487,8 @@ sv_status spec_verify_step_noalloc(const sv_attn_args* attn, const sv_sample_arg
   char* ws = nullptr;
   if ((st = scratch_for_current_device(&ws)) != SV_OK) return st;
   // the kernels write every scratch word they later read (the walk's slice
-  // counters are cleared by the row finalisation of the same call), so the
-  // previous call's contents need no clearing
+  // counters are cleared by the row-statistics kernel of the same call), so
+  // the previous call's contents need no clearing
   return spec_verify_step_timed(attn, sample, ws, kScratchBytes, stream, nullptr);
 }
 

@@ -56,18 +56,15 @@ __device__ __forceinline__ float row_sum4(float v) {
 // request; lane j owns node j and climbs its parent chain with wave shuffles
 // (each step must go to a strictly smaller index, so the climb ends within j
 // steps). A chain that breaks that rule marks the node as a child of the root.
-__device__ __forceinline__ void tree_masks(const AttnParams& p, const int32_t* parent, uint64_t* anc, int b, int j) {
-  if (b == 0 && j == 0 && p.cu_nodes[p.B] != p.N) flag(p.status, kStPacking);
-  const int n0 = p.cu_nodes[b], n1 = p.cu_nodes[b + 1];
-  const int T = n1 - n0;
-  if (n0 < 0 || T < 0 || T > p.max_nodes || n1 > p.N) {
-    if (j == 0) flag(p.status, kStPacking);
-    return;
-  }
-  const int pj = j < T ? parent[n0 + j] : -1;
+// Ancestor-or-self mask of node j (lane j of the wave; all 64 lanes call it)
+// of a request of T nodes whose parents start at par; bad = a link that
+// breaks the rule (the node is then treated as a child of the root: it sees
+// the context and itself).
+__device__ __forceinline__ uint64_t climb_mask(const int32_t* par, int T, int j, bool& bad) {
+  const int pj = j < T ? par[j] : -1;
   uint64_t m = 1ull << j;
   int x = pj, prev = j;
-  bool bad = false;
+  bad = false;
   for (int step = 0; step < kMaxNodes; ++step) {
     const bool act = j < T && !bad && x != -1;
     if (!__any(act)) break;
@@ -83,13 +80,40 @@ __device__ __forceinline__ void tree_masks(const AttnParams& p, const int32_t* p
     const int nx = __shfl(pj, go ? x : 0);
     x = go ? nx : x;
   }
+  return bad ? (1ull << j) : m;
+}
+
+__device__ __forceinline__ void tree_masks(const AttnParams& p, const int32_t* parent, uint64_t* anc, int b, int j) {
+  if (b == 0 && j == 0 && p.cu_nodes[p.B] != p.N) flag(p.status, kStPacking);
+  const int n0 = p.cu_nodes[b], n1 = p.cu_nodes[b + 1];
+  const int T = n1 - n0;
+  if (n0 < 0 || T < 0 || T > p.max_nodes || n1 > p.N) {
+    if (j == 0) flag(p.status, kStPacking);
+    return;
+  }
+  bool bad;
+  const uint64_t m = climb_mask(parent + n0, T, j, bad);
   if (j < T) {
-    if (bad) {  // treated as a child of the root: sees the context and itself
-      m = 1ull << j;
-      flag(p.status, kStTree);
-    }
+    if (bad) flag(p.status, kStTree);
     anc[n0 + j] = m;
   }
+}
+
+// The masks of one request inside an attention workgroup, when no mask
+// array exists (p.anc == nullptr: the caller gave none and the plan needs
+// no work list, so no prep launch ran): wave 0 climbs the parent array into
+// LDS and the whole workgroup waits for it (every thread calls this). The
+// request's first workgroup (report) raises the flags the prep kernel would.
+__device__ __forceinline__ void masks_in_lds(const AttnParams& p, int b, int n0, int T, bool report, uint64_t* sm) {
+  if (threadIdx.x < kWave) {
+    const int j = threadIdx.x;
+    bool bad;
+    const uint64_t m = climb_mask(p.parent + n0, T, j, bad);
+    if (j < T) sm[j] = m;
+    if (report && __any(bad) && j == 0) flag(p.status, kStTree);
+    if (report && b == 0 && j == 0 && p.cu_nodes[p.B] != p.N) flag(p.status, kStPacking);
+  }
+  __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
@@ -307,6 +331,7 @@ void attn_mfma_kernel(AttnParams p) {
   static_assert(PER_THREAD >= 1 && KT * D / 8 == PER_THREAD * NT, "tile / thread split");
   __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * D];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[KT * D];
+  __shared__ uint64_t smask[kMaxNodes];  // the request's masks when no mask array exists
 
   int job, rg;
   if (!decode_block(p, blockIdx.x, job, rg)) return;
@@ -320,7 +345,11 @@ void attn_mfma_kernel(AttnParams p) {
 
   const int n0 = p.cu_nodes[b], n1 = p.cu_nodes[b + 1];
   const int T = n1 - n0;
-  if (n0 < 0 || T < 0 || T > p.max_nodes || n1 > p.N) return;  // flagged by tree prep / host
+  const bool report = rg == 0 && split == 0 && g == 0;  // the request's first workgroup
+  if (n0 < 0 || T < 0 || T > p.max_nodes || n1 > p.N) {  // flagged by tree prep, or here without it
+    if (!p.anc && report && tid == 0) flag(p.status, kStPacking);
+    return;
+  }
   const int L = p.ctx_len[b];
   if (L < 0 || (int64_t)L + T > p.Lcap) {
     if (tid == 0 && rg == 0 && split == 0 && g == 0) flag(p.status, kStCtx);
@@ -329,6 +358,7 @@ void attn_mfma_kernel(AttnParams p) {
   const int R = p.G * T;
   const int row0 = rg * ROWS;
   if (row0 >= R) return;
+  if (!p.anc) masks_in_lds(p, b, n0, T, report, smask);
   const int nkeys = L + T;
   const int kchunk = ((nkeys + p.splits - 1) / p.splits + KT - 1) / KT * KT;
   const int kb = split * kchunk;
@@ -354,7 +384,7 @@ void attn_mfma_kernel(AttnParams p) {
     if (r < R) {
       const int j = r / p.G, hh = r - j * p.G;
       orow[i] = (n0 + j) * p.Hq + g * p.G + hh;
-      amask[i] = p.anc[n0 + j];
+      amask[i] = p.anc ? p.anc[n0 + j] : smask[j];
       const uint16_t* qp = (const uint16_t*)p.q + (int64_t)orow[i] * D;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) qf[i][ks] = *(const bf16x8_t*)(qp + 32 * ks + 8 * g4);
@@ -623,6 +653,7 @@ void attn_mfma32_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks1[KT * D];
   __shared__ __attribute__((aligned(16))) uint16_t Vs0[KT * D];
   __shared__ __attribute__((aligned(16))) uint16_t Vs1[KT * D];
+  __shared__ uint64_t smask[kMaxNodes];  // the request's masks when no mask array exists
   // LDS swizzles. K: 16-byte unit u of row `key` at u ^ (key & 15) for
   // D = 128 (u ^ (key & 7) for D = 64), so the 16 keys that one 256-byte read
   // pass serves hit 16 different units. V: 16-byte unit u at u ^ VSW (key & 3).
@@ -647,7 +678,11 @@ void attn_mfma32_kernel(AttnParams p) {
 
   const int n0 = p.cu_nodes[b], n1 = p.cu_nodes[b + 1];
   const int T = n1 - n0;
-  if (n0 < 0 || T < 0 || T > p.max_nodes || n1 > p.N) return;  // flagged by tree prep / host
+  const bool report = rg == 0 && split == 0 && g == 0;  // the request's first workgroup
+  if (n0 < 0 || T < 0 || T > p.max_nodes || n1 > p.N) {  // flagged by tree prep, or here without it
+    if (!p.anc && report && tid == 0) flag(p.status, kStPacking);
+    return;
+  }
   const int L = p.ctx_len[b];
   if (L < 0 || (int64_t)L + T > p.Lcap) {
     if (tid == 0 && rg == 0 && split == 0 && g == 0) flag(p.status, kStCtx);
@@ -656,6 +691,7 @@ void attn_mfma32_kernel(AttnParams p) {
   const int R = p.G * T;
   const int row0 = rg * ROWS;
   if (row0 >= R) return;
+  if (!p.anc) masks_in_lds(p, b, n0, T, report, smask);
   const int nkeys = L + T;
   const int kchunk = ((nkeys + p.splits - 1) / p.splits + KT - 1) / KT * KT;
   const int kb = split * kchunk;
@@ -674,7 +710,7 @@ void attn_mfma32_kernel(AttnParams p) {
   if (r < R) {
     const int j = r / p.G, hh = r - j * p.G;
     orow = (n0 + j) * p.Hq + g * p.G + hh;
-    amask = p.anc[n0 + j];
+    amask = p.anc ? p.anc[n0 + j] : smask[j];
     const uint16_t* qp = (const uint16_t*)p.q + (int64_t)orow * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] = *(const bf16x8_t*)(qp + 16 * ks + 8 * h);
@@ -1003,12 +1039,17 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
   __shared__ float Vs[KT][D];
   __shared__ float Ps[RW][KT];
 
+  __shared__ uint64_t smask[kMaxNodes];  // the request's masks when no mask array exists
   const int b = blockIdx.z, g = blockIdx.y;
   const int rg = blockIdx.x / p.splits, split = blockIdx.x % p.splits;
   const int tid = threadIdx.x, rl = tid >> 5, kl = tid & 31;
   const int n0 = p.cu_nodes[b], n1 = p.cu_nodes[b + 1];
   const int T = n1 - n0;
-  if (n0 < 0 || T < 0 || T > p.max_nodes || n1 > p.N) return;
+  const bool report = blockIdx.x == 0 && g == 0;  // the request's first workgroup
+  if (n0 < 0 || T < 0 || T > p.max_nodes || n1 > p.N) {
+    if (!p.anc && report && tid == 0) flag(p.status, kStPacking);
+    return;
+  }
   const int L = p.ctx_len[b];
   if (L < 0 || (int64_t)L + T > p.Lcap) {
     if (tid == 0 && blockIdx.x == 0 && g == 0) flag(p.status, kStCtx);
@@ -1017,6 +1058,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
   const int R = p.G * T;
   const int row0 = rg * RW;
   if (row0 >= R) return;
+  if (!p.anc) masks_in_lds(p, b, n0, T, report, smask);
   const int nkeys = L + T;
   const int kchunk = ((nkeys + p.splits - 1) / p.splits + KT - 1) / KT * KT;
   const int kb = split * kchunk;
@@ -1039,7 +1081,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
   if (r < R) {
     const int j = r / p.G, hh = r - j * p.G;
     orow = (n0 + j) * p.Hq + g * p.G + hh;
-    amask = p.anc[n0 + j];
+    amask = p.anc ? p.anc[n0 + j] : smask[j];
   }
   if (kb >= ke) {
     if (orow >= 0 && kl == 0) p.ml_part[(int64_t)split * NH + orow] = make_float2(-INFINITY, 0.f);
@@ -1121,40 +1163,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
 // time: every header and partial row of a chunk is requested at once (no
 // load waits on another), then merged online in split order, rescaling the
 // running sums whenever the maximum grows.
-__global__ __launch_bounds__(256) void attn_combine_kernel(int NH, int D, int splits, const float* o_part,
-                                                           const float2* ml_part, float* out) {
-  const int lpr = D >> 2;  // lanes per row
-  const int item = blockIdx.x * (256 / lpr) + threadIdx.x / lpr;
-  const int dl = threadIdx.x % lpr;
-  if (item >= NH) return;
-  const float4* o4 = (const float4*)o_part;
-  float M = -INFINITY, den = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s0 = 0; s0 < splits; s0 += 8) {
-    float2 ml[8];
-    float4 ov[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int s = min(s0 + u, splits - 1);  // a chunk past the last split re-reads it (ignored below)
-      ml[u] = ml_part[(int64_t)s * NH + item];
-      ov[u] = o4[((int64_t)s * NH + item) * lpr + dl];
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if (s0 + u >= splits || !(ml[u].y > 0.f)) continue;  // past the end, or the split saw no key of this row
-      const float mn = fmaxf(M, ml[u].x);
-      const float a = exp2f(M - mn), w = exp2f(ml[u].x - mn);  // M = -inf at first: a = 0
-      acc.x = acc.x * a + w * ov[u].x;
-      acc.y = acc.y * a + w * ov[u].y;
-      acc.z = acc.z * a + w * ov[u].z;
-      acc.w = acc.w * a + w * ov[u].w;
-      den = den * a + w * ml[u].y;
-      M = mn;
-    }
-  }
-  const float inv = 1.0f / den;
-  ((float4*)out)[(int64_t)item * lpr + dl] = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-}
+__global__ __launch_bounds__(256) void attn_combine_kernel(MergeArgs a) { merge_split_rows(a, blockIdx.x); }
 
 // ---------------------------------------------------------------------------
 hipError_t launch_attn_prep(const AttnParams& p, const AttnPlan& plan, const int32_t* parent, uint64_t* anc,
@@ -1194,7 +1203,7 @@ static void launch_mfma_d(const AttnParams& p, int rows_per_wg, dim3 grid, hipSt
 }
 
 hipError_t launch_attention(const AttnParams& p, const AttnPlan& plan, bool bf16, hipStream_t stream,
-                            hipEvent_t ev_start, hipEvent_t ev_stop) {
+                            hipEvent_t ev_start, hipEvent_t ev_stop, MergeArgs* defer_merge) {
   if (p.B <= 0 || p.N <= 0) return hipSuccess;
   if (ev_start) (void)hipEventRecord(ev_start, stream);
   if (bf16) {
@@ -1221,11 +1230,11 @@ hipError_t launch_attention(const AttnParams& p, const AttnPlan& plan, bool bf16
   if (ev_stop) (void)hipEventRecord(ev_stop, stream);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  if (plan.splits > 1) {
-    const int NH = p.N * p.Hq;
-    const int rows_per_block = 256 / (p.D / 4);
-    attn_combine_kernel<<<dim3((NH + rows_per_block - 1) / rows_per_block), dim3(256), 0, stream>>>(
-        NH, p.D, plan.splits, p.o_part, p.ml_part, p.out);
+  const MergeArgs m = merge_args(p.N * p.Hq, p.D, plan.splits, p.o_part, p.ml_part, p.out);
+  if (defer_merge) {
+    *defer_merge = m;  // the caller's next launch merges the splits
+  } else if (m.blocks > 0) {
+    attn_combine_kernel<<<dim3((unsigned)m.blocks), dim3(256), 0, stream>>>(m);
     err = hipGetLastError();
   }
   return err;

@@ -266,4 +266,65 @@ __device__ __forceinline__ void row_norm(const ChunkStat* st, int nch, float c, 
   argval = av;
 }
 
+// ---- split-K merge -----------------------------------------------------------
+// Merge of the per-split partial attention of `item` (a packed (node, query
+// head) row): partial rows are unnormalised outputs with their running max
+// (log2 units) and sum; they are merged online in split order. lpr = D / 4
+// lanes per row, lane dl holds one float4 of it. Headers and rows of eight
+// splits are requested at once (a chunk past the last split re-reads the
+// last one and is ignored). Used by the attention's merge kernel and, inside
+// the step, by extra blocks of the row-statistics launch.
+struct MergeArgs {
+  int32_t NH, D, splits;
+  int32_t blocks;          // 256-thread blocks needed (0: nothing to merge)
+  const float* o_part;     // [splits, NH, D]
+  const float2* ml_part;   // [splits, NH]
+  float* out;              // [NH, D]
+};
+__device__ __forceinline__ void merge_split_rows(const MergeArgs& a, int block) {
+  const int lpr = a.D >> 2;  // lanes per row
+  const int item = block * (256 / lpr) + threadIdx.x / lpr;
+  const int dl = threadIdx.x % lpr;
+  if (item >= a.NH) return;
+  const float4* o4 = (const float4*)a.o_part;
+  float M = -INFINITY, den = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = 0; s0 < a.splits; s0 += 8) {
+    float2 ml[8];
+    float4 ov[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int s = min(s0 + u, a.splits - 1);
+      ml[u] = a.ml_part[(int64_t)s * a.NH + item];
+      ov[u] = o4[((int64_t)s * a.NH + item) * lpr + dl];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (s0 + u >= a.splits || !(ml[u].y > 0.f)) continue;  // past the end, or the split saw no key of this row
+      const float mn = fmaxf(M, ml[u].x);
+      const float al = exp2f(M - mn), w = exp2f(ml[u].x - mn);  // M = -inf at first: al = 0
+      acc.x = acc.x * al + w * ov[u].x;
+      acc.y = acc.y * al + w * ov[u].y;
+      acc.z = acc.z * al + w * ov[u].z;
+      acc.w = acc.w * al + w * ov[u].w;
+      den = den * al + w * ml[u].y;
+      M = mn;
+    }
+  }
+  const float inv = 1.0f / den;
+  ((float4*)a.out)[(int64_t)item * lpr + dl] = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+}
+__host__ __device__ inline MergeArgs merge_args(int NH, int D, int splits, const float* o_part, const float2* ml_part,
+                                                float* out) {
+  MergeArgs a;
+  a.NH = NH;
+  a.D = D;
+  a.splits = splits;
+  a.blocks = splits > 1 ? (NH + 256 / (D / 4) - 1) / (256 / (D / 4)) : 0;
+  a.o_part = o_part;
+  a.ml_part = ml_part;
+  a.out = out;
+  return a;
+}
+
 }  // namespace sv

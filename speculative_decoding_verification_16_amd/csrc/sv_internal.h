@@ -17,7 +17,8 @@ struct AttnParams {
   int64_t Lcap;
   const int32_t* ctx_len;
   const int32_t* cu_nodes;
-  const uint64_t* anc;     // [N] ancestor-or-self masks
+  const uint64_t* anc;     // [N] ancestor-or-self masks, or nullptr: built per workgroup from parent
+  const int32_t* parent;   // [N] parent array (when anc is nullptr)
   const void* q;           // [N, Hq, D]
   const void* k;           // [B, Hkv, Lcap, D]
   const void* v;
@@ -62,8 +63,10 @@ inline int64_t attn_grid_blocks(int64_t n_jobs, int n_rowgroups) { return (n_job
 // compacted work list (when plan.compact), in one launch before the attention
 hipError_t launch_attn_prep(const AttnParams& p, const AttnPlan& plan, const int32_t* parent, uint64_t* anc,
                             hipStream_t stream);
+// (defer_merge: the split-K merge is not launched but described there, for
+// the caller's next launch to run; nullptr: launched here)
 hipError_t launch_attention(const AttnParams& p, const AttnPlan& plan, bool bf16, hipStream_t stream,
-                            hipEvent_t ev_start, hipEvent_t ev_stop);
+                            hipEvent_t ev_start, hipEvent_t ev_stop, MergeArgs* defer_merge = nullptr);
 
 // ---- sampler -----------------------------------------------------------------
 struct SampleParams {
@@ -103,6 +106,8 @@ struct SampleParams {
   int32_t* xcnt;            // [B, kWalkSync] workspace when slices > 1 (zeroed by the sampler)
   uint32_t join_ticks;      // start-up window of a request's slices (100 MHz ticks; 0: none, the
                             // first slice to look walks its request alone)
+  MergeArgs merge;          // the step's split-K merge, run by extra blocks of the row-statistics
+                            // launch (blocks == 0: none)
 };
 
 // per-request words of the walk's slice coordination: pass-barrier arrivals,

@@ -49,7 +49,14 @@ template <bool GREEDY, bool VEC, bool ENT = false>
 __global__ __launch_bounds__(256) void row_stats_kernel(const float* __restrict__ logits, int V, int64_t rows,
                                                         int nch, float c, ChunkStat* __restrict__ stats,
                                                         int32_t* status, int32_t* xcnt, int nsync,
+                                                        MergeArgs merge, int stat_blocks,
                                                         double2* __restrict__ ent = nullptr, double c64 = 0.0) {
+  // blocks past the statistics merge the step's split-K attention partials
+  // (one launch fewer; the work is independent of the statistics)
+  if ((int)blockIdx.x >= stat_blocks) {
+    merge_split_rows(merge, (int)blockIdx.x - stat_blocks);
+    return;
+  }
   const int lane = threadIdx.x & 63;
   const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   // the sliced walk's per-request coordination words start at zero (the
@@ -956,23 +963,25 @@ hipError_t launch_sampler(const SampleParams& p, bool vec4, hipStream_t stream, 
   if (p.B <= 0) return hipSuccess;
   const int64_t rows = (int64_t)p.N + p.B;
   const int64_t items = rows * p.nch;
-  const dim3 sgrid((unsigned)((items + 3) / 4));
+  const int nsb = (int)((items + 3) / 4);  // statistics blocks; the step's merge blocks follow
+  const dim3 sgrid((unsigned)(nsb + p.merge.blocks));
+  const dim3 pgrid((unsigned)nsb);         // the p-row output (one wave per (row, chunk) as well)
   int32_t* xc = p.slices > 1 ? p.xcnt : nullptr;
   const int ns = p.B * kWalkSync;
   if (ev.start) (void)hipEventRecord(ev.start, stream);
   if (p.greedy) {
-    if (vec4) row_stats_kernel<true, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, p.status, xc, ns);
-    else row_stats_kernel<true, false><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, p.status, xc, ns);
+    if (vec4) row_stats_kernel<true, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, p.status, xc, ns, p.merge, nsb);
+    else row_stats_kernel<true, false><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, p.status, xc, ns, p.merge, nsb);
   } else if (p.eta) {
     if (vec4)
       row_stats_kernel<false, true, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, p.status,
-                                                                    xc, ns, p.ent, p.c64);
+                                                                    xc, ns, p.merge, nsb, p.ent, p.c64);
     else
       row_stats_kernel<false, false, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats,
-                                                                     p.status, xc, ns, p.ent, p.c64);
+                                                                     p.status, xc, ns, p.merge, nsb, p.ent, p.c64);
   } else {
-    if (vec4) row_stats_kernel<false, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, p.status, xc, ns);
-    else row_stats_kernel<false, false><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, p.status, xc, ns);
+    if (vec4) row_stats_kernel<false, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, p.status, xc, ns, p.merge, nsb);
+    else row_stats_kernel<false, false><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, p.status, xc, ns, p.merge, nsb);
   }
   if (ev.stats_stop) (void)hipEventRecord(ev.stats_stop, stream);
   hipError_t err = hipGetLastError();
@@ -981,7 +990,7 @@ hipError_t launch_sampler(const SampleParams& p, bool vec4, hipStream_t stream, 
     row_finalize_kernel<<<dim3((unsigned)((rows + 63) / 64)), 256, 0, stream>>>(p, rows);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    probs_kernel<<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.rowstats, p.probs_out);
+    probs_kernel<<<pgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.rowstats, p.probs_out);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
