@@ -123,6 +123,11 @@ def parse_args():
                          "candidates, verified by the deterministic-candidate rule (q is not read)")
     ap.add_argument("--walk-mode", choices=["auto", "single", "sliced"], default="auto",
                     help="tree-walk layout (auto picks from the batch size and vocabulary)")
+    ap.add_argument("--overlap", choices=["off", "on"], default="off",
+                    help="step schedule timed: off = attention, row statistics and walk in order on one stream "
+                         "(the library's default); on = the sampler on the bench stream while the attention runs "
+                         "concurrently on a second stream (SV_OVERLAP_ON). The other schedule is timed after the "
+                         "timed region and reported beside it.")
     ap.add_argument("--paged", type=int, default=0, metavar="BLOCK",
                     help="lay the KV caches out as a shuffled pool of BLOCK-slot blocks read through a block "
                          "table (BLOCK a multiple of 64; 0 = contiguous caches)")
@@ -445,7 +450,8 @@ def main():
                               None if det else x["draft_probs"], temperature=cfg.temperature, seed=x["seed"],
                               max_nodes=x["max_T"], residual_passes=True, min_p=args.min_p,
                               siblings=args.siblings, rule=args.rule, rule_param=args.rule_param,
-                              eta=tuple(args.eta) if args.eta else None, walk_mode=args.walk_mode)
+                              eta=tuple(args.eta) if args.eta else None, walk_mode=args.walk_mode,
+                              step_overlap=args.overlap)
             calls.append((a, s, sv.StepCall(a, s)))
     torch.cuda.synchronize()
 
@@ -521,6 +527,33 @@ def main():
         plain = {"ms_per_step": round(plain_elapsed / K * 1e3, 4),
                  "step_ms_p10_p50_p90": [round(ppct(0.1), 4), round(ppct(0.5), 4), round(ppct(0.9), 4)]}
 
+    # The other step schedule (SV_OVERLAP_ON when the timed region ran OFF, and
+    # back), same inputs and step count, step events only; reported beside
+    # the timed figures. Results are bitwise the same in both schedules.
+    other = "on" if args.overlap == "off" else "off"
+    for _, s_, _ in calls:
+        s_.args.step_overlap = sv.OVERLAP_MODES[other]
+    for i in range(n_sets):
+        calls[i][2](stream)
+    stream.synchronize()
+    oev = HipEvents(2 * K)
+    t2 = time.perf_counter()
+    for i in range(K):
+        oev.record(2 * i, stream)
+        calls[i % n_sets][2](stream)
+        oev.record(2 * i + 1, stream)
+    stream.synchronize()
+    torch.cuda.synchronize()
+    other_elapsed = time.perf_counter() - t2
+    oms = sorted(oev.ms(2 * i, 2 * i + 1) for i in range(K))
+    oev.close()
+    for _, s_, _ in calls:
+        s_.args.step_overlap = sv.OVERLAP_MODES[args.overlap]
+    opct = lambda f: oms[min(K - 1, int(round(f * (K - 1))))]
+    other_sched = {"ms_per_step": round(other_elapsed / K * 1e3, 4),
+                   "step_ms_p10_p50_p90": [round(opct(0.1), 4), round(opct(0.5), 4), round(opct(0.9), 4)],
+                   "value": round(w["N"] * K / other_elapsed, 1)}
+
     ms = elapsed / K * 1e3
     value = w["N"] * K / elapsed
     acc = s.accept_len.double()
@@ -554,8 +587,13 @@ def main():
         kernels["sampler(stats+finalize+walk)"] = {
             "us": smp_ms * 1e3, "alg_bytes": smp_b, "GB_s": smp_b / smp_ms / 1e6,
             "frac": smp_b / smp_ms / 1e6 / HBM_PEAK_GBS, "residual_pass_bytes": passes_mean * per_pass}
-        rest_us = ms * 1e3 - attn_ms * 1e3 - smp_ms * 1e3
-        kernels["other(prep+combine)"] = {"us": rest_us}
+        if args.overlap == "off":
+            rest_us = ms * 1e3 - attn_ms * 1e3 - smp_ms * 1e3
+            kernels["other(prep+combine)"] = {"us": rest_us}
+        else:
+            # concurrent spans: each kernel's duration includes the time it
+            # shared the device with the other stream's kernels
+            kernels["schedule"] = "attention on a second stream, concurrent with the sampler (spans overlap)"
         dom = attn_name if attn_ms >= rs_ms else "row_stats_kernel"
         dk = kernels[dom]
         # the committed counters were taken with contiguous bf16 caches
@@ -583,6 +621,7 @@ def main():
         "ms_per_step": round(ms, 4),
         "step_ms_p10_p50_p90": [round(pct(0.1), 4), round(pct(0.5), 4), round(pct(0.9), 4)],
         **({"without_kernel_events": plain} if plain else {}),
+        f"step_overlap_{other}": other_sched,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -595,6 +634,7 @@ def main():
                    **({"siblings": "deterministic (top-k of q)"} if det else {}),
                    **({"eta": list(args.eta)} if args.eta else {}),
                    **({"walk_mode": args.walk_mode} if args.walk_mode != "auto" else {}),
+                   "step_overlap": args.overlap,
                    **({"kv_layout": f"paged, {args.paged}-slot blocks"} if args.paged else {}),
                    **({"kv_dtype": "fp8 e4m3 (scaled)"} if args.kv_fp8 else {}),
                    **({"rule": args.rule, "rule_param": args.rule_param} if args.rule in ("lenience", "interpolation")

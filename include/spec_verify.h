@@ -10,7 +10,8 @@
  *   2. lossless rejection sampling over the whole vocabulary, walking the tree
  *      and emitting the accepted path plus one bonus token
  *                                                   -> spec_verify_sample
- *   3. both, back to back on one stream             -> spec_verify_step
+ *   3. both in one call (in order on one stream, or the two concurrently
+ *      on two streams: sv_sample_args.step_overlap) -> spec_verify_step
  *
  * Sources (the method is defined there; section names are given per call):
  *   [SD]   "Speculative Decoding: Accelerating Inference Speeds in Distributed
@@ -27,7 +28,9 @@
  *  - Every pointer in the argument structs is DEVICE memory owned by the
  *    caller, except where a field says otherwise. The library allocates no
  *    device memory; scratch lives in the caller's workspace (see
- *    spec_verify_workspace_size). It keeps no state between calls and is
+ *    spec_verify_workspace_size). It keeps no state between calls (apart
+ *    from handles it creates once: spec_verify_step's second stream under
+ *    SV_OVERLAP_ON, and the noalloc entry point's scratch address) and is
  *    reentrant; two calls may run concurrently on different streams if they
  *    use different workspaces and outputs.
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
@@ -274,9 +277,28 @@ typedef struct {
    * walks alone).                                                          */
   int32_t walk_mode;
   int32_t join_ticks;
+  /* Schedule of spec_verify_step (ignored by spec_verify_sample; results are
+   * bitwise the same either way):
+   *   SV_OVERLAP_OFF (0, the default): attention, then row statistics, then
+   *     the walk, all on the caller's stream;
+   *   SV_OVERLAP_ON (1): the sampler (row statistics, then the walk) on the
+   *     caller's stream while the attention (with its split-K merge) runs on
+   *     a second stream forked from the caller's at the call's start and
+   *     joined back into it at the end (the caller's stream sees the whole
+   *     step done, as with OFF). The attention leaves part of the HBM
+   *     bandwidth unused and the row statistics stream through it. Faster for
+   *     large batches (256 requests of 152K-token rows: 0.78 -> 0.74 ms per
+   *     step on one MI355X), slower for small ones (the fork and join cost a
+   *     few microseconds); each kernel then takes longer than alone, as the
+   *     two share the device. The second stream (non-blocking, default
+   *     priority) and its two events are created by the library on first use,
+   *     one set per host thread and device, and kept until the process ends.
+   * spec_verify_step_noalloc always runs the OFF schedule.                 */
+  int32_t step_overlap;
 } sv_sample_args;
 
 enum { SV_WALK_AUTO = 0, SV_WALK_SINGLE = 1, SV_WALK_SLICED = 2 };
+enum { SV_OVERLAP_OFF = 0, SV_OVERLAP_ON = 1 };
 
 /* ------------------------------------------------------------------------ */
 /* Budgeted super-tree packing ([ECHO] section 3.1, "Super-Tree View": the

@@ -26,6 +26,7 @@ SV_OK, SV_ERR_INVALID_ARG, SV_ERR_TREE, SV_ERR_UNSUPPORTED, SV_ERR_WORKSPACE, SV
 SV_F32, SV_BF16 = 0, 1
 SIBLINGS = {"sampled": 0, "deterministic": 1}  # sv_siblings
 WALK_MODES = {"auto": 0, "single": 1, "sliced": 2}  # sv_sample_args.walk_mode
+OVERLAP_MODES = {"off": 0, "on": 1}  # sv_sample_args.step_overlap
 RULES = {"lossless": 0, "lenience": 1, "interpolation": 2, "truncation": 3}  # sv_rule
 STATUS_BITS = {0x01: "TREE_INVALID", 0x02: "PACKING", 0x04: "TOKEN_RANGE", 0x08: "NONFINITE",
                0x10: "ZERO_RESIDUAL", 0x20: "CTX_RANGE", 0x40: "SYNC", 0x80: "BLOCK_RANGE"}
@@ -51,7 +52,7 @@ class SvSampleArgs(ctypes.Structure):
                 ("max_depth", _i32),
                 ("accept_len", _P), ("accepted_nodes", _P), ("out_tokens", _P), ("probs_out", _P),
                 ("uniforms_out", _P), ("residual_passes", _P), ("status", _P), ("walk_mode", _i32),
-                ("join_ticks", _i32)]
+                ("join_ticks", _i32), ("step_overlap", _i32)]
 
 
 class SvTiming(ctypes.Structure):
@@ -204,7 +205,7 @@ class SampleCall:
     def __init__(self, cu_nodes, parent, draft_tokens, target_logits, draft_probs, *, temperature, seed, step=0,
                  request_id=None, max_nodes=0, max_depth=None, probs_out=False, uniforms_out=False,
                  residual_passes=False, status=None, min_p=0.0, siblings="sampled", rule="lossless",
-                 rule_param=1.0, eta=None, walk_mode="auto", join_ticks=0):
+                 rule_param=1.0, eta=None, walk_mode="auto", join_ticks=0, step_overlap="off"):
         load_library()
         if siblings not in SIBLINGS:
             raise ValueError(f"siblings must be one of {sorted(SIBLINGS)}")
@@ -212,6 +213,8 @@ class SampleCall:
             raise ValueError(f"rule must be one of {sorted(RULES)}")
         if walk_mode not in WALK_MODES:
             raise ValueError(f"walk_mode must be one of {sorted(WALK_MODES)}")
+        if step_overlap not in OVERLAP_MODES:
+            raise ValueError(f"step_overlap must be one of {sorted(OVERLAP_MODES)}")
         dev = target_logits.device
         assert target_logits.is_cuda and target_logits.dtype == torch.float32 and target_logits.is_contiguous()
         cu = _dev_i32(cu_nodes, dev)
@@ -251,6 +254,7 @@ class SampleCall:
         s.probs_out, s.uniforms_out, s.residual_passes = _ptr(self.probs), _ptr(self.uniforms), _ptr(self.passes)
         s.status = _ptr(self.status)
         s.walk_mode, s.join_ticks = WALK_MODES[walk_mode], int(join_ticks)
+        s.step_overlap = OVERLAP_MODES[step_overlap]
         self.args = s
         lib = load_library()
         self.ws_bytes = lib.spec_verify_workspace_size(None, ctypes.byref(s))

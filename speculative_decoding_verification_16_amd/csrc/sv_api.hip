@@ -231,6 +231,8 @@ sv_status check_sample(const sv_sample_args* s) {
     return fail(SV_ERR_INVALID_ARG, "walk_mode must be SV_WALK_AUTO, SV_WALK_SINGLE or SV_WALK_SLICED");
   if (s->join_ticks < -1 || s->join_ticks > 100000000)
     return fail(SV_ERR_INVALID_ARG, "join_ticks must be in [-1, 10^8]");
+  if (s->step_overlap != SV_OVERLAP_OFF && s->step_overlap != SV_OVERLAP_ON)
+    return fail(SV_ERR_INVALID_ARG, "step_overlap must be SV_OVERLAP_OFF or SV_OVERLAP_ON");
   const int md_needed = eff_max_nodes(s->max_nodes);
   if (s->max_depth < md_needed)
     return fail(SV_ERR_INVALID_ARG, "max_depth (%d) must be >= max_nodes (%d)", s->max_depth, md_needed);
@@ -419,6 +421,74 @@ sv_status scratch_for_current_device(char** out) {
   return SV_OK;
 }
 
+// ---- the step's second stream (SV_OVERLAP_ON) --------------------------------
+// One non-blocking stream of default priority and two events (no timing) per
+// host thread and device, created on first use and kept until the process
+// ends. Per thread, so that two host threads' forks and joins never record
+// into the same event.
+struct ForkJoin {
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+thread_local ForkJoin g_fj[64];
+
+sv_status fork_join_for_current_device(ForkJoin** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(SV_ERR_UNSUPPORTED, "device index %d above 63", dev);
+  ForkJoin& f = g_fj[dev];
+  if (!f.side) {
+    hipStream_t s = nullptr;
+    if ((e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking)) != hipSuccess) return hip_fail(e, "hipStreamCreate");
+    hipEvent_t a = nullptr, b = nullptr;
+    if ((e = hipEventCreateWithFlags(&a, hipEventDisableTiming)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&b, hipEventDisableTiming)) != hipSuccess) {
+      if (a) (void)hipEventDestroy(a);
+      (void)hipStreamDestroy(s);
+      return hip_fail(e, "hipEventCreate");
+    }
+    f.side = s;
+    f.fork = a;
+    f.join = b;
+  }
+  *out = &f;
+  return SV_OK;
+}
+
+bool step_overlapped(const sv_attn_args* a, const sv_sample_args* s) {
+  return s->step_overlap == SV_OVERLAP_ON && a->B > 0 && a->total_nodes > 0 && s->B > 0;
+}
+
+sv_status run_step(const sv_attn_args* attn, const sv_sample_args* sample, char* ws, const WsLayout& w,
+                   hipStream_t stream, const sv_timing& t, bool allow_overlap) {
+  const sv::SampleEvents sev{(hipEvent_t)t.sample_start, (hipEvent_t)t.stats_stop, (hipEvent_t)t.sample_stop};
+  sv_status st;
+  if (!allow_overlap || !step_overlapped(attn, sample)) {
+    // the attention's split-K merge runs as extra blocks of the sampler's
+    // row-statistics launch (the sampler does not read the attention output)
+    sv::MergeArgs merge{};
+    if ((st = run_attn(attn, ws, w, stream, (hipEvent_t)t.attn_start, (hipEvent_t)t.attn_stop, &merge)) != SV_OK)
+      return st;
+    return run_sample(sample, ws, w, stream, sev, merge);
+  }
+  // the attention (with its own merge) on the side stream and the sampler on
+  // the caller's, both from the call's start: they share only read-only
+  // inputs and use disjoint parts of the workspace
+  ForkJoin* fj = nullptr;
+  if ((st = fork_join_for_current_device(&fj)) != SV_OK) return st;
+  hipError_t e = hipEventRecord(fj->fork, stream);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord (fork)");
+  if ((e = hipStreamWaitEvent(fj->side, fj->fork, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent (fork)");
+  st = run_attn(attn, ws, w, fj->side, (hipEvent_t)t.attn_start, (hipEvent_t)t.attn_stop);
+  if (st == SV_OK) st = run_sample(sample, ws, w, stream, sev);
+  // joined even after a failed launch, so that the caller's stream never runs
+  // ahead of work already on the side stream
+  if ((e = hipEventRecord(fj->join, fj->side)) != hipSuccess) return hip_fail(e, "hipEventRecord (join)");
+  if ((e = hipStreamWaitEvent(stream, fj->join, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent (join)");
+  return st;
+}
+
 }  // namespace
 
 extern "C" {
@@ -457,16 +527,7 @@ sv_status spec_verify_step_timed(const sv_attn_args* attn, const sv_sample_args*
     return fail(SV_ERR_INVALID_ARG, "attn and sample args must describe the same batch (B, total_nodes, cu_nodes)");
   const WsLayout w = layout(attn, sample);
   if ((st = check_ws(w, ws, ws_bytes)) != SV_OK) return st;
-  const sv_timing t = timing ? *timing : sv_timing{};
-  // the attention's split-K merge runs as extra blocks of the sampler's
-  // row-statistics launch (the sampler does not read the attention output)
-  sv::MergeArgs merge{};
-  if ((st = run_attn(attn, (char*)ws, w, (hipStream_t)stream, (hipEvent_t)t.attn_start, (hipEvent_t)t.attn_stop,
-                     &merge)) != SV_OK)
-    return st;
-  return run_sample(sample, (char*)ws, w, (hipStream_t)stream,
-                    sv::SampleEvents{(hipEvent_t)t.sample_start, (hipEvent_t)t.stats_stop, (hipEvent_t)t.sample_stop},
-                    merge);
+  return run_step(attn, sample, (char*)ws, w, (hipStream_t)stream, timing ? *timing : sv_timing{}, true);
 }
 
 sv_status spec_verify_step(const sv_attn_args* attn, const sv_sample_args* sample, void* ws, size_t ws_bytes,
@@ -488,8 +549,11 @@ sv_status spec_verify_step_noalloc(const sv_attn_args* attn, const sv_sample_arg
   if ((st = scratch_for_current_device(&ws)) != SV_OK) return st;
   // the kernels write every scratch word they later read (the walk's slice
   // counters are cleared by the row-statistics kernel of the same call), so
-  // the previous call's contents need no clearing
-  return spec_verify_step_timed(attn, sample, ws, kScratchBytes, stream, nullptr);
+  // the previous call's contents need no clearing. One stream only: the
+  // overlapped schedule's side stream would be created on first use.
+  if (attn->B != sample->B || attn->total_nodes != sample->total_nodes || attn->cu_nodes != sample->cu_nodes)
+    return fail(SV_ERR_INVALID_ARG, "attn and sample args must describe the same batch (B, total_nodes, cu_nodes)");
+  return run_step(attn, sample, ws, w, (hipStream_t)stream, sv_timing{}, false);
 }
 
 const char* spec_verify_last_error(void) { return g_err; }

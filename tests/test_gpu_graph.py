@@ -1,7 +1,9 @@
 """spec_verify_step captured in a HIP graph: every replay, with the program's
 own eager work and synchronizations between replays, gives the eager result
 bit for bit (the library launches kernels only: no allocation, copy, memset
-or synchronization inside a call)."""
+or synchronization inside a call). Under SV_OVERLAP_ON the capture forks
+into the library's second stream and joins back, and the replays match the
+eager in-order schedule."""
 import pytest
 import torch
 
@@ -11,13 +13,14 @@ from workloads import CONFIGS, generate, scaled
 pytestmark = pytest.mark.gpu
 
 
+@pytest.mark.parametrize("overlap", ["off", "on"])
 @pytest.mark.parametrize("name", ["c2_small", "c3_small", "c5_small"])
-def test_step_graph_replays_match_eager(name):
+def test_step_graph_replays_match_eager(name, overlap):
     cfg = {"c2_small": scaled(CONFIGS["c2_llama8b_chain"], B=4, L=700, V=5000),
            "c3_small": scaled(CONFIGS["c3_eagle_tree"], B=3, L=300, V=9000),
            "c5_small": scaled(CONFIGS["c5_super_tree"], B=12, K=100, L=250, V=7001)}[name]
     w = generate(cfg, "cuda")
-    print(f"[graph] {name} B={w['B']} N={w['N']}", flush=True)
+    print(f"[graph] {name} overlap={overlap} B={w['B']} N={w['N']}", flush=True)
     a = sv.AttnCall(w["q"], w["k_cache"], w["v_cache"], w["ctx_len_t"], w["cu_nodes_t"], parent=w["parent_t"],
                     max_nodes=w["max_T"])
     s = sv.SampleCall(a.keep["cu"], w["parent_t"], w["draft_tokens"], w["logits"], w["draft_probs"],
@@ -29,6 +32,7 @@ def test_step_graph_replays_match_eager(name):
     stream.synchronize()
     keys = ("attn_out", "accept_len", "accepted_nodes", "out_tokens", "residual_passes")
     eager = {k: r[k].clone() for k in keys}
+    s.args.step_overlap = sv.OVERLAP_MODES[overlap]
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
         step(stream)
