@@ -593,7 +593,9 @@ def main():
         else:
             # concurrent spans: each kernel's duration includes the time it
             # shared the device with the other stream's kernels
-            kernels["schedule"] = "attention on a second stream, concurrent with the sampler (spans overlap)"
+            kernels["schedule"] = {"concurrent": True,
+                                   "note": "attention on a second stream, concurrent with the sampler: the spans "
+                                           "overlap and each includes time shared with the other stream"}
         dom = attn_name if attn_ms >= rs_ms else "row_stats_kernel"
         dk = kernels[dom]
         # the committed counters were taken with contiguous bf16 caches
