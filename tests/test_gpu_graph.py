@@ -27,6 +27,10 @@ def test_step_graph_replays_match_eager(name, overlap):
                       temperature=cfg.temperature, seed=w["seed"], max_nodes=w["max_T"], residual_passes=True)
     step = sv.StepCall(a, s)
     stream = torch.cuda.Stream()
+    # the inputs were generated, and the calls' outputs and workspaces
+    # allocated, in the default stream's order; the allocator may have handed
+    # out blocks whose earlier default-stream users have not run yet
+    stream.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(stream):
         r = step(stream)
     stream.synchronize()

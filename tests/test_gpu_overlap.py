@@ -14,12 +14,12 @@ pytestmark = pytest.mark.gpu
 KEYS = ("attn_out", "accept_len", "accepted_nodes", "out_tokens", "residual_passes")
 
 
-def _step(w, cfg, overlap):
-    a = sv.AttnCall(w["q"], w["k_cache"], w["v_cache"], w["ctx_len_t"], w["cu_nodes_t"], parent=w["parent_t"],
-                    max_nodes=w["max_T"])
+def _step(w, cfg, overlap, k=None, v=None, attn_kw=None, sample_kw=None):
+    a = sv.AttnCall(w["q"], w["k_cache"] if k is None else k, w["v_cache"] if v is None else v, w["ctx_len_t"],
+                    w["cu_nodes_t"], parent=w["parent_t"], max_nodes=w["max_T"], **(attn_kw or {}))
     s = sv.SampleCall(a.keep["cu"], w["parent_t"], w["draft_tokens"], w["logits"], w["draft_probs"],
                       temperature=cfg.temperature, seed=w["seed"], max_nodes=w["max_T"], residual_passes=True,
-                      step_overlap=overlap)
+                      step_overlap=overlap, **(sample_kw or {}))
     return sv.StepCall(a, s)
 
 
@@ -30,6 +30,10 @@ def test_overlap_schedule_bitwise(name):
     print(f"[overlap] {name} B={w['B']} N={w['N']}", flush=True)
     off, on = _step(w, cfg, "off"), _step(w, cfg, "on")
     stream = torch.cuda.Stream()
+    # the inputs were generated, and the calls' outputs and workspaces
+    # allocated, in the default stream's order; the allocator may have handed
+    # out blocks whose earlier default-stream users have not run yet
+    stream.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(stream):
         r = off(stream)
         ref_sum = r["attn_out"].sum()
@@ -58,6 +62,10 @@ def test_noalloc_ignores_overlap():
     w = generate(cfg, "cuda")
     on = _step(w, cfg, "on")
     stream = torch.cuda.Stream()
+    # the inputs were generated, and the calls' outputs and workspaces
+    # allocated, in the default stream's order; the allocator may have handed
+    # out blocks whose earlier default-stream users have not run yet
+    stream.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(stream):
         r = on(stream)
     torch.cuda.synchronize()
@@ -67,3 +75,55 @@ def test_noalloc_ignores_overlap():
     torch.cuda.synchronize()
     for k in KEYS:
         assert torch.equal(r[k], ref[k]), k
+
+
+@pytest.mark.parametrize("variant", ["paged_fp8", "eta", "min_p_sliced"])
+def test_overlap_schedule_optional_paths(variant):
+    """The optional layouts and allowed sets under both schedules, bitwise:
+    paged fp8 caches (C5), the eta allowed set (C3), min-p with the sliced
+    walk (C2)."""
+    import numpy as np
+
+    from workloads import to_fp8_e4m3, to_paged
+
+    name = {"paged_fp8": "c5_super_tree", "eta": "c3_eagle_tree", "min_p_sliced": "c2_llama8b_chain"}[variant]
+    cfg = get_config(name)
+    w = generate(cfg, "cuda")
+    print(f"[overlap-{variant}] {name} B={w['B']} N={w['N']}", flush=True)
+    k = v = None
+    attn_kw, sample_kw = {}, {}
+    if variant == "paged_fp8":
+        ks = float(w["k_cache"].float().abs().amax()) / 448.0
+        vs = float(w["v_cache"].float().abs().amax()) / 448.0
+        k8, v8 = to_fp8_e4m3(w["k_cache"], ks), to_fp8_e4m3(w["v_cache"], vs)
+        del w["k_cache"], w["v_cache"]
+        B_, H_, Lc, D_ = k8.shape
+        if Lc % 128:  # whole blocks
+            pad = torch.zeros((B_, H_, 128 - Lc % 128, D_), dtype=k8.dtype, device=k8.device)
+            k8, v8 = torch.cat([k8, pad], dim=2), torch.cat([v8, pad], dim=2)
+        kp, vp, bt = to_paged(k8, v8, 128, np.random.default_rng(5), spare_blocks=0)
+        k, v = kp, vp
+        attn_kw = {"block_table": torch.from_numpy(bt).cuda(), "kv_fp8_scales": (ks, vs)}
+    elif variant == "eta":
+        sample_kw = {"eta": (0.05, 0.3)}
+    else:
+        sample_kw = {"min_p": 0.05, "walk_mode": "sliced"}
+    off = _step(w, cfg, "off", k, v, attn_kw, sample_kw)
+    on = _step(w, cfg, "on", k, v, attn_kw, sample_kw)
+    stream = torch.cuda.Stream()
+    # the inputs were generated, and the calls' outputs and workspaces
+    # allocated, in the default stream's order; the allocator may have handed
+    # out blocks whose earlier default-stream users have not run yet
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        r = off(stream)
+    torch.cuda.synchronize()
+    ref = {kk: r[kk].clone() for kk in KEYS}
+    with torch.cuda.stream(stream):
+        for _ in range(2):
+            res = on(stream)
+    torch.cuda.synchronize()
+    for kk in KEYS:
+        assert torch.equal(res[kk], ref[kk]), kk
+    for c in (off, on):
+        assert int(c.sample.status.item()) == 0 and int(c.attn.status.item()) == 0
