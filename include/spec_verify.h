@@ -366,7 +366,10 @@ sv_status spec_verify_step(const sv_attn_args* attn, const sv_sample_args* sampl
                            void* ws, size_t ws_bytes, void* stream);
 
 /* Timing events of spec_verify_step_timed (measurement): hipEvent_t handles
- * created by the caller, each recorded on the call's stream when non-NULL. */
+ * created by the caller, each recorded on the call's stream when non-NULL
+ * (under SV_OVERLAP_ON, attn_start and attn_stop on the library's second
+ * stream, where the attention runs; elapsed times between events of the two
+ * streams then span concurrent work).                                      */
 typedef struct {
   void* attn_start;   /* before the attention kernel (after tree preparation) */
   void* attn_stop;    /* after the attention kernel (before a split merge)    */
