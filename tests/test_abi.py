@@ -117,8 +117,9 @@ def test_walk_layout_fields(lib):
          for m in sv.WALK_MODES.values()}
     assert len(g) == 1
     assert os.environ.get("SV_WALK_MODE") is None  # nothing reads the environment
-    src = open(os.path.join(ROOT, "speculative_decoding_verification_16_amd", "csrc", "sv_sample.hip")).read()
-    assert "getenv" not in src
+    csrc = os.path.join(ROOT, "speculative_decoding_verification_16_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        assert "getenv" not in open(os.path.join(csrc, name)).read(), name
 
 
 def test_step_overlap_field(lib):
