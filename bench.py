@@ -554,23 +554,6 @@ def main():
                    "step_ms_p10_p50_p90": [round(opct(0.1), 4), round(opct(0.5), 4), round(opct(0.9), 4)],
                    "value": round(w["N"] * K / other_elapsed, 1)}
 
-    # The sampler alone (spec_verify_sample: row statistics and walk, no
-    # attention before it), same inputs, K calls with events around each.
-    # Inside the step the same kernels run right after the MFMA-heavy
-    # attention and take longer (the part's clock and power management).
-    aev = HipEvents(2 * K)
-    for i in range(n_sets):
-        calls[i][1](stream)
-    stream.synchronize()
-    for i in range(K):
-        aev.record(2 * i, stream)
-        calls[i % n_sets][1](stream)
-        aev.record(2 * i + 1, stream)
-    stream.synchronize()
-    torch.cuda.synchronize()
-    sms = sorted(aev.ms(2 * i, 2 * i + 1) for i in range(K))
-    aev.close()
-    sampler_alone_ms = sms[K // 2]
 
     ms = elapsed / K * 1e3
     value = w["N"] * K / elapsed
@@ -605,9 +588,6 @@ def main():
         kernels["sampler(stats+finalize+walk)"] = {
             "us": smp_ms * 1e3, "alg_bytes": smp_b, "GB_s": smp_b / smp_ms / 1e6,
             "frac": smp_b / smp_ms / 1e6 / HBM_PEAK_GBS, "residual_pass_bytes": passes_mean * per_pass}
-        kernels["sampler_alone(spec_verify_sample, p50)"] = {
-            "us": sampler_alone_ms * 1e3, "alg_bytes": smp_b, "GB_s": smp_b / sampler_alone_ms / 1e6,
-            "frac": smp_b / sampler_alone_ms / 1e6 / HBM_PEAK_GBS}
         if args.overlap == "off":
             rest_us = ms * 1e3 - attn_ms * 1e3 - smp_ms * 1e3
             kernels["other(prep+combine)"] = {"us": rest_us}
