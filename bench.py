@@ -140,6 +140,9 @@ def parse_args():
                          "seconds for the large workloads)")
     ap.add_argument("--kv-fp8", action="store_true",
                     help="quantise the KV caches to OCP FP8 E4M3 bytes with per-tensor scales (bf16 workloads)")
+    ap.add_argument("--input-sets", type=int, default=0, metavar="N",
+                    help="cycle through N copies of the inputs (0 = as many as keep the per-step working set "
+                         "at 512 MB or more, up to 8)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES three times (calibrates the HBM "
                          "byte counters of rocprofv3 against a kernel of known traffic) and exit")
@@ -401,6 +404,8 @@ def main():
     # in separate buffers, at least 512 MB together (at most 8 copies).
     set_bytes = attention_bytes(w) + 8 * w["V"] * (w["N"] + w["B"])
     n_sets = max(1, min(MAX_INPUT_SETS, math.ceil(ROTATE_BYTES / set_bytes)))
+    if args.input_sets:
+        n_sets = args.input_sets
     sets = [w] + [generate(cfg, dev, candidates=cand) for _ in range(n_sets - 1)]
     if args.kv_fp8:
         from workloads import to_fp8_e4m3
