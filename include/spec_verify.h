@@ -34,7 +34,9 @@
  *    reentrant; two calls may run concurrently on different streams if they
  *    use different workspaces and outputs.
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
- *    stream) and never synchronise with the host.
+ *    stream) and never synchronise with the host. The stream and every
+ *    device pointer belong to the current HIP device of the calling thread
+ *    (the library's own handles are kept per current device).
  *  - Argument errors are found on the host before anything is enqueued: the
  *    call then returns a non-SV_OK code, enqueues nothing and leaves a message
  *    for spec_verify_last_error(). SV_ERR_HIP means a launch failed.
