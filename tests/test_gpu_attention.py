@@ -386,3 +386,20 @@ def test_fp8_attention_arguments():
         with pytest.raises(sv.SpecVerifyError):
             sv.attn(w2["q"], u8, u8, w2["ctx_len_t"], w2["cu_nodes_t"], parent=w2["parent_t"],
                     max_nodes=w2["max_T"], kv_fp8_scales=bad)
+
+
+def test_attention_very_long_context():
+    """A 2^21-key context in one (request, KV head) slab, 16 times the longest
+    configured bucket: the split planner's long-range cap, 32-bit byte
+    offsets within the slab near 2^29 and a draft chain at its far end. Every
+    output is checked against the oracle."""
+    cfg = scaled(C4_BUCKETS[0], B=1, K=3, L=1 << 21, Hq=4, Hkv=1, V=16)
+    w = generate(cfg, "cuda", sample=False)
+    print(f"[attn-long] B={w['B']} N={w['N']} Lcap={w['Lcap']}", flush=True)
+    out = _run(w)
+    assert bool(torch.isfinite(out).all())
+    items = np.array([(n, h) for n in range(w["N"]) for h in range(w["Hq"])], dtype=np.int64)
+    ref = oracle_attention(w, items)
+    got = out.cpu().numpy()[items[:, 0], items[:, 1]]
+    err = float(np.abs(got - ref).max())
+    assert err <= ATTN_TOL[cfg.dtype], err

@@ -658,3 +658,32 @@ def test_truncation_arguments():
     g1 = _gpu_sample(w, 0.0, eta=(0.1, 0.3))
     for k in ("accept_len", "accepted_nodes", "out_tokens"):
         assert torch.equal(g0[k], g1[k]), k
+
+
+def test_sampler_max_vocab():
+    """The largest vocabulary the ABI takes (2^22 tokens: 1024 chunks per row,
+    the walk's per-chunk arrays and the slices' exchange at their full size):
+    sampled walks in every layout, the greedy walk, min-p and the eta set
+    against the oracle, and p on the first and last rows."""
+    cfg = scaled(C2, B=2, K=4, V=1 << 22)
+    w = generate(cfg, "cuda", attn=False)
+    T = cfg.temperature
+    print(f"[max-vocab] B={w['B']} N={w['N']} V={cfg.V}", flush=True)
+    for mode in ("auto", "single", "sliced"):
+        r = _gpu_sample(w, T, walk_mode=mode)
+        assert int(r["status"].item()) == 0, sv.status_names(int(r["status"].item()))
+        md = r["accepted_nodes"].shape[1]
+        flagged = compare_walk(r, _oracle(w, T, md), w["B"], greedy=False)
+        print(f"  {mode}: flagged near-ties {flagged}/{w['B']}, passes {r['residual_passes'].tolist()}", flush=True)
+    r = _gpu_sample(w, 0.0)
+    assert int(r["status"].item()) == 0
+    compare_walk(r, _oracle(w, 0.0, r["accepted_nodes"].shape[1]), w["B"], greedy=True)
+    for kw in ({"min_p": 0.05}, {"eta": (0.05, 0.3)}):
+        r = _gpu_sample(w, T, **kw)
+        assert int(r["status"].item()) == 0, sv.status_names(int(r["status"].item()))
+        compare_walk(r, _oracle_kw(w, T, r["accepted_nodes"].shape[1], **kw), w["B"], greedy=False)
+    r = _gpu_sample(w, T, probs_out=True)
+    rows = np.array([0, w["N"] + w["B"] - 1])
+    p_ref = oracle.target_rows(w["logits"].cpu().numpy(), T, rows)
+    got = r["probs"][torch.from_numpy(rows).cuda()].cpu().numpy()
+    assert float(np.abs(got - p_ref).max()) <= PROB_TOL
