@@ -127,3 +127,43 @@ def test_overlap_schedule_optional_paths(variant):
         assert torch.equal(res[kk], ref[kk]), kk
     for c in (off, on):
         assert int(c.sample.status.item()) == 0 and int(c.attn.status.item()) == 0
+
+
+def test_two_host_threads_overlapped():
+    """Two host threads, each with its own stream, workspace and outputs, run
+    overlapped steps at the same time (the library's side stream and events
+    are per thread); every result equals the single-threaded in-order one."""
+    import threading
+
+    cfg = get_config("c3_eagle_tree")
+    w = generate(cfg, "cuda")
+    calls = [_step(w, cfg, "on") for _ in range(2)]
+    ref_call = _step(w, cfg, "off")
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in ref_call(torch.cuda.current_stream()).items() if k in KEYS}
+    torch.cuda.synchronize()
+    errors = []
+
+    def run(c):
+        try:
+            st = torch.cuda.Stream()
+            st.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(st):
+                for _ in range(6):
+                    c(st)
+            st.synchronize()
+        except Exception as e:  # reported in the main thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=run, args=(c,)) for c in calls]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(120)
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for c in calls:
+        r = c._results()
+        for k in KEYS:
+            assert torch.equal(r[k], ref[k]), k
+        assert int(c.sample.status.item()) == 0 and int(c.attn.status.item()) == 0
