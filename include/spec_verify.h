@@ -81,9 +81,10 @@ typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
 #define SV_STATUS_TREE_INVALID   0x01 /* parent outside [-1, j-1]: node treated as a root child (attn) / request skipped (sample) */
 #define SV_STATUS_PACKING        0x02 /* cu_nodes not monotone, T_b > max_nodes, or cu_nodes[B] != total_nodes: request skipped */
 #define SV_STATUS_TOKEN_RANGE    0x04 /* draft token outside [0, V): request skipped */
-#define SV_STATUS_NONFINITE      0x08 /* a row with a NaN or +inf logit, or whose logits are all -inf: it has no
-                                         target distribution; a walk that reaches it stops there, without a
-                                         token at that position (out_tokens[b][accept_len[b]] = -1) */
+#define SV_STATUS_NONFINITE      0x08 /* the walk reached a row with a NaN or +inf logit, or whose logits are all
+                                         -inf: it has no target distribution; the walk stops there, without a
+                                         token at that position (out_tokens[b][accept_len[b]] = -1); rows the
+                                         walk does not reach are not checked */
 #define SV_STATUS_ZERO_RESIDUAL  0x10 /* residual mass rounded to 0 after a rejection: distribution kept unchanged */
 #define SV_STATUS_CTX_RANGE      0x20 /* ctx_len[b] < 0 or ctx_len[b] + T_b > Lcap: request skipped */
 #define SV_STATUS_SYNC           0x40 /* a sampler workgroup gave up waiting for the other workgroups of its request
@@ -281,16 +282,16 @@ typedef struct {
   int32_t join_ticks;
   /* Schedule of spec_verify_step (ignored by spec_verify_sample; results are
    * bitwise the same either way):
-   *   SV_OVERLAP_OFF (0, the default): attention, then row statistics, then
-   *     the walk, all on the caller's stream;
-   *   SV_OVERLAP_ON (1): the sampler (row statistics, then the walk) on the
-   *     caller's stream while the attention (with its split-K merge) runs on
-   *     a second stream forked from the caller's at the call's start and
-   *     joined back into it at the end (the caller's stream sees the whole
-   *     step done, as with OFF). The attention leaves part of the HBM
-   *     bandwidth unused and the row statistics stream through it. Faster for
-   *     large batches (256 requests of 152K-token rows: 0.78 -> 0.74 ms per
-   *     step on one MI355X), slower for small ones (the fork and join cost a
+   *   SV_OVERLAP_OFF (0, the default): attention, then the sampler, all on
+   *     the caller's stream;
+   *   SV_OVERLAP_ON (1): the sampler on the caller's stream while the
+   *     attention (with its split-K merge) runs on a second stream forked
+   *     from the caller's at the call's start and joined back into it at the
+   *     end (the caller's stream sees the whole step done, as with OFF). The
+   *     attention leaves part of the HBM bandwidth unused and the sampler's
+   *     logit reads stream through it. Faster for large batches (256
+   *     requests of 152K-token rows: 0.68 -> 0.63 ms per step on one
+   *     MI355X), slower for small ones (the fork and join cost a
    *     few microseconds); each kernel then takes longer than alone, as the
    *     two share the device. The second stream (non-blocking, default
    *     priority) and its two events are created by the library on first use,
@@ -362,6 +363,15 @@ sv_status spec_verify_attn(const sv_attn_args* attn, void* ws, size_t ws_bytes, 
 /* Rejection-sampling walk. ws as above with spec_verify_workspace_size(NULL, sample). */
 sv_status spec_verify_sample(const sv_sample_args* sample, void* ws, size_t ws_bytes, void* stream);
 
+/* Workgroups per request of spec_verify_sample's walk for these arguments
+ * (host-visible fields only; under SV_WALK_AUTO also the current device's
+ * CU count and occupancy): 1, or 2..8 for the sliced walk. With 1 and no
+ * probs_out the walk computes the statistics of the logit rows it reaches
+ * by itself and reads no other row; otherwise a statistics pass reads every
+ * row of the batch first. 0 on invalid arguments, with the last error set.
+ * A query for callers that account for the walk's memory traffic.          */
+int32_t spec_verify_walk_slices(const sv_sample_args* sample);
+
 /* Attention then sampling on one stream; the two argument sets must describe
  * the same batch (B, total_nodes, cu_nodes). ws: spec_verify_workspace_size(attn, sample). */
 sv_status spec_verify_step(const sv_attn_args* attn, const sv_sample_args* sample,
@@ -375,8 +385,10 @@ sv_status spec_verify_step(const sv_attn_args* attn, const sv_sample_args* sampl
 typedef struct {
   void* attn_start;   /* before the attention kernel (after tree preparation) */
   void* attn_stop;    /* after the attention kernel (before a split merge)    */
-  void* sample_start; /* before the sampler's row-statistics kernel           */
-  void* stats_stop;   /* after the row-statistics kernel                      */
+  void* sample_start; /* before the sampler's first kernel                    */
+  void* stats_stop;   /* after the row-statistics kernel (which, when the walk
+                         computes its rows' statistics itself, holds only the
+                         attention's split-K merge, if any)                   */
   void* sample_stop;  /* after the walk (the sampler's last kernel)           */
 } sv_timing;
 

@@ -84,6 +84,8 @@ def load_library(path: str = LIB_PATH):
     lib.spec_verify_step_timed.restype = ctypes.c_int
     lib.spec_verify_step_noalloc.argtypes = [_P, _P, _P]
     lib.spec_verify_step_noalloc.restype = ctypes.c_int
+    lib.spec_verify_walk_slices.argtypes = [_P]
+    lib.spec_verify_walk_slices.restype = _i32
     lib.spec_verify_last_error.argtypes = []
     lib.spec_verify_last_error.restype = ctypes.c_char_p
     lib.spec_verify_struct_size.argtypes = [_i32]
@@ -272,6 +274,17 @@ class SampleCall:
         if self.passes is not None:
             r["residual_passes"] = self.passes
         return r
+
+    def walk_slices(self) -> int:
+        """spec_verify_walk_slices: workgroups per request of the walk for these
+        arguments on the current device. With 1 and no probs output the walk
+        reads only the logit rows it reaches; otherwise every row is read by a
+        statistics pass first."""
+        lib = load_library()
+        n = lib.spec_verify_walk_slices(ctypes.byref(self.args))
+        if n <= 0:
+            raise SpecVerifyError(SV_ERR_INVALID_ARG, lib.spec_verify_last_error().decode())
+        return int(n)
 
     def __call__(self, stream=None):
         _check(load_library().spec_verify_sample(ctypes.byref(self.args), _ptr(self.ws), self.ws_bytes,

@@ -337,6 +337,12 @@ sv_status run_attn(const sv_attn_args* a, char* ws, const WsLayout& w, hipStream
   return SV_OK;
 }
 
+// workgroups per request of the walk (the sliced walk's coordination words
+// exist in the workspace only when slicing can pay)
+int walk_slices_for(const sv_sample_args* s, const WsLayout& w) {
+  return w.xcnt ? sv::walk_slices(s->B, sample_nch(s), walk_passes(s), s->walk_mode) : 1;
+}
+
 sv_status run_sample(const sv_sample_args* s, char* ws, const WsLayout& w, hipStream_t st,
                      const sv::SampleEvents& ev, const sv::MergeArgs& merge = sv::MergeArgs{}) {
   if (s->B == 0) return SV_OK;
@@ -382,7 +388,7 @@ sv_status run_sample(const sv_sample_args* s, char* ws, const WsLayout& w, hipSt
   p.det = s->siblings == SV_SIBLINGS_DETERMINISTIC;
   p.rule = s->rule;
   p.rule_param = s->rule_param;
-  p.slices = w.xcnt ? sv::walk_slices(s->B, p.nch, walk_passes(s), s->walk_mode) : 1;
+  p.slices = walk_slices_for(s, w);
   p.xs = w.xcnt ? (double*)(ws + w.xs) : nullptr;
   p.xcnt = w.xcnt ? (int32_t*)(ws + w.xcnt) : nullptr;
   p.join_ticks = s->join_ticks == 0 ? sv::kJoinWindow : (s->join_ticks < 0 ? 0u : (uint32_t)s->join_ticks);
@@ -554,6 +560,12 @@ sv_status spec_verify_step_noalloc(const sv_attn_args* attn, const sv_sample_arg
   if (attn->B != sample->B || attn->total_nodes != sample->total_nodes || attn->cu_nodes != sample->cu_nodes)
     return fail(SV_ERR_INVALID_ARG, "attn and sample args must describe the same batch (B, total_nodes, cu_nodes)");
   return run_step(attn, sample, ws, w, (hipStream_t)stream, sv_timing{}, false);
+}
+
+int32_t spec_verify_walk_slices(const sv_sample_args* sample) {
+  g_err[0] = 0;
+  if (check_sample(sample) != SV_OK) return 0;
+  return walk_slices_for(sample, layout(nullptr, sample));
 }
 
 const char* spec_verify_last_error(void) { return g_err; }

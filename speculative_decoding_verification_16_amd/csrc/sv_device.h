@@ -252,11 +252,11 @@ __device__ __forceinline__ void row_norm(const ChunkStat* st, int nch, float c, 
     if (in_regs) {
 #pragma unroll
       for (int k = 0; k < kRowRegs; ++k)
-        if (cs[k].lmax != -INFINITY) acc += cs[k].s * exp2((double)(cs[k].lmax - m) * (double)c);
+        if (cs[k].lmax != -INFINITY) acc = fma(cs[k].s, exp2((double)(cs[k].lmax - m) * (double)c), acc);
     } else {
       for (int ch = gl; ch < nch; ch += kRowGroup) {
         const ChunkStat s = st[ch];
-        if (s.lmax != -INFINITY) acc += s.s * exp2((double)(s.lmax - m) * (double)c);
+        if (s.lmax != -INFINITY) acc = fma(s.s, exp2((double)(s.lmax - m) * (double)c), acc);
       }
     }
   }

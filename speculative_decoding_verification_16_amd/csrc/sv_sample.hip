@@ -45,11 +45,127 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // fp64 roundings of their exact values, so that the set is decided as its
 // definition says (the fp32 weights of the sums for p would put the
 // threshold up to ~1e-5 T off on flat rows).
+//
+// chunk_stat is that work for one chunk, by one wave (every lane calls it and
+// gets the record): the row-statistics kernel runs it for every chunk of every
+// row, and the walk, when it computes the statistics of the rows it reaches
+// itself, runs the same code on those rows. A chunk holding a NaN or +inf
+// gets arg = kBadChunk: the row has no distribution (row_norm), which the
+// walk reports when it reaches the row.
+// The arithmetic of chunk_stat on a chunk already in registers (tokens past
+// the row's end hold -inf); the lazy walk loads its chunks its own way and
+// reduces them with this same code.
+template <bool GREEDY, bool VEC, bool ENT>
+__device__ __forceinline__ void chunk_reduce(const float (&x)[64], int begin, float c, double c64, const double* tab,
+                                             ChunkStat& st, double2& se) {
+  const int lane = threadIdx.x & 63;
+  // element (i) of this lane is token begin + 4*(lane + 64*(i/4)) + i%4 (VEC)
+  // or begin + lane + 64*i (scalar); both visit a lane's tokens in increasing order
+  float mx = -INFINITY;
+  bool any_bad;
+  if (GREEDY) {
+    // the argmax (lowest index on ties) and an explicit NaN / +inf test
+    int ai = 0x7fffffff;
+    bool bad = false;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      const float v = x[i];
+      bad |= (v != v) || (v == INFINITY);
+      if (v > mx) {
+        mx = v;
+        ai = VEC ? begin + 4 * (lane + 64 * (i >> 2)) + (i & 3) : begin + lane + 64 * i;
+      }
+    }
+    any_bad = __any(bad);
+    wave_argmax(mx, ai);
+    st.lmax = mx;
+    st.arg = any_bad ? kBadChunk : (mx == -INFINITY ? begin : ai);
+    st.s = 0.0;
+    se = make_double2(0.0, 0.0);
+    return;
+  }
+  // sampling needs no argmax, and the NaN / +inf test comes from the sum:
+  // with a finite maximum a NaN logit has a NaN weight; a +inf maximum gives
+  // its own element a NaN weight (inf - inf); only a chunk whose maximum is
+  // -inf (every logit -inf or NaN) is tested element by element. A lane
+  // maximum that a signalling NaN turned into a NaN drops out of the wave
+  // maximum, and that lane's NaN weight still flags the chunk.
+#pragma unroll
+  for (int i = 0; i < 64; ++i) mx = fmaxf(mx, x[i]);
+  mx = wave_max(mx);
+  double s = 0.0, s64 = 0.0, e64 = 0.0;
+  if (mx != -INFINITY) {
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      const float w = target_weight(x[i], mx, c);
+      s += (double)w;
+      if (ENT && x[i] != -INFINITY) {
+        const double y = ((double)x[i] - (double)mx) * c64;
+        const double w64 = exp2_neg_f64(y, tab);
+        s64 += w64;
+        e64 += w64 * y;
+      }
+    }
+    s = wave_sum(s);
+    if (ENT) {
+      s64 = wave_sum(s64);
+      e64 = wave_sum(e64);
+    }
+    any_bad = s != s;
+  } else {
+    bool nan = false;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) nan |= x[i] != x[i];
+    any_bad = __any(nan);
+  }
+  st.lmax = mx;
+  st.arg = any_bad ? kBadChunk : begin;  // the argmax is read by greedy walks only
+  st.s = s;
+  se = make_double2(s64, e64);
+}
+
+// chunk_stat: the chunk's loads (tokens past the row's end as -inf), then
+// chunk_reduce.
+template <bool GREEDY, bool VEC, bool ENT>
+__device__ __forceinline__ void chunk_stat(const float* __restrict__ base, int V, int ch, float c, double c64,
+                                           const double* tab, ChunkStat& st, double2& se) {
+  const int lane = threadIdx.x & 63;
+  const int begin = ch * kChunk;
+  const int end = min(V, begin + kChunk);
+  float x[64];
+  if (VEC) {
+    const f32x4_t* b4 = (const f32x4_t*)(base + begin);
+    const int n4 = (end - begin) >> 2;  // V % 4 == 0 on this path
+    // streamed once: non-temporal loads (measured ~9 % faster on MI355X)
+    if (n4 == kChunk / 4) {  // a whole chunk (uniform): no bounds tests
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const f32x4_t v = __builtin_nontemporal_load(b4 + lane + 64 * i);
+        x[4 * i + 0] = v.x; x[4 * i + 1] = v.y; x[4 * i + 2] = v.z; x[4 * i + 3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int idx = lane + 64 * i;
+        const f32x4_t v = idx < n4 ? __builtin_nontemporal_load(b4 + idx)
+                                   : f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        x[4 * i + 0] = v.x; x[4 * i + 1] = v.y; x[4 * i + 2] = v.z; x[4 * i + 3] = v.w;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      const int idx = begin + lane + 64 * i;
+      x[i] = idx < end ? __builtin_nontemporal_load(base + idx) : -INFINITY;
+    }
+  }
+  chunk_reduce<GREEDY, VEC, ENT>(x, begin, c, c64, tab, st, se);
+}
+
 template <bool GREEDY, bool VEC, bool ENT = false>
 __global__ __launch_bounds__(256) void row_stats_kernel(const float* __restrict__ logits, int V, int64_t rows,
                                                         int nch, float c, ChunkStat* __restrict__ stats,
-                                                        int32_t* status, int32_t* xcnt, int nsync,
-                                                        MergeArgs merge, int stat_blocks,
+                                                        int32_t* xcnt, int nsync, MergeArgs merge, int stat_blocks,
                                                         double2* __restrict__ ent = nullptr, double c64 = 0.0) {
   // blocks past the statistics merge the step's split-K attention partials
   // (one launch fewer; the work is independent of the statistics)
@@ -71,72 +187,12 @@ __global__ __launch_bounds__(256) void row_stats_kernel(const float* __restrict_
   if (item >= rows * nch) return;
   const int64_t row = item / nch;
   const int ch = (int)(item - row * nch);
-  const float* base = logits + row * (int64_t)V;
-  const int begin = ch * kChunk;
-  const int end = min(V, begin + kChunk);
-
-  float x[64];
-  if (VEC) {
-    const float4* b4 = (const float4*)(base + begin);
-    const int n4 = (end - begin) >> 2;  // V % 4 == 0 on this path
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int idx = lane + 64 * i;
-      // streamed once: a non-temporal load (measured ~9 % faster on MI355X)
-      const f32x4_t v = idx < n4 ? __builtin_nontemporal_load((const f32x4_t*)b4 + idx)
-                                 : f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-      x[4 * i + 0] = v.x; x[4 * i + 1] = v.y; x[4 * i + 2] = v.z; x[4 * i + 3] = v.w;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 64; ++i) {
-      const int idx = begin + lane + 64 * i;
-      x[i] = idx < end ? __builtin_nontemporal_load(base + idx) : -INFINITY;
-    }
-  }
-  // element (i) of this lane is token begin + 4*(lane + 64*(i/4)) + i%4 (VEC)
-  // or begin + lane + 64*i (scalar); both visit a lane's tokens in increasing order
-  float mx = -INFINITY;
-  int ai = 0x7fffffff;
-  bool bad = false;
-#pragma unroll
-  for (int i = 0; i < 64; ++i) {
-    const float v = x[i];
-    bad |= (v != v) || (v == INFINITY);
-    if (v > mx) {
-      mx = v;
-      ai = VEC ? begin + 4 * (lane + 64 * (i >> 2)) + (i & 3) : begin + lane + 64 * i;
-    }
-  }
-  const bool any_bad = __any(bad);
-  if (any_bad && lane == 0) flag(status, kStNonFinite);
-  wave_argmax(mx, ai);
-  double s = 0.0, s64 = 0.0, e64 = 0.0;
-  if (!GREEDY && mx != -INFINITY) {
-#pragma unroll
-    for (int i = 0; i < 64; ++i) {
-      const float w = target_weight(x[i], mx, c);
-      s += (double)w;
-      if (ENT && x[i] != -INFINITY) {
-        const double y = ((double)x[i] - (double)mx) * c64;
-        const double w64 = exp2_neg_f64(y, tab);
-        s64 += w64;
-        e64 += w64 * y;
-      }
-    }
-    s = wave_sum(s);
-    if (ENT) {
-      s64 = wave_sum(s64);
-      e64 = wave_sum(e64);
-    }
-  }
+  ChunkStat st;
+  double2 se;
+  chunk_stat<GREEDY, VEC, ENT>(logits + row * (int64_t)V, V, ch, c, c64, tab, st, se);
   if (lane == 0) {
-    ChunkStat st;
-    st.lmax = mx;
-    st.arg = any_bad ? kBadChunk : (mx == -INFINITY ? begin : ai);
-    st.s = s;
     stats[item] = st;
-    if (ENT) ent[item] = make_double2(s64, e64);
+    if (ENT) ent[item] = se;
   }
 }
 
@@ -147,11 +203,12 @@ __global__ __launch_bounds__(256) void row_stats_kernel(const float* __restrict_
 // H = ln S - E / S, E = sum_x w_x z_x (z in nats relative to the row maximum)
 // merged from the chunk accumulators like S. The walk runs it for its own
 // rows; row_finalize_kernel runs it for every row when the p rows are an
-// output, so both see bitwise the same values.
-__device__ __forceinline__ void finalize_row(const SampleParams& p, int64_t row, RowStat& r, RowThr& thr) {
+// output, so both see bitwise the same values. st and ent point at the row's
+// chunk records (in the workspace, or in LDS for a row the walk computed).
+__device__ __forceinline__ void finalize_row_from(const SampleParams& p, const ChunkStat* st, const double2* ent,
+                                                  RowStat& r, RowThr& thr) {
   const int gl = threadIdx.x & (kRowGroup - 1);
   const int nch = p.nch;
-  const ChunkStat* st = p.stats + row * nch;
   float lmax, av;
   double S;
   int arg;
@@ -165,10 +222,10 @@ __device__ __forceinline__ void finalize_row(const SampleParams& p, int64_t row,
       const ChunkStat cs = st[ch];
       if (cs.lmax != -INFINITY) {
         const double dl = ((double)cs.lmax - (double)lmax) * p.c64;  // chunk max relative to the row's
-        const double2 se = p.ent[row * nch + ch];
+        const double2 se = ent[ch];
         const double sc = exp2(dl);
-        accS += sc * se.x;
-        accE += sc * (se.y + dl * se.x);
+        accS = fma(sc, se.x, accS);
+        accE = fma(sc, fma(dl, se.x, se.y), accE);
       }
     }
     const double S64 = group_sum(accS);
@@ -180,6 +237,96 @@ __device__ __forceinline__ void finalize_row(const SampleParams& p, int64_t row,
   r.lmax = lmax;
   r.arg = arg;
   r.S = S;
+}
+__device__ __forceinline__ void finalize_row(const SampleParams& p, int64_t row, RowStat& r, RowThr& thr) {
+  finalize_row_from(p, p.stats + row * p.nch, p.ent ? p.ent + row * p.nch : nullptr, r, thr);
+}
+
+// finalize_row_from computed by a whole wave, for the lazy walk's single row:
+// every lane takes chunks lane, lane + 64, ... for the maximum, the argmax and
+// the per-chunk fp64 factors (the exp2 of each chunk's offset from the row
+// maximum, all in parallel); the fmas then run in exactly the order of the
+// 4-lane group (lane gl takes chunks gl, gl + 4, ... in turn, then the
+// group's butterfly), so every value is bitwise that of finalize_row_from.
+// All 64 lanes call it; lanes 0..3 hold the results.
+__device__ __forceinline__ void finalize_row_wave(const SampleParams& p, const ChunkStat* st, const double2* ent,
+                                                  RowStat& r, RowThr& thr) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int gl = lane & (kRowGroup - 1);
+  const int nch = p.nch;
+  float m = -INFINITY, av = -INFINITY;
+  int ai = 0x7fffffff;
+  bool bad = false;
+  for (int ch = lane; ch < nch; ch += kWave) row_norm_acc(st[ch], m, av, ai, bad);
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    m = fmaxf(m, __shfl_xor(m, o));
+    const float ov = __shfl_xor(av, o);
+    const int oi = __shfl_xor(ai, o);
+    if (ov > av || (ov == av && oi < ai)) { av = ov; ai = oi; }
+  }
+  thr = p.mp_thr;
+  if (__any(bad)) {
+    r.lmax = -INFINITY;
+    r.arg = kBadChunk;
+    r.S = 0.0;
+    return;
+  }
+  const bool eta = p.eta && m != -INFINITY;
+  double acc = 0.0, accS = 0.0, accE = 0.0;
+  if (m != -INFINITY) {
+    for (int b0 = 0; b0 < nch; b0 += kWave) {
+      // this lane's chunk of the block: its terms (0 for a chunk with no
+      // finite logit, which adds nothing to a sum that starts at +0)
+      const int ch = b0 + lane;
+      // (the factors of each fma, so that the sums below are formed exactly
+      // as the group forms them)
+      double cs_s = 0.0, e = 0.0, sc = 0.0, sex = 0.0, inner = 0.0;
+      bool live = false;
+      if (ch < nch) {
+        const ChunkStat cs = st[ch];
+        if (cs.lmax != -INFINITY) {
+          live = true;
+          cs_s = cs.s;
+          e = exp2((double)(cs.lmax - m) * (double)p.c);
+          if (eta) {
+            const double dl = ((double)cs.lmax - (double)m) * p.c64;
+            const double2 se = ent[ch];
+            sc = exp2(dl);
+            sex = se.x;
+            inner = fma(dl, se.x, se.y);
+          }
+        }
+      }
+      // the group's order: lane gl takes chunks b0 + gl, b0 + gl + 4, ...
+      // (a chunk with no finite logit is skipped, as the group skips it)
+      const int nb = min(kWave, nch - b0);
+#pragma unroll
+      for (int k = 0; k < kWave / kRowGroup; ++k) {
+        const int src = gl + kRowGroup * k;
+        const bool use = src < nb && __shfl(live ? 1 : 0, src) != 0;
+        const double vs = __shfl(cs_s, src), ve = __shfl(e, src);
+        if (use) acc = fma(vs, ve, acc);
+        if (eta) {
+          const double vsc = __shfl(sc, src), vx = __shfl(sex, src), vin = __shfl(inner, src);
+          if (use) {
+            accS = fma(vsc, vx, accS);
+            accE = fma(vsc, vin, accE);
+          }
+        }
+      }
+    }
+  }
+  r.lmax = m;
+  r.arg = ai;
+  r.S = group_sum(acc);
+  if (eta) {
+    const double S64 = group_sum(accS);
+    const double E = group_sum(accE) * 0.69314718055994530942;  // log2 units -> nats
+    const double lnS = log(S64);
+    const double H = lnS - E / S64;
+    thr = make_row_thr(p.temp * (lnS + fmin(p.ln_eps, p.ln_delta - H)));
+  }
 }
 
 // Every row's normalisation, for the p-row output (64 rows per workgroup).
@@ -605,9 +752,25 @@ __device__ __forceinline__ void skip_request(const SampleParams& p, int b, int32
   }
 }
 
-template <bool VEC, int NT, bool TR>
+// The current row's chunk records when the walk computes the statistics of
+// the rows it reaches (LAZY), and the 2^(j/256) table of the eta sums.
+template <bool ON>
+struct LazyRow {
+  ChunkStat cst[ON ? kMaxChunks : 1];
+  double2 cent[ON ? kMaxChunks : 1];
+  double tab[ON ? kExp2Tab : 1];
+};
+
+// LAZY (one workgroup per request, no p-row output): no row-statistics pass
+// runs before the walk; the walk computes the statistics of each row when it
+// reaches it, with the row-statistics kernel's per-chunk code, so the rows
+// it never reaches (those after a rejected node) are not read at all and
+// the results are bitwise those of the other form.
+template <bool VEC, int NT, bool TR, bool LAZY = false>
 __global__ __launch_bounds__(NT) void walk_kernel(SampleParams p) {
+  static_assert(!LAZY || NT == 512, "the lazy form is the one-workgroup walk");
   __shared__ WalkShared<NT> sh;
+  __shared__ LazyRow<LAZY> lz;
   const int b = blockIdx.x / p.slices, slice = blockIdx.x - b * p.slices;
   int32_t* sync = p.slices > 1 ? p.xcnt + (int64_t)b * kWalkSync : nullptr;  // [0] passes, [1] arrivals, [2] mode
   if (sync && threadIdx.x == 0) __hip_atomic_fetch_add(sync + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -647,13 +810,18 @@ __global__ __launch_bounds__(NT) void walk_kernel(SampleParams p) {
   // (uniform by construction; said explicitly, so that the compiler keeps the
   // rows' buffer resources in scalar registers)
   const int64_t row0 = (int64_t)__builtin_amdgcn_readfirstlane(n0 + b);
-  for (int r = tid / kRowGroup; r <= T; r += NT / kRowGroup) {
-    RowStat rs;
-    RowThr th;
-    finalize_row(p, row0 + r, rs, th);
-    if ((tid & (kRowGroup - 1)) == 0) {
-      sh.rs[r] = rs;
-      if (TR) sh.th[r] = th;
+  if constexpr (LAZY) {
+    if (TR && p.eta)
+      for (int i = tid; i < kExp2Tab; i += NT) lz.tab[i] = exp2((double)i / 256.0);
+  } else {
+    for (int r = tid / kRowGroup; r <= T; r += NT / kRowGroup) {
+      RowStat rs;
+      RowThr th;
+      finalize_row(p, row0 + r, rs, th);
+      if ((tid & (kRowGroup - 1)) == 0) {
+        sh.rs[r] = rs;
+        if (TR) sh.th[r] = th;
+      }
     }
   }
   __syncthreads();
@@ -681,7 +849,7 @@ __global__ __launch_bounds__(NT) void walk_kernel(SampleParams p) {
     sh.qx[tid] = (p.greedy || p.det) ? 0.f : p.q[r * V + sh.tok[tid]];
   }
   __syncthreads();
-  if (p.det && !p.greedy && tid < T) {
+  if (!LAZY && p.det && !p.greedy && tid < T) {
     // the token's unnormalised target mass, in the same terms as the sum it
     // will be taken out of: under truncation the visit pass's fp32 weight
     // relative to the row maximum; otherwise the row statistics' weight
@@ -748,6 +916,54 @@ __global__ __launch_bounds__(NT) void walk_kernel(SampleParams p) {
     const int64_t row = row0 + r;
     const float* lrow = p.logits + row * V;
     const float* qrow = (p.greedy || !p.q) ? nullptr : p.q + row * V;
+    if constexpr (LAZY) {
+      // this row's statistics (each wave takes chunks wave, wave + NW, ...),
+      // then its normalisation, then the deterministic candidates' masses of
+      // the children of this position: what the row-statistics pass and the
+      // walk's start do for every row in the other form
+      constexpr int NW = NT / kWave;
+      const int wave = tid >> 6;
+      const float* base = uniform_ptr(lrow);
+      for (int ch = wave; ch < p.nch; ch += NW) {
+        ChunkStat cs;
+        double2 se;
+        if (p.greedy) chunk_stat<true, VEC, false>(base, p.V, ch, p.c, p.c64, lz.tab, cs, se);
+        else if (TR && p.eta) chunk_stat<false, VEC, TR>(base, p.V, ch, p.c, p.c64, lz.tab, cs, se);
+        else chunk_stat<false, VEC, false>(base, p.V, ch, p.c, p.c64, lz.tab, cs, se);
+        if (lane == 0) {
+          lz.cst[ch] = cs;
+          if (TR) lz.cent[ch] = se;
+        }
+      }
+      __syncthreads();
+      if (tid < kWave) {
+        RowStat rs;
+        RowThr th;
+        finalize_row_wave(p, lz.cst, lz.cent, rs, th);
+        if (tid == 0) {
+          sh.rs[r] = rs;
+          if (TR) sh.th[r] = th;
+        }
+      }
+      __syncthreads();
+      if (p.det && !p.greedy) {
+        if (tid < T && sh.par[tid] == pos) {
+          const float lx = sh.lgx[tid];
+          const RowStat rs = sh.rs[r];
+          double wx;
+          if (TR) {
+            wx = (double)allowed<TR>(target_weight(lx, rs.lmax, p.c), lx, rs.lmax, sh.th[r]);
+          } else {
+            const ChunkStat cs = lz.cst[sh.tok[tid] / kChunk];
+            wx = cs.lmax == -INFINITY ? 0.0
+                                      : (double)target_weight(lx, cs.lmax, p.c) *
+                                            exp2((double)(cs.lmax - rs.lmax) * (double)p.c);
+          }
+          sh.wx[tid] = wx;
+        }
+        __syncthreads();
+      }
+    }
     const RowStat st = sh.rs[r];
     const RowThr th = TR ? sh.th[r] : RowThr{};  // this row's threshold of the allowed set
     // children of pos in increasing index: the same ballot in every wave
@@ -865,7 +1081,7 @@ __global__ __launch_bounds__(NT) void walk_kernel(SampleParams p) {
       // (from the row statistics, or this position's pass under truncation)
       // minus the removed weights
       if (!TR) {
-        const ChunkStat* cs = p.stats + row * p.nch;
+        const ChunkStat* cs = LAZY ? (const ChunkStat*)lz.cst : p.stats + row * p.nch;
         for (int ch = tid; ch < p.nch; ch += NT) {
           const ChunkStat s = cs[ch];
           sh.csum[ch] = s.lmax == -INFINITY ? 0.0 : s.s * exp2((double)(s.lmax - st.lmax) * (double)p.c);
@@ -931,7 +1147,7 @@ __global__ __launch_bounds__(NT) void walk_kernel(SampleParams p) {
     if (level == 0 && TR) {  // the chunk masses of p_Theta from this position's pass
       total = Srow;
     } else if (level == 0) {
-      const ChunkStat* cs = p.stats + row * p.nch;
+      const ChunkStat* cs = LAZY ? (const ChunkStat*)lz.cst : p.stats + row * p.nch;
       for (int ch = tid; ch < p.nch; ch += NT) {
         const ChunkStat s = cs[ch];
         sh.csum[ch] = s.lmax == -INFINITY ? 0.0 : s.s * exp2((double)(s.lmax - st.lmax) * (double)p.c);
@@ -963,25 +1179,31 @@ hipError_t launch_sampler(const SampleParams& p, bool vec4, hipStream_t stream, 
   if (p.B <= 0) return hipSuccess;
   const int64_t rows = (int64_t)p.N + p.B;
   const int64_t items = rows * p.nch;
-  const int nsb = (int)((items + 3) / 4);  // statistics blocks; the step's merge blocks follow
+  // the walk computes the statistics of the rows it reaches itself (one
+  // workgroup per request, and the p rows are not an output): no statistics
+  // blocks, only the step's merge blocks if any
+  const bool lazy = p.slices == 1 && !p.probs_out;
+  const int nsb = lazy ? 0 : (int)((items + 3) / 4);  // statistics blocks; the step's merge blocks follow
   const dim3 sgrid((unsigned)(nsb + p.merge.blocks));
-  const dim3 pgrid((unsigned)nsb);         // the p-row output (one wave per (row, chunk) as well)
+  const dim3 pgrid((unsigned)((items + 3) / 4));     // the p-row output (one wave per (row, chunk) as well)
   int32_t* xc = p.slices > 1 ? p.xcnt : nullptr;
   const int ns = p.B * kWalkSync;
   if (ev.start) (void)hipEventRecord(ev.start, stream);
-  if (p.greedy) {
-    if (vec4) row_stats_kernel<true, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, p.status, xc, ns, p.merge, nsb);
-    else row_stats_kernel<true, false><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, p.status, xc, ns, p.merge, nsb);
-  } else if (p.eta) {
-    if (vec4)
-      row_stats_kernel<false, true, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, p.status,
-                                                                    xc, ns, p.merge, nsb, p.ent, p.c64);
-    else
-      row_stats_kernel<false, false, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats,
-                                                                     p.status, xc, ns, p.merge, nsb, p.ent, p.c64);
-  } else {
-    if (vec4) row_stats_kernel<false, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, p.status, xc, ns, p.merge, nsb);
-    else row_stats_kernel<false, false><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, p.status, xc, ns, p.merge, nsb);
+  if (sgrid.x > 0) {
+    if (p.greedy) {
+      if (vec4) row_stats_kernel<true, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, xc, ns, p.merge, nsb);
+      else row_stats_kernel<true, false><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, xc, ns, p.merge, nsb);
+    } else if (p.eta) {
+      if (vec4)
+        row_stats_kernel<false, true, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, xc,
+                                                                      ns, p.merge, nsb, p.ent, p.c64);
+      else
+        row_stats_kernel<false, false, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, xc,
+                                                                       ns, p.merge, nsb, p.ent, p.c64);
+    } else {
+      if (vec4) row_stats_kernel<false, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, xc, ns, p.merge, nsb);
+      else row_stats_kernel<false, false><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, xc, ns, p.merge, nsb);
+    }
   }
   if (ev.stats_stop) (void)hipEventRecord(ev.stats_stop, stream);
   hipError_t err = hipGetLastError();
@@ -1002,6 +1224,14 @@ hipError_t launch_sampler(const SampleParams& p, bool vec4, hipStream_t stream, 
     } else {
       if (vec4) walk_kernel<true, 256, false><<<grid, dim3(256), 0, stream>>>(p);
       else walk_kernel<false, 256, false><<<grid, dim3(256), 0, stream>>>(p);
+    }
+  } else if (lazy) {
+    if (p.trunc) {
+      if (vec4) walk_kernel<true, 512, true, true><<<dim3(p.B), dim3(512), 0, stream>>>(p);
+      else walk_kernel<false, 512, true, true><<<dim3(p.B), dim3(512), 0, stream>>>(p);
+    } else {
+      if (vec4) walk_kernel<true, 512, false, true><<<dim3(p.B), dim3(512), 0, stream>>>(p);
+      else walk_kernel<false, 512, false, true><<<dim3(p.B), dim3(512), 0, stream>>>(p);
     }
   } else {
     if (p.trunc) {
