@@ -577,11 +577,10 @@ def main():
     # candidates and the truncation rule's membership tests need none (the
     # truncation visit and redraw passes are not counted here)
     per_pass = 0 if det or args.rule == "truncation" else 8 * w["V"]
-    # the walk's layout: with one workgroup per request it computes the
-    # statistics of the rows it reaches itself and reads no other row; the
-    # sliced walk reads every row in a statistics pass first
-    slices = s.walk_slices()
-    lazy = slices == 1
+    # the walk's layout: workgroups per request, and whether it computes the
+    # statistics of the rows it reaches itself (reading no other row) or has a
+    # statistics pass read every row first
+    slices, lazy = s.walk_layout()
     # rows a walk reaches: the root's and one per accepted node (each read
     # whole, for its normaliser or argmax), averaged over the input sets
     visited_mean = sum(float((c[1].accept_len.double() + 1).sum().item()) for c in calls) / len(calls)
@@ -598,15 +597,17 @@ def main():
         walk_ms = smp_ms - rs_ms
         if lazy:
             # the row-statistics launch then holds only the attention's split-K
-            # merge blocks (none when the attention is not split)
-            kernels["row_stats_kernel"] = {"us": rs_ms * 1e3, "merge_only": True}
-            kernels["walk_kernel"] = {"us": walk_ms * 1e3, "alg_bytes": smp_b, "GB_s": smp_b / walk_ms / 1e6}
+            # merge blocks (none when the attention is not split) and the
+            # clearing of the sliced walk's coordination words
+            kernels["row_stats_kernel"] = {"us": rs_ms * 1e3, "statistics": False}
+            kernels["walk_kernel"] = {"us": walk_ms * 1e3, "alg_bytes": smp_b, "GB_s": smp_b / walk_ms / 1e6,
+                                      "slices": slices}
         else:
             kernels["row_stats_kernel"] = {"us": rs_ms * 1e3, "alg_bytes": rs_b, "GB_s": rs_b / rs_ms / 1e6}
             kernels["walk_kernel"] = {"us": walk_ms * 1e3, "slices": slices}
         # the whole sampler on its algorithmic bytes: the logit rows the walk
         # reaches, plus the residual passes it made (logits and q of the
-        # rejected row); the sliced layout reads every row besides
+        # rejected row); a statistics pass over every row reads more
         kernels["sampler(stats+finalize+walk)"] = {
             "us": smp_ms * 1e3, "alg_bytes": smp_b, "GB_s": smp_b / smp_ms / 1e6,
             "frac": smp_b / smp_ms / 1e6 / HBM_PEAK_GBS, "rows_reached": visited_mean,
@@ -671,7 +672,7 @@ def main():
         "cpu_baseline": cpu,
         "near_ties": parity,
         "input_sets": n_sets,
-        "walk_slices": slices,
+        "walk_layout": {"slices": slices, "reached_rows_only": lazy},
         **({"input_sha256_16": input_sha} if input_sha else {}),
         **({"hip_graph": True} if args.graph else {}),
         "kernels": {k: {kk: (round(vv, 4 if kk == "frac" else 2) if isinstance(vv, float) else vv)

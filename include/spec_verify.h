@@ -363,14 +363,17 @@ sv_status spec_verify_attn(const sv_attn_args* attn, void* ws, size_t ws_bytes, 
 /* Rejection-sampling walk. ws as above with spec_verify_workspace_size(NULL, sample). */
 sv_status spec_verify_sample(const sv_sample_args* sample, void* ws, size_t ws_bytes, void* stream);
 
-/* Workgroups per request of spec_verify_sample's walk for these arguments
- * (host-visible fields only; under SV_WALK_AUTO also the current device's
- * CU count and occupancy): 1, or 2..8 for the sliced walk. With 1 and no
- * probs_out the walk computes the statistics of the logit rows it reaches
- * by itself and reads no other row; otherwise a statistics pass reads every
- * row of the batch first. 0 on invalid arguments, with the last error set.
- * A query for callers that account for the walk's memory traffic.          */
-int32_t spec_verify_walk_slices(const sv_sample_args* sample);
+/* Layout of spec_verify_sample's walk for these arguments (host-visible
+ * fields only; under SV_WALK_AUTO also the current device's CU count and
+ * occupancy), for callers that account for the walk's memory traffic.
+ *   *slices: workgroups per request, 1, or 2..8 for the sliced walk;
+ *   *reached_rows_only: 1 when the walk computes the statistics of the logit
+ *     rows it reaches by itself and reads no other row (no probs_out, and the
+ *     N + B rows hold at least 128 MiB of logits), 0 when a statistics pass
+ *     reads every row first. Results are bitwise the same either way.
+ * Either pointer may be NULL. Returns SV_OK, or the error of invalid
+ * arguments (with the last error set); nothing runs on the device.        */
+sv_status spec_verify_walk_layout(const sv_sample_args* sample, int32_t* slices, int32_t* reached_rows_only);
 
 /* Attention then sampling on one stream; the two argument sets must describe
  * the same batch (B, total_nodes, cu_nodes). ws: spec_verify_workspace_size(attn, sample). */

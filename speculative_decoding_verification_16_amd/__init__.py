@@ -84,8 +84,8 @@ def load_library(path: str = LIB_PATH):
     lib.spec_verify_step_timed.restype = ctypes.c_int
     lib.spec_verify_step_noalloc.argtypes = [_P, _P, _P]
     lib.spec_verify_step_noalloc.restype = ctypes.c_int
-    lib.spec_verify_walk_slices.argtypes = [_P]
-    lib.spec_verify_walk_slices.restype = _i32
+    lib.spec_verify_walk_layout.argtypes = [_P, _P, _P]
+    lib.spec_verify_walk_layout.restype = ctypes.c_int
     lib.spec_verify_last_error.argtypes = []
     lib.spec_verify_last_error.restype = ctypes.c_char_p
     lib.spec_verify_struct_size.argtypes = [_i32]
@@ -275,16 +275,12 @@ class SampleCall:
             r["residual_passes"] = self.passes
         return r
 
-    def walk_slices(self) -> int:
-        """spec_verify_walk_slices: workgroups per request of the walk for these
-        arguments on the current device. With 1 and no probs output the walk
-        reads only the logit rows it reaches; otherwise every row is read by a
-        statistics pass first."""
-        lib = load_library()
-        n = lib.spec_verify_walk_slices(ctypes.byref(self.args))
-        if n <= 0:
-            raise SpecVerifyError(SV_ERR_INVALID_ARG, lib.spec_verify_last_error().decode())
-        return int(n)
+    def walk_layout(self) -> tuple:
+        """spec_verify_walk_layout on the current device: (workgroups per
+        request, whether the walk reads only the logit rows it reaches)."""
+        n, lazy = _i32(0), _i32(0)
+        _check(load_library().spec_verify_walk_layout(ctypes.byref(self.args), ctypes.byref(n), ctypes.byref(lazy)))
+        return int(n.value), bool(lazy.value)
 
     def __call__(self, stream=None):
         _check(load_library().spec_verify_sample(ctypes.byref(self.args), _ptr(self.ws), self.ws_bytes,

@@ -102,6 +102,7 @@ struct SampleParams {
   ChunkStat* stats;         // [N+B, nch] workspace
   RowStat* rowstats;        // [N+B] workspace
   int32_t slices;           // workgroups per request in the walk (1: no exchange)
+  int32_t lazy;             // the walk computes the statistics of the rows it reaches (no statistics pass)
   double* xs;               // [B, 2, 2 nch] workspace when slices > 1
   int32_t* xcnt;            // [B, kWalkSync] workspace when slices > 1 (zeroed by the sampler)
   uint32_t join_ticks;      // start-up window of a request's slices (100 MHz ticks; 0: none, the

@@ -166,7 +166,8 @@ template <bool GREEDY, bool VEC, bool ENT = false>
 __global__ __launch_bounds__(256) void row_stats_kernel(const float* __restrict__ logits, int V, int64_t rows,
                                                         int nch, float c, ChunkStat* __restrict__ stats,
                                                         int32_t* xcnt, int nsync, MergeArgs merge, int stat_blocks,
-                                                        double2* __restrict__ ent = nullptr, double c64 = 0.0) {
+                                                        int64_t stat_items, double2* __restrict__ ent = nullptr,
+                                                        double c64 = 0.0) {
   // blocks past the statistics merge the step's split-K attention partials
   // (one launch fewer; the work is independent of the statistics)
   if ((int)blockIdx.x >= stat_blocks) {
@@ -184,7 +185,7 @@ __global__ __launch_bounds__(256) void row_stats_kernel(const float* __restrict_
     tab[threadIdx.x] = exp2((double)threadIdx.x / 256.0);
     __syncthreads();  // before any thread leaves
   }
-  if (item >= rows * nch) return;
+  if (item >= stat_items) return;  // 0 when the walk computes its rows' statistics (then only the clearing)
   const int64_t row = item / nch;
   const int ch = (int)(item - row * nch);
   ChunkStat st;
@@ -510,6 +511,26 @@ __device__ __forceinline__ void publish(double* dst, double v) {
   __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Barrier of a request's slices (the pass_no-th of the request): this
+// workgroup's stores are complete before it counts itself in, so a slice that
+// has seen every arrival reads every slice's device-coherent stores.
+__device__ __forceinline__ void slice_barrier(const Slices& sl, int pass_no) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(sl.cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int target = sl.n * pass_no;
+    for (int spin = 0; __hip_atomic_load(sl.cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target; ++spin) {
+      if (spin >= kSpinLimit) {  // cannot happen while all slices are resident; never wait forever
+        flag(sl.status, kStSync);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  __syncthreads();
+}
+
 // Vocabulary pass of the request's workgroups: csum[ch] = mass of chunk ch
 // under max(0, p - cc q) (its two halves added in order); returns the total
 // (bitwise the same in every thread of every slice). pass_no counts the
@@ -577,20 +598,7 @@ __device__ __forceinline__ double residual_pass(WalkShared<NT>& sh, const float*
     // the L2 either); the wait before the arrival makes sure this wave's
     // stores have completed, so a slice that sees every arrival reads every
     // slice's masses.
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      __hip_atomic_fetch_add(sl.cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const int target = sl.n * pass_no;
-      for (int spin = 0; __hip_atomic_load(sl.cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target; ++spin) {
-        if (spin >= kSpinLimit) {  // cannot happen while all slices are resident; never wait forever
-          flag(sl.status, kStSync);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-      }
-    }
-    __syncthreads();
+    slice_barrier(sl, pass_no);
     for (int h = threadIdx.x; h < nh; h += NT)
       sh.hsum[h] = __hip_atomic_load(xb + h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -753,24 +761,42 @@ __device__ __forceinline__ void skip_request(const SampleParams& p, int b, int32
 }
 
 // The current row's chunk records when the walk computes the statistics of
-// the rows it reaches (LAZY), and the 2^(j/256) table of the eta sums.
-template <bool ON>
+// the rows it reaches (LAZY), and the eta sums' records and 2^(j/256) table
+// (TR: truncation forms only).
+template <bool ON, bool TR>
 struct LazyRow {
   ChunkStat cst[ON ? kMaxChunks : 1];
-  double2 cent[ON ? kMaxChunks : 1];
-  double tab[ON ? kExp2Tab : 1];
+  double2 cent[ON && TR ? kMaxChunks : 1];
+  double tab[ON && TR ? kExp2Tab : 1];
 };
 
-// LAZY (one workgroup per request, no p-row output): no row-statistics pass
-// runs before the walk; the walk computes the statistics of each row when it
-// reaches it, with the row-statistics kernel's per-chunk code, so the rows
-// it never reaches (those after a rejected node) are not read at all and
-// the results are bitwise those of the other form.
+// A chunk record of the row being reached, for the request's other slices:
+// device-coherent 8-byte stores into the workspace's statistics, read back
+// after the slice barrier with device-coherent loads.
+__device__ __forceinline__ void publish_chunk(ChunkStat* dst, const ChunkStat& cs) {
+  uint64_t w0;
+  __builtin_memcpy(&w0, &cs, 8);
+  __hip_atomic_store((uint64_t*)dst, w0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(&dst->s, cs.s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ ChunkStat fetch_chunk(ChunkStat* src) {
+  ChunkStat cs;
+  const uint64_t w0 = __hip_atomic_load((uint64_t*)src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_memcpy(&cs, &w0, 8);
+  cs.s = __hip_atomic_load(&src->s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return cs;
+}
+
+// LAZY (no p-row output): no row-statistics pass runs before the walk; the
+// walk computes the statistics of each row when it reaches it, with the
+// row-statistics kernel's per-chunk code, so the rows it never reaches (those
+// after a rejected node) are not read at all and the results are bitwise
+// those of the other form. A sliced request splits each row's chunks over
+// all its slices' waves and exchanges the records at a slice barrier.
 template <bool VEC, int NT, bool TR, bool LAZY = false>
-__global__ __launch_bounds__(NT) void walk_kernel(SampleParams p) {
-  static_assert(!LAZY || NT == 512, "the lazy form is the one-workgroup walk");
+__global__ __launch_bounds__(NT, 2) void walk_kernel(SampleParams p) {  // 2 waves per SIMD: two 256-thread slices per CU
   __shared__ WalkShared<NT> sh;
-  __shared__ LazyRow<LAZY> lz;
+  __shared__ LazyRow<LAZY, TR> lz;
   const int b = blockIdx.x / p.slices, slice = blockIdx.x - b * p.slices;
   int32_t* sync = p.slices > 1 ? p.xcnt + (int64_t)b * kWalkSync : nullptr;  // [0] passes, [1] arrivals, [2] mode
   if (sync && threadIdx.x == 0) __hip_atomic_fetch_add(sync + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -923,16 +949,36 @@ __global__ __launch_bounds__(NT) void walk_kernel(SampleParams p) {
       // walk's start do for every row in the other form
       constexpr int NW = NT / kWave;
       const int wave = tid >> 6;
+      const int gw = sl.id * NW + wave, GW = sl.n * NW;  // this wave among all the request's waves
       const float* base = uniform_ptr(lrow);
-      for (int ch = wave; ch < p.nch; ch += NW) {
+      ChunkStat* gst = p.stats + row * p.nch;
+      double2* gent = TR && p.eta ? p.ent + row * p.nch : nullptr;
+      for (int ch = gw; ch < p.nch; ch += GW) {
         ChunkStat cs;
         double2 se;
         if (p.greedy) chunk_stat<true, VEC, false>(base, p.V, ch, p.c, p.c64, lz.tab, cs, se);
         else if (TR && p.eta) chunk_stat<false, VEC, TR>(base, p.V, ch, p.c, p.c64, lz.tab, cs, se);
         else chunk_stat<false, VEC, false>(base, p.V, ch, p.c, p.c64, lz.tab, cs, se);
         if (lane == 0) {
-          lz.cst[ch] = cs;
-          if (TR) lz.cent[ch] = se;
+          if (sl.n > 1) {
+            publish_chunk(gst + ch, cs);
+            if (gent) {
+              publish(&gent[ch].x, se.x);
+              publish(&gent[ch].y, se.y);
+            }
+          } else {
+            lz.cst[ch] = cs;
+            if (TR) lz.cent[ch] = se;
+          }
+        }
+      }
+      if (sl.n > 1) {
+        slice_barrier(sl, ++npass);
+        for (int ch = tid; ch < p.nch; ch += NT) {
+          lz.cst[ch] = fetch_chunk(gst + ch);
+          if (gent)
+            lz.cent[ch] = make_double2(__hip_atomic_load(&gent[ch].x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                                       __hip_atomic_load(&gent[ch].y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
         }
       }
       __syncthreads();
@@ -1179,30 +1225,31 @@ hipError_t launch_sampler(const SampleParams& p, bool vec4, hipStream_t stream, 
   if (p.B <= 0) return hipSuccess;
   const int64_t rows = (int64_t)p.N + p.B;
   const int64_t items = rows * p.nch;
-  // the walk computes the statistics of the rows it reaches itself (one
-  // workgroup per request, and the p rows are not an output): no statistics
-  // blocks, only the step's merge blocks if any
-  const bool lazy = p.slices == 1 && !p.probs_out;
-  const int nsb = lazy ? 0 : (int)((items + 3) / 4);  // statistics blocks; the step's merge blocks follow
+  // when the walk computes the statistics of the rows it reaches itself: no
+  // statistics blocks, only the clearing of the sliced walk's coordination
+  // words and the step's merge blocks, if any
+  const bool lazy = p.lazy != 0;
+  const int ns = p.B * kWalkSync;
+  int32_t* xc = p.slices > 1 ? p.xcnt : nullptr;
+  const int64_t stat_items = lazy ? 0 : items;
+  const int nsb = lazy ? (xc ? (ns + 255) / 256 : 0) : (int)((items + 3) / 4);  // the merge blocks follow
   const dim3 sgrid((unsigned)(nsb + p.merge.blocks));
   const dim3 pgrid((unsigned)((items + 3) / 4));     // the p-row output (one wave per (row, chunk) as well)
-  int32_t* xc = p.slices > 1 ? p.xcnt : nullptr;
-  const int ns = p.B * kWalkSync;
   if (ev.start) (void)hipEventRecord(ev.start, stream);
   if (sgrid.x > 0) {
     if (p.greedy) {
-      if (vec4) row_stats_kernel<true, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, xc, ns, p.merge, nsb);
-      else row_stats_kernel<true, false><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, xc, ns, p.merge, nsb);
+      if (vec4) row_stats_kernel<true, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, xc, ns, p.merge, nsb, stat_items);
+      else row_stats_kernel<true, false><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, xc, ns, p.merge, nsb, stat_items);
     } else if (p.eta) {
       if (vec4)
         row_stats_kernel<false, true, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, xc,
-                                                                      ns, p.merge, nsb, p.ent, p.c64);
+                                                                      ns, p.merge, nsb, stat_items, p.ent, p.c64);
       else
         row_stats_kernel<false, false, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, xc,
-                                                                       ns, p.merge, nsb, p.ent, p.c64);
+                                                                       ns, p.merge, nsb, stat_items, p.ent, p.c64);
     } else {
-      if (vec4) row_stats_kernel<false, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, xc, ns, p.merge, nsb);
-      else row_stats_kernel<false, false><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, xc, ns, p.merge, nsb);
+      if (vec4) row_stats_kernel<false, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, xc, ns, p.merge, nsb, stat_items);
+      else row_stats_kernel<false, false><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, xc, ns, p.merge, nsb, stat_items);
     }
   }
   if (ev.stats_stop) (void)hipEventRecord(ev.stats_stop, stream);
@@ -1218,12 +1265,22 @@ hipError_t launch_sampler(const SampleParams& p, bool vec4, hipStream_t stream, 
   }
   if (p.slices > 1) {
     const dim3 grid((unsigned)(p.B * p.slices));
-    if (p.trunc) {
-      if (vec4) walk_kernel<true, 256, true><<<grid, dim3(256), 0, stream>>>(p);
-      else walk_kernel<false, 256, true><<<grid, dim3(256), 0, stream>>>(p);
+    if (lazy) {
+      if (p.trunc) {
+        if (vec4) walk_kernel<true, 256, true, true><<<grid, dim3(256), 0, stream>>>(p);
+        else walk_kernel<false, 256, true, true><<<grid, dim3(256), 0, stream>>>(p);
+      } else {
+        if (vec4) walk_kernel<true, 256, false, true><<<grid, dim3(256), 0, stream>>>(p);
+        else walk_kernel<false, 256, false, true><<<grid, dim3(256), 0, stream>>>(p);
+      }
     } else {
-      if (vec4) walk_kernel<true, 256, false><<<grid, dim3(256), 0, stream>>>(p);
-      else walk_kernel<false, 256, false><<<grid, dim3(256), 0, stream>>>(p);
+      if (p.trunc) {
+        if (vec4) walk_kernel<true, 256, true><<<grid, dim3(256), 0, stream>>>(p);
+        else walk_kernel<false, 256, true><<<grid, dim3(256), 0, stream>>>(p);
+      } else {
+        if (vec4) walk_kernel<true, 256, false><<<grid, dim3(256), 0, stream>>>(p);
+        else walk_kernel<false, 256, false><<<grid, dim3(256), 0, stream>>>(p);
+      }
     }
   } else if (lazy) {
     if (p.trunc) {
@@ -1271,9 +1328,11 @@ int walk_slices(int B, int nch, bool passes, int mode) {
   if (per_cu_cached[dev] == 0) {
     int a = 0, b = 0;
     int t = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, walk_kernel<true, 256, false>, 256, 0) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, walk_kernel<false, 256, false>, 256, 0) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&t, walk_kernel<true, 256, true>, 256, 0) != hipSuccess) {
+    // (the forms launched without the p-row output, the usual case: their
+    // LDS holds a row's chunk records besides)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, walk_kernel<true, 256, false, true>, 256, 0) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, walk_kernel<false, 256, false, true>, 256, 0) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&t, walk_kernel<true, 256, true, true>, 256, 0) != hipSuccess) {
       (void)hipGetLastError();
       a = b = t = 0;
     }

@@ -252,6 +252,32 @@ def test_walk_layouts_full_size_bitwise(name, mode):
         assert torch.equal(r[k], ref[k]), k
 
 
+@pytest.mark.parametrize("siblings", ["sampled", "deterministic"])
+@pytest.mark.parametrize("name", ["c3_eagle_tree", "c5_super_tree"])
+def test_reached_rows_match_statistics_pass(name, siblings):
+    """The walk that reduces only the rows it reaches (the default at these
+    sizes: sliced for the 16-request trees with sampled siblings, one
+    workgroup per request otherwise) and the walk after a statistics pass over
+    every row (forced by asking for the p rows) give bitwise the same
+    outputs."""
+    cfg = get_config(name)
+    w = generate(cfg, "cuda", attn=False)
+    kw = {"siblings": siblings}
+    call = sv.SampleCall(w["cu_nodes_t"], w["parent_t"], w["draft_tokens"], w["logits"], w["draft_probs"],
+                         temperature=cfg.temperature, seed=w["seed"], max_nodes=w["max_T"], **kw)
+    slices, lazy = call.walk_layout()
+    print(f"[reached-rows] {name} {siblings} B={w['B']} slices={slices} reached_rows_only={lazy}", flush=True)
+    assert lazy
+    if siblings == "sampled":
+        assert slices == (1 if name == "c5_super_tree" else 8)
+    ref = _gpu_sample(w, cfg.temperature, **kw)
+    r = _gpu_sample(w, cfg.temperature, probs_out=True, **kw)
+    for x in (ref, r):
+        assert int(x["status"].item()) == 0, sv.status_names(int(x["status"].item()))
+    for k in ("accept_len", "accepted_nodes", "out_tokens", "uniforms", "residual_passes"):
+        assert torch.equal(r[k], ref[k]), k
+
+
 @pytest.mark.skip(reason=BOARD_SKIP)
 def test_walk_board_full_batch_matches_single():
     # the batch-256 super tree used the help board by default
