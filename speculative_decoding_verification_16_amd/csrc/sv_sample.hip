@@ -243,15 +243,18 @@ __device__ __forceinline__ void finalize_row(const SampleParams& p, int64_t row,
   finalize_row_from(p, p.stats + row * p.nch, p.ent ? p.ent + row * p.nch : nullptr, r, thr);
 }
 
-// finalize_row_from computed by a whole wave, for the lazy walk's single row:
-// every lane takes chunks lane, lane + 64, ... for the maximum, the argmax and
-// the per-chunk fp64 factors (the exp2 of each chunk's offset from the row
-// maximum, all in parallel); the fmas then run in exactly the order of the
-// 4-lane group (lane gl takes chunks gl, gl + 4, ... in turn, then the
-// group's butterfly), so every value is bitwise that of finalize_row_from.
-// All 64 lanes call it; lanes 0..3 hold the results.
+// finalize_row_from computed by a whole wave, for the row a lazy walk has
+// just reduced: every lane takes chunks lane, lane + 64, ... for the maximum
+// (and, greedy, the argmax) and then for the per-chunk fp64 factors (the
+// exp2 of each chunk's offset from the row maximum, all in parallel), which
+// it leaves in LDS (f0, f1: nch doubles each; fsc: the eta set's exp2). The
+// first four lanes then run the fmas in exactly the order of the 4-lane
+// group (lane gl takes chunks gl, gl + 4, ... in turn, then the group's
+// butterfly), so every value is bitwise that of finalize_row_from (a chunk
+// with no finite logit has factors 0 and 0, and fma(0, 0, acc) is acc). All
+// 64 lanes of one wave call it; lanes 0..3 hold the results.
 __device__ __forceinline__ void finalize_row_wave(const SampleParams& p, const ChunkStat* st, const double2* ent,
-                                                  RowStat& r, RowThr& thr) {
+                                                  double* f0, double* f1, double* fsc, RowStat& r, RowThr& thr) {
   const int lane = threadIdx.x & (kWave - 1);
   const int gl = lane & (kRowGroup - 1);
   const int nch = p.nch;
@@ -259,12 +262,14 @@ __device__ __forceinline__ void finalize_row_wave(const SampleParams& p, const C
   int ai = 0x7fffffff;
   bool bad = false;
   for (int ch = lane; ch < nch; ch += kWave) row_norm_acc(st[ch], m, av, ai, bad);
+  m = wave_max(m);
+  if (p.greedy) {  // the argmax is read by greedy walks only
 #pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) {
-    m = fmaxf(m, __shfl_xor(m, o));
-    const float ov = __shfl_xor(av, o);
-    const int oi = __shfl_xor(ai, o);
-    if (ov > av || (ov == av && oi < ai)) { av = ov; ai = oi; }
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(av, o);
+      const int oi = __shfl_xor(ai, o);
+      if (ov > av || (ov == av && oi < ai)) { av = ov; ai = oi; }
+    }
   }
   thr = p.mp_thr;
   if (__any(bad)) {
@@ -274,46 +279,32 @@ __device__ __forceinline__ void finalize_row_wave(const SampleParams& p, const C
     return;
   }
   const bool eta = p.eta && m != -INFINITY;
-  double acc = 0.0, accS = 0.0, accE = 0.0;
   if (m != -INFINITY) {
-    for (int b0 = 0; b0 < nch; b0 += kWave) {
-      // this lane's chunk of the block: its terms (0 for a chunk with no
-      // finite logit, which adds nothing to a sum that starts at +0)
-      const int ch = b0 + lane;
-      // (the factors of each fma, so that the sums below are formed exactly
-      // as the group forms them)
-      double cs_s = 0.0, e = 0.0, sc = 0.0, sex = 0.0, inner = 0.0;
-      bool live = false;
-      if (ch < nch) {
+    for (int ch = lane; ch < nch; ch += kWave) {
+      const ChunkStat cs = st[ch];
+      const bool live = cs.lmax != -INFINITY;
+      f0[ch] = live ? cs.s : 0.0;
+      f1[ch] = live ? exp2((double)(cs.lmax - m) * (double)p.c) : 0.0;
+      if (eta) fsc[ch] = live ? exp2(((double)cs.lmax - (double)m) * p.c64) : 0.0;
+    }
+  }
+  // the wave's own LDS stores, read back by its first four lanes (one wave
+  // executes its LDS operations in order; the fences keep the compiler's
+  // order)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  double acc = 0.0, accS = 0.0, accE = 0.0;
+  if (m != -INFINITY && lane < kRowGroup) {
+    for (int ch = gl; ch < nch; ch += kRowGroup) acc = fma(f0[ch], f1[ch], acc);
+    if (eta) {
+      for (int ch = gl; ch < nch; ch += kRowGroup) {
         const ChunkStat cs = st[ch];
         if (cs.lmax != -INFINITY) {
-          live = true;
-          cs_s = cs.s;
-          e = exp2((double)(cs.lmax - m) * (double)p.c);
-          if (eta) {
-            const double dl = ((double)cs.lmax - (double)m) * p.c64;
-            const double2 se = ent[ch];
-            sc = exp2(dl);
-            sex = se.x;
-            inner = fma(dl, se.x, se.y);
-          }
-        }
-      }
-      // the group's order: lane gl takes chunks b0 + gl, b0 + gl + 4, ...
-      // (a chunk with no finite logit is skipped, as the group skips it)
-      const int nb = min(kWave, nch - b0);
-#pragma unroll
-      for (int k = 0; k < kWave / kRowGroup; ++k) {
-        const int src = gl + kRowGroup * k;
-        const bool use = src < nb && __shfl(live ? 1 : 0, src) != 0;
-        const double vs = __shfl(cs_s, src), ve = __shfl(e, src);
-        if (use) acc = fma(vs, ve, acc);
-        if (eta) {
-          const double vsc = __shfl(sc, src), vx = __shfl(sex, src), vin = __shfl(inner, src);
-          if (use) {
-            accS = fma(vsc, vx, accS);
-            accE = fma(vsc, vin, accE);
-          }
+          const double dl = ((double)cs.lmax - (double)m) * p.c64;
+          const double2 se = ent[ch];
+          accS = fma(fsc[ch], se.x, accS);
+          accE = fma(fsc[ch], fma(dl, se.x, se.y), accE);
         }
       }
     }
@@ -985,7 +976,9 @@ __global__ __launch_bounds__(NT, 2) void walk_kernel(SampleParams p) {  // 2 wav
       if (tid < kWave) {
         RowStat rs;
         RowThr th;
-        finalize_row_wave(p, lz.cst, lz.cent, rs, th);
+        // (scratch: the residual pass's half-chunk masses and the draw's
+        // chunk masses, both rewritten before their next use)
+        finalize_row_wave(p, lz.cst, lz.cent, sh.hsum, sh.hsum + kMaxChunks, sh.csum, rs, th);
         if (tid == 0) {
           sh.rs[r] = rs;
           if (TR) sh.th[r] = th;
