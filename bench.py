@@ -596,9 +596,9 @@ def main():
                               "TFLOP_s": attn_f / attn_ms / 1e9}
         walk_ms = smp_ms - rs_ms
         if lazy:
-            # the row-statistics launch then holds only the attention's split-K
-            # merge blocks (none when the attention is not split) and the
-            # clearing of the sliced walk's coordination words
+            # the row-statistics launch then only clears the sliced walk's
+            # coordination words (or does not run); the walk's launch also
+            # holds the attention's split-K merge blocks, if any
             kernels["row_stats_kernel"] = {"us": rs_ms * 1e3, "statistics": False}
             kernels["walk_kernel"] = {"us": walk_ms * 1e3, "alg_bytes": smp_b, "GB_s": smp_b / walk_ms / 1e6,
                                       "slices": slices}

@@ -390,9 +390,11 @@ typedef struct {
   void* attn_stop;    /* after the attention kernel (before a split merge)    */
   void* sample_start; /* before the sampler's first kernel                    */
   void* stats_stop;   /* after the row-statistics kernel (which, when the walk
-                         computes its rows' statistics itself, holds only the
-                         attention's split-K merge, if any)                   */
-  void* sample_stop;  /* after the walk (the sampler's last kernel)           */
+                         computes its rows' statistics itself, only clears the
+                         sliced walk's coordination words, or does not run) */
+  void* sample_stop;  /* after the walk (the sampler's last kernel; in the
+                         step its launch also runs the attention's split-K
+                         merge, if any, beside the walk)                      */
 } sv_timing;
 
 /* spec_verify_step that also records the events of *timing (may be NULL);

@@ -486,7 +486,7 @@ sv_status run_step(const sv_attn_args* attn, const sv_sample_args* sample, char*
   sv_status st;
   if (!allow_overlap || !step_overlapped(attn, sample)) {
     // the attention's split-K merge runs as extra blocks of the sampler's
-    // row-statistics launch (the sampler does not read the attention output)
+    // walk launch (the sampler does not read the attention output)
     sv::MergeArgs merge{};
     if ((st = run_attn(attn, ws, w, stream, (hipEvent_t)t.attn_start, (hipEvent_t)t.attn_stop, &merge)) != SV_OK)
       return st;

@@ -281,9 +281,10 @@ struct MergeArgs {
   const float2* ml_part;   // [splits, NH]
   float* out;              // [NH, D]
 };
+template <int NT = 256>
 __device__ __forceinline__ void merge_split_rows(const MergeArgs& a, int block) {
   const int lpr = a.D >> 2;  // lanes per row
-  const int item = block * (256 / lpr) + threadIdx.x / lpr;
+  const int item = block * (NT / lpr) + threadIdx.x / lpr;
   const int dl = threadIdx.x % lpr;
   if (item >= a.NH) return;
   const float4* o4 = (const float4*)a.o_part;
@@ -325,6 +326,12 @@ __host__ __device__ inline MergeArgs merge_args(int NH, int D, int splits, const
   a.ml_part = ml_part;
   a.out = out;
   return a;
+}
+// blocks of nt threads that merge_split_rows<nt> needs (0: nothing to merge)
+__host__ __device__ inline int merge_blocks(const MergeArgs& a, int nt) {
+  if (a.blocks == 0) return 0;
+  const int rows = nt / (a.D / 4);
+  return (a.NH + rows - 1) / rows;
 }
 
 }  // namespace sv

@@ -107,8 +107,8 @@ struct SampleParams {
   int32_t* xcnt;            // [B, kWalkSync] workspace when slices > 1 (zeroed by the sampler)
   uint32_t join_ticks;      // start-up window of a request's slices (100 MHz ticks; 0: none, the
                             // first slice to look walks its request alone)
-  MergeArgs merge;          // the step's split-K merge, run by extra blocks of the row-statistics
-                            // launch (blocks == 0: none)
+  MergeArgs merge;          // the step's split-K merge, run by extra blocks of the walk's launch
+                            // (blocks == 0: none)
 };
 
 // per-request words of the walk's slice coordination: pass-barrier arrivals,

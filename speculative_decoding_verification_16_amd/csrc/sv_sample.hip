@@ -165,15 +165,8 @@ __device__ __forceinline__ void chunk_stat(const float* __restrict__ base, int V
 template <bool GREEDY, bool VEC, bool ENT = false>
 __global__ __launch_bounds__(256) void row_stats_kernel(const float* __restrict__ logits, int V, int64_t rows,
                                                         int nch, float c, ChunkStat* __restrict__ stats,
-                                                        int32_t* xcnt, int nsync, MergeArgs merge, int stat_blocks,
-                                                        int64_t stat_items, double2* __restrict__ ent = nullptr,
-                                                        double c64 = 0.0) {
-  // blocks past the statistics merge the step's split-K attention partials
-  // (one launch fewer; the work is independent of the statistics)
-  if ((int)blockIdx.x >= stat_blocks) {
-    merge_split_rows(merge, (int)blockIdx.x - stat_blocks);
-    return;
-  }
+                                                        int32_t* xcnt, int nsync, int64_t stat_items,
+                                                        double2* __restrict__ ent = nullptr, double c64 = 0.0) {
   const int lane = threadIdx.x & 63;
   const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   // the sliced walk's per-request coordination words start at zero (the
@@ -788,6 +781,14 @@ template <bool VEC, int NT, bool TR, bool LAZY = false>
 __global__ __launch_bounds__(NT, 2) void walk_kernel(SampleParams p) {  // 2 waves per SIMD: two 256-thread slices per CU
   __shared__ WalkShared<NT> sh;
   __shared__ LazyRow<LAZY, TR> lz;
+  // blocks past the walk's merge the step's split-K attention partials: the
+  // walk leaves most of HBM's bandwidth and most CUs idle, and the work is
+  // independent of it (one launch fewer)
+  const int nwalk = p.B * p.slices;
+  if ((int)blockIdx.x >= nwalk) {
+    merge_split_rows<NT>(p.merge, (int)blockIdx.x - nwalk);
+    return;
+  }
   const int b = blockIdx.x / p.slices, slice = blockIdx.x - b * p.slices;
   int32_t* sync = p.slices > 1 ? p.xcnt + (int64_t)b * kWalkSync : nullptr;  // [0] passes, [1] arrivals, [2] mode
   if (sync && threadIdx.x == 0) __hip_atomic_fetch_add(sync + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1220,29 +1221,29 @@ hipError_t launch_sampler(const SampleParams& p, bool vec4, hipStream_t stream, 
   const int64_t items = rows * p.nch;
   // when the walk computes the statistics of the rows it reaches itself: no
   // statistics blocks, only the clearing of the sliced walk's coordination
-  // words and the step's merge blocks, if any
+  // words, if any
   const bool lazy = p.lazy != 0;
   const int ns = p.B * kWalkSync;
   int32_t* xc = p.slices > 1 ? p.xcnt : nullptr;
   const int64_t stat_items = lazy ? 0 : items;
-  const int nsb = lazy ? (xc ? (ns + 255) / 256 : 0) : (int)((items + 3) / 4);  // the merge blocks follow
-  const dim3 sgrid((unsigned)(nsb + p.merge.blocks));
+  const int nsb = lazy ? (xc ? (ns + 255) / 256 : 0) : (int)((items + 3) / 4);
+  const dim3 sgrid((unsigned)nsb);
   const dim3 pgrid((unsigned)((items + 3) / 4));     // the p-row output (one wave per (row, chunk) as well)
   if (ev.start) (void)hipEventRecord(ev.start, stream);
   if (sgrid.x > 0) {
     if (p.greedy) {
-      if (vec4) row_stats_kernel<true, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, xc, ns, p.merge, nsb, stat_items);
-      else row_stats_kernel<true, false><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, xc, ns, p.merge, nsb, stat_items);
+      if (vec4) row_stats_kernel<true, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, xc, ns, stat_items);
+      else row_stats_kernel<true, false><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, xc, ns, stat_items);
     } else if (p.eta) {
       if (vec4)
         row_stats_kernel<false, true, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, xc,
-                                                                      ns, p.merge, nsb, stat_items, p.ent, p.c64);
+                                                                      ns, stat_items, p.ent, p.c64);
       else
         row_stats_kernel<false, false, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, xc,
-                                                                       ns, p.merge, nsb, stat_items, p.ent, p.c64);
+                                                                       ns, stat_items, p.ent, p.c64);
     } else {
-      if (vec4) row_stats_kernel<false, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, xc, ns, p.merge, nsb, stat_items);
-      else row_stats_kernel<false, false><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, xc, ns, p.merge, nsb, stat_items);
+      if (vec4) row_stats_kernel<false, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, xc, ns, stat_items);
+      else row_stats_kernel<false, false><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, xc, ns, stat_items);
     }
   }
   if (ev.stats_stop) (void)hipEventRecord(ev.stats_stop, stream);
@@ -1256,8 +1257,9 @@ hipError_t launch_sampler(const SampleParams& p, bool vec4, hipStream_t stream, 
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
+  // the walk's grid: its workgroups, then the step's merge blocks, if any
   if (p.slices > 1) {
-    const dim3 grid((unsigned)(p.B * p.slices));
+    const dim3 grid((unsigned)(p.B * p.slices + merge_blocks(p.merge, 256)));
     if (lazy) {
       if (p.trunc) {
         if (vec4) walk_kernel<true, 256, true, true><<<grid, dim3(256), 0, stream>>>(p);
@@ -1275,21 +1277,24 @@ hipError_t launch_sampler(const SampleParams& p, bool vec4, hipStream_t stream, 
         else walk_kernel<false, 256, false><<<grid, dim3(256), 0, stream>>>(p);
       }
     }
-  } else if (lazy) {
-    if (p.trunc) {
-      if (vec4) walk_kernel<true, 512, true, true><<<dim3(p.B), dim3(512), 0, stream>>>(p);
-      else walk_kernel<false, 512, true, true><<<dim3(p.B), dim3(512), 0, stream>>>(p);
-    } else {
-      if (vec4) walk_kernel<true, 512, false, true><<<dim3(p.B), dim3(512), 0, stream>>>(p);
-      else walk_kernel<false, 512, false, true><<<dim3(p.B), dim3(512), 0, stream>>>(p);
-    }
   } else {
-    if (p.trunc) {
-      if (vec4) walk_kernel<true, 512, true><<<dim3(p.B), dim3(512), 0, stream>>>(p);
-      else walk_kernel<false, 512, true><<<dim3(p.B), dim3(512), 0, stream>>>(p);
+    const dim3 grid((unsigned)(p.B + merge_blocks(p.merge, 512)));
+    if (lazy) {
+      if (p.trunc) {
+        if (vec4) walk_kernel<true, 512, true, true><<<grid, dim3(512), 0, stream>>>(p);
+        else walk_kernel<false, 512, true, true><<<grid, dim3(512), 0, stream>>>(p);
+      } else {
+        if (vec4) walk_kernel<true, 512, false, true><<<grid, dim3(512), 0, stream>>>(p);
+        else walk_kernel<false, 512, false, true><<<grid, dim3(512), 0, stream>>>(p);
+      }
     } else {
-      if (vec4) walk_kernel<true, 512, false><<<dim3(p.B), dim3(512), 0, stream>>>(p);
-      else walk_kernel<false, 512, false><<<dim3(p.B), dim3(512), 0, stream>>>(p);
+      if (p.trunc) {
+        if (vec4) walk_kernel<true, 512, true><<<grid, dim3(512), 0, stream>>>(p);
+        else walk_kernel<false, 512, true><<<grid, dim3(512), 0, stream>>>(p);
+      } else {
+        if (vec4) walk_kernel<true, 512, false><<<grid, dim3(512), 0, stream>>>(p);
+        else walk_kernel<false, 512, false><<<grid, dim3(512), 0, stream>>>(p);
+      }
     }
   }
   if (ev.stop) (void)hipEventRecord(ev.stop, stream);
