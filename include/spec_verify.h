@@ -242,12 +242,13 @@ typedef struct {
                           H the entropy of p in nats, decided as
                           l_x - l_max >= T (ln S + ln tau) with S the row's
                           sum of exp((l - l_max)/T); the threshold is formed
-                          in fp64 per row from the row statistics pass (an
-                          extra accumulator there), whose fp32 weights put it
-                          within about 2^-24 (8 + 12 G + 3 Var + 6 G^2) T of
-                          the exact one (G = E_p[(l_max - l)/T], Var the
-                          variance of l/T under p); otherwise as min_p. Not
-                          with probs_out.                                   */
+                          in fp64 per row from per-chunk fp64 sums of fp64
+                          weights 2^y and 2^y y (y in log2 units, each
+                          weight within a few fp64 ulps), gathered with the
+                          row's statistics (by the statistics pass, or by the
+                          walk for a row it reduces itself); membership is
+                          then decided exactly as for min_p. Not with
+                          probs_out.                                         */
   float eta_delta;     /* delta of the eta set, in (0, 1] when eta_eps > 0     */
   int32_t siblings;    /* sv_siblings: how the children of a node were drafted */
   int32_t rule;        /* sv_rule (SV_RULE_LOSSLESS unless sampled siblings)   */
