@@ -284,9 +284,11 @@ sv_status hip_fail(hipError_t e, const char* what) {
 
 // defer_merge: when set, the split-K merge is described there for the
 // caller's next launch instead of being launched (the step runs it inside
-// the row-statistics launch)
+// the walk's launch). clear_words: nclear words the launch's first workgroup
+// zeroes (the step's sliced walk coordination words), or null.
 sv_status run_attn(const sv_attn_args* a, char* ws, const WsLayout& w, hipStream_t st, hipEvent_t ev_start,
-                   hipEvent_t ev_stop, sv::MergeArgs* defer_merge = nullptr) {
+                   hipEvent_t ev_stop, sv::MergeArgs* defer_merge = nullptr, int32_t* clear_words = nullptr,
+                   int nclear = 0) {
   if (a->B == 0 || a->total_nodes == 0) return SV_OK;
   const sv::AttnPlan pl = plan_attn(a);
   const int mn = eff_max_nodes(a->max_nodes);
@@ -324,6 +326,8 @@ sv_status run_attn(const sv_attn_args* a, char* ws, const WsLayout& w, hipStream
   p.v_scale = a->kv_fp8 ? a->v_scale : 1.f;
   p.scale_log2 = (float)((double)scale * (a->kv_fp8 ? (double)a->k_scale : 1.0) * 1.4426950408889634);
   p.status = a->status;
+  p.clear_words = clear_words;
+  p.nclear = nclear;
   p.block_table = a->block_table;
   p.block_size = a->block_table ? a->block_size : 0;
   p.max_blocks = a->block_table ? a->max_blocks : 0;
@@ -357,7 +361,8 @@ bool walk_lazy(const sv_sample_args* s) {
 }
 
 sv_status run_sample(const sv_sample_args* s, char* ws, const WsLayout& w, hipStream_t st,
-                     const sv::SampleEvents& ev, const sv::MergeArgs& merge = sv::MergeArgs{}) {
+                     const sv::SampleEvents& ev, const sv::MergeArgs& merge = sv::MergeArgs{},
+                     bool coord_cleared = false) {
   if (s->B == 0) return SV_OK;
   sv::SampleParams p{};
   p.merge = merge;
@@ -403,6 +408,7 @@ sv_status run_sample(const sv_sample_args* s, char* ws, const WsLayout& w, hipSt
   p.rule_param = s->rule_param;
   p.slices = walk_slices_for(s, w);
   p.lazy = walk_lazy(s) ? 1 : 0;
+  p.coord_cleared = coord_cleared ? 1 : 0;
   p.xs = w.xcnt ? (double*)(ws + w.xs) : nullptr;
   p.xcnt = w.xcnt ? (int32_t*)(ws + w.xcnt) : nullptr;
   p.join_ticks = s->join_ticks == 0 ? sv::kJoinWindow : (s->join_ticks < 0 ? 0u : (uint32_t)s->join_ticks);
@@ -486,11 +492,21 @@ sv_status run_step(const sv_attn_args* attn, const sv_sample_args* sample, char*
   sv_status st;
   if (!allow_overlap || !step_overlapped(attn, sample)) {
     // the attention's split-K merge runs as extra blocks of the sampler's
-    // walk launch (the sampler does not read the attention output)
+    // walk launch (the sampler does not read the attention output); a sliced
+    // walk without a statistics pass has its coordination words zeroed by the
+    // attention launch, which always runs when there are nodes
     sv::MergeArgs merge{};
-    if ((st = run_attn(attn, ws, w, stream, (hipEvent_t)t.attn_start, (hipEvent_t)t.attn_stop, &merge)) != SV_OK)
+    int32_t* clear = nullptr;
+    int nclear = 0;
+    if (attn->B > 0 && attn->total_nodes > 0 && sample->B > 0 && w.xcnt && walk_lazy(sample) &&
+        walk_slices_for(sample, w) > 1) {
+      clear = (int32_t*)(ws + w.xcnt);
+      nclear = sample->B * sv::kWalkSync;
+    }
+    if ((st = run_attn(attn, ws, w, stream, (hipEvent_t)t.attn_start, (hipEvent_t)t.attn_stop, &merge, clear,
+                       nclear)) != SV_OK)
       return st;
-    return run_sample(sample, ws, w, stream, sev, merge);
+    return run_sample(sample, ws, w, stream, sev, merge, clear != nullptr);
   }
   // the attention (with its own merge) on the side stream and the sampler on
   // the caller's, both from the call's start: they share only read-only
@@ -568,7 +584,8 @@ sv_status spec_verify_step_noalloc(const sv_attn_args* attn, const sv_sample_arg
   char* ws = nullptr;
   if ((st = scratch_for_current_device(&ws)) != SV_OK) return st;
   // the kernels write every scratch word they later read (the walk's slice
-  // counters are cleared by the row-statistics kernel of the same call), so
+  // counters are cleared by an earlier kernel of the same call: the
+  // attention launch, or the row-statistics launch), so
   // the previous call's contents need no clearing. One stream only: the
   // overlapped schedule's side stream would be created on first use.
   if (attn->B != sample->B || attn->total_nodes != sample->total_nodes || attn->cu_nodes != sample->cu_nodes)

@@ -238,6 +238,14 @@ __device__ __forceinline__ void attn_plan(const AttnParams& p, int32_t* items, i
   if (k == 0) item_tot[x] = carry;
 }
 
+// Inside the step, the attention launch that precedes the walk on the stream
+// also zeroes the sliced walk's per-request coordination words (its first
+// workgroup, before anything else), which saves the sampler a launch.
+__device__ __forceinline__ void clear_walk_words(const AttnParams& p, bool first) {
+  if (p.clear_words && first)
+    for (int i = threadIdx.x; i < p.nclear; i += blockDim.x) p.clear_words[i] = 0;
+}
+
 // One launch before the attention kernel: blocks [0, n_tree) build the
 // ancestor masks (16 requests per block, a wave each); one more block, when
 // the grid is compacted, builds the work list (it needs only the packing).
@@ -334,6 +342,7 @@ void attn_mfma_kernel(AttnParams p) {
   __shared__ uint64_t smask[kMaxNodes];  // the request's masks when no mask array exists
 
   int job, rg;
+  clear_walk_words(p, blockIdx.x == 0);
   if (!decode_block(p, blockIdx.x, job, rg)) return;
   const int split = job % p.splits;
   const int bg = job / p.splits;
@@ -667,6 +676,7 @@ void attn_mfma32_kernel(AttnParams p) {
   constexpr int VSW = D >= 128 ? 4 : 2;
 
   int job, rg;
+  clear_walk_words(p, blockIdx.x == 0);
   if (!decode_block(p, blockIdx.x, job, rg)) return;
   const int split = job % p.splits;
   const int bg = job / p.splits;
@@ -1033,6 +1043,7 @@ void attn_mfma32_kernel(AttnParams p) {
 // dims t%32 + 32k for the output.
 template <int D, bool PAGED = false>
 __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
+  clear_walk_words(p, blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0);
   constexpr int KT = 32, RW = 8, DPT = D / 32;
   __shared__ float Qs[RW][D];
   __shared__ float Ks[KT][D + 1];

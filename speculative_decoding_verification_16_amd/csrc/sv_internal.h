@@ -46,6 +46,10 @@ struct AttnParams {
   // multiplies the output
   bool kv_fp8;
   float v_scale;
+  // in the step: the sliced walk's coordination words, zeroed by the launch's
+  // first workgroup (the walk follows on the same stream), or null
+  int32_t* clear_words;
+  int32_t nclear;
 };
 
 struct AttnPlan {
@@ -103,6 +107,7 @@ struct SampleParams {
   RowStat* rowstats;        // [N+B] workspace
   int32_t slices;           // workgroups per request in the walk (1: no exchange)
   int32_t lazy;             // the walk computes the statistics of the rows it reaches (no statistics pass)
+  int32_t coord_cleared;    // the step's attention launch has already zeroed xcnt
   double* xs;               // [B, 2, 2 nch] workspace when slices > 1
   int32_t* xcnt;            // [B, kWalkSync] workspace when slices > 1 (zeroed by the sampler)
   uint32_t join_ticks;      // start-up window of a request's slices (100 MHz ticks; 0: none, the

@@ -1226,7 +1226,7 @@ hipError_t launch_sampler(const SampleParams& p, bool vec4, hipStream_t stream, 
   const int ns = p.B * kWalkSync;
   int32_t* xc = p.slices > 1 ? p.xcnt : nullptr;
   const int64_t stat_items = lazy ? 0 : items;
-  const int nsb = lazy ? (xc ? (ns + 255) / 256 : 0) : (int)((items + 3) / 4);
+  const int nsb = lazy ? ((xc && !p.coord_cleared) ? (ns + 255) / 256 : 0) : (int)((items + 3) / 4);
   const dim3 sgrid((unsigned)nsb);
   const dim3 pgrid((unsigned)((items + 3) / 4));     // the p-row output (one wave per (row, chunk) as well)
   if (ev.start) (void)hipEventRecord(ev.start, stream);
