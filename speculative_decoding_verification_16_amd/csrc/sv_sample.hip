@@ -163,7 +163,7 @@ __device__ __forceinline__ void chunk_stat(const float* __restrict__ base, int V
 }
 
 template <bool GREEDY, bool VEC, bool ENT = false>
-__global__ __launch_bounds__(256) void row_stats_kernel(const float* __restrict__ logits, int V, int64_t rows,
+__global__ __launch_bounds__(256) void row_stats_kernel(const float* __restrict__ logits, int V,
                                                         int nch, float c, ChunkStat* __restrict__ stats,
                                                         int32_t* xcnt, int nsync, int64_t stat_items,
                                                         double2* __restrict__ ent = nullptr, double c64 = 0.0) {
@@ -778,7 +778,7 @@ __device__ __forceinline__ ChunkStat fetch_chunk(ChunkStat* src) {
 // those of the other form. A sliced request splits each row's chunks over
 // all its slices' waves and exchanges the records at a slice barrier.
 template <bool VEC, int NT, bool TR, bool LAZY = false>
-__global__ __launch_bounds__(NT, 2) void walk_kernel(SampleParams p) {  // 2 waves per SIMD: two 256-thread slices per CU
+__global__ __launch_bounds__(NT, 2) void walk_kernel(SampleParams p) {  // >= 2 waves per SIMD: 256 VGPRs at most
   __shared__ WalkShared<NT> sh;
   __shared__ LazyRow<LAZY, TR> lz;
   // blocks past the walk's merge the step's split-K attention partials: the
@@ -1232,18 +1232,18 @@ hipError_t launch_sampler(const SampleParams& p, bool vec4, hipStream_t stream, 
   if (ev.start) (void)hipEventRecord(ev.start, stream);
   if (sgrid.x > 0) {
     if (p.greedy) {
-      if (vec4) row_stats_kernel<true, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, xc, ns, stat_items);
-      else row_stats_kernel<true, false><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, xc, ns, stat_items);
+      if (vec4) row_stats_kernel<true, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, p.nch, p.c, p.stats, xc, ns, stat_items);
+      else row_stats_kernel<true, false><<<sgrid, 256, 0, stream>>>(p.logits, p.V, p.nch, p.c, p.stats, xc, ns, stat_items);
     } else if (p.eta) {
       if (vec4)
-        row_stats_kernel<false, true, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, xc,
+        row_stats_kernel<false, true, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, p.nch, p.c, p.stats, xc,
                                                                       ns, stat_items, p.ent, p.c64);
       else
-        row_stats_kernel<false, false, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, xc,
+        row_stats_kernel<false, false, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, p.nch, p.c, p.stats, xc,
                                                                        ns, stat_items, p.ent, p.c64);
     } else {
-      if (vec4) row_stats_kernel<false, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, xc, ns, stat_items);
-      else row_stats_kernel<false, false><<<sgrid, 256, 0, stream>>>(p.logits, p.V, rows, p.nch, p.c, p.stats, xc, ns, stat_items);
+      if (vec4) row_stats_kernel<false, true><<<sgrid, 256, 0, stream>>>(p.logits, p.V, p.nch, p.c, p.stats, xc, ns, stat_items);
+      else row_stats_kernel<false, false><<<sgrid, 256, 0, stream>>>(p.logits, p.V, p.nch, p.c, p.stats, xc, ns, stat_items);
     }
   }
   if (ev.stats_stop) (void)hipEventRecord(ev.stats_stop, stream);
