@@ -190,13 +190,15 @@ def test_sampler_is_deterministic_and_step_matches_parts():
 
 
 @pytest.mark.parametrize("ticks", [-1, 1])
-@pytest.mark.parametrize("name", ["c2_small", "c3_small", "c4_small_cold", "c2_llama8b_chain"])
+@pytest.mark.parametrize("name", ["c2_small", "c3_small", "c4_small_cold", "c2_llama8b_chain", "c3_eagle_tree"])
 def test_sliced_walk_fallback_matches(name, ticks):
     # Small batches walk each request with several workgroups that first agree
     # to cooperate. No start-up window (join_ticks -1) makes the first
     # workgroup to look walk its request alone; 1 tick mixes both outcomes
     # across requests. Either way the outputs are bitwise those of the
-    # default window.
+    # default window. (The full-size EAGLE tree batch holds over 128 MiB of
+    # logits, so its walk also reduces the rows it reaches itself: alone, a
+    # slice reduces every chunk of a row with its own four waves.)
     cfg = SMALL[name] if name in SMALL else get_config(name)
     w = generate(cfg, "cuda", attn=False)
     T = cfg.temperature
