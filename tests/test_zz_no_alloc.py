@@ -31,8 +31,11 @@ def _snapshot(r):
 
 def test_noalloc_matches_step_twice_then_smaller():
     big = scaled(CONFIGS["c3_eagle_tree"], B=6, L=1500, V=20000)       # sliced walk, split-K attention
+    # 366 rows of 128256 logits (188 MB): the sliced walk reduces the rows it
+    # reaches, its coordination words zeroed by the attention launch
+    lazy = scaled(CONFIGS["c3_eagle_tree"], B=6, L=1500)
     small = scaled(CONFIGS["c5_super_tree"], B=10, K=70, L=300, V=9000)  # wide trees, other layout
-    for cfg in (big, small):
+    for cfg in (big, lazy, small):
         step = _calls(cfg)
         print(f"[noalloc] {cfg.name} B={cfg.B} ws={step.ws_bytes}", flush=True)
         ref = _snapshot(step())
