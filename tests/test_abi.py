@@ -154,6 +154,29 @@ def test_walk_layout_query(lib):
     assert lib.spec_verify_last_error()
 
 
+def test_walk_layout_of_the_workloads(lib):
+    """The size rule on the benchmark workloads' shapes (host fields only):
+    the batch-256 super tree (2048 nodes, 151936 logits) and the 16-request
+    EAGLE tree (60 nodes each, 128256 logits) reduce the rows they reach; the
+    8-request chain of 5 and the 3-node chains of 32 requests keep the
+    statistics pass; asking for the p rows always keeps it."""
+    import speculative_decoding_verification_16_amd as sv
+
+    def lazy(B, N, V, **kw):
+        n, z = ctypes.c_int32(-1), ctypes.c_int32(-1)
+        s = _sample_args(sv, B=B, total_nodes=N, V=V, max_nodes=64, max_depth=64,
+                         walk_mode=sv.WALK_MODES["single"], **kw)
+        assert lib.spec_verify_walk_layout(ctypes.byref(s), ctypes.byref(n), ctypes.byref(z)) == 0, \
+            lib.spec_verify_last_error()
+        return z.value
+
+    assert lazy(256, 2048, 151936) == 1
+    assert lazy(16, 960, 128256) == 1
+    assert lazy(8, 40, 128256) == 0
+    assert lazy(32, 96, 128256) == 0
+    assert lazy(256, 2048, 151936, probs_out=ctypes.c_void_p(0x100000)) == 0
+
+
 def test_step_overlap_field(lib):
     """step_overlap is validated on the host and does not change the
     workspace (the two schedules use the same disjoint regions)."""
