@@ -106,6 +106,45 @@ def test_draft_probability_zero(layout):
 
 @pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("T", [0.0, 1.0])
+def test_rows_without_distribution_reduced_by_the_walk(layout, T):
+    """The same four rows without a distribution in a batch of 1000 requests
+    (3000 rows of 12388 logits, over 128 MiB), so that the walk reduces the
+    rows it reaches itself instead of a statistics pass: its NaN / +inf test
+    (a NaN chunk sum, or a per-logit test of a chunk whose maximum is -inf)
+    must stop the same walks."""
+    rng = np.random.default_rng(1204)
+    V, B = V_EVEN, 1000
+    parent = np.array([-1, 0], np.int32)
+    lg = (rng.standard_normal((B * 3, V)) * 2).astype(np.float32)
+    q = _softmax_rows(lg + rng.standard_normal(lg.shape).astype(np.float32)).astype(np.float32)
+    toks = rng.integers(0, V, size=(B, 2)).astype(np.int32)
+    for b in range(5):
+        a = int(np.argmax(lg[3 * b]))
+        toks[b] = [a, 17]
+        q[3 * b, a] = 0.0
+    lg[3 * 0 + 1, 0] = np.nan
+    lg[3 * 1 + 1, 5000] = np.inf
+    lg[3 * 2 + 1, :] = -np.inf
+    lg[3 * 3 + 1, V - 1] = np.nan
+    cu = (np.arange(B + 1) * 2).astype(np.int32)
+    call = sv.SampleCall(torch.from_numpy(cu).cuda(), torch.from_numpy(np.tile(parent, B)).cuda(),
+                         torch.from_numpy(toks.reshape(-1)).cuda(), torch.from_numpy(lg).cuda(),
+                         None if T == 0 else torch.from_numpy(q).cuda(), temperature=T, seed=1, max_nodes=2,
+                         walk_mode=layout)
+    assert call.walk_layout()[1]  # the walk reduces the rows it reaches
+    del call
+    r, ref = _run(cu, np.tile(parent, B), toks.reshape(-1), lg, q, T, layout)
+    st = int(r["status"].item())
+    assert st & 0x08 and not (st & ~0x08)
+    assert all(ref["status"][b] & 0x08 for b in range(4)) and ref["status"][4] == 0
+    compare_walk(r, ref, B, greedy=T == 0, max_flagged=max(2, B // 64))
+    acc = r["accept_len"].cpu().numpy()
+    out = r["out_tokens"].cpu().numpy()
+    assert (acc[:4] == 1).all() and (out[:4, 1] == -1).all()
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("T", [0.0, 1.0])
 def test_rows_without_distribution(layout, T):
     """Row 1 (after node 0) of request k holds a NaN at index 0, a +inf, only
     -inf, or a NaN in the last chunk; node 0 is always accepted (greedy: it
