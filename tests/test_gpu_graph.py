@@ -14,11 +14,15 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("overlap", ["off", "on"])
-@pytest.mark.parametrize("name", ["c2_small", "c3_small", "c5_small"])
+@pytest.mark.parametrize("name", ["c2_small", "c3_small", "c5_small", "c3_reached_rows"])
 def test_step_graph_replays_match_eager(name, overlap):
+    # (c3_reached_rows: 366 rows of 128256 logits, over 128 MiB, so the
+    # sliced walk reduces the rows it reaches; in order, the attention launch
+    # zeroes the slices' coordination words)
     cfg = {"c2_small": scaled(CONFIGS["c2_llama8b_chain"], B=4, L=700, V=5000),
            "c3_small": scaled(CONFIGS["c3_eagle_tree"], B=3, L=300, V=9000),
-           "c5_small": scaled(CONFIGS["c5_super_tree"], B=12, K=100, L=250, V=7001)}[name]
+           "c5_small": scaled(CONFIGS["c5_super_tree"], B=12, K=100, L=250, V=7001),
+           "c3_reached_rows": scaled(CONFIGS["c3_eagle_tree"], B=6, L=1500)}[name]
     w = generate(cfg, "cuda")
     print(f"[graph] {name} overlap={overlap} B={w['B']} N={w['N']}", flush=True)
     a = sv.AttnCall(w["q"], w["k_cache"], w["v_cache"], w["ctx_len_t"], w["cu_nodes_t"], parent=w["parent_t"],
