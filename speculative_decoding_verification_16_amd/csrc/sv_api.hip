@@ -353,7 +353,7 @@ int walk_slices_for(const sv_sample_args* s, const WsLayout& w) {
 // Below that the pass takes under 20 us at the measured 6.6 TB/s, while the
 // walk's own per-row reduction adds a few microseconds of latency to every
 // row a request reaches (a chain of 3-4 rows for the 8-request, 48-row
-// batch: sampler 34 -> 54 us lazily; 16 requests of 61 rows: 119 -> 83 us).
+// batch: sampler 34 -> 54 us lazily; 16 requests of 61 rows: 119 -> 78 us).
 constexpr double kLazyMinLogitBytes = 128.0 * 1024 * 1024;
 bool walk_lazy(const sv_sample_args* s) {
   const double bytes = ((double)s->total_nodes + s->B) * (double)s->V * 4.0;
