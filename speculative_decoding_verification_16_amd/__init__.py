@@ -10,7 +10,10 @@ raise; there is no fallback.
     step(...)    both on one stream                 -> spec_verify_step
 
 AttnCall / SampleCall / StepCall prepare the argument block, outputs and
-workspace once so that repeated launches only cross the ABI.
+workspace once so that repeated launches only cross the ABI; StepCall.timed
+and StepCall.noalloc reach spec_verify_step_timed and
+spec_verify_step_noalloc, SampleCall.walk_layout spec_verify_walk_layout,
+and pack(...) / PackCall spec_verify_pack.
 """
 from __future__ import annotations
 
