@@ -574,9 +574,12 @@ def main():
     attn_b, attn_f = attention_bytes(w, 1 if args.kv_fp8 else 0), attention_flops(w)
     rs_b = row_stats_bytes(w)
     # sampled siblings: one 8V pass (logits and q) per rejection; deterministic
-    # candidates and the truncation rule's membership tests need none (the
-    # truncation visit and redraw passes are not counted here)
-    per_pass = 0 if det or args.rule == "truncation" else 8 * w["V"]
+    # candidates and the truncation rule's membership tests need none. Under
+    # min-p or eta truncation a pass reads only the chunks that hold an allowed
+    # token, a number the walk does not report: its passes are not counted
+    # there, so the sampler's fraction is a lower bound
+    truncated = args.min_p > 0 or args.eta is not None
+    per_pass = 0 if det or args.rule == "truncation" or truncated else 8 * w["V"]
     # the walk's layout: workgroups per request, and whether it computes the
     # statistics of the rows it reaches itself (reading no other row) or has a
     # statistics pass read every row first
@@ -612,7 +615,7 @@ def main():
             "us": smp_ms * 1e3, "alg_bytes": smp_b, "GB_s": smp_b / smp_ms / 1e6,
             "frac": smp_b / smp_ms / 1e6 / HBM_PEAK_GBS, "rows_reached": visited_mean,
             "rows_read": visited_mean if lazy else float(w["N"] + w["B"]),
-            "residual_pass_bytes": passes_mean * per_pass}
+            "residual_pass_bytes": passes_mean * per_pass if not truncated else None}
         if args.overlap == "off":
             rest_us = ms * 1e3 - attn_ms * 1e3 - smp_ms * 1e3
             kernels["other(prep+combine)"] = {"us": rest_us}

@@ -526,7 +526,7 @@ template <bool VEC, int NT, bool TR>
 __device__ __forceinline__ double residual_pass(WalkShared<NT>& sh, const float* lrow, const float* qrow, int V, int nch,
                                                 float lw, float lmax, float c, const RowThr& theta, double S,
                                                 double cc,
-                                                const Slices& sl, int pass_no) {
+                                                const Slices& sl, int pass_no, const ChunkStat* cst) {
   constexpr int NW = NT / kWave;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nh = 2 * nch;
@@ -534,6 +534,23 @@ __device__ __forceinline__ double residual_pass(WalkShared<NT>& sh, const float*
   double* xb = sl.xs + (pass_no & 1) * nh;
   const float ccS = (float)(cc * S);
   const double invS = 1.0 / S;
+  // Under truncation a token outside the allowed set weighs 0, and the set
+  // is an upper set of logits (l - l_max above a threshold), so a chunk whose
+  // maximum (cst: the row's chunk records) is outside holds no allowed token:
+  // its two half-chunks have mass exactly 0 and are not read. Bit k of lmask
+  // tells whether the wave's k-th half-chunk (gw + k GW) is live; later ones
+  // are looked up one by one.
+  uint64_t lmask = ~0ull;
+  if (TR) {
+    const int hl = gw + lane * GW;
+    lmask = __ballot(hl < nh && is_allowed<TR>(cst[hl >> 1].lmax, lmax, theta));
+  }
+  auto live = [&](int k, int h) -> bool {  // k and h are the same in every lane of the wave
+    if (!TR) return true;
+    if (k < 64) return (lmask >> k) & 1;
+    const float cm = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(cst[h >> 1].lmax)));
+    return is_allowed<TR>(cm, lmax, theta);
+  };
   if (VEC) {
     // two half-chunks per wave in flight: the next one's loads are issued
     // before the current one is reduced (past the row's end they read zeros).
@@ -546,28 +563,63 @@ __device__ __forceinline__ double residual_pass(WalkShared<NT>& sh, const float*
           __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(qrow), (short)0,
                                             __builtin_amdgcn_readfirstlane(cc == 0.0 ? 0 : V * 4), 0x00020000);
       HalfRegs ra, rb;
-      half_load(ra, lrs, qrs, gw, lane);
-      for (int h = gw; h < nh; h += 2 * GW) {
-        const int h1 = h + GW;
-        half_load(rb, lrs, qrs, h1, lane);
-        const double m0 = half_mass<VEC, TR>(ra, V, h, lane, lw, lmax, c, ccS, theta) * invS;
-        if (lane == 0) {
-          sh.hsum[h] = m0;
-          if (sl.n > 1) publish(xb + h, m0);
-        }
-        half_load(ra, lrs, qrs, h1 + GW, lane);
-        if (h1 < nh) {
-          const double m1 = half_mass<VEC, TR>(rb, V, h1, lane, lw, lmax, c, ccS, theta) * invS;
+      if constexpr (TR) {
+        // the loads go to live half-chunks only; a dead one gets mass 0 here.
+        // next_live(k): the wave's first live half-chunk from its k-th on
+        auto next_live = [&](int k) -> int {
+          for (int h = gw + k * GW; h < nh && !live(k, h); ++k, h += GW)
+            if (lane == 0) {
+              sh.hsum[h] = 0.0;
+              if (sl.n > 1) publish(xb + h, 0.0);
+            }
+          return k;
+        };
+        int k = next_live(0), h = gw + k * GW;
+        half_load(ra, lrs, qrs, h, lane);
+        while (h < nh) {
+          const int k1 = next_live(k + 1), h1 = gw + k1 * GW;
+          half_load(rb, lrs, qrs, h1, lane);
+          const double m0 = half_mass<VEC, TR>(ra, V, h, lane, lw, lmax, c, ccS, theta) * invS;
           if (lane == 0) {
-            sh.hsum[h1] = m1;
-            if (sl.n > 1) publish(xb + h1, m1);
+            sh.hsum[h] = m0;
+            if (sl.n > 1) publish(xb + h, m0);
+          }
+          const int k2 = h1 < nh ? next_live(k1 + 1) : k1, h2 = gw + k2 * GW;
+          half_load(ra, lrs, qrs, h2, lane);
+          if (h1 < nh) {
+            const double m1 = half_mass<VEC, TR>(rb, V, h1, lane, lw, lmax, c, ccS, theta) * invS;
+            if (lane == 0) {
+              sh.hsum[h1] = m1;
+              if (sl.n > 1) publish(xb + h1, m1);
+            }
+          }
+          k = k2;
+          h = h2;
+        }
+      } else {
+        half_load(ra, lrs, qrs, gw, lane);
+        for (int h = gw; h < nh; h += 2 * GW) {
+          const int h1 = h + GW;
+          half_load(rb, lrs, qrs, h1, lane);
+          const double m0 = half_mass<VEC, TR>(ra, V, h, lane, lw, lmax, c, ccS, theta) * invS;
+          if (lane == 0) {
+            sh.hsum[h] = m0;
+            if (sl.n > 1) publish(xb + h, m0);
+          }
+          half_load(ra, lrs, qrs, h1 + GW, lane);
+          if (h1 < nh) {
+            const double m1 = half_mass<VEC, TR>(rb, V, h1, lane, lw, lmax, c, ccS, theta) * invS;
+            if (lane == 0) {
+              sh.hsum[h1] = m1;
+              if (sl.n > 1) publish(xb + h1, m1);
+            }
           }
         }
       }
     }
   } else {
-    for (int h = gw; h < nh; h += GW) {
-      const double m = half_scalar<TR>(lrow, qrow, V, h, lw, lmax, c, ccS, theta, lane) * invS;
+    for (int k = 0, h = gw; h < nh; ++k, h += GW) {
+      const double m = live(k, h) ? half_scalar<TR>(lrow, qrow, V, h, lw, lmax, c, ccS, theta, lane) * invS : 0.0;
       if (lane == 0) {
         sh.hsum[h] = m;
         if (sl.n > 1) publish(xb + h, m);
@@ -1006,6 +1058,8 @@ __global__ __launch_bounds__(NT, 2) void walk_kernel(SampleParams p) {  // >= 2 
     }
     const RowStat st = sh.rs[r];
     const RowThr th = TR ? sh.th[r] : RowThr{};  // this row's threshold of the allowed set
+    // this row's chunk records (in LDS when the walk reduced the row itself)
+    const ChunkStat* rowcs = LAZY ? (const ChunkStat*)lz.cst : p.stats + row * p.nch;
     // children of pos in increasing index: the same ballot in every wave
     const uint64_t kids = __ballot(lane < T && sh.par[lane] == pos);
     if (st.lmax == -INFINITY) {  // no finite logit: p is undefined here, stop without a token
@@ -1052,7 +1106,7 @@ __global__ __launch_bounds__(NT, 2) void walk_kernel(SampleParams p) {  // >= 2 
       double cc = 0.0, total = 0.0;
       if (kids) {
         total = residual_pass<VEC, NT, TR>(sh, lrow, qrow, p.V, p.nch, INFINITY, st.lmax, p.c, th, 1.0, -1.0, sl,
-                                           ++npass);
+                                           ++npass, rowcs);
         if (__builtin_amdgcn_readfirstlane(total > 0.0 ? 1 : 0)) {
           level = 1;
           lw = INFINITY;
@@ -1063,7 +1117,7 @@ __global__ __launch_bounds__(NT, 2) void walk_kernel(SampleParams p) {  // >= 2 
       }
       if (level == 0)
         total = residual_pass<VEC, NT, TR>(sh, lrow, qrow, p.V, p.nch, st.lmax, st.lmax, p.c, th, 1.0, 0.0, sl,
-                                           ++npass);
+                                           ++npass, rowcs);
       if (!lead) return;  // the draw needs no other slice
       const double uf = uniform01(p.seed, rid, 0u, 1u, p.step);
       bonus = draw_token<VEC, NT, TR>(sh, lrow, qrow, p.V, p.nch, level, lw, st.lmax, p.c, th, 1.0, cc, uf, total, 0);
@@ -1076,7 +1130,7 @@ __global__ __launch_bounds__(NT, 2) void walk_kernel(SampleParams p) {  // >= 2 
     double Srow = st.S;
     bool csum_ok = false;      // csum holds the chunk masses of the current level
     if (TR) {
-      Srow = residual_pass<VEC, NT, TR>(sh, lrow, qrow, p.V, p.nch, st.lmax, st.lmax, p.c, th, 1.0, 0.0, sl, ++npass);
+      Srow = residual_pass<VEC, NT, TR>(sh, lrow, qrow, p.V, p.nch, st.lmax, st.lmax, p.c, th, 1.0, 0.0, sl, ++npass, rowcs);
       csum_ok = true;
     }
     if (p.det) {
@@ -1121,7 +1175,7 @@ __global__ __launch_bounds__(NT, 2) void walk_kernel(SampleParams p) {  // >= 2 
       // (from the row statistics, or this position's pass under truncation)
       // minus the removed weights
       if (!TR) {
-        const ChunkStat* cs = LAZY ? (const ChunkStat*)lz.cst : p.stats + row * p.nch;
+        const ChunkStat* cs = rowcs;
         for (int ch = tid; ch < p.nch; ch += NT) {
           const ChunkStat s = cs[ch];
           sh.csum[ch] = s.lmax == -INFINITY ? 0.0 : s.s * exp2((double)(s.lmax - st.lmax) * (double)p.c);
@@ -1164,7 +1218,7 @@ __global__ __launch_bounds__(NT, 2) void walk_kernel(SampleParams p) {  // >= 2 
       // rejected: the next sibling is tested against the next residual level
       const double cn = cc + M;
       const double Mn =
-          residual_pass<VEC, NT, TR>(sh, lrow, qrow, p.V, p.nch, st.lmax, st.lmax, p.c, th, Srow, cn, sl, ++npass);
+          residual_pass<VEC, NT, TR>(sh, lrow, qrow, p.V, p.nch, st.lmax, st.lmax, p.c, th, Srow, cn, sl, ++npass, rowcs);
       ++passes;
       if (__builtin_amdgcn_readfirstlane(Mn > 0.0 ? 1 : 0)) {
         cc = cn;
@@ -1187,7 +1241,7 @@ __global__ __launch_bounds__(NT, 2) void walk_kernel(SampleParams p) {  // >= 2 
     if (level == 0 && TR) {  // the chunk masses of p_Theta from this position's pass
       total = Srow;
     } else if (level == 0) {
-      const ChunkStat* cs = LAZY ? (const ChunkStat*)lz.cst : p.stats + row * p.nch;
+      const ChunkStat* cs = rowcs;
       for (int ch = tid; ch < p.nch; ch += NT) {
         const ChunkStat s = cs[ch];
         sh.csum[ch] = s.lmax == -INFINITY ? 0.0 : s.s * exp2((double)(s.lmax - st.lmax) * (double)p.c);
@@ -1196,7 +1250,7 @@ __global__ __launch_bounds__(NT, 2) void walk_kernel(SampleParams p) {  // >= 2 
       total = st.S;
     } else {
       if (!csum_ok) {
-        residual_pass<VEC, NT, TR>(sh, lrow, qrow, p.V, p.nch, st.lmax, st.lmax, p.c, th, Srow, cc, sl, ++npass);
+        residual_pass<VEC, NT, TR>(sh, lrow, qrow, p.V, p.nch, st.lmax, st.lmax, p.c, th, Srow, cc, sl, ++npass, rowcs);
         ++passes;
       }
       total = M;
