@@ -929,6 +929,15 @@ void attn_mfma32_kernel(AttnParams p) {
     }
     l += lsum;
     m = mnew;
+    // The wave issues its PV MFMAs at raised priority, so that the SIMD's
+    // other wave, if it is in its softmax, runs its VALU work beside them
+    // rather than in step with this wave. In eight-wave workgroups the two
+    // waves of a SIMD are waves w and w + 4: only the upper one raises its
+    // priority. (Measured on MI355X: C5 attention 432 -> 424 us, C3 even;
+    // raising it during the softmax instead, or on both waves of an eight-wave
+    // SIMD, was slower.)
+    const bool pv_prio = NW == 4 || wave >= 4;
+    if (pv_prio) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int kq = kk >> 1, v0 = 8 * (kk & 1);
@@ -948,6 +957,7 @@ void attn_mfma32_kernel(AttnParams p) {
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk, o[db], 0, 0, 0);
       }
     }
+    if (pv_prio) __builtin_amdgcn_s_setprio(0);
   };
 
   // Pipeline: K runs one tile ahead of V. At the top of iteration t the loads
