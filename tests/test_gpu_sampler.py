@@ -706,10 +706,15 @@ def test_sampler_max_vocab():
     r = _gpu_sample(w, 0.0)
     assert int(r["status"].item()) == 0
     compare_walk(r, _oracle(w, 0.0, r["accepted_nodes"].shape[1]), w["B"], greedy=True)
-    for kw in ({"min_p": 0.05}, {"eta": (0.05, 0.3)}):
-        r = _gpu_sample(w, T, **kw)
+    # truncated passes skip the chunks with no allowed token; in the single
+    # layout a wave visits 256 half-chunks of a row, past the 64 its first
+    # liveness ballot covers
+    for kw, mode in (({"min_p": 0.05}, "auto"), ({"min_p": 0.05}, "single"), ({"eta": (0.05, 0.3)}, "auto"),
+                     ({"eta": (0.05, 0.3)}, "single")):
+        r = _gpu_sample(w, T, walk_mode=mode, **kw)
         assert int(r["status"].item()) == 0, sv.status_names(int(r["status"].item()))
-        compare_walk(r, _oracle_kw(w, T, r["accepted_nodes"].shape[1], **kw), w["B"], greedy=False)
+        flagged = compare_walk(r, _oracle_kw(w, T, r["accepted_nodes"].shape[1], **kw), w["B"], greedy=False)
+        print(f"  {kw} {mode}: flagged {flagged}/{w['B']}, passes {r['residual_passes'].tolist()}", flush=True)
     r = _gpu_sample(w, T, probs_out=True)
     rows = np.array([0, w["N"] + w["B"] - 1])
     p_ref = oracle.target_rows(w["logits"].cpu().numpy(), T, rows)
