@@ -379,7 +379,7 @@ def main():
     args = parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the verification step shards by request "
-              "with no inter-GPU traffic, and this build measures one GPU's share.", file=sys.stderr)
+              "with no inter-GPU traffic, so one GPU's share is what it measures.", file=sys.stderr)
         sys.exit(2)
 
     if args.copy_probe:
